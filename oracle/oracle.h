@@ -1,0 +1,160 @@
+/*
+ * CPU ORACLE -- TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, obviously correct CPU implementation of one batch-1
+ * speculative-decode verify step of a DeepSeek-style mixture-of-experts decoder
+ * layer, and of the stack around it (embedding, final norm, LM head, greedy
+ * acceptance).  Only the test suite, the smoke check and the benchmark's CPU
+ * baseline may load or call it.  It shares no code with the GPU library.
+ *
+ * Sources of the computation:
+ *  - Which operations make up the layer and in what order (RMSNorm, Q and
+ *    latent-KV projections with RoPE and KV insert, latent attention over the
+ *    KV cache for T = k+1 verify rows, router softmax/top-k, routed and shared
+ *    SwiGLU experts, residual adds): "Why one GB300 doesn't beat 4x RTX PRO
+ *    6000 at single-stream decode", section "Where the 11.2 ms goes" (the
+ *    per-kernel table: norm/quant, q-norm-rope-insert, FlashMLA decode
+ *    attention, top-k, prepare-megamoe, MegaMoE, lm_head, rejection kernel)
+ *    and section "Tier 2: the fusion program" (norm -> gate -> top-k -> shared
+ *    expert); the same report, section "The decomposition", for verify blocks
+ *    of k drafts plus one row, tiled for at most 8 rows.
+ *  - The multi-head latent attention algebra (latent KV cache c, decoupled
+ *    RoPE key shared by all heads, absorbed query q~ = W_UK^T q^C): the
+ *    DeepSeek-V2 paper, section 2.1 "Multi-Head Latent Attention"; the pages
+ *    name FlashMLA as the attention kernel ("DeepSeek-V4.1-Flash breaks 1,000
+ *    tokens per second for one user", section "Appendix: method").
+ *  - RMSNorm (Zhang and Sennrich 2019), RoPE (Su et al., RoFormer, 2021,
+ *    adjacent-pair form), SwiGLU (Shazeer 2020), softmax top-k gating with
+ *    renormalised gates over the selected experts.
+ *  - OCP 8-bit floating point specification (E4M3) for fp8 weights.
+ *
+ * Readings where the pages are silent (each listed in the design notes):
+ * eps = 1e-6; softmax scale 1/sqrt(d_h + d_r); RoPE base 10000 with the angle
+ * p * theta_j formed in double; selection by logit with ties to the lower
+ * expert index; gates = softmax probabilities of the selected experts
+ * renormalised to sum to 1; the shared expert is added with weight 1; new KV
+ * rows are rounded to the cache's storage format and read back by attention.
+ *
+ * Arithmetic: weights are widened/dequantised exactly (fp8: (float)q * s);
+ * activations are fp32; every dot product accumulates in fp32 in increasing
+ * index order.  The *_f64 entry points redo the layer in double precision in
+ * the un-absorbed form (per-head keys and values expanded from the latent).
+ */
+#ifndef MK_ORACLE_H
+#define MK_ORACLE_H
+#include <stdint.h>
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_FP8B128 = 2 };
+
+typedef struct orc_cfg {
+  int d;          /* hidden size */
+  int n_h, d_h;   /* heads, per-head content dim */
+  int d_c, d_r;   /* latent KV rank, decoupled RoPE dim (even) */
+  int E, top_k;   /* routed experts, experts picked per token */
+  int n_shared;   /* shared experts (always applied, weight 1) */
+  int f;          /* expert FFN width */
+  int attn_fmt;   /* ORC_F32 | ORC_BF16: W_Q, W_DKV, W_UK, W_UV, W_O, W_R */
+  int exp_fmt;    /* ORC_F32 | ORC_BF16 | ORC_FP8B128: W1, W3, W2 */
+  int kv_fmt;     /* ORC_F32 | ORC_BF16 */
+  float eps;      /* RMSNorm epsilon */
+  double rope_base;
+} orc_cfg;
+
+/* Canonical (row-major) weights.  Expert slot e in [0, E) is routed expert e,
+ * slot E + s is shared expert s.  A NULL expert pointer is allowed for experts
+ * no token selects; using one is an error (-3).
+ *   W_Q   [n_h*(d_h+d_r)][d]   head h owns rows h*(d_h+d_r) ...: first d_h = q^C, last d_r = q^R
+ *   W_DKV [d_c+d_r][d]         first d_c rows -> latent c, last d_r -> pre-RoPE shared key
+ *   W_UK  [n_h][d_h][d_c]      k^C_h = W_UK[h] c
+ *   W_UV  [n_h][d_h][d_c]      v_h   = W_UV[h] c
+ *   W_O   [d][n_h*d_h]
+ *   W_R   [E][d], router_bias [E] or NULL
+ *   W1,W3 [f][d], W2 [d][f]; fp8 scales [ceil(rows/128)][ceil(cols/128)]   */
+typedef struct orc_weights {
+  const float* gamma1;
+  const float* gamma2;
+  const void* wq;
+  const void* wdkv;
+  const void* wuk;
+  const void* wuv;
+  const void* wo;
+  const void* wr;
+  const float* router_bias;
+  const void* const* w1;
+  const void* const* w3;
+  const void* const* w2;
+  const float* const* s1;
+  const float* const* s3;
+  const float* const* s2;
+} orc_weights;
+
+/* Optional intermediate outputs (any pointer may be NULL). */
+typedef struct orc_attn_taps {
+  float* x;     /* [T][d]                 RMSNorm-1 output                        */
+  float* q;     /* [T][n_h][d_h+d_r]      per-head q^C and RoPE-rotated q^R       */
+  float* ckv;   /* [T][d_c+d_r]           latent c and RoPE-rotated key (unrounded) */
+  float* qabs;  /* [T][n_h][d_c]          absorbed query q~                       */
+  float* z;     /* [T][n_h][d_c]          attention-weighted latent               */
+  float* o;     /* [T][n_h*d_h]           per-head value up-projection            */
+} orc_attn_taps;
+
+typedef struct orc_moe_taps {
+  float* xp;       /* [T][d]        RMSNorm-2 output                 */
+  float* logits;   /* [T][E]        router logits (bias included)    */
+  int32_t* sel;    /* [T][top_k]    selected experts, best first     */
+  float* gate;     /* [T][top_k]    renormalised gate weights        */
+  float* y_sel;    /* [T][top_k][d] expert outputs of the picks      */
+  float* y_shared; /* [T][d]        sum of shared-expert outputs     */
+} orc_moe_taps;
+
+/* Attention block: Hp = H + W_O(attention).  Writes KV rows [L, L+T) of `kv`
+ * ([capacity][d_c+d_r] in kv_fmt) and reads rows [0, L+i] for verify row i.
+ * Returns 0, or a negative code on bad arguments. */
+int orc_attn_block(const orc_cfg* c, const orc_weights* w, const float* H, int T,
+                   void* kv, int L, float* Hp, const orc_attn_taps* taps);
+
+/* Router only: x' = RMSNorm(Hp)*gamma2, logits, top-k selection and gates. */
+int orc_router(const orc_cfg* c, const orc_weights* w, const float* Hp, int T,
+               float* xp, float* logits, int32_t* sel, float* gate);
+
+/* MoE block: out = Hp + sum_t gate_t * expert_{sel_t}(x') + sum_s shared_s(x').
+ * If force_sel is non-NULL ([T][top_k]) the selection is taken from it and the
+ * gates are recomputed from the logits for those experts. */
+int orc_moe_block(const orc_cfg* c, const orc_weights* w, const float* Hp, int T,
+                  const int32_t* force_sel, float* out, const orc_moe_taps* taps);
+
+/* Whole layer = attention block then MoE block. */
+int orc_layer_step(const orc_cfg* c, const orc_weights* w, const float* H, int T,
+                   void* kv, int L, float* out, const orc_attn_taps* at, const orc_moe_taps* mt);
+
+/* Double-precision brute force of the whole layer, un-absorbed form.  Reads
+ * KV rows [0, L) from `kv` (not modified); the new rows are rounded to kv_fmt
+ * (as the cache stores them) and written to kv_new_f64 ([T][d_c+d_r], may be
+ * NULL).  force_sel as in orc_moe_block.  Outputs in double. */
+int orc_layer_step_f64(const orc_cfg* c, const orc_weights* w, const float* H, int T,
+                       const void* kv, int L, const int32_t* force_sel,
+                       double* out, double* hp_out, double* kv_new_f64, double* logits_out,
+                       int32_t* sel_out);
+
+/* Stack pieces (bf16 tables [V][d]).  h[i] = Emb[tokens[i]] widened to fp32. */
+int orc_embed(const uint16_t* emb, int V, int d, const int32_t* tokens, int T, float* h);
+/* logits[i] = W_head (RMSNorm(h_i) * gamma_f), fp32; argmax with ties to the lower id. */
+int orc_head(const uint16_t* head, int V, int d, const float* gamma_f, float eps,
+             const float* h, int T, float* logits, int32_t* argmax);
+/* Greedy verification.  tokens = t0, d_1 .. d_{T-1}; a = argmax per row.
+ * n = largest n <= T-1 with d_j == a_{j-1} for every j <= n.  Commits n+1 tokens
+ * (d_1..d_n, a_n) into committed[0..n]; returns n+1. */
+int orc_greedy_accept(const int32_t* tokens, const int32_t* a, int T, int32_t* committed);
+
+/* Format helpers, exposed for the tests. */
+float orc_bf16_to_f32(uint16_t b);
+uint16_t orc_f32_to_bf16(float x);
+float orc_e4m3_to_f32(uint8_t q);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

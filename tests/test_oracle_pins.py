@@ -1,0 +1,371 @@
+"""Pins of the CPU oracle to things other than itself (no GPU needed).
+
+Each test checks the oracle against a closed form, an invariant, a special case
+that reduces to a textbook or library routine, the fp64 un-absorbed brute force,
+or a published format table, chosen so that a plausible slip (a dropped term, a
+wrong sign or index, a transposed operand) fails at least one of them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from synth import recipe
+from synth.configs import C0, C1, LayerShape
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+# A small bf16/fp8 shape with several 128x128 scale blocks and ragged edges.
+C0Q = LayerShape("micro_fp8", d=256, n_h=2, d_h=32, d_c=64, d_r=16, E=6, top_k=2, n_shared=1,
+                 f=160, T=3, L=7, attn_fmt="bf16", exp_fmt="fp8", kv_fmt="bf16")
+
+
+def normwise(a, ref):
+    a = np.asarray(a, np.float64).reshape(ref.shape[0], -1)
+    ref = np.asarray(ref, np.float64).reshape(ref.shape[0], -1)
+    return (np.abs(a - ref).max(axis=1) / np.abs(ref).max(axis=1)).max()
+
+
+def fresh(s, seed=0):
+    w = recipe.layer_weights_host(s, seed, 0)
+    H = recipe.hidden_host(s, seed)
+    kv = recipe.kv_prefill_host(s, seed)
+    return w, H, kv
+
+
+# ---------------------------------------------------------------- formats
+def test_e4m3_decode_matches_ocp_table():
+    g = json.load(open(os.path.join(GOLD, "ocp_e4m3_values.json")))
+    L = oracle.lib()
+    for code, val in g["values"].items():
+        assert L.orc_e4m3_to_f32(int(code, 16)) == val, code
+    for code in g["nan_codes"]:
+        assert math.isnan(L.orc_e4m3_to_f32(int(code, 16)))
+
+
+def test_e4m3_encoder_inverts_decoder_on_all_codes():
+    """Generator encoder (synth) against the oracle's decoder: two implementations."""
+    L = oracle.lib()
+    for q in range(256):
+        if q in (0x7F, 0xFF):
+            continue
+        v = L.orc_e4m3_to_f32(q)
+        back = synth.e4m3_encode(v)
+        if q == 0x80:          # -0 encodes with its sign
+            assert back == 0x80
+            continue
+        assert back == q, (hex(q), v, hex(back))
+
+
+def test_e4m3_encoder_rounding_and_saturation():
+    L = oracle.lib()
+    vals = sorted({L.orc_e4m3_to_f32(q) for q in range(0x7F) if q != 0x7F})
+    for lo, hi in zip(vals[:-1], vals[1:]):
+        mid = (lo + hi) / 2.0
+        got = L.orc_e4m3_to_f32(synth.e4m3_encode(np.float32(mid)))
+        qlo, qhi = synth.e4m3_encode(lo), synth.e4m3_encode(hi)
+        want = lo if (qlo % 2 == 0) else hi            # ties to the even code
+        assert got == want, (lo, hi, got)
+        assert L.orc_e4m3_to_f32(synth.e4m3_encode(np.nextafter(np.float32(mid), np.float32(0)))) == lo
+    assert synth.e4m3_encode(1e6) == 0x7E and synth.e4m3_encode(-500.0) == 0xFE
+    assert synth.e4m3_encode(460.0) == 0x7E
+
+
+def test_bf16_round_to_nearest_even():
+    g = json.load(open(os.path.join(GOLD, "bf16_values.json")))
+    L = oracle.lib()
+    for e in g["encode"]:
+        f = np.array([int(e["f32_bits"], 16)], np.uint32).view(np.float32)[0]
+        assert L.orc_f32_to_bf16(float(f)) == int(e["bf16"], 16), e
+        assert synth.bf16_encode(float(f)) == int(e["bf16"], 16), e
+    # every finite bf16 value survives widen -> round
+    for b in range(0, 0x10000, 7):
+        if (b & 0x7F80) == 0x7F80:
+            continue
+        assert L.orc_f32_to_bf16(L.orc_bf16_to_f32(b)) == b
+
+
+# ---------------------------------------------------------------- generator
+def test_generator_moments_and_determinism():
+    x = synth.normal_f32(1 << 20, 0, synth.stream_id("wq"), 0.02)
+    assert abs(x.mean()) < 0.02 * 0.01
+    assert abs(x.std() / 0.02 - 1.0) < 0.01
+    assert np.array_equal(x, synth.normal_f32(1 << 20, 0, synth.stream_id("wq"), 0.02))
+    y = synth.normal_f32(1 << 10, 0, synth.stream_id("wq", 0, 1), 0.02)
+    assert not np.array_equal(x[: 1 << 10], y)
+    # Irwin-Hall(4) is bounded by 2*sqrt(3) standard deviations
+    assert np.abs(x).max() <= 2 * math.sqrt(3) * 0.02 * 1.0001
+    # offset addressing is counter-based
+    assert np.array_equal(x[100:200], synth.normal_f32(100, 0, synth.stream_id("wq"), 0.02, offset=100))
+
+
+def test_generator_gain_mean():
+    g = synth.normal_f32(1 << 16, 0, synth.stream_id("gamma1"), 0.1, mean=1.0)
+    assert abs(g.mean() - 1.0) < 2e-3 and abs(g.std() - 0.1) < 2e-3
+
+
+def test_fp8_blocks_dequantise_to_the_drawn_values():
+    R, K = 300, 200
+    q, s = synth.fp8_blocks(R, K, 0, synth.stream_id("w1"), 0.02)
+    w = synth.normal_f32((R, K), 0, synth.stream_id("w1"), 0.02)
+    L = oracle.lib()
+    lut = np.array([L.orc_e4m3_to_f32(i) for i in range(256)], np.float32)
+    deq = lut[q] * np.repeat(np.repeat(s, 128, 0), 128, 1)[:R, :K]
+    # E4M3 keeps 3 mantissa bits: relative error <= 2^-4 for normals
+    big = np.abs(w) > 2 ** -6 * np.repeat(np.repeat(s, 128, 0), 128, 1)[:R, :K]
+    assert np.all(np.abs(deq - w)[big] <= np.abs(w)[big] * 2 ** -4 + 1e-12)
+    # the block maximum maps to +-448 exactly
+    for br in range(s.shape[0]):
+        for bk in range(s.shape[1]):
+            blk = q[br * 128:(br + 1) * 128, bk * 128:(bk + 1) * 128]
+            assert np.abs(lut[blk]).max() == 448.0
+
+
+# ---------------------------------------------------------------- whole layer vs fp64 brute force
+@pytest.mark.parametrize("shape", [C0, C1, C0Q], ids=lambda s: s.name)
+def test_layer_matches_fp64_unabsorbed_bruteforce(shape):
+    w, H, kv = fresh(shape)
+    kv64 = kv.copy()
+    out, taps = oracle.layer_step(shape, w, H, kv, shape.L)
+    ref = oracle.layer_step_f64(shape, w, H, kv64, shape.L, force_sel=taps["sel"])
+    assert normwise(out, ref["out"]) < 1e-5
+    # the attention branch Hp - H is ~1% of H: fp32 rounding of Hp (half an ulp of
+    # |H| <= 4, i.e. 2.4e-7) over a branch of ~1e-2 bounds this near 3e-5
+    assert normwise(taps["Hp"].astype(np.float64) - H, ref["Hp"] - H) < 1e-4
+    kvn = oracle.bf16_to_f32(kv[shape.L:shape.L + shape.T]) if shape.kv_fmt == "bf16" else kv[shape.L:shape.L + shape.T]
+    # new rows: storage rounding may flip one bf16 ulp between fp32 and fp64 paths
+    tol = 1e-5 if shape.kv_fmt == "f32" else 2 ** -7
+    assert normwise(kvn, ref["kv_new"]) < tol
+    # unforced fp64 selection agrees away from near-ties
+    lg = ref["logits"]
+    srt = -np.sort(-lg, axis=1)
+    gap = srt[:, shape.top_k - 1] - srt[:, shape.top_k]
+    for i in range(shape.T):
+        if gap[i] > 1e-4:
+            assert set(taps["sel"][i]) == set(np.argsort(-lg[i], kind="stable")[: shape.top_k])
+
+
+# ---------------------------------------------------------------- causal invariant
+@pytest.mark.parametrize("shape", [C0, C0Q], ids=lambda s: s.name)
+def test_verify_rows_equal_sequential_single_token_steps_bitwise(shape):
+    w, H, kv = fresh(shape)
+    kv_seq = kv.copy()
+    out, _ = oracle.layer_step(shape, w, H, kv, shape.L)
+    one = shape.with_(T=1)
+    outs = []
+    for i in range(shape.T):
+        o, _ = oracle.layer_step(one, w, H[i:i + 1], kv_seq, shape.L + i)
+        outs.append(o)
+    assert np.array_equal(out, np.concatenate(outs))
+    assert np.array_equal(kv, kv_seq)
+
+
+def test_later_rows_do_not_change_earlier_outputs():
+    """Row i only sees cache rows <= L+i: perturbing row T-1's input leaves rows < T-1 alone."""
+    s = C0
+    w, H, kv = fresh(s)
+    out1, _ = oracle.layer_step(s, w, H, kv.copy(), s.L)
+    H2 = H.copy()
+    H2[-1] += 1.0
+    out2, _ = oracle.layer_step(s, w, H2, kv.copy(), s.L)
+    assert np.array_equal(out1[:-1], out2[:-1])
+    assert not np.array_equal(out1[-1], out2[-1])
+
+
+# ---------------------------------------------------------------- attention special cases
+def test_empty_cache_single_token_attends_to_its_own_row():
+    s = C0.with_(T=1, L=0)
+    w, H, kv = fresh(s)
+    _, taps = oracle.layer_step(s, w, H, kv, 0)
+    own = kv[0, : s.d_c]
+    for h in range(s.n_h):
+        assert np.array_equal(taps["z"][0, h], own)
+
+
+def test_zero_query_gives_mean_of_latents():
+    s = C0
+    w, H, kv = fresh(s)
+    w["wq"] = np.zeros_like(w["wq"])
+    _, taps = oracle.layer_step(s, w, H, kv, s.L)
+    for i in range(s.T):
+        mean = kv[: s.L + i + 1, : s.d_c].astype(np.float64).mean(axis=0)
+        for h in range(s.n_h):
+            assert np.allclose(taps["z"][i, h], mean, rtol=0, atol=1e-6)
+
+
+def test_absorbed_query_is_wuk_transpose_times_qc():
+    s = C0
+    w, H, kv = fresh(s)
+    _, taps = oracle.layer_step(s, w, H, kv, s.L)
+    for h in range(s.n_h):
+        qc = taps["q"][:, h, : s.d_h].astype(np.float64)
+        ref = qc @ w["wuk"][h].astype(np.float64)            # [T][d_c]
+        assert np.allclose(taps["qabs"][:, h], ref, atol=1e-5)
+
+
+# ---------------------------------------------------------------- norm / rope
+def test_rmsnorm_constant_vector_closed_form():
+    s = C0.with_(T=1, L=0)
+    w, _, kv = fresh(s)
+    a = -3.0
+    H = np.full((1, s.d), a, np.float32)
+    _, taps = oracle.layer_step(s, w, H, kv, 0)
+    want = np.sign(a) * abs(a) / math.sqrt(a * a + s.eps) * w["gamma1"].astype(np.float64)
+    assert np.allclose(taps["x"][0], want, rtol=2e-7, atol=0)
+
+
+def test_rmsnorm_scale_invariance():
+    s = C0.with_(T=1, L=0)
+    w, H, kv = fresh(s)
+    _, t1 = oracle.layer_step(s, w, H, kv.copy(), 0)
+    _, t2 = oracle.layer_step(s, w, H * 8.0, kv.copy(), 0)   # power of two: exact scaling
+    assert np.allclose(t1["x"], t2["x"], rtol=1e-6, atol=1e-7)
+
+
+def test_rope_position_zero_is_identity_and_rotation_sign():
+    s = C0.with_(T=2, L=0)
+    w, H, kv = fresh(s)
+    _, taps = oracle.layer_step(s, w, H, kv, 0)
+    wd = w["wdkv"].astype(np.float64)
+    for i, pos in enumerate((0, 1)):
+        kr = wd[s.d_c:] @ taps["x"][i].astype(np.float64)      # pre-rotation key
+        got = taps["ckv"][i, s.d_c:].astype(np.float64)
+        # pair norms are preserved
+        assert np.allclose(np.hypot(got[0::2], got[1::2]), np.hypot(kr[0::2], kr[1::2]), rtol=1e-5)
+        # pair 0 has theta = 1: rotation by `pos` radians, counter-clockwise
+        c, sn = math.cos(pos), math.sin(pos)
+        assert np.allclose(got[:2], [kr[0] * c - kr[1] * sn, kr[0] * sn + kr[1] * c], atol=1e-5)
+        if pos == 0:
+            assert np.allclose(got, kr, atol=1e-5)
+
+
+def test_rope_is_relative_same_token_inner_product_invariant_to_offset():
+    s = C0.with_(T=1, L=0)
+    w, H, kv = fresh(s)
+    s2 = s.with_(L=1000, kv_capacity=1001)
+    kv2 = np.zeros((1001, s.kvw), np.float32)
+    _, t1 = oracle.layer_step(s, w, H, kv, 0)
+    _, t2 = oracle.layer_step(s2, w, H, kv2, 1000)
+    for h in range(s.n_h):
+        ip1 = np.dot(t1["q"][0, h, s.d_h:].astype(np.float64), t1["ckv"][0, s.d_c:].astype(np.float64))
+        ip2 = np.dot(t2["q"][0, h, s.d_h:].astype(np.float64), t2["ckv"][0, s.d_c:].astype(np.float64))
+        assert abs(ip1 - ip2) < 1e-4 * (1 + abs(ip1))
+
+
+# ---------------------------------------------------------------- router
+@pytest.mark.parametrize("shape", [C1, C0Q], ids=lambda s: s.name)
+def test_router_topk_set_and_gates(shape):
+    w, H, kv = fresh(shape)
+    _, taps = oracle.layer_step(shape, w, H, kv, shape.L)
+    lg = taps["logits"].astype(np.float64)
+    for i in range(shape.T):
+        order = np.argsort(-lg[i], kind="stable")
+        assert list(taps["sel"][i]) == list(order[: shape.top_k])
+        g = taps["gate"][i].astype(np.float64)
+        assert abs(g.sum() - 1.0) < 1e-6 and np.all(g > 0)
+        assert np.all(np.diff(g) <= 0)                      # ordered like the logits
+        p = np.exp(lg[i] - lg[i].max())
+        p /= p.sum()
+        ref = p[taps["sel"][i]] / p[taps["sel"][i]].sum()  # softmax then renormalise
+        assert np.allclose(g, ref, rtol=1e-5)
+
+
+def test_router_ties_go_to_lower_index():
+    s = C0.with_(T=1, L=0)
+    w, H, kv = fresh(s)
+    w["wr"] = np.tile(w["wr"][:1], (s.E, 1))                # all logits equal
+    _, taps = oracle.layer_step(s, w, H, kv, 0)
+    assert list(taps["sel"][0]) == list(range(s.top_k))
+    assert np.allclose(taps["gate"][0], 1.0 / s.top_k)
+
+
+def test_router_bias_enters_selection():
+    s = C0.with_(T=1, L=0)
+    w, H, kv = fresh(s)
+    w["router_bias"] = np.zeros(s.E, np.float32)
+    w["router_bias"][s.E - 1] = 1e3
+    _, taps = oracle.layer_step(s, w, H, kv, 0)
+    assert taps["sel"][0][0] == s.E - 1
+    assert taps["logits"][0][s.E - 1] > 900
+
+
+# ---------------------------------------------------------------- MoE special cases
+def test_single_expert_reduces_to_dense_swiglu_ffn():
+    s = C0.with_(E=1, top_k=1, n_shared=0, T=2)
+    w, H, kv = fresh(s)
+    out, taps = oracle.layer_step(s, w, H, kv, s.L)
+    w1, w3, w2 = (a.astype(np.float64) for a in w["experts"][0][:3])
+    xp = taps["xp"].astype(np.float64)
+    a = xp @ w1.T
+    ffn = ((a / (1 + np.exp(-a))) * (xp @ w3.T)) @ w2.T
+    assert np.allclose(taps["gate"], 1.0)
+    assert np.allclose(out, taps["Hp"].astype(np.float64) + ffn, atol=1e-5)
+
+
+def test_zero_down_projection_leaves_residual():
+    s = C0
+    w, H, kv = fresh(s)
+    for e, t in w["experts"].items():
+        w["experts"][e] = (t[0], t[1], np.zeros_like(t[2])) + t[3:]
+    out, taps = oracle.layer_step(s, w, H, kv, s.L)
+    assert np.array_equal(out, taps["Hp"])
+    w["wo"] = np.zeros_like(w["wo"])
+    out2, _ = oracle.layer_step(s, w, H, recipe.kv_prefill_host(s), s.L)
+    assert np.array_equal(out2, H)
+
+
+def test_fp8_block_scale_indexing_against_explicit_dense_matrix():
+    """Codes all 1.0 and a distinct power-of-two scale per 128x128 block: the
+    dequantised matrix is the block-constant scale map, known exactly."""
+    s = C0Q.with_(E=1, top_k=1, n_shared=0, T=1, L=0)
+    w, H, kv = fresh(s)
+    one = 0x38
+    mats = []
+    tup = []
+    for R, K in ((s.f, s.d), (s.f, s.d), (s.d, s.f)):
+        nbr, nbk = (R + 127) // 128, (K + 127) // 128
+        sc = np.array([[2.0 ** (-(i * nbk + j) - 6) for j in range(nbk)] for i in range(nbr)], np.float32)
+        tup.append((np.full((R, K), one, np.uint8), sc))
+        mats.append(np.repeat(np.repeat(sc.astype(np.float64), 128, 0), 128, 1)[:R, :K])
+    w["experts"] = {0: (tup[0][0], tup[1][0], tup[2][0], tup[0][1], tup[1][1], tup[2][1])}
+    out, taps = oracle.layer_step(s, w, H, kv, 0)
+    xp = taps["xp"].astype(np.float64)
+    a = xp @ mats[0].T
+    ffn = ((a / (1 + np.exp(-a))) * (xp @ mats[1].T)) @ mats[2].T
+    assert np.allclose(out - taps["Hp"], ffn, rtol=1e-5, atol=1e-9)
+
+
+def test_forced_selection_equal_to_own_selection_is_identity():
+    s = C0Q
+    w, H, kv = fresh(s)
+    out, taps = oracle.layer_step(s, w, H, kv.copy(), s.L)
+    out2, _ = oracle.layer_step(s, w, H, kv.copy(), s.L, force_sel=taps["sel"])
+    assert np.array_equal(out, out2)
+
+
+# ---------------------------------------------------------------- stack pieces
+def test_greedy_accept_cases():
+    t = np.array([5, 7, 9, 11], np.int32)
+    assert list(oracle.greedy_accept(t, [7, 9, 11, 13])) == [7, 9, 11, 13]     # all accepted
+    assert list(oracle.greedy_accept(t, [1, 2, 3, 4])) == [1]                  # none
+    assert list(oracle.greedy_accept(t, [7, 2, 11, 4])) == [7, 2]              # stops at first miss
+    assert list(oracle.greedy_accept(t[:1], [8])) == [8]                       # T = 1
+
+
+def test_head_argmax_ties_go_to_lower_id_and_embed_gathers_rows():
+    V, d = 10, 64
+    emb = synth.normal_bf16((V, d), 0, synth.stream_id("emb"), 0.02)
+    head = np.tile(emb[3:4], (V, 1))
+    gf = np.ones(d, np.float32)
+    h = oracle.embed(emb, np.array([3, 3], np.int32))
+    assert np.array_equal(h[0], oracle.bf16_to_f32(emb[3]))
+    _, am = oracle.head(head, gf, h)
+    assert list(am) == [0, 0]
+    head2 = head.copy()
+    head2[6] = emb[3] * 0 + synth.normal_bf16(d, 1, 1, 0.5)
+    lg, am2 = oracle.head(head2, gf, h)
+    assert am2[0] == int(np.argmax(lg[0]))
