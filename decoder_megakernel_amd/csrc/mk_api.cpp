@@ -1,0 +1,743 @@
+// The C ABI (include/mk.h): validation, sizing, packing launches, layer and
+// stack set-up, step launches.  No device memory is allocated here: every
+// buffer is the caller's.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "mk_common.h"
+#include "mk_host.h"
+
+using namespace mk;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+#define HIP_OK(expr)                                                                   \
+  do {                                                                                 \
+    hipError_t e_ = (expr);                                                            \
+    if (e_ != hipSuccess) return fail(MK_ERR_HIP, "%s: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Dims {
+  int d, nh, dh, dc, dr, qw, kvw, nq, E, topk, nshared, f;
+  int af, ef, kf;
+};
+
+Dims dims_of(const mk_layer_config* c) {
+  Dims D;
+  D.d = c->d_model; D.nh = c->n_heads; D.dh = c->d_head; D.dc = c->d_latent; D.dr = c->d_rope;
+  D.qw = D.dh + D.dr; D.kvw = D.dc + D.dr; D.nq = D.nh * D.qw; D.E = c->n_experts; D.topk = c->top_k;
+  D.nshared = c->n_shared; D.f = c->d_ff; D.af = c->attn_format; D.ef = c->expert_format; D.kf = c->kv_format;
+  return D;
+}
+
+int check_cfg(const mk_layer_config* c) {
+  if (!c) return fail(MK_ERR_INVALID_ARG, "null config");
+  if (c->abi_version != MK_ABI_VERSION)
+    return fail(MK_ERR_ABI_MISMATCH, "config abi_version %d, library %d", c->abi_version, MK_ABI_VERSION);
+  const Dims D = dims_of(c);
+  if (D.d <= 0 || D.nh <= 0 || D.dh <= 0 || D.dc <= 0 || D.dr <= 0 || D.E <= 0 || D.topk <= 0 || D.f <= 0)
+    return fail(MK_ERR_INVALID_ARG, "non-positive dimension");
+  if (D.af < 0 || D.af > 1 || D.ef < 0 || D.ef > 2 || D.kf < 0 || D.kf > 1)
+    return fail(MK_ERR_INVALID_ARG, "unknown format");
+  if (c->has_router_bias != 0 && c->has_router_bias != 1) return fail(MK_ERR_INVALID_ARG, "has_router_bias must be 0 or 1");
+  if (!(c->rms_eps >= 0.f) || !(c->rope_base > 0.f)) return fail(MK_ERR_INVALID_ARG, "bad eps or rope base");
+  const bool f32 = D.af == MK_FMT_F32 && D.ef == MK_FMT_F32 && D.kf == MK_FMT_F32;
+  const bool bf = D.af == MK_FMT_BF16 && D.kf == MK_FMT_BF16 && (D.ef == MK_FMT_BF16 || D.ef == MK_FMT_FP8_B128);
+  if (!f32 && !bf)
+    return fail(MK_ERR_UNSUPPORTED_SHAPE, "formats must be all F32, or BF16 attention/KV with BF16 or FP8_B128 experts");
+  if (D.d % 128 || D.f % 128) return fail(MK_ERR_UNSUPPORTED_SHAPE, "d_model and d_ff must be multiples of 128");
+  if (D.dh % 32 || D.dc % 32 || D.dr % 32) return fail(MK_ERR_UNSUPPORTED_SHAPE, "d_head, d_latent, d_rope must be multiples of 32");
+  if (D.E % 16) return fail(MK_ERR_UNSUPPORTED_SHAPE, "n_experts must be a multiple of 16");
+  if (D.E > 4096) return fail(MK_ERR_UNSUPPORTED_SHAPE, "n_experts must be <= 4096");
+  if (D.topk > kMaxTopK || D.topk > D.E) return fail(MK_ERR_UNSUPPORTED_SHAPE, "top_k must be <= 16 and <= n_experts");
+  if (D.nshared < 0 || D.nshared > 1) return fail(MK_ERR_UNSUPPORTED_SHAPE, "n_shared must be 0 or 1");
+  if (f32 && (D.kvw > 160 || D.dc > 128)) return fail(MK_ERR_UNSUPPORTED_SHAPE, "fp32 layers: d_latent <= 128, d_latent + d_rope <= 160");
+  if (bf && (D.kvw > 576 || D.dc > 512)) return fail(MK_ERR_UNSUPPORTED_SHAPE, "bf16 layers: d_latent <= 512, d_latent + d_rope <= 576");
+  const int es = f32 ? 4 : 2;
+  const int dmax = std::max(D.d, std::max(D.nh * D.dh, D.f));
+  const long long xb = align256((size_t)kMaxT * (dmax + kXPad) * es);
+  const long long lds_router = 2 * xb + 2 * kWaves * 64 * 4 * 4;
+  const long long lds_route = xb + 32768 + (long long)kMaxT * D.E * 4 + 3 * kMaxT * kMaxTopK * 4 +
+                              (kMaxT * kMaxTopK + 8) * 4 + (long long)D.E * 4 + 16;
+  const long long lds_att = std::max((long long)kWaves * 16 * (D.dc + 8) * es + 16LL * (D.kvw + 8) * es,
+                                     4LL * 16 * D.dc * 4 + 4 * 16 * 2 * 4);
+  const long long lim = kLdsBytes - 1024;
+  if (lds_router > lim || lds_route > lim || lds_att > lim)
+    return fail(MK_ERR_UNSUPPORTED_SHAPE, "shape exceeds the LDS plan (router %lld, route %lld, attention %lld > %lld bytes)",
+                lds_router, lds_route, lds_att, lim);
+  if (!layer_kernel_for(D.af, D.ef, D.kf, D.kvw, D.dc)) return fail(MK_ERR_UNSUPPORTED_SHAPE, "no kernel for this shape");
+  return MK_OK;
+}
+
+// packed sizes
+long long tiles_bytes(int R, int K, int fmt) { return (long long)((R + 15) / 16) * ((K + tile_k(fmt) - 1) / tile_k(fmt)) * 1024; }
+long long exp_w13(const Dims& D) { return 2 * tiles_bytes(D.f, D.d, D.ef); }
+long long exp_w2(const Dims& D) { return tiles_bytes(D.d, D.f, D.ef); }
+long long exp_scales(const Dims& D) {
+  if (D.ef != MK_FMT_FP8_B128) return 0;
+  const long long a = (long long)((D.f + 127) / 128) * ((D.d + 127) / 128);
+  return align256((size_t)(3 * a * 4));
+}
+
+int packed_bytes(const mk_layer_config* c, int tensor, size_t* out) {
+  const Dims D = dims_of(c);
+  long long b = 0;
+  switch (tensor) {
+    case MK_T_WQ: b = tiles_bytes(D.nq, D.d, D.af); break;
+    case MK_T_WDKV: b = tiles_bytes(D.kvw, D.d, D.af); break;
+    case MK_T_WUK: b = (long long)D.nh * tiles_bytes(D.dc, D.dh, D.af); break;
+    case MK_T_WUV: b = (long long)D.nh * tiles_bytes(D.dh, D.dc, D.af); break;
+    case MK_T_WO: b = tiles_bytes(D.d, D.nh * D.dh, D.af); break;
+    case MK_T_WR: b = tiles_bytes(D.E, D.d, D.af); break;
+    case MK_T_EXPERT: b = exp_w13(D) + exp_w2(D) + exp_scales(D); break;
+    default: return fail(MK_ERR_INVALID_ARG, "unknown tensor id %d", tensor);
+  }
+  *out = (size_t)b;
+  return MK_OK;
+}
+
+// choose the k-split S (a divisor of KT) that minimises the largest per-workgroup tile count
+int choose_split(int RT, int KT, int nwg) {
+  int best = 1;
+  long long best_cost = -1;
+  for (int S = 1; S <= KT && S <= 64; ++S) {
+    if (KT % S) continue;
+    const long long U = (long long)RT * S;
+    const long long cost = ((U + nwg - 1) / nwg) * (KT / S);
+    if (best_cost < 0 || cost < best_cost) { best = S; best_cost = cost; }
+  }
+  return best;
+}
+
+struct DevInfo {
+  int cus = 0, wgs_per_cu = 0, nwg = 0;
+  bool gfx950 = false;
+  char name[64] = {0};
+  long long mem = 0;
+};
+
+int device_info(int dev, DevInfo* di, LayerKernelFn fn) {
+  hipDeviceProp_t prop;
+  HIP_OK(hipGetDeviceProperties(&prop, dev));
+  di->cus = prop.multiProcessorCount;
+  di->mem = (long long)prop.totalGlobalMem;
+  std::strncpy(di->name, prop.gcnArchName, sizeof(di->name) - 1);
+  di->gfx950 = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (!di->gfx950) return fail(MK_ERR_UNSUPPORTED_DEVICE, "device %d is %s, not gfx950", dev, prop.gcnArchName);
+  if (fn) {
+    int cur = 0;
+    HIP_OK(hipGetDevice(&cur));
+    HIP_OK(hipSetDevice(dev));
+    HIP_OK(hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes));
+    int n = 0;
+    HIP_OK(hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, kThreads, kLdsBytes));
+    HIP_OK(hipSetDevice(cur));
+    di->wgs_per_cu = n;
+    if (n < 1) return fail(MK_ERR_NOT_CORESIDENT, "layer kernel cannot be resident (occupancy %d)", n);
+    di->nwg = di->cus;   // one workgroup per compute unit
+  }
+  return MK_OK;
+}
+
+struct WsLayout {
+  size_t qkv_part, qrope, qabs, att_part, att_ml, z, o, hp, logit_part, route_sel, route_gate, logits, hbuf, ybuf, total;
+};
+struct StLayout {
+  size_t bar, att_cnt, experts, trace, total;
+};
+
+WsLayout ws_layout(const Dims& D, const Schedule& s) {
+  WsLayout w;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
+  const int T = kMaxT;
+  const int nqt = (T * D.nh + 15) / 16;
+  const int units = std::max(s.nwg, nqt);
+  const int slots = std::min(D.E, T * D.topk) + D.nshared;
+  w.qkv_part = take((size_t)s.s_q * T * (D.nq + D.kvw) * 4);
+  w.qrope = take((size_t)T * D.nh * D.dr * 4);
+  w.qabs = take((size_t)T * D.nh * D.dc * 4);
+  w.att_part = take((size_t)units * 16 * D.dc * 4);
+  w.att_ml = take((size_t)units * 16 * 2 * 4);
+  w.z = take((size_t)T * D.nh * D.dc * 4);
+  w.o = take((size_t)T * D.nh * D.dh * 4);
+  w.hp = take((size_t)T * D.d * 4);
+  w.logit_part = take((size_t)s.s_r * T * D.E * 4);
+  w.route_sel = take((size_t)T * kMaxTopK * 4);
+  w.route_gate = take((size_t)T * kMaxTopK * 4);
+  w.logits = take((size_t)T * D.E * 4);
+  w.hbuf = take((size_t)slots * T * D.f * 4);
+  w.ybuf = take((size_t)slots * T * D.d * 4);
+  w.total = off;
+  return w;
+}
+
+StLayout st_layout(const Dims& D, const Schedule& s) {
+  StLayout l;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
+  l.bar = take(sizeof(BarrierState));
+  l.att_cnt = take(64 * 4);
+  l.experts = take((size_t)(D.E + D.nshared) * 8);
+  l.trace = take((size_t)s.nwg * (2 + 2 * kBarriers) * 8);
+  l.total = off;
+  return l;
+}
+
+Schedule make_schedule(const Dims& D, int nwg) {
+  Schedule s;
+  s.nwg = nwg;
+  const int KTa = D.d / tile_k(D.af);
+  s.s_q = choose_split(D.nq / 16 + (D.kvw + 15) / 16, KTa, nwg);
+  s.s_r = choose_split(D.E / 16, KTa, nwg);
+  return s;
+}
+
+}  // namespace
+
+struct mk_layer {
+  mk_layer_config cfg;
+  Dims D;
+  int dev;
+  DevInfo di;
+  Schedule sch;
+  WsLayout wl;
+  StLayout sl;
+  char* state;
+  char* ws;
+  LayerKernelFn fn;
+  LayerParams base;
+  int trace_on;
+  long long timeout_us;
+  long long steps, launches;
+  int last_T;
+};
+
+struct mk_model {
+  mk_layer* const* layers_host;
+  mk_layer** layers;
+  int n_layers;
+  const uint16_t* emb;
+  const void* head;
+  const float* gamma_f;
+  int V;
+  void** kv;
+  int capacity;
+  char* state;
+  float* hidden;       // [2][kMaxT][d]
+  int32_t* kv_len;
+  float* best_val;
+  int32_t* best_idx;
+  uint32_t* counter;
+  int nwg_head;
+};
+
+extern "C" {
+
+int mk_abi_version(void) { return MK_ABI_VERSION; }
+const char* mk_last_error(void) { return g_err.c_str(); }
+
+int mk_query_device(int hip_device, mk_device_info* out) {
+  if (!out) return fail(MK_ERR_INVALID_ARG, "null output");
+  std::memset(out, 0, sizeof *out);
+  int n = 0;
+  HIP_OK(hipGetDeviceCount(&n));
+  if (hip_device < 0 || hip_device >= n) return fail(MK_ERR_INVALID_ARG, "no HIP device %d", hip_device);
+  DevInfo di;
+  LayerKernelFn fn = layer_kernel_for(MK_FMT_BF16, MK_FMT_FP8_B128, MK_FMT_BF16, 576, 512);
+  hipDeviceProp_t prop;
+  HIP_OK(hipGetDeviceProperties(&prop, hip_device));
+  out->hip_device = hip_device;
+  out->n_cus = prop.multiProcessorCount;
+  out->hbm_bytes = (int64_t)prop.totalGlobalMem;
+  std::strncpy(out->arch_name, prop.gcnArchName, sizeof(out->arch_name) - 1);
+  int rc = device_info(hip_device, &di, fn);
+  out->is_gfx950 = di.gfx950 ? 1 : 0;
+  if (rc != MK_OK) return rc;
+  out->wgs_per_cu = di.wgs_per_cu;
+  out->grid_wgs = di.nwg;
+  out->threads_per_wg = kThreads;
+  out->lds_bytes_per_wg = kLdsBytes;
+  return MK_OK;
+}
+
+int mk_check_config(const mk_layer_config* cfg) { return check_cfg(cfg); }
+
+int mk_packed_bytes(const mk_layer_config* cfg, int tensor, size_t* bytes) {
+  int rc = check_cfg(cfg);
+  if (rc) return rc;
+  if (!bytes) return fail(MK_ERR_INVALID_ARG, "null output");
+  return packed_bytes(cfg, tensor, bytes);
+}
+
+int mk_kv_bytes(const mk_layer_config* cfg, int32_t capacity, size_t* bytes) {
+  int rc = check_cfg(cfg);
+  if (rc) return rc;
+  if (!bytes || capacity < 0) return fail(MK_ERR_INVALID_ARG, "bad arguments");
+  *bytes = (size_t)capacity * (cfg->d_latent + cfg->d_rope) * (cfg->kv_format == MK_FMT_F32 ? 4 : 2);
+  return MK_OK;
+}
+
+static int sizes_for(const mk_layer_config* cfg, int dev, WsLayout* wl, StLayout* sl) {
+  int rc = check_cfg(cfg);
+  if (rc) return rc;
+  const Dims D = dims_of(cfg);
+  DevInfo di;
+  rc = device_info(dev, &di, layer_kernel_for(D.af, D.ef, D.kf, D.kvw, D.dc));
+  if (rc) return rc;
+  const Schedule s = make_schedule(D, di.nwg);
+  if (wl) *wl = ws_layout(D, s);
+  if (sl) *sl = st_layout(D, s);
+  return MK_OK;
+}
+
+int mk_layer_state_bytes(const mk_layer_config* cfg, int hip_device, size_t* bytes) {
+  if (!bytes) return fail(MK_ERR_INVALID_ARG, "null output");
+  StLayout sl;
+  int rc = sizes_for(cfg, hip_device, nullptr, &sl);
+  if (rc) return rc;
+  *bytes = sl.total;
+  return MK_OK;
+}
+
+int mk_layer_workspace_bytes(const mk_layer_config* cfg, int hip_device, size_t* bytes) {
+  if (!bytes) return fail(MK_ERR_INVALID_ARG, "null output");
+  WsLayout wl;
+  int rc = sizes_for(cfg, hip_device, &wl, nullptr);
+  if (rc) return rc;
+  *bytes = wl.total;
+  return MK_OK;
+}
+
+int mk_pack_tensor(const mk_layer_config* cfg, int tensor, const void* src, void* dst, void* stream) {
+  int rc = check_cfg(cfg);
+  if (rc) return rc;
+  if (!src || !dst) return fail(MK_ERR_INVALID_ARG, "null tensor");
+  const Dims D = dims_of(cfg);
+  hipStream_t s = (hipStream_t)stream;
+  const int f = D.af;
+  switch (tensor) {
+    case MK_T_WQ: rc = launch_pack(src, f, 1, D.nq, D.d, 0, D.d, 1, dst, 1024, 0, s); break;
+    case MK_T_WDKV: rc = launch_pack(src, f, 1, D.kvw, D.d, 0, D.d, 1, dst, 1024, 0, s); break;
+    // per head, rows m (d_latent) and columns e (d_head): element = W_UK[h][e][m]
+    case MK_T_WUK: rc = launch_pack(src, f, D.nh, D.dc, D.dh, (long long)D.dh * D.dc, 1, D.dc, dst, 1024, 0, s); break;
+    case MK_T_WUV: rc = launch_pack(src, f, D.nh, D.dh, D.dc, (long long)D.dh * D.dc, D.dc, 1, dst, 1024, 0, s); break;
+    case MK_T_WO: rc = launch_pack(src, f, 1, D.d, D.nh * D.dh, 0, D.nh * D.dh, 1, dst, 1024, 0, s); break;
+    case MK_T_WR: rc = launch_pack(src, f, 1, D.E, D.d, 0, D.d, 1, dst, 1024, 0, s); break;
+    default: return fail(MK_ERR_INVALID_ARG, "tensor %d is not packed with mk_pack_tensor", tensor);
+  }
+  if (rc) return fail(MK_ERR_HIP, "pack launch failed: %s", hipGetErrorString((hipError_t)rc));
+  return MK_OK;
+}
+
+int mk_pack_expert(const mk_layer_config* cfg, const void* w1, const void* w3, const void* w2, const float* s1,
+                   const float* s3, const float* s2, void* dst, void* stream) {
+  int rc = check_cfg(cfg);
+  if (rc) return rc;
+  const Dims D = dims_of(cfg);
+  if (!w1 || !w3 || !w2 || !dst) return fail(MK_ERR_INVALID_ARG, "null tensor");
+  const bool fp8 = D.ef == MK_FMT_FP8_B128;
+  if (fp8 && (!s1 || !s3 || !s2)) return fail(MK_ERR_INVALID_ARG, "fp8 experts need three scale arrays");
+  hipStream_t s = (hipStream_t)stream;
+  const long long w13 = exp_w13(D), w2b = exp_w2(D);
+  rc = launch_pack(w1, D.ef, 1, D.f, D.d, 0, D.d, 1, dst, 2048, 0, s);
+  if (!rc) rc = launch_pack(w3, D.ef, 1, D.f, D.d, 0, D.d, 1, dst, 2048, 1024, s);
+  if (!rc) rc = launch_pack(w2, D.ef, 1, D.d, D.f, 0, D.f, 1, dst, 1024, w13, s);
+  if (rc) return fail(MK_ERR_HIP, "pack launch failed: %s", hipGetErrorString((hipError_t)rc));
+  if (fp8) {
+    const size_t a = (size_t)((D.f + 127) / 128) * ((D.d + 127) / 128) * 4;
+    char* sc = (char*)dst + w13 + w2b;
+    HIP_OK(hipMemcpyAsync(sc, s1, a, hipMemcpyDeviceToDevice, s));
+    HIP_OK(hipMemcpyAsync(sc + a, s3, a, hipMemcpyDeviceToDevice, s));
+    HIP_OK(hipMemcpyAsync(sc + 2 * a, s2, a, hipMemcpyDeviceToDevice, s));
+  }
+  return MK_OK;
+}
+
+int mk_layer_init(const mk_layer_config* cfg, const mk_layer_weights* w, void* state_dev, void* workspace_dev,
+                  int hip_device, mk_layer** out) {
+  if (!out) return fail(MK_ERR_INVALID_ARG, "null output");
+  *out = nullptr;
+  int rc = check_cfg(cfg);
+  if (rc) return rc;
+  if (!w || !state_dev || !workspace_dev) return fail(MK_ERR_INVALID_ARG, "null weights, state or workspace");
+  if (!w->gamma1 || !w->gamma2 || !w->wq || !w->wdkv || !w->wuk || !w->wuv || !w->wo || !w->wr || !w->experts)
+    return fail(MK_ERR_INVALID_ARG, "null weight tensor");
+  if ((cfg->has_router_bias != 0) != (w->router_bias != nullptr))
+    return fail(MK_ERR_INVALID_ARG, "router_bias must be given iff has_router_bias");
+  const Dims D = dims_of(cfg);
+  for (int e = 0; e < D.E + D.nshared; ++e)
+    if (!w->experts[e]) return fail(MK_ERR_INVALID_ARG, "expert block %d is null", e);
+  LayerKernelFn fn = layer_kernel_for(D.af, D.ef, D.kf, D.kvw, D.dc);
+  DevInfo di;
+  rc = device_info(hip_device, &di, fn);
+  if (rc) return rc;
+  mk_layer* L = new (std::nothrow) mk_layer();
+  if (!L) return fail(MK_ERR_INVALID_ARG, "out of host memory");
+  L->cfg = *cfg;
+  L->D = D;
+  L->dev = hip_device;
+  L->di = di;
+  L->sch = make_schedule(D, di.nwg);
+  L->wl = ws_layout(D, L->sch);
+  L->sl = st_layout(D, L->sch);
+  L->state = (char*)state_dev;
+  L->ws = (char*)workspace_dev;
+  L->fn = fn;
+  L->trace_on = 0;
+  L->timeout_us = 2000000;
+  L->steps = L->launches = 0;
+  L->last_T = 0;
+  int cur = 0;
+  hipGetDevice(&cur);
+  hipSetDevice(hip_device);
+  hipError_t e1 = hipMemset(L->state, 0, L->sl.total);
+  hipError_t e2 = hipMemcpy(L->state + L->sl.experts, w->experts, (size_t)(D.E + D.nshared) * 8, hipMemcpyHostToDevice);
+  hipError_t e3 = hipDeviceSynchronize();
+  hipSetDevice(cur);
+  if (e1 != hipSuccess || e2 != hipSuccess || e3 != hipSuccess) {
+    delete L;
+    return fail(MK_ERR_HIP, "state initialisation failed: %s", hipGetErrorString(e1 != hipSuccess ? e1 : (e2 != hipSuccess ? e2 : e3)));
+  }
+  LayerParams& p = L->base;
+  std::memset(&p, 0, sizeof p);
+  p.d = D.d; p.nh = D.nh; p.dh = D.dh; p.dc = D.dc; p.dr = D.dr; p.qw = D.qw; p.kvw = D.kvw; p.nq = D.nq;
+  p.E = D.E; p.topk = D.topk; p.nshared = D.nshared; p.f = D.f;
+  p.eps = cfg->rms_eps;
+  p.scale = (float)(1.0 / std::sqrt((double)(D.dh + D.dr)));
+  p.rope_base = (double)cfg->rope_base;
+  p.g1 = w->gamma1; p.g2 = w->gamma2;
+  p.wq = (const uint8_t*)w->wq; p.wdkv = (const uint8_t*)w->wdkv; p.wuk = (const uint8_t*)w->wuk;
+  p.wuv = (const uint8_t*)w->wuv; p.wo = (const uint8_t*)w->wo; p.wr = (const uint8_t*)w->wr;
+  p.rbias = w->router_bias;
+  p.experts = (const uint8_t* const*)(L->state + L->sl.experts);
+  p.exp_w13_bytes = exp_w13(D);
+  p.exp_w2_bytes = exp_w2(D);
+  char* ws = L->ws;
+  p.qkv_part = (float*)(ws + L->wl.qkv_part);
+  p.qrope = (float*)(ws + L->wl.qrope);
+  p.qabs = (float*)(ws + L->wl.qabs);
+  p.att_part = (float*)(ws + L->wl.att_part);
+  p.att_ml = (float*)(ws + L->wl.att_ml);
+  p.z = (float*)(ws + L->wl.z);
+  p.o = (float*)(ws + L->wl.o);
+  p.hp = (float*)(ws + L->wl.hp);
+  p.logit_part = (float*)(ws + L->wl.logit_part);
+  p.route_sel = (int32_t*)(ws + L->wl.route_sel);
+  p.route_gate = (float*)(ws + L->wl.route_gate);
+  p.logits = (float*)(ws + L->wl.logits);
+  p.hbuf = (float*)(ws + L->wl.hbuf);
+  p.ybuf = (float*)(ws + L->wl.ybuf);
+  p.bar = (BarrierState*)(L->state + L->sl.bar);
+  p.att_cnt = (uint32_t*)(L->state + L->sl.att_cnt);
+  p.trace = nullptr;
+  p.sch = L->sch;
+  *out = L;
+  return MK_OK;
+}
+
+static int launch_layer(mk_layer* L, const float* hin, int T, void* kv_rows, int capacity, int length,
+                        const int32_t* len_dev, float* hout, hipStream_t s) {
+  LayerParams p = L->base;
+  p.T = T;
+  p.L = length;
+  p.L_dev = len_dev;
+  p.H = hin;
+  p.out = hout;
+  p.kv = kv_rows;
+  p.kv_capacity = capacity;
+  p.trace = L->trace_on ? (long long*)(L->state + L->sl.trace) : nullptr;
+  p.timeout_ticks = L->timeout_us * 100;
+  void* args[] = {&p};
+  hipError_t e = hipLaunchKernel((const void*)L->fn, dim3(L->sch.nwg), dim3(kThreads), args, kLdsBytes, s);
+  if (e != hipSuccess) return fail(MK_ERR_HIP, "layer launch: %s", hipGetErrorString(e));
+  L->steps++;
+  L->launches++;
+  L->last_T = T;
+  return MK_OK;
+}
+
+int mk_decode_step(mk_layer* L, const float* hidden_in, int T, const mk_kv_cache* kv, float* hidden_out, void* stream) {
+  if (!L || !hidden_in || !kv || !kv->rows || !hidden_out) return fail(MK_ERR_INVALID_ARG, "null argument");
+  if (T < 1 || T > kMaxT) return fail(MK_ERR_INVALID_ARG, "T=%d outside [1, %d]", T, kMaxT);
+  if (kv->length < 0 || kv->capacity < 0 || (long long)kv->length + T > kv->capacity)
+    return fail(MK_ERR_INVALID_ARG, "KV length %d + T %d exceeds capacity %d", kv->length, T, kv->capacity);
+  if (hidden_in == hidden_out) return fail(MK_ERR_INVALID_ARG, "hidden_out may not alias hidden_in");
+  return launch_layer(L, hidden_in, T, kv->rows, kv->capacity, kv->length, nullptr, hidden_out, (hipStream_t)stream);
+}
+
+int mk_debug_tap(mk_layer* L, int tap, void* host_dst, size_t bytes, void* stream) {
+  if (!L || !host_dst) return fail(MK_ERR_INVALID_ARG, "null argument");
+  const Dims& D = L->D;
+  const int T = L->last_T;
+  if (T <= 0) return fail(MK_ERR_INVALID_ARG, "no step has run on this layer");
+  const char* src = nullptr;
+  size_t need = 0;
+  const LayerParams& p = L->base;
+  switch (tap) {
+    case 1: src = (const char*)p.qabs; need = (size_t)T * D.nh * D.dc * 4; break;
+    case 2: src = (const char*)p.z; need = (size_t)T * D.nh * D.dc * 4; break;
+    case 3: src = (const char*)p.o; need = (size_t)T * D.nh * D.dh * 4; break;
+    case 4: src = (const char*)p.hp; need = (size_t)T * D.d * 4; break;
+    case 5: src = (const char*)p.logits; need = (size_t)T * D.E * 4; break;
+    case 6: src = (const char*)p.route_sel; need = (size_t)T * D.topk * 4; break;
+    case 7: src = (const char*)p.route_gate; need = (size_t)T * D.topk * 4; break;
+    case 0: {
+      // Q with rotated q^R: rebuild [T][nh][qw] from the split-K partials and the rotated part
+      if (bytes < (size_t)T * D.nh * D.qw * 4) return fail(MK_ERR_INVALID_ARG, "tap buffer too small");
+      const int S = L->sch.s_q, nrow = D.nq + D.kvw;
+      std::string tmp((size_t)S * T * nrow * 4, '\0');
+      std::string rq((size_t)T * D.nh * D.dr * 4, '\0');
+      HIP_OK(hipStreamSynchronize((hipStream_t)stream));
+      HIP_OK(hipMemcpy(&tmp[0], p.qkv_part, tmp.size(), hipMemcpyDeviceToHost));
+      HIP_OK(hipMemcpy(&rq[0], p.qrope, rq.size(), hipMemcpyDeviceToHost));
+      const float* pt = (const float*)tmp.data();
+      const float* pr = (const float*)rq.data();
+      float* o = (float*)host_dst;
+      for (int t = 0; t < T; ++t)
+        for (int h = 0; h < D.nh; ++h)
+          for (int e = 0; e < D.qw; ++e) {
+            float v;
+            if (e < D.dh) {
+              v = 0.f;
+              for (int s = 0; s < S; ++s) v += pt[((size_t)s * T + t) * nrow + h * D.qw + e];
+            } else {
+              v = pr[((size_t)t * D.nh + h) * D.dr + (e - D.dh)];
+            }
+            o[((size_t)t * D.nh + h) * D.qw + e] = v;
+          }
+      return MK_OK;
+    }
+    default: return fail(MK_ERR_INVALID_ARG, "unknown tap %d", tap);
+  }
+  if (bytes < need) return fail(MK_ERR_INVALID_ARG, "tap buffer too small (%zu < %zu)", bytes, need);
+  HIP_OK(hipStreamSynchronize((hipStream_t)stream));
+  HIP_OK(hipMemcpy(host_dst, src, need, hipMemcpyDeviceToHost));
+  return MK_OK;
+}
+
+int mk_get_stats(const mk_layer* L, mk_stats* out) {
+  if (!L || !out) return fail(MK_ERR_INVALID_ARG, "null argument");
+  out->steps = L->steps;
+  out->launches = L->launches;
+  out->grid_wgs = L->sch.nwg;
+  out->threads_per_wg = kThreads;
+  out->barriers_per_step = kBarriers;
+  out->trace_enabled = L->trace_on;
+  return MK_OK;
+}
+
+int mk_set_trace(mk_layer* L, int enabled) {
+  if (!L) return fail(MK_ERR_INVALID_ARG, "null layer");
+  L->trace_on = enabled ? 1 : 0;
+  return MK_OK;
+}
+
+int mk_read_trace(mk_layer* L, int64_t* host_dst, size_t bytes, void* stream) {
+  if (!L || !host_dst) return fail(MK_ERR_INVALID_ARG, "null argument");
+  const size_t need = (size_t)L->sch.nwg * (2 + 2 * kBarriers) * 8;
+  if (bytes < need) return fail(MK_ERR_INVALID_ARG, "trace buffer too small (%zu < %zu)", bytes, need);
+  HIP_OK(hipStreamSynchronize((hipStream_t)stream));
+  HIP_OK(hipMemcpy(host_dst, L->state + L->sl.trace, need, hipMemcpyDeviceToHost));
+  return MK_OK;
+}
+
+int mk_set_barrier_timeout_us(mk_layer* L, int64_t us) {
+  if (!L || us <= 0) return fail(MK_ERR_INVALID_ARG, "bad argument");
+  L->timeout_us = us;
+  return MK_OK;
+}
+
+int mk_sync_status(mk_layer* L) {
+  if (!L) return fail(MK_ERR_INVALID_ARG, "null layer");
+  uint32_t fault = 0;
+  HIP_OK(hipMemcpy(&fault, L->state + L->sl.bar + offsetof(BarrierState, fault), 4, hipMemcpyDeviceToHost));
+  if (fault == 1) return fail(MK_ERR_TIMEOUT, "a grid barrier wait exceeded its bound");
+  if (fault == 2) return fail(MK_ERR_INVALID_ARG, "device KV length + T exceeded the cache capacity");
+  if (fault != 0) return fail(MK_ERR_DEVICE_FAULT, "device fault word %u", fault);
+  return MK_OK;
+}
+
+int mk_layer_reset(mk_layer* L) {
+  if (!L) return fail(MK_ERR_INVALID_ARG, "null layer");
+  int cur = 0;
+  hipGetDevice(&cur);
+  hipSetDevice(L->dev);
+  hipError_t e1 = hipMemset(L->state + L->sl.bar, 0, sizeof(BarrierState));
+  hipError_t e2 = hipMemset(L->state + L->sl.att_cnt, 0, 64 * 4);
+  hipError_t e3 = hipDeviceSynchronize();
+  hipSetDevice(cur);
+  if (e1 != hipSuccess || e2 != hipSuccess || e3 != hipSuccess) return fail(MK_ERR_HIP, "reset failed");
+  return MK_OK;
+}
+
+void mk_layer_destroy(mk_layer* L) { delete L; }
+
+// ------------------------------------------------------------------ stack
+int mk_head_packed_bytes(int32_t vocab, int32_t d_model, size_t* bytes) {
+  if (!bytes || vocab <= 0 || d_model <= 0 || vocab % 16 || d_model % 128)
+    return fail(MK_ERR_INVALID_ARG, "vocab must be a positive multiple of 16 and d_model of 128");
+  *bytes = (size_t)tiles_bytes(vocab, d_model, MK_FMT_BF16);
+  return MK_OK;
+}
+
+int mk_pack_head(int32_t vocab, int32_t d_model, const uint16_t* src_bf16, void* dst, void* stream) {
+  size_t b;
+  int rc = mk_head_packed_bytes(vocab, d_model, &b);
+  if (rc) return rc;
+  if (!src_bf16 || !dst) return fail(MK_ERR_INVALID_ARG, "null tensor");
+  rc = launch_pack(src_bf16, MK_FMT_BF16, 1, vocab, d_model, 0, d_model, 1, dst, 1024, 0, (hipStream_t)stream);
+  if (rc) return fail(MK_ERR_HIP, "pack launch failed");
+  return MK_OK;
+}
+
+struct ModelStLayout {
+  size_t len, counter, best_val, best_idx, total;
+};
+static ModelStLayout model_layout(int nwg) {
+  ModelStLayout l;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
+  l.len = take(4);
+  l.counter = take(4);
+  l.best_val = take((size_t)nwg * 8 * 4);
+  l.best_idx = take((size_t)nwg * 8 * 4);
+  l.total = off;
+  return l;
+}
+
+static int head_grid(int dev, int* nwg) {
+  hipDeviceProp_t prop;
+  HIP_OK(hipGetDeviceProperties(&prop, dev));
+  int cur = 0;
+  HIP_OK(hipGetDevice(&cur));
+  HIP_OK(hipSetDevice(dev));
+  int occ = 0;
+  int rc = head_kernel_occupancy(&occ);
+  HIP_OK(hipSetDevice(cur));
+  if (rc) return fail(MK_ERR_HIP, "head kernel occupancy query failed");
+  if (occ < 1) return fail(MK_ERR_NOT_CORESIDENT, "head kernel cannot be resident");
+  *nwg = prop.multiProcessorCount;
+  return MK_OK;
+}
+
+int mk_model_state_bytes(int32_t n_layers, int32_t vocab, int hip_device, size_t* bytes) {
+  if (!bytes || n_layers <= 0 || vocab <= 0) return fail(MK_ERR_INVALID_ARG, "bad arguments");
+  int nwg = 0;
+  int rc = head_grid(hip_device, &nwg);
+  if (rc) return rc;
+  *bytes = model_layout(nwg).total;
+  return MK_OK;
+}
+
+int mk_model_init(mk_layer* const* layers, int32_t n_layers, const uint16_t* embedding, const void* head_packed,
+                  const float* gamma_final, int32_t vocab, void* const* kv_rows, int32_t capacity, void* state_dev,
+                  void* hidden_dev, mk_model** out) {
+  if (!out) return fail(MK_ERR_INVALID_ARG, "null output");
+  *out = nullptr;
+  if (!layers || n_layers <= 0 || !embedding || !head_packed || !gamma_final || !kv_rows || !state_dev || !hidden_dev)
+    return fail(MK_ERR_INVALID_ARG, "null argument");
+  for (int l = 0; l < n_layers; ++l) {
+    if (!layers[l] || !kv_rows[l]) return fail(MK_ERR_INVALID_ARG, "layer %d or its KV rows are null", l);
+    if (std::memcmp(&layers[l]->cfg, &layers[0]->cfg, sizeof(mk_layer_config)) != 0)
+      return fail(MK_ERR_INVALID_ARG, "layer %d has a different config", l);
+  }
+  size_t hb;
+  int rc = mk_head_packed_bytes(vocab, layers[0]->D.d, &hb);
+  if (rc) return rc;
+  int nwg = 0;
+  rc = head_grid(layers[0]->dev, &nwg);
+  if (rc) return rc;
+  mk_model* m = new (std::nothrow) mk_model();
+  if (!m) return fail(MK_ERR_INVALID_ARG, "out of host memory");
+  m->layers = new mk_layer*[n_layers];
+  m->kv = new void*[n_layers];
+  for (int l = 0; l < n_layers; ++l) {
+    m->layers[l] = layers[l];
+    m->kv[l] = kv_rows[l];
+  }
+  m->n_layers = n_layers;
+  m->emb = embedding;
+  m->head = head_packed;
+  m->gamma_f = gamma_final;
+  m->V = vocab;
+  m->capacity = capacity;
+  m->state = (char*)state_dev;
+  m->hidden = (float*)hidden_dev;
+  const ModelStLayout ml = model_layout(nwg);
+  m->kv_len = (int32_t*)(m->state + ml.len);
+  m->counter = (uint32_t*)(m->state + ml.counter);
+  m->best_val = (float*)(m->state + ml.best_val);
+  m->best_idx = (int32_t*)(m->state + ml.best_idx);
+  m->nwg_head = nwg;
+  hipError_t e = hipMemset(m->state, 0, ml.total);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) {
+    delete[] m->layers;
+    delete[] m->kv;
+    delete m;
+    return fail(MK_ERR_HIP, "model state initialisation: %s", hipGetErrorString(e));
+  }
+  *out = m;
+  return MK_OK;
+}
+
+int mk_model_set_length(mk_model* m, int32_t length) {
+  if (!m || length < 0 || length > m->capacity) return fail(MK_ERR_INVALID_ARG, "bad length");
+  HIP_OK(hipMemcpy(m->kv_len, &length, 4, hipMemcpyHostToDevice));
+  return MK_OK;
+}
+
+const int32_t* mk_model_length_ptr(const mk_model* m) { return m ? m->kv_len : nullptr; }
+
+int mk_model_step(mk_model* m, int32_t* tokens_dev, int T, const int32_t* next_drafts_dev, int32_t* argmax_dev,
+                  int32_t* committed_dev, float* logits_dev, void* stream) {
+  if (!m || !tokens_dev || !argmax_dev || !committed_dev) return fail(MK_ERR_INVALID_ARG, "null argument");
+  if (T < 1 || T > kMaxT) return fail(MK_ERR_INVALID_ARG, "T=%d outside [1, %d]", T, kMaxT);
+  hipStream_t s = (hipStream_t)stream;
+  const int d = m->layers[0]->D.d;
+  float* h0 = m->hidden;
+  float* h1 = m->hidden + (size_t)kMaxT * d;
+  int rc = launch_embed(m->emb, m->V, d, tokens_dev, T, h0, s);
+  if (rc) return fail(MK_ERR_HIP, "embedding launch failed");
+  for (int l = 0; l < m->n_layers; ++l) {
+    // the KV length lives in device memory; capacity is checked by the caller's loop bound
+    rc = launch_layer(m->layers[l], (l & 1) ? h1 : h0, T, m->kv[l], m->capacity, 0, m->kv_len, (l & 1) ? h0 : h1, s);
+    if (rc) return rc;
+  }
+  float* hf = (m->n_layers & 1) ? h1 : h0;
+  rc = launch_head(m->head, m->V, d, m->gamma_f, m->layers[0]->cfg.rms_eps, hf, T, logits_dev, m->best_val,
+                   m->best_idx, m->counter, tokens_dev, next_drafts_dev, argmax_dev, committed_dev, m->kv_len,
+                   m->nwg_head, s);
+  if (rc) return fail(MK_ERR_HIP, "head launch failed");
+  return MK_OK;
+}
+
+void mk_model_destroy(mk_model* m) {
+  if (!m) return;
+  delete[] m->layers;
+  delete[] m->kv;
+  delete m;
+}
+
+}  // extern "C"

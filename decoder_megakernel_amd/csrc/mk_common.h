@@ -1,0 +1,90 @@
+// Definitions shared by the host side (mk_api.cpp) and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/mk.h"
+
+namespace mk {
+
+constexpr int kThreads = 512;            // threads per workgroup (8 wave64s)
+constexpr int kWaves = kThreads / 64;
+constexpr int kMaxT = 8;                 // verify rows the LDS budget is sized for
+constexpr int kXPad = 8;                 // LDS row padding of activation operands (elements)
+constexpr int kBarriers = 8;             // grid barriers in one layer launch
+constexpr int kLdsBytes = 160 * 1024 - 256;
+constexpr int kMaxTopK = 16;
+
+// Packed tile geometry: one tile = 16 rows x kTileK[fmt] columns = 1 KiB,
+// lane l holds row (l % 16) and 16 consecutive bytes of columns
+// (l / 16) * (kTileK / 4) ... ; tiles of a matrix are row-tile major.
+__host__ __device__ constexpr int tile_k(int fmt) { return fmt == MK_FMT_F32 ? 16 : (fmt == MK_FMT_BF16 ? 32 : 64); }
+__host__ __device__ constexpr int elem_bytes(int fmt) { return fmt == MK_FMT_F32 ? 4 : (fmt == MK_FMT_BF16 ? 2 : 1); }
+
+// Per-layer device state (persistent across steps; zeroed at init).
+struct alignas(256) BarrierState {
+  uint32_t count;
+  uint32_t pad0[63];
+  uint32_t gen;
+  uint32_t pad1[63];
+  uint32_t fault;          // 0 ok, 1 barrier timeout, 2 KV length out of range
+  uint32_t pad2[63];
+};
+
+// Schedule chosen at init for this device and shape.
+struct Schedule {
+  int nwg;                 // persistent grid (all co-resident)
+  int s_q;                 // k-splits of the Q / latent-KV projection
+  int s_r;                 // k-splits of the router projection
+};
+
+// Kernel parameters (passed by value).
+struct LayerParams {
+  // shape
+  int d, nh, dh, dc, dr, qw, kvw, nq, E, topk, nshared, f, T;
+  int L;                   // cached positions before the step (host value) ...
+  const int32_t* L_dev;    // ... or read from device memory when non-null
+  float eps, scale;
+  double rope_base;
+  // tensors
+  const float* H;          // [T][d]
+  float* out;              // [T][d]
+  void* kv;                // [cap][kvw]
+  int kv_capacity;         // rows of `kv`
+  const float* g1;
+  const float* g2;
+  const uint8_t* wq;
+  const uint8_t* wdkv;
+  const uint8_t* wuk;
+  const uint8_t* wuv;
+  const uint8_t* wo;
+  const uint8_t* wr;
+  const float* rbias;
+  const uint8_t* const* experts;   // [E + nshared] packed expert blocks
+  // packed expert block geometry (bytes)
+  long long exp_w13_bytes;         // interleaved W1/W3 tiles
+  long long exp_w2_bytes;          // W2 tiles
+  // workspace
+  float* qkv_part;         // [s_q][T][nq + kvw]
+  float* qrope;            // [T][nh][dr]
+  float* qabs;             // [T][nh][dc]
+  float* att_part;         // [units][16][dc]
+  float* att_ml;           // [units][16][2]
+  float* z;                // [T][nh][dc]
+  float* o;                // [T][nh*dh]
+  float* hp;               // [T][d]
+  float* logit_part;       // [s_r][T][E]
+  int32_t* route_sel;      // [T][topk]
+  float* route_gate;       // [T][topk]
+  float* logits;           // [T][E] (written by workgroup 0)
+  float* hbuf;             // [slots][T][f]
+  float* ybuf;             // [slots][T][d]
+  // state
+  BarrierState* bar;
+  uint32_t* att_cnt;       // [max query tiles]
+  long long* trace;        // [nwg][2 + 2*kBarriers] or null
+  long long timeout_ticks; // 100 MHz ticks
+  Schedule sch;
+};
+
+}  // namespace mk

@@ -1,0 +1,21 @@
+// Host-side entry points into the kernel translation units.
+#pragma once
+#include "mk_common.h"
+
+namespace mk {
+
+typedef void (*LayerKernelFn)(LayerParams);
+LayerKernelFn layer_kernel_for(int af, int ef, int kf, int kvw, int dc);
+
+int launch_pack(const void* src, int fmt, int nb, int R, int K, long long sb, long long sr, long long sk,
+                void* dst, long long dst_stride, long long dst_off, hipStream_t stream);
+
+struct HeadParams;
+int launch_embed(const uint16_t* emb, int V, int d, const int32_t* tokens, int T, float* h, hipStream_t s);
+int launch_head(const void* head_packed, int V, int d, const float* gamma, float eps, const float* h, int T,
+                float* logits, float* best_val, int32_t* best_idx, uint32_t* counter, int32_t* tokens,
+                const int32_t* next_drafts, int32_t* argmax, int32_t* committed, int32_t* kv_len,
+                int nwg, hipStream_t s);
+int head_kernel_occupancy(int* wgs_per_cu);
+
+}  // namespace mk

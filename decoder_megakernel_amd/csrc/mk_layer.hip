@@ -1,0 +1,866 @@
+// The layer megakernel: one persistent launch computes a whole verify step of a
+// latent-attention mixture-of-experts decoder layer (the step listed, kernel by
+// kernel, in "Why one GB300 doesn't beat 4x RTX PRO 6000 at single-stream
+// decode", section "Where the 11.2 ms goes"; the attention algebra is the
+// multi-head latent attention of the DeepSeek-V2 paper, section 2.1).
+//
+// Phases, separated by grid barriers (all workgroups are co-resident):
+//   P0  RMSNorm-1 (every workgroup, into LDS) ; [W_Q; W_DKV] x, split-K partials
+//   P1  RoPE on q^R and the shared key, KV insert ; absorbed query q~ = W_UK^T q^C
+//   P2  latent attention, split over (query tile, KV range); the last split of a
+//       query tile to finish merges all splits (log-sum-exp) into z
+//   P3  o = W_UV z
+//   P4  H' = H + W_O o
+//   P5  RMSNorm-2 (every workgroup, into LDS) ; router logits, split-K partials
+//   P6  softmax / top-k / gates / distinct-expert work list (every workgroup,
+//       identical) ; gate+up projections of every listed expert: silu(W1 x) * W3 x
+//   P7  down projections W2 h of every listed expert
+//   P8  out = H' + sum_k gate_k y_k + y_shared
+#include "mk_device.h"
+
+namespace mk {
+
+// ------------------------------------------------------------------ LDS plan
+struct LdsPlan {
+  int xb;        // bytes of one activation operand [kMaxT][dmax + pad]
+  __device__ LdsPlan(const LayerParams& p, int esize) {
+    int dmax = p.d;
+    if (p.nh * p.dh > dmax) dmax = p.nh * p.dh;
+    if (p.f > dmax) dmax = p.f;
+    xb = kMaxT * (dmax + kXPad) * esize;
+    xb = (xb + 255) & ~255;
+  }
+};
+constexpr int kMiscOff = kLdsBytes - 1024;     // 256 floats of scratch + the barrier flag
+constexpr int kFlagOff = kLdsBytes - 16;
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+__device__ __forceinline__ void split_range(int total, int parts, int i, int& a, int& b) {
+  long long q = (long long)total * i / parts, r = (long long)total * (i + 1) / parts;
+  a = (int)q;
+  b = (int)r;
+}
+
+template <class A> __device__ inline A to_act(float v);
+template <> __device__ inline float to_act<float>(float v) { return v; }
+template <> __device__ inline __bf16 to_act<__bf16>(float v) { return (__bf16)v; }
+
+// x[t][k] = (h[t][k] * rsqrt(mean(h[t]^2) + eps)) * gamma[k] -> LDS (activation type).
+// For `lo` != null also writes the bf16 remainder x - bf16(x) (router operand).
+template <class A>
+__device__ __forceinline__ void rmsnorm_to_lds(const float* h, const float* gamma, int T, int d, float eps, A* xs,
+                               A* lo, int XS, char* smem) {
+  float* rs = reinterpret_cast<float*>(smem + kMiscOff);
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (w < T) {
+    float ss = 0.f;
+    for (int k = lane; k < d; k += 64) {
+      float v = h[(long long)w * d + k];
+      ss += v * v;
+    }
+    ss = wave_sum(ss);
+    if (lane == 0) rs[w] = 1.0f / sqrtf(ss / (float)d + eps);
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < T * d; i += kThreads) {
+    const int t = i / d, k = i - t * d;
+    const float x = (h[(long long)t * d + k] * rs[t]) * gamma[k];
+    const A xa = to_act<A>(x);
+    xs[t * XS + k] = xa;
+    if (lo) lo[t * XS + k] = to_act<A>(x - (float)xa);
+  }
+  __syncthreads();
+}
+
+template <class A>
+__device__ __forceinline__ const A* b_lane(const A* xs, int XS, int T, int TK) {
+  const int lane = threadIdx.x & 63;
+  const int j = lane & 15, g = lane >> 4;
+  const int jj = j < T ? j : T - 1;
+  return xs + jj * XS + g * (TK / 4);
+}
+
+// ------------------------------------------------------------------ P0
+template <int AF>
+__device__ __forceinline__ void phase_qkv(const LayerParams& p, char* smem) {
+  typedef typename Act<AF>::T A;
+  constexpr int TK = tile_k(AF);
+  const int T = p.T, XS = p.d + kXPad;
+  LdsPlan lp(p, sizeof(A));
+  A* xs = reinterpret_cast<A*>(smem);
+  float* red = reinterpret_cast<float*>(smem + lp.xb);
+  rmsnorm_to_lds<A>(p.H, p.g1, T, p.d, p.eps, xs, (A*)nullptr, XS, smem);
+  const int RTq = p.nq / 16, RTkv = (p.kvw + 15) / 16, KT = p.d / TK, S = p.sch.s_q, NT = KT / S;
+  const int U = (RTq + RTkv) * S;
+  int u0, u1;
+  split_range(U, gridDim.x, blockIdx.x, u0, u1);
+  const A* bl = b_lane<A>(xs, XS, T, TK);
+  const int nrow = p.nq + p.kvw;
+  struct Src {
+    const uint8_t* wq; const uint8_t* wd; int RTq, KT, S, NT; const A* bl;
+    __device__ const uint8_t* tile(int u, int t) const {
+      int rt = u / S, s = u - rt * S;
+      const uint8_t* base = rt < RTq ? wq + (long long)rt * KT * 1024 : wd + (long long)(rt - RTq) * KT * 1024;
+      return base + (long long)(s * NT + t) * 1024;
+    }
+    __device__ const A* bptr(int u, int t) const { int s = u % S; return bl + (s * NT + t) * TK; }
+    __device__ float scale(int, int) const { return 1.f; }
+    __device__ float scale2(int, int) const { return 1.f; }
+  } src{p.wq, p.wdkv, RTq, KT, S, NT, bl};
+  float* part = p.qkv_part;
+  const int nq = p.nq, kvw = p.kvw;
+  auto epi = [=](int u, int row, int col, float v, float) {
+    int rt = u / S, s = u - rt * S;
+    int idx;
+    if (rt < RTq) idx = rt * 16 + row;
+    else {
+      int r = (rt - RTq) * 16 + row;
+      if (r >= kvw) return;
+      idx = nq + r;
+    }
+    part[((long long)s * T + col) * nrow + idx] = v;
+  };
+  run_units<AF, false, false>(u0, u1, NT, T, src, epi, red);
+}
+
+// ------------------------------------------------------------------ P1
+__device__ __forceinline__ void rope_pair(float& v0, float& v1, long long pos, int pidx, int dr, double base) {
+  const double th = pow(base, -2.0 * (double)pidx / (double)dr);
+  const double a = (double)pos * th;
+  const float c = (float)cos(a), s = (float)sin(a);
+  const float x0 = v0, x1 = v1;
+  v0 = x0 * c - x1 * s;
+  v1 = x0 * s + x1 * c;
+}
+
+template <int KF>
+__device__ __forceinline__ void phase_rope_kv(const LayerParams& p, int L) {
+  const int T = p.T, S = p.sch.s_q, nrow = p.nq + p.kvw, dr2 = p.dr / 2;
+  const int per_t = p.dc + dr2 + p.nh * dr2;
+  const float* part = p.qkv_part;
+  auto psum = [&](int t, int idx) {
+    float v = 0.f;
+    for (int s = 0; s < S; ++s) v += part[((long long)s * T + t) * nrow + idx];
+    return v;
+  };
+  for (int it = blockIdx.x * kThreads + threadIdx.x; it < T * per_t; it += gridDim.x * kThreads) {
+    const int t = it / per_t, r = it - t * per_t;
+    const long long pos = (long long)L + t;
+    if (r < p.dc) {
+      float v = psum(t, p.nq + r);
+      if (KF == MK_FMT_F32) reinterpret_cast<float*>(p.kv)[pos * p.kvw + r] = v;
+      else reinterpret_cast<__bf16*>(p.kv)[pos * p.kvw + r] = (__bf16)v;
+    } else if (r < p.dc + dr2) {
+      const int pi = r - p.dc;
+      float v0 = psum(t, p.nq + p.dc + 2 * pi), v1 = psum(t, p.nq + p.dc + 2 * pi + 1);
+      rope_pair(v0, v1, pos, pi, p.dr, p.rope_base);
+      const long long o = pos * p.kvw + p.dc + 2 * pi;
+      if (KF == MK_FMT_F32) {
+        reinterpret_cast<float*>(p.kv)[o] = v0;
+        reinterpret_cast<float*>(p.kv)[o + 1] = v1;
+      } else {
+        reinterpret_cast<__bf16*>(p.kv)[o] = (__bf16)v0;
+        reinterpret_cast<__bf16*>(p.kv)[o + 1] = (__bf16)v1;
+      }
+    } else {
+      const int q = r - p.dc - dr2, h = q / dr2, pi = q - h * dr2;
+      const int base = h * p.qw + p.dh + 2 * pi;
+      float v0 = psum(t, base), v1 = psum(t, base + 1);
+      rope_pair(v0, v1, pos, pi, p.dr, p.rope_base);
+      p.qrope[((long long)t * p.nh + h) * p.dr + 2 * pi] = v0;
+      p.qrope[((long long)t * p.nh + h) * p.dr + 2 * pi + 1] = v1;
+    }
+  }
+}
+
+// B operand held in registers for wave-level units.
+template <int FMT> struct BReg { typedef bf16x8 T; };
+template <> struct BReg<MK_FMT_F32> { typedef f32x4 T; };
+
+template <int FMT>
+__device__ __forceinline__ f32x4 tile_mma_reg(const u32x4& a, const typename BReg<FMT>::T& b, f32x4 acc);
+template <>
+__device__ __forceinline__ f32x4 tile_mma_reg<MK_FMT_F32>(const u32x4& a, const f32x4& b, f32x4 acc) {
+  f32x4 av = __builtin_bit_cast(f32x4, a);
+  acc = mma_f32_k4(av[0], b[0], acc);
+  acc = mma_f32_k4(av[1], b[1], acc);
+  acc = mma_f32_k4(av[2], b[2], acc);
+  acc = mma_f32_k4(av[3], b[3], acc);
+  return acc;
+}
+template <>
+__device__ __forceinline__ f32x4 tile_mma_reg<MK_FMT_BF16>(const u32x4& a, const bf16x8& b, f32x4 acc) {
+  return mma_bf16_k32(__builtin_bit_cast(bf16x8, a), b, acc);
+}
+// 4 (f32) or 8 (bf16) consecutive floats from global memory as the B-operand type
+template <int FMT>
+__device__ __forceinline__ typename BReg<FMT>::T load_b(const float* src);
+template <>
+__device__ __forceinline__ f32x4 load_b<MK_FMT_F32>(const float* src) { return *reinterpret_cast<const f32x4*>(src); }
+template <>
+__device__ __forceinline__ bf16x8 load_b<MK_FMT_BF16>(const float* src) {
+  return to_bf16x8(*reinterpret_cast<const f32x4*>(src), *reinterpret_cast<const f32x4*>(src + 4));
+}
+
+template <int FMT>
+__device__ __forceinline__ typename BReg<FMT>::T make_b(const f32x4& a, const f32x4& b);
+template <>
+__device__ __forceinline__ f32x4 make_b<MK_FMT_F32>(const f32x4& a, const f32x4&) { return a; }
+template <>
+__device__ __forceinline__ bf16x8 make_b<MK_FMT_BF16>(const f32x4& a, const f32x4& b) { return to_bf16x8(a, b); }
+
+// q~[t][h][m] = sum_e W_UK[h][e][m] q^C[t][h][e]  (wave-level units: one head, 16 m-rows, all of K)
+template <int AF>
+__device__ __forceinline__ void phase_absorb(const LayerParams& p) {
+  constexpr int TK = tile_k(AF);
+  constexpr int EPL = TK / 4;          // elements per lane per tile
+  const int T = p.T, S = p.sch.s_q, nrow = p.nq + p.kvw;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, j = lane & 15, g = lane >> 4;
+  const int jj = j < T ? j : T - 1;
+  const int RT = p.dc / 16, KT = p.dh / TK, U = p.nh * RT;
+  for (int u = blockIdx.x * kWaves + w; u < U; u += gridDim.x * kWaves) {
+    const int h = u / RT, rt = u - h * RT;
+    const uint8_t* tiles = p.wuk + (long long)u * KT * 1024 + lane * 16;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int kt = 0; kt < KT; ++kt) {
+      const u32x4 a = ld_stream16(tiles + kt * 1024);
+      const int e0 = kt * TK + g * EPL;
+      f32x4 q0 = {0.f, 0.f, 0.f, 0.f}, q1 = {0.f, 0.f, 0.f, 0.f};
+      for (int s = 0; s < S; ++s) {
+        const float* src = p.qkv_part + ((long long)s * T + jj) * nrow + h * p.qw + e0;
+        q0 += *reinterpret_cast<const f32x4*>(src);
+        if (EPL == 8) q1 += *reinterpret_cast<const f32x4*>(src + 4);
+      }
+      acc = tile_mma_reg<AF>(a, make_b<AF>(q0, q1), acc);
+    }
+    if (j < T) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        p.qabs[((long long)j * p.nh + h) * p.dc + rt * 16 + 4 * g + e] = acc[e];
+    }
+  }
+}
+
+// ------------------------------------------------------------------ P2 attention
+// Units (query tile of 16 queries q = t*nh + h, KV range).  Per wave: chunks of
+// 16 keys; S^T = K Q^T on the matrix cores (keys x queries), online softmax per
+// query column, Z^T += C^T P^T with C staged in the wave's LDS slice.
+template <int KF>
+struct AttnTypes;
+template <> struct AttnTypes<MK_FMT_BF16> {
+  typedef __bf16 E;
+  static constexpr int KBW = 32;   // dims per QK block
+};
+template <> struct AttnTypes<MK_FMT_F32> {
+  typedef float E;
+  static constexpr int KBW = 16;
+};
+
+template <int KF, int KBMAX, int DBMAX>
+__device__ __forceinline__ void phase_attention(const LayerParams& p, int L, char* smem, int* flag) {
+  typedef typename AttnTypes<KF>::E E;
+  constexpr int KBW = AttnTypes<KF>::KBW;
+  const int T = p.T, nh = p.nh, dc = p.dc, kvw = p.kvw;
+  const int NQ = T * nh, NQT = (NQ + 15) / 16, Lt = L + T;
+  const int KB = kvw / KBW, DB = dc / 16;
+  int s_kv = (int)gridDim.x / NQT;
+  if (s_kv >= 8) s_kv = s_kv / 8 * 8;
+  if (s_kv < 1) s_kv = 1;
+  const int nchunk_all = (Lt + 15) / 16;
+  if (s_kv > nchunk_all) s_kv = nchunk_all;
+  const int SK = ((Lt + s_kv - 1) / s_kv + 15) / 16 * 16;
+  const int units = NQT * s_kv;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, j = lane & 15, g = lane >> 4;
+  const int CS = dc + 8;                               // LDS row stride of a staged chunk
+  E* cb = reinterpret_cast<E*>(smem) + (long long)w * 16 * CS;
+  const int QS = kvw + 8;                              // LDS row stride of the query tile
+  E* qs = reinterpret_cast<E*>(smem) + (long long)kWaves * 16 * CS;
+  const E* qlane = qs + j * QS + g * (KBW / 4);
+  const E* kvp = reinterpret_cast<const E*>(p.kv);
+  for (int u = blockIdx.x; u < units; u += gridDim.x) {
+    const int qt = u / s_kv, s = u - qt * s_kv;
+    const int qi = qt * 16 + j, qc = qi < NQ ? qi : NQ - 1;
+    const int tq = qc / nh;
+    const int limit = L + tq;                          // keys 0..limit are visible
+    // query tile -> LDS (shared by the 8 waves): qs[16][kvw + 8] = [q~ | rotated q^R]
+    __syncthreads();
+    for (int i = threadIdx.x; i < 16 * kvw; i += kThreads) {
+      const int jq = i / kvw, dd = i - jq * kvw;
+      const int qq = min(qt * 16 + jq, NQ - 1);
+      const int tt = qq / nh, hh = qq - tt * nh;
+      const float v = dd < dc ? p.qabs[((long long)tt * nh + hh) * dc + dd]
+                              : p.qrope[((long long)tt * nh + hh) * p.dr + (dd - dc)];
+      qs[jq * QS + dd] = (E)v;
+    }
+    __syncthreads();
+    const int k0 = s * SK, k1 = min(Lt, k0 + SK);
+    const int nch = k1 > k0 ? (k1 - k0 + 15) / 16 : 0;
+    float m_run = -INFINITY, l_run = 0.f;
+    f32x4 acc[DBMAX];
+#pragma unroll
+    for (int db = 0; db < DBMAX; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int c = w; c < nch; c += kWaves) {
+      const int kbase = k0 + c * 16;
+      const int key = min(kbase + j, Lt - 1);          // lane (g, i=j) loads key i
+      const E* row = kvp + (long long)key * kvw;
+      // S^T = K Q^T over the key dims; the latent part of the chunk is also
+      // staged (row-major) in this wave's LDS slice for the value product
+      f32x4 st = {0.f, 0.f, 0.f, 0.f};
+      constexpr int KH = (KBMAX + 1) / 2;
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        u32x4 kr[KH];
+#pragma unroll
+        for (int i = 0; i < KH; ++i) {
+          const int kb = half * KH + i;
+          if (kb < KB) kr[i] = ld16(row + kb * KBW + g * (KBW / 4));
+        }
+#pragma unroll
+        for (int i = 0; i < KH; ++i) {
+          const int kb = half * KH + i;
+          if (kb < KB) {
+            st = tile_mma_reg<KF>(kr[i], *reinterpret_cast<const typename BReg<KF>::T*>(qlane + kb * KBW), st);
+            if (kb * KBW < dc) *reinterpret_cast<u32x4*>(cb + j * CS + kb * KBW + g * (KBW / 4)) = kr[i];
+          }
+        }
+      }
+      // scores: lane (g, j) elem e = S[query j][key kbase + 4g + e]
+      float sc[4];
+      float cmax = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int kk = kbase + 4 * g + e;
+        sc[e] = (kk <= limit && kk < k1) ? st[e] * p.scale : -INFINITY;
+        cmax = fmaxf(cmax, sc[e]);
+      }
+      cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
+      cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
+      const float m_new = fmaxf(m_run, cmax);
+      float alpha, pe[4];
+      if (m_new == -INFINITY) {
+        alpha = 1.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pe[e] = 0.f;
+      } else {
+        alpha = __expf(m_run - m_new);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pe[e] = __expf(sc[e] - m_new);
+      }
+      float ps = pe[0] + pe[1] + pe[2] + pe[3];
+      ps += __shfl_xor(ps, 16);
+      ps += __shfl_xor(ps, 32);
+      l_run = l_run * alpha + ps;
+      m_run = m_new;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      if (KF == MK_FMT_BF16) {
+        bf16x4 pb;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pb[e] = (__bf16)pe[e];
+#pragma unroll
+        for (int db = 0; db < DBMAX; ++db) {
+          if (db < DB) {
+            bf16x4 av;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) av[e] = (__bf16)cb[(4 * g + e) * CS + db * 16 + j];
+            acc[db] = mma_bf16_k16(av, pb, acc[db] * alpha);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int db = 0; db < DBMAX; ++db) {
+          if (db < DB) {
+            f32x4 a = acc[db] * alpha;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) a = mma_f32_k4((float)cb[(4 * g + e) * CS + db * 16 + j], pe[e], a);
+            acc[db] = a;
+          }
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+    // merge the 8 waves' (m, l, Z) in LDS, tree order 4+0.., 2+0.., 1+0
+    __syncthreads();
+    float* mb = reinterpret_cast<float*>(smem);                 // [4][16][dc]
+    float* ml = reinterpret_cast<float*>(smem) + 4 * 16 * dc;   // [4][16][2]
+    for (int half = 4; half >= 1; half >>= 1) {
+      if (w >= half && w < 2 * half) {
+        float* zb = mb + (long long)(w - half) * 16 * dc;
+#pragma unroll
+        for (int db = 0; db < DBMAX; ++db)
+          if (db < DB)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) zb[j * dc + db * 16 + 4 * g + e] = acc[db][e];
+        if (g == 0) {
+          ml[((w - half) * 16 + j) * 2] = m_run;
+          ml[((w - half) * 16 + j) * 2 + 1] = l_run;
+        }
+      }
+      __syncthreads();
+      if (w < half) {
+        const float* zb = mb + (long long)w * 16 * dc;
+        const float mo = ml[(w * 16 + j) * 2], lo = ml[(w * 16 + j) * 2 + 1];
+        const float M = fmaxf(m_run, mo);
+        float sa = 0.f, sb = 0.f;
+        if (M != -INFINITY) {
+          sa = __expf(m_run - M);
+          sb = __expf(mo - M);
+        }
+#pragma unroll
+        for (int db = 0; db < DBMAX; ++db)
+          if (db < DB)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[db][e] = acc[db][e] * sa + zb[j * dc + db * 16 + 4 * g + e] * sb;
+        l_run = l_run * sa + lo * sb;
+        m_run = M;
+      }
+      __syncthreads();
+    }
+    if (w == 0) {
+      float* zp = p.att_part + (long long)u * 16 * dc;
+#pragma unroll
+      for (int db = 0; db < DBMAX; ++db)
+        if (db < DB)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) zp[j * dc + db * 16 + 4 * g + e] = acc[db][e];
+      if (g == 0) {
+        p.att_ml[((long long)u * 16 + j) * 2] = m_run;
+        p.att_ml[((long long)u * 16 + j) * 2 + 1] = l_run;
+      }
+    }
+    // the last split of this query tile to finish merges all splits into z
+    wg_release_begin();
+    if (threadIdx.x == 0) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      const uint32_t old = __hip_atomic_fetch_add(&p.att_cnt[qt], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const int last = old == (uint32_t)(s_kv - 1);
+      if (last) {
+        __hip_atomic_store(&p.att_cnt[qt], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      }
+      *flag = last;
+    }
+    __syncthreads();
+    if (*flag) {
+      const int ub = qt * s_kv;
+      for (int it = threadIdx.x; it < 16 * dc; it += kThreads) {
+        const int jq = it / dc, dd = it - jq * dc;
+        const int qq = qt * 16 + jq;
+        if (qq >= NQ) continue;
+        float M = -INFINITY;
+        for (int ss = 0; ss < s_kv; ++ss) M = fmaxf(M, p.att_ml[((long long)(ub + ss) * 16 + jq) * 2]);
+        float num = 0.f, den = 0.f;
+        for (int ss = 0; ss < s_kv; ++ss) {
+          const float ms = p.att_ml[((long long)(ub + ss) * 16 + jq) * 2];
+          if (ms == -INFINITY) continue;
+          const float wgt = __expf(ms - M);
+          den += wgt * p.att_ml[((long long)(ub + ss) * 16 + jq) * 2 + 1];
+          num += wgt * p.att_part[((long long)(ub + ss) * 16 + jq) * dc + dd];
+        }
+        p.z[(long long)qq * dc + dd] = num / den;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ------------------------------------------------------------------ P3  o = W_UV z
+template <int AF>
+__device__ __forceinline__ void phase_uv(const LayerParams& p) {
+  constexpr int TK = tile_k(AF);
+  constexpr int EPL = TK / 4;
+  const int T = p.T;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, j = lane & 15, g = lane >> 4;
+  const int jj = j < T ? j : T - 1;
+  const int RT = p.dh / 16, KT = p.dc / TK, U = p.nh * RT;
+  for (int u = blockIdx.x * kWaves + w; u < U; u += gridDim.x * kWaves) {
+    const int h = u / RT, rt = u - h * RT;
+    const uint8_t* tiles = p.wuv + (long long)u * KT * 1024 + lane * 16;
+    const float* zr = p.z + ((long long)jj * p.nh + h) * p.dc + g * EPL;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    int kt = 0;
+    for (; kt + 4 <= KT; kt += 4) {
+      u32x4 a0 = ld_stream16(tiles + (kt + 0) * 1024), a1 = ld_stream16(tiles + (kt + 1) * 1024);
+      u32x4 a2 = ld_stream16(tiles + (kt + 2) * 1024), a3 = ld_stream16(tiles + (kt + 3) * 1024);
+      acc = tile_mma_reg<AF>(a0, load_b<AF>(zr + (kt + 0) * TK), acc);
+      acc = tile_mma_reg<AF>(a1, load_b<AF>(zr + (kt + 1) * TK), acc);
+      acc = tile_mma_reg<AF>(a2, load_b<AF>(zr + (kt + 2) * TK), acc);
+      acc = tile_mma_reg<AF>(a3, load_b<AF>(zr + (kt + 3) * TK), acc);
+    }
+    for (; kt < KT; ++kt) acc = tile_mma_reg<AF>(ld_stream16(tiles + kt * 1024), load_b<AF>(zr + kt * TK), acc);
+    if (j < T) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) p.o[(long long)j * p.nh * p.dh + h * p.dh + rt * 16 + 4 * g + e] = acc[e];
+    }
+  }
+}
+
+// ------------------------------------------------------------------ P4  H' = H + W_O o
+template <int AF>
+__device__ __forceinline__ void phase_wo(const LayerParams& p, char* smem) {
+  typedef typename Act<AF>::T A;
+  constexpr int TK = tile_k(AF);
+  const int T = p.T, K = p.nh * p.dh, XS = K + kXPad;
+  LdsPlan lp(p, sizeof(A));
+  A* xs = reinterpret_cast<A*>(smem);
+  float* red = reinterpret_cast<float*>(smem + lp.xb);
+  const int KT = K / TK, U = p.d / 16;
+  int u0, u1;
+  split_range(U, gridDim.x, blockIdx.x, u0, u1);
+  if (u1 <= u0) return;
+  for (int i = threadIdx.x; i < T * K; i += kThreads) {
+    const int t = i / K, k = i - t * K;
+    xs[t * XS + k] = to_act<A>(p.o[i]);
+  }
+  __syncthreads();
+  const A* bl = b_lane<A>(xs, XS, T, TK);
+  struct Src {
+    const uint8_t* wo; int KT; const A* bl;
+    __device__ const uint8_t* tile(int u, int t) const { return wo + ((long long)u * KT + t) * 1024; }
+    __device__ const A* bptr(int, int t) const { return bl + t * TK; }
+    __device__ float scale(int, int) const { return 1.f; }
+    __device__ float scale2(int, int) const { return 1.f; }
+  } src{p.wo, KT, bl};
+  const float* H = p.H;
+  float* hp = p.hp;
+  const int d = p.d;
+  auto epi = [=](int u, int row, int col, float v, float) {
+    const long long i = (long long)col * d + u * 16 + row;
+    hp[i] = H[i] + v;
+  };
+  run_units<AF, false, false>(u0, u1, KT, T, src, epi, red);
+}
+
+// ------------------------------------------------------------------ P5 router
+template <int AF>
+__device__ __forceinline__ void phase_router(const LayerParams& p, char* smem) {
+  typedef typename Act<AF>::T A;
+  constexpr int TK = tile_k(AF);
+  const int T = p.T, XS = p.d + kXPad;
+  LdsPlan lp(p, sizeof(A));
+  A* xs = reinterpret_cast<A*>(smem);
+  A* xlo = AF == MK_FMT_F32 ? (A*)nullptr : reinterpret_cast<A*>(smem + lp.xb);
+  float* red = reinterpret_cast<float*>(smem + 2 * lp.xb);
+  rmsnorm_to_lds<A>(p.hp, p.g2, T, p.d, p.eps, xs, xlo, XS, smem);
+  const int KT = p.d / TK, S = p.sch.s_r, NT = KT / S, RT = p.E / 16;
+  const int U = RT * S;
+  int u0, u1;
+  split_range(U, gridDim.x, blockIdx.x, u0, u1);
+  const A* bl = b_lane<A>(xs, XS, T, TK);
+  struct Src {
+    const uint8_t* wr; int KT, S, NT; const A* bl; long long lo_off;
+    __device__ const uint8_t* tile(int u, int t) const {
+      int rt = u / S, s = u - rt * S;
+      return wr + ((long long)rt * KT + s * NT + t) * 1024;
+    }
+    __device__ const A* bptr(int u, int t) const { return bl + (u % S * NT + t) * TK; }
+    __device__ float scale(int, int) const { return 1.f; }
+    __device__ float scale2(int, int) const { return 1.f; }
+  } src{p.wr, KT, S, NT, bl, (long long)(lp.xb / (int)sizeof(A))};
+  float* lp_out = p.logit_part;
+  const int E = p.E;
+  auto epi = [=](int u, int row, int col, float v, float) {
+    int rt = u / S, s = u - rt * S;
+    lp_out[((long long)s * T + col) * E + rt * 16 + row] = v;
+  };
+  run_units<AF, false, AF != MK_FMT_F32>(u0, u1, NT, T, src, epi, red);
+}
+
+// ------------------------------------------------------------------ P6 routing + gate/up
+struct RouteLds {
+  float* lg;       // [T][E]
+  int* sel;        // [T][topk]
+  float* gate;     // [T][topk]
+  int* slot_of;    // [T][topk]
+  int* slots;      // [slots]
+  int* flags;      // [E]
+  int* nslots;     // [1]
+};
+__device__ __forceinline__ RouteLds route_lds(const LayerParams& p, char* smem, int xb) {
+  char* b = smem + xb + 32768;
+  RouteLds r;
+  r.lg = reinterpret_cast<float*>(b);
+  b += (size_t)kMaxT * p.E * 4;
+  r.sel = reinterpret_cast<int*>(b);
+  b += kMaxT * kMaxTopK * 4;
+  r.gate = reinterpret_cast<float*>(b);
+  b += kMaxT * kMaxTopK * 4;
+  r.slot_of = reinterpret_cast<int*>(b);
+  b += kMaxT * kMaxTopK * 4;
+  r.slots = reinterpret_cast<int*>(b);
+  b += (kMaxT * kMaxTopK + 8) * 4;
+  r.flags = reinterpret_cast<int*>(b);
+  b += (size_t)p.E * 4;
+  r.nslots = reinterpret_cast<int*>(b);
+  return r;
+}
+
+// softmax over all experts, top-k by logit (ties to the lower index), gates =
+// selected probabilities renormalised; then the ascending list of distinct
+// selected experts followed by the shared experts.  Identical in every workgroup.
+__device__ __forceinline__ void route(const LayerParams& p, const RouteLds& r) {
+  const int T = p.T, E = p.E, K = p.topk;
+  for (int i = threadIdx.x; i < T * E; i += kThreads) {
+    const int t = i / E, e = i - t * E;
+    float v = 0.f;
+    for (int s = 0; s < p.sch.s_r; ++s) v += p.logit_part[((long long)s * T + t) * E + e];
+    if (p.rbias) v += p.rbias[e];
+    r.lg[i] = v;
+  }
+  for (int i = threadIdx.x; i < E; i += kThreads) r.flags[i] = 0;
+  __syncthreads();
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (w < T) {
+    const float* lg = r.lg + w * E;
+    float mx = -INFINITY;
+    for (int e = lane; e < E; e += 64) mx = fmaxf(mx, lg[e]);
+    mx = wave_max(mx);
+    float se = 0.f;
+    for (int e = lane; e < E; e += 64) se += __expf(lg[e] - mx);
+    se = wave_sum(se);
+    unsigned long long taken = 0;      // lane-local bit i <-> expert lane + 64*i
+    float psel = 0.f;
+    for (int k = 0; k < K; ++k) {
+      float bv = -INFINITY;
+      int bi = 0x7fffffff;
+      for (int i = 0, e = lane; e < E; ++i, e += 64) {
+        if (!((taken >> i) & 1ull)) {
+          const float v = lg[e];
+          if (v > bv || (v == bv && e < bi)) { bv = v; bi = e; }
+        }
+      }
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        const float ov = __shfl_xor(bv, o);
+        const int oi = __shfl_xor(bi, o);
+        if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+      }
+      if (bi >= E) bi = 0;            // only for non-finite logits; keeps indices in range
+      if ((bi & 63) == lane) taken |= 1ull << (bi >> 6);
+      const float pr = __expf(bv - mx) / se;
+      psel += pr;
+      if (lane == 0) {
+        r.sel[w * kMaxTopK + k] = bi;
+        r.gate[w * kMaxTopK + k] = pr;
+      }
+    }
+    if (lane == 0)
+      for (int k = 0; k < K; ++k) r.gate[w * kMaxTopK + k] = r.gate[w * kMaxTopK + k] / psel;
+  }
+  __syncthreads();
+  if (threadIdx.x < T * K) {
+    const int t = threadIdx.x / K, k = threadIdx.x - t * K;
+    r.flags[r.sel[t * kMaxTopK + k]] = 1;
+  }
+  __syncthreads();
+  if (w == 0) {
+    int base = 0;
+    for (int c0 = 0; c0 < E; c0 += 64) {
+      const int e = c0 + lane;
+      const int f = e < E ? r.flags[e] : 0;
+      const unsigned long long m = __ballot(f);
+      if (f) {
+        const int idx = base + __popcll(m & ((1ull << lane) - 1ull));
+        r.slots[idx] = e;
+        r.flags[e] = idx + 1;          // slot + 1
+      }
+      base += __popcll(m);
+    }
+    if (lane < p.nshared) r.slots[base + lane] = E + lane;
+    if (lane == 0) *r.nslots = base + p.nshared;
+  }
+  __syncthreads();
+  if (threadIdx.x < T * K) {
+    const int t = threadIdx.x / K, k = threadIdx.x - t * K;
+    r.slot_of[t * kMaxTopK + k] = r.flags[r.sel[t * kMaxTopK + k]] - 1;
+  }
+  __syncthreads();
+  if (blockIdx.x == 0) {
+    for (int i = threadIdx.x; i < T * K; i += kThreads) {
+      const int t = i / K, k = i - t * K;
+      p.route_sel[i] = r.sel[t * kMaxTopK + k];
+      p.route_gate[i] = r.gate[t * kMaxTopK + k];
+    }
+    for (int i = threadIdx.x; i < T * E; i += kThreads) p.logits[i] = r.lg[i];
+  }
+}
+
+template <int AF, int EF>
+__device__ __forceinline__ void phase_route_gateup(const LayerParams& p, char* smem) {
+  typedef typename Act<EF>::T A;
+  static_assert((AF == MK_FMT_F32) == (EF == MK_FMT_F32), "activation types must agree");
+  constexpr int TK = tile_k(EF);
+  const int T = p.T, XS = p.d + kXPad;
+  LdsPlan lp(p, sizeof(A));
+  const A* xs = reinterpret_cast<const A*>(smem);      // x' (hi part) from P5
+  float* red = reinterpret_cast<float*>(smem + lp.xb);
+  RouteLds r = route_lds(p, smem, lp.xb);
+  route(p, r);
+  const int ns = *r.nslots;
+  const int RT = p.f / 16, KT = p.d / TK, U = ns * RT;
+  int u0, u1;
+  split_range(U, gridDim.x, blockIdx.x, u0, u1);
+  const A* bl = b_lane<A>(xs, XS, T, TK);
+  const int nbk = (p.d + 127) / 128;
+  struct Src {
+    const uint8_t* const* ex; const int* slots; int RT, KT, nbk; const A* bl;
+    long long sc_off, sc3_off;
+    __device__ const uint8_t* tile(int u, int t) const {
+      const int sl = u / RT, rt = u - sl * RT;
+      return ex[slots[sl]] + ((long long)rt * KT + t) * 2048;
+    }
+    __device__ const A* bptr(int, int t) const { return bl + t * TK; }
+    __device__ float scale(int u, int t) const {
+      const int sl = u / RT, rt = u - sl * RT;
+      const float* s = reinterpret_cast<const float*>(ex[slots[sl]] + sc_off);
+      return s[(rt >> 3) * nbk + (t * TK >> 7)];
+    }
+    __device__ float scale2(int u, int t) const {
+      const int sl = u / RT, rt = u - sl * RT;
+      const float* s = reinterpret_cast<const float*>(ex[slots[sl]] + sc3_off);
+      return s[(rt >> 3) * nbk + (t * TK >> 7)];
+    }
+  };
+  const long long nsc13 = (long long)((p.f + 127) / 128) * nbk;
+  const long long sc_off = p.exp_w13_bytes + p.exp_w2_bytes;
+  Src src{p.experts, r.slots, RT, KT, nbk, bl, sc_off, sc_off + nsc13 * 4};
+  float* hb = p.hbuf;
+  const int f = p.f;
+  auto epi = [=](int u, int row, int col, float v, float v2) {
+    const int sl = u / RT, rt = u - sl * RT;
+    const float sg = v / (1.0f + expf(-v));
+    hb[((long long)sl * T + col) * f + rt * 16 + row] = sg * v2;
+  };
+  run_units<EF, true, false>(u0, u1, KT, T, src, epi, red);
+}
+
+// ------------------------------------------------------------------ P7 down projections
+template <int EF>
+__device__ __forceinline__ void phase_down(const LayerParams& p, char* smem) {
+  typedef typename Act<EF>::T A;
+  constexpr int TK = tile_k(EF);
+  const int T = p.T, XS = p.f + kXPad;
+  LdsPlan lp(p, sizeof(A));
+  A* xs = reinterpret_cast<A*>(smem);
+  float* red = reinterpret_cast<float*>(smem + lp.xb);
+  RouteLds r = route_lds(p, smem, lp.xb);
+  const int ns = *r.nslots;
+  const int RT = p.d / 16, KT = p.f / TK, U = ns * RT;
+  int u0, u1;
+  split_range(U, gridDim.x, blockIdx.x, u0, u1);
+  const A* bl = b_lane<A>(xs, XS, T, TK);
+  const int nbk = (p.f + 127) / 128;
+  const long long nsc13 = (long long)((p.f + 127) / 128) * ((p.d + 127) / 128);
+  const long long sc2_off = p.exp_w13_bytes + p.exp_w2_bytes + 2 * nsc13 * 4;
+  struct Src {
+    const uint8_t* blk; int RT, KT, nbk; const A* bl; long long w2_off, sc2_off;
+    __device__ const uint8_t* tile(int u, int t) const {
+      const int rt = u % RT;
+      return blk + w2_off + ((long long)rt * KT + t) * 1024;
+    }
+    __device__ const A* bptr(int, int t) const { return bl + t * TK; }
+    __device__ float scale(int u, int t) const {
+      const int rt = u % RT;
+      return reinterpret_cast<const float*>(blk + sc2_off)[(rt >> 3) * nbk + (t * TK >> 7)];
+    }
+    __device__ float scale2(int, int) const { return 1.f; }
+  };
+  float* yb = p.ybuf;
+  const int d = p.d, f = p.f;
+  int u = u0;
+  while (u < u1) {
+    const int sl = u / RT;
+    const int ue = min(u1, (sl + 1) * RT);
+    const float* hsrc = p.hbuf + (long long)sl * T * f;
+    for (int i = threadIdx.x; i < T * f; i += kThreads) {
+      const int t = i / f, k = i - t * f;
+      xs[t * XS + k] = to_act<A>(hsrc[i]);
+    }
+    __syncthreads();
+    Src src{p.experts[r.slots[sl]], RT, KT, nbk, bl, p.exp_w13_bytes, sc2_off};
+    auto epi = [=](int uu, int row, int col, float v, float) {
+      const int rt = uu % RT;
+      yb[((long long)sl * T + col) * d + rt * 16 + row] = v;
+    };
+    run_units<EF, false, false>(u, ue, KT, T, src, epi, red);
+    u = ue;
+  }
+}
+
+// ------------------------------------------------------------------ P8 combine
+__device__ __forceinline__ void phase_combine(const LayerParams& p, char* smem, int xb) {
+  RouteLds r = route_lds(p, smem, xb);
+  const int T = p.T, d = p.d, K = p.topk, ns = *r.nslots;
+  for (int i = blockIdx.x * kThreads + threadIdx.x; i < T * d; i += gridDim.x * kThreads) {
+    const int t = i / d, c = i - t * d;
+    float v = p.hp[i];
+    for (int k = 0; k < K; ++k)
+      v += r.gate[t * kMaxTopK + k] * p.ybuf[((long long)r.slot_of[t * kMaxTopK + k] * T + t) * d + c];
+    for (int s = 0; s < p.nshared; ++s) v += p.ybuf[((long long)(ns - p.nshared + s) * T + t) * d + c];
+    p.out[i] = v;
+  }
+}
+
+// ------------------------------------------------------------------ the kernel
+template <int AF, int EF, int KF, int KBMAX, int DBMAX>
+__global__ __launch_bounds__(kThreads, 1) void layer_kernel(LayerParams p) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  int* flag = reinterpret_cast<int*>(smem + kFlagOff);
+  const int L = p.L_dev ? *p.L_dev : p.L;
+  if (L < 0 || (long long)L + p.T > p.kv_capacity) {
+    // every workgroup reads the same L and leaves before the first barrier
+    if (blockIdx.x == 0 && threadIdx.x == 0)
+      __hip_atomic_store(&p.bar->fault, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
+  if (p.trace && threadIdx.x == 0) p.trace[(long long)blockIdx.x * (2 + 2 * kBarriers)] = (long long)clock100();
+  phase_qkv<AF>(p, smem);
+  if (!grid_barrier(p, 0, flag)) return;
+  phase_rope_kv<KF>(p, L);
+  phase_absorb<AF>(p);
+  if (!grid_barrier(p, 1, flag)) return;
+  phase_attention<KF, KBMAX, DBMAX>(p, L, smem, flag);
+  if (!grid_barrier(p, 2, flag)) return;
+  phase_uv<AF>(p);
+  if (!grid_barrier(p, 3, flag)) return;
+  phase_wo<AF>(p, smem);
+  if (!grid_barrier(p, 4, flag)) return;
+  phase_router<AF>(p, smem);
+  if (!grid_barrier(p, 5, flag)) return;
+  phase_route_gateup<AF, EF>(p, smem);
+  if (!grid_barrier(p, 6, flag)) return;
+  phase_down<EF>(p, smem);
+  if (!grid_barrier(p, 7, flag)) return;
+  LdsPlan lp(p, EF == MK_FMT_F32 ? 4 : 2);
+  phase_combine(p, smem, lp.xb);
+  if (p.trace && threadIdx.x == 0)
+    p.trace[(long long)blockIdx.x * (2 + 2 * kBarriers) + 1 + 2 * kBarriers] = (long long)clock100();
+}
+
+// Instantiations: all-fp32 (d_latent + d_rope <= 160, d_latent <= 128),
+// bf16 attention with bf16 or fp8 experts (d_latent + d_rope <= 576, d_latent <= 512).
+typedef void (*LayerKernelFn)(LayerParams);
+LayerKernelFn layer_kernel_for(int af, int ef, int kf, int kvw, int dc) {
+  if (af == MK_FMT_F32 && ef == MK_FMT_F32 && kf == MK_FMT_F32 && kvw <= 160 && dc <= 128)
+    return layer_kernel<MK_FMT_F32, MK_FMT_F32, MK_FMT_F32, 10, 8>;
+  if (af == MK_FMT_BF16 && kf == MK_FMT_BF16 && kvw <= 576 && dc <= 512) {
+    if (ef == MK_FMT_BF16) return layer_kernel<MK_FMT_BF16, MK_FMT_BF16, MK_FMT_BF16, 18, 32>;
+    if (ef == MK_FMT_FP8_B128) return layer_kernel<MK_FMT_BF16, MK_FMT_FP8_B128, MK_FMT_BF16, 18, 32>;
+  }
+  return nullptr;
+}
+
+}  // namespace mk

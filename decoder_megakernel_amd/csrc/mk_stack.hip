@@ -1,0 +1,158 @@
+// Stack pieces around the layer kernel: embedding gather, and one launch that
+// does the final RMSNorm, the LM-head projection, the argmax per verify row
+// and greedy acceptance of the drafts (the lm_head and rejection-kernel rows of
+// the per-step kernel table in "Why one GB300 doesn't beat 4x RTX PRO 6000 at
+// single-stream decode", section "Where the 11.2 ms goes"; greedy decoding as
+// the engine gate uses it, "DeepSeek-V4.1-Flash breaks 1,000 tokens per second
+// for one user", section "The safety layer").
+#include "mk_device.h"
+#include "mk_host.h"
+
+namespace mk {
+
+__global__ __launch_bounds__(256) void embed_kernel(const uint16_t* emb, int V, int d, const int32_t* tokens, int T,
+                                                    float* h) {
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < T * d; i += gridDim.x * 256) {
+    const int t = i / d, k = i - t * d;
+    int tok = tokens[t];
+    tok = tok < 0 ? 0 : (tok >= V ? V - 1 : tok);
+    h[i] = __uint_as_float((uint32_t)emb[(long long)tok * d + k] << 16);
+  }
+}
+
+int launch_embed(const uint16_t* emb, int V, int d, const int32_t* tokens, int T, float* h, hipStream_t s) {
+  hipLaunchKernelGGL(embed_kernel, dim3(64), dim3(256), 0, s, emb, V, d, tokens, T, h);
+  return (int)hipGetLastError();
+}
+
+struct HeadArgs {
+  const uint8_t* head; int V, d; const float* gamma; float eps; const float* h; int T;
+  float* logits; float* best_val; int32_t* best_idx; uint32_t* counter; int32_t* tokens;
+  const int32_t* next_drafts; int32_t* argmax; int32_t* committed; int32_t* kv_len;
+};
+
+constexpr int kHeadLds = 8 * (8192 + kXPad) * 2 + 2 * kWaves * 64 * 4 * 4 + 1024;
+
+__global__ __launch_bounds__(kThreads, 1) void head_kernel(HeadArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int T = a.T, d = a.d, XS = d + kXPad;
+  __bf16* xs = reinterpret_cast<__bf16*>(smem);
+  float* red = reinterpret_cast<float*>(smem + 8 * XS * 2);
+  float* misc = reinterpret_cast<float*>(smem + kHeadLds - 1024);
+  // final RMSNorm into LDS
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (w < T) {
+    float ss = 0.f;
+    for (int k = lane; k < d; k += 64) {
+      const float v = a.h[(long long)w * d + k];
+      ss += v * v;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+    if (lane == 0) misc[w] = 1.0f / sqrtf(ss / (float)d + a.eps);
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < T * d; i += kThreads) {
+    const int t = i / d, k = i - t * d;
+    xs[t * XS + k] = (__bf16)((a.h[i] * misc[t]) * a.gamma[k]);
+  }
+  __syncthreads();
+  const int RT = a.V / 16, KT = d / 32;
+  const long long U = RT;
+  const int u0 = (int)(U * blockIdx.x / gridDim.x), u1 = (int)(U * (blockIdx.x + 1) / gridDim.x);
+  const int j = lane & 15, g = lane >> 4;
+  const __bf16* bl = xs + (j < T ? j : T - 1) * XS + g * 8;
+  struct Src {
+    const uint8_t* head; int KT; const __bf16* bl;
+    __device__ const uint8_t* tile(int u, int t) const { return head + ((long long)u * KT + t) * 1024; }
+    __device__ const __bf16* bptr(int, int t) const { return bl + t * 32; }
+    __device__ float scale(int, int) const { return 1.f; }
+    __device__ float scale2(int, int) const { return 1.f; }
+  } src{a.head, KT, bl};
+  float bv = -INFINITY;
+  int bi = 0x7fffffff;
+  float* logits = a.logits;
+  const int V = a.V;
+  auto epi = [&](int u, int row, int col, float v, float) {
+    const int id = u * 16 + row;
+    if (logits) logits[(long long)col * V + id] = v;
+    if (v > bv || (v == bv && id < bi)) { bv = v; bi = id; }
+  };
+  run_units<MK_FMT_BF16, false, false>(u0, u1, KT, T, src, epi, red);
+  // workgroup best per row: threads (row, col) with the same col hold candidates
+  float* cv = misc + 16;
+  int* ci = reinterpret_cast<int*>(misc + 16 + 256);
+  if (threadIdx.x < 256) {
+    cv[threadIdx.x] = bv;
+    ci[threadIdx.x] = bi;
+  }
+  __syncthreads();
+  if (threadIdx.x < T) {
+    float v = -INFINITY;
+    int id = 0x7fffffff;
+    for (int r = 0; r < 16; ++r) {
+      const float ov = cv[r * 16 + threadIdx.x];
+      const int oi = ci[r * 16 + threadIdx.x];
+      if (ov > v || (ov == v && oi < id)) { v = ov; id = oi; }
+    }
+    a.best_val[blockIdx.x * 8 + threadIdx.x] = v;
+    a.best_idx[blockIdx.x * 8 + threadIdx.x] = id;
+  }
+  // the last workgroup to finish reduces over the grid and verifies the drafts
+  wg_release_begin();
+  int* flag = reinterpret_cast<int*>(misc + 250);
+  if (threadIdx.x == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    const uint32_t old = __hip_atomic_fetch_add(a.counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int last = old == gridDim.x - 1;
+    if (last) {
+      __hip_atomic_store(a.counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    }
+    *flag = last;
+  }
+  __syncthreads();
+  if (!*flag) return;
+  int* am = reinterpret_cast<int*>(misc + 200);
+  if (threadIdx.x < T) {
+    float v = -INFINITY;
+    int id = 0x7fffffff;
+    for (int b = 0; b < (int)gridDim.x; ++b) {
+      const float ov = a.best_val[b * 8 + threadIdx.x];
+      const int oi = a.best_idx[b * 8 + threadIdx.x];
+      if (ov > v || (ov == v && oi < id)) { v = ov; id = oi; }
+    }
+    am[threadIdx.x] = id;
+    a.argmax[threadIdx.x] = id;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int n = 0;
+    while (n + 1 <= T - 1 && a.tokens[n + 1] == am[n]) ++n;
+    a.committed[0] = n + 1;
+    for (int i = 1; i <= n; ++i) a.committed[i] = a.tokens[i];
+    a.committed[n + 1] = am[n];
+    if (a.kv_len) a.kv_len[0] += n + 1;
+    a.tokens[0] = am[n];
+    if (a.next_drafts)
+      for (int i = 1; i < T; ++i) a.tokens[i] = a.next_drafts[i - 1];
+  }
+}
+
+int head_kernel_occupancy(int* wgs_per_cu) {
+  hipError_t e = hipFuncSetAttribute((const void*)head_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kHeadLds);
+  if (e != hipSuccess) return (int)e;
+  return (int)hipOccupancyMaxActiveBlocksPerMultiprocessor(wgs_per_cu, head_kernel, kThreads, kHeadLds);
+}
+
+int launch_head(const void* head_packed, int V, int d, const float* gamma, float eps, const float* h, int T,
+                float* logits, float* best_val, int32_t* best_idx, uint32_t* counter, int32_t* tokens,
+                const int32_t* next_drafts, int32_t* argmax, int32_t* committed, int32_t* kv_len, int nwg,
+                hipStream_t s) {
+  HeadArgs a{(const uint8_t*)head_packed, V, d, gamma, eps, h, T, logits, best_val, best_idx, counter, tokens,
+             next_drafts, argmax, committed, kv_len};
+  hipLaunchKernelGGL(head_kernel, dim3(nwg), dim3(kThreads), kHeadLds, s, a);
+  return (int)hipGetLastError();
+}
+
+}  // namespace mk

@@ -1,0 +1,243 @@
+/*
+ * mk -- a fused batch-1 speculative-decode verify step for a DeepSeek-style
+ * mixture-of-experts decoder layer on AMD Instinct MI355X (gfx950).
+ *
+ * One call of mk_decode_step runs one whole layer as ONE persistent kernel
+ * launch: RMSNorm, Q and latent-KV projections with RoPE and KV insert, latent
+ * attention over the KV cache for T verify rows, router softmax/top-k, routed
+ * and shared SwiGLU experts, and both residual adds.  What the layer computes
+ * follows "Why one GB300 doesn't beat 4x RTX PRO 6000 at single-stream
+ * decode" (section "Where the 11.2 ms goes": the per-kernel table of one
+ * verify step; section "Tier 2: the fusion program": norm -> gate -> top-k ->
+ * shared expert fused per layer; section "Corrections to things we said": one
+ * persistent kernel per decoder layer, tiled for at most 8 rows) and the
+ * multi-head latent attention of the DeepSeek-V2 paper (section 2.1).  The
+ * fused one-launch-per-layer design answers that report's finding that about a
+ * thousand sub-10-microsecond kernels per step cost 40% of the step.
+ *
+ * Conventions
+ *  - Every function returns MK_OK (0) or a negative mk_status; no exceptions
+ *    cross this boundary.  mk_last_error() gives a message for the calling
+ *    thread's last failure.
+ *  - There is no fallback path: an unsupported device or shape is an error,
+ *    never a slower kernel ("DeepSeek-V4.1-Flash breaks 1,000 tokens per second
+ *    for one user", section "What NVIDIA shipped, and why B300 was refused":
+ *    the plugin refuses rather than falling back silently).
+ *  - The caller allocates every device buffer (packed weights, KV rows, layer
+ *    state, workspace, inputs, outputs), sized with the *_bytes queries.  The
+ *    library keeps borrowed pointers until mk_layer_destroy / mk_model_destroy
+ *    and allocates no device memory.
+ *  - Step calls are asynchronous on the caller's HIP stream (a hipStream_t
+ *    passed as void*, NULL = default stream).  A device-side failure (a grid
+ *    barrier that timed out) is reported by mk_sync_status after the stream
+ *    has been synchronised.
+ *  - Calls that use the same workspace, state or KV rows must not overlap in
+ *    time (issue them on one stream).  Two persistent launches running at once
+ *    on one GPU can starve each other of compute units; the bounded barrier
+ *    wait then reports MK_ERR_TIMEOUT rather than hanging.
+ */
+#ifndef MK_H
+#define MK_H
+#include <stddef.h>
+#include <stdint.h>
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MK_ABI_VERSION 1
+#define MK_MAX_T 16          /* verify rows per step (the MFMA column count) */
+
+typedef enum mk_status {
+  MK_OK = 0,
+  MK_ERR_INVALID_ARG = -1,       /* null pointer, T out of range, capacity too small, ... */
+  MK_ERR_ABI_MISMATCH = -2,      /* config.abi_version != MK_ABI_VERSION */
+  MK_ERR_UNSUPPORTED_DEVICE = -3,/* not gfx950 */
+  MK_ERR_NOT_CORESIDENT = -4,    /* the persistent grid cannot be resident at once */
+  MK_ERR_HIP = -5,               /* a HIP runtime call failed */
+  MK_ERR_TIMEOUT = -6,           /* a grid barrier wait exceeded its bound */
+  MK_ERR_DEVICE_FAULT = -7,      /* the device reported another failure */
+  MK_ERR_UNSUPPORTED_SHAPE = -8  /* dimensions the kernels are not built for */
+} mk_status;
+
+/* Storage formats.  FP8_B128: OCP E4M3 ("FN": bias 7, max 448) codes with one
+ * fp32 scale per 128x128 block of the [rows][cols] matrix (value = code * scale). */
+typedef enum mk_format { MK_FMT_F32 = 0, MK_FMT_BF16 = 1, MK_FMT_FP8_B128 = 2 } mk_format;
+
+/* Layer shape.  Canonical weight layouts (row-major) that mk_pack_* consume:
+ *   W_Q   [n_heads*(d_head+d_rope)][d_model]  head h owns rows h*(d_head+d_rope)..:
+ *                                             first d_head -> q^C, last d_rope -> q^R
+ *   W_DKV [d_latent+d_rope][d_model]          first d_latent -> latent c, last d_rope -> shared key
+ *   W_UK  [n_heads][d_head][d_latent]         k^C_h = W_UK[h] c   (used absorbed: q~ = W_UK[h]^T q^C)
+ *   W_UV  [n_heads][d_head][d_latent]         o_h = W_UV[h] z_h
+ *   W_O   [d_model][n_heads*d_head]
+ *   W_R   [n_experts][d_model]                router; optional bias [n_experts] fp32
+ *   W1,W3 [d_ff][d_model], W2 [d_model][d_ff] per expert (SwiGLU: W2 (silu(W1 x) * W3 x))
+ * attn_format applies to W_Q, W_DKV, W_UK, W_UV, W_O, W_R (F32 or BF16);
+ * expert_format to W1, W3, W2 (F32, BF16 or FP8_B128); kv_format to the cache.
+ * Supported shapes: d_model, d_ff multiples of 128; d_head, d_latent multiples
+ * of 32; d_rope a multiple of 32; n_experts a multiple of 16; top_k <= 16.
+ * Formats must be all F32, or attention/KV BF16 with experts BF16 or FP8_B128. */
+typedef struct mk_layer_config {
+  int32_t abi_version;       /* must be MK_ABI_VERSION */
+  int32_t d_model;
+  int32_t n_heads;
+  int32_t d_head;
+  int32_t d_latent;
+  int32_t d_rope;
+  int32_t n_experts;
+  int32_t top_k;
+  int32_t n_shared;          /* 0 or 1 */
+  int32_t d_ff;
+  int32_t attn_format;
+  int32_t expert_format;
+  int32_t kv_format;
+  int32_t has_router_bias;
+  float rms_eps;             /* RMSNorm epsilon */
+  float rope_base;           /* RoPE base (angles formed in double on the device) */
+} mk_layer_config;
+
+typedef struct mk_device_info {
+  int32_t hip_device;
+  int32_t is_gfx950;
+  int32_t n_cus;             /* compute units the device reports (never assumed) */
+  int32_t wgs_per_cu;        /* co-resident workgroups of the layer kernel per CU */
+  int32_t grid_wgs;          /* persistent grid size used */
+  int32_t threads_per_wg;
+  int32_t lds_bytes_per_wg;
+  int32_t pad;
+  int64_t hbm_bytes;
+  char arch_name[64];
+} mk_device_info;
+
+/* Packed tensors (pre-tiled for coalesced streaming; opaque layout). */
+typedef enum mk_tensor {
+  MK_T_WQ = 0, MK_T_WDKV = 1, MK_T_WUK = 2, MK_T_WUV = 3, MK_T_WO = 4, MK_T_WR = 5,
+  MK_T_EXPERT = 6            /* W1, W3, W2 (and fp8 scales) of one expert in one block */
+} mk_tensor;
+
+/* Packed layer weights (device pointers). */
+typedef struct mk_layer_weights {
+  const float* gamma1;       /* [d_model] fp32 RMSNorm gain before attention */
+  const float* gamma2;       /* [d_model] fp32 RMSNorm gain before the MoE block */
+  const void* wq;
+  const void* wdkv;
+  const void* wuk;
+  const void* wuv;
+  const void* wo;
+  const void* wr;
+  const float* router_bias;  /* [n_experts] fp32, non-NULL iff has_router_bias */
+  const void* const* experts;/* HOST array of n_experts + n_shared device pointers to packed
+                                expert blocks; slot n_experts + s is shared expert s.  Blocks
+                                may be shared between layers. */
+} mk_layer_weights;
+
+/* KV cache of one layer: rows [capacity][d_latent + d_rope] in kv_format, row
+ * j = latent c_j followed by its RoPE-rotated key.  A step reads rows
+ * [0, length) plus its own new rows and writes rows [length, length+T); it does
+ * not change `length` (the caller commits accepted rows). */
+typedef struct mk_kv_cache {
+  void* rows;
+  int32_t capacity;
+  int32_t length;
+} mk_kv_cache;
+
+typedef struct mk_stats {
+  int64_t steps;             /* mk_decode_step calls that launched */
+  int64_t launches;          /* kernel launches issued by those calls (one per step) */
+  int32_t grid_wgs;
+  int32_t threads_per_wg;
+  int32_t barriers_per_step; /* grid-wide barriers inside one launch */
+  int32_t trace_enabled;
+} mk_stats;
+
+typedef struct mk_layer mk_layer;
+typedef struct mk_model mk_model;
+
+/* ---- version, device, sizes ------------------------------------------------ */
+int mk_abi_version(void);
+const char* mk_last_error(void);
+/* Fills `out` for `hip_device`; MK_ERR_UNSUPPORTED_DEVICE if it is not gfx950. */
+int mk_query_device(int hip_device, mk_device_info* out);
+/* Validates a config (ABI version, formats, supported shape). */
+int mk_check_config(const mk_layer_config* cfg);
+int mk_packed_bytes(const mk_layer_config* cfg, int tensor, size_t* bytes);
+int mk_kv_bytes(const mk_layer_config* cfg, int32_t capacity, size_t* bytes);
+/* Per-layer device state (expert table, counters, trace); one per mk_layer. */
+int mk_layer_state_bytes(const mk_layer_config* cfg, int hip_device, size_t* bytes);
+/* Scratch shared by layers that run one after another on one stream. */
+int mk_layer_workspace_bytes(const mk_layer_config* cfg, int hip_device, size_t* bytes);
+
+/* ---- packing (asynchronous on `stream`) ------------------------------------ */
+/* src: canonical device tensor in the tensor's format (layouts above). */
+int mk_pack_tensor(const mk_layer_config* cfg, int tensor, const void* src, void* dst, void* stream);
+/* One expert: canonical W1, W3 [d_ff][d_model], W2 [d_model][d_ff] in expert_format;
+ * for FP8_B128 the three fp32 scale arrays [ceil(rows/128)][ceil(cols/128)], else NULL. */
+int mk_pack_expert(const mk_layer_config* cfg, const void* w1, const void* w3, const void* w2,
+                   const float* s1, const float* s3, const float* s2, void* dst, void* stream);
+
+/* ---- layer ------------------------------------------------------------------- */
+/* Checks the device (gfx950, co-residency of the persistent grid), copies the
+ * expert table into `state`, clears its counters (synchronously). */
+int mk_layer_init(const mk_layer_config* cfg, const mk_layer_weights* w, void* state_dev,
+                  void* workspace_dev, int hip_device, mk_layer** out);
+/* One verify step: hidden_in [T][d_model] fp32 (device) -> hidden_out [T][d_model]
+ * fp32 (device; may not alias hidden_in); writes KV rows [length, length+T).
+ * MK_ERR_INVALID_ARG if T is not in [1, MK_MAX_T] or length + T > capacity. */
+int mk_decode_step(mk_layer* layer, const float* hidden_in, int T, const mk_kv_cache* kv,
+                   float* hidden_out, void* stream);
+/* Copies the step's intermediate results from the workspace to host memory
+ * (synchronises `stream`).  tap: 0 = Q [T][n_h][d_h+d_r] (q^R rotated),
+ * 1 = absorbed query q~ [T][n_h][d_latent], 2 = attention latent z [T][n_h][d_latent],
+ * 3 = o [T][n_h*d_head], 4 = post-attention hidden [T][d_model], 5 = router logits
+ * [T][n_experts], 6 = selected experts int32 [T][top_k], 7 = gates [T][top_k].
+ * Valid only after a step on this layer and before another layer reuses the workspace. */
+int mk_debug_tap(mk_layer* layer, int tap, void* host_dst, size_t bytes, void* stream);
+int mk_get_stats(const mk_layer* layer, mk_stats* out);
+/* Enables per-workgroup phase timestamps (written into the layer state). */
+int mk_set_trace(mk_layer* layer, int enabled);
+/* Copies the trace of the last step: int64 ticks of a 100 MHz clock,
+ * [grid_wgs][2 + 2*barriers_per_step]: start, (arrive, release) per barrier, end. */
+int mk_read_trace(mk_layer* layer, int64_t* host_dst, size_t bytes, void* stream);
+/* Barrier wait bound in microseconds (default 2,000,000). */
+int mk_set_barrier_timeout_us(mk_layer* layer, int64_t us);
+/* Synchronises nothing; reads the device fault word (call after the stream is
+ * synchronised).  MK_OK, or MK_ERR_TIMEOUT if a barrier wait gave up. */
+int mk_sync_status(mk_layer* layer);
+/* Clears barrier counters and the fault word (synchronous). */
+int mk_layer_reset(mk_layer* layer);
+void mk_layer_destroy(mk_layer* layer);
+
+/* ---- stack ------------------------------------------------------------------- */
+/* A stack of layers plus bf16 embedding and LM-head tables [vocab][d_model]
+ * (the head packed with mk_pack_head) and a final RMSNorm gain.  One step:
+ * embedding gather, every layer (one launch each), final norm + LM head +
+ * argmax (ties to the lower id) + greedy acceptance, all on the device with the
+ * KV length kept in device memory (no host synchronisation). */
+int mk_head_packed_bytes(int32_t vocab, int32_t d_model, size_t* bytes);
+int mk_pack_head(int32_t vocab, int32_t d_model, const uint16_t* src_bf16, void* dst, void* stream);
+int mk_model_state_bytes(int32_t n_layers, int32_t vocab, int hip_device, size_t* bytes);
+/* layers: n_layers initialised layers sharing one config; kv_rows: HOST array of
+ * n_layers device pointers, each [capacity][d_latent + d_rope]. */
+int mk_model_init(mk_layer* const* layers, int32_t n_layers, const uint16_t* embedding,
+                  const void* head_packed, const float* gamma_final, int32_t vocab,
+                  void* const* kv_rows, int32_t capacity, void* state_dev, void* hidden_dev,
+                  mk_model** out);
+/* Sets the committed KV length (synchronous copy). */
+int mk_model_set_length(mk_model* m, int32_t length);
+/* Device pointer to the committed KV length (int32). */
+const int32_t* mk_model_length_ptr(const mk_model* m);
+/* One verify step.  tokens_dev [T]: t0 then T-1 drafts.  Greedy verification:
+ * a_i = argmax of row i; n = the largest n <= T-1 with draft_j == a_{j-1} for
+ * all j <= n; n+1 tokens are committed (drafts 1..n and a_n).  Writes
+ * argmax_dev [T], committed_dev [1 + T] (count, then the tokens), advances the
+ * device KV length by n+1 and sets tokens_dev[0] = a_n; if next_drafts_dev
+ * ([T-1]) is non-NULL it is copied into tokens_dev[1..T-1] for the next step.
+ * logits_dev ([T][vocab] fp32) may be NULL. */
+int mk_model_step(mk_model* m, int32_t* tokens_dev, int T, const int32_t* next_drafts_dev,
+                  int32_t* argmax_dev, int32_t* committed_dev, float* logits_dev, void* stream);
+void mk_model_destroy(mk_model* m);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,119 @@
+"""Helpers shared by the GPU parity tests: run one layer step on the GPU through
+the C ABI and the same step in the CPU oracle, then compare.
+
+Comparison rules:
+  - floating outputs: normwise error per row, max_j |y_j - r_j| / max_j |r_j|,
+    taken separately on the attention branch (H' - H), the MoE branch
+    (out - H'), the output and the new KV rows; tolerances 1e-4 (fp32
+    layers), 2e-2 (bf16 weights), 5e-2 (fp8 experts);
+  - expert selection: identical sets except at near-ties, where the oracle's
+    k-th and (k+1)-th logits are within 1e-3; there every GPU pick must be
+    within 1e-3 of the oracle's k-th logit, and the oracle is re-run with the
+    GPU's picks forced before the outputs are compared.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+from synth import recipe
+
+TAU_SEL = 1e-3
+TOL = {"f32": 1e-4, "bf16": 2e-2, "fp8": 5e-2}
+
+
+def tol_of(s):
+    if s.exp_fmt == "fp8":
+        return TOL["fp8"]
+    if "bf16" in (s.attn_fmt, s.exp_fmt, s.kv_fmt):
+        return TOL["bf16"]
+    return TOL["f32"]
+
+
+def normwise(a, ref):
+    a = np.asarray(a, np.float64).reshape(ref.shape[0], -1)
+    ref = np.asarray(ref, np.float64).reshape(ref.shape[0], -1)
+    den = np.abs(ref).max(axis=1)
+    den[den == 0] = 1.0
+    return float((np.abs(a - ref).max(axis=1) / den).max())
+
+
+def kv_to_f32(kv_np, fmt):
+    return oracle.bf16_to_f32(kv_np.view(np.uint16)) if fmt == "bf16" else kv_np.astype(np.float32)
+
+
+def gpu_step(dl, s, H_dev, kv_dev, L, T=None):
+    """Runs one step; returns (out, new KV rows as float32, taps dict)."""
+    from decoder_megakernel_amd import MK_OK
+    T = T or s.T
+    out = torch.empty((T, s.d), dtype=torch.float32, device=H_dev.device)
+    dl.step(H_dev, T, kv_dev, L, out)
+    torch.cuda.synchronize()
+    assert dl.layer.sync_status() == MK_OK
+    taps = {}
+    for name, tap, shape, dt in (("Hp", 4, (T, s.d), np.float32), ("logits", 5, (T, s.E), np.float32),
+                                 ("sel", 6, (T, s.top_k), np.int32), ("gate", 7, (T, s.top_k), np.float32),
+                                 ("z", 2, (T, s.n_h, s.d_c), np.float32), ("qabs", 1, (T, s.n_h, s.d_c), np.float32),
+                                 ("o", 3, (T, s.n_h * s.d_h), np.float32), ("q", 0, (T, s.n_h, s.qw), np.float32)):
+        buf = np.empty(shape, dt)
+        dl.layer.debug_tap(tap, buf)
+        taps[name] = buf
+    kvn = kv_dev[L:L + T].cpu().numpy()
+    return out.cpu().numpy(), kv_to_f32(kvn, s.kv_fmt), taps
+
+
+def oracle_step(s, seed, layer, H, L, kv_host=None, force_sel=None, full_weights=None):
+    """Oracle layer step on the host copies of the same seeded inputs.
+    Returns (out, new KV rows float32, taps, weights used)."""
+    kv = recipe.kv_prefill_host(s, seed, layer) if kv_host is None else kv_host
+    if full_weights is not None:
+        out, taps = oracle.layer_step(s, full_weights, H, kv, L, force_sel=force_sel)
+        w = full_weights
+    else:
+        out, taps, w = oracle.layer_step_lazy(s, seed, layer, H, kv, L, force_sel=force_sel)
+    return out, kv_to_f32(kv[L:L + H.shape[0]], s.kv_fmt), taps, w
+
+
+def compare_selection(s, gpu_sel, ora_logits, ora_sel):
+    """Returns (n_near_ties, needs_forced_rerun); asserts the selection rule."""
+    T, k = gpu_sel.shape
+    near = 0
+    forced = False
+    for i in range(T):
+        lg = ora_logits[i].astype(np.float64)
+        srt = np.sort(lg)[::-1]
+        gap = srt[k - 1] - srt[k] if k < len(srt) else np.inf
+        if gap > TAU_SEL:
+            assert set(gpu_sel[i].tolist()) == set(ora_sel[i].tolist()), (i, gpu_sel[i], ora_sel[i])
+        else:
+            near += 1
+            kth = srt[k - 1]
+            for e in gpu_sel[i]:
+                assert lg[e] >= kth - TAU_SEL, (i, e, lg[e], kth)
+            if set(gpu_sel[i].tolist()) != set(ora_sel[i].tolist()):
+                forced = True
+    return near, forced
+
+
+def check_layer(s, seed, layer, g_out, g_kv, g_taps, H, L, kv_host=None, full_weights=None, report=None):
+    """Full parity check of one step against the oracle.  Returns a dict of errors."""
+    o_out, o_kv, o_taps, w = oracle_step(s, seed, layer, H, L, kv_host=kv_host, full_weights=full_weights)
+    near, forced = compare_selection(s, g_taps["sel"], o_taps["logits"], o_taps["sel"])
+    if forced:
+        kvh = recipe.kv_prefill_host(s, seed, layer) if kv_host is None else kv_host
+        o_out, o_kv, o_taps, w = oracle_step(s, seed, layer, H, L, kv_host=kvh, force_sel=g_taps["sel"],
+                                             full_weights=full_weights)
+    tol = tol_of(s)
+    errs = {
+        "attn_branch": normwise(g_taps["Hp"].astype(np.float64) - H, o_taps["Hp"].astype(np.float64) - H),
+        "moe_branch": normwise(g_out.astype(np.float64) - g_taps["Hp"], o_out.astype(np.float64) - o_taps["Hp"]),
+        "out": normwise(g_out, o_out),
+        "kv_new": normwise(g_kv, o_kv),
+        "near_ties": near,
+    }
+    if report is not None:
+        report.update(errs)
+    for k in ("attn_branch", "moe_branch", "out", "kv_new"):
+        assert errs[k] <= tol, (k, errs, tol)
+    return errs

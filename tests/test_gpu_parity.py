@@ -1,0 +1,105 @@
+"""GPU parity: the HIP verify step (through the C ABI) against the CPU oracle on
+identical seeded inputs (rules in tests/parity.py)."""
+import numpy as np
+import pytest
+
+from synth import recipe
+from synth.configs import C1, C2, C3, C4, LayerShape
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+# Several tiles in every dimension, ragged tails (L+T not a multiple of 16,
+# T < 16 MFMA columns, expert counts not a multiple of the grid).
+MID_BF16 = LayerShape("mid_bf16", d=512, n_h=4, d_h=64, d_c=128, d_r=32, E=32, top_k=4, n_shared=1, f=256,
+                      T=5, L=77, attn_fmt="bf16", exp_fmt="bf16", kv_fmt="bf16")
+MID_FP8 = LayerShape("mid_fp8", d=640, n_h=6, d_h=64, d_c=256, d_r=64, E=48, top_k=6, n_shared=1, f=384,
+                     T=7, L=300, attn_fmt="bf16", exp_fmt="fp8", kv_fmt="bf16")
+MID_F32 = LayerShape("mid_f32", d=384, n_h=4, d_h=32, d_c=96, d_r=32, E=16, top_k=3, n_shared=1, f=256,
+                     T=3, L=45, attn_fmt="f32", exp_fmt="f32", kv_fmt="f32")
+
+
+def _run(s, seed=0, layer=0, L=None, T=None, full_weights=True):
+    from decoder_megakernel_amd import harness
+    import parity
+    L = s.L if L is None else L
+    T = s.T if T is None else T
+    s2 = s.with_(L=L, T=T, kv_capacity=max(s.capacity, L + T))
+    print("[parity] %s seed=%d L=%d T=%d" % (s.name, seed, L, T), flush=True)
+    dl = harness.DeviceLayer(s2, seed, layer)
+    kv = harness.kv_cache(s2, seed, layer)
+    H = recipe.hidden_host(s2, seed, layer)
+    Hd = torch.from_numpy(H).cuda()
+    g_out, g_kv, g_taps = parity.gpu_step(dl, s2, Hd, kv, L, T)
+    w = recipe.layer_weights_host(s2, seed, layer) if full_weights else None
+    rep = {}
+    errs = parity.check_layer(s2, seed, layer, g_out, g_kv, g_taps, H, L, full_weights=w, report=rep)
+    print("[parity] %s errors %s" % (s.name, errs), flush=True)
+    return dl, kv, Hd, g_out, g_kv, errs
+
+
+@pytest.mark.parametrize("shape", [C1, MID_F32, MID_BF16, MID_FP8], ids=lambda s: s.name)
+def test_small_shapes_match_oracle(shape):
+    _run(shape)
+
+
+def test_single_row_empty_cache():
+    _run(MID_BF16, L=0, T=1)
+
+
+def test_max_rows():
+    _run(MID_FP8, T=8, L=13)
+
+
+def test_full_size_bf16_E128_T6_L2048():
+    _run(C2, full_weights=False)
+
+
+def test_full_size_fp8_E384_T8_L8192():
+    _run(C3, full_weights=False)
+
+
+def test_full_size_fp8_E384_T6_L65536_skew():
+    _run(C4, full_weights=False)
+
+
+def test_run_twice_bitwise_identical():
+    from decoder_megakernel_amd import harness
+    s = MID_FP8
+    dl = harness.DeviceLayer(s, 0, 0)
+    H = harness.hidden(s)
+    outs = []
+    for _ in range(2):
+        kv = harness.kv_cache(s)
+        out = torch.empty_like(H)
+        dl.step(H, s.T, kv, s.L, out)
+        torch.cuda.synchronize()
+        outs.append((out.cpu().numpy().view(np.uint32), kv.cpu().numpy().view(np.uint16)))
+    assert np.array_equal(outs[0][0], outs[1][0])
+    assert np.array_equal(outs[0][1], outs[1][1])
+
+
+def test_verify_rows_match_sequential_single_row_steps():
+    """Causal invariant on the GPU: row i of a T-row step equals (to tolerance)
+    a single-row step at position L+i on the cache the earlier rows built."""
+    from decoder_megakernel_amd import harness
+    import parity
+    s = MID_BF16
+    dl = harness.DeviceLayer(s, 0, 0)
+    H = harness.hidden(s)
+    kv = harness.kv_cache(s)
+    out = torch.empty_like(H)
+    dl.step(H, s.T, kv, s.L, out)
+    kv2 = harness.kv_cache(s)
+    outs = []
+    for i in range(s.T):
+        o = torch.empty((1, s.d), dtype=torch.float32, device="cuda")
+        dl.step(H[i:i + 1].contiguous(), 1, kv2, s.L + i, o)
+        outs.append(o)
+    torch.cuda.synchronize()
+    seq = torch.cat(outs).cpu().numpy()
+    assert parity.normwise(out.cpu().numpy(), seq) < 2e-2
+    kvs = parity.kv_to_f32(kv2[s.L:s.L + s.T].cpu().numpy(), "bf16")
+    kvb = parity.kv_to_f32(kv[s.L:s.L + s.T].cpu().numpy(), "bf16")
+    assert parity.normwise(kvb, kvs) < 2e-2
