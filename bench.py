@@ -1,0 +1,288 @@
+#!/usr/bin/env python3
+"""Benchmark of the batch-1 speculative-decode verify loop on one MI355X.
+
+Default workload: the 32-layer stack of fp8-expert MoE layers (384 routed
+experts top-8 + 1 shared, hidden 4096, T = 6 verify rows, KV cache from 4096
+positions, vocab 129280), run as a device-resident verify loop: every step is
+the embedding gather, 32 layer launches and one LM-head/argmax/accept launch,
+with the KV length kept on the device.  Weights and inputs are synthetic and
+seeded (the trained model is not used); with random weights almost no draft is
+accepted, so a step commits ~1 token.
+
+Printed: one JSON line with the step time, tokens/s per stream, per-layer
+microseconds, algorithmic HBM bytes and bandwidth, the roofline of the layer
+kernel (live HIP-event timing of its launches), and the CPU oracle timed on a
+bounded sample as a baseline.  --workload C2|C3|C4 times a single layer
+instead (three rotating weight copies so the 256 MB last-level cache cannot
+serve repeats).
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode step µs/layer & tok/s/stream at T=6; achieved HBM GB/s vs peak"
+PEAK_GBPS = 8000.0      # MI355X HBM3E peak
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def attn_bytes(s):
+    e = 2 if s.attn_fmt == "bf16" else 4
+    return e * (s.n_h * s.qw * s.d + s.kvw * s.d + 2 * s.n_h * s.d_h * s.d_c + s.d * s.n_h * s.d_h)
+
+
+def router_bytes(s):
+    return (2 if s.attn_fmt == "bf16" else 4) * s.E * s.d + (4 * s.E if s.routing == "skew" else 0)
+
+
+def expert_bytes(s):
+    if s.exp_fmt == "fp8":
+        nsc = ((s.f + 127) // 128) * ((s.d + 127) // 128)
+        return 3 * s.f * s.d + 3 * nsc * 4
+    return 3 * s.f * s.d * (2 if s.exp_fmt == "bf16" else 4)
+
+
+def layer_bytes(s, L, slots):
+    """Algorithmic bytes of one layer step: touched weights, KV read/write, activations in/out."""
+    kv_e = 2 if s.kv_fmt == "bf16" else 4
+    kv = (L + s.T) * s.kvw * kv_e + s.T * s.kvw * kv_e
+    act = 2 * s.T * s.d * 4 + 2 * s.d * 4
+    return attn_bytes(s) + router_bytes(s) + slots * expert_bytes(s) + kv + act
+
+
+def read_i32(dev_ptr):
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so")
+    out = ctypes.c_int32(0)
+    if hip.hipMemcpy(ctypes.byref(out), ctypes.c_void_p(dev_ptr), ctypes.c_size_t(4), ctypes.c_int(2)) != 0:
+        raise RuntimeError("hipMemcpy failed")
+    return out.value
+
+
+def cores_used():
+    n = len(os.sched_getaffinity(0))
+    omp = os.environ.get("OMP_NUM_THREADS")
+    return min(n, int(omp)) if omp and omp.isdigit() else n
+
+
+def cpu_baseline_stack(s, tokens_per_step):
+    """The oracle (untuned) on a bounded sample: one layer step (layer 0, T rows
+    at the initial cache length, experts drawn on demand) and one LM-head step;
+    a stack step is extrapolated as n_layers layer steps + one head step."""
+    import oracle
+    from synth import recipe
+    w = recipe.layer_weights_host(s, 0, 0, experts=[])
+    H = recipe.hidden_host(s, 0, 0)
+    kv = recipe.kv_prefill_host(s, 0, 0)
+    # draw the routed experts this step needs outside the timed region
+    _, _, wx = oracle.layer_step_lazy(s, 0, 0, H, kv.copy(), s.L, base_weights=w)
+    t0 = time.perf_counter()
+    oracle.layer_step(s, wx, H, kv, s.L)
+    t_layer = time.perf_counter() - t0
+    emb, head, gf = recipe.stack_tables_host(s, 0)
+    h = oracle.embed(emb, recipe.tokens_host(s, 0, 0))
+    t0 = time.perf_counter()
+    oracle.head(head, gf, h, s.eps, want_logits=False)
+    t_head = time.perf_counter() - t0
+    t_step = s.n_layers * t_layer + t_head
+    return {"value": tokens_per_step / t_step, "unit": "tok/s/stream", "cores": cores_used(), "kind": "oracle",
+            "sample": "one layer step (layer 0, T=%d, L=%d, experts drawn beforehand) took %.2f s and one LM-head "
+                      "step %.2f s; stack step = %d x layer + head = %.1f s; tokens/step as realized on the GPU"
+                      % (s.T, s.L, t_layer, t_head, s.n_layers, t_step)}
+
+
+def cpu_baseline_layer(s):
+    import oracle
+    from synth import recipe
+    w = recipe.layer_weights_host(s, 0, 0, experts=[])
+    H = recipe.hidden_host(s, 0, 0)
+    kv = recipe.kv_prefill_host(s, 0, 0)
+    _, _, wx = oracle.layer_step_lazy(s, 0, 0, H, kv.copy(), s.L, base_weights=w)
+    t0 = time.perf_counter()
+    oracle.layer_step(s, wx, H, kv, s.L)
+    t = time.perf_counter() - t0
+    return {"value": t * 1e6, "unit": "us/layer", "cores": cores_used(), "kind": "oracle",
+            "sample": "one layer step (T=%d, L=%d), experts drawn beforehand" % (s.T, s.L)}
+
+
+def run_stack(s, args):
+    import torch
+    from decoder_megakernel_amd import harness
+    from synth import recipe
+    dev = torch.device("cuda", 0)
+    n_layers = args.layers or s.n_layers
+    s = s.with_(n_layers=n_layers)
+    t0 = time.perf_counter()
+    st = harness.DeviceStack(s, seed=0)
+    log("[bench] stack of %d layers built in %.1f s" % (n_layers, time.perf_counter() - t0))
+    K, W = args.steps, args.warmup
+    drafts = np.stack([recipe.tokens_host(s, 0, i + 1)[1:] for i in range(W + K)]).astype(np.int32)
+    drafts_d = torch.from_numpy(drafts).to(dev)
+    tokens = torch.from_numpy(recipe.tokens_host(s, 0, 0)).to(dev)
+    am = torch.empty(s.T, dtype=torch.int32, device=dev)
+    com = torch.zeros(s.T + 1, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
+    for i in range(W):
+        st.model.step(tokens.data_ptr(), s.T, drafts_d[i].data_ptr(), am.data_ptr(), com.data_ptr(), None, sh)
+    torch.cuda.synchronize(dev)
+    len0 = read_i32(st.model.length_ptr())
+    stats0 = [dl.layer.stats() for dl in st.layers]
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize(dev)
+    ev0.record(stream)
+    for i in range(K):
+        st.model.step(tokens.data_ptr(), s.T, drafts_d[W + i].data_ptr(), am.data_ptr(), com.data_ptr(), None, sh)
+    ev1.record(stream)
+    torch.cuda.synchronize(dev)
+    for dl in st.layers:
+        if dl.layer.sync_status() != 0:
+            raise RuntimeError("device fault during the timed steps")
+    ms = ev0.elapsed_time(ev1)
+    len1 = read_i32(st.model.length_ptr())
+    stats1 = [dl.layer.stats() for dl in st.layers]
+    committed = len1 - len0
+    slots = [(b.expert_blocks_sum - a.expert_blocks_sum) / max(1, b.device_launches - a.device_launches)
+             for a, b in zip(stats0, stats1)]
+    Lavg = 0.5 * (len0 + len1)
+    step_bytes = sum(layer_bytes(s, Lavg, sl) for sl in slots) + s.V * s.d * 2 + s.T * s.d * 2 + s.d * 4
+    ms_step = ms / K
+    tok_s = committed / (ms / 1e3)
+
+    # dominant kernel: the layer launches of a step, timed alone (HIP events on the launch stream)
+    reps = args.layer_reps
+    h = torch.from_numpy(recipe.hidden_host(s, 0, 0)).to(dev)
+    buf = [h.clone(), torch.empty_like(h)]
+    Lnow = len1
+    stats2 = [dl.layer.stats() for dl in st.layers]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize(dev)
+    e0.record(stream)
+    for r in range(reps):
+        for l, dl in enumerate(st.layers):
+            dl.layer.decode_step(buf[l & 1].data_ptr(), s.T, st.kv[l].data_ptr(), st.capacity, Lnow,
+                                 buf[(l + 1) & 1].data_ptr(), sh)
+    e1.record(stream)
+    torch.cuda.synchronize(dev)
+    launches = reps * n_layers
+    us_layer = e0.elapsed_time(e1) * 1e3 / launches
+    stats3 = [dl.layer.stats() for dl in st.layers]
+    slots_l = [(b.expert_blocks_sum - a.expert_blocks_sum) / max(1, b.device_launches - a.device_launches)
+               for a, b in zip(stats2, stats3)]
+    lb = sum(layer_bytes(s, Lnow, sl) for sl in slots_l) / n_layers
+    achieved = lb / (us_layer * 1e-6) / 1e9
+    res = {
+        "metric": METRIC, "value": round(tok_s, 3), "unit": "tok/s/stream", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": s.name, "layers": n_layers, "T": s.T, "kv_len_start": len0, "kv_len_end": len1,
+                   "experts": s.E, "top_k": s.top_k, "shared": s.n_shared, "d_model": s.d, "d_ff": s.f,
+                   "vocab": s.V, "expert_pools": s.n_pools, "weights": "fp8 e4m3 experts (128x128 fp32 scales), "
+                   "bf16 attention/router/embedding/head", "kv": s.kv_fmt,
+                   "compute": "bf16 MFMA operands, fp32 accumulation"},
+        "tokens_per_step": round(committed / K, 4),
+        "us_per_layer_step": round(ms_step * 1e3 / n_layers, 2),
+        "us_per_layer_kernel": round(us_layer, 2),
+        "step_bytes": int(step_bytes),
+        "hbm_gbps_step": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
+        "experts_streamed_per_layer": round(float(np.mean(slots)), 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "layer_kernel<bf16, fp8, bf16>", "bytes_per_launch": int(lb),
+                     "avg_launch_us": round(us_layer, 2), "launches_timed": launches},
+    }
+    if args.cpu_baseline:
+        log("[bench] CPU oracle baseline ...")
+        res["cpu_baseline"] = cpu_baseline_stack(s, committed / K)
+    return res
+
+
+def run_layer(s, args):
+    import torch
+    from decoder_megakernel_amd import harness
+    dev = torch.device("cuda", 0)
+    copies = []
+    ws = None
+    for seed in range(3):
+        dl = harness.DeviceLayer(s, seed, 0, workspace=ws)
+        ws = dl.workspace
+        copies.append((dl, harness.kv_cache(s, seed), [harness.hidden(s, seed, 0, j) for j in range(4)]))
+    log("[bench] 3 weight copies of %s built" % s.name)
+    stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
+    out = torch.empty((s.T, s.d), dtype=torch.float32, device=dev)
+    seq = [(c, j) for j in range(4) for c in range(3)]
+
+    def run(n, off):
+        for i in range(n):
+            c, j = seq[(off + i) % len(seq)]
+            dl, kv, hs = copies[c]
+            dl.layer.decode_step(hs[j].data_ptr(), s.T, kv.data_ptr(), kv.shape[0], s.L, out.data_ptr(), sh)
+
+    run(args.warmup, 0)
+    torch.cuda.synchronize(dev)
+    st0 = [c[0].layer.stats() for c in copies]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    run(args.steps, args.warmup)
+    e1.record(stream)
+    torch.cuda.synchronize(dev)
+    us = e0.elapsed_time(e1) * 1e3 / args.steps
+    st1 = [c[0].layer.stats() for c in copies]
+    slots = sum(b.expert_blocks_sum - a.expert_blocks_sum for a, b in zip(st0, st1)) / args.steps
+    lb = layer_bytes(s, s.L, slots)
+    achieved = lb / (us * 1e-6) / 1e9
+    res = {
+        "metric": METRIC, "value": round(us, 2), "unit": "us/layer", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(us / 1e3, 4), "higher_is_better": False, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": s.name, "T": s.T, "L": s.L, "experts": s.E, "top_k": s.top_k, "d_model": s.d,
+                   "d_ff": s.f, "expert_format": s.exp_fmt, "weight_copies": 3},
+        "experts_streamed_per_step": round(slots, 2), "step_bytes": int(lb),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_GBPS, 4), "traffic": None, "bytes_per_launch": int(lb),
+                     "avg_launch_us": round(us, 2)},
+    }
+    if args.cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_layer(s)
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--workload", default="C5", choices=["C2", "C3", "C4", "C5"])
+    ap.add_argument("--layers", type=int, default=None, help="stack depth override (diagnostics only)")
+    ap.add_argument("--layer-reps", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (the layer's sharding is "
+              "described in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    from synth.configs import BY_KEY
+    s = BY_KEY[args.workload]
+    if s.n_layers > 1:
+        args.steps = args.steps or 256
+        args.warmup = args.warmup if args.warmup is not None else 8
+        res = run_stack(s, args)
+    else:
+        args.steps = args.steps or 60
+        args.warmup = args.warmup if args.warmup is not None else 12
+        res = run_layer(s, args)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -14,7 +14,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmk.so")
 
 MK_ABI_VERSION = 1
-MK_MAX_T = 8   # verify rows the kernels are built for (the header allows up to 16 in its ABI)
+MK_MAX_T = 8   # verify rows per step
 
 MK_OK = 0
 MK_ERR_INVALID_ARG = -1
@@ -78,7 +78,8 @@ class KvCache(ctypes.Structure):
 
 class Stats(ctypes.Structure):
     _fields_ = [("steps", ctypes.c_int64), ("launches", ctypes.c_int64), ("grid_wgs", _i32),
-                ("threads_per_wg", _i32), ("barriers_per_step", _i32), ("trace_enabled", _i32)]
+                ("threads_per_wg", _i32), ("barriers_per_step", _i32), ("trace_enabled", _i32),
+                ("device_launches", ctypes.c_int64), ("expert_blocks_sum", ctypes.c_int64)]
 
 
 def _load():

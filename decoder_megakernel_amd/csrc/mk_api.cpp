@@ -544,6 +544,10 @@ int mk_get_stats(const mk_layer* L, mk_stats* out) {
   out->threads_per_wg = kThreads;
   out->barriers_per_step = kBarriers;
   out->trace_enabled = L->trace_on;
+  unsigned long long dv[2] = {0, 0};
+  HIP_OK(hipMemcpy(dv, L->state + L->sl.bar + offsetof(BarrierState, slots_sum), 16, hipMemcpyDeviceToHost));
+  out->expert_blocks_sum = (int64_t)dv[0];
+  out->device_launches = (int64_t)dv[1];
   return MK_OK;
 }
 

@@ -9,7 +9,7 @@ namespace mk {
 
 constexpr int kThreads = 512;            // threads per workgroup (8 wave64s)
 constexpr int kWaves = kThreads / 64;
-constexpr int kMaxT = 8;                 // verify rows the LDS budget is sized for
+constexpr int kMaxT = MK_MAX_T;          // verify rows the LDS budget is sized for
 constexpr int kXPad = 8;                 // LDS row padding of activation operands (elements)
 constexpr int kBarriers = 8;             // grid barriers in one layer launch
 constexpr int kLdsBytes = 160 * 1024 - 256;
@@ -29,6 +29,9 @@ struct alignas(256) BarrierState {
   uint32_t pad1[63];
   uint32_t fault;          // 0 ok, 1 barrier timeout, 2 KV length out of range
   uint32_t pad2[63];
+  unsigned long long slots_sum;   // sum over launches of experts streamed (routed distinct + shared)
+  unsigned long long launches;    // launches that reached the expert phase
+  uint32_t pad3[60];
 };
 
 // Schedule chosen at init for this device and shape.

@@ -695,6 +695,10 @@ __device__ __forceinline__ void route(const LayerParams& p, const RouteLds& r) {
       p.route_gate[i] = r.gate[t * kMaxTopK + k];
     }
     for (int i = threadIdx.x; i < T * E; i += kThreads) p.logits[i] = r.lg[i];
+    if (threadIdx.x == 0) {
+      p.bar->slots_sum += (unsigned long long)*r.nslots;
+      p.bar->launches += 1ull;
+    }
   }
 }
 

@@ -45,7 +45,7 @@ extern "C" {
 #endif
 
 #define MK_ABI_VERSION 1
-#define MK_MAX_T 16          /* verify rows per step (the MFMA column count) */
+#define MK_MAX_T 8           /* verify rows per step: k drafts + 1, at most 8 */
 
 typedef enum mk_status {
   MK_OK = 0,
@@ -148,6 +148,9 @@ typedef struct mk_stats {
   int32_t threads_per_wg;
   int32_t barriers_per_step; /* grid-wide barriers inside one launch */
   int32_t trace_enabled;
+  int64_t device_launches;   /* launches that reached the expert phase (read from the device) */
+  int64_t expert_blocks_sum; /* sum over those launches of expert weight blocks streamed
+                                (distinct routed experts + shared experts) */
 } mk_stats;
 
 typedef struct mk_layer mk_layer;
@@ -192,6 +195,7 @@ int mk_decode_step(mk_layer* layer, const float* hidden_in, int T, const mk_kv_c
  * [T][n_experts], 6 = selected experts int32 [T][top_k], 7 = gates [T][top_k].
  * Valid only after a step on this layer and before another layer reuses the workspace. */
 int mk_debug_tap(mk_layer* layer, int tap, void* host_dst, size_t bytes, void* stream);
+/* Synchronous: reads the device counters of this layer's state. */
 int mk_get_stats(const mk_layer* layer, mk_stats* out);
 /* Enables per-workgroup phase timestamps (written into the layer state). */
 int mk_set_trace(mk_layer* layer, int enabled);
