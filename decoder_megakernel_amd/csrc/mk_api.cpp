@@ -78,10 +78,13 @@ int check_cfg(const mk_layer_config* c) {
   const long long xb = align256((size_t)kMaxT * (dmax + kXPad) * es);
   const long long lds_router = 2 * xb + 2 * kWaves * 64 * 4 * 4;
   const long long lds_route = xb + 32768 + (long long)kMaxT * D.E * 4 + 3 * kMaxT * kMaxTopK * 4 +
-                              (kMaxT * kMaxTopK + 8) * 4 + (long long)D.E * 4 + 16;
+                              (kMaxT * kMaxTopK + 8) * 4 + (long long)D.E * 4 + 16 + (kMaxT * kMaxTopK + 8) * 8;
   const long long lds_att = std::max((long long)kWaves * 16 * (D.dc + 8) * es + 16LL * (D.kvw + 8) * es,
                                      4LL * 16 * D.dc * 4 + 4 * 16 * 2 * 4);
   const long long lim = kLdsBytes - 1024;
+  // the down projection stages two experts' activations below the routing tables
+  if (2LL * kMaxT * (D.f + kXPad) * es > xb + 32768)
+    return fail(MK_ERR_UNSUPPORTED_SHAPE, "d_ff too large for the LDS plan");
   if (lds_router > lim || lds_route > lim || lds_att > lim)
     return fail(MK_ERR_UNSUPPORTED_SHAPE, "shape exceeds the LDS plan (router %lld, route %lld, attention %lld > %lld bytes)",
                 lds_router, lds_route, lds_att, lim);
@@ -116,14 +119,18 @@ int packed_bytes(const mk_layer_config* c, int tensor, size_t* out) {
   return MK_OK;
 }
 
-// choose the k-split S (a divisor of KT) that minimises the largest per-workgroup tile count
+// Choose the k-split S (a divisor of KT leaving >= 2 tiles per wave per unit)
+// that minimises the busiest workgroup's time: units x (tile slots per wave +
+// a fixed per-unit cost of about two tile slots for the reduction).
 int choose_split(int RT, int KT, int nwg) {
   int best = 1;
   long long best_cost = -1;
-  for (int S = 1; S <= KT && S <= 64; ++S) {
+  for (int S = 1; S <= KT; ++S) {
     if (KT % S) continue;
+    const int NT = KT / S;
+    if (NT < 2 * kWaves && S > 1) break;
     const long long U = (long long)RT * S;
-    const long long cost = ((U + nwg - 1) / nwg) * (KT / S);
+    const long long cost = ((U + nwg - 1) / nwg) * ((NT + kWaves - 1) / kWaves + 2);
     if (best_cost < 0 || cost < best_cost) { best = S; best_cost = cost; }
   }
   return best;
@@ -160,7 +167,8 @@ int device_info(int dev, DevInfo* di, LayerKernelFn fn) {
 }
 
 struct WsLayout {
-  size_t qkv_part, qrope, qabs, att_part, att_ml, z, o, hp, logit_part, route_sel, route_gate, logits, hbuf, ybuf, total;
+  size_t qkv_part, qrope, qabs, att_part, att_ml, z, o, hp, logit_part, route_sel, route_gate, logits, hbuf, ybuf, dummy,
+      total;
 };
 struct StLayout {
   size_t bar, att_cnt, experts, trace, total;
@@ -188,6 +196,7 @@ WsLayout ws_layout(const Dims& D, const Schedule& s) {
   w.logits = take((size_t)T * D.E * 4);
   w.hbuf = take((size_t)slots * T * D.f * 4);
   w.ybuf = take((size_t)slots * T * D.d * 4);
+  w.dummy = take(32768);
   w.total = off;
   return w;
 }
@@ -249,6 +258,7 @@ struct mk_model {
   float* best_val;
   int32_t* best_idx;
   uint32_t* counter;
+  const uint8_t* dummy;
   int nwg_head;
 };
 
@@ -448,6 +458,7 @@ int mk_layer_init(const mk_layer_config* cfg, const mk_layer_weights* w, void* s
   p.logits = (float*)(ws + L->wl.logits);
   p.hbuf = (float*)(ws + L->wl.hbuf);
   p.ybuf = (float*)(ws + L->wl.ybuf);
+  p.dummy = (const uint8_t*)(ws + L->wl.dummy);
   p.bar = (BarrierState*)(L->state + L->sl.bar);
   p.att_cnt = (uint32_t*)(L->state + L->sl.att_cnt);
   p.trace = nullptr;
@@ -616,7 +627,7 @@ int mk_pack_head(int32_t vocab, int32_t d_model, const uint16_t* src_bf16, void*
 }
 
 struct ModelStLayout {
-  size_t len, counter, best_val, best_idx, total;
+  size_t len, counter, best_val, best_idx, dummy, total;
 };
 static ModelStLayout model_layout(int nwg) {
   ModelStLayout l;
@@ -626,6 +637,7 @@ static ModelStLayout model_layout(int nwg) {
   l.counter = take(4);
   l.best_val = take((size_t)nwg * 8 * 4);
   l.best_idx = take((size_t)nwg * 8 * 4);
+  l.dummy = take(32768);
   l.total = off;
   return l;
 }
@@ -693,6 +705,7 @@ int mk_model_init(mk_layer* const* layers, int32_t n_layers, const uint16_t* emb
   m->counter = (uint32_t*)(m->state + ml.counter);
   m->best_val = (float*)(m->state + ml.best_val);
   m->best_idx = (int32_t*)(m->state + ml.best_idx);
+  m->dummy = (const uint8_t*)(m->state + ml.dummy);
   m->nwg_head = nwg;
   hipError_t e = hipMemset(m->state, 0, ml.total);
   if (e == hipSuccess) e = hipDeviceSynchronize();
@@ -732,7 +745,7 @@ int mk_model_step(mk_model* m, int32_t* tokens_dev, int T, const int32_t* next_d
   float* hf = (m->n_layers & 1) ? h1 : h0;
   rc = launch_head(m->head, m->V, d, m->gamma_f, m->layers[0]->cfg.rms_eps, hf, T, logits_dev, m->best_val,
                    m->best_idx, m->counter, tokens_dev, next_drafts_dev, argmax_dev, committed_dev, m->kv_len,
-                   m->nwg_head, s);
+                   m->dummy, m->nwg_head, s);
   if (rc) return fail(MK_ERR_HIP, "head launch failed");
   return MK_OK;
 }

@@ -82,6 +82,7 @@ struct LayerParams {
   float* logits;           // [T][E] (written by workgroup 0)
   float* hbuf;             // [slots][T][f]
   float* ybuf;             // [slots][T][d]
+  const uint8_t* dummy;    // 32 KiB scratch read by the streams' last (discarded) prefetch
   // state
   BarrierState* bar;
   uint32_t* att_cnt;       // [max query tiles]

@@ -140,11 +140,14 @@ __device__ __forceinline__ bool grid_barrier(const LayerParams& p, int idx, int*
 // A "unit" is 16 output rows times a range of NT weight tiles.  The 8 waves of
 // the workgroup split the unit's tiles (wave w takes tiles w, w+8, ...), each
 // accumulates a 16x16 MFMA block, and the partial blocks are summed in LDS in
-// wave order (deterministic).  Loads run D tiles ahead across unit boundaries.
-// Src provides: tile(u, t) -> const uint8_t*, bptr(u, t) -> B-operand pointer
-// for this lane, scale(u, t) (fp8 only), and for DUAL units a second tile
-// stream (W3 beside W1) at tile(u, t) + 1024 with scale2(u, t).
-// Epi(u, row, col, v[, v2]) is called for every row < 16 and col < T.
+// wave order (deterministic).  Every wave keeps D tile loads in flight (16 KiB
+// per wave, the depth this GPU needs to approach its streaming bandwidth) and
+// the stream runs on across unit boundaries.
+// Src provides: base(u) -> first byte of unit u's tile 0 (tiles are `stride`
+// bytes apart; for DUAL units the second matrix's tile sits 1024 bytes after
+// the first), bbase(u) -> this lane's B-operand pointer for tile 0 of unit u,
+// and for fp8 sbase(u) / sbase2(u) -> the unit's row of 128x128 block scales.
+// Epi(u, row, col, v, v2) is called for every row < 16 and col < T.
 template <int FMT, bool DUAL>
 struct UnitRed {
   static constexpr int kFloats = kWaves * 64 * 4 * (DUAL ? 2 : 1);
@@ -155,25 +158,55 @@ struct UnitRed {
 // keeps ~16 mantissa bits of an fp32 activation (used for the router logits).
 template <int FMT, bool DUAL, bool HILO, class Src, class Epi>
 __device__ __forceinline__ void run_units(int u0, int u1, int NT, int T, const Src& src, const Epi& epi, float* red) {
+  constexpr int D = DUAL ? 8 : 16;
+  constexpr int TK = tile_k(FMT);
+  constexpr long long STRIDE = DUAL ? 2048 : 1024;
   const int w = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int c = (NT + kWaves - 1) / kWaves;  // tile slots per wave per unit
-  const int total = (u1 - u0) * c;
+  const int nu = u1 - u0;
+  const int total = nu * c;
   if (total <= 0) return;
-  constexpr int D = 8;
   u32x4 buf[D];
   u32x4 buf2[D];
-  auto issue = [&](int q, int r) {
-    int uu = q / c, j = q - uu * c, t = w + kWaves * j;
+  float sc[D], sc2[D];
+  // issue cursor (fp8 block scales travel with their tiles)
+  int iu = 0, ij = 0;
+  const uint8_t* ib = src.base(u0) + lane * 16;
+  const float* isp = nullptr;
+  const float* isp2 = nullptr;
+  if constexpr (FMT == MK_FMT_FP8_B128) {
+    isp = src.sbase(u0);
+    if constexpr (DUAL) isp2 = src.sbase2(u0);
+  }
+  auto issue = [&](int r) {
+    const int t = w + kWaves * ij;
     if (t < NT) {
-      const uint8_t* tp = src.tile(u0 + uu, t) + lane * 16;
+      const uint8_t* tp = ib + (long long)t * STRIDE;
       buf[r] = ld_stream16(tp);
       if constexpr (DUAL) buf2[r] = ld_stream16(tp + 1024);
+      if constexpr (FMT == MK_FMT_FP8_B128) {
+        sc[r] = isp[(t * TK) >> 7];
+        if constexpr (DUAL) sc2[r] = isp2[(t * TK) >> 7];
+      }
+    }
+    if (++ij == c) {
+      ij = 0;
+      if (++iu < nu) {
+        ib = src.base(u0 + iu) + lane * 16;
+        if constexpr (FMT == MK_FMT_FP8_B128) {
+          isp = src.sbase(u0 + iu);
+          if constexpr (DUAL) isp2 = src.sbase2(u0 + iu);
+        }
+      }
     }
   };
 #pragma unroll
   for (int r = 0; r < D; ++r)
-    if (r < total) issue(r, r);
+    if (r < total) issue(r);
+  // consume cursor
+  int cu = 0, cj = 0;
+  const typename Act<FMT>::T* bp0 = src.bbase(u0);
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   f32x4 acc2 = {0.f, 0.f, 0.f, 0.f};
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
@@ -182,16 +215,15 @@ __device__ __forceinline__ void run_units(int u0, int u1, int NT, int T, const S
     for (int r = 0; r < D; ++r) {
       const int q = q0 + r;
       if (q < total) {
-        const int uu = q / c, j = q - uu * c, t = w + kWaves * j;
+        const int t = w + kWaves * cj;
         if (t < NT) {
-          const auto* bp = src.bptr(u0 + uu, t);
+          const auto* bp = bp0 + t * TK;
           if constexpr (FMT == MK_FMT_FP8_B128) {
-            f32x4 tmp = tile_mma<FMT>(buf[r], bp, zero);
-            const float s = src.scale(u0 + uu, t);
-            acc += tmp * s;
+            const f32x4 tmp = tile_mma<FMT>(buf[r], bp, zero);
+            acc += tmp * sc[r];
             if constexpr (DUAL) {
-              f32x4 tmp2 = tile_mma<FMT>(buf2[r], bp, zero);
-              acc2 += tmp2 * src.scale2(u0 + uu, t);
+              const f32x4 tmp2 = tile_mma<FMT>(buf2[r], bp, zero);
+              acc2 += tmp2 * sc2[r];
             }
           } else {
             acc = tile_mma<FMT>(buf[r], bp, acc);
@@ -199,10 +231,11 @@ __device__ __forceinline__ void run_units(int u0, int u1, int NT, int T, const S
             if constexpr (DUAL) acc2 = tile_mma<FMT>(buf2[r], bp, acc2);
           }
         }
-        if (q + D < total) issue(q + D, r);
-        if (j == c - 1) {
+        if (q + D < total) issue(r);
+        if (++cj == c) {
           // unit boundary: deterministic reduction over the 8 waves
-          float* rb = red + ((uu & 1) ? UnitRed<FMT, DUAL>::kFloats : 0);
+          cj = 0;
+          float* rb = red + ((cu & 1) ? UnitRed<FMT, DUAL>::kFloats : 0);
           *reinterpret_cast<f32x4*>(rb + (w * 64 + lane) * 4) = acc;
           if constexpr (DUAL) *reinterpret_cast<f32x4*>(rb + kWaves * 64 * 4 + (w * 64 + lane) * 4) = acc2;
           __syncthreads();
@@ -216,16 +249,258 @@ __device__ __forceinline__ void run_units(int u0, int u1, int NT, int T, const S
                 v += rb[(ww * 64 + l) * 4 + e];
                 if constexpr (DUAL) v2 += rb[kWaves * 64 * 4 + (ww * 64 + l) * 4 + e];
               }
-              epi(u0 + uu, row, col, v, v2);
+              epi(u0 + cu, row, col, v, v2);
             }
           }
           acc = zero;
           acc2 = zero;
+          if (++cu < nu) bp0 = src.bbase(u0 + cu);
         }
       }
     }
   }
   __syncthreads();
+}
+
+
+// Wave-level units: each wave of the workgroup owns whole units (16 rows, all
+// NT tiles) -- units u0 + w, u0 + w + 8, ... of the workgroup's range -- so no
+// cross-wave reduction or workgroup barrier is needed; the D-deep load ring runs
+// across the wave's units.  Epi(u, row, col, v, v2) is called per lane for the
+// four rows it holds (row = 4*(lane/16) + e, col = lane % 16 < T).
+template <int FMT, bool DUAL, class Src, class Epi>
+__device__ __forceinline__ void run_wave_units(int u0, int u1, int NT, int T, const Src& src, const Epi& epi) {
+  constexpr int D = DUAL ? 8 : 16;
+  constexpr int TK = tile_k(FMT);
+  constexpr long long STRIDE = DUAL ? 2048 : 1024;
+  const int w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int nu = u1 - u0 > w ? (u1 - u0 - w + kWaves - 1) / kWaves : 0;   // units of this wave
+  const int total = nu * NT;
+  if (total <= 0) return;
+  u32x4 buf[D];
+  u32x4 buf2[D];
+  float sc[D], sc2[D];
+  int iu = 0, it = 0;
+  const uint8_t* ib = src.base(u0 + w) + lane * 16;
+  const float* isp = nullptr;
+  const float* isp2 = nullptr;
+  if constexpr (FMT == MK_FMT_FP8_B128) {
+    isp = src.sbase(u0 + w);
+    if constexpr (DUAL) isp2 = src.sbase2(u0 + w);
+  }
+  auto issue = [&](int r) {
+    const uint8_t* tp = ib + (long long)it * STRIDE;
+    buf[r] = ld_stream16(tp);
+    if constexpr (DUAL) buf2[r] = ld_stream16(tp + 1024);
+    if constexpr (FMT == MK_FMT_FP8_B128) {
+      sc[r] = isp[(it * TK) >> 7];
+      if constexpr (DUAL) sc2[r] = isp2[(it * TK) >> 7];
+    }
+    if (++it == NT) {
+      it = 0;
+      if (++iu < nu) {
+        const int u = u0 + w + kWaves * iu;
+        ib = src.base(u) + lane * 16;
+        if constexpr (FMT == MK_FMT_FP8_B128) {
+          isp = src.sbase(u);
+          if constexpr (DUAL) isp2 = src.sbase2(u);
+        }
+      }
+    }
+  };
+#pragma unroll
+  for (int r = 0; r < D; ++r)
+    if (r < total) issue(r);
+  int cu = 0, ct = 0;
+  const typename Act<FMT>::T* bp0 = src.bbase(u0 + w);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  f32x4 acc2 = {0.f, 0.f, 0.f, 0.f};
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  for (int q0 = 0; q0 < total; q0 += D) {
+#pragma unroll
+    for (int r = 0; r < D; ++r) {
+      const int q = q0 + r;
+      if (q < total) {
+        const auto* bp = bp0 + ct * TK;
+        if constexpr (FMT == MK_FMT_FP8_B128) {
+          const f32x4 tmp = tile_mma<FMT>(buf[r], bp, zero);
+          acc += tmp * sc[r];
+          if constexpr (DUAL) {
+            const f32x4 tmp2 = tile_mma<FMT>(buf2[r], bp, zero);
+            acc2 += tmp2 * sc2[r];
+          }
+        } else {
+          acc = tile_mma<FMT>(buf[r], bp, acc);
+          if constexpr (DUAL) acc2 = tile_mma<FMT>(buf2[r], bp, acc2);
+        }
+        if (q + D < total) issue(r);
+        if (++ct == NT) {
+          ct = 0;
+          const int u = u0 + w + kWaves * cu;
+          const int col = lane & 15, g = lane >> 4;
+          if (col < T) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) epi(u, 4 * g + e, col, acc[e], acc2[e]);
+          }
+          acc = zero;
+          acc2 = zero;
+          if (++cu < nu) bp0 = src.bbase(u0 + w + kWaves * cu);
+        }
+      }
+    }
+  }
+}
+
+
+// Branch-free streaming engine.  A wave's work is a sequence of chunks of D
+// contiguous tiles; a chunk lies inside one unit.  WG mode: every unit's NT
+// tiles are cut into 8 contiguous slices, wave w takes slice w of each unit of
+// the workgroup's range, and unit results are reduced across waves in LDS.
+// Wave mode: wave w owns units u0+w, u0+w+8, ... whole.  The loop body is
+// straight-line (the next chunk's loads are issued unconditionally, the very
+// last prefetch reads `dummy`, an L2-resident scratch block), so the compiler
+// can keep exact s_waitcnt counts and D loads stay in flight.
+// Requires: slice (NT/8 in WG mode, NT in wave mode) a multiple of D.
+template <int FMT, bool DUAL, bool HILO, bool WG, int D, class Src, class Epi>
+__device__ __forceinline__ void run_stream(int u0, int u1, int NT, int T, const Src& src, const Epi& epi, float* red,
+                                           const uint8_t* dummy) {
+  constexpr int TK = tile_k(FMT);
+  constexpr long long STRIDE = DUAL ? 2048 : 1024;
+  const int w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int slice = WG ? NT / kWaves : NT;
+  const int cps = slice / D;
+  const int ustep = WG ? 1 : kWaves;
+  const int ufirst = WG ? u0 : u0 + w;
+  const int nu = WG ? (u1 - u0) : (u1 - u0 > w ? (u1 - u0 - w + kWaves - 1) / kWaves : 0);
+  const int nchunks = nu * cps;
+  if (nchunks <= 0) return;
+  const int toff = WG ? w * slice : 0;
+  const float* dsc = reinterpret_cast<const float*>(dummy);
+  u32x4 buf[D];
+  u32x4 buf2[D];
+  float sc[D], sc2[D];
+  auto load_chunk = [&](const uint8_t* cbase, const float* sp, const float* sp2, int tfirst) {
+#pragma unroll
+    for (int r = 0; r < D; ++r) {
+      buf[r] = ld_stream16(cbase + r * STRIDE);
+      if constexpr (DUAL) buf2[r] = ld_stream16(cbase + r * STRIDE + 1024);
+      if constexpr (FMT == MK_FMT_FP8_B128) {
+        sc[r] = sp[((tfirst + r) * TK) >> 7];
+        if constexpr (DUAL) sc2[r] = sp2[((tfirst + r) * TK) >> 7];
+      }
+    }
+  };
+  {
+    const int u = ufirst;
+    const float* sp = nullptr;
+    const float* sp2 = nullptr;
+    if constexpr (FMT == MK_FMT_FP8_B128) {
+      sp = src.sbase(u);
+      if constexpr (DUAL) sp2 = src.sbase2(u);
+    }
+    load_chunk(src.base(u) + lane * 16 + (long long)toff * STRIDE, sp, sp2, toff);
+  }
+  int cu = 0, cc = 0;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  f32x4 acc2 = {0.f, 0.f, 0.f, 0.f};
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < nchunks; ++k) {
+    int ncc = cc + 1, ncu = cu;
+    if (ncc == cps) {
+      ncc = 0;
+      ++ncu;
+    }
+    const bool has_next = k + 1 < nchunks;
+    const int un = ufirst + ncu * ustep;
+    const int tn = toff + ncc * D;
+    const uint8_t* nb = has_next ? src.base(un) + lane * 16 + (long long)tn * STRIDE : dummy + lane * 16;
+    const float* nsp = dsc;
+    const float* nsp2 = dsc;
+    if constexpr (FMT == MK_FMT_FP8_B128) {
+      if (has_next) {
+        nsp = src.sbase(un);
+        if constexpr (DUAL) nsp2 = src.sbase2(un);
+      }
+    }
+    const int tc = toff + cc * D;
+    const auto* bp = src.bbase(ufirst + cu * ustep) + tc * TK;
+#pragma unroll
+    for (int r = 0; r < D; ++r) {
+      if constexpr (FMT == MK_FMT_FP8_B128) {
+        const f32x4 tmp = tile_mma<FMT>(buf[r], bp + r * TK, zero);
+        acc += tmp * sc[r];
+        if constexpr (DUAL) {
+          const f32x4 tmp2 = tile_mma<FMT>(buf2[r], bp + r * TK, zero);
+          acc2 += tmp2 * sc2[r];
+        }
+      } else {
+        acc = tile_mma<FMT>(buf[r], bp + r * TK, acc);
+        if constexpr (HILO) acc = tile_mma<FMT>(buf[r], bp + r * TK + src.lo_off, acc);
+        if constexpr (DUAL) acc2 = tile_mma<FMT>(buf2[r], bp + r * TK, acc2);
+      }
+      buf[r] = ld_stream16(nb + r * STRIDE);
+      if constexpr (DUAL) buf2[r] = ld_stream16(nb + r * STRIDE + 1024);
+      if constexpr (FMT == MK_FMT_FP8_B128) {
+        sc[r] = nsp[has_next ? (((tn + r) * TK) >> 7) : 0];
+        if constexpr (DUAL) sc2[r] = nsp2[has_next ? (((tn + r) * TK) >> 7) : 0];
+      }
+    }
+    if (ncc == 0) {
+      const int u = ufirst + cu * ustep;
+      if constexpr (WG) {
+        float* rb = red + ((cu & 1) ? UnitRed<FMT, DUAL>::kFloats : 0);
+        *reinterpret_cast<f32x4*>(rb + (w * 64 + lane) * 4) = acc;
+        if constexpr (DUAL) *reinterpret_cast<f32x4*>(rb + kWaves * 64 * 4 + (w * 64 + lane) * 4) = acc2;
+        __syncthreads();
+        if (threadIdx.x < 256) {
+          const int col = threadIdx.x & 15, row = threadIdx.x >> 4;
+          const int l = (row >> 2) * 16 + col, e = row & 3;
+          if (col < T) {
+            float v = 0.f, v2 = 0.f;
+#pragma unroll
+            for (int ww = 0; ww < kWaves; ++ww) {
+              v += rb[(ww * 64 + l) * 4 + e];
+              if constexpr (DUAL) v2 += rb[kWaves * 64 * 4 + (ww * 64 + l) * 4 + e];
+            }
+            epi(u, row, col, v, v2);
+          }
+        }
+      } else {
+        const int col = lane & 15, g = lane >> 4;
+        if (col < T) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) epi(u, 4 * g + e, col, acc[e], acc2[e]);
+        }
+      }
+      acc = zero;
+      acc2 = zero;
+    }
+    cc = ncc;
+    cu = ncu;
+  }
+  if constexpr (WG) __syncthreads();
+}
+
+// Dispatch: the branch-free engine when the slice length allows, else the
+// general engines (ragged shapes).
+template <int FMT, bool DUAL, bool HILO, class Src, class Epi>
+__device__ __forceinline__ void stream_units_wg(int u0, int u1, int NT, int T, const Src& src, const Epi& epi,
+                                                float* red, const uint8_t* dummy) {
+  const int slice = NT % kWaves == 0 ? NT / kWaves : 0;
+  constexpr int DMAX = DUAL ? 8 : 16;
+  if (slice > 0 && slice % DMAX == 0) run_stream<FMT, DUAL, HILO, true, DMAX>(u0, u1, NT, T, src, epi, red, dummy);
+  else if (slice > 0 && slice % 4 == 0) run_stream<FMT, DUAL, HILO, true, 4>(u0, u1, NT, T, src, epi, red, dummy);
+  else if (slice > 0 && slice % 2 == 0) run_stream<FMT, DUAL, HILO, true, 2>(u0, u1, NT, T, src, epi, red, dummy);
+  else run_units<FMT, DUAL, HILO>(u0, u1, NT, T, src, epi, red);
+}
+template <int FMT, bool DUAL, class Src, class Epi>
+__device__ __forceinline__ void stream_units_wave(int u0, int u1, int NT, int T, const Src& src, const Epi& epi,
+                                                  const uint8_t* dummy) {
+  constexpr int DMAX = DUAL ? 8 : 16;
+  if (NT % DMAX == 0) run_stream<FMT, DUAL, false, false, DMAX>(u0, u1, NT, T, src, epi, nullptr, dummy);
+  else run_wave_units<FMT, DUAL>(u0, u1, NT, T, src, epi);
 }
 
 }  // namespace mk

@@ -55,29 +55,78 @@ template <class A> __device__ inline A to_act(float v);
 template <> __device__ inline float to_act<float>(float v) { return v; }
 template <> __device__ inline __bf16 to_act<__bf16>(float v) { return (__bf16)v; }
 
-// x[t][k] = (h[t][k] * rsqrt(mean(h[t]^2) + eps)) * gamma[k] -> LDS (activation type).
-// For `lo` != null also writes the bf16 remainder x - bf16(x) (router operand).
-template <class A>
-__device__ __forceinline__ void rmsnorm_to_lds(const float* h, const float* gamma, int T, int d, float eps, A* xs,
-                               A* lo, int XS, char* smem) {
-  float* rs = reinterpret_cast<float*>(smem + kMiscOff);
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  if (w < T) {
-    float ss = 0.f;
-    for (int k = lane; k < d; k += 64) {
-      float v = h[(long long)w * d + k];
-      ss += v * v;
-    }
-    ss = wave_sum(ss);
-    if (lane == 0) rs[w] = 1.0f / sqrtf(ss / (float)d + eps);
+template <class A> __device__ __forceinline__ void store4(A* dst, const f32x4& v);
+template <> __device__ __forceinline__ void store4<float>(float* dst, const f32x4& v) {
+  *reinterpret_cast<f32x4*>(dst) = v;
+}
+template <> __device__ __forceinline__ void store4<__bf16>(__bf16* dst, const f32x4& v) {
+  bf16x4 b;
+  b[0] = (__bf16)v[0]; b[1] = (__bf16)v[1]; b[2] = (__bf16)v[2]; b[3] = (__bf16)v[3];
+  *reinterpret_cast<bf16x4*>(dst) = b;
+}
+template <class A> __device__ __forceinline__ f32x4 round4(const f32x4& v);
+template <> __device__ __forceinline__ f32x4 round4<float>(const f32x4& v) { return v; }
+template <> __device__ __forceinline__ f32x4 round4<__bf16>(const f32x4& v) {
+  return f32x4{(float)(__bf16)v[0], (float)(__bf16)v[1], (float)(__bf16)v[2], (float)(__bf16)v[3]};
+}
+
+// Copies rows src[T][K] (fp32, global) into the LDS operand xs[T][XS] (activation
+// type), issuing every load of the workgroup at once (T*K <= 32768).  With NORM
+// each row is RMS-normalised on the way: x = (h * (1/sqrt(mean(h^2) + eps))) * gamma,
+// the sum of squares reduced in a fixed order.  `lo` (optional) receives the
+// bf16 remainder x - bf16(x) for the router's split operand.
+template <class A, bool NORM>
+__device__ __forceinline__ void rows_to_lds(const float* src, int T, int K, A* xs, A* lo, int XS,
+                                            const float* gamma, float eps, char* smem) {
+  constexpr int CH = 16;
+  const int n4 = K / 4, total = T * n4;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  f32x4 v[CH];
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int i = tid + c * kThreads;
+    if (i < total) v[c] = *reinterpret_cast<const f32x4*>(src + (long long)i * 4);
   }
-  __syncthreads();
-  for (int i = threadIdx.x; i < T * d; i += kThreads) {
-    const int t = i / d, k = i - t * d;
-    const float x = (h[(long long)t * d + k] * rs[t]) * gamma[k];
-    const A xa = to_act<A>(x);
-    xs[t * XS + k] = xa;
-    if (lo) lo[t * XS + k] = to_act<A>(x - (float)xa);
+  float* rs = reinterpret_cast<float*>(smem + kMiscOff);           // [kMaxT]
+  if constexpr (NORM) {
+    float* red = rs + 16;                                          // [kWaves][kMaxT]
+    float ss[kMaxT];
+#pragma unroll
+    for (int t = 0; t < kMaxT; ++t) ss[t] = 0.f;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int i = tid + c * kThreads;
+      if (i < total) {
+        const int t = i / n4;
+        const float q = v[c][0] * v[c][0] + v[c][1] * v[c][1] + v[c][2] * v[c][2] + v[c][3] * v[c][3];
+#pragma unroll
+        for (int tt = 0; tt < kMaxT; ++tt)
+          if (tt == t) ss[tt] += q;
+      }
+    }
+#pragma unroll
+    for (int tt = 0; tt < kMaxT; ++tt) {
+      const float r = wave_sum(ss[tt]);
+      if (lane == 0) red[w * kMaxT + tt] = r;
+    }
+    __syncthreads();
+    if (tid < T) {
+      float tot = 0.f;
+      for (int ww = 0; ww < kWaves; ++ww) tot += red[ww * kMaxT + tid];
+      rs[tid] = 1.0f / sqrtf(tot / (float)K + eps);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int i = tid + c * kThreads;
+    if (i < total) {
+      const int t = i / n4, k = (i - t * n4) * 4;
+      f32x4 x = v[c];
+      if constexpr (NORM) x = (x * rs[t]) * *reinterpret_cast<const f32x4*>(gamma + k);
+      store4<A>(xs + t * XS + k, x);
+      if (lo) store4<A>(lo + t * XS + k, x - round4<A>(x));
+    }
   }
   __syncthreads();
 }
@@ -99,7 +148,7 @@ __device__ __forceinline__ void phase_qkv(const LayerParams& p, char* smem) {
   LdsPlan lp(p, sizeof(A));
   A* xs = reinterpret_cast<A*>(smem);
   float* red = reinterpret_cast<float*>(smem + lp.xb);
-  rmsnorm_to_lds<A>(p.H, p.g1, T, p.d, p.eps, xs, (A*)nullptr, XS, smem);
+  rows_to_lds<A, true>(p.H, T, p.d, xs, (A*)nullptr, XS, p.g1, p.eps, smem);
   const int RTq = p.nq / 16, RTkv = (p.kvw + 15) / 16, KT = p.d / TK, S = p.sch.s_q, NT = KT / S;
   const int U = (RTq + RTkv) * S;
   int u0, u1;
@@ -108,14 +157,14 @@ __device__ __forceinline__ void phase_qkv(const LayerParams& p, char* smem) {
   const int nrow = p.nq + p.kvw;
   struct Src {
     const uint8_t* wq; const uint8_t* wd; int RTq, KT, S, NT; const A* bl;
-    __device__ const uint8_t* tile(int u, int t) const {
-      int rt = u / S, s = u - rt * S;
-      const uint8_t* base = rt < RTq ? wq + (long long)rt * KT * 1024 : wd + (long long)(rt - RTq) * KT * 1024;
-      return base + (long long)(s * NT + t) * 1024;
+    __device__ const uint8_t* base(int u) const {
+      const int rt = u / S, s = u - rt * S;
+      const uint8_t* b = rt < RTq ? wq + (long long)rt * KT * 1024 : wd + (long long)(rt - RTq) * KT * 1024;
+      return b + (long long)s * NT * 1024;
     }
-    __device__ const A* bptr(int u, int t) const { int s = u % S; return bl + (s * NT + t) * TK; }
-    __device__ float scale(int, int) const { return 1.f; }
-    __device__ float scale2(int, int) const { return 1.f; }
+    __device__ const A* bbase(int u) const { return bl + (u % S) * NT * TK; }
+    __device__ const float* sbase(int) const { return nullptr; }
+    __device__ const float* sbase2(int) const { return nullptr; }
   } src{p.wq, p.wdkv, RTq, KT, S, NT, bl};
   float* part = p.qkv_part;
   const int nq = p.nq, kvw = p.kvw;
@@ -130,7 +179,7 @@ __device__ __forceinline__ void phase_qkv(const LayerParams& p, char* smem) {
     }
     part[((long long)s * T + col) * nrow + idx] = v;
   };
-  run_units<AF, false, false>(u0, u1, NT, T, src, epi, red);
+  stream_units_wg<AF, false, false>(u0, u1, NT, T, src, epi, red, p.dummy);
 }
 
 // ------------------------------------------------------------------ P1
@@ -232,8 +281,14 @@ __device__ __forceinline__ void phase_absorb(const LayerParams& p) {
     const int h = u / RT, rt = u - h * RT;
     const uint8_t* tiles = p.wuk + (long long)u * KT * 1024 + lane * 16;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int kt = 0; kt < KT; ++kt) {
-      const u32x4 a = ld_stream16(tiles + kt * 1024);
+    u32x4 at[8];
+#pragma unroll
+    for (int kt = 0; kt < 8; ++kt)
+      if (kt < KT) at[kt] = ld_stream16(tiles + kt * 1024);
+#pragma unroll
+    for (int kt = 0; kt < 8; ++kt) {
+      if (kt >= KT) break;
+      const u32x4 a = at[kt];
       const int e0 = kt * TK + g * EPL;
       f32x4 q0 = {0.f, 0.f, 0.f, 0.f}, q1 = {0.f, 0.f, 0.f, 0.f};
       for (int s = 0; s < S; ++s) {
@@ -294,13 +349,27 @@ __device__ __forceinline__ void phase_attention(const LayerParams& p, int L, cha
     const int limit = L + tq;                          // keys 0..limit are visible
     // query tile -> LDS (shared by the 8 waves): qs[16][kvw + 8] = [q~ | rotated q^R]
     __syncthreads();
-    for (int i = threadIdx.x; i < 16 * kvw; i += kThreads) {
-      const int jq = i / kvw, dd = i - jq * kvw;
-      const int qq = min(qt * 16 + jq, NQ - 1);
-      const int tt = qq / nh, hh = qq - tt * nh;
-      const float v = dd < dc ? p.qabs[((long long)tt * nh + hh) * dc + dd]
-                              : p.qrope[((long long)tt * nh + hh) * p.dr + (dd - dc)];
-      qs[jq * QS + dd] = (E)v;
+    {
+      const int n4 = kvw / 4;
+      f32x4 qv[5];
+#pragma unroll
+      for (int c = 0; c < 5; ++c) {
+        const int i = threadIdx.x + c * kThreads;
+        if (i < 16 * n4) {
+          const int jq = i / n4, dd = (i - jq * n4) * 4;
+          const int qq = min(qt * 16 + jq, NQ - 1);
+          const float* src = dd < dc ? p.qabs + (long long)qq * dc + dd : p.qrope + (long long)qq * p.dr + (dd - dc);
+          qv[c] = *reinterpret_cast<const f32x4*>(src);
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < 5; ++c) {
+        const int i = threadIdx.x + c * kThreads;
+        if (i < 16 * n4) {
+          const int jq = i / n4, dd = (i - jq * n4) * 4;
+          store4<E>(qs + jq * QS + dd, qv[c]);
+        }
+      }
     }
     __syncthreads();
     const int k0 = s * SK, k1 = min(Lt, k0 + SK);
@@ -316,9 +385,10 @@ __device__ __forceinline__ void phase_attention(const LayerParams& p, int L, cha
       // S^T = K Q^T over the key dims; the latent part of the chunk is also
       // staged (row-major) in this wave's LDS slice for the value product
       f32x4 st = {0.f, 0.f, 0.f, 0.f};
-      constexpr int KH = (KBMAX + 1) / 2;
+      constexpr int NB = 3;                              // key-dim blocks loaded in 3 batches
+      constexpr int KH = (KBMAX + NB - 1) / NB;
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
+      for (int half = 0; half < NB; ++half) {
         u32x4 kr[KH];
 #pragma unroll
         for (int i = 0; i < KH; ++i) {
@@ -455,22 +525,45 @@ __device__ __forceinline__ void phase_attention(const LayerParams& p, int L, cha
     }
     __syncthreads();
     if (*flag) {
+      // combination weights per (split, query): exp(m_s - M) / sum_s exp(m_s - M) l_s
       const int ub = qt * s_kv;
-      for (int it = threadIdx.x; it < 16 * dc; it += kThreads) {
-        const int jq = it / dc, dd = it - jq * dc;
+      float* mm = reinterpret_cast<float*>(smem);          // [s_kv][16]
+      float* cf = mm + s_kv * 16;                          // [s_kv][16]
+      for (int i = threadIdx.x; i < s_kv * 16; i += kThreads) mm[i] = p.att_ml[((long long)ub * 16 + i) * 2];
+      for (int i = threadIdx.x; i < s_kv * 16; i += kThreads) cf[i] = p.att_ml[((long long)ub * 16 + i) * 2 + 1];
+      __syncthreads();
+      if (threadIdx.x < 16) {
+        const int jq = threadIdx.x;
+        float M = -INFINITY;
+        for (int ss = 0; ss < s_kv; ++ss) M = fmaxf(M, mm[ss * 16 + jq]);
+        float den = 0.f;
+        for (int ss = 0; ss < s_kv; ++ss) {
+          const float wgt = mm[ss * 16 + jq] == -INFINITY ? 0.f : __expf(mm[ss * 16 + jq] - M);
+          mm[ss * 16 + jq] = wgt;
+          den += wgt * cf[ss * 16 + jq];
+        }
+        for (int ss = 0; ss < s_kv; ++ss) cf[ss * 16 + jq] = mm[ss * 16 + jq] / den;
+      }
+      __syncthreads();
+      const int dq = dc / 4;
+      for (int it = threadIdx.x; it < 16 * dq; it += kThreads) {
+        const int jq = it / dq, d4 = it - jq * dq;
         const int qq = qt * 16 + jq;
         if (qq >= NQ) continue;
-        float M = -INFINITY;
-        for (int ss = 0; ss < s_kv; ++ss) M = fmaxf(M, p.att_ml[((long long)(ub + ss) * 16 + jq) * 2]);
-        float num = 0.f, den = 0.f;
-        for (int ss = 0; ss < s_kv; ++ss) {
-          const float ms = p.att_ml[((long long)(ub + ss) * 16 + jq) * 2];
-          if (ms == -INFINITY) continue;
-          const float wgt = __expf(ms - M);
-          den += wgt * p.att_ml[((long long)(ub + ss) * 16 + jq) * 2 + 1];
-          num += wgt * p.att_part[((long long)(ub + ss) * 16 + jq) * dc + dd];
+        const f32x4* zp = reinterpret_cast<const f32x4*>(p.att_part + ((long long)ub * 16 + jq) * dc) + d4;
+        const long long sstride = 16LL * dc / 4;
+        f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0, a2 = a0, a3 = a0;
+        int ss = 0;
+        for (; ss + 4 <= s_kv; ss += 4) {
+          const f32x4 z0 = zp[(ss + 0) * sstride], z1 = zp[(ss + 1) * sstride];
+          const f32x4 z2 = zp[(ss + 2) * sstride], z3 = zp[(ss + 3) * sstride];
+          a0 += z0 * cf[(ss + 0) * 16 + jq];
+          a1 += z1 * cf[(ss + 1) * 16 + jq];
+          a2 += z2 * cf[(ss + 2) * 16 + jq];
+          a3 += z3 * cf[(ss + 3) * 16 + jq];
         }
-        p.z[(long long)qq * dc + dd] = num / den;
+        for (; ss < s_kv; ++ss) a0 += zp[ss * sstride] * cf[ss * 16 + jq];
+        *reinterpret_cast<f32x4*>(p.z + (long long)qq * dc + d4 * 4) = (a0 + a1) + (a2 + a3);
       }
     }
     __syncthreads();
@@ -491,16 +584,20 @@ __device__ __forceinline__ void phase_uv(const LayerParams& p) {
     const uint8_t* tiles = p.wuv + (long long)u * KT * 1024 + lane * 16;
     const float* zr = p.z + ((long long)jj * p.nh + h) * p.dc + g * EPL;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    int kt = 0;
-    for (; kt + 4 <= KT; kt += 4) {
-      u32x4 a0 = ld_stream16(tiles + (kt + 0) * 1024), a1 = ld_stream16(tiles + (kt + 1) * 1024);
-      u32x4 a2 = ld_stream16(tiles + (kt + 2) * 1024), a3 = ld_stream16(tiles + (kt + 3) * 1024);
-      acc = tile_mma_reg<AF>(a0, load_b<AF>(zr + (kt + 0) * TK), acc);
-      acc = tile_mma_reg<AF>(a1, load_b<AF>(zr + (kt + 1) * TK), acc);
-      acc = tile_mma_reg<AF>(a2, load_b<AF>(zr + (kt + 2) * TK), acc);
-      acc = tile_mma_reg<AF>(a3, load_b<AF>(zr + (kt + 3) * TK), acc);
+    constexpr int KB = 8;
+    for (int k0 = 0; k0 < KT; k0 += KB) {
+      u32x4 at[KB];
+      typename BReg<AF>::T bt[KB];
+#pragma unroll
+      for (int i = 0; i < KB; ++i)
+        if (k0 + i < KT) {
+          at[i] = ld_stream16(tiles + (k0 + i) * 1024);
+          bt[i] = load_b<AF>(zr + (k0 + i) * TK);
+        }
+#pragma unroll
+      for (int i = 0; i < KB; ++i)
+        if (k0 + i < KT) acc = tile_mma_reg<AF>(at[i], bt[i], acc);
     }
-    for (; kt < KT; ++kt) acc = tile_mma_reg<AF>(ld_stream16(tiles + kt * 1024), load_b<AF>(zr + kt * TK), acc);
     if (j < T) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) p.o[(long long)j * p.nh * p.dh + h * p.dh + rt * 16 + 4 * g + e] = acc[e];
@@ -521,18 +618,14 @@ __device__ __forceinline__ void phase_wo(const LayerParams& p, char* smem) {
   int u0, u1;
   split_range(U, gridDim.x, blockIdx.x, u0, u1);
   if (u1 <= u0) return;
-  for (int i = threadIdx.x; i < T * K; i += kThreads) {
-    const int t = i / K, k = i - t * K;
-    xs[t * XS + k] = to_act<A>(p.o[i]);
-  }
-  __syncthreads();
+  rows_to_lds<A, false>(p.o, T, K, xs, (A*)nullptr, XS, nullptr, 0.f, smem);
   const A* bl = b_lane<A>(xs, XS, T, TK);
   struct Src {
     const uint8_t* wo; int KT; const A* bl;
-    __device__ const uint8_t* tile(int u, int t) const { return wo + ((long long)u * KT + t) * 1024; }
-    __device__ const A* bptr(int, int t) const { return bl + t * TK; }
-    __device__ float scale(int, int) const { return 1.f; }
-    __device__ float scale2(int, int) const { return 1.f; }
+    __device__ const uint8_t* base(int u) const { return wo + (long long)u * KT * 1024; }
+    __device__ const A* bbase(int) const { return bl; }
+    __device__ const float* sbase(int) const { return nullptr; }
+    __device__ const float* sbase2(int) const { return nullptr; }
   } src{p.wo, KT, bl};
   const float* H = p.H;
   float* hp = p.hp;
@@ -541,7 +634,7 @@ __device__ __forceinline__ void phase_wo(const LayerParams& p, char* smem) {
     const long long i = (long long)col * d + u * 16 + row;
     hp[i] = H[i] + v;
   };
-  run_units<AF, false, false>(u0, u1, KT, T, src, epi, red);
+  stream_units_wg<AF, false, false>(u0, u1, KT, T, src, epi, red, p.dummy);
 }
 
 // ------------------------------------------------------------------ P5 router
@@ -554,7 +647,7 @@ __device__ __forceinline__ void phase_router(const LayerParams& p, char* smem) {
   A* xs = reinterpret_cast<A*>(smem);
   A* xlo = AF == MK_FMT_F32 ? (A*)nullptr : reinterpret_cast<A*>(smem + lp.xb);
   float* red = reinterpret_cast<float*>(smem + 2 * lp.xb);
-  rmsnorm_to_lds<A>(p.hp, p.g2, T, p.d, p.eps, xs, xlo, XS, smem);
+  rows_to_lds<A, true>(p.hp, T, p.d, xs, xlo, XS, p.g2, p.eps, smem);
   const int KT = p.d / TK, S = p.sch.s_r, NT = KT / S, RT = p.E / 16;
   const int U = RT * S;
   int u0, u1;
@@ -562,13 +655,13 @@ __device__ __forceinline__ void phase_router(const LayerParams& p, char* smem) {
   const A* bl = b_lane<A>(xs, XS, T, TK);
   struct Src {
     const uint8_t* wr; int KT, S, NT; const A* bl; long long lo_off;
-    __device__ const uint8_t* tile(int u, int t) const {
-      int rt = u / S, s = u - rt * S;
-      return wr + ((long long)rt * KT + s * NT + t) * 1024;
+    __device__ const uint8_t* base(int u) const {
+      const int rt = u / S, s = u - rt * S;
+      return wr + ((long long)rt * KT + s * NT) * 1024;
     }
-    __device__ const A* bptr(int u, int t) const { return bl + (u % S * NT + t) * TK; }
-    __device__ float scale(int, int) const { return 1.f; }
-    __device__ float scale2(int, int) const { return 1.f; }
+    __device__ const A* bbase(int u) const { return bl + (u % S) * NT * TK; }
+    __device__ const float* sbase(int) const { return nullptr; }
+    __device__ const float* sbase2(int) const { return nullptr; }
   } src{p.wr, KT, S, NT, bl, (long long)(lp.xb / (int)sizeof(A))};
   float* lp_out = p.logit_part;
   const int E = p.E;
@@ -576,7 +669,7 @@ __device__ __forceinline__ void phase_router(const LayerParams& p, char* smem) {
     int rt = u / S, s = u - rt * S;
     lp_out[((long long)s * T + col) * E + rt * 16 + row] = v;
   };
-  run_units<AF, false, AF != MK_FMT_F32>(u0, u1, NT, T, src, epi, red);
+  stream_units_wg<AF, false, AF != MK_FMT_F32>(u0, u1, NT, T, src, epi, red, p.dummy);
 }
 
 // ------------------------------------------------------------------ P6 routing + gate/up
@@ -588,6 +681,7 @@ struct RouteLds {
   int* slots;      // [slots]
   int* flags;      // [E]
   int* nslots;     // [1]
+  const uint8_t** blk;   // [slots] packed expert block of each slot
 };
 __device__ __forceinline__ RouteLds route_lds(const LayerParams& p, char* smem, int xb) {
   char* b = smem + xb + 32768;
@@ -605,6 +699,8 @@ __device__ __forceinline__ RouteLds route_lds(const LayerParams& p, char* smem, 
   r.flags = reinterpret_cast<int*>(b);
   b += (size_t)p.E * 4;
   r.nslots = reinterpret_cast<int*>(b);
+  b += 16;
+  r.blk = reinterpret_cast<const uint8_t**>(b);
   return r;
 }
 
@@ -687,6 +783,7 @@ __device__ __forceinline__ void route(const LayerParams& p, const RouteLds& r) {
     const int t = threadIdx.x / K, k = threadIdx.x - t * K;
     r.slot_of[t * kMaxTopK + k] = r.flags[r.sel[t * kMaxTopK + k]] - 1;
   }
+  if (threadIdx.x < *r.nslots) r.blk[threadIdx.x] = p.experts[r.slots[threadIdx.x]];
   __syncthreads();
   if (blockIdx.x == 0) {
     for (int i = threadIdx.x; i < T * K; i += kThreads) {
@@ -720,27 +817,24 @@ __device__ __forceinline__ void phase_route_gateup(const LayerParams& p, char* s
   const A* bl = b_lane<A>(xs, XS, T, TK);
   const int nbk = (p.d + 127) / 128;
   struct Src {
-    const uint8_t* const* ex; const int* slots; int RT, KT, nbk; const A* bl;
-    long long sc_off, sc3_off;
-    __device__ const uint8_t* tile(int u, int t) const {
+    const uint8_t* const* blk; int RT, KT, nbk; const A* bl; long long sc_off, sc3_off;
+    __device__ const uint8_t* base(int u) const {
       const int sl = u / RT, rt = u - sl * RT;
-      return ex[slots[sl]] + ((long long)rt * KT + t) * 2048;
+      return blk[sl] + (long long)rt * KT * 2048;
     }
-    __device__ const A* bptr(int, int t) const { return bl + t * TK; }
-    __device__ float scale(int u, int t) const {
+    __device__ const A* bbase(int) const { return bl; }
+    __device__ const float* sbase(int u) const {
       const int sl = u / RT, rt = u - sl * RT;
-      const float* s = reinterpret_cast<const float*>(ex[slots[sl]] + sc_off);
-      return s[(rt >> 3) * nbk + (t * TK >> 7)];
+      return reinterpret_cast<const float*>(blk[sl] + sc_off) + (rt >> 3) * nbk;
     }
-    __device__ float scale2(int u, int t) const {
+    __device__ const float* sbase2(int u) const {
       const int sl = u / RT, rt = u - sl * RT;
-      const float* s = reinterpret_cast<const float*>(ex[slots[sl]] + sc3_off);
-      return s[(rt >> 3) * nbk + (t * TK >> 7)];
+      return reinterpret_cast<const float*>(blk[sl] + sc3_off) + (rt >> 3) * nbk;
     }
   };
   const long long nsc13 = (long long)((p.f + 127) / 128) * nbk;
   const long long sc_off = p.exp_w13_bytes + p.exp_w2_bytes;
-  Src src{p.experts, r.slots, RT, KT, nbk, bl, sc_off, sc_off + nsc13 * 4};
+  Src src{r.blk, RT, KT, nbk, bl, sc_off, sc_off + nsc13 * 4};
   float* hb = p.hbuf;
   const int f = p.f;
   auto epi = [=](int u, int row, int col, float v, float v2) {
@@ -748,7 +842,8 @@ __device__ __forceinline__ void phase_route_gateup(const LayerParams& p, char* s
     const float sg = v / (1.0f + expf(-v));
     hb[((long long)sl * T + col) * f + rt * 16 + row] = sg * v2;
   };
-  run_units<EF, true, false>(u0, u1, KT, T, src, epi, red);
+  if (U >= 2 * (int)gridDim.x * kWaves) stream_units_wave<EF, true>(u0, u1, KT, T, src, epi, p.dummy);
+  else stream_units_wg<EF, true, false>(u0, u1, KT, T, src, epi, red, p.dummy);
 }
 
 // ------------------------------------------------------------------ P7 down projections
@@ -771,36 +866,57 @@ __device__ __forceinline__ void phase_down(const LayerParams& p, char* smem) {
   const long long sc2_off = p.exp_w13_bytes + p.exp_w2_bytes + 2 * nsc13 * 4;
   struct Src {
     const uint8_t* blk; int RT, KT, nbk; const A* bl; long long w2_off, sc2_off;
-    __device__ const uint8_t* tile(int u, int t) const {
-      const int rt = u % RT;
-      return blk + w2_off + ((long long)rt * KT + t) * 1024;
+    __device__ const uint8_t* base(int u) const { return blk + w2_off + (long long)(u % RT) * KT * 1024; }
+    __device__ const A* bbase(int) const { return bl; }
+    __device__ const float* sbase(int u) const {
+      return reinterpret_cast<const float*>(blk + sc2_off) + ((u % RT) >> 3) * nbk;
     }
-    __device__ const A* bptr(int, int t) const { return bl + t * TK; }
-    __device__ float scale(int u, int t) const {
-      const int rt = u % RT;
-      return reinterpret_cast<const float*>(blk + sc2_off)[(rt >> 3) * nbk + (t * TK >> 7)];
+    __device__ const float* sbase2(int) const { return nullptr; }
+  };
+  // several slots per source: each unit finds its slot's block and staged operand
+  struct SrcMulti {
+    const uint8_t* const* blk; int RT, KT, nbk, sa; const A* bl; long long slot_elems, w2_off, sc2_off;
+    __device__ const uint8_t* base(int u) const {
+      return blk[u / RT] + w2_off + (long long)(u % RT) * KT * 1024;
     }
-    __device__ float scale2(int, int) const { return 1.f; }
+    __device__ const A* bbase(int u) const { return bl + (u / RT - sa) * slot_elems; }
+    __device__ const float* sbase(int u) const {
+      return reinterpret_cast<const float*>(blk[u / RT] + sc2_off) + ((u % RT) >> 3) * nbk;
+    }
+    __device__ const float* sbase2(int) const { return nullptr; }
   };
   float* yb = p.ybuf;
   const int d = p.d, f = p.f;
-  int u = u0;
-  while (u < u1) {
-    const int sl = u / RT;
-    const int ue = min(u1, (sl + 1) * RT);
-    const float* hsrc = p.hbuf + (long long)sl * T * f;
-    for (int i = threadIdx.x; i < T * f; i += kThreads) {
-      const int t = i / f, k = i - t * f;
-      xs[t * XS + k] = to_act<A>(hsrc[i]);
+  auto epi = [=](int uu, int row, int col, float v, float) {
+    const int sl = uu / RT, rt = uu - sl * RT;
+    yb[((long long)sl * T + col) * d + rt * 16 + row] = v;
+  };
+  if (U >= 2 * (int)gridDim.x * kWaves) {
+    // wave-level units; stage up to two slots' activations at a time
+    const long long slot_elems = (long long)kMaxT * XS;
+    int u = u0;
+    while (u < u1) {
+      const int sa = u / RT;
+      const int ue = min(u1, (sa + 2) * RT);
+      const int sb = (ue - 1) / RT;
+      for (int sl = sa; sl <= sb; ++sl)
+        rows_to_lds<A, false>(p.hbuf + (long long)sl * T * f, T, f, xs + (sl - sa) * slot_elems, (A*)nullptr, XS,
+                              nullptr, 0.f, smem);
+      SrcMulti src{r.blk, RT, KT, nbk, sa, bl, slot_elems, p.exp_w13_bytes, sc2_off};
+      stream_units_wave<EF, false>(u, ue, KT, T, src, epi, p.dummy);
+      __syncthreads();
+      u = ue;
     }
-    __syncthreads();
-    Src src{p.experts[r.slots[sl]], RT, KT, nbk, bl, p.exp_w13_bytes, sc2_off};
-    auto epi = [=](int uu, int row, int col, float v, float) {
-      const int rt = uu % RT;
-      yb[((long long)sl * T + col) * d + rt * 16 + row] = v;
-    };
-    run_units<EF, false, false>(u, ue, KT, T, src, epi, red);
-    u = ue;
+  } else {
+    int u = u0;
+    while (u < u1) {
+      const int sl = u / RT;
+      const int ue = min(u1, (sl + 1) * RT);
+      rows_to_lds<A, false>(p.hbuf + (long long)sl * T * f, T, f, xs, (A*)nullptr, XS, nullptr, 0.f, smem);
+      Src src{r.blk[sl], RT, KT, nbk, bl, p.exp_w13_bytes, sc2_off};
+      stream_units_wg<EF, false, false>(u, ue, KT, T, src, epi, red, p.dummy);
+      u = ue;
+    }
   }
 }
 

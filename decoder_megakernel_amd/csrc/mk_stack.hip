@@ -28,7 +28,7 @@ int launch_embed(const uint16_t* emb, int V, int d, const int32_t* tokens, int T
 struct HeadArgs {
   const uint8_t* head; int V, d; const float* gamma; float eps; const float* h; int T;
   float* logits; float* best_val; int32_t* best_idx; uint32_t* counter; int32_t* tokens;
-  const int32_t* next_drafts; int32_t* argmax; int32_t* committed; int32_t* kv_len;
+  const int32_t* next_drafts; int32_t* argmax; int32_t* committed; int32_t* kv_len; const uint8_t* dummy;
 };
 
 constexpr int kHeadLds = 8 * (8192 + kXPad) * 2 + 2 * kWaves * 64 * 4 * 4 + 1024;
@@ -64,10 +64,10 @@ __global__ __launch_bounds__(kThreads, 1) void head_kernel(HeadArgs a) {
   const __bf16* bl = xs + (j < T ? j : T - 1) * XS + g * 8;
   struct Src {
     const uint8_t* head; int KT; const __bf16* bl;
-    __device__ const uint8_t* tile(int u, int t) const { return head + ((long long)u * KT + t) * 1024; }
-    __device__ const __bf16* bptr(int, int t) const { return bl + t * 32; }
-    __device__ float scale(int, int) const { return 1.f; }
-    __device__ float scale2(int, int) const { return 1.f; }
+    __device__ const uint8_t* base(int u) const { return head + (long long)u * KT * 1024; }
+    __device__ const __bf16* bbase(int) const { return bl; }
+    __device__ const float* sbase(int) const { return nullptr; }
+    __device__ const float* sbase2(int) const { return nullptr; }
   } src{a.head, KT, bl};
   float bv = -INFINITY;
   int bi = 0x7fffffff;
@@ -78,19 +78,18 @@ __global__ __launch_bounds__(kThreads, 1) void head_kernel(HeadArgs a) {
     if (logits) logits[(long long)col * V + id] = v;
     if (v > bv || (v == bv && id < bi)) { bv = v; bi = id; }
   };
-  run_units<MK_FMT_BF16, false, false>(u0, u1, KT, T, src, epi, red);
-  // workgroup best per row: threads (row, col) with the same col hold candidates
-  float* cv = misc + 16;
-  int* ci = reinterpret_cast<int*>(misc + 16 + 256);
-  if (threadIdx.x < 256) {
-    cv[threadIdx.x] = bv;
-    ci[threadIdx.x] = bi;
-  }
+  (void)red;
+  stream_units_wave<MK_FMT_BF16, false>(u0, u1, KT, T, src, epi, a.dummy);
+  // workgroup best per row: every thread holds a candidate for column lane % 16
+  float* cv = reinterpret_cast<float*>(smem + 8 * XS * 2);
+  int* ci = reinterpret_cast<int*>(cv + kThreads);
+  cv[threadIdx.x] = bv;
+  ci[threadIdx.x] = bi;
   __syncthreads();
   if (threadIdx.x < T) {
     float v = -INFINITY;
     int id = 0x7fffffff;
-    for (int r = 0; r < 16; ++r) {
+    for (int r = 0; r < kThreads / 16; ++r) {
       const float ov = cv[r * 16 + threadIdx.x];
       const int oi = ci[r * 16 + threadIdx.x];
       if (ov > v || (ov == v && oi < id)) { v = ov; id = oi; }
@@ -147,10 +146,10 @@ int head_kernel_occupancy(int* wgs_per_cu) {
 
 int launch_head(const void* head_packed, int V, int d, const float* gamma, float eps, const float* h, int T,
                 float* logits, float* best_val, int32_t* best_idx, uint32_t* counter, int32_t* tokens,
-                const int32_t* next_drafts, int32_t* argmax, int32_t* committed, int32_t* kv_len, int nwg,
-                hipStream_t s) {
+                const int32_t* next_drafts, int32_t* argmax, int32_t* committed, int32_t* kv_len,
+                const uint8_t* dummy, int nwg, hipStream_t s) {
   HeadArgs a{(const uint8_t*)head_packed, V, d, gamma, eps, h, T, logits, best_val, best_idx, counter, tokens,
-             next_drafts, argmax, committed, kv_len};
+             next_drafts, argmax, committed, kv_len, dummy};
   hipLaunchKernelGGL(head_kernel, dim3(nwg), dim3(kThreads), kHeadLds, s, a);
   return (int)hipGetLastError();
 }
