@@ -266,6 +266,9 @@ def main():
     ap.add_argument("--layers", type=int, default=None, help="stack depth override (diagnostics only)")
     ap.add_argument("--layer-reps", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="after timing, run one device-to-device copy of this many MiB (a known-size kernel "
+                         "for scaling hardware byte counters in a profile)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (the layer's sharding is "
@@ -281,6 +284,15 @@ def main():
         args.steps = args.steps or 60
         args.warmup = args.warmup if args.warmup is not None else 12
         res = run_layer(s, args)
+    if args.calib_copy_mib:
+        import torch
+        n = args.calib_copy_mib << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] calibration copy of %d MiB done" % args.calib_copy_mib)
     print(json.dumps(res), flush=True)
 
 

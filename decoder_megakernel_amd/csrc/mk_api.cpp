@@ -80,7 +80,7 @@ int check_cfg(const mk_layer_config* c) {
   const long long lds_route = xb + 32768 + (long long)kMaxT * D.E * 4 + 3 * kMaxT * kMaxTopK * 4 +
                               (kMaxT * kMaxTopK + 8) * 4 + (long long)D.E * 4 + 16 + (kMaxT * kMaxTopK + 8) * 8;
   const long long lds_att = std::max((long long)kWaves * 16 * (D.dc + 8) * es + 16LL * (D.kvw + 8) * es,
-                                     4LL * 16 * D.dc * 4 + 4 * 16 * 2 * 4);
+                                     4LL * 16 * D.dc * 4 + 4 * 64 * 2 * 4);
   const long long lim = kLdsBytes - 1024;
   // the down projection stages two experts' activations below the routing tables
   if (2LL * kMaxT * (D.f + kXPad) * es > xb + 32768)
@@ -208,7 +208,7 @@ StLayout st_layout(const Dims& D, const Schedule& s) {
   l.bar = take(sizeof(BarrierState));
   l.att_cnt = take(64 * 4);
   l.experts = take((size_t)(D.E + D.nshared) * 8);
-  l.trace = take((size_t)s.nwg * (2 + 2 * kBarriers) * 8);
+  l.trace = take((size_t)s.nwg * kTraceStride * 8);
   l.total = off;
   return l;
 }
@@ -564,13 +564,18 @@ int mk_get_stats(const mk_layer* L, mk_stats* out) {
 
 int mk_set_trace(mk_layer* L, int enabled) {
   if (!L) return fail(MK_ERR_INVALID_ARG, "null layer");
+  if (enabled && !L->trace_on) {
+    HIP_OK(hipDeviceSynchronize());
+    HIP_OK(hipMemset(L->state + L->sl.trace, 0, (size_t)L->sch.nwg * kTraceStride * 8));
+    HIP_OK(hipDeviceSynchronize());
+  }
   L->trace_on = enabled ? 1 : 0;
   return MK_OK;
 }
 
 int mk_read_trace(mk_layer* L, int64_t* host_dst, size_t bytes, void* stream) {
   if (!L || !host_dst) return fail(MK_ERR_INVALID_ARG, "null argument");
-  const size_t need = (size_t)L->sch.nwg * (2 + 2 * kBarriers) * 8;
+  const size_t need = (size_t)L->sch.nwg * kTraceStride * 8;
   if (bytes < need) return fail(MK_ERR_INVALID_ARG, "trace buffer too small (%zu < %zu)", bytes, need);
   HIP_OK(hipStreamSynchronize((hipStream_t)stream));
   HIP_OK(hipMemcpy(host_dst, L->state + L->sl.trace, need, hipMemcpyDeviceToHost));

@@ -12,6 +12,8 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kMaxT = MK_MAX_T;          // verify rows the LDS budget is sized for
 constexpr int kXPad = 8;                 // LDS row padding of activation operands (elements)
 constexpr int kBarriers = 8;             // grid barriers in one layer launch
+constexpr int kTraceX = 8;               // extra per-workgroup timestamps (attention sub-phases)
+constexpr int kTraceStride = 2 + 2 * kBarriers + kTraceX;
 constexpr int kLdsBytes = 160 * 1024 - 256;
 constexpr int kMaxTopK = 16;
 

@@ -102,7 +102,7 @@ __device__ __forceinline__ bool grid_barrier(const LayerParams& p, int idx, int*
   if (threadIdx.x == 0) {
     int ok = 1;
     uint64_t t0 = clock100();
-    if (p.trace) p.trace[(long long)blockIdx.x * (2 + 2 * kBarriers) + 1 + 2 * idx] = (long long)t0;
+    if (p.trace) p.trace[(long long)blockIdx.x * kTraceStride + 1 + 2 * idx] = (long long)t0;
     BarrierState* b = p.bar;
     if (__hip_atomic_load(&b->fault, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) {
       ok = 0;
@@ -129,7 +129,7 @@ __device__ __forceinline__ bool grid_barrier(const LayerParams& p, int idx, int*
       }
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     }
-    if (p.trace) p.trace[(long long)blockIdx.x * (2 + 2 * kBarriers) + 2 + 2 * idx] = (long long)clock100();
+    if (p.trace) p.trace[(long long)blockIdx.x * kTraceStride + 2 + 2 * idx] = (long long)clock100();
     *lds_flag = ok;
   }
   __syncthreads();

@@ -34,6 +34,12 @@ struct LdsPlan {
 constexpr int kMiscOff = kLdsBytes - 1024;     // 256 floats of scratch + the barrier flag
 constexpr int kFlagOff = kLdsBytes - 16;
 
+// attention sub-phase timestamp (thread 0, only when tracing)
+__device__ __forceinline__ void trace_x(const LayerParams& p, int slot) {
+  if (p.trace && threadIdx.x == 0)
+    p.trace[(long long)blockIdx.x * kTraceStride + 2 + 2 * kBarriers + slot] = (long long)clock100();
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
@@ -329,7 +335,6 @@ __device__ __forceinline__ void phase_attention(const LayerParams& p, int L, cha
   const int NQ = T * nh, NQT = (NQ + 15) / 16, Lt = L + T;
   const int KB = kvw / KBW, DB = dc / 16;
   int s_kv = (int)gridDim.x / NQT;
-  if (s_kv >= 8) s_kv = s_kv / 8 * 8;
   if (s_kv < 1) s_kv = 1;
   const int nchunk_all = (Lt + 15) / 16;
   if (s_kv > nchunk_all) s_kv = nchunk_all;
@@ -372,6 +377,7 @@ __device__ __forceinline__ void phase_attention(const LayerParams& p, int L, cha
       }
     }
     __syncthreads();
+    trace_x(p, 0);
     const int k0 = s * SK, k1 = min(Lt, k0 + SK);
     const int nch = k1 > k0 ? (k1 - k0 + 15) / 16 : 0;
     float m_run = -INFINITY, l_run = 0.f;
@@ -464,25 +470,25 @@ __device__ __forceinline__ void phase_attention(const LayerParams& p, int L, cha
     }
     // merge the 8 waves' (m, l, Z) in LDS, tree order 4+0.., 2+0.., 1+0
     __syncthreads();
-    float* mb = reinterpret_cast<float*>(smem);                 // [4][16][dc]
-    float* ml = reinterpret_cast<float*>(smem) + 4 * 16 * dc;   // [4][16][2]
+    trace_x(p, 1);
+    // Partial state layout (LDS and global): block db of the latent holds, per
+    // lane, the 4 values acc[db] (MFMA result layout: lane (g, j) has dims
+    // 16 db + 4 g + e of query j), so every access is one 16-byte vector.
+    f32x4* mb = reinterpret_cast<f32x4*>(smem);                 // [4][DB][64]
+    float* ml = reinterpret_cast<float*>(smem) + 4 * DB * 64 * 4;   // [4][64][2]
     for (int half = 4; half >= 1; half >>= 1) {
       if (w >= half && w < 2 * half) {
-        float* zb = mb + (long long)(w - half) * 16 * dc;
+        f32x4* zb = mb + (long long)(w - half) * DB * 64;
 #pragma unroll
         for (int db = 0; db < DBMAX; ++db)
-          if (db < DB)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) zb[j * dc + db * 16 + 4 * g + e] = acc[db][e];
-        if (g == 0) {
-          ml[((w - half) * 16 + j) * 2] = m_run;
-          ml[((w - half) * 16 + j) * 2 + 1] = l_run;
-        }
+          if (db < DB) zb[db * 64 + lane] = acc[db];
+        ml[((w - half) * 64 + lane) * 2] = m_run;
+        ml[((w - half) * 64 + lane) * 2 + 1] = l_run;
       }
       __syncthreads();
       if (w < half) {
-        const float* zb = mb + (long long)w * 16 * dc;
-        const float mo = ml[(w * 16 + j) * 2], lo = ml[(w * 16 + j) * 2 + 1];
+        const f32x4* zb = mb + (long long)w * DB * 64;
+        const float mo = ml[(w * 64 + lane) * 2], lo = ml[(w * 64 + lane) * 2 + 1];
         const float M = fmaxf(m_run, mo);
         float sa = 0.f, sb = 0.f;
         if (M != -INFINITY) {
@@ -491,39 +497,44 @@ __device__ __forceinline__ void phase_attention(const LayerParams& p, int L, cha
         }
 #pragma unroll
         for (int db = 0; db < DBMAX; ++db)
-          if (db < DB)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[db][e] = acc[db][e] * sa + zb[j * dc + db * 16 + 4 * g + e] * sb;
+          if (db < DB) acc[db] = acc[db] * sa + zb[db * 64 + lane] * sb;
         l_run = l_run * sa + lo * sb;
         m_run = M;
       }
       __syncthreads();
     }
     if (w == 0) {
-      float* zp = p.att_part + (long long)u * 16 * dc;
+      f32x4* zp = reinterpret_cast<f32x4*>(p.att_part + (long long)u * 16 * dc);
 #pragma unroll
       for (int db = 0; db < DBMAX; ++db)
-        if (db < DB)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) zp[j * dc + db * 16 + 4 * g + e] = acc[db][e];
+        if (db < DB) zp[db * 64 + lane] = acc[db];
       if (g == 0) {
         p.att_ml[((long long)u * 16 + j) * 2] = m_run;
         p.att_ml[((long long)u * 16 + j) * 2 + 1] = l_run;
       }
     }
-    // the last split of this query tile to finish merges all splits into z
+    trace_x(p, 2);
+    // every split of this query tile waits for its siblings, then merges 1/s_kv
+    // of the latent into z (the counters are cleared at kernel start)
     wg_release_begin();
     if (threadIdx.x == 0) {
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-      const uint32_t old = __hip_atomic_fetch_add(&p.att_cnt[qt], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const int last = old == (uint32_t)(s_kv - 1);
-      if (last) {
-        __hip_atomic_store(&p.att_cnt[qt], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      __hip_atomic_fetch_add(&p.att_cnt[qt], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const uint64_t t0 = clock100();
+      int ok = 1;
+      while (__hip_atomic_load(&p.att_cnt[qt], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (uint32_t)s_kv) {
+        __builtin_amdgcn_s_sleep(1);
+        if ((long long)(clock100() - t0) > p.timeout_ticks) {
+          __hip_atomic_store(&p.bar->fault, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          ok = 0;
+          break;
+        }
       }
-      *flag = last;
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      *flag = ok;
     }
     __syncthreads();
+    trace_x(p, 3);
     if (*flag) {
       // combination weights per (split, query): exp(m_s - M) / sum_s exp(m_s - M) l_s
       const int ub = qt * s_kv;
@@ -545,26 +556,31 @@ __device__ __forceinline__ void phase_attention(const LayerParams& p, int L, cha
         for (int ss = 0; ss < s_kv; ++ss) cf[ss * 16 + jq] = mm[ss * 16 + jq] / den;
       }
       __syncthreads();
-      const int dq = dc / 4;
-      for (int it = threadIdx.x; it < 16 * dq; it += kThreads) {
-        const int jq = it / dq, d4 = it - jq * dq;
+      // this split's share of the items, in storage order: item i = (block i / 64, lane i % 64)
+      const int n_items = DB * 64;
+      int i0, i1;
+      split_range(n_items, s_kv, s, i0, i1);
+      const f32x4* zb = reinterpret_cast<const f32x4*>(p.att_part + (long long)ub * 16 * dc);
+      const long long sstride = 16LL * dc / 4;
+      for (int it = i0 + threadIdx.x; it < i1; it += kThreads) {
+        const int db = it >> 6, ln = it & 63, jq = ln & 15, gq = ln >> 4;
         const int qq = qt * 16 + jq;
         if (qq >= NQ) continue;
-        const f32x4* zp = reinterpret_cast<const f32x4*>(p.att_part + ((long long)ub * 16 + jq) * dc) + d4;
-        const long long sstride = 16LL * dc / 4;
-        f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0, a2 = a0, a3 = a0;
+        const f32x4* zp = zb + it;
+        f32x4 a0 = {0.f, 0.f, 0.f, 0.f};
         int ss = 0;
-        for (; ss + 4 <= s_kv; ss += 4) {
-          const f32x4 z0 = zp[(ss + 0) * sstride], z1 = zp[(ss + 1) * sstride];
-          const f32x4 z2 = zp[(ss + 2) * sstride], z3 = zp[(ss + 3) * sstride];
-          a0 += z0 * cf[(ss + 0) * 16 + jq];
-          a1 += z1 * cf[(ss + 1) * 16 + jq];
-          a2 += z2 * cf[(ss + 2) * 16 + jq];
-          a3 += z3 * cf[(ss + 3) * 16 + jq];
+        for (; ss + 8 <= s_kv; ss += 8) {
+          f32x4 zz[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) zz[i] = zp[(ss + i) * sstride];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) a0 += zz[i] * cf[(ss + i) * 16 + jq];
         }
         for (; ss < s_kv; ++ss) a0 += zp[ss * sstride] * cf[ss * 16 + jq];
-        *reinterpret_cast<f32x4*>(p.z + (long long)qq * dc + d4 * 4) = (a0 + a1) + (a2 + a3);
+        *reinterpret_cast<f32x4*>(p.z + (long long)qq * dc + db * 16 + gq * 4) = a0;
       }
+      __syncthreads();
+      trace_x(p, 4);
     }
     __syncthreads();
   }
@@ -946,7 +962,9 @@ __global__ __launch_bounds__(kThreads, 1) void layer_kernel(LayerParams p) {
       __hip_atomic_store(&p.bar->fault, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return;
   }
-  if (p.trace && threadIdx.x == 0) p.trace[(long long)blockIdx.x * (2 + 2 * kBarriers)] = (long long)clock100();
+  if (p.trace && threadIdx.x == 0) p.trace[(long long)blockIdx.x * kTraceStride] = (long long)clock100();
+  // attention split counters: cleared here, used after two grid barriers
+  if (blockIdx.x == 0 && threadIdx.x < 64) p.att_cnt[threadIdx.x] = 0u;
   phase_qkv<AF>(p, smem);
   if (!grid_barrier(p, 0, flag)) return;
   phase_rope_kv<KF>(p, L);
@@ -967,7 +985,7 @@ __global__ __launch_bounds__(kThreads, 1) void layer_kernel(LayerParams p) {
   LdsPlan lp(p, EF == MK_FMT_F32 ? 4 : 2);
   phase_combine(p, smem, lp.xb);
   if (p.trace && threadIdx.x == 0)
-    p.trace[(long long)blockIdx.x * (2 + 2 * kBarriers) + 1 + 2 * kBarriers] = (long long)clock100();
+    p.trace[(long long)blockIdx.x * kTraceStride + 1 + 2 * kBarriers] = (long long)clock100();
 }
 
 // Instantiations: all-fp32 (d_latent + d_rope <= 160, d_latent <= 128),

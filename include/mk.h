@@ -197,10 +197,12 @@ int mk_decode_step(mk_layer* layer, const float* hidden_in, int T, const mk_kv_c
 int mk_debug_tap(mk_layer* layer, int tap, void* host_dst, size_t bytes, void* stream);
 /* Synchronous: reads the device counters of this layer's state. */
 int mk_get_stats(const mk_layer* layer, mk_stats* out);
-/* Enables per-workgroup phase timestamps (written into the layer state). */
+/* Enables per-workgroup phase timestamps (written into the layer state);
+ * enabling clears the trace buffer (synchronous). */
 int mk_set_trace(mk_layer* layer, int enabled);
 /* Copies the trace of the last step: int64 ticks of a 100 MHz clock,
- * [grid_wgs][2 + 2*barriers_per_step]: start, (arrive, release) per barrier, end. */
+ * [grid_wgs][2 + 2*barriers_per_step + 8]: start, (arrive, release) per barrier, end,
+ * then 8 attention sub-phase stamps (0 where a workgroup had no attention unit). */
 int mk_read_trace(mk_layer* layer, int64_t* host_dst, size_t bytes, void* stream);
 /* Barrier wait bound in microseconds (default 2,000,000). */
 int mk_set_barrier_timeout_us(mk_layer* layer, int64_t us);
