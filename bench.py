@@ -59,6 +59,30 @@ def layer_bytes(s, L, slots):
     return attn_bytes(s) + router_bytes(s) + slots * expert_bytes(s) + kv + act
 
 
+def kernel_source_hash():
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "decoder_megakernel_amd", "csrc")
+    for f in sorted(glob.glob(os.path.join(csrc, "*.h")) + glob.glob(os.path.join(csrc, "*.hip")) +
+                    glob.glob(os.path.join(csrc, "*.cpp"))):
+        h.update(os.path.basename(f).encode())
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
+
+
+def measured_traffic(name):
+    """HBM bytes per launch from the committed counter profile, or None when the
+    kernel sources have changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", name)
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("source_sha256") != kernel_source_hash():
+        return None
+    return rec["hbm_bytes_per_launch"]
+
+
 def read_i32(dev_ptr):
     import ctypes
     hip = ctypes.CDLL("libamdhip64.so")
@@ -196,7 +220,8 @@ def run_stack(s, args):
         "hbm_gbps_step": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
         "experts_streamed_per_layer": round(float(np.mean(slots)), 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_GBPS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_GBPS, 4),
+                     "traffic": measured_traffic("layer_kernel_stack32_fp8_T6_hbm_counters.json"),
                      "kernel": "layer_kernel<bf16, fp8, bf16>", "bytes_per_launch": int(lb),
                      "avg_launch_us": round(us_layer, 2), "launches_timed": launches},
     }
@@ -267,8 +292,8 @@ def main():
     ap.add_argument("--layer-reps", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
-                    help="after timing, run one device-to-device copy of this many MiB (a known-size kernel "
-                         "for scaling hardware byte counters in a profile)")
+                    help="after timing, run one elementwise kernel reading and writing this many MiB (a "
+                         "known-size kernel for scaling hardware byte counters in a profile)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (the layer's sharding is "
@@ -290,7 +315,7 @@ def main():
         src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
-        dst.copy_(src)
+        torch.mul(src, 2.0, out=dst)      # reads and writes exactly n bytes each
         torch.cuda.synchronize()
         log("[bench] calibration copy of %d MiB done" % args.calib_copy_mib)
     print(json.dumps(res), flush=True)
