@@ -68,13 +68,15 @@ int check_cfg(const mk_layer_config* c) {
   if (D.d % 128 || D.f % 128) return fail(MK_ERR_UNSUPPORTED_SHAPE, "d_model and d_ff must be multiples of 128");
   if (D.dh % 32 || D.dc % 32 || D.dr % 32) return fail(MK_ERR_UNSUPPORTED_SHAPE, "d_head, d_latent, d_rope must be multiples of 32");
   if (D.E % 16) return fail(MK_ERR_UNSUPPORTED_SHAPE, "n_experts must be a multiple of 16");
-  if (D.E > 4096) return fail(MK_ERR_UNSUPPORTED_SHAPE, "n_experts must be <= 4096");
+  if (D.E > kMaxExperts) return fail(MK_ERR_UNSUPPORTED_SHAPE, "n_experts must be <= %d", kMaxExperts);
   if (D.topk > kMaxTopK || D.topk > D.E) return fail(MK_ERR_UNSUPPORTED_SHAPE, "top_k must be <= 16 and <= n_experts");
   if (D.nshared < 0 || D.nshared > 1) return fail(MK_ERR_UNSUPPORTED_SHAPE, "n_shared must be 0 or 1");
   if (f32 && (D.kvw > 160 || D.dc > 128)) return fail(MK_ERR_UNSUPPORTED_SHAPE, "fp32 layers: d_latent <= 128, d_latent + d_rope <= 160");
   if (bf && (D.kvw > 576 || D.dc > 512)) return fail(MK_ERR_UNSUPPORTED_SHAPE, "bf16 layers: d_latent <= 512, d_latent + d_rope <= 576");
   const int es = f32 ? 4 : 2;
   const int dmax = std::max(D.d, std::max(D.nh * D.dh, D.f));
+  if (dmax > kMaxStageK)
+    return fail(MK_ERR_UNSUPPORTED_SHAPE, "d_model, n_heads*d_head and d_ff must be <= %d", kMaxStageK);
   const long long xb = align256((size_t)kMaxT * (dmax + kXPad) * es);
   const long long lds_router = 2 * xb + 2 * kWaves * 64 * 4 * 4;
   const long long lds_route = xb + 32768 + (long long)kMaxT * D.E * 4 + 3 * kMaxT * kMaxTopK * 4 +
@@ -162,6 +164,9 @@ int device_info(int dev, DevInfo* di, LayerKernelFn fn) {
     di->wgs_per_cu = n;
     if (n < 1) return fail(MK_ERR_NOT_CORESIDENT, "layer kernel cannot be resident (occupancy %d)", n);
     di->nwg = di->cus;   // one workgroup per compute unit
+    if (di->nwg > kBarGroup * kMaxBarGroups)
+      return fail(MK_ERR_UNSUPPORTED_DEVICE, "%d compute units exceed the barrier's %d workgroups", di->nwg,
+                  kBarGroup * kMaxBarGroups);
   }
   return MK_OK;
 }
@@ -190,7 +195,7 @@ WsLayout ws_layout(const Dims& D, const Schedule& s) {
   w.z = take((size_t)T * D.nh * D.dc * 4);
   w.o = take((size_t)T * D.nh * D.dh * 4);
   w.hp = take((size_t)T * D.d * 4);
-  w.logit_part = take((size_t)s.s_r * T * D.E * 4);
+  w.logit_part = take((size_t)T * D.E * 4);
   w.route_sel = take((size_t)T * kMaxTopK * 4);
   w.route_gate = take((size_t)T * kMaxTopK * 4);
   w.logits = take((size_t)T * D.E * 4);
@@ -218,7 +223,6 @@ Schedule make_schedule(const Dims& D, int nwg) {
   s.nwg = nwg;
   const int KTa = D.d / tile_k(D.af);
   s.s_q = choose_split(D.nq / 16 + (D.kvw + 15) / 16, KTa, nwg);
-  s.s_r = choose_split(D.E / 16, KTa, nwg);
   return s;
 }
 

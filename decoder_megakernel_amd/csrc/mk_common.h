@@ -12,10 +12,13 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kMaxT = MK_MAX_T;          // verify rows the LDS budget is sized for
 constexpr int kXPad = 8;                 // LDS row padding of activation operands (elements)
 constexpr int kBarriers = 8;             // grid barriers in one layer launch
-constexpr int kTraceX = 8;               // extra per-workgroup timestamps (attention sub-phases)
+constexpr int kTraceX = 16;              // extra per-workgroup timestamps (sub-phase marks)
 constexpr int kTraceStride = 2 + 2 * kBarriers + kTraceX;
 constexpr int kLdsBytes = 160 * 1024 - 256;
 constexpr int kMaxTopK = 16;
+constexpr int kMaxExperts = 1024;        // routed experts per layer (16 logits per lane)
+constexpr int kStageCh = 18;             // float4s per lane when staging one activation row
+constexpr int kMaxStageK = kStageCh * 64 * 4;   // longest activation row (elements)
 
 // Packed tile geometry: one tile = 16 rows x kTileK[fmt] columns = 1 KiB,
 // lane l holds row (l % 16) and 16 consecutive bytes of columns
@@ -24,9 +27,18 @@ __host__ __device__ constexpr int tile_k(int fmt) { return fmt == MK_FMT_F32 ? 1
 __host__ __device__ constexpr int elem_bytes(int fmt) { return fmt == MK_FMT_F32 ? 4 : (fmt == MK_FMT_BF16 ? 2 : 1); }
 
 // Per-layer device state (persistent across steps; zeroed at init).
+// The grid barrier is two-level: workgroups arrive on the counter of their
+// group of kBarGroup consecutive workgroups; the last of a group arrives on
+// `top`; the last group leader advances `gen`.  Counters only ever grow (the
+// last arriver is the one whose arrival makes the count a multiple of the
+// group size), so nothing is reset between barriers or launches.
+constexpr int kBarGroup = 16;
+constexpr int kMaxBarGroups = 64;        // grids of up to 1024 workgroups
+struct alignas(256) BarrierLine {
+  unsigned long long n;
+  uint32_t pad[62];
+};
 struct alignas(256) BarrierState {
-  uint32_t count;
-  uint32_t pad0[63];
   uint32_t gen;
   uint32_t pad1[63];
   uint32_t fault;          // 0 ok, 1 barrier timeout, 2 KV length out of range
@@ -34,13 +46,14 @@ struct alignas(256) BarrierState {
   unsigned long long slots_sum;   // sum over launches of experts streamed (routed distinct + shared)
   unsigned long long launches;    // launches that reached the expert phase
   uint32_t pad3[60];
+  BarrierLine top;
+  BarrierLine grp[kMaxBarGroups];
 };
 
 // Schedule chosen at init for this device and shape.
 struct Schedule {
   int nwg;                 // persistent grid (all co-resident)
   int s_q;                 // k-splits of the Q / latent-KV projection
-  int s_r;                 // k-splits of the router projection
 };
 
 // Kernel parameters (passed by value).
@@ -78,7 +91,7 @@ struct LayerParams {
   float* z;                // [T][nh][dc]
   float* o;                // [T][nh*dh]
   float* hp;               // [T][d]
-  float* logit_part;       // [s_r][T][E]
+  float* logit_part;       // [T][E] router logits before the bias
   int32_t* route_sel;      // [T][topk]
   float* route_gate;       // [T][topk]
   float* logits;           // [T][E] (written by workgroup 0)

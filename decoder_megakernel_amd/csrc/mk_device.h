@@ -23,13 +23,18 @@ __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<
 // (s_waitcnt vmcnt(0); expcnt and lgkmcnt left at their maxima).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-// Makes this workgroup's global writes visible device-wide: every wave drains
-// its own stores, then one agent-scope release (L2 write-back) by thread 0.
-// Must be called by all threads of the workgroup.
+// Drains this workgroup's outstanding memory operations: every wave waits for
+// its own loads and stores, then the workgroup synchronises.  Must be called by
+// all threads of the workgroup.
 __device__ __forceinline__ void wg_release_begin() {
   wait_vmem();
   __syncthreads();
 }
+
+// Agent-scope release (L2 write-back of this compute unit's XCD, so other XCDs
+// can read what this workgroup wrote) and acquire (drop stale cached copies).
+__device__ __forceinline__ void release_agent() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
+__device__ __forceinline__ void acquire_agent() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
 
 __device__ __forceinline__ uint64_t clock100() { return __builtin_amdgcn_s_memrealtime(); }
 
@@ -94,9 +99,11 @@ __device__ __forceinline__ f32x4 tile_mma<MK_FMT_FP8_B128>(const u32x4& a, const
 }
 
 // ------------------------------------------------------------------ grid barrier
-// Sense-reversing barrier over the whole persistent grid.  The wait is bounded:
-// past `timeout_ticks` (100 MHz clock) the fault word is set and every later
-// barrier returns false at once, so all workgroups leave the kernel.
+// Two-level barrier over the whole persistent grid (see BarrierState).  Each
+// workgroup drains its stores and releases them at agent scope before it
+// arrives, and acquires after the release of the barrier.  The wait is bounded: past `timeout_ticks` (100 MHz clock) the fault word is set
+// and every later barrier returns false at once, so all workgroups leave the
+// kernel.
 __device__ __forceinline__ bool grid_barrier(const LayerParams& p, int idx, int* lds_flag) {
   wg_release_begin();
   if (threadIdx.x == 0) {
@@ -107,12 +114,18 @@ __device__ __forceinline__ bool grid_barrier(const LayerParams& p, int idx, int*
     if (__hip_atomic_load(&b->fault, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) {
       ok = 0;
     } else {
-      uint32_t g = __hip_atomic_load(&b->gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-      uint32_t old = __hip_atomic_fetch_add(&b->count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (old == (uint32_t)gridDim.x - 1) {
-        __hip_atomic_store(&b->count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_fetch_add(&b->gen, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      // the generation is read (and waited for) before this workgroup arrives
+      const uint32_t g = __hip_atomic_load(&b->gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      release_agent();
+      const int nwg = (int)gridDim.x, grp = (int)blockIdx.x / kBarGroup;
+      const int ngrp = (nwg + kBarGroup - 1) / kBarGroup;
+      const unsigned long long gsz = (unsigned long long)min(kBarGroup, nwg - grp * kBarGroup);
+      bool last = false;
+      if ((__hip_atomic_fetch_add(&b->grp[grp].n, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1) % gsz == 0)
+        last = (__hip_atomic_fetch_add(&b->top.n, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1) %
+                   (unsigned long long)ngrp == 0;
+      if (last) {
+        __hip_atomic_fetch_add(&b->gen, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       } else {
         while (__hip_atomic_load(&b->gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == g) {
           __builtin_amdgcn_s_sleep(1);
@@ -127,7 +140,7 @@ __device__ __forceinline__ bool grid_barrier(const LayerParams& p, int idx, int*
           }
         }
       }
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      acquire_agent();
     }
     if (p.trace) p.trace[(long long)blockIdx.x * kTraceStride + 2 + 2 * idx] = (long long)clock100();
     *lds_flag = ok;

@@ -11,9 +11,10 @@
 //       query tile to finish merges all splits (log-sum-exp) into z
 //   P3  o = W_UV z
 //   P4  H' = H + W_O o
-//   P5  RMSNorm-2 (every workgroup, into LDS) ; router logits, split-K partials
+//   P5  RMSNorm-2 (every workgroup, into LDS) ; router logits on E/16
+//       workgroups, the shared experts' gate+up on the others
 //   P6  softmax / top-k / gates / distinct-expert work list (every workgroup,
-//       identical) ; gate+up projections of every listed expert: silu(W1 x) * W3 x
+//       identical) ; gate+up projections of every routed expert: silu(W1 x) * W3 x
 //   P7  down projections W2 h of every listed expert
 //   P8  out = H' + sum_k gate_k y_k + y_shared
 #include "mk_device.h"
@@ -34,7 +35,7 @@ struct LdsPlan {
 constexpr int kMiscOff = kLdsBytes - 1024;     // 256 floats of scratch + the barrier flag
 constexpr int kFlagOff = kLdsBytes - 16;
 
-// attention sub-phase timestamp (thread 0, only when tracing)
+// sub-phase timestamp (thread 0, only when tracing)
 __device__ __forceinline__ void trace_x(const LayerParams& p, int slot) {
   if (p.trace && threadIdx.x == 0)
     p.trace[(long long)blockIdx.x * kTraceStride + 2 + 2 * kBarriers + slot] = (long long)clock100();
@@ -76,62 +77,55 @@ template <> __device__ __forceinline__ f32x4 round4<__bf16>(const f32x4& v) {
   return f32x4{(float)(__bf16)v[0], (float)(__bf16)v[1], (float)(__bf16)v[2], (float)(__bf16)v[3]};
 }
 
-// Copies rows src[T][K] (fp32, global) into the LDS operand xs[T][XS] (activation
-// type), issuing every load of the workgroup at once (T*K <= 32768).  With NORM
-// each row is RMS-normalised on the way: x = (h * (1/sqrt(mean(h^2) + eps))) * gamma,
-// the sum of squares reduced in a fixed order.  `lo` (optional) receives the
-// bf16 remainder x - bf16(x) for the router's split operand.
+// Stages T <= kMaxT fp32 rows of length K (K % 4 == 0, K <= kMaxStageK) into
+// LDS as the MFMA operand type, row stride XS.  Wave w stages row w (lane l
+// handles float4 columns l, l + 64, ...), so each row's loads, its sum of
+// squares and its scaling stay inside one wave: one round trip to memory, one
+// wave reduction, one workgroup barrier at the end.  With NORM each row is
+// RMS-normalised on the way: x = (h * (1/sqrt(mean(h^2) + eps))) * gamma.
+// `lo` (optional) receives the remainder x - round(x) for the router's split
+// operand.
+static_assert(kMaxT <= kWaves, "one staged row per wave");
 template <class A, bool NORM>
 __device__ __forceinline__ void rows_to_lds(const float* src, int T, int K, A* xs, A* lo, int XS,
-                                            const float* gamma, float eps, char* smem) {
-  constexpr int CH = 16;
-  const int n4 = K / 4, total = T * n4;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  f32x4 v[CH];
+                                            const float* gamma, float eps, char* smem,
+                                            long long* tr = nullptr) {
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n4 = K / 4;
+  (void)smem;
+  if (w < T) {
+    const float* row = src + (long long)w * K;
+    f32x4 v[kStageCh];
+    f32x4 gm[kStageCh];
 #pragma unroll
-  for (int c = 0; c < CH; ++c) {
-    const int i = tid + c * kThreads;
-    if (i < total) v[c] = *reinterpret_cast<const f32x4*>(src + (long long)i * 4);
-  }
-  float* rs = reinterpret_cast<float*>(smem + kMiscOff);           // [kMaxT]
-  if constexpr (NORM) {
-    float* red = rs + 16;                                          // [kWaves][kMaxT]
-    float ss[kMaxT];
-#pragma unroll
-    for (int t = 0; t < kMaxT; ++t) ss[t] = 0.f;
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int i = tid + c * kThreads;
-      if (i < total) {
-        const int t = i / n4;
-        const float q = v[c][0] * v[c][0] + v[c][1] * v[c][1] + v[c][2] * v[c][2] + v[c][3] * v[c][3];
-#pragma unroll
-        for (int tt = 0; tt < kMaxT; ++tt)
-          if (tt == t) ss[tt] += q;
+    for (int c = 0; c < kStageCh; ++c) {
+      const int i = lane + 64 * c;
+      if (i < n4) {
+        v[c] = *reinterpret_cast<const f32x4*>(row + 4 * i);
+        if constexpr (NORM) gm[c] = *reinterpret_cast<const f32x4*>(gamma + 4 * i);
       }
     }
+    float r = 1.f;
+    if constexpr (NORM) {
+      float ss = 0.f;
 #pragma unroll
-    for (int tt = 0; tt < kMaxT; ++tt) {
-      const float r = wave_sum(ss[tt]);
-      if (lane == 0) red[w * kMaxT + tt] = r;
+      for (int c = 0; c < kStageCh; ++c)
+        if (lane + 64 * c < n4) ss += v[c][0] * v[c][0] + v[c][1] * v[c][1] + v[c][2] * v[c][2] + v[c][3] * v[c][3];
+      if (tr && lane == 0 && w == 0) tr[10] = (long long)clock100();
+      ss = wave_sum(ss);
+      r = 1.0f / sqrtf(ss / (float)K + eps);
+      if (tr && lane == 0 && w == 0) tr[11] = (long long)clock100();
     }
-    __syncthreads();
-    if (tid < T) {
-      float tot = 0.f;
-      for (int ww = 0; ww < kWaves; ++ww) tot += red[ww * kMaxT + tid];
-      rs[tid] = 1.0f / sqrtf(tot / (float)K + eps);
-    }
-    __syncthreads();
-  }
+    A* xr = xs + (long long)w * XS;
 #pragma unroll
-  for (int c = 0; c < CH; ++c) {
-    const int i = tid + c * kThreads;
-    if (i < total) {
-      const int t = i / n4, k = (i - t * n4) * 4;
-      f32x4 x = v[c];
-      if constexpr (NORM) x = (x * rs[t]) * *reinterpret_cast<const f32x4*>(gamma + k);
-      store4<A>(xs + t * XS + k, x);
-      if (lo) store4<A>(lo + t * XS + k, x - round4<A>(x));
+    for (int c = 0; c < kStageCh; ++c) {
+      const int i = lane + 64 * c;
+      if (i < n4) {
+        f32x4 x = v[c];
+        if constexpr (NORM) x = (x * r) * gm[c];
+        store4<A>(xr + 4 * i, x);
+        if (lo) store4<A>(lo + (long long)w * XS + 4 * i, x - round4<A>(x));
+      }
     }
   }
   __syncthreads();
@@ -154,7 +148,9 @@ __device__ __forceinline__ void phase_qkv(const LayerParams& p, char* smem) {
   LdsPlan lp(p, sizeof(A));
   A* xs = reinterpret_cast<A*>(smem);
   float* red = reinterpret_cast<float*>(smem + lp.xb);
-  rows_to_lds<A, true>(p.H, T, p.d, xs, (A*)nullptr, XS, p.g1, p.eps, smem);
+  rows_to_lds<A, true>(p.H, T, p.d, xs, (A*)nullptr, XS, p.g1, p.eps, smem,
+                       p.trace ? p.trace + (long long)blockIdx.x * kTraceStride + 2 + 2 * kBarriers : nullptr);
+  trace_x(p, 5);
   const int RTq = p.nq / 16, RTkv = (p.kvw + 15) / 16, KT = p.d / TK, S = p.sch.s_q, NT = KT / S;
   const int U = (RTq + RTkv) * S;
   int u0, u1;
@@ -199,7 +195,9 @@ __device__ __forceinline__ void rope_pair(float& v0, float& v1, long long pos, i
 }
 
 template <int KF>
-__device__ __forceinline__ void phase_rope_kv(const LayerParams& p, int L) {
+// Work items are spread over the threads [tid0, tid0 + nthreads) of the grid
+// given by the caller (`tid` is this thread's index in that range).
+__device__ __forceinline__ void phase_rope_kv(const LayerParams& p, int L, int tid, int nthreads) {
   const int T = p.T, S = p.sch.s_q, nrow = p.nq + p.kvw, dr2 = p.dr / 2;
   const int per_t = p.dc + dr2 + p.nh * dr2;
   const float* part = p.qkv_part;
@@ -208,7 +206,7 @@ __device__ __forceinline__ void phase_rope_kv(const LayerParams& p, int L) {
     for (int s = 0; s < S; ++s) v += part[((long long)s * T + t) * nrow + idx];
     return v;
   };
-  for (int it = blockIdx.x * kThreads + threadIdx.x; it < T * per_t; it += gridDim.x * kThreads) {
+  for (int it = tid; it < T * per_t; it += nthreads) {
     const int t = it / per_t, r = it - t * per_t;
     const long long pos = (long long)L + t;
     if (r < p.dc) {
@@ -283,7 +281,7 @@ __device__ __forceinline__ void phase_absorb(const LayerParams& p) {
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, j = lane & 15, g = lane >> 4;
   const int jj = j < T ? j : T - 1;
   const int RT = p.dc / 16, KT = p.dh / TK, U = p.nh * RT;
-  for (int u = blockIdx.x * kWaves + w; u < U; u += gridDim.x * kWaves) {
+  for (int u = blockIdx.x + gridDim.x * w; u < U; u += gridDim.x * kWaves) {
     const int h = u / RT, rt = u - h * RT;
     const uint8_t* tiles = p.wuk + (long long)u * KT * 1024 + lane * 16;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -518,7 +516,7 @@ __device__ __forceinline__ void phase_attention(const LayerParams& p, int L, cha
     // of the latent into z (the counters are cleared at kernel start)
     wg_release_begin();
     if (threadIdx.x == 0) {
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      release_agent();
       __hip_atomic_fetch_add(&p.att_cnt[qt], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       const uint64_t t0 = clock100();
       int ok = 1;
@@ -530,7 +528,7 @@ __device__ __forceinline__ void phase_attention(const LayerParams& p, int L, cha
           break;
         }
       }
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      acquire_agent();
       *flag = ok;
     }
     __syncthreads();
@@ -587,37 +585,53 @@ __device__ __forceinline__ void phase_attention(const LayerParams& p, int L, cha
 }
 
 // ------------------------------------------------------------------ P3  o = W_UV z
+// One unit (head h, 16 rows of d_head, all d_latent columns) per workgroup at a
+// time; the 8 waves split the unit's tiles, load their tiles and z slices in
+// one round trip, and the partial blocks are summed in LDS in wave order.
 template <int AF>
-__device__ __forceinline__ void phase_uv(const LayerParams& p) {
+__device__ __forceinline__ void phase_uv(const LayerParams& p, char* smem) {
   constexpr int TK = tile_k(AF);
   constexpr int EPL = TK / 4;
+  constexpr int CMAX = 2;              // tiles per wave: d_latent / tile_k <= 16
   const int T = p.T;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, j = lane & 15, g = lane >> 4;
   const int jj = j < T ? j : T - 1;
   const int RT = p.dh / 16, KT = p.dc / TK, U = p.nh * RT;
-  for (int u = blockIdx.x * kWaves + w; u < U; u += gridDim.x * kWaves) {
+  const int c = (KT + kWaves - 1) / kWaves;
+  float* red = reinterpret_cast<float*>(smem);      // [kWaves][64][4]
+  for (int u = blockIdx.x; u < U; u += gridDim.x) {
     const int h = u / RT, rt = u - h * RT;
     const uint8_t* tiles = p.wuv + (long long)u * KT * 1024 + lane * 16;
     const float* zr = p.z + ((long long)jj * p.nh + h) * p.dc + g * EPL;
+    u32x4 at[CMAX];
+    typename BReg<AF>::T bt[CMAX];
+#pragma unroll
+    for (int i = 0; i < CMAX; ++i) {
+      const int kt = w * c + i;
+      if (i < c && kt < KT) {
+        at[i] = ld_stream16(tiles + kt * 1024);
+        bt[i] = load_b<AF>(zr + kt * TK);
+      }
+    }
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    constexpr int KB = 8;
-    for (int k0 = 0; k0 < KT; k0 += KB) {
-      u32x4 at[KB];
-      typename BReg<AF>::T bt[KB];
 #pragma unroll
-      for (int i = 0; i < KB; ++i)
-        if (k0 + i < KT) {
-          at[i] = ld_stream16(tiles + (k0 + i) * 1024);
-          bt[i] = load_b<AF>(zr + (k0 + i) * TK);
-        }
-#pragma unroll
-      for (int i = 0; i < KB; ++i)
-        if (k0 + i < KT) acc = tile_mma_reg<AF>(at[i], bt[i], acc);
+    for (int i = 0; i < CMAX; ++i) {
+      const int kt = w * c + i;
+      if (i < c && kt < KT) acc = tile_mma_reg<AF>(at[i], bt[i], acc);
     }
-    if (j < T) {
+    *reinterpret_cast<f32x4*>(red + (w * 64 + lane) * 4) = acc;
+    __syncthreads();
+    if (threadIdx.x < 256) {
+      const int col = threadIdx.x & 15, row = threadIdx.x >> 4;
+      const int l = (row >> 2) * 16 + col, e = row & 3;
+      if (col < T) {
+        float v = 0.f;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) p.o[(long long)j * p.nh * p.dh + h * p.dh + rt * 16 + 4 * g + e] = acc[e];
+        for (int ww = 0; ww < kWaves; ++ww) v += red[(ww * 64 + l) * 4 + e];
+        p.o[(long long)col * p.nh * p.dh + h * p.dh + rt * 16 + row] = v;
+      }
     }
+    __syncthreads();
   }
 }
 
@@ -635,6 +649,7 @@ __device__ __forceinline__ void phase_wo(const LayerParams& p, char* smem) {
   split_range(U, gridDim.x, blockIdx.x, u0, u1);
   if (u1 <= u0) return;
   rows_to_lds<A, false>(p.o, T, K, xs, (A*)nullptr, XS, nullptr, 0.f, smem);
+  trace_x(p, 6);
   const A* bl = b_lane<A>(xs, XS, T, TK);
   struct Src {
     const uint8_t* wo; int KT; const A* bl;
@@ -653,39 +668,99 @@ __device__ __forceinline__ void phase_wo(const LayerParams& p, char* smem) {
   stream_units_wg<AF, false, false>(u0, u1, KT, T, src, epi, red, p.dummy);
 }
 
+// ------------------------------------------------------------------ gate/up units
+// Unit u = (slot s0 + u / RT, 16 rows rt = u % RT of d_ff): h = silu(W1 x') * W3 x'
+// for all T rows, W1 and W3 tiles interleaved in the packed expert block.
+// blk[i] is the packed block of slot s0 + i.
+template <int EF, bool WAVE>
+__device__ __forceinline__ void gateup_units(const LayerParams& p, const uint8_t* const* blk, int s0, int u0, int u1,
+                                             const typename Act<EF>::T* xs, float* red) {
+  typedef typename Act<EF>::T A;
+  constexpr int TK = tile_k(EF);
+  const int T = p.T, XS = p.d + kXPad;
+  const int RT = p.f / 16, KT = p.d / TK;
+  const A* bl = b_lane<A>(xs, XS, T, TK);
+  const int nbk = (p.d + 127) / 128;
+  struct Src {
+    const uint8_t* const* blk; int RT, KT, nbk; const A* bl; long long sc_off, sc3_off;
+    __device__ const uint8_t* base(int u) const {
+      const int sl = u / RT, rt = u - sl * RT;
+      return blk[sl] + (long long)rt * KT * 2048;
+    }
+    __device__ const A* bbase(int) const { return bl; }
+    __device__ const float* sbase(int u) const {
+      const int sl = u / RT, rt = u - sl * RT;
+      return reinterpret_cast<const float*>(blk[sl] + sc_off) + (rt >> 3) * nbk;
+    }
+    __device__ const float* sbase2(int u) const {
+      const int sl = u / RT, rt = u - sl * RT;
+      return reinterpret_cast<const float*>(blk[sl] + sc3_off) + (rt >> 3) * nbk;
+    }
+  };
+  const long long nsc13 = (long long)((p.f + 127) / 128) * nbk;
+  const long long sc_off = p.exp_w13_bytes + p.exp_w2_bytes;
+  Src src{blk, RT, KT, nbk, bl, sc_off, sc_off + nsc13 * 4};
+  float* hb = p.hbuf;
+  const int f = p.f;
+  auto epi = [=](int u, int row, int col, float v, float v2) {
+    const int sl = s0 + u / RT, rt = u % RT;
+    const float sg = v / (1.0f + expf(-v));
+    hb[((long long)sl * T + col) * f + rt * 16 + row] = sg * v2;
+  };
+  if constexpr (WAVE) stream_units_wave<EF, true>(u0, u1, KT, T, src, epi, p.dummy);
+  else stream_units_wg<EF, true, false>(u0, u1, KT, T, src, epi, red, p.dummy);
+}
+
+// The shared experts do not depend on routing: when the grid has workgroups
+// beyond the router's E/16 units, those run the shared experts' gate/up in the
+// router phase (into slots 0 .. n_shared-1).
+__device__ __forceinline__ bool shared_early(const LayerParams& p) {
+  return p.nshared > 0 && (int)gridDim.x > p.E / 16;
+}
+
 // ------------------------------------------------------------------ P5 router
-template <int AF>
+template <int AF, int EF>
 __device__ __forceinline__ void phase_router(const LayerParams& p, char* smem) {
   typedef typename Act<AF>::T A;
   constexpr int TK = tile_k(AF);
   const int T = p.T, XS = p.d + kXPad;
   LdsPlan lp(p, sizeof(A));
   A* xs = reinterpret_cast<A*>(smem);
+  const int RT = p.E / 16;              // router units: 16 experts, all of d_model
+  const bool early = shared_early(p);
+  if (early && (int)blockIdx.x >= RT) {
+    rows_to_lds<A, true>(p.hp, T, p.d, xs, (A*)nullptr, XS, p.g2, p.eps, smem);
+    trace_x(p, 7);
+    const int nwg = (int)gridDim.x - RT, U = p.nshared * (p.f / 16);
+    int u0, u1;
+    split_range(U, nwg, (int)blockIdx.x - RT, u0, u1);
+    gateup_units<EF, false>(p, p.experts + p.E, 0, u0, u1, xs, reinterpret_cast<float*>(smem + lp.xb));
+    return;
+  }
   A* xlo = AF == MK_FMT_F32 ? (A*)nullptr : reinterpret_cast<A*>(smem + lp.xb);
   float* red = reinterpret_cast<float*>(smem + 2 * lp.xb);
   rows_to_lds<A, true>(p.hp, T, p.d, xs, xlo, XS, p.g2, p.eps, smem);
-  const int KT = p.d / TK, S = p.sch.s_r, NT = KT / S, RT = p.E / 16;
-  const int U = RT * S;
+  trace_x(p, 7);
+  const int KT = p.d / TK;
   int u0, u1;
-  split_range(U, gridDim.x, blockIdx.x, u0, u1);
+  if (early) {
+    u0 = blockIdx.x;
+    u1 = u0 + 1;
+  } else {
+    split_range(RT, gridDim.x, blockIdx.x, u0, u1);
+  }
   const A* bl = b_lane<A>(xs, XS, T, TK);
   struct Src {
-    const uint8_t* wr; int KT, S, NT; const A* bl; long long lo_off;
-    __device__ const uint8_t* base(int u) const {
-      const int rt = u / S, s = u - rt * S;
-      return wr + ((long long)rt * KT + s * NT) * 1024;
-    }
-    __device__ const A* bbase(int u) const { return bl + (u % S) * NT * TK; }
+    const uint8_t* wr; int KT; const A* bl; long long lo_off;
+    __device__ const uint8_t* base(int u) const { return wr + (long long)u * KT * 1024; }
+    __device__ const A* bbase(int) const { return bl; }
     __device__ const float* sbase(int) const { return nullptr; }
     __device__ const float* sbase2(int) const { return nullptr; }
-  } src{p.wr, KT, S, NT, bl, (long long)(lp.xb / (int)sizeof(A))};
-  float* lp_out = p.logit_part;
+  } src{p.wr, KT, bl, (long long)(lp.xb / (int)sizeof(A))};
+  float* lg = p.logit_part;
   const int E = p.E;
-  auto epi = [=](int u, int row, int col, float v, float) {
-    int rt = u / S, s = u - rt * S;
-    lp_out[((long long)s * T + col) * E + rt * 16 + row] = v;
-  };
-  stream_units_wg<AF, false, AF != MK_FMT_F32>(u0, u1, NT, T, src, epi, red, p.dummy);
+  auto epi = [=](int u, int row, int col, float v, float) { lg[(long long)col * E + u * 16 + row] = v; };
+  stream_units_wg<AF, false, AF != MK_FMT_F32>(u0, u1, KT, T, src, epi, red, p.dummy);
 }
 
 // ------------------------------------------------------------------ P6 routing + gate/up
@@ -720,66 +795,114 @@ __device__ __forceinline__ RouteLds route_lds(const LayerParams& p, char* smem, 
   return r;
 }
 
+// Orderable key of a float: a > b  <=>  fkey(a) > fkey(b) (for non-NaN values).
+__device__ __forceinline__ uint32_t fkey(float v) {
+  const uint32_t b = __float_as_uint(v);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ unsigned long long lanemask_lt() {
+  const int lane = threadIdx.x & 63;
+  return lane ? (~0ull >> (64 - lane)) : 0ull;
+}
+
 // softmax over all experts, top-k by logit (ties to the lower index), gates =
-// selected probabilities renormalised; then the ascending list of distinct
-// selected experts followed by the shared experts.  Identical in every workgroup.
-__device__ __forceinline__ void route(const LayerParams& p, const RouteLds& r) {
-  const int T = p.T, E = p.E, K = p.topk;
-  for (int i = threadIdx.x; i < T * E; i += kThreads) {
-    const int t = i / E, e = i - t * E;
-    float v = 0.f;
-    for (int s = 0; s < p.sch.s_r; ++s) v += p.logit_part[((long long)s * T + t) * E + e];
-    if (p.rbias) v += p.rbias[e];
-    r.lg[i] = v;
-  }
-  for (int i = threadIdx.x; i < E; i += kThreads) r.flags[i] = 0;
-  __syncthreads();
+// selected probabilities renormalised; then the slot list: the shared experts
+// first, then the distinct selected experts in ascending order.  Identical in
+// every workgroup.  Wave t < T handles token t with its logits in registers
+// (lane l holds experts l, l + 64, ...; absent ones get key 0, below every
+// real key): the k-th largest key is found bit by bit (32 ballot/popcount
+// rounds), then the experts above it, plus the lowest-indexed ones equal to
+// it, are compacted in ascending expert order.
+template <int EPL>
+__device__ __forceinline__ void route_token(const LayerParams& p, const RouteLds& r) {
+  const int E = p.E, K = p.topk;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  if (w < T) {
-    const float* lg = r.lg + w * E;
-    float mx = -INFINITY;
-    for (int e = lane; e < E; e += 64) mx = fmaxf(mx, lg[e]);
-    mx = wave_max(mx);
-    float se = 0.f;
-    for (int e = lane; e < E; e += 64) se += __expf(lg[e] - mx);
-    se = wave_sum(se);
-    unsigned long long taken = 0;      // lane-local bit i <-> expert lane + 64*i
-    float psel = 0.f;
-    for (int k = 0; k < K; ++k) {
-      float bv = -INFINITY;
-      int bi = 0x7fffffff;
-      for (int i = 0, e = lane; e < E; ++i, e += 64) {
-        if (!((taken >> i) & 1ull)) {
-          const float v = lg[e];
-          if (v > bv || (v == bv && e < bi)) { bv = v; bi = e; }
-        }
-      }
+  float lv[EPL];
+  float bv[EPL];
 #pragma unroll
-      for (int o = 32; o > 0; o >>= 1) {
-        const float ov = __shfl_xor(bv, o);
-        const int oi = __shfl_xor(bi, o);
-        if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-      }
-      if (bi >= E) bi = 0;            // only for non-finite logits; keeps indices in range
-      if ((bi & 63) == lane) taken |= 1ull << (bi >> 6);
-      const float pr = __expf(bv - mx) / se;
-      psel += pr;
-      if (lane == 0) {
-        r.sel[w * kMaxTopK + k] = bi;
-        r.gate[w * kMaxTopK + k] = pr;
-      }
+  for (int i = 0; i < EPL; ++i) {
+    const int e = min(lane + 64 * i, E - 1);
+    lv[i] = p.logit_part[(long long)w * E + e];
+    bv[i] = p.rbias ? p.rbias[e] : 0.f;
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    lv[i] += bv[i];
+    mx = fmaxf(mx, lv[i]);             // clamped duplicates do not change the max
+  }
+  mx = wave_max(mx);
+  float se = 0.f;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i)
+    if (lane + 64 * i < E) se += __expf(lv[i] - mx);
+  se = wave_sum(se);
+  trace_x(p, 12);
+  uint32_t key[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) key[i] = lane + 64 * i < E ? fkey(lv[i]) : 0u;
+  uint32_t thr = 0u;                    // the K-th largest key
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t cand = thr | (1u << b);
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) cnt += __popcll(__ballot(key[i] >= cand));
+    if (cnt >= K) thr = cand;
+  }
+  int n_gt = 0;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) n_gt += __popcll(__ballot(key[i] > thr));
+  const int need_eq = K - n_gt;
+  const unsigned long long lt = lanemask_lt();
+  int base_eq = 0, base = 0;
+  float ps = 0.f;
+  bool sel[EPL];
+  float pr[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const unsigned long long meq = __ballot(key[i] == thr);
+    const int rank_eq = base_eq + __popcll(meq & lt);
+    base_eq += __popcll(meq);
+    sel[i] = key[i] > thr || (key[i] == thr && rank_eq < need_eq);
+    pr[i] = __expf(lv[i] - mx) / se;
+    ps += sel[i] ? pr[i] : 0.f;
+  }
+  const float psel = wave_sum(ps);
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const unsigned long long m = __ballot(sel[i]);
+    if (sel[i]) {
+      const int k = base + __popcll(m & lt);
+      r.sel[w * kMaxTopK + k] = lane + 64 * i;
+      r.gate[w * kMaxTopK + k] = pr[i] / psel;
     }
-    if (lane == 0)
-      for (int k = 0; k < K; ++k) r.gate[w * kMaxTopK + k] = r.gate[w * kMaxTopK + k] / psel;
+    base += __popcll(m);
+  }
+  if (blockIdx.x == 0) {
+#pragma unroll
+    for (int i = 0; i < EPL; ++i)
+      if (lane + 64 * i < E) p.logits[(long long)w * E + lane + 64 * i] = lv[i];
+  }
+}
+
+__device__ __forceinline__ void route(const LayerParams& p, const RouteLds& r) {
+  const int T = p.T, E = p.E, K = p.topk, S0 = p.nshared;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  for (int i = threadIdx.x; i < E; i += kThreads) r.flags[i] = 0;
+  if (w < T) {
+    if (E <= 512) route_token<8>(p, r);
+    else route_token<kMaxExperts / 64>(p, r);
   }
   __syncthreads();
+  trace_x(p, 13);
   if (threadIdx.x < T * K) {
     const int t = threadIdx.x / K, k = threadIdx.x - t * K;
     r.flags[r.sel[t * kMaxTopK + k]] = 1;
   }
   __syncthreads();
   if (w == 0) {
-    int base = 0;
+    if (lane < S0) r.slots[lane] = E + lane;
+    int base = S0;
     for (int c0 = 0; c0 < E; c0 += 64) {
       const int e = c0 + lane;
       const int f = e < E ? r.flags[e] : 0;
@@ -791,8 +914,7 @@ __device__ __forceinline__ void route(const LayerParams& p, const RouteLds& r) {
       }
       base += __popcll(m);
     }
-    if (lane < p.nshared) r.slots[base + lane] = E + lane;
-    if (lane == 0) *r.nslots = base + p.nshared;
+    if (lane == 0) *r.nslots = base;
   }
   __syncthreads();
   if (threadIdx.x < T * K) {
@@ -807,7 +929,6 @@ __device__ __forceinline__ void route(const LayerParams& p, const RouteLds& r) {
       p.route_sel[i] = r.sel[t * kMaxTopK + k];
       p.route_gate[i] = r.gate[t * kMaxTopK + k];
     }
-    for (int i = threadIdx.x; i < T * E; i += kThreads) p.logits[i] = r.lg[i];
     if (threadIdx.x == 0) {
       p.bar->slots_sum += (unsigned long long)*r.nslots;
       p.bar->launches += 1ull;
@@ -819,47 +940,19 @@ template <int AF, int EF>
 __device__ __forceinline__ void phase_route_gateup(const LayerParams& p, char* smem) {
   typedef typename Act<EF>::T A;
   static_assert((AF == MK_FMT_F32) == (EF == MK_FMT_F32), "activation types must agree");
-  constexpr int TK = tile_k(EF);
-  const int T = p.T, XS = p.d + kXPad;
   LdsPlan lp(p, sizeof(A));
   const A* xs = reinterpret_cast<const A*>(smem);      // x' (hi part) from P5
   float* red = reinterpret_cast<float*>(smem + lp.xb);
   RouteLds r = route_lds(p, smem, lp.xb);
   route(p, r);
+  trace_x(p, 8);
+  const int s0 = shared_early(p) ? p.nshared : 0;     // slots whose gate/up ran in P5
   const int ns = *r.nslots;
-  const int RT = p.f / 16, KT = p.d / TK, U = ns * RT;
+  const int U = (ns - s0) * (p.f / 16);
   int u0, u1;
   split_range(U, gridDim.x, blockIdx.x, u0, u1);
-  const A* bl = b_lane<A>(xs, XS, T, TK);
-  const int nbk = (p.d + 127) / 128;
-  struct Src {
-    const uint8_t* const* blk; int RT, KT, nbk; const A* bl; long long sc_off, sc3_off;
-    __device__ const uint8_t* base(int u) const {
-      const int sl = u / RT, rt = u - sl * RT;
-      return blk[sl] + (long long)rt * KT * 2048;
-    }
-    __device__ const A* bbase(int) const { return bl; }
-    __device__ const float* sbase(int u) const {
-      const int sl = u / RT, rt = u - sl * RT;
-      return reinterpret_cast<const float*>(blk[sl] + sc_off) + (rt >> 3) * nbk;
-    }
-    __device__ const float* sbase2(int u) const {
-      const int sl = u / RT, rt = u - sl * RT;
-      return reinterpret_cast<const float*>(blk[sl] + sc3_off) + (rt >> 3) * nbk;
-    }
-  };
-  const long long nsc13 = (long long)((p.f + 127) / 128) * nbk;
-  const long long sc_off = p.exp_w13_bytes + p.exp_w2_bytes;
-  Src src{r.blk, RT, KT, nbk, bl, sc_off, sc_off + nsc13 * 4};
-  float* hb = p.hbuf;
-  const int f = p.f;
-  auto epi = [=](int u, int row, int col, float v, float v2) {
-    const int sl = u / RT, rt = u - sl * RT;
-    const float sg = v / (1.0f + expf(-v));
-    hb[((long long)sl * T + col) * f + rt * 16 + row] = sg * v2;
-  };
-  if (U >= 2 * (int)gridDim.x * kWaves) stream_units_wave<EF, true>(u0, u1, KT, T, src, epi, p.dummy);
-  else stream_units_wg<EF, true, false>(u0, u1, KT, T, src, epi, red, p.dummy);
+  if (U >= 2 * (int)gridDim.x * kWaves) gateup_units<EF, true>(p, r.blk + s0, s0, u0, u1, xs, red);
+  else gateup_units<EF, false>(p, r.blk + s0, s0, u0, u1, xs, red);
 }
 
 // ------------------------------------------------------------------ P7 down projections
@@ -918,6 +1011,7 @@ __device__ __forceinline__ void phase_down(const LayerParams& p, char* smem) {
       for (int sl = sa; sl <= sb; ++sl)
         rows_to_lds<A, false>(p.hbuf + (long long)sl * T * f, T, f, xs + (sl - sa) * slot_elems, (A*)nullptr, XS,
                               nullptr, 0.f, smem);
+      if (u == u0) trace_x(p, 9);
       SrcMulti src{r.blk, RT, KT, nbk, sa, bl, slot_elems, p.exp_w13_bytes, sc2_off};
       stream_units_wave<EF, false>(u, ue, KT, T, src, epi, p.dummy);
       __syncthreads();
@@ -939,13 +1033,13 @@ __device__ __forceinline__ void phase_down(const LayerParams& p, char* smem) {
 // ------------------------------------------------------------------ P8 combine
 __device__ __forceinline__ void phase_combine(const LayerParams& p, char* smem, int xb) {
   RouteLds r = route_lds(p, smem, xb);
-  const int T = p.T, d = p.d, K = p.topk, ns = *r.nslots;
+  const int T = p.T, d = p.d, K = p.topk;
   for (int i = blockIdx.x * kThreads + threadIdx.x; i < T * d; i += gridDim.x * kThreads) {
     const int t = i / d, c = i - t * d;
     float v = p.hp[i];
     for (int k = 0; k < K; ++k)
       v += r.gate[t * kMaxTopK + k] * p.ybuf[((long long)r.slot_of[t * kMaxTopK + k] * T + t) * d + c];
-    for (int s = 0; s < p.nshared; ++s) v += p.ybuf[((long long)(ns - p.nshared + s) * T + t) * d + c];
+    for (int s = 0; s < p.nshared; ++s) v += p.ybuf[((long long)s * T + t) * d + c];
     p.out[i] = v;
   }
 }
@@ -964,19 +1058,31 @@ __global__ __launch_bounds__(kThreads, 1) void layer_kernel(LayerParams p) {
   }
   if (p.trace && threadIdx.x == 0) p.trace[(long long)blockIdx.x * kTraceStride] = (long long)clock100();
   // attention split counters: cleared here, used after two grid barriers
-  if (blockIdx.x == 0 && threadIdx.x < 64) p.att_cnt[threadIdx.x] = 0u;
+  if (blockIdx.x == 0 && threadIdx.x < 64)
+    __hip_atomic_store(&p.att_cnt[threadIdx.x], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   phase_qkv<AF>(p, smem);
   if (!grid_barrier(p, 0, flag)) return;
-  phase_rope_kv<KF>(p, L);
-  phase_absorb<AF>(p);
+  {
+    // absorbed-query units on waves [0, wa) of every workgroup; when they fit
+    // in half the waves, RoPE / KV insert runs on the other half meanwhile
+    const int wa = (p.nh * (p.dc / 16) + (int)gridDim.x - 1) / (int)gridDim.x;
+    if (wa <= kWaves / 2) {
+      if ((int)threadIdx.x < kThreads / 2) phase_absorb<AF>(p);
+      else phase_rope_kv<KF>(p, L, blockIdx.x * (kThreads / 2) + threadIdx.x - kThreads / 2,
+                             gridDim.x * (kThreads / 2));
+    } else {
+      phase_rope_kv<KF>(p, L, blockIdx.x * kThreads + threadIdx.x, gridDim.x * kThreads);
+      phase_absorb<AF>(p);
+    }
+  }
   if (!grid_barrier(p, 1, flag)) return;
   phase_attention<KF, KBMAX, DBMAX>(p, L, smem, flag);
   if (!grid_barrier(p, 2, flag)) return;
-  phase_uv<AF>(p);
+  phase_uv<AF>(p, smem);
   if (!grid_barrier(p, 3, flag)) return;
   phase_wo<AF>(p, smem);
   if (!grid_barrier(p, 4, flag)) return;
-  phase_router<AF>(p, smem);
+  phase_router<AF, EF>(p, smem);
   if (!grid_barrier(p, 5, flag)) return;
   phase_route_gateup<AF, EF>(p, smem);
   if (!grid_barrier(p, 6, flag)) return;

@@ -163,7 +163,9 @@ class DeviceStack:
     """A stack of layers (expert pools shared as the shape says) plus embedding and LM head."""
 
     def __init__(self, s: LayerShape, seed: int = 0, device: int = 0, n_layers: int | None = None,
-                 capacity: int | None = None):
+                 capacity: int | None = None, private_workspaces: bool = False):
+        """private_workspaces: one workspace per layer (so every layer's debug
+        taps survive a model step) instead of one shared by all layers."""
         self.s = s
         n_layers = n_layers or s.n_layers
         cfg = config_of(s)
@@ -180,7 +182,8 @@ class DeviceStack:
                 if pl not in self.pools:
                     self.pools[pl] = ExpertPool(s, seed, pl, device, stager)
                 pool = self.pools[pl]
-            self.layers.append(DeviceLayer(s, seed, l, device, workspace=self.workspace, pool=pool, stager=stager))
+            ws = None if private_workspaces else self.workspace
+            self.layers.append(DeviceLayer(s, seed, l, device, workspace=ws, pool=pool, stager=stager))
         V, d = s.V, s.d
         self.emb = torch.empty((V, d), dtype=torch.int16, device=dev)
         synth.dev_normal_bf16(self.emb.data_ptr(), V * d, seed, synth.stream_id("emb"), recipe.W_SIGMA)

@@ -75,7 +75,8 @@ typedef enum mk_format { MK_FMT_F32 = 0, MK_FMT_BF16 = 1, MK_FMT_FP8_B128 = 2 } 
  * attn_format applies to W_Q, W_DKV, W_UK, W_UV, W_O, W_R (F32 or BF16);
  * expert_format to W1, W3, W2 (F32, BF16 or FP8_B128); kv_format to the cache.
  * Supported shapes: d_model, d_ff multiples of 128; d_head, d_latent multiples
- * of 32; d_rope a multiple of 32; n_experts a multiple of 16; top_k <= 16.
+ * of 32; d_rope a multiple of 32; n_experts a multiple of 16 and <= 1024;
+ * top_k <= 16; d_model, n_heads*d_head and d_ff <= 4608.
  * Formats must be all F32, or attention/KV BF16 with experts BF16 or FP8_B128. */
 typedef struct mk_layer_config {
   int32_t abi_version;       /* must be MK_ABI_VERSION */
@@ -201,8 +202,11 @@ int mk_get_stats(const mk_layer* layer, mk_stats* out);
  * enabling clears the trace buffer (synchronous). */
 int mk_set_trace(mk_layer* layer, int enabled);
 /* Copies the trace of the last step: int64 ticks of a 100 MHz clock,
- * [grid_wgs][2 + 2*barriers_per_step + 8]: start, (arrive, release) per barrier, end,
- * then 8 attention sub-phase stamps (0 where a workgroup had no attention unit). */
+ * [grid_wgs][2 + 2*barriers_per_step + 16]: start, (arrive, release) per barrier, end,
+ * then 16 sub-phase stamps (0 where a workgroup did not reach the mark): 0-4 attention
+ * (query tile staged, key chunks done, wave merge written, split counter, split merge
+ * done), 5 projection input normalised, 6 output-projection input staged, 7 router
+ * input normalised, 8 routing done, 9 first down-projection input staged. */
 int mk_read_trace(mk_layer* layer, int64_t* host_dst, size_t bytes, void* stream);
 /* Barrier wait bound in microseconds (default 2,000,000). */
 int mk_set_barrier_timeout_us(mk_layer* layer, int64_t us);

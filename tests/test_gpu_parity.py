@@ -80,6 +80,31 @@ def test_run_twice_bitwise_identical():
     assert np.array_equal(outs[0][1], outs[1][1])
 
 
+def test_back_to_back_layers_sharing_a_workspace():
+    """Two layers launched back to back on one stream, sharing one workspace,
+    with no host synchronisation in between, give bitwise the results each
+    gives alone (a stale cached line of the first launch would show here)."""
+    from decoder_megakernel_amd import harness
+    s = MID_FP8.with_(T=6, L=40, kv_capacity=64)
+    H1 = torch.from_numpy(recipe.hidden_host(s, 0, 0, step=0)).cuda()
+    H2 = torch.from_numpy(recipe.hidden_host(s, 0, 1, step=1)).cuda()
+    alone = harness.DeviceLayer(s, 0, 1)
+    kva = harness.kv_cache(s, 0, 1)
+    ref = torch.empty_like(H2)
+    alone.step(H2, s.T, kva, s.L, ref)
+    torch.cuda.synchronize()
+    l0 = harness.DeviceLayer(s, 0, 0)
+    l1 = harness.DeviceLayer(s, 0, 1, workspace=l0.workspace)
+    for _ in range(2):
+        kv0, kv1 = harness.kv_cache(s, 0, 0), harness.kv_cache(s, 0, 1)
+        o0, o1 = torch.empty_like(H1), torch.empty_like(H2)
+        l0.step(H1, s.T, kv0, s.L, o0)
+        l1.step(H2, s.T, kv1, s.L, o1)
+        torch.cuda.synchronize()
+        assert np.array_equal(o1.cpu().numpy().view(np.uint32), ref.cpu().numpy().view(np.uint32))
+        assert np.array_equal(kv1.cpu().numpy().view(np.uint16), kva.cpu().numpy().view(np.uint16))
+
+
 def test_verify_rows_match_sequential_single_row_steps():
     """Causal invariant on the GPU: row i of a T-row step equals (to tolerance)
     a single-row step at position L+i on the cache the earlier rows built."""
