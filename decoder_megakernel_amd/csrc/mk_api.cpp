@@ -68,6 +68,7 @@ int check_cfg(const mk_layer_config* c) {
   if (D.d % 128 || D.f % 128) return fail(MK_ERR_UNSUPPORTED_SHAPE, "d_model and d_ff must be multiples of 128");
   if (D.dh % 32 || D.dc % 32 || D.dr % 32) return fail(MK_ERR_UNSUPPORTED_SHAPE, "d_head, d_latent, d_rope must be multiples of 32");
   if (D.E % 16) return fail(MK_ERR_UNSUPPORTED_SHAPE, "n_experts must be a multiple of 16");
+  if ((kMaxT * D.nh + 15) / 16 > 64) return fail(MK_ERR_UNSUPPORTED_SHAPE, "n_heads must be <= 128");
   if (D.E > kMaxExperts) return fail(MK_ERR_UNSUPPORTED_SHAPE, "n_experts must be <= %d", kMaxExperts);
   if (D.topk > kMaxTopK || D.topk > D.E) return fail(MK_ERR_UNSUPPORTED_SHAPE, "top_k must be <= 16 and <= n_experts");
   if (D.nshared < 0 || D.nshared > 1) return fail(MK_ERR_UNSUPPORTED_SHAPE, "n_shared must be 0 or 1");
@@ -512,7 +513,7 @@ int mk_debug_tap(mk_layer* L, int tap, void* host_dst, size_t bytes, void* strea
   switch (tap) {
     case 1: src = (const char*)p.qabs; need = (size_t)T * D.nh * D.dc * 4; break;
     case 2: src = (const char*)p.z; need = (size_t)T * D.nh * D.dc * 4; break;
-    case 3: src = (const char*)p.o; need = (size_t)T * D.nh * D.dh * 4; break;
+    case 3: src = (const char*)p.o; need = (size_t)T * D.nh * D.dh * (D.af == MK_FMT_F32 ? 4 : 2); break;
     case 4: src = (const char*)p.hp; need = (size_t)T * D.d * 4; break;
     case 5: src = (const char*)p.logits; need = (size_t)T * D.E * 4; break;
     case 6: src = (const char*)p.route_sel; need = (size_t)T * D.topk * 4; break;
@@ -608,7 +609,7 @@ int mk_layer_reset(mk_layer* L) {
   hipGetDevice(&cur);
   hipSetDevice(L->dev);
   hipError_t e1 = hipMemset(L->state + L->sl.bar, 0, sizeof(BarrierState));
-  hipError_t e2 = hipMemset(L->state + L->sl.att_cnt, 0, 64 * 4);
+  hipError_t e2 = hipMemset(L->state + L->sl.att_cnt, 0, L->sl.experts - L->sl.att_cnt);
   hipError_t e3 = hipDeviceSynchronize();
   hipSetDevice(cur);
   if (e1 != hipSuccess || e2 != hipSuccess || e3 != hipSuccess) return fail(MK_ERR_HIP, "reset failed");

@@ -89,13 +89,13 @@ struct LayerParams {
   float* att_part;         // [units][16][dc]
   float* att_ml;           // [units][16][2]
   float* z;                // [T][nh][dc]
-  float* o;                // [T][nh*dh]
+  float* o;                // [T][nh*dh] in the activation type (fp32 or bf16)
   float* hp;               // [T][d]
   float* logit_part;       // [T][E] router logits before the bias
   int32_t* route_sel;      // [T][topk]
   float* route_gate;       // [T][topk]
   float* logits;           // [T][E] (written by workgroup 0)
-  float* hbuf;             // [slots][T][f]
+  float* hbuf;             // [slots][T][f] in the expert activation type (fp32 or bf16)
   float* ybuf;             // [slots][T][d]
   const uint8_t* dummy;    // 32 KiB scratch read by the streams' last (discarded) prefetch
   // state

@@ -131,6 +131,32 @@ __device__ __forceinline__ void rows_to_lds(const float* src, int T, int K, A* x
   __syncthreads();
 }
 
+// Copies T <= kMaxT rows of length K already in the operand type A from global
+// memory into LDS (row stride XS): wave w copies row w in 16-byte pieces.
+template <class A>
+__device__ __forceinline__ void rows_copy_lds(const A* src, int T, int K, A* xs, int XS) {
+  constexpr int EPV = 16 / sizeof(A);                  // elements per 16 bytes
+  constexpr int CH = kMaxStageK / EPV / 64;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int nv = K / EPV;
+  if (w < T) {
+    const A* row = src + (long long)w * K;
+    u32x4 v[CH];
+#pragma unroll
+    for (int c = 0; c < CH; ++c)
+      if (lane + 64 * c < nv) v[c] = ld16(row + (lane + 64 * c) * EPV);
+    A* xr = xs + (long long)w * XS;
+#pragma unroll
+    for (int c = 0; c < CH; ++c)
+      if (lane + 64 * c < nv) {
+        const uint2 lo = {v[c][0], v[c][1]}, hi = {v[c][2], v[c][3]};
+        *reinterpret_cast<uint2*>(xr + (lane + 64 * c) * EPV) = lo;
+        *reinterpret_cast<uint2*>(xr + (lane + 64 * c) * EPV + EPV / 2) = hi;
+      }
+  }
+  __syncthreads();
+}
+
 template <class A>
 __device__ __forceinline__ const A* b_lane(const A* xs, int XS, int T, int TK) {
   const int lane = threadIdx.x & 63;
@@ -628,7 +654,8 @@ __device__ __forceinline__ void phase_uv(const LayerParams& p, char* smem) {
         float v = 0.f;
 #pragma unroll
         for (int ww = 0; ww < kWaves; ++ww) v += red[(ww * 64 + l) * 4 + e];
-        p.o[(long long)col * p.nh * p.dh + h * p.dh + rt * 16 + row] = v;
+        reinterpret_cast<typename Act<AF>::T*>(p.o)[(long long)col * p.nh * p.dh + h * p.dh + rt * 16 + row] =
+            to_act<typename Act<AF>::T>(v);
       }
     }
     __syncthreads();
@@ -648,7 +675,7 @@ __device__ __forceinline__ void phase_wo(const LayerParams& p, char* smem) {
   int u0, u1;
   split_range(U, gridDim.x, blockIdx.x, u0, u1);
   if (u1 <= u0) return;
-  rows_to_lds<A, false>(p.o, T, K, xs, (A*)nullptr, XS, nullptr, 0.f, smem);
+  rows_copy_lds<A>(reinterpret_cast<const A*>(p.o), T, K, xs, XS);
   trace_x(p, 6);
   const A* bl = b_lane<A>(xs, XS, T, TK);
   struct Src {
@@ -672,7 +699,8 @@ __device__ __forceinline__ void phase_wo(const LayerParams& p, char* smem) {
 // Unit u = (slot s0 + u / RT, 16 rows rt = u % RT of d_ff): h = silu(W1 x') * W3 x'
 // for all T rows, W1 and W3 tiles interleaved in the packed expert block.
 // blk[i] is the packed block of slot s0 + i.
-template <int EF, bool WAVE>
+// MODE 0: workgroup units [u0, u1); 1: wave units [u0, u1).
+template <int EF, int MODE>
 __device__ __forceinline__ void gateup_units(const LayerParams& p, const uint8_t* const* blk, int s0, int u0, int u1,
                                              const typename Act<EF>::T* xs, float* red) {
   typedef typename Act<EF>::T A;
@@ -700,14 +728,14 @@ __device__ __forceinline__ void gateup_units(const LayerParams& p, const uint8_t
   const long long nsc13 = (long long)((p.f + 127) / 128) * nbk;
   const long long sc_off = p.exp_w13_bytes + p.exp_w2_bytes;
   Src src{blk, RT, KT, nbk, bl, sc_off, sc_off + nsc13 * 4};
-  float* hb = p.hbuf;
+  A* hb = reinterpret_cast<A*>(p.hbuf);
   const int f = p.f;
   auto epi = [=](int u, int row, int col, float v, float v2) {
     const int sl = s0 + u / RT, rt = u % RT;
     const float sg = v / (1.0f + expf(-v));
-    hb[((long long)sl * T + col) * f + rt * 16 + row] = sg * v2;
+    hb[((long long)sl * T + col) * f + rt * 16 + row] = to_act<A>(sg * v2);
   };
-  if constexpr (WAVE) stream_units_wave<EF, true>(u0, u1, KT, T, src, epi, p.dummy);
+  if constexpr (MODE == 1) stream_units_wave<EF, true>(u0, u1, KT, T, src, epi, p.dummy);
   else stream_units_wg<EF, true, false>(u0, u1, KT, T, src, epi, red, p.dummy);
 }
 
@@ -734,7 +762,7 @@ __device__ __forceinline__ void phase_router(const LayerParams& p, char* smem) {
     const int nwg = (int)gridDim.x - RT, U = p.nshared * (p.f / 16);
     int u0, u1;
     split_range(U, nwg, (int)blockIdx.x - RT, u0, u1);
-    gateup_units<EF, false>(p, p.experts + p.E, 0, u0, u1, xs, reinterpret_cast<float*>(smem + lp.xb));
+    gateup_units<EF, 0>(p, p.experts + p.E, 0, u0, u1, xs, reinterpret_cast<float*>(smem + lp.xb));
     return;
   }
   A* xlo = AF == MK_FMT_F32 ? (A*)nullptr : reinterpret_cast<A*>(smem + lp.xb);
@@ -951,8 +979,10 @@ __device__ __forceinline__ void phase_route_gateup(const LayerParams& p, char* s
   const int U = (ns - s0) * (p.f / 16);
   int u0, u1;
   split_range(U, gridDim.x, blockIdx.x, u0, u1);
-  if (U >= 2 * (int)gridDim.x * kWaves) gateup_units<EF, true>(p, r.blk + s0, s0, u0, u1, xs, red);
-  else gateup_units<EF, false>(p, r.blk + s0, s0, u0, u1, xs, red);
+  if (U >= 2 * (int)gridDim.x * kWaves)
+    gateup_units<EF, 1>(p, r.blk + s0, s0, u0, u1, xs, red);
+  else
+    gateup_units<EF, 0>(p, r.blk + s0, s0, u0, u1, xs, red);
 }
 
 // ------------------------------------------------------------------ P7 down projections
@@ -1009,8 +1039,8 @@ __device__ __forceinline__ void phase_down(const LayerParams& p, char* smem) {
       const int ue = min(u1, (sa + 2) * RT);
       const int sb = (ue - 1) / RT;
       for (int sl = sa; sl <= sb; ++sl)
-        rows_to_lds<A, false>(p.hbuf + (long long)sl * T * f, T, f, xs + (sl - sa) * slot_elems, (A*)nullptr, XS,
-                              nullptr, 0.f, smem);
+        rows_copy_lds<A>(reinterpret_cast<const A*>(p.hbuf) + (long long)sl * T * f, T, f, xs + (sl - sa) * slot_elems,
+                         XS);
       if (u == u0) trace_x(p, 9);
       SrcMulti src{r.blk, RT, KT, nbk, sa, bl, slot_elems, p.exp_w13_bytes, sc2_off};
       stream_units_wave<EF, false>(u, ue, KT, T, src, epi, p.dummy);
@@ -1022,7 +1052,7 @@ __device__ __forceinline__ void phase_down(const LayerParams& p, char* smem) {
     while (u < u1) {
       const int sl = u / RT;
       const int ue = min(u1, (sl + 1) * RT);
-      rows_to_lds<A, false>(p.hbuf + (long long)sl * T * f, T, f, xs, (A*)nullptr, XS, nullptr, 0.f, smem);
+      rows_copy_lds<A>(reinterpret_cast<const A*>(p.hbuf) + (long long)sl * T * f, T, f, xs, XS);
       Src src{r.blk[sl], RT, KT, nbk, bl, p.exp_w13_bytes, sc2_off};
       stream_units_wg<EF, false, false>(u, ue, KT, T, src, epi, red, p.dummy);
       u = ue;

@@ -192,8 +192,10 @@ int mk_decode_step(mk_layer* layer, const float* hidden_in, int T, const mk_kv_c
 /* Copies the step's intermediate results from the workspace to host memory
  * (synchronises `stream`).  tap: 0 = Q [T][n_h][d_h+d_r] (q^R rotated),
  * 1 = absorbed query q~ [T][n_h][d_latent], 2 = attention latent z [T][n_h][d_latent],
- * 3 = o [T][n_h*d_head], 4 = post-attention hidden [T][d_model], 5 = router logits
- * [T][n_experts], 6 = selected experts int32 [T][top_k], 7 = gates [T][top_k].
+ * 3 = o [T][n_h*d_head] (fp32 for F32 layers, else bf16 bit patterns: it is kept
+ * in the matrix-core operand format), 4 = post-attention hidden [T][d_model],
+ * 5 = router logits [T][n_experts], 6 = selected experts int32 [T][top_k],
+ * 7 = gates [T][top_k].
  * Valid only after a step on this layer and before another layer reuses the workspace. */
 int mk_debug_tap(mk_layer* layer, int tap, void* host_dst, size_t bytes, void* stream);
 /* Synchronous: reads the device counters of this layer's state. */

@@ -52,13 +52,14 @@ def gpu_step(dl, s, H_dev, kv_dev, L, T=None):
     torch.cuda.synchronize()
     assert dl.layer.sync_status() == MK_OK
     taps = {}
+    o_dt = np.float32 if s.attn_fmt == "f32" else np.uint16     # o is kept in the operand format
     for name, tap, shape, dt in (("Hp", 4, (T, s.d), np.float32), ("logits", 5, (T, s.E), np.float32),
                                  ("sel", 6, (T, s.top_k), np.int32), ("gate", 7, (T, s.top_k), np.float32),
                                  ("z", 2, (T, s.n_h, s.d_c), np.float32), ("qabs", 1, (T, s.n_h, s.d_c), np.float32),
-                                 ("o", 3, (T, s.n_h * s.d_h), np.float32), ("q", 0, (T, s.n_h, s.qw), np.float32)):
+                                 ("o", 3, (T, s.n_h * s.d_h), o_dt), ("q", 0, (T, s.n_h, s.qw), np.float32)):
         buf = np.empty(shape, dt)
         dl.layer.debug_tap(tap, buf)
-        taps[name] = buf
+        taps[name] = oracle.bf16_to_f32(buf) if dt == np.uint16 else buf
     kvn = kv_dev[L:L + T].cpu().numpy()
     return out.cpu().numpy(), kv_to_f32(kvn, s.kv_fmt), taps
 
