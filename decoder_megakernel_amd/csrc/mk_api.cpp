@@ -69,6 +69,7 @@ int check_cfg(const mk_layer_config* c) {
   if (D.dh % 32 || D.dc % 32 || D.dr % 32) return fail(MK_ERR_UNSUPPORTED_SHAPE, "d_head, d_latent, d_rope must be multiples of 32");
   if (D.E % 16) return fail(MK_ERR_UNSUPPORTED_SHAPE, "n_experts must be a multiple of 16");
   if ((kMaxT * D.nh + 15) / 16 > 64) return fail(MK_ERR_UNSUPPORTED_SHAPE, "n_heads must be <= 128");
+  if (D.dh > 16 * kWaves) return fail(MK_ERR_UNSUPPORTED_SHAPE, "d_head must be <= %d", 16 * kWaves);
   if (D.E > kMaxExperts) return fail(MK_ERR_UNSUPPORTED_SHAPE, "n_experts must be <= %d", kMaxExperts);
   if (D.topk > kMaxTopK || D.topk > D.E) return fail(MK_ERR_UNSUPPORTED_SHAPE, "top_k must be <= 16 and <= n_experts");
   if (D.nshared < 0 || D.nshared > 1) return fail(MK_ERR_UNSUPPORTED_SHAPE, "n_shared must be 0 or 1");
@@ -173,7 +174,8 @@ int device_info(int dev, DevInfo* di, LayerKernelFn fn) {
 }
 
 struct WsLayout {
-  size_t qkv_part, qrope, qabs, att_part, att_ml, z, o, hp, logit_part, route_sel, route_gate, logits, hbuf, ybuf, dummy,
+  size_t qkv_part, qrope, qabs, att_part, att_ml, z, o, hp, logit_part, route_sel, route_gate, route_pub, logits, hbuf,
+      ybuf, dummy,
       total;
 };
 struct StLayout {
@@ -199,6 +201,7 @@ WsLayout ws_layout(const Dims& D, const Schedule& s) {
   w.logit_part = take((size_t)T * D.E * 4);
   w.route_sel = take((size_t)T * kMaxTopK * 4);
   w.route_gate = take((size_t)T * kMaxTopK * 4);
+  w.route_pub = take(4096);
   w.logits = take((size_t)T * D.E * 4);
   w.hbuf = take((size_t)slots * T * D.f * 4);
   w.ybuf = take((size_t)slots * T * D.d * 4);
@@ -212,7 +215,7 @@ StLayout st_layout(const Dims& D, const Schedule& s) {
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
   l.bar = take(sizeof(BarrierState));
-  l.att_cnt = take(64 * 4);
+  l.att_cnt = take((kRouteCnt + 1) * 4);
   l.experts = take((size_t)(D.E + D.nshared) * 8);
   l.trace = take((size_t)s.nwg * kTraceStride * 8);
   l.total = off;
@@ -460,6 +463,7 @@ int mk_layer_init(const mk_layer_config* cfg, const mk_layer_weights* w, void* s
   p.logit_part = (float*)(ws + L->wl.logit_part);
   p.route_sel = (int32_t*)(ws + L->wl.route_sel);
   p.route_gate = (float*)(ws + L->wl.route_gate);
+  p.route_pub = (int32_t*)(ws + L->wl.route_pub);
   p.logits = (float*)(ws + L->wl.logits);
   p.hbuf = (float*)(ws + L->wl.hbuf);
   p.ybuf = (float*)(ws + L->wl.ybuf);

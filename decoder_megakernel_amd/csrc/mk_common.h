@@ -11,11 +11,12 @@ constexpr int kThreads = 512;            // threads per workgroup (8 wave64s)
 constexpr int kWaves = kThreads / 64;
 constexpr int kMaxT = MK_MAX_T;          // verify rows the LDS budget is sized for
 constexpr int kXPad = 8;                 // LDS row padding of activation operands (elements)
-constexpr int kBarriers = 8;             // grid barriers in one layer launch
+constexpr int kBarriers = 9;             // grid barriers in one layer launch
 constexpr int kTraceX = 16;              // extra per-workgroup timestamps (sub-phase marks)
 constexpr int kTraceStride = 2 + 2 * kBarriers + kTraceX;
 constexpr int kLdsBytes = 160 * 1024 - 256;
 constexpr int kMaxTopK = 16;
+constexpr int kRouteCnt = 64;            // index of the router-completion counter in att_cnt
 constexpr int kMaxExperts = 1024;        // routed experts per layer (16 logits per lane)
 constexpr int kStageCh = 18;             // float4s per lane when staging one activation row
 constexpr int kMaxStageK = kStageCh * 64 * 4;   // longest activation row (elements)
@@ -94,6 +95,8 @@ struct LayerParams {
   float* logit_part;       // [T][E] router logits before the bias
   int32_t* route_sel;      // [T][topk]
   float* route_gate;       // [T][topk]
+  int32_t* route_pub;      // routing published for the expert phases: [0] slot count,
+                           // [16 + t*topk + k] slot of pick (t, k), 8-byte block pointers from byte 1024
   float* logits;           // [T][E] (written by workgroup 0)
   float* hbuf;             // [slots][T][f] in the expert activation type (fp32 or bf16)
   float* ybuf;             // [slots][T][d]

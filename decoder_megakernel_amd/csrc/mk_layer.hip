@@ -7,14 +7,15 @@
 // Phases, separated by grid barriers (all workgroups are co-resident):
 //   P0  RMSNorm-1 (every workgroup, into LDS) ; [W_Q; W_DKV] x, split-K partials
 //   P1  RoPE on q^R and the shared key, KV insert ; absorbed query q~ = W_UK^T q^C
-//   P2  latent attention, split over (query tile, KV range); the last split of a
-//       query tile to finish merges all splits (log-sum-exp) into z
-//   P3  o = W_UV z
+//   P2  latent attention, split over (query tile, KV range): partial (Z, max, sum)
+//   P3a merge of the KV splits (log-sum-exp) into z
+//   P3b o = W_UV z
 //   P4  H' = H + W_O o
 //   P5  RMSNorm-2 (every workgroup, into LDS) ; router logits on E/16
-//       workgroups, the shared experts' gate+up on the others
-//   P6  softmax / top-k / gates / distinct-expert work list (every workgroup,
-//       identical) ; gate+up projections of every routed expert: silu(W1 x) * W3 x
+//       workgroups, the shared experts' gate+up on the others; the last router
+//       workgroup to finish computes softmax / top-k / gates / the distinct-
+//       expert work list and publishes them
+//   P6  gate+up projections of every routed expert: silu(W1 x) * W3 x
 //   P7  down projections W2 h of every listed expert
 //   P8  out = H' + sum_k gate_k y_k + y_shared
 #include "mk_device.h"
@@ -339,7 +340,9 @@ __device__ __forceinline__ void phase_absorb(const LayerParams& p) {
 // ------------------------------------------------------------------ P2 attention
 // Units (query tile of 16 queries q = t*nh + h, KV range).  Per wave: chunks of
 // 16 keys; S^T = K Q^T on the matrix cores (keys x queries), online softmax per
-// query column, Z^T += C^T P^T with C staged in the wave's LDS slice.
+// query column, Z^T += C^T P^T with C staged in the wave's LDS slice.  The 8
+// waves' states are merged in LDS and the split's partial (Z, running max,
+// running sum) is written out; P3 merges the splits.
 template <int KF>
 struct AttnTypes;
 template <> struct AttnTypes<MK_FMT_BF16> {
@@ -351,18 +354,24 @@ template <> struct AttnTypes<MK_FMT_F32> {
   static constexpr int KBW = 16;
 };
 
+// KV splits per query tile and keys per split (the same in P2 and P3).
+__device__ __forceinline__ void attn_splits(int NQT, int Lt, int& s_kv, int& SK) {
+  s_kv = (int)gridDim.x / NQT;
+  if (s_kv < 1) s_kv = 1;
+  const int nchunk_all = (Lt + 15) / 16;
+  if (s_kv > nchunk_all) s_kv = nchunk_all;
+  SK = ((Lt + s_kv - 1) / s_kv + 15) / 16 * 16;
+}
+
 template <int KF, int KBMAX, int DBMAX>
-__device__ __forceinline__ void phase_attention(const LayerParams& p, int L, char* smem, int* flag) {
+__device__ __forceinline__ void phase_attention(const LayerParams& p, int L, char* smem) {
   typedef typename AttnTypes<KF>::E E;
   constexpr int KBW = AttnTypes<KF>::KBW;
   const int T = p.T, nh = p.nh, dc = p.dc, kvw = p.kvw;
   const int NQ = T * nh, NQT = (NQ + 15) / 16, Lt = L + T;
   const int KB = kvw / KBW, DB = dc / 16;
-  int s_kv = (int)gridDim.x / NQT;
-  if (s_kv < 1) s_kv = 1;
-  const int nchunk_all = (Lt + 15) / 16;
-  if (s_kv > nchunk_all) s_kv = nchunk_all;
-  const int SK = ((Lt + s_kv - 1) / s_kv + 15) / 16 * 16;
+  int s_kv, SK;
+  attn_splits(NQT, Lt, s_kv, SK);
   const int units = NQT * s_kv;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, j = lane & 15, g = lane >> 4;
   const int CS = dc + 8;                               // LDS row stride of a staged chunk
@@ -538,79 +547,82 @@ __device__ __forceinline__ void phase_attention(const LayerParams& p, int L, cha
       }
     }
     trace_x(p, 2);
-    // every split of this query tile waits for its siblings, then merges 1/s_kv
-    // of the latent into z (the counters are cleared at kernel start)
-    wg_release_begin();
-    if (threadIdx.x == 0) {
-      release_agent();
-      __hip_atomic_fetch_add(&p.att_cnt[qt], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const uint64_t t0 = clock100();
-      int ok = 1;
-      while (__hip_atomic_load(&p.att_cnt[qt], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (uint32_t)s_kv) {
-        __builtin_amdgcn_s_sleep(1);
-        if ((long long)(clock100() - t0) > p.timeout_ticks) {
-          __hip_atomic_store(&p.bar->fault, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          ok = 0;
-          break;
-        }
-      }
-      acquire_agent();
-      *flag = ok;
-    }
-    __syncthreads();
-    trace_x(p, 3);
-    if (*flag) {
-      // combination weights per (split, query): exp(m_s - M) / sum_s exp(m_s - M) l_s
-      const int ub = qt * s_kv;
-      float* mm = reinterpret_cast<float*>(smem);          // [s_kv][16]
-      float* cf = mm + s_kv * 16;                          // [s_kv][16]
-      for (int i = threadIdx.x; i < s_kv * 16; i += kThreads) mm[i] = p.att_ml[((long long)ub * 16 + i) * 2];
-      for (int i = threadIdx.x; i < s_kv * 16; i += kThreads) cf[i] = p.att_ml[((long long)ub * 16 + i) * 2 + 1];
-      __syncthreads();
-      if (threadIdx.x < 16) {
-        const int jq = threadIdx.x;
-        float M = -INFINITY;
-        for (int ss = 0; ss < s_kv; ++ss) M = fmaxf(M, mm[ss * 16 + jq]);
-        float den = 0.f;
-        for (int ss = 0; ss < s_kv; ++ss) {
-          const float wgt = mm[ss * 16 + jq] == -INFINITY ? 0.f : __expf(mm[ss * 16 + jq] - M);
-          mm[ss * 16 + jq] = wgt;
-          den += wgt * cf[ss * 16 + jq];
-        }
-        for (int ss = 0; ss < s_kv; ++ss) cf[ss * 16 + jq] = mm[ss * 16 + jq] / den;
-      }
-      __syncthreads();
-      // this split's share of the items, in storage order: item i = (block i / 64, lane i % 64)
-      const int n_items = DB * 64;
-      int i0, i1;
-      split_range(n_items, s_kv, s, i0, i1);
-      const f32x4* zb = reinterpret_cast<const f32x4*>(p.att_part + (long long)ub * 16 * dc);
-      const long long sstride = 16LL * dc / 4;
-      for (int it = i0 + threadIdx.x; it < i1; it += kThreads) {
-        const int db = it >> 6, ln = it & 63, jq = ln & 15, gq = ln >> 4;
-        const int qq = qt * 16 + jq;
-        if (qq >= NQ) continue;
-        const f32x4* zp = zb + it;
-        f32x4 a0 = {0.f, 0.f, 0.f, 0.f};
-        int ss = 0;
-        for (; ss + 8 <= s_kv; ss += 8) {
-          f32x4 zz[8];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) zz[i] = zp[(ss + i) * sstride];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) a0 += zz[i] * cf[(ss + i) * 16 + jq];
-        }
-        for (; ss < s_kv; ++ss) a0 += zp[ss * sstride] * cf[ss * 16 + jq];
-        *reinterpret_cast<f32x4*>(p.z + (long long)qq * dc + db * 16 + gq * 4) = a0;
-      }
-      __syncthreads();
-      trace_x(p, 4);
-    }
-    __syncthreads();
   }
 }
 
-// ------------------------------------------------------------------ P3  o = W_UV z
+// ------------------------------------------------------------------ P3a  merge of the KV splits
+// Unit (query tile qt, split s) as in P2: it merges 1/s_kv of the tile's latent
+// items (item i = (16-dim block i / 64, lane i % 64) of the partial layout)
+// over all splits, with weights exp(m_s - M) / sum_s exp(m_s - M) l_s, into z.
+// Four threads share an item, each summing every fourth split.
+__device__ __forceinline__ void phase_merge(const LayerParams& p, int L, char* smem) {
+  const int T = p.T, nh = p.nh, dc = p.dc;
+  const int NQ = T * nh, NQT = (NQ + 15) / 16;
+  int s_kv, SK;
+  attn_splits(NQT, L + T, s_kv, SK);
+  const int units = NQT * s_kv, DB = dc / 16;
+  float* mm = reinterpret_cast<float*>(smem);          // [s_kv][16] running max, then weight
+  float* cf = mm + s_kv * 16;                          // [s_kv][16] running sum
+  float* red = cf + s_kv * 16;                         // [4][128][4] partial sums of the 4 thread groups
+  for (int u = blockIdx.x; u < units; u += gridDim.x) {
+    const int qt = u / s_kv, s = u - qt * s_kv;
+    const int ub = qt * s_kv;
+    for (int i = threadIdx.x; i < s_kv * 16; i += kThreads) {
+      mm[i] = p.att_ml[((long long)ub * 16 + i) * 2];
+      cf[i] = p.att_ml[((long long)ub * 16 + i) * 2 + 1];
+    }
+    __syncthreads();
+    if (threadIdx.x < 16) {
+      const int jq = threadIdx.x;
+      float M = -INFINITY;
+      for (int ss = 0; ss < s_kv; ++ss) M = fmaxf(M, mm[ss * 16 + jq]);
+      float den = 0.f;
+      for (int ss = 0; ss < s_kv; ++ss) {
+        const float wgt = mm[ss * 16 + jq] == -INFINITY ? 0.f : __expf(mm[ss * 16 + jq] - M);
+        mm[ss * 16 + jq] = wgt;
+        den += wgt * cf[ss * 16 + jq];
+      }
+      for (int ss = 0; ss < s_kv; ++ss) mm[ss * 16 + jq] /= den;
+    }
+    __syncthreads();
+    int i0, i1;
+    split_range(DB * 64, s_kv, s, i0, i1);
+    const f32x4* zb = reinterpret_cast<const f32x4*>(p.att_part + (long long)ub * 16 * dc);
+    const long long sstride = 16LL * dc / 4;
+    const int quarter = threadIdx.x >> 7, slot = threadIdx.x & 127;
+    for (int base = i0; base < i1; base += 128) {
+      const int it = base + slot;
+      const bool ok = it < i1;
+      const int ln = it & 63, jq = ln & 15;
+      f32x4 a0 = {0.f, 0.f, 0.f, 0.f};
+      if (ok) {
+        const f32x4* zp = zb + it;
+        int ss = quarter;
+        for (; ss + 12 < s_kv; ss += 16) {
+          f32x4 zz[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) zz[i] = zp[(ss + 4 * i) * sstride];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) a0 += zz[i] * mm[(ss + 4 * i) * 16 + jq];
+        }
+        for (; ss < s_kv; ss += 4) a0 += zp[ss * sstride] * mm[ss * 16 + jq];
+      }
+      *reinterpret_cast<f32x4*>(red + (quarter * 128 + slot) * 4) = a0;
+      __syncthreads();
+      if (threadIdx.x < 128 && ok) {
+        f32x4 v = *reinterpret_cast<const f32x4*>(red + slot * 4);
+#pragma unroll
+        for (int q4 = 1; q4 < 4; ++q4) v += *reinterpret_cast<const f32x4*>(red + (q4 * 128 + slot) * 4);
+        const int db = it >> 6, gq = ln >> 4;
+        const int qq = qt * 16 + jq;
+        if (qq < NQ) *reinterpret_cast<f32x4*>(p.z + (long long)qq * dc + db * 16 + gq * 4) = v;
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// ------------------------------------------------------------------ P3b  o = W_UV z
 // One unit (head h, 16 rows of d_head, all d_latent columns) per workgroup at a
 // time; the 8 waves split the unit's tiles, load their tiles and z slices in
 // one round trip, and the partial blocks are summed in LDS in wave order.
@@ -695,103 +707,7 @@ __device__ __forceinline__ void phase_wo(const LayerParams& p, char* smem) {
   stream_units_wg<AF, false, false>(u0, u1, KT, T, src, epi, red, p.dummy);
 }
 
-// ------------------------------------------------------------------ gate/up units
-// Unit u = (slot s0 + u / RT, 16 rows rt = u % RT of d_ff): h = silu(W1 x') * W3 x'
-// for all T rows, W1 and W3 tiles interleaved in the packed expert block.
-// blk[i] is the packed block of slot s0 + i.
-// MODE 0: workgroup units [u0, u1); 1: wave units [u0, u1).
-template <int EF, int MODE>
-__device__ __forceinline__ void gateup_units(const LayerParams& p, const uint8_t* const* blk, int s0, int u0, int u1,
-                                             const typename Act<EF>::T* xs, float* red) {
-  typedef typename Act<EF>::T A;
-  constexpr int TK = tile_k(EF);
-  const int T = p.T, XS = p.d + kXPad;
-  const int RT = p.f / 16, KT = p.d / TK;
-  const A* bl = b_lane<A>(xs, XS, T, TK);
-  const int nbk = (p.d + 127) / 128;
-  struct Src {
-    const uint8_t* const* blk; int RT, KT, nbk; const A* bl; long long sc_off, sc3_off;
-    __device__ const uint8_t* base(int u) const {
-      const int sl = u / RT, rt = u - sl * RT;
-      return blk[sl] + (long long)rt * KT * 2048;
-    }
-    __device__ const A* bbase(int) const { return bl; }
-    __device__ const float* sbase(int u) const {
-      const int sl = u / RT, rt = u - sl * RT;
-      return reinterpret_cast<const float*>(blk[sl] + sc_off) + (rt >> 3) * nbk;
-    }
-    __device__ const float* sbase2(int u) const {
-      const int sl = u / RT, rt = u - sl * RT;
-      return reinterpret_cast<const float*>(blk[sl] + sc3_off) + (rt >> 3) * nbk;
-    }
-  };
-  const long long nsc13 = (long long)((p.f + 127) / 128) * nbk;
-  const long long sc_off = p.exp_w13_bytes + p.exp_w2_bytes;
-  Src src{blk, RT, KT, nbk, bl, sc_off, sc_off + nsc13 * 4};
-  A* hb = reinterpret_cast<A*>(p.hbuf);
-  const int f = p.f;
-  auto epi = [=](int u, int row, int col, float v, float v2) {
-    const int sl = s0 + u / RT, rt = u % RT;
-    const float sg = v / (1.0f + expf(-v));
-    hb[((long long)sl * T + col) * f + rt * 16 + row] = to_act<A>(sg * v2);
-  };
-  if constexpr (MODE == 1) stream_units_wave<EF, true>(u0, u1, KT, T, src, epi, p.dummy);
-  else stream_units_wg<EF, true, false>(u0, u1, KT, T, src, epi, red, p.dummy);
-}
-
-// The shared experts do not depend on routing: when the grid has workgroups
-// beyond the router's E/16 units, those run the shared experts' gate/up in the
-// router phase (into slots 0 .. n_shared-1).
-__device__ __forceinline__ bool shared_early(const LayerParams& p) {
-  return p.nshared > 0 && (int)gridDim.x > p.E / 16;
-}
-
-// ------------------------------------------------------------------ P5 router
-template <int AF, int EF>
-__device__ __forceinline__ void phase_router(const LayerParams& p, char* smem) {
-  typedef typename Act<AF>::T A;
-  constexpr int TK = tile_k(AF);
-  const int T = p.T, XS = p.d + kXPad;
-  LdsPlan lp(p, sizeof(A));
-  A* xs = reinterpret_cast<A*>(smem);
-  const int RT = p.E / 16;              // router units: 16 experts, all of d_model
-  const bool early = shared_early(p);
-  if (early && (int)blockIdx.x >= RT) {
-    rows_to_lds<A, true>(p.hp, T, p.d, xs, (A*)nullptr, XS, p.g2, p.eps, smem);
-    trace_x(p, 7);
-    const int nwg = (int)gridDim.x - RT, U = p.nshared * (p.f / 16);
-    int u0, u1;
-    split_range(U, nwg, (int)blockIdx.x - RT, u0, u1);
-    gateup_units<EF, 0>(p, p.experts + p.E, 0, u0, u1, xs, reinterpret_cast<float*>(smem + lp.xb));
-    return;
-  }
-  A* xlo = AF == MK_FMT_F32 ? (A*)nullptr : reinterpret_cast<A*>(smem + lp.xb);
-  float* red = reinterpret_cast<float*>(smem + 2 * lp.xb);
-  rows_to_lds<A, true>(p.hp, T, p.d, xs, xlo, XS, p.g2, p.eps, smem);
-  trace_x(p, 7);
-  const int KT = p.d / TK;
-  int u0, u1;
-  if (early) {
-    u0 = blockIdx.x;
-    u1 = u0 + 1;
-  } else {
-    split_range(RT, gridDim.x, blockIdx.x, u0, u1);
-  }
-  const A* bl = b_lane<A>(xs, XS, T, TK);
-  struct Src {
-    const uint8_t* wr; int KT; const A* bl; long long lo_off;
-    __device__ const uint8_t* base(int u) const { return wr + (long long)u * KT * 1024; }
-    __device__ const A* bbase(int) const { return bl; }
-    __device__ const float* sbase(int) const { return nullptr; }
-    __device__ const float* sbase2(int) const { return nullptr; }
-  } src{p.wr, KT, bl, (long long)(lp.xb / (int)sizeof(A))};
-  float* lg = p.logit_part;
-  const int E = p.E;
-  auto epi = [=](int u, int row, int col, float v, float) { lg[(long long)col * E + u * 16 + row] = v; };
-  stream_units_wg<AF, false, AF != MK_FMT_F32>(u0, u1, KT, T, src, epi, red, p.dummy);
-}
-
-// ------------------------------------------------------------------ P6 routing + gate/up
+// ------------------------------------------------------------------ routing
 struct RouteLds {
   float* lg;       // [T][E]
   int* sel;        // [T][topk]
@@ -906,19 +822,22 @@ __device__ __forceinline__ void route_token(const LayerParams& p, const RouteLds
     }
     base += __popcll(m);
   }
-  if (blockIdx.x == 0) {
 #pragma unroll
-    for (int i = 0; i < EPL; ++i)
-      if (lane + 64 * i < E) p.logits[(long long)w * E + lane + 64 * i] = lv[i];
-  }
+  for (int i = 0; i < EPL; ++i)
+    if (lane + 64 * i < E) p.logits[(long long)w * E + lane + 64 * i] = lv[i];
 }
 
 __device__ __forceinline__ void route(const LayerParams& p, const RouteLds& r) {
   const int T = p.T, E = p.E, K = p.topk, S0 = p.nshared;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // the expert block table, loaded into LDS (the logit area is free) while the
+  // token waves load their logits
+  const uint8_t** etab = reinterpret_cast<const uint8_t**>(r.lg);
+  for (int i = threadIdx.x; i < E + S0; i += kThreads) etab[i] = p.experts[i];
   for (int i = threadIdx.x; i < E; i += kThreads) r.flags[i] = 0;
   if (w < T) {
-    if (E <= 512) route_token<8>(p, r);
+    if (E <= 384) route_token<6>(p, r);
+    else if (E <= 512) route_token<8>(p, r);
     else route_token<kMaxExperts / 64>(p, r);
   }
   __syncthreads();
@@ -949,21 +868,164 @@ __device__ __forceinline__ void route(const LayerParams& p, const RouteLds& r) {
     const int t = threadIdx.x / K, k = threadIdx.x - t * K;
     r.slot_of[t * kMaxTopK + k] = r.flags[r.sel[t * kMaxTopK + k]] - 1;
   }
-  if (threadIdx.x < *r.nslots) r.blk[threadIdx.x] = p.experts[r.slots[threadIdx.x]];
   __syncthreads();
-  if (blockIdx.x == 0) {
-    for (int i = threadIdx.x; i < T * K; i += kThreads) {
-      const int t = i / K, k = i - t * K;
-      p.route_sel[i] = r.sel[t * kMaxTopK + k];
-      p.route_gate[i] = r.gate[t * kMaxTopK + k];
-    }
-    if (threadIdx.x == 0) {
-      p.bar->slots_sum += (unsigned long long)*r.nslots;
-      p.bar->launches += 1ull;
-    }
+  // publish for every workgroup (read back after the next grid barrier)
+  const int ns = *r.nslots;
+  const uint8_t** pub_blk = reinterpret_cast<const uint8_t**>(reinterpret_cast<char*>(p.route_pub) + 1024);
+  if (threadIdx.x < ns) pub_blk[threadIdx.x] = etab[r.slots[threadIdx.x]];
+  for (int i = threadIdx.x; i < T * K; i += kThreads) {
+    const int t = i / K, k = i - t * K;
+    p.route_sel[i] = r.sel[t * kMaxTopK + k];
+    p.route_gate[i] = r.gate[t * kMaxTopK + k];
+    p.route_pub[16 + i] = r.slot_of[t * kMaxTopK + k];
+  }
+  if (threadIdx.x == 0) {
+    p.route_pub[0] = ns;
+    p.bar->slots_sum += (unsigned long long)ns;
+    p.bar->launches += 1ull;
   }
 }
 
+// Every workgroup: the published routing into its LDS tables.
+__device__ __forceinline__ void route_load(const LayerParams& p, const RouteLds& r) {
+  const int T = p.T, K = p.topk;
+  const uint8_t* const* pub_blk =
+      reinterpret_cast<const uint8_t* const*>(reinterpret_cast<const char*>(p.route_pub) + 1024);
+  constexpr int kMaxSlots = kMaxT * kMaxTopK + 8;
+  const int tid = threadIdx.x;
+  int sel = 0, so = 0;
+  float gt = 0.f;
+  const uint8_t* b = nullptr;
+  int ns = 0;
+  if (tid < T * K) {
+    sel = p.route_sel[tid];
+    gt = p.route_gate[tid];
+    so = p.route_pub[16 + tid];
+  }
+  if (tid < kMaxSlots) b = pub_blk[tid];
+  if (tid == 0) ns = p.route_pub[0];
+  if (tid < T * K) {
+    const int t = tid / K, k = tid - t * K;
+    r.sel[t * kMaxTopK + k] = sel;
+    r.gate[t * kMaxTopK + k] = gt;
+    r.slot_of[t * kMaxTopK + k] = so;
+  }
+  if (tid < kMaxSlots) r.blk[tid] = b;
+  if (tid == 0) *r.nslots = ns;
+  __syncthreads();
+}
+
+// ------------------------------------------------------------------ gate/up units
+// Unit u = (slot s0 + u / RT, 16 rows rt = u % RT of d_ff): h = silu(W1 x') * W3 x'
+// for all T rows, W1 and W3 tiles interleaved in the packed expert block.
+// blk[i] is the packed block of slot s0 + i.
+// MODE 0: workgroup units [u0, u1); 1: wave units [u0, u1).
+template <int EF, int MODE>
+__device__ __forceinline__ void gateup_units(const LayerParams& p, const uint8_t* const* blk, int s0, int u0, int u1,
+                                             const typename Act<EF>::T* xs, float* red) {
+  typedef typename Act<EF>::T A;
+  constexpr int TK = tile_k(EF);
+  const int T = p.T, XS = p.d + kXPad;
+  const int RT = p.f / 16, KT = p.d / TK;
+  const A* bl = b_lane<A>(xs, XS, T, TK);
+  const int nbk = (p.d + 127) / 128;
+  struct Src {
+    const uint8_t* const* blk; int RT, KT, nbk; const A* bl; long long sc_off, sc3_off;
+    __device__ const uint8_t* base(int u) const {
+      const int sl = u / RT, rt = u - sl * RT;
+      return blk[sl] + (long long)rt * KT * 2048;
+    }
+    __device__ const A* bbase(int) const { return bl; }
+    __device__ const float* sbase(int u) const {
+      const int sl = u / RT, rt = u - sl * RT;
+      return reinterpret_cast<const float*>(blk[sl] + sc_off) + (rt >> 3) * nbk;
+    }
+    __device__ const float* sbase2(int u) const {
+      const int sl = u / RT, rt = u - sl * RT;
+      return reinterpret_cast<const float*>(blk[sl] + sc3_off) + (rt >> 3) * nbk;
+    }
+  };
+  const long long nsc13 = (long long)((p.f + 127) / 128) * nbk;
+  const long long sc_off = p.exp_w13_bytes + p.exp_w2_bytes;
+  Src src{blk, RT, KT, nbk, bl, sc_off, sc_off + nsc13 * 4};
+  A* hb = reinterpret_cast<A*>(p.hbuf);
+  const int f = p.f;
+  auto epi = [=](int u, int row, int col, float v, float v2) {
+    const int sl = s0 + u / RT, rt = u % RT;
+    const float sg = v / (1.0f + expf(-v));
+    hb[((long long)sl * T + col) * f + rt * 16 + row] = to_act<A>(sg * v2);
+  };
+  if constexpr (MODE == 1) stream_units_wave<EF, true>(u0, u1, KT, T, src, epi, p.dummy);
+  else stream_units_wg<EF, true, false>(u0, u1, KT, T, src, epi, red, p.dummy);
+}
+
+// The shared experts do not depend on routing: when the grid has workgroups
+// beyond the router's E/16 units, those run the shared experts' gate/up in the
+// router phase (into slots 0 .. n_shared-1).
+__device__ __forceinline__ bool shared_early(const LayerParams& p) {
+  return p.nshared > 0 && (int)gridDim.x > p.E / 16;
+}
+
+// ------------------------------------------------------------------ P5 router
+template <int AF, int EF>
+__device__ __forceinline__ void phase_router(const LayerParams& p, char* smem) {
+  typedef typename Act<AF>::T A;
+  constexpr int TK = tile_k(AF);
+  const int T = p.T, XS = p.d + kXPad;
+  LdsPlan lp(p, sizeof(A));
+  A* xs = reinterpret_cast<A*>(smem);
+  const int RT = p.E / 16;              // router units: 16 experts, all of d_model
+  const bool early = shared_early(p);
+  if (early && (int)blockIdx.x >= RT) {
+    rows_to_lds<A, true>(p.hp, T, p.d, xs, (A*)nullptr, XS, p.g2, p.eps, smem);
+    trace_x(p, 7);
+    const int nwg = (int)gridDim.x - RT, U = p.nshared * (p.f / 16);
+    int u0, u1;
+    split_range(U, nwg, (int)blockIdx.x - RT, u0, u1);
+    gateup_units<EF, 0>(p, p.experts + p.E, 0, u0, u1, xs, reinterpret_cast<float*>(smem + lp.xb));
+    return;
+  }
+  A* xlo = AF == MK_FMT_F32 ? (A*)nullptr : reinterpret_cast<A*>(smem + lp.xb);
+  float* red = reinterpret_cast<float*>(smem + 2 * lp.xb);
+  rows_to_lds<A, true>(p.hp, T, p.d, xs, xlo, XS, p.g2, p.eps, smem);
+  trace_x(p, 7);
+  const int KT = p.d / TK;
+  int u0, u1;
+  if (early) {
+    u0 = blockIdx.x;
+    u1 = u0 + 1;
+  } else {
+    split_range(RT, gridDim.x, blockIdx.x, u0, u1);
+  }
+  const A* bl = b_lane<A>(xs, XS, T, TK);
+  struct Src {
+    const uint8_t* wr; int KT; const A* bl; long long lo_off;
+    __device__ const uint8_t* base(int u) const { return wr + (long long)u * KT * 1024; }
+    __device__ const A* bbase(int) const { return bl; }
+    __device__ const float* sbase(int) const { return nullptr; }
+    __device__ const float* sbase2(int) const { return nullptr; }
+  } src{p.wr, KT, bl, (long long)(lp.xb / (int)sizeof(A))};
+  float* lg = p.logit_part;
+  const int E = p.E;
+  auto epi = [=](int u, int row, int col, float v, float) { lg[(long long)col * E + u * 16 + row] = v; };
+  stream_units_wg<AF, false, AF != MK_FMT_F32>(u0, u1, KT, T, src, epi, red, p.dummy);
+  if (u1 <= u0) return;
+  // the last workgroup to finish its router units computes the routing
+  int* flag = reinterpret_cast<int*>(smem + kFlagOff);
+  wg_release_begin();
+  if (threadIdx.x == 0) {
+    release_agent();
+    const uint32_t target = (uint32_t)min(RT, (int)gridDim.x);
+    const uint32_t old =
+        __hip_atomic_fetch_add(&p.att_cnt[kRouteCnt], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *flag = old + 1 == target;
+    if (old + 1 == target) acquire_agent();
+  }
+  __syncthreads();
+  if (*flag) route(p, route_lds(p, smem, lp.xb));
+}
+
+// ------------------------------------------------------------------ P6 gate/up
 template <int AF, int EF>
 __device__ __forceinline__ void phase_route_gateup(const LayerParams& p, char* smem) {
   typedef typename Act<EF>::T A;
@@ -972,7 +1034,7 @@ __device__ __forceinline__ void phase_route_gateup(const LayerParams& p, char* s
   const A* xs = reinterpret_cast<const A*>(smem);      // x' (hi part) from P5
   float* red = reinterpret_cast<float*>(smem + lp.xb);
   RouteLds r = route_lds(p, smem, lp.xb);
-  route(p, r);
+  route_load(p, r);
   trace_x(p, 8);
   const int s0 = shared_early(p) ? p.nshared : 0;     // slots whose gate/up ran in P5
   const int ns = *r.nslots;
@@ -1088,7 +1150,7 @@ __global__ __launch_bounds__(kThreads, 1) void layer_kernel(LayerParams p) {
   }
   if (p.trace && threadIdx.x == 0) p.trace[(long long)blockIdx.x * kTraceStride] = (long long)clock100();
   // attention split counters: cleared here, used after two grid barriers
-  if (blockIdx.x == 0 && threadIdx.x < 64)
+  if (blockIdx.x == 0 && threadIdx.x <= kRouteCnt)
     __hip_atomic_store(&p.att_cnt[threadIdx.x], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   phase_qkv<AF>(p, smem);
   if (!grid_barrier(p, 0, flag)) return;
@@ -1106,18 +1168,20 @@ __global__ __launch_bounds__(kThreads, 1) void layer_kernel(LayerParams p) {
     }
   }
   if (!grid_barrier(p, 1, flag)) return;
-  phase_attention<KF, KBMAX, DBMAX>(p, L, smem, flag);
+  phase_attention<KF, KBMAX, DBMAX>(p, L, smem);
   if (!grid_barrier(p, 2, flag)) return;
-  phase_uv<AF>(p, smem);
+  phase_merge(p, L, smem);
   if (!grid_barrier(p, 3, flag)) return;
-  phase_wo<AF>(p, smem);
+  phase_uv<AF>(p, smem);
   if (!grid_barrier(p, 4, flag)) return;
-  phase_router<AF, EF>(p, smem);
+  phase_wo<AF>(p, smem);
   if (!grid_barrier(p, 5, flag)) return;
-  phase_route_gateup<AF, EF>(p, smem);
+  phase_router<AF, EF>(p, smem);
   if (!grid_barrier(p, 6, flag)) return;
-  phase_down<EF>(p, smem);
+  phase_route_gateup<AF, EF>(p, smem);
   if (!grid_barrier(p, 7, flag)) return;
+  phase_down<EF>(p, smem);
+  if (!grid_barrier(p, 8, flag)) return;
   LdsPlan lp(p, EF == MK_FMT_F32 ? 4 : 2);
   phase_combine(p, smem, lp.xb);
   if (p.trace && threadIdx.x == 0)
