@@ -363,13 +363,16 @@ __device__ __forceinline__ void attn_splits(int NQT, int Lt, int& s_kv, int& SK)
   SK = ((Lt + s_kv - 1) / s_kv + 15) / 16 * 16;
 }
 
-template <int KF, int KBMAX, int DBMAX>
+// EXACT: d_latent + d_rope == KBMAX * KBW and d_latent == 16 * DBMAX, so every
+// per-block bound is a compile-time constant (no guards inside the loops).
+template <int KF, int KBMAX, int DBMAX, bool EXACT>
 __device__ __forceinline__ void phase_attention(const LayerParams& p, int L, char* smem) {
   typedef typename AttnTypes<KF>::E E;
   constexpr int KBW = AttnTypes<KF>::KBW;
-  const int T = p.T, nh = p.nh, dc = p.dc, kvw = p.kvw;
+  const int T = p.T, nh = p.nh;
+  const int dc = EXACT ? 16 * DBMAX : p.dc, kvw = EXACT ? KBMAX * KBW : p.kvw;
   const int NQ = T * nh, NQT = (NQ + 15) / 16, Lt = L + T;
-  const int KB = kvw / KBW, DB = dc / 16;
+  const int KB = EXACT ? KBMAX : kvw / KBW, DB = EXACT ? DBMAX : dc / 16;
   int s_kv, SK;
   attn_splits(NQT, Lt, s_kv, SK);
   const int units = NQT * s_kv;
@@ -1137,7 +1140,7 @@ __device__ __forceinline__ void phase_combine(const LayerParams& p, char* smem, 
 }
 
 // ------------------------------------------------------------------ the kernel
-template <int AF, int EF, int KF, int KBMAX, int DBMAX>
+template <int AF, int EF, int KF, int KBMAX, int DBMAX, bool EXACT>
 __global__ __launch_bounds__(kThreads, 1) void layer_kernel(LayerParams p) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   int* flag = reinterpret_cast<int*>(smem + kFlagOff);
@@ -1168,7 +1171,7 @@ __global__ __launch_bounds__(kThreads, 1) void layer_kernel(LayerParams p) {
     }
   }
   if (!grid_barrier(p, 1, flag)) return;
-  phase_attention<KF, KBMAX, DBMAX>(p, L, smem);
+  phase_attention<KF, KBMAX, DBMAX, EXACT>(p, L, smem);
   if (!grid_barrier(p, 2, flag)) return;
   phase_merge(p, L, smem);
   if (!grid_barrier(p, 3, flag)) return;
@@ -1189,14 +1192,20 @@ __global__ __launch_bounds__(kThreads, 1) void layer_kernel(LayerParams p) {
 }
 
 // Instantiations: all-fp32 (d_latent + d_rope <= 160, d_latent <= 128),
-// bf16 attention with bf16 or fp8 experts (d_latent + d_rope <= 576, d_latent <= 512).
+// bf16 attention with bf16 or fp8 experts (d_latent + d_rope <= 576, d_latent <= 512),
+// the latter also specialised for exactly 512 + 64 latent dims.
 typedef void (*LayerKernelFn)(LayerParams);
 LayerKernelFn layer_kernel_for(int af, int ef, int kf, int kvw, int dc) {
   if (af == MK_FMT_F32 && ef == MK_FMT_F32 && kf == MK_FMT_F32 && kvw <= 160 && dc <= 128)
-    return layer_kernel<MK_FMT_F32, MK_FMT_F32, MK_FMT_F32, 10, 8>;
+    return layer_kernel<MK_FMT_F32, MK_FMT_F32, MK_FMT_F32, 10, 8, false>;
   if (af == MK_FMT_BF16 && kf == MK_FMT_BF16 && kvw <= 576 && dc <= 512) {
-    if (ef == MK_FMT_BF16) return layer_kernel<MK_FMT_BF16, MK_FMT_BF16, MK_FMT_BF16, 18, 32>;
-    if (ef == MK_FMT_FP8_B128) return layer_kernel<MK_FMT_BF16, MK_FMT_FP8_B128, MK_FMT_BF16, 18, 32>;
+    const bool exact = kvw == 576 && dc == 512;
+    if (ef == MK_FMT_BF16)
+      return exact ? layer_kernel<MK_FMT_BF16, MK_FMT_BF16, MK_FMT_BF16, 18, 32, true>
+                   : layer_kernel<MK_FMT_BF16, MK_FMT_BF16, MK_FMT_BF16, 18, 32, false>;
+    if (ef == MK_FMT_FP8_B128)
+      return exact ? layer_kernel<MK_FMT_BF16, MK_FMT_FP8_B128, MK_FMT_BF16, 18, 32, true>
+                   : layer_kernel<MK_FMT_BF16, MK_FMT_FP8_B128, MK_FMT_BF16, 18, 32, false>;
   }
   return nullptr;
 }
