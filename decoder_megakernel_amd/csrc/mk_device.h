@@ -375,9 +375,43 @@ __device__ __forceinline__ void run_wave_units(int u0, int u1, int NT, int T, co
 // last prefetch reads `dummy`, an L2-resident scratch block), so the compiler
 // can keep exact s_waitcnt counts and D loads stay in flight.
 // Requires: slice (NT/8 in WG mode, NT in wave mode) a multiple of D.
-template <int FMT, bool DUAL, bool HILO, bool WG, int D, class Src, class Epi>
+// Registers of one chunk of D tiles (and, for fp8, their block scales).
+template <int FMT, bool DUAL, int D>
+struct Chunk {
+  u32x4 buf[D];
+  u32x4 buf2[D];
+  float sc[D], sc2[D];
+};
+
+// Issues the loads of a stream's first chunk (the same one run_stream would
+// load first), so that they can be in flight while the activation operand is
+// staged; run_stream<..., PRIMED = true> then starts from these registers.
+template <int FMT, bool DUAL, bool WG, int D, class Src>
+__device__ __forceinline__ void stream_prime(Chunk<FMT, DUAL, D>& c, int u0, int u1, int NT, const Src& src) {
+  constexpr int TK = tile_k(FMT);
+  constexpr long long STRIDE = DUAL ? 2048 : 1024;
+  const int w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int slice = WG ? NT / kWaves : NT;
+  const int nu = WG ? (u1 - u0) : (u1 - u0 > w ? (u1 - u0 - w + kWaves - 1) / kWaves : 0);
+  if (nu <= 0 || slice / D <= 0) return;
+  const int u = WG ? u0 : u0 + w;
+  const int toff = WG ? w * slice : 0;
+  const uint8_t* cbase = src.base(u) + lane * 16 + (long long)toff * STRIDE;
+#pragma unroll
+  for (int r = 0; r < D; ++r) {
+    c.buf[r] = ld_stream16(cbase + r * STRIDE);
+    if constexpr (DUAL) c.buf2[r] = ld_stream16(cbase + r * STRIDE + 1024);
+    if constexpr (FMT == MK_FMT_FP8_B128) {
+      c.sc[r] = src.sbase(u)[((toff + r) * TK) >> 7];
+      if constexpr (DUAL) c.sc2[r] = src.sbase2(u)[((toff + r) * TK) >> 7];
+    }
+  }
+}
+
+template <int FMT, bool DUAL, bool HILO, bool WG, int D, bool PRIMED = false, class Src, class Epi>
 __device__ __forceinline__ void run_stream(int u0, int u1, int NT, int T, const Src& src, const Epi& epi, float* red,
-                                           const uint8_t* dummy) {
+                                           const uint8_t* dummy, Chunk<FMT, DUAL, D>* pre = nullptr) {
   constexpr int TK = tile_k(FMT);
   constexpr long long STRIDE = DUAL ? 2048 : 1024;
   const int w = threadIdx.x >> 6;
@@ -391,9 +425,12 @@ __device__ __forceinline__ void run_stream(int u0, int u1, int NT, int T, const 
   if (nchunks <= 0) return;
   const int toff = WG ? w * slice : 0;
   const float* dsc = reinterpret_cast<const float*>(dummy);
-  u32x4 buf[D];
-  u32x4 buf2[D];
-  float sc[D], sc2[D];
+  Chunk<FMT, DUAL, D> local;
+  Chunk<FMT, DUAL, D>& ck = PRIMED ? *pre : local;
+  u32x4 (&buf)[D] = ck.buf;
+  u32x4 (&buf2)[D] = ck.buf2;
+  float (&sc)[D] = ck.sc;
+  float (&sc2)[D] = ck.sc2;
   auto load_chunk = [&](const uint8_t* cbase, const float* sp, const float* sp2, int tfirst) {
 #pragma unroll
     for (int r = 0; r < D; ++r) {
@@ -405,7 +442,7 @@ __device__ __forceinline__ void run_stream(int u0, int u1, int NT, int T, const 
       }
     }
   };
-  {
+  if constexpr (!PRIMED) {
     const int u = ufirst;
     const float* sp = nullptr;
     const float* sp2 = nullptr;
@@ -508,6 +545,22 @@ __device__ __forceinline__ void stream_units_wg(int u0, int u1, int NT, int T, c
   else if (slice > 0 && slice % 2 == 0) run_stream<FMT, DUAL, HILO, true, 2>(u0, u1, NT, T, src, epi, red, dummy);
   else run_units<FMT, DUAL, HILO>(u0, u1, NT, T, src, epi, red);
 }
+// Workgroup-mode streaming whose first chunk may have been primed: when the
+// slice allows the full-depth engine (`primed` tells whether stream_prime ran
+// with the same arguments), else the general engines.
+template <int FMT, bool DUAL, bool HILO, class Src, class Epi>
+__device__ __forceinline__ void stream_units_wg_primed(int u0, int u1, int NT, int T, const Src& src, const Epi& epi,
+                                                       float* red, const uint8_t* dummy,
+                                                       Chunk<FMT, DUAL, DUAL ? 8 : 16>& pre, bool primed) {
+  constexpr int DMAX = DUAL ? 8 : 16;
+  if (primed) run_stream<FMT, DUAL, HILO, true, DMAX, true>(u0, u1, NT, T, src, epi, red, dummy, &pre);
+  else stream_units_wg<FMT, DUAL, HILO>(u0, u1, NT, T, src, epi, red, dummy);
+}
+// Whether stream_units_wg_primed can use a primed first chunk for this slice.
+__host__ __device__ constexpr bool wg_primable(int NT, bool dual) {
+  return NT % kWaves == 0 && (NT / kWaves) % (dual ? 8 : 16) == 0;
+}
+
 template <int FMT, bool DUAL, class Src, class Epi>
 __device__ __forceinline__ void stream_units_wave(int u0, int u1, int NT, int T, const Src& src, const Epi& epi,
                                                   const uint8_t* dummy) {

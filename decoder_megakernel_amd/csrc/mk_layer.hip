@@ -175,9 +175,6 @@ __device__ __forceinline__ void phase_qkv(const LayerParams& p, char* smem) {
   LdsPlan lp(p, sizeof(A));
   A* xs = reinterpret_cast<A*>(smem);
   float* red = reinterpret_cast<float*>(smem + lp.xb);
-  rows_to_lds<A, true>(p.H, T, p.d, xs, (A*)nullptr, XS, p.g1, p.eps, smem,
-                       p.trace ? p.trace + (long long)blockIdx.x * kTraceStride + 2 + 2 * kBarriers : nullptr);
-  trace_x(p, 5);
   const int RTq = p.nq / 16, RTkv = (p.kvw + 15) / 16, KT = p.d / TK, S = p.sch.s_q, NT = KT / S;
   const int U = (RTq + RTkv) * S;
   int u0, u1;
@@ -208,7 +205,14 @@ __device__ __forceinline__ void phase_qkv(const LayerParams& p, char* smem) {
     }
     part[((long long)s * T + col) * nrow + idx] = v;
   };
-  stream_units_wg<AF, false, false>(u0, u1, NT, T, src, epi, red, p.dummy);
+  // the first weight chunk is requested before the input rows are normalised
+  Chunk<AF, false, 16> ck;
+  const bool pr = wg_primable(NT, false);
+  if (pr) stream_prime<AF, false, true, 16>(ck, u0, u1, NT, src);
+  rows_to_lds<A, true>(p.H, T, p.d, xs, (A*)nullptr, XS, p.g1, p.eps, smem,
+                       p.trace ? p.trace + (long long)blockIdx.x * kTraceStride + 2 + 2 * kBarriers : nullptr);
+  trace_x(p, 5);
+  stream_units_wg_primed<AF, false, false>(u0, u1, NT, T, src, epi, red, p.dummy, ck, pr);
 }
 
 // ------------------------------------------------------------------ P1
@@ -690,8 +694,6 @@ __device__ __forceinline__ void phase_wo(const LayerParams& p, char* smem) {
   int u0, u1;
   split_range(U, gridDim.x, blockIdx.x, u0, u1);
   if (u1 <= u0) return;
-  rows_copy_lds<A>(reinterpret_cast<const A*>(p.o), T, K, xs, XS);
-  trace_x(p, 6);
   const A* bl = b_lane<A>(xs, XS, T, TK);
   struct Src {
     const uint8_t* wo; int KT; const A* bl;
@@ -707,7 +709,12 @@ __device__ __forceinline__ void phase_wo(const LayerParams& p, char* smem) {
     const long long i = (long long)col * d + u * 16 + row;
     hp[i] = H[i] + v;
   };
-  stream_units_wg<AF, false, false>(u0, u1, KT, T, src, epi, red, p.dummy);
+  Chunk<AF, false, 16> ck;
+  const bool pr = wg_primable(KT, false);
+  if (pr) stream_prime<AF, false, true, 16>(ck, u0, u1, KT, src);
+  rows_copy_lds<A>(reinterpret_cast<const A*>(p.o), T, K, xs, XS);
+  trace_x(p, 6);
+  stream_units_wg_primed<AF, false, false>(u0, u1, KT, T, src, epi, red, p.dummy, ck, pr);
 }
 
 // ------------------------------------------------------------------ routing
@@ -922,10 +929,14 @@ __device__ __forceinline__ void route_load(const LayerParams& p, const RouteLds&
 // Unit u = (slot s0 + u / RT, 16 rows rt = u % RT of d_ff): h = silu(W1 x') * W3 x'
 // for all T rows, W1 and W3 tiles interleaved in the packed expert block.
 // blk[i] is the packed block of slot s0 + i.
-// MODE 0: workgroup units [u0, u1); 1: wave units [u0, u1).
-template <int EF, int MODE>
+struct NoStage {
+  __device__ void operator()() const {}
+};
+// MODE 0: workgroup units [u0, u1); 1: wave units [u0, u1).  `stage` runs after
+// the first weight chunk was requested and before it is used (workgroup mode).
+template <int EF, int MODE, class Stage = NoStage>
 __device__ __forceinline__ void gateup_units(const LayerParams& p, const uint8_t* const* blk, int s0, int u0, int u1,
-                                             const typename Act<EF>::T* xs, float* red) {
+                                             const typename Act<EF>::T* xs, float* red, const Stage& stage = Stage()) {
   typedef typename Act<EF>::T A;
   constexpr int TK = tile_k(EF);
   const int T = p.T, XS = p.d + kXPad;
@@ -958,8 +969,16 @@ __device__ __forceinline__ void gateup_units(const LayerParams& p, const uint8_t
     const float sg = v / (1.0f + expf(-v));
     hb[((long long)sl * T + col) * f + rt * 16 + row] = to_act<A>(sg * v2);
   };
-  if constexpr (MODE == 1) stream_units_wave<EF, true>(u0, u1, KT, T, src, epi, p.dummy);
-  else stream_units_wg<EF, true, false>(u0, u1, KT, T, src, epi, red, p.dummy);
+  if constexpr (MODE == 1) {
+    stage();
+    stream_units_wave<EF, true>(u0, u1, KT, T, src, epi, p.dummy);
+  } else {
+    Chunk<EF, true, 8> ck;
+    const bool pr = wg_primable(KT, true);
+    if (pr) stream_prime<EF, true, true, 8>(ck, u0, u1, KT, src);
+    stage();
+    stream_units_wg_primed<EF, true, false>(u0, u1, KT, T, src, epi, red, p.dummy, ck, pr);
+  }
 }
 
 // The shared experts do not depend on routing: when the grid has workgroups
@@ -980,18 +999,19 @@ __device__ __forceinline__ void phase_router(const LayerParams& p, char* smem) {
   const int RT = p.E / 16;              // router units: 16 experts, all of d_model
   const bool early = shared_early(p);
   if (early && (int)blockIdx.x >= RT) {
-    rows_to_lds<A, true>(p.hp, T, p.d, xs, (A*)nullptr, XS, p.g2, p.eps, smem);
-    trace_x(p, 7);
     const int nwg = (int)gridDim.x - RT, U = p.nshared * (p.f / 16);
     int u0, u1;
     split_range(U, nwg, (int)blockIdx.x - RT, u0, u1);
-    gateup_units<EF, 0>(p, p.experts + p.E, 0, u0, u1, xs, reinterpret_cast<float*>(smem + lp.xb));
+    auto stage = [&]() {
+      rows_to_lds<A, true>(p.hp, T, p.d, xs, (A*)nullptr, XS, p.g2, p.eps, smem);
+      trace_x(p, 7);
+    };
+    if (u1 > u0) gateup_units<EF, 0>(p, p.experts + p.E, 0, u0, u1, xs, reinterpret_cast<float*>(smem + lp.xb), stage);
+    else stage();
     return;
   }
   A* xlo = AF == MK_FMT_F32 ? (A*)nullptr : reinterpret_cast<A*>(smem + lp.xb);
   float* red = reinterpret_cast<float*>(smem + 2 * lp.xb);
-  rows_to_lds<A, true>(p.hp, T, p.d, xs, xlo, XS, p.g2, p.eps, smem);
-  trace_x(p, 7);
   const int KT = p.d / TK;
   int u0, u1;
   if (early) {
@@ -1011,7 +1031,12 @@ __device__ __forceinline__ void phase_router(const LayerParams& p, char* smem) {
   float* lg = p.logit_part;
   const int E = p.E;
   auto epi = [=](int u, int row, int col, float v, float) { lg[(long long)col * E + u * 16 + row] = v; };
-  stream_units_wg<AF, false, AF != MK_FMT_F32>(u0, u1, KT, T, src, epi, red, p.dummy);
+  Chunk<AF, false, 16> ck;
+  const bool pr = wg_primable(KT, false);
+  if (pr) stream_prime<AF, false, true, 16>(ck, u0, u1, KT, src);
+  rows_to_lds<A, true>(p.hp, T, p.d, xs, xlo, XS, p.g2, p.eps, smem);
+  trace_x(p, 7);
+  stream_units_wg_primed<AF, false, AF != MK_FMT_F32>(u0, u1, KT, T, src, epi, red, p.dummy, ck, pr);
   if (u1 <= u0) return;
   // the last workgroup to finish its router units computes the routing
   int* flag = reinterpret_cast<int*>(smem + kFlagOff);
