@@ -80,7 +80,7 @@ int check_cfg(const mk_layer_config* c) {
   if (dmax > kMaxStageK)
     return fail(MK_ERR_UNSUPPORTED_SHAPE, "d_model, n_heads*d_head and d_ff must be <= %d", kMaxStageK);
   const long long xb = align256((size_t)kMaxT * (dmax + kXPad) * es);
-  const long long lds_router = 2 * xb + 2 * kWaves * 64 * 4 * 4;
+  const long long lds_router = 2 * xb + 2 * kWaves * 64 * 4 * 4 + 4LL * kMaxT * 16 * 4;
   const long long lds_route = xb + 32768 + (long long)kMaxT * D.E * 4 + 3 * kMaxT * kMaxTopK * 4 +
                               (kMaxT * kMaxTopK + 8) * 4 + (long long)D.E * 4 + 16 + (kMaxT * kMaxTopK + 8) * 8;
   const long long lds_att = std::max((long long)kWaves * 16 * (D.dc + 8) * es + 16LL * (D.kvw + 8) * es,
@@ -174,7 +174,7 @@ int device_info(int dev, DevInfo* di, LayerKernelFn fn) {
 }
 
 struct WsLayout {
-  size_t qkv_part, qrope, qabs, att_part, att_ml, z, o, hp, logit_part, route_sel, route_gate, route_pub, logits, hbuf,
+  size_t qkv_part, qrope, qabs, att_part, att_ml, z, o, hp, route_sel, route_gate, route_pub, route_cand, logits, hbuf,
       ybuf, dummy,
       total;
 };
@@ -198,10 +198,10 @@ WsLayout ws_layout(const Dims& D, const Schedule& s) {
   w.z = take((size_t)T * D.nh * D.dc * 4);
   w.o = take((size_t)T * D.nh * D.dh * 4);
   w.hp = take((size_t)T * D.d * 4);
-  w.logit_part = take((size_t)T * D.E * 4);
   w.route_sel = take((size_t)T * kMaxTopK * 4);
   w.route_gate = take((size_t)T * kMaxTopK * 4);
   w.route_pub = take(4096);
+  w.route_cand = take((size_t)2 * T * (D.E / 16) * 16 * 4);
   w.logits = take((size_t)T * D.E * 4);
   w.hbuf = take((size_t)slots * T * D.f * 4);
   w.ybuf = take((size_t)slots * T * D.d * 4);
@@ -410,6 +410,9 @@ int mk_layer_init(const mk_layer_config* cfg, const mk_layer_weights* w, void* s
   DevInfo di;
   rc = device_info(hip_device, &di, fn);
   if (rc) return rc;
+  if ((D.E / 16 + di.nwg - 1) / di.nwg > 4)
+    return fail(MK_ERR_UNSUPPORTED_SHAPE, "n_experts / 16 exceeds 4 router units per workgroup on %d workgroups",
+                di.nwg);
   mk_layer* L = new (std::nothrow) mk_layer();
   if (!L) return fail(MK_ERR_INVALID_ARG, "out of host memory");
   L->cfg = *cfg;
@@ -460,10 +463,10 @@ int mk_layer_init(const mk_layer_config* cfg, const mk_layer_weights* w, void* s
   p.z = (float*)(ws + L->wl.z);
   p.o = (float*)(ws + L->wl.o);
   p.hp = (float*)(ws + L->wl.hp);
-  p.logit_part = (float*)(ws + L->wl.logit_part);
   p.route_sel = (int32_t*)(ws + L->wl.route_sel);
   p.route_gate = (float*)(ws + L->wl.route_gate);
   p.route_pub = (int32_t*)(ws + L->wl.route_pub);
+  p.route_cand = (float*)(ws + L->wl.route_cand);
   p.logits = (float*)(ws + L->wl.logits);
   p.hbuf = (float*)(ws + L->wl.hbuf);
   p.ybuf = (float*)(ws + L->wl.ybuf);

@@ -92,9 +92,9 @@ struct LayerParams {
   float* z;                // [T][nh][dc]
   float* o;                // [T][nh*dh] in the activation type (fp32 or bf16)
   float* hp;               // [T][d]
-  float* logit_part;       // [T][E] router logits before the bias
   int32_t* route_sel;      // [T][topk]
   float* route_gate;       // [T][topk]
+  float* route_cand;       // router candidates: [T][E/16][16] biased logits, then [T][E/16][16] int expert ids
   int32_t* route_pub;      // routing published for the expert phases: [0] slot count,
                            // [16 + t*topk + k] slot of pick (t, k), 8-byte block pointers from byte 1024
   float* logits;           // [T][E] (written by workgroup 0)

@@ -759,42 +759,40 @@ __device__ __forceinline__ unsigned long long lanemask_lt() {
   return lane ? (~0ull >> (64 - lane)) : 0ull;
 }
 
-// softmax over all experts, top-k by logit (ties to the lower index), gates =
-// selected probabilities renormalised; then the slot list: the shared experts
-// first, then the distinct selected experts in ascending order.  Identical in
-// every workgroup.  Wave t < T handles token t with its logits in registers
-// (lane l holds experts l, l + 64, ...; absent ones get key 0, below every
-// real key): the k-th largest key is found bit by bit (32 ballot/popcount
-// rounds), then the experts above it, plus the lowest-indexed ones equal to
-// it, are compacted in ascending expert order.
+// Top-k by logit (ties to the lower index) and gates = selected softmax
+// probabilities renormalised (the normaliser over all experts cancels, so the
+// gates are exp(l - m) / sum over the selection of exp(l' - m)); then the slot
+// list: the shared experts first, then the distinct selected experts in
+// ascending order.  Wave t < T handles token t from the candidates the router
+// workgroups kept (the top min(k, 16) of every 16 experts, which contain the
+// overall top k), laid out in ascending expert order, held in registers (lane
+// l holds candidates l, l + 64, ...; absent ones get key 0, below every real
+// key): the k-th largest key is found bit by bit (32 ballot/popcount rounds),
+// then the candidates above it, plus the lowest-indexed ones equal to it, are
+// compacted in ascending expert order.
 template <int EPL>
-__device__ __forceinline__ void route_token(const LayerParams& p, const RouteLds& r) {
-  const int E = p.E, K = p.topk;
+__device__ __forceinline__ void route_cands(const LayerParams& p, const RouteLds& r) {
+  const int K = p.topk, K8 = min(K, 16), RT = p.E / 16, NC = RT * K8;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const float* cv = p.route_cand + (long long)w * RT * 16;
+  const int* ci = reinterpret_cast<const int*>(p.route_cand) + ((long long)p.T + w) * RT * 16;
   float lv[EPL];
-  float bv[EPL];
+  int id[EPL];
 #pragma unroll
   for (int i = 0; i < EPL; ++i) {
-    const int e = min(lane + 64 * i, E - 1);
-    lv[i] = p.logit_part[(long long)w * E + e];
-    bv[i] = p.rbias ? p.rbias[e] : 0.f;
+    const int c = min(lane + 64 * i, NC - 1);
+    const int o = (c / K8) * 16 + c % K8;
+    lv[i] = cv[o];
+    id[i] = ci[o];
   }
   float mx = -INFINITY;
 #pragma unroll
-  for (int i = 0; i < EPL; ++i) {
-    lv[i] += bv[i];
-    mx = fmaxf(mx, lv[i]);             // clamped duplicates do not change the max
-  }
+  for (int i = 0; i < EPL; ++i) mx = fmaxf(mx, lv[i]);   // clamped duplicates do not change the max
   mx = wave_max(mx);
-  float se = 0.f;
-#pragma unroll
-  for (int i = 0; i < EPL; ++i)
-    if (lane + 64 * i < E) se += __expf(lv[i] - mx);
-  se = wave_sum(se);
   trace_x(p, 12);
   uint32_t key[EPL];
 #pragma unroll
-  for (int i = 0; i < EPL; ++i) key[i] = lane + 64 * i < E ? fkey(lv[i]) : 0u;
+  for (int i = 0; i < EPL; ++i) key[i] = lane + 64 * i < NC ? fkey(lv[i]) : 0u;
   uint32_t thr = 0u;                    // the K-th largest key
   for (int b = 31; b >= 0; --b) {
     const uint32_t cand = thr | (1u << b);
@@ -811,15 +809,15 @@ __device__ __forceinline__ void route_token(const LayerParams& p, const RouteLds
   int base_eq = 0, base = 0;
   float ps = 0.f;
   bool sel[EPL];
-  float pr[EPL];
+  float ex[EPL];
 #pragma unroll
   for (int i = 0; i < EPL; ++i) {
     const unsigned long long meq = __ballot(key[i] == thr);
     const int rank_eq = base_eq + __popcll(meq & lt);
     base_eq += __popcll(meq);
     sel[i] = key[i] > thr || (key[i] == thr && rank_eq < need_eq);
-    pr[i] = __expf(lv[i] - mx) / se;
-    ps += sel[i] ? pr[i] : 0.f;
+    ex[i] = __expf(lv[i] - mx);
+    ps += sel[i] ? ex[i] : 0.f;
   }
   const float psel = wave_sum(ps);
 #pragma unroll
@@ -827,28 +825,54 @@ __device__ __forceinline__ void route_token(const LayerParams& p, const RouteLds
     const unsigned long long m = __ballot(sel[i]);
     if (sel[i]) {
       const int k = base + __popcll(m & lt);
-      r.sel[w * kMaxTopK + k] = lane + 64 * i;
-      r.gate[w * kMaxTopK + k] = pr[i] / psel;
+      r.sel[w * kMaxTopK + k] = id[i];
+      r.gate[w * kMaxTopK + k] = ex[i] / psel;
     }
     base += __popcll(m);
   }
-#pragma unroll
-  for (int i = 0; i < EPL; ++i)
-    if (lane + 64 * i < E) p.logits[(long long)w * E + lane + 64 * i] = lv[i];
+}
+
+// Router workgroup, after its units: for every unit (16 experts) and token,
+// the biased logits (also written to the logits tap) and the top min(k, 16)
+// of the 16 by (logit, lower index), compacted in ascending expert order.
+// lgl[unit - u0][t][16] holds the unit's unbiased logits.
+__device__ __forceinline__ void router_candidates(const LayerParams& p, const float* lgl, int u0, int u1) {
+  const int T = p.T, E = p.E, K8 = min(p.topk, 16), RT = E / 16;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  for (int u = u0; u < u1; ++u) {
+    if (w < T && lane < 16) {
+      const int e = u * 16 + lane;
+      const float v = lgl[((u - u0) * kMaxT + w) * 16 + lane] + (p.rbias ? p.rbias[e] : 0.f);
+      p.logits[(long long)w * E + e] = v;
+      const uint32_t k = fkey(v);
+      int rank = 0;
+      for (int j = 0; j < 16; ++j) {
+        const uint32_t kj = __shfl(k, j, 16);
+        rank += (kj > k || (kj == k && j < lane)) ? 1 : 0;
+      }
+      const bool s = rank < K8;
+      const unsigned long long m = __ballot(s) & 0xFFFFull;
+      if (s) {
+        const int pos = __popcll(m & lanemask_lt());
+        const long long o = ((long long)w * RT + u) * 16 + pos;
+        p.route_cand[o] = v;
+        reinterpret_cast<int*>(p.route_cand)[(long long)T * RT * 16 + o] = e;
+      }
+    }
+  }
 }
 
 __device__ __forceinline__ void route(const LayerParams& p, const RouteLds& r) {
   const int T = p.T, E = p.E, K = p.topk, S0 = p.nshared;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   // the expert block table, loaded into LDS (the logit area is free) while the
-  // token waves load their logits
+  // token waves load their candidates
   const uint8_t** etab = reinterpret_cast<const uint8_t**>(r.lg);
   for (int i = threadIdx.x; i < E + S0; i += kThreads) etab[i] = p.experts[i];
   for (int i = threadIdx.x; i < E; i += kThreads) r.flags[i] = 0;
   if (w < T) {
-    if (E <= 384) route_token<6>(p, r);
-    else if (E <= 512) route_token<8>(p, r);
-    else route_token<kMaxExperts / 64>(p, r);
+    if ((E / 16) * min(K, 16) <= 256) route_cands<4>(p, r);
+    else route_cands<kMaxExperts / 64>(p, r);
   }
   __syncthreads();
   trace_x(p, 13);
@@ -1028,9 +1052,8 @@ __device__ __forceinline__ void phase_router(const LayerParams& p, char* smem) {
     __device__ const float* sbase(int) const { return nullptr; }
     __device__ const float* sbase2(int) const { return nullptr; }
   } src{p.wr, KT, bl, (long long)(lp.xb / (int)sizeof(A))};
-  float* lg = p.logit_part;
-  const int E = p.E;
-  auto epi = [=](int u, int row, int col, float v, float) { lg[(long long)col * E + u * 16 + row] = v; };
+  float* lgl = reinterpret_cast<float*>(smem + 2 * lp.xb + 2 * kWaves * 64 * 4 * 4);   // [4][kMaxT][16]
+  auto epi = [=](int u, int row, int col, float v, float) { lgl[((u - u0) * kMaxT + col) * 16 + row] = v; };
   Chunk<AF, false, 16> ck;
   const bool pr = wg_primable(KT, false);
   if (pr) stream_prime<AF, false, true, 16>(ck, u0, u1, KT, src);
@@ -1038,6 +1061,8 @@ __device__ __forceinline__ void phase_router(const LayerParams& p, char* smem) {
   trace_x(p, 7);
   stream_units_wg_primed<AF, false, AF != MK_FMT_F32>(u0, u1, KT, T, src, epi, red, p.dummy, ck, pr);
   if (u1 <= u0) return;
+  __syncthreads();
+  router_candidates(p, lgl, u0, u1);
   // the last workgroup to finish its router units computes the routing
   int* flag = reinterpret_cast<int*>(smem + kFlagOff);
   wg_release_begin();
