@@ -9,7 +9,10 @@ LIB = os.path.join(HERE, "libmk.so")
 SOURCES = ["mk_api.cpp", "mk_layer.hip", "mk_pack.hip", "mk_stack.hip"]
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-         "-munsafe-fp-atomics", "-Wno-unused-result"]
+         "-munsafe-fp-atomics", "-Wno-unused-result",
+         # atomics here are issued by one lane; the wave-level rewrite would
+         # wait for the result (and every load in flight) right after issue
+         "-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]
 
 
 def build(verbose: bool = False, extra=()) -> str:

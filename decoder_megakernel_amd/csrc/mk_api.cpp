@@ -84,7 +84,7 @@ int check_cfg(const mk_layer_config* c) {
   const long long lds_route = xb + 32768 + (long long)kMaxT * D.E * 4 + 3 * kMaxT * kMaxTopK * 4 +
                               (kMaxT * kMaxTopK + 8) * 4 + (long long)D.E * 4 + 16 + (kMaxT * kMaxTopK + 8) * 8;
   const long long lds_att = std::max((long long)kWaves * 16 * (D.dc + 8) * es + 16LL * (D.kvw + 8) * es,
-                                     4LL * 16 * D.dc * 4 + 4 * 64 * 2 * 4);
+                                     4LL * 16 * D.dc * 4 + 8 * 64 * 2 * 4);
   const long long lim = kLdsBytes - 1024;
   // the down projection stages two experts' activations below the routing tables
   if (2LL * kMaxT * (D.f + kXPad) * es > xb + 32768)
@@ -215,7 +215,7 @@ StLayout st_layout(const Dims& D, const Schedule& s) {
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
   l.bar = take(sizeof(BarrierState));
-  l.att_cnt = take((kRouteCnt + 1) * 4);
+  l.att_cnt = take((kGateCnt + 8 * kCntStride) * 4);
   l.experts = take((size_t)(D.E + D.nshared) * 8);
   l.trace = take((size_t)s.nwg * kTraceStride * 8);
   l.total = off;

@@ -17,6 +17,9 @@ constexpr int kTraceStride = 2 + 2 * kBarriers + kTraceX;
 constexpr int kLdsBytes = 160 * 1024 - 256;
 constexpr int kMaxTopK = 16;
 constexpr int kRouteCnt = 64;            // index of the router-completion counter in att_cnt
+constexpr int kGateCnt = 128;            // index of the first of 8 gate/up ticket counters in att_cnt,
+constexpr int kCntStride = 64;           // which sit 256 bytes apart (device-scope atomics on one
+                                         // line are serialised where they are performed)
 constexpr int kMaxExperts = 1024;        // routed experts per layer (16 logits per lane)
 constexpr int kStageCh = 18;             // float4s per lane when staging one activation row
 constexpr int kMaxStageK = kStageCh * 64 * 4;   // longest activation row (elements)

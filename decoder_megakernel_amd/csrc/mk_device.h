@@ -14,10 +14,32 @@ typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 
 // ------------------------------------------------------------------ memory helpers
-__device__ __forceinline__ u32x4 ld_stream16(const uint8_t* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+// Loads from device (global) memory through global-address-space pointers.
+// A load through a generic pointer becomes a FLAT instruction, which also
+// counts in the LDS counter: every wait for an LDS read would then wait for
+// all weight loads in flight as well.
+template <class T>
+using gptr = const __attribute__((address_space(1))) T*;
+template <class T>
+__device__ __forceinline__ T ldg(const T* p) {
+  return *(gptr<T>)(p);
 }
-__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ u32x4 ld_stream16(const uint8_t* p) {
+  return __builtin_nontemporal_load((gptr<u32x4>)(p));
+}
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *(gptr<u32x4>)(p); }
+
+// LDS transpose read (gfx950 ds_read_b64_tr_b16).  Within each group of 16
+// lanes, let D[i][k] be the k-th 16-bit element of the 8 bytes at lane i's
+// address; lane l of the group receives D[4e + l/4][l%4] as its element e.
+// Hence, for a row-major bf16 matrix M in LDS, lane i = 4e + q pointing at
+// M[r0 + e][c0 + 4q] hands every lane l the column slice M[r0 .. r0+3][c0 + l].
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ bf16x4 lds_read_tr16(const __bf16* p) {
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+  return __builtin_bit_cast(bf16x4, v);
+}
 
 // Wait until this wave's outstanding vector memory operations completed
 // (s_waitcnt vmcnt(0); expcnt and lgkmcnt left at their maxima).
@@ -98,6 +120,17 @@ __device__ __forceinline__ f32x4 tile_mma<MK_FMT_FP8_B128>(const u32x4& a, const
   return acc;
 }
 
+// ------------------------------------------------------------------ tracing
+// Timestamps of a traced launch are kept in LDS (the last KiB of the dynamic
+// allocation, which no phase uses) and written out once at the end, so that no
+// trace store is outstanding when a phase waits on its memory counter.
+constexpr int kTraceLdsOff = kLdsBytes - 1024;
+static_assert(kTraceStride * 8 <= 1024 - 16, "trace stamps and the barrier flag share the last KiB of LDS");
+__device__ __forceinline__ long long* trace_lds() {
+  extern __shared__ __attribute__((aligned(16))) char dyn_lds[];
+  return reinterpret_cast<long long*>(dyn_lds + kTraceLdsOff);
+}
+
 // ------------------------------------------------------------------ grid barrier
 // Two-level barrier over the whole persistent grid (see BarrierState).  Each
 // workgroup drains its stores and releases them at agent scope before it
@@ -109,7 +142,7 @@ __device__ __forceinline__ bool grid_barrier(const LayerParams& p, int idx, int*
   if (threadIdx.x == 0) {
     int ok = 1;
     uint64_t t0 = clock100();
-    if (p.trace) p.trace[(long long)blockIdx.x * kTraceStride + 1 + 2 * idx] = (long long)t0;
+    if (p.trace) trace_lds()[1 + 2 * idx] = (long long)t0;
     BarrierState* b = p.bar;
     if (__hip_atomic_load(&b->fault, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) {
       ok = 0;
@@ -142,7 +175,7 @@ __device__ __forceinline__ bool grid_barrier(const LayerParams& p, int idx, int*
       }
       acquire_agent();
     }
-    if (p.trace) p.trace[(long long)blockIdx.x * kTraceStride + 2 + 2 * idx] = (long long)clock100();
+    if (p.trace) trace_lds()[2 + 2 * idx] = (long long)clock100();
     *lds_flag = ok;
   }
   __syncthreads();
@@ -199,8 +232,8 @@ __device__ __forceinline__ void run_units(int u0, int u1, int NT, int T, const S
       buf[r] = ld_stream16(tp);
       if constexpr (DUAL) buf2[r] = ld_stream16(tp + 1024);
       if constexpr (FMT == MK_FMT_FP8_B128) {
-        sc[r] = isp[(t * TK) >> 7];
-        if constexpr (DUAL) sc2[r] = isp2[(t * TK) >> 7];
+        sc[r] = ldg(isp + ((t * TK) >> 7));
+        if constexpr (DUAL) sc2[r] = ldg(isp2 + ((t * TK) >> 7));
       }
     }
     if (++ij == c) {
@@ -307,8 +340,8 @@ __device__ __forceinline__ void run_wave_units(int u0, int u1, int NT, int T, co
     buf[r] = ld_stream16(tp);
     if constexpr (DUAL) buf2[r] = ld_stream16(tp + 1024);
     if constexpr (FMT == MK_FMT_FP8_B128) {
-      sc[r] = isp[(it * TK) >> 7];
-      if constexpr (DUAL) sc2[r] = isp2[(it * TK) >> 7];
+      sc[r] = ldg(isp + ((it * TK) >> 7));
+      if constexpr (DUAL) sc2[r] = ldg(isp2 + ((it * TK) >> 7));
     }
     if (++it == NT) {
       it = 0;
@@ -403,8 +436,8 @@ __device__ __forceinline__ void stream_prime(Chunk<FMT, DUAL, D>& c, int u0, int
     c.buf[r] = ld_stream16(cbase + r * STRIDE);
     if constexpr (DUAL) c.buf2[r] = ld_stream16(cbase + r * STRIDE + 1024);
     if constexpr (FMT == MK_FMT_FP8_B128) {
-      c.sc[r] = src.sbase(u)[((toff + r) * TK) >> 7];
-      if constexpr (DUAL) c.sc2[r] = src.sbase2(u)[((toff + r) * TK) >> 7];
+      c.sc[r] = ldg(src.sbase(u) + (((toff + r) * TK) >> 7));
+      if constexpr (DUAL) c.sc2[r] = ldg(src.sbase2(u) + (((toff + r) * TK) >> 7));
     }
   }
 }
@@ -437,8 +470,8 @@ __device__ __forceinline__ void run_stream(int u0, int u1, int NT, int T, const 
       buf[r] = ld_stream16(cbase + r * STRIDE);
       if constexpr (DUAL) buf2[r] = ld_stream16(cbase + r * STRIDE + 1024);
       if constexpr (FMT == MK_FMT_FP8_B128) {
-        sc[r] = sp[((tfirst + r) * TK) >> 7];
-        if constexpr (DUAL) sc2[r] = sp2[((tfirst + r) * TK) >> 7];
+        sc[r] = ldg(sp + (((tfirst + r) * TK) >> 7));
+        if constexpr (DUAL) sc2[r] = ldg(sp2 + (((tfirst + r) * TK) >> 7));
       }
     }
   };
@@ -493,8 +526,8 @@ __device__ __forceinline__ void run_stream(int u0, int u1, int NT, int T, const 
       buf[r] = ld_stream16(nb + r * STRIDE);
       if constexpr (DUAL) buf2[r] = ld_stream16(nb + r * STRIDE + 1024);
       if constexpr (FMT == MK_FMT_FP8_B128) {
-        sc[r] = nsp[has_next ? (((tn + r) * TK) >> 7) : 0];
-        if constexpr (DUAL) sc2[r] = nsp2[has_next ? (((tn + r) * TK) >> 7) : 0];
+        sc[r] = ldg(nsp + (has_next ? (((tn + r) * TK) >> 7) : 0));
+        if constexpr (DUAL) sc2[r] = ldg(nsp2 + (has_next ? (((tn + r) * TK) >> 7) : 0));
       }
     }
     if (ncc == 0) {
@@ -531,6 +564,132 @@ __device__ __forceinline__ void run_stream(int u0, int u1, int NT, int T, const 
     cu = ncu;
   }
   if constexpr (WG) __syncthreads();
+}
+
+// Workgroup-mode streaming over a unit sequence handed out at run time, so
+// that workgroups on faster XCDs take more units.  Workgroup b first takes
+// units b and b + nwg; the others (2 nwg + i) are handed out by eight ticket
+// counters, counter c owning the units with i % 8 == c: a workgroup draws
+// from the counter of its XCD (b % 8) and moves on to the next counter when
+// that one is exhausted, which spreads the atomics over eight addresses.
+// Wave 0 asks for the ticket of unit j+2 when unit j starts and publishes the
+// answer through LDS (`seq`, two slots) at unit j's reduction, so the ticket's
+// round trip overlaps a whole unit of streaming and the next unit's first
+// chunk is always requested one chunk ahead, as in run_stream.  The counters
+// `ctr[kCntStride * c]` must be zero before the first workgroup gets here.  Requires slice = NT/8
+// to be a multiple of D.
+template <int FMT, bool DUAL, int D, class Src, class Epi>
+__device__ __forceinline__ void run_stream_dyn(int U, int NT, int T, const Src& src, const Epi& epi, float* red,
+                                               const uint8_t* dummy, uint32_t* ctr, int* seq) {
+  constexpr int TK = tile_k(FMT);
+  constexpr long long STRIDE = DUAL ? 2048 : 1024;
+  const int w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int nwg = (int)gridDim.x;
+  const int slice = NT / kWaves;
+  const int cps = slice / D;
+  const int toff = w * slice;
+  int cur = (int)blockIdx.x < U ? (int)blockIdx.x : -1;
+  int nxt = (int)blockIdx.x + nwg < U ? (int)blockIdx.x + nwg : -1;
+  if (cur < 0 || cps <= 0) return;
+  const float* dsc = reinterpret_cast<const float*>(dummy);
+  u32x4 buf[D], buf2[D];
+  float sc[D], sc2[D];
+  {
+    const uint8_t* cbase = src.base(cur) + lane * 16 + (long long)toff * STRIDE;
+#pragma unroll
+    for (int r = 0; r < D; ++r) {
+      buf[r] = ld_stream16(cbase + r * STRIDE);
+      if constexpr (DUAL) buf2[r] = ld_stream16(cbase + r * STRIDE + 1024);
+      if constexpr (FMT == MK_FMT_FP8_B128) {
+        sc[r] = ldg(src.sbase(cur) + (((toff + r) * TK) >> 7));
+        if constexpr (DUAL) sc2[r] = ldg(src.sbase2(cur) + (((toff + r) * TK) >> 7));
+      }
+    }
+  }
+  uint32_t tk = 0;
+  int cq = (int)blockIdx.x & 7;     // counter drawn from (thread 0)
+  int cc = 0, par = 0;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  f32x4 acc2 = {0.f, 0.f, 0.f, 0.f};
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  while (true) {
+    if (cc == 0 && threadIdx.x == 0)
+      tk = __hip_atomic_fetch_add(ctr + kCntStride * cq, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    int ncc = cc + 1, un = cur;
+    if (ncc == cps) {
+      ncc = 0;
+      un = nxt;
+    }
+    const bool has_next = un >= 0;
+    const int tn = toff + ncc * D;
+    const uint8_t* nb = has_next ? src.base(un) + lane * 16 + (long long)tn * STRIDE : dummy + lane * 16;
+    const float* nsp = dsc;
+    const float* nsp2 = dsc;
+    if constexpr (FMT == MK_FMT_FP8_B128) {
+      if (has_next) {
+        nsp = src.sbase(un);
+        if constexpr (DUAL) nsp2 = src.sbase2(un);
+      }
+    }
+    const auto* bp = src.bbase(cur) + (toff + cc * D) * TK;
+#pragma unroll
+    for (int r = 0; r < D; ++r) {
+      if constexpr (FMT == MK_FMT_FP8_B128) {
+        const f32x4 tmp = tile_mma<FMT>(buf[r], bp + r * TK, zero);
+        acc += tmp * sc[r];
+        if constexpr (DUAL) {
+          const f32x4 tmp2 = tile_mma<FMT>(buf2[r], bp + r * TK, zero);
+          acc2 += tmp2 * sc2[r];
+        }
+      } else {
+        acc = tile_mma<FMT>(buf[r], bp + r * TK, acc);
+        if constexpr (DUAL) acc2 = tile_mma<FMT>(buf2[r], bp + r * TK, acc2);
+      }
+      buf[r] = ld_stream16(nb + r * STRIDE);
+      if constexpr (DUAL) buf2[r] = ld_stream16(nb + r * STRIDE + 1024);
+      if constexpr (FMT == MK_FMT_FP8_B128) {
+        sc[r] = ldg(nsp + (has_next ? (((tn + r) * TK) >> 7) : 0));
+        if constexpr (DUAL) sc2[r] = ldg(nsp2 + (has_next ? (((tn + r) * TK) >> 7) : 0));
+      }
+    }
+    cc = ncc;
+    if (ncc != 0) continue;
+    // unit `cur` complete: reduce across the waves, publish the unit after nxt
+    float* rb = red + (par ? UnitRed<FMT, DUAL>::kFloats : 0);
+    *reinterpret_cast<f32x4*>(rb + (w * 64 + lane) * 4) = acc;
+    if constexpr (DUAL) *reinterpret_cast<f32x4*>(rb + kWaves * 64 * 4 + (w * 64 + lane) * 4) = acc2;
+    if (threadIdx.x == 0) {
+      long long un2 = 2LL * nwg + 8LL * tk + cq;
+      for (int tries = 1; un2 >= U && tries < 8; ++tries) {
+        cq = (cq + 1) & 7;
+        tk = __hip_atomic_fetch_add(ctr + kCntStride * cq, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        un2 = 2LL * nwg + 8LL * tk + cq;
+      }
+      seq[par] = un2 < U ? (int)un2 : -1;
+    }
+    __syncthreads();
+    if (threadIdx.x < 256) {
+      const int col = threadIdx.x & 15, row = threadIdx.x >> 4;
+      const int l = (row >> 2) * 16 + col, e = row & 3;
+      if (col < T) {
+        float v = 0.f, v2 = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < kWaves; ++ww) {
+          v += rb[(ww * 64 + l) * 4 + e];
+          if constexpr (DUAL) v2 += rb[kWaves * 64 * 4 + (ww * 64 + l) * 4 + e];
+        }
+        epi(cur, row, col, v, v2);
+      }
+    }
+    acc = zero;
+    acc2 = zero;
+    cur = nxt;
+    nxt = nxt >= 0 ? seq[par] : -1;
+    par ^= 1;
+    if (cur < 0) break;
+  }
+  __syncthreads();
 }
 
 // Dispatch: the branch-free engine when the slice length allows, else the

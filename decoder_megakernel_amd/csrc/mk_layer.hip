@@ -33,13 +33,16 @@ struct LdsPlan {
     xb = (xb + 255) & ~255;
   }
 };
-constexpr int kMiscOff = kLdsBytes - 1024;     // 256 floats of scratch + the barrier flag
-constexpr int kFlagOff = kLdsBytes - 16;
+constexpr int kFlagOff = kLdsBytes - 16;        // the barrier flag, after the trace stamps
+constexpr int kSeqOff = kLdsBytes - 32;         // two ints: unit sequence of the ticket-fed streams
+__device__ __forceinline__ int* seq_lds() {
+  extern __shared__ __attribute__((aligned(16))) char dyn_lds[];
+  return reinterpret_cast<int*>(dyn_lds + kSeqOff);
+}
 
 // sub-phase timestamp (thread 0, only when tracing)
 __device__ __forceinline__ void trace_x(const LayerParams& p, int slot) {
-  if (p.trace && threadIdx.x == 0)
-    p.trace[(long long)blockIdx.x * kTraceStride + 2 + 2 * kBarriers + slot] = (long long)clock100();
+  if (p.trace && threadIdx.x == 0) trace_lds()[2 + 2 * kBarriers + slot] = (long long)clock100();
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
@@ -90,7 +93,7 @@ static_assert(kMaxT <= kWaves, "one staged row per wave");
 template <class A, bool NORM>
 __device__ __forceinline__ void rows_to_lds(const float* src, int T, int K, A* xs, A* lo, int XS,
                                             const float* gamma, float eps, char* smem,
-                                            long long* tr = nullptr) {
+                                            bool tr = false) {
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n4 = K / 4;
   (void)smem;
@@ -102,8 +105,8 @@ __device__ __forceinline__ void rows_to_lds(const float* src, int T, int K, A* x
     for (int c = 0; c < kStageCh; ++c) {
       const int i = lane + 64 * c;
       if (i < n4) {
-        v[c] = *reinterpret_cast<const f32x4*>(row + 4 * i);
-        if constexpr (NORM) gm[c] = *reinterpret_cast<const f32x4*>(gamma + 4 * i);
+        v[c] = ldg(reinterpret_cast<const f32x4*>(row + 4 * i));
+        if constexpr (NORM) gm[c] = ldg(reinterpret_cast<const f32x4*>(gamma + 4 * i));
       }
     }
     float r = 1.f;
@@ -112,10 +115,10 @@ __device__ __forceinline__ void rows_to_lds(const float* src, int T, int K, A* x
 #pragma unroll
       for (int c = 0; c < kStageCh; ++c)
         if (lane + 64 * c < n4) ss += v[c][0] * v[c][0] + v[c][1] * v[c][1] + v[c][2] * v[c][2] + v[c][3] * v[c][3];
-      if (tr && lane == 0 && w == 0) tr[10] = (long long)clock100();
+      if (tr && lane == 0 && w == 0) trace_lds()[2 + 2 * kBarriers + 10] = (long long)clock100();
       ss = wave_sum(ss);
       r = 1.0f / sqrtf(ss / (float)K + eps);
-      if (tr && lane == 0 && w == 0) tr[11] = (long long)clock100();
+      if (tr && lane == 0 && w == 0) trace_lds()[2 + 2 * kBarriers + 11] = (long long)clock100();
     }
     A* xr = xs + (long long)w * XS;
 #pragma unroll
@@ -210,7 +213,7 @@ __device__ __forceinline__ void phase_qkv(const LayerParams& p, char* smem) {
   const bool pr = wg_primable(NT, false);
   if (pr) stream_prime<AF, false, true, 16>(ck, u0, u1, NT, src);
   rows_to_lds<A, true>(p.H, T, p.d, xs, (A*)nullptr, XS, p.g1, p.eps, smem,
-                       p.trace ? p.trace + (long long)blockIdx.x * kTraceStride + 2 + 2 * kBarriers : nullptr);
+                       p.trace != nullptr);
   trace_x(p, 5);
   stream_units_wg_primed<AF, false, false>(u0, u1, NT, T, src, epi, red, p.dummy, ck, pr);
 }
@@ -234,7 +237,7 @@ __device__ __forceinline__ void phase_rope_kv(const LayerParams& p, int L, int t
   const float* part = p.qkv_part;
   auto psum = [&](int t, int idx) {
     float v = 0.f;
-    for (int s = 0; s < S; ++s) v += part[((long long)s * T + t) * nrow + idx];
+    for (int s = 0; s < S; ++s) v += ldg(part + ((long long)s * T + t) * nrow + idx);
     return v;
   };
   for (int it = tid; it < T * per_t; it += nthreads) {
@@ -290,10 +293,10 @@ __device__ __forceinline__ f32x4 tile_mma_reg<MK_FMT_BF16>(const u32x4& a, const
 template <int FMT>
 __device__ __forceinline__ typename BReg<FMT>::T load_b(const float* src);
 template <>
-__device__ __forceinline__ f32x4 load_b<MK_FMT_F32>(const float* src) { return *reinterpret_cast<const f32x4*>(src); }
+__device__ __forceinline__ f32x4 load_b<MK_FMT_F32>(const float* src) { return ldg(reinterpret_cast<const f32x4*>(src)); }
 template <>
 __device__ __forceinline__ bf16x8 load_b<MK_FMT_BF16>(const float* src) {
-  return to_bf16x8(*reinterpret_cast<const f32x4*>(src), *reinterpret_cast<const f32x4*>(src + 4));
+  return to_bf16x8(ldg(reinterpret_cast<const f32x4*>(src)), ldg(reinterpret_cast<const f32x4*>(src + 4)));
 }
 
 template <int FMT>
@@ -328,8 +331,8 @@ __device__ __forceinline__ void phase_absorb(const LayerParams& p) {
       f32x4 q0 = {0.f, 0.f, 0.f, 0.f}, q1 = {0.f, 0.f, 0.f, 0.f};
       for (int s = 0; s < S; ++s) {
         const float* src = p.qkv_part + ((long long)s * T + jj) * nrow + h * p.qw + e0;
-        q0 += *reinterpret_cast<const f32x4*>(src);
-        if (EPL == 8) q1 += *reinterpret_cast<const f32x4*>(src + 4);
+        q0 += ldg(reinterpret_cast<const f32x4*>(src));
+        if (EPL == 8) q1 += ldg(reinterpret_cast<const f32x4*>(src + 4));
       }
       acc = tile_mma_reg<AF>(a, make_b<AF>(q0, q1), acc);
     }
@@ -404,7 +407,7 @@ __device__ __forceinline__ void phase_attention(const LayerParams& p, int L, cha
           const int jq = i / n4, dd = (i - jq * n4) * 4;
           const int qq = min(qt * 16 + jq, NQ - 1);
           const float* src = dd < dc ? p.qabs + (long long)qq * dc + dd : p.qrope + (long long)qq * p.dr + (dd - dc);
-          qv[c] = *reinterpret_cast<const f32x4*>(src);
+          qv[c] = ldg(reinterpret_cast<const f32x4*>(src));
         }
       }
 #pragma unroll
@@ -484,14 +487,18 @@ __device__ __forceinline__ void phase_attention(const LayerParams& p, int L, cha
         bf16x4 pb;
 #pragma unroll
         for (int e = 0; e < 4; ++e) pb[e] = (__bf16)pe[e];
+        // A operand (dims x keys) read transposed from the row-major chunk:
+        // lane (g, 4e + q) points at key 4g + e, dims 16 db + 4q .. + 3
+        const __bf16* tb = reinterpret_cast<const __bf16*>(cb) + (4 * g + (j >> 2)) * CS + 4 * (j & 3);
 #pragma unroll
-        for (int db = 0; db < DBMAX; ++db) {
-          if (db < DB) {
-            bf16x4 av;
+        for (int d0 = 0; d0 < DBMAX; d0 += 8) {
+          bf16x4 av[8];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) av[e] = (__bf16)cb[(4 * g + e) * CS + db * 16 + j];
-            acc[db] = mma_bf16_k16(av, pb, acc[db] * alpha);
-          }
+          for (int i = 0; i < 8; ++i)
+            if (d0 + i < DB) av[i] = lds_read_tr16(tb + (d0 + i) * 16);
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            if (d0 + i < DB) acc[d0 + i] = mma_bf16_k16(av[i], pb, acc[d0 + i] * alpha);
         }
       } else {
 #pragma unroll
@@ -508,50 +515,72 @@ __device__ __forceinline__ void phase_attention(const LayerParams& p, int L, cha
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
-    // merge the 8 waves' (m, l, Z) in LDS, tree order 4+0.., 2+0.., 1+0
+    // merge the 8 waves' (m, l, Z): every wave rescales its state to the
+    // common maximum; waves 4..7 hand their Z to waves 0..3 through LDS, the
+    // four pair sums go back to LDS, and wave w sums latent blocks w, w+8, ...
+    // of the four in a fixed order and writes them out.
     __syncthreads();
     trace_x(p, 1);
     // Partial state layout (LDS and global): block db of the latent holds, per
     // lane, the 4 values acc[db] (MFMA result layout: lane (g, j) has dims
     // 16 db + 4 g + e of query j), so every access is one 16-byte vector.
     f32x4* mb = reinterpret_cast<f32x4*>(smem);                 // [4][DB][64]
-    float* ml = reinterpret_cast<float*>(smem) + 4 * DB * 64 * 4;   // [4][64][2]
-    for (int half = 4; half >= 1; half >>= 1) {
-      if (w >= half && w < 2 * half) {
-        f32x4* zb = mb + (long long)(w - half) * DB * 64;
+    float* ml = reinterpret_cast<float*>(smem) + 4 * DB * 64 * 4;   // [8][64][2]
+    ml[(w * 64 + lane) * 2] = m_run;
+    ml[(w * 64 + lane) * 2 + 1] = l_run;
+    __syncthreads();
+    float M = -INFINITY;
 #pragma unroll
-        for (int db = 0; db < DBMAX; ++db)
-          if (db < DB) zb[db * 64 + lane] = acc[db];
-        ml[((w - half) * 64 + lane) * 2] = m_run;
-        ml[((w - half) * 64 + lane) * 2 + 1] = l_run;
-      }
-      __syncthreads();
-      if (w < half) {
-        const f32x4* zb = mb + (long long)w * DB * 64;
-        const float mo = ml[(w * 64 + lane) * 2], lo = ml[(w * 64 + lane) * 2 + 1];
-        const float M = fmaxf(m_run, mo);
-        float sa = 0.f, sb = 0.f;
-        if (M != -INFINITY) {
-          sa = __expf(m_run - M);
-          sb = __expf(mo - M);
-        }
-#pragma unroll
-        for (int db = 0; db < DBMAX; ++db)
-          if (db < DB) acc[db] = acc[db] * sa + zb[db * 64 + lane] * sb;
-        l_run = l_run * sa + lo * sb;
-        m_run = M;
-      }
-      __syncthreads();
-    }
-    if (w == 0) {
-      f32x4* zp = reinterpret_cast<f32x4*>(p.att_part + (long long)u * 16 * dc);
+    for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, ml[(ww * 64 + lane) * 2]);
+    const float sw = M == -INFINITY ? 0.f : __expf(m_run - M);
+    if (w >= 4) {
+      f32x4* zb = mb + (long long)(w - 4) * DB * 64;
 #pragma unroll
       for (int db = 0; db < DBMAX; ++db)
-        if (db < DB) zp[db * 64 + lane] = acc[db];
-      if (g == 0) {
-        p.att_ml[((long long)u * 16 + j) * 2] = m_run;
-        p.att_ml[((long long)u * 16 + j) * 2 + 1] = l_run;
+        if (db < DB) zb[db * 64 + lane] = acc[db] * sw;
+    }
+    __syncthreads();
+    if (w < 4) {
+      f32x4* zb = mb + (long long)w * DB * 64;
+#pragma unroll
+      for (int d0 = 0; d0 < DBMAX; d0 += 8) {
+        f32x4 t[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          if (d0 + i < DB) t[i] = zb[(d0 + i) * 64 + lane];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          if (d0 + i < DB) zb[(d0 + i) * 64 + lane] = acc[d0 + i] * sw + t[i];
       }
+    }
+    __syncthreads();
+    {
+      f32x4* zp = reinterpret_cast<f32x4*>(p.att_part + (long long)u * 16 * dc);
+      constexpr int NBW = (DBMAX + kWaves - 1) / kWaves;
+      f32x4 t[NBW][4];
+#pragma unroll
+      for (int i = 0; i < NBW; ++i) {
+        const int db = w + kWaves * i;
+        if (db < DB) {
+#pragma unroll
+          for (int b = 0; b < 4; ++b) t[i][b] = mb[((long long)b * DB + db) * 64 + lane];
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < NBW; ++i) {
+        const int db = w + kWaves * i;
+        if (db < DB) zp[db * 64 + lane] = (t[i][0] + t[i][1]) + (t[i][2] + t[i][3]);
+      }
+    }
+    if (w == 0 && g == 0) {
+      float Ls = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < kWaves; ++ww) {
+        const float mw = ml[(ww * 64 + lane) * 2];
+        Ls += mw == -INFINITY ? 0.f : ml[(ww * 64 + lane) * 2 + 1] * __expf(mw - M);
+      }
+      p.att_ml[((long long)u * 16 + j) * 2] = M;
+      p.att_ml[((long long)u * 16 + j) * 2 + 1] = Ls;
     }
     trace_x(p, 2);
   }
@@ -575,8 +604,8 @@ __device__ __forceinline__ void phase_merge(const LayerParams& p, int L, char* s
     const int qt = u / s_kv, s = u - qt * s_kv;
     const int ub = qt * s_kv;
     for (int i = threadIdx.x; i < s_kv * 16; i += kThreads) {
-      mm[i] = p.att_ml[((long long)ub * 16 + i) * 2];
-      cf[i] = p.att_ml[((long long)ub * 16 + i) * 2 + 1];
+      mm[i] = ldg(p.att_ml + ((long long)ub * 16 + i) * 2);
+      cf[i] = ldg(p.att_ml + ((long long)ub * 16 + i) * 2 + 1);
     }
     __syncthreads();
     if (threadIdx.x < 16) {
@@ -608,11 +637,11 @@ __device__ __forceinline__ void phase_merge(const LayerParams& p, int L, char* s
         for (; ss + 12 < s_kv; ss += 16) {
           f32x4 zz[4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) zz[i] = zp[(ss + 4 * i) * sstride];
+          for (int i = 0; i < 4; ++i) zz[i] = ldg(zp + (ss + 4 * i) * sstride);
 #pragma unroll
           for (int i = 0; i < 4; ++i) a0 += zz[i] * mm[(ss + 4 * i) * 16 + jq];
         }
-        for (; ss < s_kv; ss += 4) a0 += zp[ss * sstride] * mm[ss * 16 + jq];
+        for (; ss < s_kv; ss += 4) a0 += ldg(zp + ss * sstride) * mm[ss * 16 + jq];
       }
       *reinterpret_cast<f32x4*>(red + (quarter * 128 + slot) * 4) = a0;
       __syncthreads();
@@ -707,7 +736,7 @@ __device__ __forceinline__ void phase_wo(const LayerParams& p, char* smem) {
   const int d = p.d;
   auto epi = [=](int u, int row, int col, float v, float) {
     const long long i = (long long)col * d + u * 16 + row;
-    hp[i] = H[i] + v;
+    hp[i] = ldg(H + i) + v;
   };
   Chunk<AF, false, 16> ck;
   const bool pr = wg_primable(KT, false);
@@ -782,8 +811,8 @@ __device__ __forceinline__ void route_cands(const LayerParams& p, const RouteLds
   for (int i = 0; i < EPL; ++i) {
     const int c = min(lane + 64 * i, NC - 1);
     const int o = (c / K8) * 16 + c % K8;
-    lv[i] = cv[o];
-    id[i] = ci[o];
+    lv[i] = ldg(cv + o);
+    id[i] = ldg(ci + o);
   }
   float mx = -INFINITY;
 #pragma unroll
@@ -842,7 +871,7 @@ __device__ __forceinline__ void router_candidates(const LayerParams& p, const fl
   for (int u = u0; u < u1; ++u) {
     if (w < T && lane < 16) {
       const int e = u * 16 + lane;
-      const float v = lgl[((u - u0) * kMaxT + w) * 16 + lane] + (p.rbias ? p.rbias[e] : 0.f);
+      const float v = lgl[((u - u0) * kMaxT + w) * 16 + lane] + (p.rbias ? ldg(p.rbias + e) : 0.f);
       p.logits[(long long)w * E + e] = v;
       const uint32_t k = fkey(v);
       int rank = 0;
@@ -932,12 +961,12 @@ __device__ __forceinline__ void route_load(const LayerParams& p, const RouteLds&
   const uint8_t* b = nullptr;
   int ns = 0;
   if (tid < T * K) {
-    sel = p.route_sel[tid];
-    gt = p.route_gate[tid];
-    so = p.route_pub[16 + tid];
+    sel = ldg(p.route_sel + tid);
+    gt = ldg(p.route_gate + tid);
+    so = ldg(p.route_pub + 16 + tid);
   }
-  if (tid < kMaxSlots) b = pub_blk[tid];
-  if (tid == 0) ns = p.route_pub[0];
+  if (tid < kMaxSlots) b = ldg(pub_blk + tid);
+  if (tid == 0) ns = ldg(p.route_pub);
   if (tid < T * K) {
     const int t = tid / K, k = tid - t * K;
     r.sel[t * kMaxTopK + k] = sel;
@@ -956,7 +985,8 @@ __device__ __forceinline__ void route_load(const LayerParams& p, const RouteLds&
 struct NoStage {
   __device__ void operator()() const {}
 };
-// MODE 0: workgroup units [u0, u1); 1: wave units [u0, u1).  `stage` runs after
+// MODE 0: workgroup units [u0, u1); 1: wave units [u0, u1); 2: workgroup units
+// 0 .. u1-1 handed out at run time by the ticket counters.  `stage` runs after
 // the first weight chunk was requested and before it is used (workgroup mode).
 template <int EF, int MODE, class Stage = NoStage>
 __device__ __forceinline__ void gateup_units(const LayerParams& p, const uint8_t* const* blk, int s0, int u0, int u1,
@@ -993,7 +1023,10 @@ __device__ __forceinline__ void gateup_units(const LayerParams& p, const uint8_t
     const float sg = v / (1.0f + expf(-v));
     hb[((long long)sl * T + col) * f + rt * 16 + row] = to_act<A>(sg * v2);
   };
-  if constexpr (MODE == 1) {
+  if constexpr (MODE == 2) {
+    stage();
+    run_stream_dyn<EF, true, 8>(u1, KT, T, src, epi, red, p.dummy, p.att_cnt + kGateCnt, seq_lds());
+  } else if constexpr (MODE == 1) {
     stage();
     stream_units_wave<EF, true>(u0, u1, KT, T, src, epi, p.dummy);
   } else {
@@ -1092,6 +1125,12 @@ __device__ __forceinline__ void phase_route_gateup(const LayerParams& p, char* s
   const int s0 = shared_early(p) ? p.nshared : 0;     // slots whose gate/up ran in P5
   const int ns = *r.nslots;
   const int U = (ns - s0) * (p.f / 16);
+  const int KT = p.d / tile_k(EF);
+  if (KT % kWaves == 0 && (KT / kWaves) % 8 == 0) {
+    // units handed out at run time (ticket counter), 8 waves per unit
+    gateup_units<EF, 2>(p, r.blk + s0, s0, 0, U, xs, red);
+    return;
+  }
   int u0, u1;
   split_range(U, gridDim.x, blockIdx.x, u0, u1);
   if (U >= 2 * (int)gridDim.x * kWaves)
@@ -1181,10 +1220,10 @@ __device__ __forceinline__ void phase_combine(const LayerParams& p, char* smem, 
   const int T = p.T, d = p.d, K = p.topk;
   for (int i = blockIdx.x * kThreads + threadIdx.x; i < T * d; i += gridDim.x * kThreads) {
     const int t = i / d, c = i - t * d;
-    float v = p.hp[i];
+    float v = ldg(p.hp + i);
     for (int k = 0; k < K; ++k)
-      v += r.gate[t * kMaxTopK + k] * p.ybuf[((long long)r.slot_of[t * kMaxTopK + k] * T + t) * d + c];
-    for (int s = 0; s < p.nshared; ++s) v += p.ybuf[((long long)s * T + t) * d + c];
+      v += r.gate[t * kMaxTopK + k] * ldg(p.ybuf + ((long long)r.slot_of[t * kMaxTopK + k] * T + t) * d + c);
+    for (int s = 0; s < p.nshared; ++s) v += ldg(p.ybuf + ((long long)s * T + t) * d + c);
     p.out[i] = v;
   }
 }
@@ -1194,17 +1233,24 @@ template <int AF, int EF, int KF, int KBMAX, int DBMAX, bool EXACT>
 __global__ __launch_bounds__(kThreads, 1) void layer_kernel(LayerParams p) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   int* flag = reinterpret_cast<int*>(smem + kFlagOff);
-  const int L = p.L_dev ? *p.L_dev : p.L;
+  const int L = p.L_dev ? ldg(p.L_dev) : p.L;
   if (L < 0 || (long long)L + p.T > p.kv_capacity) {
     // every workgroup reads the same L and leaves before the first barrier
     if (blockIdx.x == 0 && threadIdx.x == 0)
       __hip_atomic_store(&p.bar->fault, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return;
   }
-  if (p.trace && threadIdx.x == 0) p.trace[(long long)blockIdx.x * kTraceStride] = (long long)clock100();
+  if (p.trace && threadIdx.x == 0) {
+    long long* tl = trace_lds();
+    for (int i = 1; i < kTraceStride; ++i) tl[i] = 0;
+    tl[0] = (long long)clock100();
+  }
   // attention split counters: cleared here, used after two grid barriers
   if (blockIdx.x == 0 && threadIdx.x <= kRouteCnt)
     __hip_atomic_store(&p.att_cnt[threadIdx.x], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (blockIdx.x == 0 && threadIdx.x < 8)
+    __hip_atomic_store(&p.att_cnt[kGateCnt + kCntStride * threadIdx.x], 0u, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
   phase_qkv<AF>(p, smem);
   if (!grid_barrier(p, 0, flag)) return;
   {
@@ -1237,8 +1283,11 @@ __global__ __launch_bounds__(kThreads, 1) void layer_kernel(LayerParams p) {
   if (!grid_barrier(p, 8, flag)) return;
   LdsPlan lp(p, EF == MK_FMT_F32 ? 4 : 2);
   phase_combine(p, smem, lp.xb);
-  if (p.trace && threadIdx.x == 0)
-    p.trace[(long long)blockIdx.x * kTraceStride + 1 + 2 * kBarriers] = (long long)clock100();
+  if (p.trace && threadIdx.x == 0) {
+    long long* tl = trace_lds();
+    tl[1 + 2 * kBarriers] = (long long)clock100();
+    for (int i = 0; i < kTraceStride; ++i) p.trace[(long long)blockIdx.x * kTraceStride + i] = tl[i];
+  }
 }
 
 // Instantiations: all-fp32 (d_latent + d_rope <= 160, d_latent <= 128),
