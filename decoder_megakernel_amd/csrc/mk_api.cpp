@@ -42,6 +42,10 @@ struct Dims {
   int af, ef, kf;
 };
 
+LayerKernelFn kernel_of(const Dims& D) {
+  return layer_kernel_for(D.af, D.ef, D.kf, D.d, D.nh, D.dh, D.dc, D.dr, D.E, D.topk, D.nshared, D.f);
+}
+
 Dims dims_of(const mk_layer_config* c) {
   Dims D;
   D.d = c->d_model; D.nh = c->n_heads; D.dh = c->d_head; D.dc = c->d_latent; D.dr = c->d_rope;
@@ -79,6 +83,7 @@ int check_cfg(const mk_layer_config* c) {
   const int dmax = std::max(D.d, std::max(D.nh * D.dh, D.f));
   if (dmax > kMaxStageK)
     return fail(MK_ERR_UNSUPPORTED_SHAPE, "d_model, n_heads*d_head and d_ff must be <= %d", kMaxStageK);
+  if (D.d > kMaxModel) return fail(MK_ERR_UNSUPPORTED_SHAPE, "d_model must be <= %d", kMaxModel);
   const long long xb = align256((size_t)kMaxT * (dmax + kXPad) * es);
   const long long lds_router = 2 * xb + 2 * kWaves * 64 * 4 * 4 + 4LL * kMaxT * 16 * 4;
   const long long lds_route = xb + 32768 + (long long)kMaxT * D.E * 4 + 3 * kMaxT * kMaxTopK * 4 +
@@ -92,7 +97,7 @@ int check_cfg(const mk_layer_config* c) {
   if (lds_router > lim || lds_route > lim || lds_att > lim)
     return fail(MK_ERR_UNSUPPORTED_SHAPE, "shape exceeds the LDS plan (router %lld, route %lld, attention %lld > %lld bytes)",
                 lds_router, lds_route, lds_att, lim);
-  if (!layer_kernel_for(D.af, D.ef, D.kf, D.kvw, D.dc)) return fail(MK_ERR_UNSUPPORTED_SHAPE, "no kernel for this shape");
+  if (!kernel_of(D)) return fail(MK_ERR_UNSUPPORTED_SHAPE, "no kernel for this shape");
   return MK_OK;
 }
 
@@ -282,7 +287,7 @@ int mk_query_device(int hip_device, mk_device_info* out) {
   HIP_OK(hipGetDeviceCount(&n));
   if (hip_device < 0 || hip_device >= n) return fail(MK_ERR_INVALID_ARG, "no HIP device %d", hip_device);
   DevInfo di;
-  LayerKernelFn fn = layer_kernel_for(MK_FMT_BF16, MK_FMT_FP8_B128, MK_FMT_BF16, 576, 512);
+  LayerKernelFn fn = layer_kernel_for(MK_FMT_BF16, MK_FMT_FP8_B128, MK_FMT_BF16, 4096, 32, 128, 512, 64, 384, 8, 1, 2048);
   hipDeviceProp_t prop;
   HIP_OK(hipGetDeviceProperties(&prop, hip_device));
   out->hip_device = hip_device;
@@ -321,7 +326,7 @@ static int sizes_for(const mk_layer_config* cfg, int dev, WsLayout* wl, StLayout
   if (rc) return rc;
   const Dims D = dims_of(cfg);
   DevInfo di;
-  rc = device_info(dev, &di, layer_kernel_for(D.af, D.ef, D.kf, D.kvw, D.dc));
+  rc = device_info(dev, &di, kernel_of(D));
   if (rc) return rc;
   const Schedule s = make_schedule(D, di.nwg);
   if (wl) *wl = ws_layout(D, s);
@@ -406,7 +411,7 @@ int mk_layer_init(const mk_layer_config* cfg, const mk_layer_weights* w, void* s
   const Dims D = dims_of(cfg);
   for (int e = 0; e < D.E + D.nshared; ++e)
     if (!w->experts[e]) return fail(MK_ERR_INVALID_ARG, "expert block %d is null", e);
-  LayerKernelFn fn = layer_kernel_for(D.af, D.ef, D.kf, D.kvw, D.dc);
+  LayerKernelFn fn = kernel_of(D);
   DevInfo di;
   rc = device_info(hip_device, &di, fn);
   if (rc) return rc;

@@ -23,6 +23,8 @@ constexpr int kCntStride = 64;           // which sit 256 bytes apart (device-sc
 constexpr int kMaxExperts = 1024;        // routed experts per layer (16 logits per lane)
 constexpr int kStageCh = 18;             // float4s per lane when staging one activation row
 constexpr int kMaxStageK = kStageCh * 64 * 4;   // longest activation row (elements)
+constexpr int kNormCh = 16;              // float4s per lane when normalising one hidden row
+constexpr int kMaxModel = kNormCh * 64 * 4;     // longest hidden row (d_model)
 
 // Packed tile geometry: one tile = 16 rows x kTileK[fmt] columns = 1 KiB,
 // lane l holds row (l % 16) and 16 consecutive bytes of columns

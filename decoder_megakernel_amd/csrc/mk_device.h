@@ -419,25 +419,42 @@ struct Chunk {
 // Issues the loads of a stream's first chunk (the same one run_stream would
 // load first), so that they can be in flight while the activation operand is
 // staged; run_stream<..., PRIMED = true> then starts from these registers.
+// The D loads are issued whether or not this workgroup has work (without work,
+// or with `enable` false, they read `dummy`), so the number of loads in flight
+// after the call does not depend on a branch and later waits for older loads
+// can count past them.
 template <int FMT, bool DUAL, bool WG, int D, class Src>
-__device__ __forceinline__ void stream_prime(Chunk<FMT, DUAL, D>& c, int u0, int u1, int NT, const Src& src) {
+__device__ __forceinline__ void stream_prime(Chunk<FMT, DUAL, D>& c, int u0, int u1, int NT, const Src& src,
+                                             const uint8_t* dummy, bool enable = true) {
   constexpr int TK = tile_k(FMT);
   constexpr long long STRIDE = DUAL ? 2048 : 1024;
   const int w = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int slice = WG ? NT / kWaves : NT;
   const int nu = WG ? (u1 - u0) : (u1 - u0 > w ? (u1 - u0 - w + kWaves - 1) / kWaves : 0);
-  if (nu <= 0 || slice / D <= 0) return;
-  const int u = WG ? u0 : u0 + w;
+  const bool any = enable && nu > 0 && slice / D > 0;
   const int toff = WG ? w * slice : 0;
-  const uint8_t* cbase = src.base(u) + lane * 16 + (long long)toff * STRIDE;
+  const uint8_t* cbase = dummy + lane * 16;
+  const float* sp = reinterpret_cast<const float*>(dummy);
+  const float* sp2 = sp;
+  int soff = 0;
+  if (any) {
+    const int u = WG ? u0 : u0 + w;
+    cbase = src.base(u) + lane * 16 + (long long)toff * STRIDE;
+    if constexpr (FMT == MK_FMT_FP8_B128) {
+      sp = src.sbase(u);
+      if constexpr (DUAL) sp2 = src.sbase2(u);
+    }
+    soff = toff;
+  }
 #pragma unroll
   for (int r = 0; r < D; ++r) {
     c.buf[r] = ld_stream16(cbase + r * STRIDE);
     if constexpr (DUAL) c.buf2[r] = ld_stream16(cbase + r * STRIDE + 1024);
     if constexpr (FMT == MK_FMT_FP8_B128) {
-      c.sc[r] = ldg(src.sbase(u) + (((toff + r) * TK) >> 7));
-      if constexpr (DUAL) c.sc2[r] = ldg(src.sbase2(u) + (((toff + r) * TK) >> 7));
+      const int si = any ? (((soff + r) * TK) >> 7) : 0;
+      c.sc[r] = ldg(sp + si);
+      if constexpr (DUAL) c.sc2[r] = ldg(sp2 + si);
     }
   }
 }

@@ -5,7 +5,9 @@
 namespace mk {
 
 typedef void (*LayerKernelFn)(LayerParams);
-LayerKernelFn layer_kernel_for(int af, int ef, int kf, int kvw, int dc);
+// The kernel instance for a layer's formats and dimensions (null if none).
+LayerKernelFn layer_kernel_for(int af, int ef, int kf, int d, int nh, int dh, int dc, int dr, int E, int topk,
+                               int nshared, int f);
 
 int launch_pack(const void* src, int fmt, int nb, int R, int K, long long sb, long long sr, long long sk,
                 void* dst, long long dst_stride, long long dst_off, hipStream_t stream);

@@ -18,6 +18,8 @@
 //   P6  gate+up projections of every routed expert: silu(W1 x) * W3 x
 //   P7  down projections W2 h of every listed expert
 //   P8  out = H' + sum_k gate_k y_k + y_shared
+#include <type_traits>
+
 #include "mk_device.h"
 
 namespace mk {
@@ -56,6 +58,39 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// Sums of N values over the wave, all reduced together so that each step's
+// cross-lane moves are issued back to back: DPP moves (VALU, no LDS round
+// trip) combine the lanes of each row of 16, then two swizzles combine the
+// four rows.  The association differs from lane to lane, so the N results are
+// to be read from one lane (lane 0 here).
+template <int N>
+__device__ __forceinline__ void wave_sums(float (&v)[N]) {
+  auto dpp = [](float x, auto ctrl) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), decltype(ctrl)::value, 0xF, 0xF, false));
+  };
+  typedef std::integral_constant<int, 0xB1> qp1032;    // quad_perm [1,0,3,2]
+  typedef std::integral_constant<int, 0x4E> qp2301;    // quad_perm [2,3,0,1]
+  typedef std::integral_constant<int, 0x124> ror4;     // row_ror:4
+  typedef std::integral_constant<int, 0x128> ror8;     // row_ror:8
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] += dpp(v[i], qp1032());
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] += dpp(v[i], qp2301());
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] += dpp(v[i], ror4());
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] += dpp(v[i], ror8());
+  float u[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) u[i] = __shfl_xor(v[i], 16);
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] += u[i];
+#pragma unroll
+  for (int i = 0; i < N; ++i) u[i] = __shfl_xor(v[i], 32);
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] += u[i];
+}
+
 __device__ __forceinline__ void split_range(int total, int parts, int i, int& a, int& b) {
   long long q = (long long)total * i / parts, r = (long long)total * (i + 1) / parts;
   a = (int)q;
@@ -81,84 +116,130 @@ template <> __device__ __forceinline__ f32x4 round4<__bf16>(const f32x4& v) {
   return f32x4{(float)(__bf16)v[0], (float)(__bf16)v[1], (float)(__bf16)v[2], (float)(__bf16)v[3]};
 }
 
-// Stages T <= kMaxT fp32 rows of length K (K % 4 == 0, K <= kMaxStageK) into
-// LDS as the MFMA operand type, row stride XS.  Wave w stages row w (lane l
-// handles float4 columns l, l + 64, ...), so each row's loads, its sum of
-// squares and its scaling stay inside one wave: one round trip to memory, one
-// wave reduction, one workgroup barrier at the end.  With NORM each row is
-// RMS-normalised on the way: x = (h * (1/sqrt(mean(h^2) + eps))) * gamma.
+// Stages T <= kMaxT fp32 rows of length K (K % 4 == 0, K <= kMaxModel) into
+// LDS as the MFMA operand type, row stride XS.  Wave w holds the float4
+// columns w*64 + lane + 512 c of every row, so a lane keeps at most
+// kMaxT x kRowCh float4s and the gain slice they share.  With NORM each row is
+// RMS-normalised on the way, x = (h * (1/sqrt(mean(h^2) + eps))) * gamma: the
+// waves' partial sums of squares meet in LDS and are added in wave order.
 // `lo` (optional) receives the remainder x - round(x) for the router's split
 // operand.
-static_assert(kMaxT <= kWaves, "one staged row per wave");
+//
+// issue() only requests the row (and gain) loads; finish() normalises and
+// stores them.  A phase that also streams weights calls issue(), then requests
+// its first weight chunk, then finish(): each wave's loads complete in order,
+// so the activation rows arrive ahead of the weights instead of behind them.
+// Every lane issues the same number of loads (indices past a row are clamped
+// to its last float4, rows past T-1 to row T-1; neither is stored), so the
+// compiler can wait for exactly the older loads.
+constexpr int kRowCh = kMaxModel / (kWaves * 64 * 4);     // float4s per lane per row
+constexpr int kNormLdsOff = kLdsBytes - 640;              // [kWaves][kMaxT] partial sums
+static_assert(kTraceStride * 8 <= 384, "the normalisation partials follow the trace stamps");
 template <class A, bool NORM>
-__device__ __forceinline__ void rows_to_lds(const float* src, int T, int K, A* xs, A* lo, int XS,
-                                            const float* gamma, float eps, char* smem,
-                                            bool tr = false) {
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int n4 = K / 4;
-  (void)smem;
-  if (w < T) {
-    const float* row = src + (long long)w * K;
-    f32x4 v[kStageCh];
-    f32x4 gm[kStageCh];
+struct RowStager {
+  f32x4 v[kMaxT][kRowCh];
+  f32x4 gm[kRowCh];
+  __device__ __forceinline__ void issue(const float* src, int T, int K, const float* gamma) {
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int n4 = K / 4;
 #pragma unroll
-    for (int c = 0; c < kStageCh; ++c) {
-      const int i = lane + 64 * c;
-      if (i < n4) {
-        v[c] = ldg(reinterpret_cast<const f32x4*>(row + 4 * i));
-        if constexpr (NORM) gm[c] = ldg(reinterpret_cast<const f32x4*>(gamma + 4 * i));
-      }
-    }
-    float r = 1.f;
-    if constexpr (NORM) {
-      float ss = 0.f;
+    for (int c = 0; c < kRowCh; ++c) {
+      const int i = min(w * 64 + lane + c * kWaves * 64, n4 - 1);
+      if constexpr (NORM) gm[c] = ldg(reinterpret_cast<const f32x4*>(gamma + 4 * i));
 #pragma unroll
-      for (int c = 0; c < kStageCh; ++c)
-        if (lane + 64 * c < n4) ss += v[c][0] * v[c][0] + v[c][1] * v[c][1] + v[c][2] * v[c][2] + v[c][3] * v[c][3];
-      if (tr && lane == 0 && w == 0) trace_lds()[2 + 2 * kBarriers + 10] = (long long)clock100();
-      ss = wave_sum(ss);
-      r = 1.0f / sqrtf(ss / (float)K + eps);
-      if (tr && lane == 0 && w == 0) trace_lds()[2 + 2 * kBarriers + 11] = (long long)clock100();
-    }
-    A* xr = xs + (long long)w * XS;
-#pragma unroll
-    for (int c = 0; c < kStageCh; ++c) {
-      const int i = lane + 64 * c;
-      if (i < n4) {
-        f32x4 x = v[c];
-        if constexpr (NORM) x = (x * r) * gm[c];
-        store4<A>(xr + 4 * i, x);
-        if (lo) store4<A>(lo + (long long)w * XS + 4 * i, x - round4<A>(x));
-      }
+      for (int t = 0; t < kMaxT; ++t)
+        v[t][c] = ldg(reinterpret_cast<const f32x4*>(src + (long long)min(t, T - 1) * K + 4 * i));
     }
   }
-  __syncthreads();
-}
+  __device__ __forceinline__ void finish(int T, int K, A* xs, A* lo, int XS, float eps, bool tr = false) {
+    extern __shared__ __attribute__((aligned(16))) char dyn_lds[];
+    float* part = reinterpret_cast<float*>(dyn_lds + kNormLdsOff);
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int n4 = K / 4;
+    float r[kMaxT];
+    if constexpr (NORM) {
+      float ss[kMaxT];
+#pragma unroll
+      for (int t = 0; t < kMaxT; ++t) {
+        ss[t] = 0.f;
+#pragma unroll
+        for (int c = 0; c < kRowCh; ++c)
+          if (w * 64 + lane + c * kWaves * 64 < n4)
+            ss[t] += v[t][c][0] * v[t][c][0] + v[t][c][1] * v[t][c][1] + v[t][c][2] * v[t][c][2] +
+                     v[t][c][3] * v[t][c][3];
+      }
+      if (tr && threadIdx.x == 0) trace_lds()[2 + 2 * kBarriers + 11] = (long long)clock100();
+      wave_sums(ss);
+      if (lane == 0) {
+#pragma unroll
+        for (int t = 0; t < kMaxT; ++t) part[w * kMaxT + t] = ss[t];
+      }
+      __syncthreads();
+      if (tr && threadIdx.x == 0) trace_lds()[2 + 2 * kBarriers + 14] = (long long)clock100();
+#pragma unroll
+      for (int t = 0; t < kMaxT; ++t) {
+        float ss = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < kWaves; ++ww) ss += part[ww * kMaxT + t];
+        r[t] = 1.0f / sqrtf(ss / (float)K + eps);
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < kRowCh; ++c) {
+      const int i = w * 64 + lane + c * kWaves * 64;
+      if (i < n4) {
+#pragma unroll
+        for (int t = 0; t < kMaxT; ++t) {
+          if (t < T) {
+            f32x4 x = v[t][c];
+            if constexpr (NORM) x = (x * r[t]) * gm[c];
+            store4<A>(xs + (long long)t * XS + 4 * i, x);
+            if (lo) store4<A>(lo + (long long)t * XS + 4 * i, x - round4<A>(x));
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+};
 
 // Copies T <= kMaxT rows of length K already in the operand type A from global
 // memory into LDS (row stride XS): wave w copies row w in 16-byte pieces.
+// issue() / finish() split as in RowStager.
+template <class A>
+struct RowCopier {
+  static constexpr int EPV = 16 / sizeof(A);                  // elements per 16 bytes
+  static constexpr int CH = kMaxStageK / EPV / 64;
+  u32x4 v[CH];
+  __device__ __forceinline__ void issue(const A* src, int T, int K) {
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int nv = K / EPV;
+    const A* row = src + (long long)min(w, T - 1) * K;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) v[c] = ld16(row + min(lane + 64 * c, nv - 1) * EPV);
+  }
+  __device__ __forceinline__ void finish(int T, int K, A* xs, int XS) {
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int nv = K / EPV;
+    if (w < T) {
+      A* xr = xs + (long long)w * XS;
+#pragma unroll
+      for (int c = 0; c < CH; ++c)
+        if (lane + 64 * c < nv) {
+          const uint2 lo = {v[c][0], v[c][1]}, hi = {v[c][2], v[c][3]};
+          *reinterpret_cast<uint2*>(xr + (lane + 64 * c) * EPV) = lo;
+          *reinterpret_cast<uint2*>(xr + (lane + 64 * c) * EPV + EPV / 2) = hi;
+        }
+    }
+    __syncthreads();
+  }
+};
+
 template <class A>
 __device__ __forceinline__ void rows_copy_lds(const A* src, int T, int K, A* xs, int XS) {
-  constexpr int EPV = 16 / sizeof(A);                  // elements per 16 bytes
-  constexpr int CH = kMaxStageK / EPV / 64;
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int nv = K / EPV;
-  if (w < T) {
-    const A* row = src + (long long)w * K;
-    u32x4 v[CH];
-#pragma unroll
-    for (int c = 0; c < CH; ++c)
-      if (lane + 64 * c < nv) v[c] = ld16(row + (lane + 64 * c) * EPV);
-    A* xr = xs + (long long)w * XS;
-#pragma unroll
-    for (int c = 0; c < CH; ++c)
-      if (lane + 64 * c < nv) {
-        const uint2 lo = {v[c][0], v[c][1]}, hi = {v[c][2], v[c][3]};
-        *reinterpret_cast<uint2*>(xr + (lane + 64 * c) * EPV) = lo;
-        *reinterpret_cast<uint2*>(xr + (lane + 64 * c) * EPV + EPV / 2) = hi;
-      }
-  }
-  __syncthreads();
+  RowCopier<A> c;
+  c.issue(src, T, K);
+  c.finish(T, K, xs, XS);
 }
 
 template <class A>
@@ -208,12 +289,16 @@ __device__ __forceinline__ void phase_qkv(const LayerParams& p, char* smem) {
     }
     part[((long long)s * T + col) * nrow + idx] = v;
   };
-  // the first weight chunk is requested before the input rows are normalised
+  // the input rows are requested first, then the first weight chunk, so the
+  // rows are normalised while the weights are on their way
+  RowStager<A, true> rs;
+  rs.issue(p.H, T, p.d, p.g1);
+  trace_x(p, 10);
   Chunk<AF, false, 16> ck;
   const bool pr = wg_primable(NT, false);
-  if (pr) stream_prime<AF, false, true, 16>(ck, u0, u1, NT, src);
-  rows_to_lds<A, true>(p.H, T, p.d, xs, (A*)nullptr, XS, p.g1, p.eps, smem,
-                       p.trace != nullptr);
+  stream_prime<AF, false, true, 16>(ck, u0, u1, NT, src, p.dummy, pr);
+  trace_x(p, 3);
+  rs.finish(T, p.d, xs, (A*)nullptr, XS, p.eps, p.trace != nullptr);
   trace_x(p, 5);
   stream_units_wg_primed<AF, false, false>(u0, u1, NT, T, src, epi, red, p.dummy, ck, pr);
 }
@@ -738,10 +823,12 @@ __device__ __forceinline__ void phase_wo(const LayerParams& p, char* smem) {
     const long long i = (long long)col * d + u * 16 + row;
     hp[i] = ldg(H + i) + v;
   };
+  RowCopier<A> rc;
+  rc.issue(reinterpret_cast<const A*>(p.o), T, K);
   Chunk<AF, false, 16> ck;
   const bool pr = wg_primable(KT, false);
-  if (pr) stream_prime<AF, false, true, 16>(ck, u0, u1, KT, src);
-  rows_copy_lds<A>(reinterpret_cast<const A*>(p.o), T, K, xs, XS);
+  stream_prime<AF, false, true, 16>(ck, u0, u1, KT, src, p.dummy, pr);
+  rc.finish(T, K, xs, XS);
   trace_x(p, 6);
   stream_units_wg_primed<AF, false, false>(u0, u1, KT, T, src, epi, red, p.dummy, ck, pr);
 }
@@ -983,14 +1070,16 @@ __device__ __forceinline__ void route_load(const LayerParams& p, const RouteLds&
 // for all T rows, W1 and W3 tiles interleaved in the packed expert block.
 // blk[i] is the packed block of slot s0 + i.
 struct NoStage {
-  __device__ void operator()() const {}
+  __device__ void issue() {}
+  __device__ void finish() {}
 };
 // MODE 0: workgroup units [u0, u1); 1: wave units [u0, u1); 2: workgroup units
-// 0 .. u1-1 handed out at run time by the ticket counters.  `stage` runs after
-// the first weight chunk was requested and before it is used (workgroup mode).
+// 0 .. u1-1 handed out at run time by the ticket counters.  `stage` requests
+// the activation operand (issue) before the first weight chunk is requested
+// and stores it (finish) before that chunk is used (workgroup mode).
 template <int EF, int MODE, class Stage = NoStage>
 __device__ __forceinline__ void gateup_units(const LayerParams& p, const uint8_t* const* blk, int s0, int u0, int u1,
-                                             const typename Act<EF>::T* xs, float* red, const Stage& stage = Stage()) {
+                                             const typename Act<EF>::T* xs, float* red, Stage stage = Stage()) {
   typedef typename Act<EF>::T A;
   constexpr int TK = tile_k(EF);
   const int T = p.T, XS = p.d + kXPad;
@@ -1024,16 +1113,19 @@ __device__ __forceinline__ void gateup_units(const LayerParams& p, const uint8_t
     hb[((long long)sl * T + col) * f + rt * 16 + row] = to_act<A>(sg * v2);
   };
   if constexpr (MODE == 2) {
-    stage();
+    stage.issue();
+    stage.finish();
     run_stream_dyn<EF, true, 8>(u1, KT, T, src, epi, red, p.dummy, p.att_cnt + kGateCnt, seq_lds());
   } else if constexpr (MODE == 1) {
-    stage();
+    stage.issue();
+    stage.finish();
     stream_units_wave<EF, true>(u0, u1, KT, T, src, epi, p.dummy);
   } else {
+    stage.issue();
     Chunk<EF, true, 8> ck;
     const bool pr = wg_primable(KT, true);
-    if (pr) stream_prime<EF, true, true, 8>(ck, u0, u1, KT, src);
-    stage();
+    stream_prime<EF, true, true, 8>(ck, u0, u1, KT, src, p.dummy, pr);
+    stage.finish();
     stream_units_wg_primed<EF, true, false>(u0, u1, KT, T, src, epi, red, p.dummy, ck, pr);
   }
 }
@@ -1059,12 +1151,24 @@ __device__ __forceinline__ void phase_router(const LayerParams& p, char* smem) {
     const int nwg = (int)gridDim.x - RT, U = p.nshared * (p.f / 16);
     int u0, u1;
     split_range(U, nwg, (int)blockIdx.x - RT, u0, u1);
-    auto stage = [&]() {
-      rows_to_lds<A, true>(p.hp, T, p.d, xs, (A*)nullptr, XS, p.g2, p.eps, smem);
-      trace_x(p, 7);
-    };
-    if (u1 > u0) gateup_units<EF, 0>(p, p.experts + p.E, 0, u0, u1, xs, reinterpret_cast<float*>(smem + lp.xb), stage);
-    else stage();
+    // RMSNorm-2 of H' into LDS, requested ahead of the first weight chunk
+    struct Stage {
+      const LayerParams& p;
+      A* xs;
+      int XS;
+      RowStager<A, true> rs;
+      __device__ void issue() { rs.issue(p.hp, p.T, p.d, p.g2); }
+      __device__ void finish() {
+        rs.finish(p.T, p.d, xs, (A*)nullptr, XS, p.eps);
+        trace_x(p, 7);
+      }
+    } stage{p, xs, XS};
+    if (u1 > u0) {
+      gateup_units<EF, 0>(p, p.experts + p.E, 0, u0, u1, xs, reinterpret_cast<float*>(smem + lp.xb), stage);
+    } else {
+      stage.issue();
+      stage.finish();
+    }
     return;
   }
   A* xlo = AF == MK_FMT_F32 ? (A*)nullptr : reinterpret_cast<A*>(smem + lp.xb);
@@ -1087,10 +1191,12 @@ __device__ __forceinline__ void phase_router(const LayerParams& p, char* smem) {
   } src{p.wr, KT, bl, (long long)(lp.xb / (int)sizeof(A))};
   float* lgl = reinterpret_cast<float*>(smem + 2 * lp.xb + 2 * kWaves * 64 * 4 * 4);   // [4][kMaxT][16]
   auto epi = [=](int u, int row, int col, float v, float) { lgl[((u - u0) * kMaxT + col) * 16 + row] = v; };
+  RowStager<A, true> rs;
+  rs.issue(p.hp, T, p.d, p.g2);
   Chunk<AF, false, 16> ck;
   const bool pr = wg_primable(KT, false);
-  if (pr) stream_prime<AF, false, true, 16>(ck, u0, u1, KT, src);
-  rows_to_lds<A, true>(p.hp, T, p.d, xs, xlo, XS, p.g2, p.eps, smem);
+  stream_prime<AF, false, true, 16>(ck, u0, u1, KT, src, p.dummy, pr);
+  rs.finish(T, p.d, xs, xlo, XS, p.eps);
   trace_x(p, 7);
   stream_units_wg_primed<AF, false, AF != MK_FMT_F32>(u0, u1, KT, T, src, epi, red, p.dummy, ck, pr);
   if (u1 <= u0) return;
@@ -1229,8 +1335,30 @@ __device__ __forceinline__ void phase_combine(const LayerParams& p, char* smem, 
 }
 
 // ------------------------------------------------------------------ the kernel
-template <int AF, int EF, int KF, int KBMAX, int DBMAX, bool EXACT>
+// Layer shapes with an instance of their own, where every dimension is a
+// compile-time constant: address arithmetic folds, the ragged-shape engines
+// drop out, and fewer values stay live across phases.
+struct SpecShape {
+  int d, nh, dh, dc, dr, E, topk, nshared, f;
+};
+constexpr SpecShape kSpecShapes[] = {
+    {0, 0, 0, 0, 0, 0, 0, 0, 0},                 // 0: dimensions read from the parameters
+    {4096, 32, 128, 512, 64, 128, 8, 1, 1024},   // 1: 128 experts of width 1024
+    {4096, 32, 128, 512, 64, 384, 8, 1, 2048},   // 2: 384 experts of width 2048
+};
+template <int SPEC>
+__device__ __forceinline__ void specialise(LayerParams& p) {
+  if constexpr (SPEC > 0) {
+    constexpr SpecShape s = kSpecShapes[SPEC];
+    p.d = s.d; p.nh = s.nh; p.dh = s.dh; p.dc = s.dc; p.dr = s.dr;
+    p.qw = s.dh + s.dr; p.kvw = s.dc + s.dr; p.nq = s.nh * (s.dh + s.dr);
+    p.E = s.E; p.topk = s.topk; p.nshared = s.nshared; p.f = s.f;
+  }
+}
+
+template <int AF, int EF, int KF, int KBMAX, int DBMAX, bool EXACT, int SPEC>
 __global__ __launch_bounds__(kThreads, 1) void layer_kernel(LayerParams p) {
+  specialise<SPEC>(p);
   extern __shared__ __attribute__((aligned(16))) char smem[];
   int* flag = reinterpret_cast<int*>(smem + kFlagOff);
   const int L = p.L_dev ? ldg(p.L_dev) : p.L;
@@ -1292,19 +1420,26 @@ __global__ __launch_bounds__(kThreads, 1) void layer_kernel(LayerParams p) {
 
 // Instantiations: all-fp32 (d_latent + d_rope <= 160, d_latent <= 128),
 // bf16 attention with bf16 or fp8 experts (d_latent + d_rope <= 576, d_latent <= 512),
-// the latter also specialised for exactly 512 + 64 latent dims.
+// and the two fixed shapes of kSpecShapes (512 + 64 latent dims, so the
+// attention loop bounds are constants too).
 typedef void (*LayerKernelFn)(LayerParams);
-LayerKernelFn layer_kernel_for(int af, int ef, int kf, int kvw, int dc) {
+LayerKernelFn layer_kernel_for(int af, int ef, int kf, int d, int nh, int dh, int dc, int dr, int E, int topk,
+                               int nshared, int f) {
+  const int kvw = dc + dr;
+  auto is = [&](int i) {
+    const SpecShape& s = kSpecShapes[i];
+    return d == s.d && nh == s.nh && dh == s.dh && dc == s.dc && dr == s.dr && E == s.E && topk == s.topk &&
+           nshared == s.nshared && f == s.f;
+  };
   if (af == MK_FMT_F32 && ef == MK_FMT_F32 && kf == MK_FMT_F32 && kvw <= 160 && dc <= 128)
-    return layer_kernel<MK_FMT_F32, MK_FMT_F32, MK_FMT_F32, 10, 8, false>;
+    return layer_kernel<MK_FMT_F32, MK_FMT_F32, MK_FMT_F32, 10, 8, false, 0>;
   if (af == MK_FMT_BF16 && kf == MK_FMT_BF16 && kvw <= 576 && dc <= 512) {
-    const bool exact = kvw == 576 && dc == 512;
     if (ef == MK_FMT_BF16)
-      return exact ? layer_kernel<MK_FMT_BF16, MK_FMT_BF16, MK_FMT_BF16, 18, 32, true>
-                   : layer_kernel<MK_FMT_BF16, MK_FMT_BF16, MK_FMT_BF16, 18, 32, false>;
+      return is(1) ? layer_kernel<MK_FMT_BF16, MK_FMT_BF16, MK_FMT_BF16, 18, 32, true, 1>
+                   : layer_kernel<MK_FMT_BF16, MK_FMT_BF16, MK_FMT_BF16, 18, 32, false, 0>;
     if (ef == MK_FMT_FP8_B128)
-      return exact ? layer_kernel<MK_FMT_BF16, MK_FMT_FP8_B128, MK_FMT_BF16, 18, 32, true>
-                   : layer_kernel<MK_FMT_BF16, MK_FMT_FP8_B128, MK_FMT_BF16, 18, 32, false>;
+      return is(2) ? layer_kernel<MK_FMT_BF16, MK_FMT_FP8_B128, MK_FMT_BF16, 18, 32, true, 2>
+                   : layer_kernel<MK_FMT_BF16, MK_FMT_FP8_B128, MK_FMT_BF16, 18, 32, false, 0>;
   }
   return nullptr;
 }

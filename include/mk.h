@@ -76,7 +76,7 @@ typedef enum mk_format { MK_FMT_F32 = 0, MK_FMT_BF16 = 1, MK_FMT_FP8_B128 = 2 } 
  * expert_format to W1, W3, W2 (F32, BF16 or FP8_B128); kv_format to the cache.
  * Supported shapes: d_model, d_ff multiples of 128; d_head, d_latent multiples
  * of 32, d_head <= 128, n_heads <= 128; d_rope a multiple of 32; n_experts a multiple of 16 and <= 1024;
- * top_k <= 16; d_model, n_heads*d_head and d_ff <= 4608.
+ * top_k <= 16; d_model <= 4096; n_heads*d_head and d_ff <= 4608.
  * Formats must be all F32, or attention/KV BF16 with experts BF16 or FP8_B128. */
 typedef struct mk_layer_config {
   int32_t abi_version;       /* must be MK_ABI_VERSION */
