@@ -220,7 +220,7 @@ StLayout st_layout(const Dims& D, const Schedule& s) {
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
   l.bar = take(sizeof(BarrierState));
-  l.att_cnt = take((kGateCnt + 8 * kCntStride) * 4);
+  l.att_cnt = take(kCntWords * 4);
   l.experts = take((size_t)(D.E + D.nshared) * 8);
   l.trace = take((size_t)s.nwg * kTraceStride * 8);
   l.total = off;

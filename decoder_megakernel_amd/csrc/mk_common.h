@@ -11,7 +11,7 @@ constexpr int kThreads = 512;            // threads per workgroup (8 wave64s)
 constexpr int kWaves = kThreads / 64;
 constexpr int kMaxT = MK_MAX_T;          // verify rows the LDS budget is sized for
 constexpr int kXPad = 8;                 // LDS row padding of activation operands (elements)
-constexpr int kBarriers = 9;             // grid barriers in one layer launch
+constexpr int kBarriers = 8;             // grid barriers in one layer launch
 constexpr int kTraceX = 16;              // extra per-workgroup timestamps (sub-phase marks)
 constexpr int kTraceStride = 2 + 2 * kBarriers + kTraceX;
 constexpr int kLdsBytes = 160 * 1024 - 256;
@@ -20,6 +20,8 @@ constexpr int kRouteCnt = 64;            // index of the router-completion count
 constexpr int kGateCnt = 128;            // index of the first of 8 gate/up ticket counters in att_cnt,
 constexpr int kCntStride = 64;           // which sit 256 bytes apart (device-scope atomics on one
                                          // line are serialised where they are performed)
+constexpr int kDownCnt = kGateCnt + 8 * kCntStride;   // the 8 down-projection ticket counters
+constexpr int kCntWords = kDownCnt + 8 * kCntStride;  // words of the counter area
 constexpr int kMaxExperts = 1024;        // routed experts per layer (16 logits per lane)
 constexpr int kStageCh = 18;             // float4s per lane when staging one activation row
 constexpr int kMaxStageK = kStageCh * 64 * 4;   // longest activation row (elements)
@@ -40,6 +42,7 @@ __host__ __device__ constexpr int elem_bytes(int fmt) { return fmt == MK_FMT_F32
 // group size), so nothing is reset between barriers or launches.
 constexpr int kBarGroup = 16;
 constexpr int kMaxBarGroups = 64;        // grids of up to 1024 workgroups
+constexpr int kMaxGrid = kBarGroup * kMaxBarGroups;
 struct alignas(256) BarrierLine {
   unsigned long long n;
   uint32_t pad[62];

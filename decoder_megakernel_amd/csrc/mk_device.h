@@ -73,9 +73,14 @@ __device__ __forceinline__ f32x4 fp8x4_to_f32(uint32_t w) {
   f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
   return f32x4{lo[0], lo[1], hi[0], hi[1]};
 }
-// eight codes -> eight bf16 (exact: every E4M3 value is a bf16 value)
+// eight codes -> eight bf16 (exact: every E4M3 value is a bf16 value, and the
+// scale is 1), two codes per instruction
 __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
-  return to_bf16x8(fp8x4_to_f32(w0), fp8x4_to_f32(w1));
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
+  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
 // ------------------------------------------------------------------ MFMA

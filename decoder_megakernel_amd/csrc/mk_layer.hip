@@ -8,8 +8,8 @@
 //   P0  RMSNorm-1 (every workgroup, into LDS) ; [W_Q; W_DKV] x, split-K partials
 //   P1  RoPE on q^R and the shared key, KV insert ; absorbed query q~ = W_UK^T q^C
 //   P2  latent attention, split over (query tile, KV range): partial (Z, max, sum)
-//   P3a merge of the KV splits (log-sum-exp) into z
-//   P3b o = W_UV z
+//   P3  merge of the KV splits (log-sum-exp) into z and o = W_UV z, per
+//       (head, pair of verify rows)
 //   P4  H' = H + W_O o
 //   P5  RMSNorm-2 (every workgroup, into LDS) ; router logits on E/16
 //       workgroups, the shared experts' gate+up on the others; the last router
@@ -606,9 +606,11 @@ __device__ __forceinline__ void phase_attention(const LayerParams& p, int L, cha
     // of the four in a fixed order and writes them out.
     __syncthreads();
     trace_x(p, 1);
-    // Partial state layout (LDS and global): block db of the latent holds, per
-    // lane, the 4 values acc[db] (MFMA result layout: lane (g, j) has dims
-    // 16 db + 4 g + e of query j), so every access is one 16-byte vector.
+    // Partial state layout in LDS: block db of the latent holds, per lane, the
+    // 4 values acc[db] (MFMA result layout: lane (g, j) has dims 16 db + 4 g + e
+    // of query j), so every access is one 16-byte vector.  In global memory the
+    // partial is query-major ([16 queries][d_latent]), so that the merge reads
+    // one query's latent as contiguous memory.
     f32x4* mb = reinterpret_cast<f32x4*>(smem);                 // [4][DB][64]
     float* ml = reinterpret_cast<float*>(smem) + 4 * DB * 64 * 4;   // [8][64][2]
     ml[(w * 64 + lane) * 2] = m_run;
@@ -654,7 +656,7 @@ __device__ __forceinline__ void phase_attention(const LayerParams& p, int L, cha
 #pragma unroll
       for (int i = 0; i < NBW; ++i) {
         const int db = w + kWaves * i;
-        if (db < DB) zp[db * 64 + lane] = (t[i][0] + t[i][1]) + (t[i][2] + t[i][3]);
+        if (db < DB) zp[j * (dc / 4) + db * 4 + g] = (t[i][0] + t[i][1]) + (t[i][2] + t[i][3]);
       }
     }
     if (w == 0 && g == 0) {
@@ -671,127 +673,115 @@ __device__ __forceinline__ void phase_attention(const LayerParams& p, int L, cha
   }
 }
 
-// ------------------------------------------------------------------ P3a  merge of the KV splits
-// Unit (query tile qt, split s) as in P2: it merges 1/s_kv of the tile's latent
-// items (item i = (16-dim block i / 64, lane i % 64) of the partial layout)
-// over all splits, with weights exp(m_s - M) / sum_s exp(m_s - M) l_s, into z.
-// Four threads share an item, each summing every fourth split.
-__device__ __forceinline__ void phase_merge(const LayerParams& p, int L, char* smem) {
-  const int T = p.T, nh = p.nh, dc = p.dc;
+// ------------------------------------------------------------------ P3  split merge and o = W_UV z
+// One unit = (head h, a group of up to kMergeRows verify rows).  Wave w
+// requests row tile w of W_UV^(h) first; then two threads per latent item
+// (row ti, float4 r4 of the latent) each load the (max, sum) and the partial
+// of half of the KV splits in one round trip and merge them with their own
+// running maximum; the halves are combined through LDS into
+// z = sum_s exp(m_s - M) Z_s / sum_s exp(m_s - M) l_s, kept in LDS as the
+// matrix-core operand (and written to the z buffer); finally wave w multiplies
+// its row tile.  Only the queries of its own unit are merged, so no partial is
+// read twice and no grid barrier separates the merge from the up-projection.
+constexpr int kMergeRows = 2;
+constexpr int kMergeSB = 12;                      // splits per thread per batch
+constexpr int kMergeXOff = 8192;                  // LDS: half-merge exchange after the z operand
+template <int AF>
+__device__ __forceinline__ void phase_merge_uv(const LayerParams& p, int L, char* smem) {
+  typedef typename Act<AF>::T A;
+  constexpr int TK = tile_k(AF);
+  constexpr int KTMAX = 16;                       // d_latent / tile_k <= 16 for every supported shape
+  const int T = p.T, nh = p.nh, dc = p.dc, dh = p.dh;
   const int NQ = T * nh, NQT = (NQ + 15) / 16;
   int s_kv, SK;
   attn_splits(NQT, L + T, s_kv, SK);
-  const int units = NQT * s_kv, DB = dc / 16;
-  float* mm = reinterpret_cast<float*>(smem);          // [s_kv][16] running max, then weight
-  float* cf = mm + s_kv * 16;                          // [s_kv][16] running sum
-  float* red = cf + s_kv * 16;                         // [4][128][4] partial sums of the 4 thread groups
-  for (int u = blockIdx.x; u < units; u += gridDim.x) {
-    const int qt = u / s_kv, s = u - qt * s_kv;
-    const int ub = qt * s_kv;
-    for (int i = threadIdx.x; i < s_kv * 16; i += kThreads) {
-      mm[i] = ldg(p.att_ml + ((long long)ub * 16 + i) * 2);
-      cf[i] = ldg(p.att_ml + ((long long)ub * 16 + i) * 2 + 1);
-    }
-    __syncthreads();
-    if (threadIdx.x < 16) {
-      const int jq = threadIdx.x;
-      float M = -INFINITY;
-      for (int ss = 0; ss < s_kv; ++ss) M = fmaxf(M, mm[ss * 16 + jq]);
-      float den = 0.f;
-      for (int ss = 0; ss < s_kv; ++ss) {
-        const float wgt = mm[ss * 16 + jq] == -INFINITY ? 0.f : __expf(mm[ss * 16 + jq] - M);
-        mm[ss * 16 + jq] = wgt;
-        den += wgt * cf[ss * 16 + jq];
-      }
-      for (int ss = 0; ss < s_kv; ++ss) mm[ss * 16 + jq] /= den;
-    }
-    __syncthreads();
-    int i0, i1;
-    split_range(DB * 64, s_kv, s, i0, i1);
-    const f32x4* zb = reinterpret_cast<const f32x4*>(p.att_part + (long long)ub * 16 * dc);
-    const long long sstride = 16LL * dc / 4;
-    const int quarter = threadIdx.x >> 7, slot = threadIdx.x & 127;
-    for (int base = i0; base < i1; base += 128) {
-      const int it = base + slot;
-      const bool ok = it < i1;
-      const int ln = it & 63, jq = ln & 15;
-      f32x4 a0 = {0.f, 0.f, 0.f, 0.f};
-      if (ok) {
-        const f32x4* zp = zb + it;
-        int ss = quarter;
-        for (; ss + 12 < s_kv; ss += 16) {
-          f32x4 zz[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) zz[i] = ldg(zp + (ss + 4 * i) * sstride);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) a0 += zz[i] * mm[(ss + 4 * i) * 16 + jq];
-        }
-        for (; ss < s_kv; ss += 4) a0 += ldg(zp + ss * sstride) * mm[ss * 16 + jq];
-      }
-      *reinterpret_cast<f32x4*>(red + (quarter * 128 + slot) * 4) = a0;
-      __syncthreads();
-      if (threadIdx.x < 128 && ok) {
-        f32x4 v = *reinterpret_cast<const f32x4*>(red + slot * 4);
-#pragma unroll
-        for (int q4 = 1; q4 < 4; ++q4) v += *reinterpret_cast<const f32x4*>(red + (q4 * 128 + slot) * 4);
-        const int db = it >> 6, gq = ln >> 4;
-        const int qq = qt * 16 + jq;
-        if (qq < NQ) *reinterpret_cast<f32x4*>(p.z + (long long)qq * dc + db * 16 + gq * 4) = v;
-      }
-      __syncthreads();
-    }
-  }
-}
-
-// ------------------------------------------------------------------ P3b  o = W_UV z
-// One unit (head h, 16 rows of d_head, all d_latent columns) per workgroup at a
-// time; the 8 waves split the unit's tiles, load their tiles and z slices in
-// one round trip, and the partial blocks are summed in LDS in wave order.
-template <int AF>
-__device__ __forceinline__ void phase_uv(const LayerParams& p, char* smem) {
-  constexpr int TK = tile_k(AF);
-  constexpr int EPL = TK / 4;
-  constexpr int CMAX = 2;              // tiles per wave: d_latent / tile_k <= 16
-  const int T = p.T;
+  const int TG = (T + kMergeRows - 1) / kMergeRows;
+  const int U = nh * TG, XS = dc + kXPad, RT = dh / 16, KT = dc / TK, D4 = dc / 4;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, j = lane & 15, g = lane >> 4;
-  const int jj = j < T ? j : T - 1;
-  const int RT = p.dh / 16, KT = p.dc / TK, U = p.nh * RT;
-  const int c = (KT + kWaves - 1) / kWaves;
-  float* red = reinterpret_cast<float*>(smem);      // [kWaves][64][4]
+  A* zs = reinterpret_cast<A*>(smem);                                  // [kMergeRows][XS]
+  float* xch = reinterpret_cast<float*>(smem + kMergeXOff);            // [256 items][8]: M, L, Z
+  const f32x4* part = reinterpret_cast<const f32x4*>(p.att_part);
+  const f32x2* mlp = reinterpret_cast<const f32x2*>(p.att_ml);
   for (int u = blockIdx.x; u < U; u += gridDim.x) {
-    const int h = u / RT, rt = u - h * RT;
-    const uint8_t* tiles = p.wuv + (long long)u * KT * 1024 + lane * 16;
-    const float* zr = p.z + ((long long)jj * p.nh + h) * p.dc + g * EPL;
-    u32x4 at[CMAX];
-    typename BReg<AF>::T bt[CMAX];
+    const int h = u / TG, tg = u - h * TG;
+    const int t0 = tg * kMergeRows, nt = min(kMergeRows, T - t0);
+    // (1) this wave's W_UV row tile (waves past the last row tile load it again)
+    u32x4 wt[KTMAX];
+    {
+      const uint8_t* tb = p.wuv + ((long long)(h * RT + min(w, RT - 1)) * KT) * 1024 + lane * 16;
 #pragma unroll
-    for (int i = 0; i < CMAX; ++i) {
-      const int kt = w * c + i;
-      if (i < c && kt < KT) {
-        at[i] = ld_stream16(tiles + kt * 1024);
-        bt[i] = load_b<AF>(zr + kt * TK);
+      for (int kt = 0; kt < KTMAX; ++kt) wt[kt] = ld_stream16(tb + (long long)min(kt, KT - 1) * 1024);
+    }
+    // (2) half merges: item it = (ti, r4), half hf takes splits hf, hf + 2, ...
+    const int it = min((int)threadIdx.x & 255, nt * D4 - 1), hf = threadIdx.x >> 8;
+    const int ti = it / D4, r4 = it - ti * D4;
+    const int q = (t0 + ti) * nh + h, qt = q >> 4, jq = q & 15;
+    const f32x4* zp = part + (long long)qt * s_kv * 4 * dc + jq * D4 + r4;
+    const f32x2* mp = mlp + (long long)qt * s_kv * 16 + jq;
+    float Mh = -INFINITY, Lh = 0.f;
+    f32x4 Zh = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = hf; s0 < s_kv; s0 += 2 * kMergeSB) {
+      f32x2 ml[kMergeSB];
+      f32x4 zz[kMergeSB];
+#pragma unroll
+      for (int b = 0; b < kMergeSB; ++b) {
+        const int sp = min(s0 + 2 * b, s_kv - 1);
+        ml[b] = ldg(mp + (long long)sp * 16);
+        zz[b] = ldg(zp + (long long)sp * 4 * dc);
+      }
+      float Mb = Mh;
+#pragma unroll
+      for (int b = 0; b < kMergeSB; ++b)
+        if (s0 + 2 * b < s_kv) Mb = fmaxf(Mb, ml[b][0]);
+      if (Mb != -INFINITY) {
+        const float sc = Mh == -INFINITY ? 0.f : __expf(Mh - Mb);
+        Lh *= sc;
+        Zh *= sc;
+#pragma unroll
+        for (int b = 0; b < kMergeSB; ++b) {
+          if (s0 + 2 * b < s_kv && ml[b][0] != -INFINITY) {
+            const float e = __expf(ml[b][0] - Mb);
+            Lh += e * ml[b][1];
+            Zh += zz[b] * e;
+          }
+        }
+        Mh = Mb;
       }
     }
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int i = 0; i < CMAX; ++i) {
-      const int kt = w * c + i;
-      if (i < c && kt < KT) acc = tile_mma_reg<AF>(at[i], bt[i], acc);
+    __syncthreads();                              // LDS reuse across units
+    if (hf == 1) {
+      float* x = xch + (threadIdx.x & 255) * 8;
+      x[0] = Mh;
+      x[1] = Lh;
+      *reinterpret_cast<f32x4*>(x + 4) = Zh;
     }
-    *reinterpret_cast<f32x4*>(red + (w * 64 + lane) * 4) = acc;
     __syncthreads();
-    if (threadIdx.x < 256) {
-      const int col = threadIdx.x & 15, row = threadIdx.x >> 4;
-      const int l = (row >> 2) * 16 + col, e = row & 3;
-      if (col < T) {
-        float v = 0.f;
+    if (hf == 0 && (int)threadIdx.x < nt * D4) {
+      const float* x = xch + threadIdx.x * 8;
+      const float M1 = x[0], L1 = x[1];
+      const f32x4 Z1 = *reinterpret_cast<const f32x4*>(x + 4);
+      const float M = fmaxf(Mh, M1);
+      const float a0 = Mh == -INFINITY ? 0.f : __expf(Mh - M), a1 = M1 == -INFINITY ? 0.f : __expf(M1 - M);
+      const f32x4 zv = (Zh * a0 + Z1 * a1) / (a0 * Lh + a1 * L1);
+      store4<A>(zs + ti * XS + 4 * r4, zv);
+      *reinterpret_cast<f32x4*>(p.z + (long long)q * dc + 4 * r4) = zv;
+    }
+    __syncthreads();
+    // (3) o rows of head h for the group: wave w multiplies row tile w
+    if (w < RT) {
+      const int jj = j < nt ? j : nt - 1;
+      const A* bp = zs + jj * XS + g * (TK / 4);
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ww = 0; ww < kWaves; ++ww) v += red[(ww * 64 + l) * 4 + e];
-        reinterpret_cast<typename Act<AF>::T*>(p.o)[(long long)col * p.nh * p.dh + h * p.dh + rt * 16 + row] =
-            to_act<typename Act<AF>::T>(v);
+      for (int kt = 0; kt < KTMAX; ++kt)
+        if (kt < KT) acc = tile_mma<AF>(wt[kt], bp + kt * TK, acc);
+      if (j < nt) {
+        A* o = reinterpret_cast<A*>(p.o);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          o[(long long)(t0 + j) * nh * dh + h * dh + w * 16 + 4 * g + e] = to_act<A>(acc[e]);
       }
     }
-    __syncthreads();
   }
 }
 
@@ -1245,6 +1235,186 @@ __device__ __forceinline__ void phase_route_gateup(const LayerParams& p, char* s
     gateup_units<EF, 0>(p, r.blk + s0, s0, u0, u1, xs, red);
 }
 
+// ------------------------------------------------------------------ P7 down projections (ticket-fed)
+// Unit u = (slot u / QP, row tiles 4 (u % QP) .. 4 (u % QP) + 3 of d_model),
+// QP = d_model / 64: four row tiles times all KT tiles of W2.  Wave w streams
+// row tile 4 (u % QP) + (w & 3) over K half w >> 2 (KT / 2 tiles in chunks of
+// D, the next chunk requested while the current one is multiplied, across unit
+// boundaries), and waves w and w + 4 add their blocks in LDS.  Units are handed
+// out as in run_stream_dyn: workgroup b takes units b and b + nwg, then draws
+// tickets, so workgroups on faster XCDs take more units.  The rows of a unit's
+// slot (h, T x d_ff in the operand type) sit in one of two LDS buffers; those of
+// the next unit's slot are requested when a unit starts and stored into the
+// other buffer once its chunks have been multiplied, so a change of slot costs
+// no extra round trip.
+__host__ __device__ constexpr bool down_dyn_fits(int d, int f, int tk, int es, int xb) {
+  return d % 64 == 0 && (f / tk) % 32 == 0 && 2 * kMaxT * (f + kXPad) * es <= xb;
+}
+
+template <int EF>
+__device__ __forceinline__ void phase_down_dyn(const LayerParams& p, char* smem, int xb, const RouteLds& r) {
+  typedef typename Act<EF>::T A;
+  constexpr int TK = tile_k(EF);
+  constexpr int D = 16;
+  constexpr int EPV = 16 / sizeof(A);                      // elements per 16 bytes
+  constexpr int HCH = (kMaxT * kMaxStageK / EPV + kThreads - 1) / kThreads;
+  const int T = p.T, f = p.f, d = p.d, HS = f + kXPad;
+  const int hch = (kMaxT * f / EPV + kThreads - 1) / kThreads;   // 16-byte pieces per thread (<= HCH)
+  const int ns = *r.nslots;
+  const int QP = d / 64, KT = f / TK, NTh = KT / 2, cps = NTh / D;
+  const int U = ns * QP;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int sub = w & 3, kp = w >> 2;
+  const int nwg = (int)gridDim.x;
+  const int nbk = (f + 127) / 128;
+  const long long w2_off = p.exp_w13_bytes;
+  const long long sc2_off = p.exp_w13_bytes + p.exp_w2_bytes +
+                            2LL * ((p.f + 127) / 128) * ((p.d + 127) / 128) * 4;
+  // the two row buffers: hls + 0 and hls + hsz (offsets rather than an array of
+  // pointers, so that every access stays an LDS access and never becomes FLAT)
+  A* const hls = reinterpret_cast<A*>(smem);
+  const int hsz = kMaxT * HS;
+  float* red = reinterpret_cast<float*>(smem + xb);        // [2][8 waves][64][4]
+  uint32_t* ctr = p.att_cnt + kDownCnt;
+  int* seq = seq_lds();
+  const float* dsc = reinterpret_cast<const float*>(p.dummy);
+  int cur = (int)blockIdx.x < U ? (int)blockIdx.x : -1;
+  int nxt = (int)blockIdx.x + nwg < U ? (int)blockIdx.x + nwg : -1;
+  if (cur < 0 || cps <= 0) return;
+  const int n16 = T * f / EPV;                              // 16-byte pieces of one slot's rows
+  const int p16 = f / EPV;                                  // ... of one row
+  auto h_src = [&](int sl, int c) {
+    const int i = min((int)threadIdx.x + kThreads * c, n16 - 1);
+    return reinterpret_cast<const A*>(p.hbuf) + (long long)sl * T * f + (long long)i * EPV;
+  };
+  auto h_dst = [&](A* buf, int c, A*& dst) {
+    const int i = (int)threadIdx.x + kThreads * c;
+    if (i >= n16) return false;
+    const int t = i / p16, k0 = (i - t * p16) * EPV;
+    dst = buf + (long long)t * HS + k0;
+    return true;
+  };
+  auto h_store = [&](A* buf, const u32x4* hv) {
+#pragma unroll
+    for (int c = 0; c < HCH; ++c) {
+      A* dst;
+      if (c < hch && h_dst(buf, c, dst)) {
+        *reinterpret_cast<uint2*>(dst) = uint2{hv[c][0], hv[c][1]};
+        *reinterpret_cast<uint2*>(dst + EPV / 2) = uint2{hv[c][2], hv[c][3]};
+      }
+    }
+  };
+  auto wbase = [&](int u) {
+    const int sl = u / QP, rt = 4 * (u - sl * QP) + sub;
+    return r.blk[sl] + w2_off + (long long)rt * KT * 1024 + lane * 16 + (long long)kp * NTh * 1024;
+  };
+  auto sbase = [&](int u) {
+    const int sl = u / QP, rt = 4 * (u - sl * QP) + sub;
+    return reinterpret_cast<const float*>(r.blk[sl] + sc2_off) + (rt >> 3) * nbk;
+  };
+  // the first unit's rows, staged synchronously
+  int hb = 0;
+  {
+    u32x4 hv[HCH];
+#pragma unroll
+    for (int c = 0; c < HCH; ++c)
+      if (c < hch) hv[c] = ld16(h_src(cur / QP, c));
+    h_store(hls, hv);
+  }
+  __syncthreads();
+  u32x4 buf[D];
+  float sc[D];
+  {
+    const uint8_t* cb = wbase(cur);
+    const float* sp = EF == MK_FMT_FP8_B128 ? sbase(cur) : dsc;
+#pragma unroll
+    for (int rr = 0; rr < D; ++rr) {
+      buf[rr] = ld_stream16(cb + rr * 1024);
+      if constexpr (EF == MK_FMT_FP8_B128) sc[rr] = ldg(sp + (((kp * NTh + rr) * TK) >> 7));
+    }
+  }
+  uint32_t tk = 0;
+  int cq = (int)blockIdx.x & 7;
+  int cc = 0, par = 0;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  const int j = lane & 15, g = lane >> 4, jj = j < T ? j : T - 1;
+  u32x4 hv[HCH];
+  bool hnext = false;
+  float* yb = p.ybuf;
+  while (true) {
+    if (cc == 0) {
+      if (threadIdx.x == 0)
+        tk = __hip_atomic_fetch_add(ctr + kCntStride * cq, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      // the next unit's rows, stored only when its slot differs; requested
+      // either way (the current slot's rows, then) so that the number of loads
+      // in flight does not depend on a branch
+      hnext = nxt >= 0 && nxt / QP != cur / QP;
+      const int hsl = hnext ? nxt / QP : cur / QP;
+#pragma unroll
+      for (int c = 0; c < HCH; ++c)
+        if (c < hch) hv[c] = ld16(h_src(hsl, c));
+    }
+    int ncc = cc + 1, un = cur;
+    if (ncc == cps) {
+      ncc = 0;
+      un = nxt;
+    }
+    const bool has_next = un >= 0;
+    const uint8_t* nb = has_next ? wbase(un) + (long long)ncc * D * 1024 : p.dummy + lane * 16;
+    const float* nsp = dsc;
+    if constexpr (EF == MK_FMT_FP8_B128) {
+      if (has_next) nsp = sbase(un);
+    }
+    const A* bp = hls + hb * hsz + jj * HS + g * (TK / 4) + (kp * NTh + cc * D) * TK;
+#pragma unroll
+    for (int rr = 0; rr < D; ++rr) {
+      if constexpr (EF == MK_FMT_FP8_B128) {
+        const f32x4 tmp = tile_mma<EF>(buf[rr], bp + rr * TK, zero);
+        acc += tmp * sc[rr];
+      } else {
+        acc = tile_mma<EF>(buf[rr], bp + rr * TK, acc);
+      }
+      buf[rr] = ld_stream16(nb + rr * 1024);
+      if constexpr (EF == MK_FMT_FP8_B128)
+        sc[rr] = ldg(nsp + (has_next ? (((kp * NTh + ncc * D + rr) * TK) >> 7) : 0));
+    }
+    cc = ncc;
+    if (ncc != 0) continue;
+    // unit `cur` complete: the next slot's rows into the other buffer, the
+    // blocks of waves w and w + 4 added, the unit after nxt published
+    if (hnext) h_store(hls + (hb ^ 1) * hsz, hv);
+    float* rb = red + par * (kWaves * 64 * 4);
+    *reinterpret_cast<f32x4*>(rb + (w * 64 + lane) * 4) = acc;
+    if (threadIdx.x == 0) {
+      long long un2 = 2LL * nwg + 8LL * tk + cq;
+      for (int tries = 1; un2 >= U && tries < 8; ++tries) {
+        cq = (cq + 1) & 7;
+        tk = __hip_atomic_fetch_add(ctr + kCntStride * cq, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        un2 = 2LL * nwg + 8LL * tk + cq;
+      }
+      seq[par] = un2 < U ? (int)un2 : -1;
+    }
+    __syncthreads();
+    {
+      const int s4 = threadIdx.x >> 7, rem = threadIdx.x & 127, row = rem >> 3, col = rem & 7;
+      if (col < T) {
+        const int l = (row >> 2) * 16 + col, e = row & 3;
+        const float v = rb[(s4 * 64 + l) * 4 + e] + rb[((s4 + 4) * 64 + l) * 4 + e];
+        const int sl = cur / QP, rt = 4 * (cur - sl * QP) + s4;
+        yb[((long long)sl * T + col) * d + rt * 16 + row] = v;
+      }
+    }
+    acc = zero;
+    if (hnext) hb ^= 1;
+    cur = nxt;
+    nxt = nxt >= 0 ? seq[par] : -1;
+    par ^= 1;
+    if (cur < 0) break;
+  }
+  __syncthreads();
+}
+
 // ------------------------------------------------------------------ P7 down projections
 template <int EF>
 __device__ __forceinline__ void phase_down(const LayerParams& p, char* smem) {
@@ -1290,6 +1460,10 @@ __device__ __forceinline__ void phase_down(const LayerParams& p, char* smem) {
     const int sl = uu / RT, rt = uu - sl * RT;
     yb[((long long)sl * T + col) * d + rt * 16 + row] = v;
   };
+  if (down_dyn_fits(p.d, p.f, TK, (int)sizeof(A), lp.xb)) {
+    phase_down_dyn<EF>(p, smem, lp.xb, r);
+    return;
+  }
   if (U >= 2 * (int)gridDim.x * kWaves) {
     // wave-level units; stage up to two slots' activations at a time
     const long long slot_elems = (long long)kMaxT * XS;
@@ -1376,9 +1550,9 @@ __global__ __launch_bounds__(kThreads, 1) void layer_kernel(LayerParams p) {
   // attention split counters: cleared here, used after two grid barriers
   if (blockIdx.x == 0 && threadIdx.x <= kRouteCnt)
     __hip_atomic_store(&p.att_cnt[threadIdx.x], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if (blockIdx.x == 0 && threadIdx.x < 8)
+  if (blockIdx.x == 0 && threadIdx.x < 16)
     __hip_atomic_store(&p.att_cnt[kGateCnt + kCntStride * threadIdx.x], 0u, __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
+                       __HIP_MEMORY_SCOPE_AGENT);   // gate/up and down ticket counters
   phase_qkv<AF>(p, smem);
   if (!grid_barrier(p, 0, flag)) return;
   {
@@ -1397,18 +1571,16 @@ __global__ __launch_bounds__(kThreads, 1) void layer_kernel(LayerParams p) {
   if (!grid_barrier(p, 1, flag)) return;
   phase_attention<KF, KBMAX, DBMAX, EXACT>(p, L, smem);
   if (!grid_barrier(p, 2, flag)) return;
-  phase_merge(p, L, smem);
+  phase_merge_uv<AF>(p, L, smem);
   if (!grid_barrier(p, 3, flag)) return;
-  phase_uv<AF>(p, smem);
-  if (!grid_barrier(p, 4, flag)) return;
   phase_wo<AF>(p, smem);
-  if (!grid_barrier(p, 5, flag)) return;
+  if (!grid_barrier(p, 4, flag)) return;
   phase_router<AF, EF>(p, smem);
-  if (!grid_barrier(p, 6, flag)) return;
+  if (!grid_barrier(p, 5, flag)) return;
   phase_route_gateup<AF, EF>(p, smem);
-  if (!grid_barrier(p, 7, flag)) return;
+  if (!grid_barrier(p, 6, flag)) return;
   phase_down<EF>(p, smem);
-  if (!grid_barrier(p, 8, flag)) return;
+  if (!grid_barrier(p, 7, flag)) return;
   LdsPlan lp(p, EF == MK_FMT_F32 ? 4 : 2);
   phase_combine(p, smem, lp.xb);
   if (p.trace && threadIdx.x == 0) {
