@@ -179,7 +179,7 @@ int device_info(int dev, DevInfo* di, LayerKernelFn fn) {
 }
 
 struct WsLayout {
-  size_t qkv_part, qrope, qabs, att_part, att_ml, z, o, hp, route_sel, route_gate, route_pub, route_cand, logits, hbuf,
+  size_t qkv_part, qrope, qabs, att_part, att_ml, z, o, hp, route_sel, route_gate, route_cand, logits, hbuf,
       ybuf, dummy,
       total;
 };
@@ -205,7 +205,6 @@ WsLayout ws_layout(const Dims& D, const Schedule& s) {
   w.hp = take((size_t)T * D.d * 4);
   w.route_sel = take((size_t)T * kMaxTopK * 4);
   w.route_gate = take((size_t)T * kMaxTopK * 4);
-  w.route_pub = take(4096);
   w.route_cand = take((size_t)2 * T * (D.E / 16) * 16 * 4);
   w.logits = take((size_t)T * D.E * 4);
   w.hbuf = take((size_t)slots * T * D.f * 4);
@@ -470,7 +469,6 @@ int mk_layer_init(const mk_layer_config* cfg, const mk_layer_weights* w, void* s
   p.hp = (float*)(ws + L->wl.hp);
   p.route_sel = (int32_t*)(ws + L->wl.route_sel);
   p.route_gate = (float*)(ws + L->wl.route_gate);
-  p.route_pub = (int32_t*)(ws + L->wl.route_pub);
   p.route_cand = (float*)(ws + L->wl.route_cand);
   p.logits = (float*)(ws + L->wl.logits);
   p.hbuf = (float*)(ws + L->wl.hbuf);

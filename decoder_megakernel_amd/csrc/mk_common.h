@@ -16,7 +16,6 @@ constexpr int kTraceX = 16;              // extra per-workgroup timestamps (sub-
 constexpr int kTraceStride = 2 + 2 * kBarriers + kTraceX;
 constexpr int kLdsBytes = 160 * 1024 - 256;
 constexpr int kMaxTopK = 16;
-constexpr int kRouteCnt = 64;            // index of the router-completion counter in att_cnt
 constexpr int kGateCnt = 128;            // index of the first of 8 gate/up ticket counters in att_cnt,
 constexpr int kCntStride = 64;           // which sit 256 bytes apart (device-scope atomics on one
                                          // line are serialised where they are performed)
@@ -103,15 +102,13 @@ struct LayerParams {
   int32_t* route_sel;      // [T][topk]
   float* route_gate;       // [T][topk]
   float* route_cand;       // router candidates: [T][E/16][16] biased logits, then [T][E/16][16] int expert ids
-  int32_t* route_pub;      // routing published for the expert phases: [0] slot count,
-                           // [16 + t*topk + k] slot of pick (t, k), 8-byte block pointers from byte 1024
   float* logits;           // [T][E] (written by workgroup 0)
   float* hbuf;             // [slots][T][f] in the expert activation type (fp32 or bf16)
   float* ybuf;             // [slots][T][d]
   const uint8_t* dummy;    // 32 KiB scratch read by the streams' last (discarded) prefetch
   // state
   BarrierState* bar;
-  uint32_t* att_cnt;       // [max query tiles]
+  uint32_t* att_cnt;       // ticket counters (gate/up at kGateCnt, down at kDownCnt)
   long long* trace;        // [nwg][2 + 2*kBarriers] or null
   long long timeout_ticks; // 100 MHz ticks
   Schedule sch;

@@ -12,10 +12,10 @@
 //       (head, pair of verify rows)
 //   P4  H' = H + W_O o
 //   P5  RMSNorm-2 (every workgroup, into LDS) ; router logits on E/16
-//       workgroups, the shared experts' gate+up on the others; the last router
-//       workgroup to finish computes softmax / top-k / gates / the distinct-
-//       expert work list and publishes them
-//   P6  gate+up projections of every routed expert: silu(W1 x) * W3 x
+//       workgroups, each keeping the top k of its 16 experts per token as
+//       candidates; the shared experts' gate+up on the other workgroups
+//   P6  every workgroup: top-k / gates / the distinct-expert work list from the
+//       candidates; gate+up projections of every routed expert: silu(W1 x) * W3 x
 //   P7  down projections W2 h of every listed expert
 //   P8  out = H' + sum_k gate_k y_k + y_shared
 #include <type_traits>
@@ -968,7 +968,13 @@ __device__ __forceinline__ void router_candidates(const LayerParams& p, const fl
   }
 }
 
-__device__ __forceinline__ void route(const LayerParams& p, const RouteLds& r) {
+// Every workgroup, at the start of the expert phases: the routing computed
+// into its own LDS tables from the router workgroups' candidates -- the top k
+// and gates per token (route_cands), then the slot list: the shared experts
+// first, then the distinct selected experts in ascending order, each with its
+// packed block.  Workgroup 0 also writes the selection and gates out (debug
+// taps) and counts the experts streamed.
+__device__ __forceinline__ void route_local(const LayerParams& p, const RouteLds& r) {
   const int T = p.T, E = p.E, K = p.topk, S0 = p.nshared;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   // the expert block table, loaded into LDS (the logit area is free) while the
@@ -1004,54 +1010,23 @@ __device__ __forceinline__ void route(const LayerParams& p, const RouteLds& r) {
     if (lane == 0) *r.nslots = base;
   }
   __syncthreads();
+  const int ns = *r.nslots;
   if (threadIdx.x < T * K) {
     const int t = threadIdx.x / K, k = threadIdx.x - t * K;
     r.slot_of[t * kMaxTopK + k] = r.flags[r.sel[t * kMaxTopK + k]] - 1;
   }
-  __syncthreads();
-  // publish for every workgroup (read back after the next grid barrier)
-  const int ns = *r.nslots;
-  const uint8_t** pub_blk = reinterpret_cast<const uint8_t**>(reinterpret_cast<char*>(p.route_pub) + 1024);
-  if (threadIdx.x < ns) pub_blk[threadIdx.x] = etab[r.slots[threadIdx.x]];
-  for (int i = threadIdx.x; i < T * K; i += kThreads) {
-    const int t = i / K, k = i - t * K;
-    p.route_sel[i] = r.sel[t * kMaxTopK + k];
-    p.route_gate[i] = r.gate[t * kMaxTopK + k];
-    p.route_pub[16 + i] = r.slot_of[t * kMaxTopK + k];
+  if ((int)threadIdx.x < ns) r.blk[threadIdx.x] = etab[r.slots[threadIdx.x]];
+  if (blockIdx.x == 0) {
+    for (int i = threadIdx.x; i < T * K; i += kThreads) {
+      const int t = i / K, k = i - t * K;
+      p.route_sel[i] = r.sel[t * kMaxTopK + k];
+      p.route_gate[i] = r.gate[t * kMaxTopK + k];
+    }
+    if (threadIdx.x == 0) {
+      p.bar->slots_sum += (unsigned long long)ns;
+      p.bar->launches += 1ull;
+    }
   }
-  if (threadIdx.x == 0) {
-    p.route_pub[0] = ns;
-    p.bar->slots_sum += (unsigned long long)ns;
-    p.bar->launches += 1ull;
-  }
-}
-
-// Every workgroup: the published routing into its LDS tables.
-__device__ __forceinline__ void route_load(const LayerParams& p, const RouteLds& r) {
-  const int T = p.T, K = p.topk;
-  const uint8_t* const* pub_blk =
-      reinterpret_cast<const uint8_t* const*>(reinterpret_cast<const char*>(p.route_pub) + 1024);
-  constexpr int kMaxSlots = kMaxT * kMaxTopK + 8;
-  const int tid = threadIdx.x;
-  int sel = 0, so = 0;
-  float gt = 0.f;
-  const uint8_t* b = nullptr;
-  int ns = 0;
-  if (tid < T * K) {
-    sel = ldg(p.route_sel + tid);
-    gt = ldg(p.route_gate + tid);
-    so = ldg(p.route_pub + 16 + tid);
-  }
-  if (tid < kMaxSlots) b = ldg(pub_blk + tid);
-  if (tid == 0) ns = ldg(p.route_pub);
-  if (tid < T * K) {
-    const int t = tid / K, k = tid - t * K;
-    r.sel[t * kMaxTopK + k] = sel;
-    r.gate[t * kMaxTopK + k] = gt;
-    r.slot_of[t * kMaxTopK + k] = so;
-  }
-  if (tid < kMaxSlots) r.blk[tid] = b;
-  if (tid == 0) *r.nslots = ns;
   __syncthreads();
 }
 
@@ -1192,19 +1167,6 @@ __device__ __forceinline__ void phase_router(const LayerParams& p, char* smem) {
   if (u1 <= u0) return;
   __syncthreads();
   router_candidates(p, lgl, u0, u1);
-  // the last workgroup to finish its router units computes the routing
-  int* flag = reinterpret_cast<int*>(smem + kFlagOff);
-  wg_release_begin();
-  if (threadIdx.x == 0) {
-    release_agent();
-    const uint32_t target = (uint32_t)min(RT, (int)gridDim.x);
-    const uint32_t old =
-        __hip_atomic_fetch_add(&p.att_cnt[kRouteCnt], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    *flag = old + 1 == target;
-    if (old + 1 == target) acquire_agent();
-  }
-  __syncthreads();
-  if (*flag) route(p, route_lds(p, smem, lp.xb));
 }
 
 // ------------------------------------------------------------------ P6 gate/up
@@ -1216,7 +1178,7 @@ __device__ __forceinline__ void phase_route_gateup(const LayerParams& p, char* s
   const A* xs = reinterpret_cast<const A*>(smem);      // x' (hi part) from P5
   float* red = reinterpret_cast<float*>(smem + lp.xb);
   RouteLds r = route_lds(p, smem, lp.xb);
-  route_load(p, r);
+  route_local(p, r);
   trace_x(p, 8);
   const int s0 = shared_early(p) ? p.nshared : 0;     // slots whose gate/up ran in P5
   const int ns = *r.nslots;
@@ -1547,9 +1509,7 @@ __global__ __launch_bounds__(kThreads, 1) void layer_kernel(LayerParams p) {
     for (int i = 1; i < kTraceStride; ++i) tl[i] = 0;
     tl[0] = (long long)clock100();
   }
-  // attention split counters: cleared here, used after two grid barriers
-  if (blockIdx.x == 0 && threadIdx.x <= kRouteCnt)
-    __hip_atomic_store(&p.att_cnt[threadIdx.x], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // ticket counters of the expert phases: cleared here, used after several grid barriers
   if (blockIdx.x == 0 && threadIdx.x < 16)
     __hip_atomic_store(&p.att_cnt[kGateCnt + kCntStride * threadIdx.x], 0u, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);   // gate/up and down ticket counters
