@@ -20,7 +20,10 @@ constexpr int kGateCnt = 128;            // index of the first of 8 gate/up tick
 constexpr int kCntStride = 64;           // which sit 256 bytes apart (device-scope atomics on one
                                          // line are serialised where they are performed)
 constexpr int kDownCnt = kGateCnt + 8 * kCntStride;   // the 8 down-projection ticket counters
-constexpr int kCntWords = kDownCnt + 8 * kCntStride;  // words of the counter area
+constexpr int kSlotCnt = kDownCnt + 8 * kCntStride;   // per-slot gate/up completion counters,
+constexpr int kSlotStride = 16;                       // 64 bytes apart
+constexpr int kMaxSlots = MK_MAX_T * kMaxTopK + 8;
+constexpr int kCntWords = kSlotCnt + kSlotStride * kMaxSlots;   // words of the counter area
 constexpr int kMaxExperts = 1024;        // routed experts per layer (16 logits per lane)
 constexpr int kStageCh = 18;             // float4s per lane when staging one activation row
 constexpr int kMaxStageK = kStageCh * 64 * 4;   // longest activation row (elements)

@@ -2,6 +2,8 @@
 // products, the grid barrier, and the workgroup "unit engine" that streams
 // pre-tiled weights through the matrix cores.
 #pragma once
+#include <type_traits>
+
 #include "mk_common.h"
 
 namespace mk {
@@ -600,9 +602,21 @@ __device__ __forceinline__ void run_stream(int u0, int u1, int NT, int T, const 
 // chunk is always requested one chunk ahead, as in run_stream.  The counters
 // `ctr[kCntStride * c]` must be zero before the first workgroup gets here.  Requires slice = NT/8
 // to be a multiple of D.
-template <int FMT, bool DUAL, int D, class Src, class Epi>
+//
+// With a Done callback (not NoDone), the epilogue works on row pairs instead:
+// epi(u, row0, col, v0, v2_0, v1, v2_1) for rows row0 and row0 + 1 (threads
+// < 128), which then wait until their stores have completed; after a
+// workgroup barrier thread 0 calls done(u).  Each wave keeps one chunk in
+// flight and the next unit's multiplications wait for that chunk anyway, so
+// the wait costs little.
+struct NoDone {
+  __device__ void operator()(int) const {}
+};
+template <int FMT, bool DUAL, int D, class Src, class Epi, class Done = NoDone>
 __device__ __forceinline__ void run_stream_dyn(int U, int NT, int T, const Src& src, const Epi& epi, float* red,
-                                               const uint8_t* dummy, uint32_t* ctr, int* seq) {
+                                               const uint8_t* dummy, uint32_t* ctr, int* seq,
+                                               const Done& done = Done()) {
+  constexpr bool kPairs = !std::is_same<Done, NoDone>::value;
   constexpr int TK = tile_k(FMT);
   constexpr long long STRIDE = DUAL ? 2048 : 1024;
   const int w = threadIdx.x >> 6;
@@ -691,18 +705,41 @@ __device__ __forceinline__ void run_stream_dyn(int U, int NT, int T, const Src& 
       seq[par] = un2 < U ? (int)un2 : -1;
     }
     __syncthreads();
-    if (threadIdx.x < 256) {
-      const int col = threadIdx.x & 15, row = threadIdx.x >> 4;
-      const int l = (row >> 2) * 16 + col, e = row & 3;
-      if (col < T) {
-        float v = 0.f, v2 = 0.f;
+    if constexpr (!kPairs) {
+      if (threadIdx.x < 256) {
+        const int col = threadIdx.x & 15, row = threadIdx.x >> 4;
+        const int l = (row >> 2) * 16 + col, e = row & 3;
+        if (col < T) {
+          float v = 0.f, v2 = 0.f;
 #pragma unroll
-        for (int ww = 0; ww < kWaves; ++ww) {
-          v += rb[(ww * 64 + l) * 4 + e];
-          if constexpr (DUAL) v2 += rb[kWaves * 64 * 4 + (ww * 64 + l) * 4 + e];
+          for (int ww = 0; ww < kWaves; ++ww) {
+            v += rb[(ww * 64 + l) * 4 + e];
+            if constexpr (DUAL) v2 += rb[kWaves * 64 * 4 + (ww * 64 + l) * 4 + e];
+          }
+          epi(cur, row, col, v, v2);
         }
-        epi(cur, row, col, v, v2);
       }
+    } else {
+      if (threadIdx.x < 128) {
+        const int col = threadIdx.x & 15, row = (threadIdx.x >> 4) * 2;
+        const int l = (row >> 2) * 16 + col, e = row & 3;
+        if (col < T) {
+          float v0 = 0.f, v1 = 0.f, w0 = 0.f, w1 = 0.f;
+#pragma unroll
+          for (int ww = 0; ww < kWaves; ++ww) {
+            v0 += rb[(ww * 64 + l) * 4 + e];
+            v1 += rb[(ww * 64 + l) * 4 + e + 1];
+            if constexpr (DUAL) {
+              w0 += rb[kWaves * 64 * 4 + (ww * 64 + l) * 4 + e];
+              w1 += rb[kWaves * 64 * 4 + (ww * 64 + l) * 4 + e + 1];
+            }
+          }
+          epi(cur, row, col, v0, w0, v1, w1);
+        }
+        wait_vmem();
+      }
+      __syncthreads();
+      if (threadIdx.x == 0) done(cur);
     }
     acc = zero;
     acc2 = zero;

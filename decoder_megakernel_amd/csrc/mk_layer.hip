@@ -1039,7 +1039,8 @@ struct NoStage {
   __device__ void finish() {}
 };
 // MODE 0: workgroup units [u0, u1); 1: wave units [u0, u1); 2: workgroup units
-// 0 .. u1-1 handed out at run time by the ticket counters.  `stage` requests
+// 0 .. u1-1 handed out at run time by the ticket counters; 3: as 2, and every
+// completed unit counted on its slot's completion counter.  `stage` requests
 // the activation operand (issue) before the first weight chunk is requested
 // and stores it (finish) before that chunk is used (workgroup mode).
 template <int EF, int MODE, class Stage = NoStage>
@@ -1077,7 +1078,30 @@ __device__ __forceinline__ void gateup_units(const LayerParams& p, const uint8_t
     const float sg = v / (1.0f + expf(-v));
     hb[((long long)sl * T + col) * f + rt * 16 + row] = to_act<A>(sg * v2);
   };
-  if constexpr (MODE == 2) {
+  if constexpr (MODE == 3) {
+    // row pairs written with agent-scope stores (they pass this XCD's L2, so a
+    // down projection on any XCD reads them once the slot's counter is full)
+    auto epi2 = [=](int u, int row, int col, float v0, float w0, float v1, float w1) {
+      const int sl = s0 + u / RT, rt = u % RT;
+      const float h0 = (v0 / (1.0f + expf(-v0))) * w0, h1 = (v1 / (1.0f + expf(-v1))) * w1;
+      A* dst = hb + ((long long)sl * T + col) * f + rt * 16 + row;
+      if constexpr (sizeof(A) == 2) {
+        const bf16x2 pr = {(__bf16)h0, (__bf16)h1};
+        __hip_atomic_store(reinterpret_cast<uint32_t*>(dst), __builtin_bit_cast(uint32_t, pr), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      } else {
+        __hip_atomic_store(reinterpret_cast<float*>(dst), h0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(reinterpret_cast<float*>(dst) + 1, h1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    };
+    uint32_t* scnt = p.att_cnt + kSlotCnt;
+    auto done = [=](int u) {
+      __hip_atomic_fetch_add(scnt + kSlotStride * (s0 + u / RT), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    stage.issue();
+    stage.finish();
+    run_stream_dyn<EF, true, 8>(u1, KT, T, src, epi2, red, p.dummy, p.att_cnt + kGateCnt, seq_lds(), done);
+  } else if constexpr (MODE == 2) {
     stage.issue();
     stage.finish();
     run_stream_dyn<EF, true, 8>(u1, KT, T, src, epi, red, p.dummy, p.att_cnt + kGateCnt, seq_lds());
@@ -1204,24 +1228,40 @@ __device__ __forceinline__ void phase_route_gateup(const LayerParams& p, char* s
 // D, the next chunk requested while the current one is multiplied, across unit
 // boundaries), and waves w and w + 4 add their blocks in LDS.  Units are handed
 // out as in run_stream_dyn: workgroup b takes units b and b + nwg, then draws
-// tickets, so workgroups on faster XCDs take more units.  The rows of a unit's
-// slot (h, T x d_ff in the operand type) sit in one of two LDS buffers; those of
-// the next unit's slot are requested when a unit starts and stored into the
-// other buffer once its chunks have been multiplied, so a change of slot costs
-// no extra round trip.
+// tickets, so workgroups on faster XCDs take more units.
+//
+// The rows of a unit's slot (h, T x d_ff in the operand type) sit in one of two
+// LDS buffers.  When the next unit's slot differs, its rows are requested at the
+// end of the current unit and stored into the other buffer when the next unit
+// starts.  Slots from `s_wait` on may still be in their gate/up phase (no grid
+// barrier in between): their rows are read only after the slot's completion
+// counter has reached d_ff / 16 (thread 0 requests the counter when a unit
+// starts and checks it, waiting if needed, when the unit ends), and they are read
+// with agent-scope loads, which do not return stale lines of this XCD's L2.
 __host__ __device__ constexpr bool down_dyn_fits(int d, int f, int tk, int es, int xb) {
-  return d % 64 == 0 && (f / tk) % 32 == 0 && 2 * kMaxT * (f + kXPad) * es <= xb;
+  return d % 64 == 0 && (f / tk) % 32 == 0 && 2 * kMaxT * (f + kXPad) * es <= xb &&
+         kMaxT * f * es <= 16 * kThreads * 4;
+}
+
+// Whether the expert phases run fused: ticket-fed gate/up units whose slot
+// completion counters let ticket-fed down projections start without a grid
+// barrier in between.
+template <int EF>
+__device__ __forceinline__ bool experts_fused(const LayerParams& p, int xb) {
+  constexpr int TK = tile_k(EF);
+  const int KT = p.d / TK;
+  return KT % kWaves == 0 && (KT / kWaves) % 8 == 0 &&
+         down_dyn_fits(p.d, p.f, TK, (int)sizeof(typename Act<EF>::T), xb);
 }
 
 template <int EF>
-__device__ __forceinline__ void phase_down_dyn(const LayerParams& p, char* smem, int xb, const RouteLds& r) {
+__device__ __forceinline__ bool phase_down_dyn(const LayerParams& p, char* smem, int xb, const RouteLds& r,
+                                               int s_wait) {
   typedef typename Act<EF>::T A;
   constexpr int TK = tile_k(EF);
   constexpr int D = 16;
-  constexpr int EPV = 16 / sizeof(A);                      // elements per 16 bytes
-  constexpr int HCH = (kMaxT * kMaxStageK / EPV + kThreads - 1) / kThreads;
+  constexpr int HW = 16;                                   // dwords of expert rows per thread, at most
   const int T = p.T, f = p.f, d = p.d, HS = f + kXPad;
-  const int hch = (kMaxT * f / EPV + kThreads - 1) / kThreads;   // 16-byte pieces per thread (<= HCH)
   const int ns = *r.nslots;
   const int QP = d / 64, KT = f / TK, NTh = KT / 2, cps = NTh / D;
   const int U = ns * QP;
@@ -1238,33 +1278,49 @@ __device__ __forceinline__ void phase_down_dyn(const LayerParams& p, char* smem,
   const int hsz = kMaxT * HS;
   float* red = reinterpret_cast<float*>(smem + xb);        // [2][8 waves][64][4]
   uint32_t* ctr = p.att_cnt + kDownCnt;
+  const uint32_t* scnt = p.att_cnt + kSlotCnt;
+  const uint32_t need = (uint32_t)(f / 16);                // gate/up units of one slot
   int* seq = seq_lds();
+  int* flag = reinterpret_cast<int*>(smem + kFlagOff);
   const float* dsc = reinterpret_cast<const float*>(p.dummy);
   int cur = (int)blockIdx.x < U ? (int)blockIdx.x : -1;
   int nxt = (int)blockIdx.x + nwg < U ? (int)blockIdx.x + nwg : -1;
-  if (cur < 0 || cps <= 0) return;
-  const int n16 = T * f / EPV;                              // 16-byte pieces of one slot's rows
-  const int p16 = f / EPV;                                  // ... of one row
-  auto h_src = [&](int sl, int c) {
-    const int i = min((int)threadIdx.x + kThreads * c, n16 - 1);
-    return reinterpret_cast<const A*>(p.hbuf) + (long long)sl * T * f + (long long)i * EPV;
-  };
-  auto h_dst = [&](A* buf, int c, A*& dst) {
-    const int i = (int)threadIdx.x + kThreads * c;
-    if (i >= n16) return false;
-    const int t = i / p16, k0 = (i - t * p16) * EPV;
-    dst = buf + (long long)t * HS + k0;
-    return true;
-  };
-  auto h_store = [&](A* buf, const u32x4* hv) {
+  if (cur < 0 || cps <= 0) return true;
+  const int n32 = T * f * (int)sizeof(A) / 4;             // dwords of one slot's rows
+  const int rw = f * (int)sizeof(A) / 4;                  // dwords of one row
+  const int hw = (kMaxT * f * (int)sizeof(A) / 4 + kThreads - 1) / kThreads;
+  auto h_load = [&](int sl, uint32_t* hv) {
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(reinterpret_cast<const A*>(p.hbuf) + (long long)sl * T * f);
 #pragma unroll
-    for (int c = 0; c < HCH; ++c) {
-      A* dst;
-      if (c < hch && h_dst(buf, c, dst)) {
-        *reinterpret_cast<uint2*>(dst) = uint2{hv[c][0], hv[c][1]};
-        *reinterpret_cast<uint2*>(dst + EPV / 2) = uint2{hv[c][2], hv[c][3]};
+    for (int c = 0; c < HW; ++c)
+      if (c < hw)
+        hv[c] = __hip_atomic_load(src + min((int)threadIdx.x + kThreads * c, n32 - 1), __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
+  };
+  auto h_store = [&](A* buf, const uint32_t* hv) {
+#pragma unroll
+    for (int c = 0; c < HW; ++c) {
+      const int i = (int)threadIdx.x + kThreads * c;
+      if (c < hw && i < n32) {
+        const int t = i / rw;
+        reinterpret_cast<uint32_t*>(buf + (long long)t * HS)[i - t * rw] = hv[c];
       }
     }
+  };
+  // thread 0: waits (bounded) until slot sl's gate/up units are all complete;
+  // false when the wait timed out or another workgroup reported a fault
+  auto slot_ready = [&](int sl, uint32_t seen) -> int {
+    if (sl < s_wait || seen >= need) return 1;
+    const uint64_t t0 = clock100();
+    while (__hip_atomic_load(scnt + kSlotStride * sl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < need) {
+      __builtin_amdgcn_s_sleep(1);
+      if ((long long)(clock100() - t0) > p.timeout_ticks) {
+        __hip_atomic_store(&p.bar->fault, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return 0;
+      }
+      if (__hip_atomic_load(&p.bar->fault, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) return 0;
+    }
+    return 1;
   };
   auto wbase = [&](int u) {
     const int sl = u / QP, rt = 4 * (u - sl * QP) + sub;
@@ -1275,14 +1331,12 @@ __device__ __forceinline__ void phase_down_dyn(const LayerParams& p, char* smem,
     return reinterpret_cast<const float*>(r.blk[sl] + sc2_off) + (rt >> 3) * nbk;
   };
   // the first unit's rows, staged synchronously
-  int hb = 0;
-  {
-    u32x4 hv[HCH];
-#pragma unroll
-    for (int c = 0; c < HCH; ++c)
-      if (c < hch) hv[c] = ld16(h_src(cur / QP, c));
-    h_store(hls, hv);
-  }
+  if (threadIdx.x == 0) *flag = slot_ready(cur / QP, 0);
+  __syncthreads();
+  if (!*flag) return false;
+  uint32_t hv[HW];
+  h_load(cur / QP, hv);
+  h_store(hls, hv);
   __syncthreads();
   u32x4 buf[D];
   float sc[D];
@@ -1295,27 +1349,29 @@ __device__ __forceinline__ void phase_down_dyn(const LayerParams& p, char* smem,
       if constexpr (EF == MK_FMT_FP8_B128) sc[rr] = ldg(sp + (((kp * NTh + rr) * TK) >> 7));
     }
   }
-  uint32_t tk = 0;
+  uint32_t tk = 0, cseen = 0;
   int cq = (int)blockIdx.x & 7;
-  int cc = 0, par = 0;
+  int cc = 0, par = 0, hb = 0;
+  bool hpend = false;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
   const int j = lane & 15, g = lane >> 4, jj = j < T ? j : T - 1;
-  u32x4 hv[HCH];
-  bool hnext = false;
   float* yb = p.ybuf;
   while (true) {
     if (cc == 0) {
-      if (threadIdx.x == 0)
+      if (hpend) {
+        // this unit's rows, requested when the previous unit ended
+        h_store(hls + (hb ^ 1) * hsz, hv);
+        __syncthreads();
+        hb ^= 1;
+      }
+      if (threadIdx.x == 0) {
         tk = __hip_atomic_fetch_add(ctr + kCntStride * cq, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      // the next unit's rows, stored only when its slot differs; requested
-      // either way (the current slot's rows, then) so that the number of loads
-      // in flight does not depend on a branch
-      hnext = nxt >= 0 && nxt / QP != cur / QP;
-      const int hsl = hnext ? nxt / QP : cur / QP;
-#pragma unroll
-      for (int c = 0; c < HCH; ++c)
-        if (c < hch) hv[c] = ld16(h_src(hsl, c));
+        const int ns2 = nxt >= 0 ? nxt / QP : 0;
+        cseen = (nxt >= 0 && ns2 != cur / QP && ns2 >= s_wait)
+                    ? __hip_atomic_load(scnt + kSlotStride * ns2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                    : need;
+      }
     }
     int ncc = cc + 1, un = cur;
     if (ncc == cps) {
@@ -1343,9 +1399,8 @@ __device__ __forceinline__ void phase_down_dyn(const LayerParams& p, char* smem,
     }
     cc = ncc;
     if (ncc != 0) continue;
-    // unit `cur` complete: the next slot's rows into the other buffer, the
-    // blocks of waves w and w + 4 added, the unit after nxt published
-    if (hnext) h_store(hls + (hb ^ 1) * hsz, hv);
+    // unit `cur` complete: the blocks of waves w and w + 4 added, the unit
+    // after nxt published, the next slot's completion confirmed
     float* rb = red + par * (kWaves * 64 * 4);
     *reinterpret_cast<f32x4*>(rb + (w * 64 + lane) * 4) = acc;
     if (threadIdx.x == 0) {
@@ -1356,8 +1411,10 @@ __device__ __forceinline__ void phase_down_dyn(const LayerParams& p, char* smem,
         un2 = 2LL * nwg + 8LL * tk + cq;
       }
       seq[par] = un2 < U ? (int)un2 : -1;
+      *flag = (nxt >= 0 && nxt / QP != cur / QP) ? slot_ready(nxt / QP, cseen) : 1;
     }
     __syncthreads();
+    if (!*flag) return false;
     {
       const int s4 = threadIdx.x >> 7, rem = threadIdx.x & 127, row = rem >> 3, col = rem & 7;
       if (col < T) {
@@ -1367,14 +1424,19 @@ __device__ __forceinline__ void phase_down_dyn(const LayerParams& p, char* smem,
         yb[((long long)sl * T + col) * d + rt * 16 + row] = v;
       }
     }
+    // the next unit's rows, when its slot differs; requested either way (the
+    // current slot's rows again) so that the loads in flight never depend on a
+    // branch
+    hpend = nxt >= 0 && nxt / QP != cur / QP;
+    h_load(hpend ? nxt / QP : cur / QP, hv);
     acc = zero;
-    if (hnext) hb ^= 1;
     cur = nxt;
     nxt = nxt >= 0 ? seq[par] : -1;
     par ^= 1;
     if (cur < 0) break;
   }
   __syncthreads();
+  return true;
 }
 
 // ------------------------------------------------------------------ P7 down projections
@@ -1423,7 +1485,7 @@ __device__ __forceinline__ void phase_down(const LayerParams& p, char* smem) {
     yb[((long long)sl * T + col) * d + rt * 16 + row] = v;
   };
   if (down_dyn_fits(p.d, p.f, TK, (int)sizeof(A), lp.xb)) {
-    phase_down_dyn<EF>(p, smem, lp.xb, r);
+    phase_down_dyn<EF>(p, smem, lp.xb, r, 1 << 30);
     return;
   }
   if (U >= 2 * (int)gridDim.x * kWaves) {
@@ -1454,6 +1516,25 @@ __device__ __forceinline__ void phase_down(const LayerParams& p, char* smem) {
       u = ue;
     }
   }
+}
+
+// The fused expert phases: routing, ticket-fed gate/up (counted per slot), then
+// ticket-fed down projections, which wait per slot instead of at a grid barrier.
+template <int AF, int EF>
+__device__ __forceinline__ void phase_experts_fused(const LayerParams& p, char* smem) {
+  typedef typename Act<EF>::T A;
+  LdsPlan lp(p, sizeof(A));
+  const A* xs = reinterpret_cast<const A*>(smem);      // x' (hi part) from P5
+  float* red = reinterpret_cast<float*>(smem + lp.xb);
+  RouteLds r = route_lds(p, smem, lp.xb);
+  route_local(p, r);
+  trace_x(p, 8);
+  const int s0 = shared_early(p) ? p.nshared : 0;     // slots whose gate/up ran in P5
+  const int ns = *r.nslots;
+  gateup_units<EF, 3>(p, r.blk + s0, s0, 0, (ns - s0) * (p.f / 16), xs, red);
+  __syncthreads();
+  trace_x(p, 9);
+  phase_down_dyn<EF>(p, smem, lp.xb, r, s0);
 }
 
 // ------------------------------------------------------------------ P8 combine
@@ -1513,6 +1594,9 @@ __global__ __launch_bounds__(kThreads, 1) void layer_kernel(LayerParams p) {
   if (blockIdx.x == 0 && threadIdx.x < 16)
     __hip_atomic_store(&p.att_cnt[kGateCnt + kCntStride * threadIdx.x], 0u, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);   // gate/up and down ticket counters
+  if (blockIdx.x == 0 && threadIdx.x < kMaxSlots)
+    __hip_atomic_store(&p.att_cnt[kSlotCnt + kSlotStride * threadIdx.x], 0u, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);   // slot completion counters
   phase_qkv<AF>(p, smem);
   if (!grid_barrier(p, 0, flag)) return;
   {
@@ -1537,9 +1621,13 @@ __global__ __launch_bounds__(kThreads, 1) void layer_kernel(LayerParams p) {
   if (!grid_barrier(p, 4, flag)) return;
   phase_router<AF, EF>(p, smem);
   if (!grid_barrier(p, 5, flag)) return;
-  phase_route_gateup<AF, EF>(p, smem);
-  if (!grid_barrier(p, 6, flag)) return;
-  phase_down<EF>(p, smem);
+  if (experts_fused<EF>(p, LdsPlan(p, EF == MK_FMT_F32 ? 4 : 2).xb)) {
+    phase_experts_fused<AF, EF>(p, smem);
+  } else {
+    phase_route_gateup<AF, EF>(p, smem);
+    if (!grid_barrier(p, 6, flag)) return;
+    phase_down<EF>(p, smem);
+  }
   if (!grid_barrier(p, 7, flag)) return;
   LdsPlan lp(p, EF == MK_FMT_F32 ? 4 : 2);
   phase_combine(p, smem, lp.xb);

@@ -18,9 +18,10 @@ MID_FP8 = LayerShape("mid_fp8", d=640, n_h=6, d_h=64, d_c=256, d_r=64, E=48, top
                      T=7, L=300, attn_fmt="bf16", exp_fmt="fp8", kv_fmt="bf16")
 MID_F32 = LayerShape("mid_f32", d=384, n_h=4, d_h=32, d_c=96, d_r=32, E=16, top_k=3, n_shared=1, f=256,
                      T=3, L=45, attn_fmt="f32", exp_fmt="f32", kv_fmt="f32")
-# Expert widths of 32 tiles and d_model >= 2 d_ff: the down projection runs as
-# ticket-fed four-row-tile units with the expert rows double-buffered in LDS.
-MID_F32_DOWN = LayerShape("mid_f32_down", d=1024, n_h=4, d_h=64, d_c=128, d_r=32, E=16, top_k=2, n_shared=1,
+# Expert widths of 32 tiles, d_model of 64 tiles and d_model >= 2 d_ff: the
+# expert phases run fused (ticket-fed gate/up counted per slot, then ticket-fed
+# four-row-tile down projections with the expert rows double-buffered in LDS).
+MID_F32_DOWN = LayerShape("mid_f32_down", d=2048, n_h=4, d_h=64, d_c=128, d_r=32, E=16, top_k=2, n_shared=1,
                           f=512, T=5, L=50, attn_fmt="f32", exp_fmt="f32", kv_fmt="f32")
 MID_BF16_DOWN = LayerShape("mid_bf16_down", d=2048, n_h=4, d_h=64, d_c=128, d_r=32, E=16, top_k=4, n_shared=1,
                            f=1024, T=6, L=100, attn_fmt="bf16", exp_fmt="bf16", kv_fmt="bf16")
