@@ -430,7 +430,11 @@ struct Chunk {
 // or with `enable` false, they read `dummy`), so the number of loads in flight
 // after the call does not depend on a branch and later waits for older loads
 // can count past them.
-template <int FMT, bool DUAL, bool WG, int D, class Src>
+//
+// Only the first PD tiles of the chunk are requested here (the rest when the
+// stream starts): a whole chunk from every wave of the grid would fill the
+// memory queues, and the activation loads that follow would wait behind it.
+template <int FMT, bool DUAL, bool WG, int D, int PD = D, class Src>
 __device__ __forceinline__ void stream_prime(Chunk<FMT, DUAL, D>& c, int u0, int u1, int NT, const Src& src,
                                              const uint8_t* dummy, bool enable = true) {
   constexpr int TK = tile_k(FMT);
@@ -455,7 +459,7 @@ __device__ __forceinline__ void stream_prime(Chunk<FMT, DUAL, D>& c, int u0, int
     soff = toff;
   }
 #pragma unroll
-  for (int r = 0; r < D; ++r) {
+  for (int r = 0; r < PD; ++r) {
     c.buf[r] = ld_stream16(cbase + r * STRIDE);
     if constexpr (DUAL) c.buf2[r] = ld_stream16(cbase + r * STRIDE + 1024);
     if constexpr (FMT == MK_FMT_FP8_B128) {
@@ -466,7 +470,7 @@ __device__ __forceinline__ void stream_prime(Chunk<FMT, DUAL, D>& c, int u0, int
   }
 }
 
-template <int FMT, bool DUAL, bool HILO, bool WG, int D, bool PRIMED = false, class Src, class Epi>
+template <int FMT, bool DUAL, bool HILO, bool WG, int D, bool PRIMED = false, int PD = D, class Src, class Epi>
 __device__ __forceinline__ void run_stream(int u0, int u1, int NT, int T, const Src& src, const Epi& epi, float* red,
                                            const uint8_t* dummy, Chunk<FMT, DUAL, D>* pre = nullptr) {
   constexpr int TK = tile_k(FMT);
@@ -508,6 +512,19 @@ __device__ __forceinline__ void run_stream(int u0, int u1, int NT, int T, const 
       if constexpr (DUAL) sp2 = src.sbase2(u);
     }
     load_chunk(src.base(u) + lane * 16 + (long long)toff * STRIDE, sp, sp2, toff);
+  } else if constexpr (PD < D) {
+    // the tiles of the first chunk that stream_prime left out
+    const int u = ufirst;
+    const uint8_t* cbase = src.base(u) + lane * 16 + (long long)toff * STRIDE;
+#pragma unroll
+    for (int r = PD; r < D; ++r) {
+      buf[r] = ld_stream16(cbase + r * STRIDE);
+      if constexpr (DUAL) buf2[r] = ld_stream16(cbase + r * STRIDE + 1024);
+      if constexpr (FMT == MK_FMT_FP8_B128) {
+        sc[r] = ldg(src.sbase(u) + (((toff + r) * TK) >> 7));
+        if constexpr (DUAL) sc2[r] = ldg(src.sbase2(u) + (((toff + r) * TK) >> 7));
+      }
+    }
   }
   int cu = 0, cc = 0;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -766,12 +783,12 @@ __device__ __forceinline__ void stream_units_wg(int u0, int u1, int NT, int T, c
 // Workgroup-mode streaming whose first chunk may have been primed: when the
 // slice allows the full-depth engine (`primed` tells whether stream_prime ran
 // with the same arguments), else the general engines.
-template <int FMT, bool DUAL, bool HILO, class Src, class Epi>
+template <int FMT, bool DUAL, bool HILO, int PD = (DUAL ? 8 : 16), class Src, class Epi>
 __device__ __forceinline__ void stream_units_wg_primed(int u0, int u1, int NT, int T, const Src& src, const Epi& epi,
                                                        float* red, const uint8_t* dummy,
                                                        Chunk<FMT, DUAL, DUAL ? 8 : 16>& pre, bool primed) {
   constexpr int DMAX = DUAL ? 8 : 16;
-  if (primed) run_stream<FMT, DUAL, HILO, true, DMAX, true>(u0, u1, NT, T, src, epi, red, dummy, &pre);
+  if (primed) run_stream<FMT, DUAL, HILO, true, DMAX, true, PD>(u0, u1, NT, T, src, epi, red, dummy, &pre);
   else stream_units_wg<FMT, DUAL, HILO>(u0, u1, NT, T, src, epi, red, dummy);
 }
 // Whether stream_units_wg_primed can use a primed first chunk for this slice.

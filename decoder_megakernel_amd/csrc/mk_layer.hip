@@ -24,6 +24,9 @@
 
 namespace mk {
 
+// Tiles of a phase's first chunk requested ahead of its activation rows (of 16).
+constexpr int kPrimeTiles = 8;
+
 // ------------------------------------------------------------------ LDS plan
 struct LdsPlan {
   int xb;        // bytes of one activation operand [kMaxT][dmax + pad]
@@ -296,11 +299,11 @@ __device__ __forceinline__ void phase_qkv(const LayerParams& p, char* smem) {
   trace_x(p, 10);
   Chunk<AF, false, 16> ck;
   const bool pr = wg_primable(NT, false);
-  stream_prime<AF, false, true, 16>(ck, u0, u1, NT, src, p.dummy, pr);
+  stream_prime<AF, false, true, 16, kPrimeTiles>(ck, u0, u1, NT, src, p.dummy, pr);
   trace_x(p, 3);
   rs.finish(T, p.d, xs, (A*)nullptr, XS, p.eps, p.trace != nullptr);
   trace_x(p, 5);
-  stream_units_wg_primed<AF, false, false>(u0, u1, NT, T, src, epi, red, p.dummy, ck, pr);
+  stream_units_wg_primed<AF, false, false, kPrimeTiles>(u0, u1, NT, T, src, epi, red, p.dummy, ck, pr);
 }
 
 // ------------------------------------------------------------------ P1
@@ -817,10 +820,10 @@ __device__ __forceinline__ void phase_wo(const LayerParams& p, char* smem) {
   rc.issue(reinterpret_cast<const A*>(p.o), T, K);
   Chunk<AF, false, 16> ck;
   const bool pr = wg_primable(KT, false);
-  stream_prime<AF, false, true, 16>(ck, u0, u1, KT, src, p.dummy, pr);
+  stream_prime<AF, false, true, 16, kPrimeTiles>(ck, u0, u1, KT, src, p.dummy, pr);
   rc.finish(T, K, xs, XS);
   trace_x(p, 6);
-  stream_units_wg_primed<AF, false, false>(u0, u1, KT, T, src, epi, red, p.dummy, ck, pr);
+  stream_units_wg_primed<AF, false, false, kPrimeTiles>(u0, u1, KT, T, src, epi, red, p.dummy, ck, pr);
 }
 
 // ------------------------------------------------------------------ routing
@@ -1113,9 +1116,9 @@ __device__ __forceinline__ void gateup_units(const LayerParams& p, const uint8_t
     stage.issue();
     Chunk<EF, true, 8> ck;
     const bool pr = wg_primable(KT, true);
-    stream_prime<EF, true, true, 8>(ck, u0, u1, KT, src, p.dummy, pr);
+    stream_prime<EF, true, true, 8, kPrimeTiles / 2>(ck, u0, u1, KT, src, p.dummy, pr);
     stage.finish();
-    stream_units_wg_primed<EF, true, false>(u0, u1, KT, T, src, epi, red, p.dummy, ck, pr);
+    stream_units_wg_primed<EF, true, false, kPrimeTiles / 2>(u0, u1, KT, T, src, epi, red, p.dummy, ck, pr);
   }
 }
 
@@ -1184,10 +1187,10 @@ __device__ __forceinline__ void phase_router(const LayerParams& p, char* smem) {
   rs.issue(p.hp, T, p.d, p.g2);
   Chunk<AF, false, 16> ck;
   const bool pr = wg_primable(KT, false);
-  stream_prime<AF, false, true, 16>(ck, u0, u1, KT, src, p.dummy, pr);
+  stream_prime<AF, false, true, 16, kPrimeTiles>(ck, u0, u1, KT, src, p.dummy, pr);
   rs.finish(T, p.d, xs, xlo, XS, p.eps);
   trace_x(p, 7);
-  stream_units_wg_primed<AF, false, AF != MK_FMT_F32>(u0, u1, KT, T, src, epi, red, p.dummy, ck, pr);
+  stream_units_wg_primed<AF, false, AF != MK_FMT_F32, kPrimeTiles>(u0, u1, KT, T, src, epi, red, p.dummy, ck, pr);
   if (u1 <= u0) return;
   __syncthreads();
   router_candidates(p, lgl, u0, u1);
@@ -1552,16 +1555,17 @@ __device__ __forceinline__ void phase_combine(const LayerParams& p, char* smem, 
 }
 
 // ------------------------------------------------------------------ the kernel
-// Layer shapes with an instance of their own, where every dimension is a
-// compile-time constant: address arithmetic folds, the ragged-shape engines
-// drop out, and fewer values stay live across phases.
+// Layer shapes with an instance of their own, where every dimension (and the
+// projection's split-K factor, 1) is a compile-time constant: address
+// arithmetic folds, the ragged-shape engines drop out, and fewer values stay
+// live across phases.
 struct SpecShape {
-  int d, nh, dh, dc, dr, E, topk, nshared, f;
+  int d, nh, dh, dc, dr, E, topk, nshared, f, s_q;
 };
 constexpr SpecShape kSpecShapes[] = {
-    {0, 0, 0, 0, 0, 0, 0, 0, 0},                 // 0: dimensions read from the parameters
-    {4096, 32, 128, 512, 64, 128, 8, 1, 1024},   // 1: 128 experts of width 1024
-    {4096, 32, 128, 512, 64, 384, 8, 1, 2048},   // 2: 384 experts of width 2048
+    {0, 0, 0, 0, 0, 0, 0, 0, 0, 0},                 // 0: dimensions read from the parameters
+    {4096, 32, 128, 512, 64, 128, 8, 1, 1024, 1},   // 1: 128 experts of width 1024
+    {4096, 32, 128, 512, 64, 384, 8, 1, 2048, 1},   // 2: 384 experts of width 2048
 };
 template <int SPEC>
 __device__ __forceinline__ void specialise(LayerParams& p) {
@@ -1570,6 +1574,7 @@ __device__ __forceinline__ void specialise(LayerParams& p) {
     p.d = s.d; p.nh = s.nh; p.dh = s.dh; p.dc = s.dc; p.dr = s.dr;
     p.qw = s.dh + s.dr; p.kvw = s.dc + s.dr; p.nq = s.nh * (s.dh + s.dr);
     p.E = s.E; p.topk = s.topk; p.nshared = s.nshared; p.f = s.f;
+    p.sch.s_q = s.s_q;
   }
 }
 
@@ -1644,12 +1649,12 @@ __global__ __launch_bounds__(kThreads, 1) void layer_kernel(LayerParams p) {
 // attention loop bounds are constants too).
 typedef void (*LayerKernelFn)(LayerParams);
 LayerKernelFn layer_kernel_for(int af, int ef, int kf, int d, int nh, int dh, int dc, int dr, int E, int topk,
-                               int nshared, int f) {
+                               int nshared, int f, int s_q) {
   const int kvw = dc + dr;
   auto is = [&](int i) {
     const SpecShape& s = kSpecShapes[i];
     return d == s.d && nh == s.nh && dh == s.dh && dc == s.dc && dr == s.dr && E == s.E && topk == s.topk &&
-           nshared == s.nshared && f == s.f;
+           nshared == s.nshared && f == s.f && (s_q == 0 || s_q == s.s_q);
   };
   if (af == MK_FMT_F32 && ef == MK_FMT_F32 && kf == MK_FMT_F32 && kvw <= 160 && dc <= 128)
     return layer_kernel<MK_FMT_F32, MK_FMT_F32, MK_FMT_F32, 10, 8, false, 0>;
