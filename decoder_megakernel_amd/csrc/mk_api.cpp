@@ -89,8 +89,14 @@ int check_cfg(const mk_layer_config* c) {
   const long long lds_router = 2 * xb + 2 * kWaves * 64 * 4 * 4 + 4LL * kMaxT * 16 * 4;
   const long long lds_route = xb + 32768 + (long long)kMaxT * D.E * 4 + 3 * kMaxT * kMaxTopK * 4 +
                               (kMaxT * kMaxTopK + 8) * 4 + (long long)D.E * 4 + 16 + (kMaxT * kMaxTopK + 8) * 8;
-  const long long lds_att = std::max((long long)kWaves * 16 * (D.dc + 8) * es + 16LL * (D.kvw + 8) * es,
-                                     4LL * 16 * D.dc * 4 + 8 * 64 * 2 * 4);
+  // attention: per-wave value slices (half the latent, key-dim blocks of 16 fp32
+  // or 32 bf16 dims), the query tile, two rounds of score halves; then the
+  // merge of the four wave pairs
+  const int kbw = f32 ? 16 : 32, la = (D.dc / kbw + 1) / 2;
+  const long long lds_att =
+      std::max(((long long)kWaves * 16 * (la * kbw + 8) * es + 16LL * (D.kvw + 8) * es + 15) / 16 * 16 +
+                   2LL * kWaves * 64 * 16,
+               4LL * 16 * D.dc * 4 + 8 * 64 * 2 * 4);
   const long long lim = kLdsBytes - 1024;
   // the down projection stages two experts' activations below the routing tables
   if (2LL * kMaxT * (D.f + kXPad) * es > xb + 32768)

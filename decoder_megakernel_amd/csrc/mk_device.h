@@ -57,7 +57,13 @@ __device__ __forceinline__ void wg_release_begin() {
 
 // Agent-scope release (L2 write-back of this compute unit's XCD, so other XCDs
 // can read what this workgroup wrote) and acquire (drop stale cached copies).
-__device__ __forceinline__ void release_agent() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
+// The write-back is complete when the wave's memory counter drains; the fence
+// alone may leave that wait out when no load or store of the wave is pending
+// (the write-back itself is not counted as pending), so it is spelled out.
+__device__ __forceinline__ void release_agent() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  wait_vmem();
+}
 __device__ __forceinline__ void acquire_agent() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
 
 __device__ __forceinline__ uint64_t clock100() { return __builtin_amdgcn_s_memrealtime(); }

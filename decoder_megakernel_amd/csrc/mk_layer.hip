@@ -460,44 +460,83 @@ __device__ __forceinline__ void attn_splits(int NQT, int Lt, int& s_kv, int& SK)
 
 // EXACT: d_latent + d_rope == KBMAX * KBW and d_latent == 16 * DBMAX, so every
 // per-block bound is a compile-time constant (no guards inside the loops).
+//
+// One unit = (query tile of 16 rows of [q~ | q^R], a split of the keys).  The
+// waves form four pairs; pair c takes key chunks (16 keys) c, c + 4, ... of the
+// split, and wave 2c + h of the pair takes half h of the key dims: latent
+// blocks [0, la) or [la, n_lat) (la = ceil(n_lat / 2)) plus a share of the
+// RoPE blocks.  Each wave computes its half of S = Q K^T for the chunk, the two
+// halves are added through LDS (both waves then hold the same scores and run
+// the same online softmax), and each wave multiplies P into its own half of
+// the latent accumulator Z with the value rows it already loaded (its latent
+// blocks, staged in its LDS slice and read transposed).  The next chunk's key
+// rows are requested before the current chunk is used.  At the end the four
+// pairs' (m, l, Z) are merged in LDS.
 template <int KF, int KBMAX, int DBMAX, bool EXACT>
 __device__ __forceinline__ void phase_attention(const LayerParams& p, int L, char* smem) {
   typedef typename AttnTypes<KF>::E E;
   constexpr int KBW = AttnTypes<KF>::KBW;
+  constexpr int PB = KBW / 16;                         // 16-dim value blocks per key-dim block
+  constexpr int NLMAX = DBMAX / PB;                    // latent key-dim blocks, at most
+  constexpr int KHMAX = EXACT ? (NLMAX + 1) / 2 + (KBMAX - NLMAX + 1) / 2 : (KBMAX + 1) / 2;
+  constexpr int DBH = (NLMAX + 1) / 2 * PB;            // value blocks per half, at most
   const int T = p.T, nh = p.nh;
   const int dc = EXACT ? 16 * DBMAX : p.dc, kvw = EXACT ? KBMAX * KBW : p.kvw;
   const int NQ = T * nh, NQT = (NQ + 15) / 16, Lt = L + T;
-  const int KB = EXACT ? KBMAX : kvw / KBW, DB = EXACT ? DBMAX : dc / 16;
+  const int nlat = EXACT ? NLMAX : dc / KBW, KB = EXACT ? KBMAX : kvw / KBW, nrope = KB - nlat;
+  const int la = (nlat + 1) / 2, ra = nrope / 2;
   int s_kv, SK;
   attn_splits(NQT, Lt, s_kv, SK);
   const int units = NQT * s_kv;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, j = lane & 15, g = lane >> 4;
-  const int CS = dc + 8;                               // LDS row stride of a staged chunk
-  E* cb = reinterpret_cast<E*>(smem) + (long long)w * 16 * CS;
+  const int hf = w & 1, cg = w >> 1;
+  // this wave's key-dim blocks: nl latent ones from l0, then nr RoPE ones from r0
+  const int l0 = hf ? la : 0, nl = hf ? nlat - la : la;
+  const int r0 = nlat + (hf ? ra : 0), nr = hf ? nrope - ra : ra;
+  const int nk = nl + nr;
+  const int CSH = la * KBW + 8;                        // LDS row stride of a value slice
+  E* vs = reinterpret_cast<E*>(smem) + (long long)w * 16 * CSH;
   const int QS = kvw + 8;                              // LDS row stride of the query tile
-  E* qs = reinterpret_cast<E*>(smem) + (long long)kWaves * 16 * CS;
+  E* qs = reinterpret_cast<E*>(smem) + (long long)kWaves * 16 * CSH;
+  f32x4* sx = reinterpret_cast<f32x4*>(smem + (((long long)kWaves * 16 * CSH + 16LL * QS) * sizeof(E) + 15) / 16 * 16);
   const E* qlane = qs + j * QS + g * (KBW / 4);
   const E* kvp = reinterpret_cast<const E*>(p.kv);
+  auto kblk = [&](int i) { return (EXACT ? i < NLMAX / 2 : i < nl) ? l0 + i : r0 + i - nl; };
   for (int u = blockIdx.x; u < units; u += gridDim.x) {
     const int qt = u / s_kv, s = u - qt * s_kv;
     const int qi = qt * 16 + j, qc = qi < NQ ? qi : NQ - 1;
     const int tq = qc / nh;
     const int limit = L + tq;                          // keys 0..limit are visible
-    // query tile -> LDS (shared by the 8 waves): qs[16][kvw + 8] = [q~ | rotated q^R]
+    const int k0 = s * SK, k1 = min(Lt, k0 + SK);
+    const int nch = k1 > k0 ? (k1 - k0 + 15) / 16 : 0;
+    const int nit = (nch + 3) / 4;                     // chunk rounds (the same for every wave)
+    // key rows of chunk c of this split, this wave's dims; chunks past the
+    // split read clamped rows (their scores are masked)
+    u32x4 ka[KHMAX], kn[KHMAX];
+    auto load_chunk = [&](int c, u32x4 (&kr)[KHMAX]) {
+      const int key = min(k0 + c * 16 + j, Lt - 1);
+      const E* row = kvp + (long long)key * kvw + g * (KBW / 4);
+#pragma unroll
+      for (int i = 0; i < KHMAX; ++i)
+        if (EXACT || i < nk) kr[i] = ld16(row + kblk(i) * KBW);
+    };
+    // query tile -> LDS (shared by the 8 waves): qs[16][kvw + 8] = [q~ | rotated q^R];
+    // its loads go out first, then this wave's first key rows, so that
+    // storing the query waits for the query only
     __syncthreads();
     {
       const int n4 = kvw / 4;
       f32x4 qv[5];
 #pragma unroll
       for (int c = 0; c < 5; ++c) {
-        const int i = threadIdx.x + c * kThreads;
-        if (i < 16 * n4) {
-          const int jq = i / n4, dd = (i - jq * n4) * 4;
-          const int qq = min(qt * 16 + jq, NQ - 1);
-          const float* src = dd < dc ? p.qabs + (long long)qq * dc + dd : p.qrope + (long long)qq * p.dr + (dd - dc);
-          qv[c] = ldg(reinterpret_cast<const f32x4*>(src));
-        }
+        const int i = min((int)threadIdx.x + c * kThreads, 16 * n4 - 1);
+        const int jq = i / n4, dd = (i - jq * n4) * 4;
+        const int qq = min(qt * 16 + jq, NQ - 1);
+        const float* src = dd < dc ? p.qabs + (long long)qq * dc + dd : p.qrope + (long long)qq * p.dr + (dd - dc);
+        qv[c] = ldg(reinterpret_cast<const f32x4*>(src));
       }
+      __builtin_amdgcn_sched_barrier(0);     // keep every query load ahead of the key rows
+      load_chunk(cg, ka);
 #pragma unroll
       for (int c = 0; c < 5; ++c) {
         const int i = threadIdx.x + c * kThreads;
@@ -509,37 +548,32 @@ __device__ __forceinline__ void phase_attention(const LayerParams& p, int L, cha
     }
     __syncthreads();
     trace_x(p, 0);
-    const int k0 = s * SK, k1 = min(Lt, k0 + SK);
-    const int nch = k1 > k0 ? (k1 - k0 + 15) / 16 : 0;
     float m_run = -INFINITY, l_run = 0.f;
-    f32x4 acc[DBMAX];
+    f32x4 acc[DBH];
 #pragma unroll
-    for (int db = 0; db < DBMAX; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int c = w; c < nch; c += kWaves) {
+    for (int db = 0; db < DBH; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int it = 0; it < nit; ++it) {
+      const int c = cg + 4 * it;
       const int kbase = k0 + c * 16;
-      const int key = min(kbase + j, Lt - 1);          // lane (g, i=j) loads key i
-      const E* row = kvp + (long long)key * kvw;
-      // S^T = K Q^T over the key dims; the latent part of the chunk is also
-      // staged (row-major) in this wave's LDS slice for the value product
+      load_chunk(c + 4, kn);
+      // this wave's half of S^T = K Q^T; its latent blocks also go to its
+      // value slice (row-major) for the value product
       f32x4 st = {0.f, 0.f, 0.f, 0.f};
-      constexpr int NB = 3;                              // key-dim blocks loaded in 3 batches
-      constexpr int KH = (KBMAX + NB - 1) / NB;
 #pragma unroll
-      for (int half = 0; half < NB; ++half) {
-        u32x4 kr[KH];
-#pragma unroll
-        for (int i = 0; i < KH; ++i) {
-          const int kb = half * KH + i;
-          if (kb < KB) kr[i] = ld16(row + kb * KBW + g * (KBW / 4));
+      for (int i = 0; i < KHMAX; ++i) {
+        if (EXACT || i < nk) {
+          st = tile_mma_reg<KF>(ka[i], *reinterpret_cast<const typename BReg<KF>::T*>(qlane + kblk(i) * KBW), st);
+          if (EXACT ? i < NLMAX / 2 : i < nl)
+            *reinterpret_cast<u32x4*>(vs + j * CSH + i * KBW + g * (KBW / 4)) = ka[i];
         }
-#pragma unroll
-        for (int i = 0; i < KH; ++i) {
-          const int kb = half * KH + i;
-          if (kb < KB) {
-            st = tile_mma_reg<KF>(kr[i], *reinterpret_cast<const typename BReg<KF>::T*>(qlane + kb * KBW), st);
-            if (kb * KBW < dc) *reinterpret_cast<u32x4*>(cb + j * CS + kb * KBW + g * (KBW / 4)) = kr[i];
-          }
-        }
+      }
+      // the two halves added (the same order of addition in both waves)
+      f32x4* sxb = sx + (it & 1) * (kWaves * 64);
+      sxb[w * 64 + lane] = st;
+      __syncthreads();
+      {
+        const f32x4 o = sxb[(w ^ 1) * 64 + lane];
+        st = hf ? o + st : st + o;
       }
       // scores: lane (g, j) elem e = S[query j][key kbase + 4g + e]
       float sc[4];
@@ -568,52 +602,53 @@ __device__ __forceinline__ void phase_attention(const LayerParams& p, int L, cha
       ps += __shfl_xor(ps, 32);
       l_run = l_run * alpha + ps;
       m_run = m_new;
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const int DBh = EXACT ? DBH : nl * PB;
       if (KF == MK_FMT_BF16) {
         bf16x4 pb;
 #pragma unroll
         for (int e = 0; e < 4; ++e) pb[e] = (__bf16)pe[e];
-        // A operand (dims x keys) read transposed from the row-major chunk:
+        // A operand (dims x keys) read transposed from the row-major slice:
         // lane (g, 4e + q) points at key 4g + e, dims 16 db + 4q .. + 3
-        const __bf16* tb = reinterpret_cast<const __bf16*>(cb) + (4 * g + (j >> 2)) * CS + 4 * (j & 3);
+        const __bf16* tb = reinterpret_cast<const __bf16*>(vs) + (4 * g + (j >> 2)) * CSH + 4 * (j & 3);
 #pragma unroll
-        for (int d0 = 0; d0 < DBMAX; d0 += 8) {
+        for (int d0 = 0; d0 < DBH; d0 += 8) {
           bf16x4 av[8];
 #pragma unroll
           for (int i = 0; i < 8; ++i)
-            if (d0 + i < DB) av[i] = lds_read_tr16(tb + (d0 + i) * 16);
+            if (d0 + i < DBh) av[i] = lds_read_tr16(tb + (d0 + i) * 16);
 #pragma unroll
           for (int i = 0; i < 8; ++i)
-            if (d0 + i < DB) acc[d0 + i] = mma_bf16_k16(av[i], pb, acc[d0 + i] * alpha);
+            if (d0 + i < DBh) acc[d0 + i] = mma_bf16_k16(av[i], pb, acc[d0 + i] * alpha);
         }
       } else {
 #pragma unroll
-        for (int db = 0; db < DBMAX; ++db) {
-          if (db < DB) {
+        for (int db = 0; db < DBH; ++db) {
+          if (db < DBh) {
             f32x4 a = acc[db] * alpha;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) a = mma_f32_k4((float)cb[(4 * g + e) * CS + db * 16 + j], pe[e], a);
+            for (int e = 0; e < 4; ++e) a = mma_f32_k4((float)vs[(4 * g + e) * CSH + db * 16 + j], pe[e], a);
             acc[db] = a;
           }
         }
       }
+      // the slice is rewritten by the next round of this wave only
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int i = 0; i < KHMAX; ++i) ka[i] = kn[i];
     }
-    // merge the 8 waves' (m, l, Z): every wave rescales its state to the
-    // common maximum; waves 4..7 hand their Z to waves 0..3 through LDS, the
-    // four pair sums go back to LDS, and wave w sums latent blocks w, w+8, ...
-    // of the four in a fixed order and writes them out.
+    // merge the four pairs' (m, l, Z): every wave rescales its half of Z to the
+    // common maximum and stores it; wave w then adds latent blocks w, w + 8, ...
+    // over the pairs in a fixed order and writes them out.
     __syncthreads();
     trace_x(p, 1);
-    // Partial state layout in LDS: block db of the latent holds, per lane, the
-    // 4 values acc[db] (MFMA result layout: lane (g, j) has dims 16 db + 4 g + e
-    // of query j), so every access is one 16-byte vector.  In global memory the
-    // partial is query-major ([16 queries][d_latent]), so that the merge reads
-    // one query's latent as contiguous memory.
+    // Partial state layout in LDS: block b of the latent of pair c holds, per
+    // lane, the 4 values of acc (MFMA result layout: lane (g, j) has dims
+    // 16 b + 4 g + e of query j), so every access is one 16-byte vector.  In
+    // global memory the partial is query-major ([16 queries][d_latent]), so
+    // that the merge reads one query's latent as contiguous memory.
+    const int DB = dc / 16;
     f32x4* mb = reinterpret_cast<f32x4*>(smem);                 // [4][DB][64]
     float* ml = reinterpret_cast<float*>(smem) + 4 * DB * 64 * 4;   // [8][64][2]
     ml[(w * 64 + lane) * 2] = m_run;
@@ -621,27 +656,14 @@ __device__ __forceinline__ void phase_attention(const LayerParams& p, int L, cha
     __syncthreads();
     float M = -INFINITY;
 #pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, ml[(ww * 64 + lane) * 2]);
+    for (int cc = 0; cc < 4; ++cc) M = fmaxf(M, ml[(2 * cc * 64 + lane) * 2]);
     const float sw = M == -INFINITY ? 0.f : __expf(m_run - M);
-    if (w >= 4) {
-      f32x4* zb = mb + (long long)(w - 4) * DB * 64;
+    {
+      const int DBh = EXACT ? DBH : nl * PB;
+      f32x4* zb = mb + ((long long)cg * DB + l0 * PB) * 64;
 #pragma unroll
-      for (int db = 0; db < DBMAX; ++db)
-        if (db < DB) zb[db * 64 + lane] = acc[db] * sw;
-    }
-    __syncthreads();
-    if (w < 4) {
-      f32x4* zb = mb + (long long)w * DB * 64;
-#pragma unroll
-      for (int d0 = 0; d0 < DBMAX; d0 += 8) {
-        f32x4 t[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          if (d0 + i < DB) t[i] = zb[(d0 + i) * 64 + lane];
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          if (d0 + i < DB) zb[(d0 + i) * 64 + lane] = acc[d0 + i] * sw + t[i];
-      }
+      for (int db = 0; db < DBH; ++db)
+        if (db < DBh) zb[db * 64 + lane] = acc[db] * sw;
     }
     __syncthreads();
     {
@@ -665,9 +687,9 @@ __device__ __forceinline__ void phase_attention(const LayerParams& p, int L, cha
     if (w == 0 && g == 0) {
       float Ls = 0.f;
 #pragma unroll
-      for (int ww = 0; ww < kWaves; ++ww) {
-        const float mw = ml[(ww * 64 + lane) * 2];
-        Ls += mw == -INFINITY ? 0.f : ml[(ww * 64 + lane) * 2 + 1] * __expf(mw - M);
+      for (int cc = 0; cc < 4; ++cc) {
+        const float mw = ml[(2 * cc * 64 + lane) * 2];
+        Ls += mw == -INFINITY ? 0.f : ml[(2 * cc * 64 + lane) * 2 + 1] * __expf(mw - M);
       }
       p.att_ml[((long long)u * 16 + j) * 2] = M;
       p.att_ml[((long long)u * 16 + j) * 2 + 1] = Ls;

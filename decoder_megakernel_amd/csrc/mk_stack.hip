@@ -101,7 +101,7 @@ __global__ __launch_bounds__(kThreads, 1) void head_kernel(HeadArgs a) {
   wg_release_begin();
   int* flag = reinterpret_cast<int*>(misc + 250);
   if (threadIdx.x == 0) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    release_agent();
     const uint32_t old = __hip_atomic_fetch_add(a.counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const int last = old == gridDim.x - 1;
     if (last) {
