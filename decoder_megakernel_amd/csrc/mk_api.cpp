@@ -43,8 +43,8 @@ struct Dims {
 };
 
 // s_q: the projection's split-K factor of the schedule (0 when not known yet).
-LayerKernelFn kernel_of(const Dims& D, int s_q = 0) {
-  return layer_kernel_for(D.af, D.ef, D.kf, D.d, D.nh, D.dh, D.dc, D.dr, D.E, D.topk, D.nshared, D.f, s_q);
+LayerKernelFn kernel_of(const Dims& D, int s_q = 0, int nwg = 0) {
+  return layer_kernel_for(D.af, D.ef, D.kf, D.d, D.nh, D.dh, D.dc, D.dr, D.E, D.topk, D.nshared, D.f, s_q, nwg);
 }
 
 Dims dims_of(const mk_layer_config* c) {
@@ -236,6 +236,7 @@ StLayout st_layout(const Dims& D, const Schedule& s) {
 Schedule make_schedule(const Dims& D, int nwg) {
   Schedule s;
   s.nwg = nwg;
+  s.grid_min = 0;
   const int KTa = D.d / tile_k(D.af);
   s.s_q = choose_split(D.nq / 16 + (D.kvw + 15) / 16, KTa, nwg);
   return s;
@@ -293,7 +294,7 @@ int mk_query_device(int hip_device, mk_device_info* out) {
   HIP_OK(hipGetDeviceCount(&n));
   if (hip_device < 0 || hip_device >= n) return fail(MK_ERR_INVALID_ARG, "no HIP device %d", hip_device);
   DevInfo di;
-  LayerKernelFn fn = layer_kernel_for(MK_FMT_BF16, MK_FMT_FP8_B128, MK_FMT_BF16, 4096, 32, 128, 512, 64, 384, 8, 1, 2048, 0);
+  LayerKernelFn fn = layer_kernel_for(MK_FMT_BF16, MK_FMT_FP8_B128, MK_FMT_BF16, 4096, 32, 128, 512, 64, 384, 8, 1, 2048, 0, 0);
   hipDeviceProp_t prop;
   HIP_OK(hipGetDeviceProperties(&prop, hip_device));
   out->hip_device = hip_device;
@@ -435,7 +436,7 @@ int mk_layer_init(const mk_layer_config* cfg, const mk_layer_weights* w, void* s
   L->sl = st_layout(D, L->sch);
   L->state = (char*)state_dev;
   L->ws = (char*)workspace_dev;
-  L->fn = kernel_of(D, L->sch.s_q);   // the instance for this schedule (same occupancy)
+  L->fn = kernel_of(D, L->sch.s_q, L->sch.nwg);   // the instance for this schedule (same occupancy)
   L->trace_on = 0;
   L->timeout_us = 2000000;
   L->steps = L->launches = 0;

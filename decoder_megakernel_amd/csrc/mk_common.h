@@ -65,7 +65,11 @@ struct alignas(256) BarrierState {
 struct Schedule {
   int nwg;                 // persistent grid (all co-resident)
   int s_q;                 // k-splits of the Q / latent-KV projection
+  int grid_min;            // a lower bound of nwg fixed at compile time (0: none)
 };
+// Instances for fixed layer shapes assume at least this many workgroups (one
+// per CU on MI355X), so that choices depending on the grid size fold.
+constexpr int kSpecMinGrid = 256;
 
 // Kernel parameters (passed by value).
 struct LayerParams {

@@ -6,10 +6,11 @@ namespace mk {
 
 typedef void (*LayerKernelFn)(LayerParams);
 // The kernel instance for a layer's formats and dimensions (null if none).
-// s_q is the schedule's split-K factor of the projection (0: not known yet; an
-// instance is returned whenever one exists for some factor).
+// s_q is the schedule's split-K factor of the projection and nwg its grid size
+// (0: not known yet; an instance is returned whenever one exists for some
+// factor and grid).
 LayerKernelFn layer_kernel_for(int af, int ef, int kf, int d, int nh, int dh, int dc, int dr, int E, int topk,
-                               int nshared, int f, int s_q);
+                               int nshared, int f, int s_q, int nwg);
 
 int launch_pack(const void* src, int fmt, int nb, int R, int K, long long sb, long long sr, long long sk,
                 void* dst, long long dst_stride, long long dst_off, hipStream_t stream);

@@ -1148,7 +1148,7 @@ __device__ __forceinline__ void gateup_units(const LayerParams& p, const uint8_t
 // beyond the router's E/16 units, those run the shared experts' gate/up in the
 // router phase (into slots 0 .. n_shared-1).
 __device__ __forceinline__ bool shared_early(const LayerParams& p) {
-  return p.nshared > 0 && (int)gridDim.x > p.E / 16;
+  return p.nshared > 0 && (p.sch.grid_min > p.E / 16 || (int)gridDim.x > p.E / 16);
 }
 
 // ------------------------------------------------------------------ P5 router
@@ -1597,6 +1597,7 @@ __device__ __forceinline__ void specialise(LayerParams& p) {
     p.qw = s.dh + s.dr; p.kvw = s.dc + s.dr; p.nq = s.nh * (s.dh + s.dr);
     p.E = s.E; p.topk = s.topk; p.nshared = s.nshared; p.f = s.f;
     p.sch.s_q = s.s_q;
+    p.sch.grid_min = kSpecMinGrid;
   }
 }
 
@@ -1629,7 +1630,8 @@ __global__ __launch_bounds__(kThreads, 1) void layer_kernel(LayerParams p) {
   {
     // absorbed-query units on waves [0, wa) of every workgroup; when they fit
     // in half the waves, RoPE / KV insert runs on the other half meanwhile
-    const int wa = (p.nh * (p.dc / 16) + (int)gridDim.x - 1) / (int)gridDim.x;
+    const int gs = p.sch.grid_min > 0 ? p.sch.grid_min : (int)gridDim.x;   // never above the grid
+    const int wa = (p.nh * (p.dc / 16) + gs - 1) / gs;
     if (wa <= kWaves / 2) {
       if ((int)threadIdx.x < kThreads / 2) phase_absorb<AF>(p);
       else phase_rope_kv<KF>(p, L, blockIdx.x * (kThreads / 2) + threadIdx.x - kThreads / 2,
@@ -1671,12 +1673,12 @@ __global__ __launch_bounds__(kThreads, 1) void layer_kernel(LayerParams p) {
 // attention loop bounds are constants too).
 typedef void (*LayerKernelFn)(LayerParams);
 LayerKernelFn layer_kernel_for(int af, int ef, int kf, int d, int nh, int dh, int dc, int dr, int E, int topk,
-                               int nshared, int f, int s_q) {
+                               int nshared, int f, int s_q, int nwg) {
   const int kvw = dc + dr;
   auto is = [&](int i) {
     const SpecShape& s = kSpecShapes[i];
     return d == s.d && nh == s.nh && dh == s.dh && dc == s.dc && dr == s.dr && E == s.E && topk == s.topk &&
-           nshared == s.nshared && f == s.f && (s_q == 0 || s_q == s.s_q);
+           nshared == s.nshared && f == s.f && (s_q == 0 || s_q == s.s_q) && (nwg == 0 || nwg >= kSpecMinGrid);
   };
   if (af == MK_FMT_F32 && ef == MK_FMT_F32 && kf == MK_FMT_F32 && kvw <= 160 && dc <= 128)
     return layer_kernel<MK_FMT_F32, MK_FMT_F32, MK_FMT_F32, 10, 8, false, 0>;
