@@ -6,6 +6,7 @@
 #include <algorithm>
 #include <cstdarg>
 #include <cstdio>
+#include <cmath>
 #include <cstring>
 #include <new>
 #include <string>
@@ -459,6 +460,7 @@ int mk_layer_init(const mk_layer_config* cfg, const mk_layer_weights* w, void* s
   p.eps = cfg->rms_eps;
   p.scale = (float)(1.0 / std::sqrt((double)(D.dh + D.dr)));
   p.rope_base = (double)cfg->rope_base;
+  p.rope_step = std::pow((double)cfg->rope_base, -2.0 / (double)D.dr);
   p.g1 = w->gamma1; p.g2 = w->gamma2;
   p.wq = (const uint8_t*)w->wq; p.wdkv = (const uint8_t*)w->wdkv; p.wuk = (const uint8_t*)w->wuk;
   p.wuv = (const uint8_t*)w->wuv; p.wo = (const uint8_t*)w->wo; p.wr = (const uint8_t*)w->wr;

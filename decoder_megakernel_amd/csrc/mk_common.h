@@ -79,6 +79,7 @@ struct LayerParams {
   const int32_t* L_dev;    // ... or read from device memory when non-null
   float eps, scale;
   double rope_base;
+  double rope_step;        // rope_base^(-2 / d_rope): pair i turns by pos * rope_step^i radians
   // tensors
   const float* H;          // [T][d]
   float* out;              // [T][d]

@@ -123,7 +123,8 @@ template <> __device__ __forceinline__ f32x4 round4<__bf16>(const f32x4& v) {
 // LDS as the MFMA operand type, row stride XS.  Wave w holds the float4
 // columns w*64 + lane + 512 c of every row, so a lane keeps at most
 // kMaxT x kRowCh float4s and the gain slice they share.  With NORM each row is
-// RMS-normalised on the way, x = (h * (1/sqrt(mean(h^2) + eps))) * gamma: the
+// RMS-normalised on the way, x = (h * rsqrt(mean(h^2) + eps)) * gamma (the
+// VALU's reciprocal square root instruction, about 1 ulp): the
 // waves' partial sums of squares meet in LDS and are added in wave order.
 // `lo` (optional) receives the remainder x - round(x) for the router's split
 // operand.
@@ -161,6 +162,7 @@ struct RowStager {
     const int n4 = K / 4;
     float r[kMaxT];
     if constexpr (NORM) {
+      const float invK = 1.0f / (float)K;
       float ss[kMaxT];
 #pragma unroll
       for (int t = 0; t < kMaxT; ++t) {
@@ -184,7 +186,7 @@ struct RowStager {
         float ss = 0.f;
 #pragma unroll
         for (int ww = 0; ww < kWaves; ++ww) ss += part[ww * kMaxT + t];
-        r[t] = 1.0f / sqrtf(ss / (float)K + eps);
+        r[t] = __builtin_amdgcn_rsqf(ss * invK + eps);
       }
     }
 #pragma unroll
@@ -307,13 +309,44 @@ __device__ __forceinline__ void phase_qkv(const LayerParams& p, char* smem) {
 }
 
 // ------------------------------------------------------------------ P1
-__device__ __forceinline__ void rope_pair(float& v0, float& v1, long long pos, int pidx, int dr, double base) {
-  const double th = pow(base, -2.0 * (double)pidx / (double)dr);
-  const double a = (double)pos * th;
-  const float c = (float)cos(a), s = (float)sin(a);
-  const float x0 = v0, x1 = v1;
-  v0 = x0 * c - x1 * s;
-  v1 = x0 * s + x1 * c;
+// sin and cos of 2 pi x for |x| <= 1/2 (x in turns), in fp64: x is split into
+// the nearest quarter turn n/4 and g = x - n/4 in [-1/8, 1/8], the Taylor
+// series of sin and cos at t = 2 pi g (|t| <= pi/4) are summed to t^17 and t^16
+// (remainders below 1e-17), and the quarter turn swaps and negates the pair.
+__device__ __forceinline__ void sincos_turns(double x, double& sn, double& cs) {
+  const double n = rint(4.0 * x);
+  const double t = (x - 0.25 * n) * 6.283185307179586476925286766559;
+  const double t2 = t * t;
+  double ps = 0.0, pc = 0.0;
+  double fs = 1.0 / 355687428096000.0;        // 1/17!
+  double fc = 1.0 / 20922789888000.0;         // 1/16!
+#pragma unroll
+  for (int k = 8; k >= 0; --k) {
+    ps = ps * t2 + ((k & 1) ? -fs : fs);
+    pc = pc * t2 + ((k & 1) ? -fc : fc);
+    fs *= (double)((2 * k + 1) * (2 * k));    // 1/(2k+1)! -> 1/(2k-1)!
+    fc *= (double)((2 * k) * (2 * k - 1));    // 1/(2k)!   -> 1/(2k-2)!
+  }
+  const double s0 = ps * t, c0 = pc;
+  const int q = (int)n & 3;
+  sn = q == 0 ? s0 : q == 1 ? c0 : q == 2 ? -s0 : -c0;
+  cs = q == 0 ? c0 : q == 1 ? -s0 : q == 2 ? -c0 : s0;
+}
+
+// Rotation of pair i at position pos by the angle pos * rope_base^(-2i/d_rope):
+// the frequency is rope_step^i (square-and-multiply in fp64), the angle is
+// taken in turns and reduced to [-1/2, 1/2] in fp64 before sin and cos.
+__device__ __forceinline__ void rope_cs(long long pos, int pidx, double step, float& c, float& s) {
+  double th = 1.0, b = step;
+  for (int e = pidx; e > 0; e >>= 1) {
+    if (e & 1) th *= b;
+    b *= b;
+  }
+  const double x = (double)pos * (th * 0.15915494309189533576888376337251);   // / (2 pi)
+  double sn, cs;
+  sincos_turns(x - rint(x), sn, cs);
+  c = (float)cs;
+  s = (float)sn;
 }
 
 template <int KF>
@@ -335,10 +368,17 @@ __device__ __forceinline__ void phase_rope_kv(const LayerParams& p, int L, int t
       float v = psum(t, p.nq + r);
       if (KF == MK_FMT_F32) reinterpret_cast<float*>(p.kv)[pos * p.kvw + r] = v;
       else reinterpret_cast<__bf16*>(p.kv)[pos * p.kvw + r] = (__bf16)v;
-    } else if (r < p.dc + dr2) {
-      const int pi = r - p.dc;
-      float v0 = psum(t, p.nq + p.dc + 2 * pi), v1 = psum(t, p.nq + p.dc + 2 * pi + 1);
-      rope_pair(v0, v1, pos, pi, p.dr, p.rope_base);
+      continue;
+    }
+    // a RoPE pair: of the key (k^R, into the cache) or of head h's query
+    const bool key = r < p.dc + dr2;
+    const int q = r - p.dc - dr2, h = key ? 0 : q / dr2, pi = key ? r - p.dc : q - h * dr2;
+    const int src = key ? p.nq + p.dc + 2 * pi : h * p.qw + p.dh + 2 * pi;
+    const float x0 = psum(t, src), x1 = psum(t, src + 1);
+    float c, sn;
+    rope_cs(pos, pi, p.rope_step, c, sn);
+    const float v0 = x0 * c - x1 * sn, v1 = x0 * sn + x1 * c;
+    if (key) {
       const long long o = pos * p.kvw + p.dc + 2 * pi;
       if (KF == MK_FMT_F32) {
         reinterpret_cast<float*>(p.kv)[o] = v0;
@@ -348,10 +388,6 @@ __device__ __forceinline__ void phase_rope_kv(const LayerParams& p, int L, int t
         reinterpret_cast<__bf16*>(p.kv)[o + 1] = (__bf16)v1;
       }
     } else {
-      const int q = r - p.dc - dr2, h = q / dr2, pi = q - h * dr2;
-      const int base = h * p.qw + p.dh + 2 * pi;
-      float v0 = psum(t, base), v1 = psum(t, base + 1);
-      rope_pair(v0, v1, pos, pi, p.dr, p.rope_base);
       p.qrope[((long long)t * p.nh + h) * p.dr + 2 * pi] = v0;
       p.qrope[((long long)t * p.nh + h) * p.dr + 2 * pi + 1] = v1;
     }
