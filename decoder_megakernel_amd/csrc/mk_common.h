@@ -39,15 +39,20 @@ __host__ __device__ constexpr int elem_bytes(int fmt) { return fmt == MK_FMT_F32
 // Per-layer device state (persistent across steps; zeroed at init).
 // The grid barrier is two-level: workgroups arrive on the counter of their
 // group of kBarGroup consecutive workgroups; the last of a group arrives on
-// `top`; the last group leader advances `gen`.  Counters only ever grow (the
-// last arriver is the one whose arrival makes the count a multiple of the
-// group size), so nothing is reset between barriers or launches.
+// `top`; the last group leader advances `gen`, which releases everyone.  The
+// 32-bit counters only grow (wrapping), and every barrier adds a power of two
+// to each: kBarGroup to a group counter (the first workgroup of a smaller last
+// group adds the missing arrivals), and the next power of two >= the number of
+// groups to `top` (group 0's leader adds the missing ones).  The last arriver
+// is the one whose addition makes the count a multiple of that power, so
+// nothing is reset between barriers or launches.
 constexpr int kBarGroup = 16;
+static_assert((kBarGroup & (kBarGroup - 1)) == 0, "the group size must be a power of two");
 constexpr int kMaxBarGroups = 64;        // grids of up to 1024 workgroups
 constexpr int kMaxGrid = kBarGroup * kMaxBarGroups;
 struct alignas(256) BarrierLine {
-  unsigned long long n;
-  uint32_t pad[62];
+  uint32_t n;
+  uint32_t pad[63];
 };
 struct alignas(256) BarrierState {
   uint32_t gen;

@@ -163,13 +163,17 @@ __device__ __forceinline__ bool grid_barrier(const LayerParams& p, int idx, int*
       // the generation is read (and waited for) before this workgroup arrives
       const uint32_t g = __hip_atomic_load(&b->gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       release_agent();
-      const int nwg = (int)gridDim.x, grp = (int)blockIdx.x / kBarGroup;
-      const int ngrp = (nwg + kBarGroup - 1) / kBarGroup;
-      const unsigned long long gsz = (unsigned long long)min(kBarGroup, nwg - grp * kBarGroup);
+      const uint32_t nwg = gridDim.x, grp = blockIdx.x / kBarGroup;
+      const uint32_t ngrp = (nwg + kBarGroup - 1) / kBarGroup;
+      const uint32_t gsz = min((uint32_t)kBarGroup, nwg - grp * kBarGroup);
+      const uint32_t add = blockIdx.x % kBarGroup == 0 ? kBarGroup - gsz + 1 : 1u;
+      const uint32_t tpow = ngrp > 1 ? 1u << (32 - __builtin_clz(ngrp - 1)) : 1u;
+      const uint32_t tadd = grp == 0 ? tpow - ngrp + 1 : 1u;
       bool last = false;
-      if ((__hip_atomic_fetch_add(&b->grp[grp].n, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1) % gsz == 0)
-        last = (__hip_atomic_fetch_add(&b->top.n, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1) %
-                   (unsigned long long)ngrp == 0;
+      if (((__hip_atomic_fetch_add(&b->grp[grp].n, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + add) &
+           (kBarGroup - 1)) == 0)
+        last = ((__hip_atomic_fetch_add(&b->top.n, tadd, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + tadd) &
+                (tpow - 1)) == 0;
       if (last) {
         __hip_atomic_fetch_add(&b->gen, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       } else {
@@ -711,6 +715,11 @@ __device__ __forceinline__ void run_stream_dyn(int U, int NT, int T, const Src& 
         sc[r] = ldg(nsp + (has_next ? (((tn + r) * TK) >> 7) : 0));
         if constexpr (DUAL) sc2[r] = ldg(nsp2 + (has_next ? (((tn + r) * TK) >> 7) : 0));
       }
+      // tile r's next load leaves before tile r + 1 is used: the loads stay in
+      // the order they are consumed, so each wait is for one tile and D tiles
+      // stay in flight (left to itself the scheduler bunches the loads late
+      // and an early tile then waits for nearly the whole chunk)
+      __builtin_amdgcn_sched_barrier(0);
     }
     cc = ncc;
     if (ncc != 0) continue;

@@ -94,10 +94,10 @@ __device__ __forceinline__ void wave_sums(float (&v)[N]) {
   for (int i = 0; i < N; ++i) v[i] += u[i];
 }
 
+// [a, b) = the i-th of `parts` near-equal slices of [0, total) (total * parts < 2^32)
 __device__ __forceinline__ void split_range(int total, int parts, int i, int& a, int& b) {
-  long long q = (long long)total * i / parts, r = (long long)total * (i + 1) / parts;
-  a = (int)q;
-  b = (int)r;
+  a = (int)((unsigned)total * (unsigned)i / (unsigned)parts);
+  b = (int)((unsigned)total * (unsigned)(i + 1) / (unsigned)parts);
 }
 
 template <class A> __device__ inline A to_act(float v);
@@ -1287,9 +1287,11 @@ __device__ __forceinline__ void phase_route_gateup(const LayerParams& p, char* s
 // QP = d_model / 64: four row tiles times all KT tiles of W2.  Wave w streams
 // row tile 4 (u % QP) + (w & 3) over K half w >> 2 (KT / 2 tiles in chunks of
 // D, the next chunk requested while the current one is multiplied, across unit
-// boundaries), and waves w and w + 4 add their blocks in LDS.  Units are handed
-// out as in run_stream_dyn: workgroup b takes units b and b + nwg, then draws
-// tickets, so workgroups on faster XCDs take more units.
+// boundaries), and waves w and w + 4 add their blocks in LDS.  Workgroup b
+// first takes a run of R = min(8, units / nwg) consecutive units starting at
+// b R (one slot, so its rows are loaded once), then draws tickets for the rest
+// as run_stream_dyn does, so workgroups on faster XCDs take more units and the
+// last units are spread over the grid.
 //
 // The rows of a unit's slot (h, T x d_ff in the operand type) sit in one of two
 // LDS buffers.  When the next unit's slot differs, its rows are requested at the
@@ -1344,8 +1346,19 @@ __device__ __forceinline__ bool phase_down_dyn(const LayerParams& p, char* smem,
   int* seq = seq_lds();
   int* flag = reinterpret_cast<int*>(smem + kFlagOff);
   const float* dsc = reinterpret_cast<const float*>(p.dummy);
-  int cur = (int)blockIdx.x < U ? (int)blockIdx.x : -1;
-  int nxt = (int)blockIdx.x + nwg < U ? (int)blockIdx.x + nwg : -1;
+  // This workgroup's first RS units are fixed: a run of R consecutive units
+  // (four row tiles each, all in one slot when R divides d_model / 64) when
+  // there are at least two per workgroup, else units b and b + nwg; the rest
+  // come from the tickets.  Consecutive units of one slot share its rows.
+  const int R = min(8, U / nwg);
+  const int RS = R >= 2 ? R : 2;
+  auto static_unit = [&](int k) {
+    const int u = R >= 2 ? (int)blockIdx.x * R + k : (int)blockIdx.x + k * nwg;
+    return u < U ? u : -1;
+  };
+  int cur = static_unit(0);
+  int nxt = static_unit(1);
+  int kk = 0;                                              // cur's place in this workgroup's sequence
   if (cur < 0 || cps <= 0) return true;
   const int n32 = T * f * (int)sizeof(A) / 4;             // dwords of one slot's rows
   const int rw = f * (int)sizeof(A) / 4;                  // dwords of one row
@@ -1427,7 +1440,8 @@ __device__ __forceinline__ bool phase_down_dyn(const LayerParams& p, char* smem,
         hb ^= 1;
       }
       if (threadIdx.x == 0) {
-        tk = __hip_atomic_fetch_add(ctr + kCntStride * cq, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (kk + 2 >= RS)
+          tk = __hip_atomic_fetch_add(ctr + kCntStride * cq, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const int ns2 = nxt >= 0 ? nxt / QP : 0;
         cseen = (nxt >= 0 && ns2 != cur / QP && ns2 >= s_wait)
                     ? __hip_atomic_load(scnt + kSlotStride * ns2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
@@ -1457,6 +1471,7 @@ __device__ __forceinline__ bool phase_down_dyn(const LayerParams& p, char* smem,
       buf[rr] = ld_stream16(nb + rr * 1024);
       if constexpr (EF == MK_FMT_FP8_B128)
         sc[rr] = ldg(nsp + (has_next ? (((kp * NTh + ncc * D + rr) * TK) >> 7) : 0));
+      __builtin_amdgcn_sched_barrier(0);   // loads in consumption order (see run_stream_dyn)
     }
     cc = ncc;
     if (ncc != 0) continue;
@@ -1465,13 +1480,17 @@ __device__ __forceinline__ bool phase_down_dyn(const LayerParams& p, char* smem,
     float* rb = red + par * (kWaves * 64 * 4);
     *reinterpret_cast<f32x4*>(rb + (w * 64 + lane) * 4) = acc;
     if (threadIdx.x == 0) {
-      long long un2 = 2LL * nwg + 8LL * tk + cq;
-      for (int tries = 1; un2 >= U && tries < 8; ++tries) {
-        cq = (cq + 1) & 7;
-        tk = __hip_atomic_fetch_add(ctr + kCntStride * cq, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        un2 = 2LL * nwg + 8LL * tk + cq;
+      if (kk + 2 < RS) {
+        seq[par] = static_unit(kk + 2);
+      } else {
+        long long un2 = (long long)RS * nwg + 8LL * tk + cq;
+        for (int tries = 1; un2 >= U && tries < 8; ++tries) {
+          cq = (cq + 1) & 7;
+          tk = __hip_atomic_fetch_add(ctr + kCntStride * cq, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          un2 = (long long)RS * nwg + 8LL * tk + cq;
+        }
+        seq[par] = un2 < U ? (int)un2 : -1;
       }
-      seq[par] = un2 < U ? (int)un2 : -1;
       *flag = (nxt >= 0 && nxt / QP != cur / QP) ? slot_ready(nxt / QP, cseen) : 1;
     }
     __syncthreads();
@@ -1485,15 +1504,15 @@ __device__ __forceinline__ bool phase_down_dyn(const LayerParams& p, char* smem,
         yb[((long long)sl * T + col) * d + rt * 16 + row] = v;
       }
     }
-    // the next unit's rows, when its slot differs; requested either way (the
-    // current slot's rows again) so that the loads in flight never depend on a
-    // branch
+    // the next unit's rows, when its slot differs (they are waited for when
+    // it starts, together with every older load)
     hpend = nxt >= 0 && nxt / QP != cur / QP;
-    h_load(hpend ? nxt / QP : cur / QP, hv);
+    if (hpend) h_load(nxt / QP, hv);
     acc = zero;
     cur = nxt;
     nxt = nxt >= 0 ? seq[par] : -1;
     par ^= 1;
+    ++kk;
     if (cur < 0) break;
   }
   __syncthreads();
