@@ -928,80 +928,64 @@ __device__ __forceinline__ unsigned long long lanemask_lt() {
 
 // Top-k by logit (ties to the lower index) and gates = selected softmax
 // probabilities renormalised (the normaliser over all experts cancels, so the
-// gates are exp(l - m) / sum over the selection of exp(l' - m)); then the slot
-// list: the shared experts first, then the distinct selected experts in
-// ascending order.  Wave t < T handles token t from the candidates the router
-// workgroups kept (the top min(k, 16) of every 16 experts, which contain the
-// overall top k), laid out in ascending expert order, held in registers (lane
-// l holds candidates l, l + 64, ...; absent ones get key 0, below every real
-// key): the k-th largest key is found bit by bit (32 ballot/popcount rounds),
-// then the candidates above it, plus the lowest-indexed ones equal to it, are
-// compacted in ascending expert order.
-template <int EPL>
+// gates are exp(l - m) / sum over the selection of exp(l' - m), m the largest
+// selected logit).  Wave t < T handles token t: lane u < E/16 holds the
+// candidates its router unit kept (the top min(k, 16) of 16 experts, which
+// together contain the overall top k), in descending order, and k rounds each
+// take the largest head among the lanes (the lowest lane on ties: lower units
+// hold lower experts) and advance that lane's list.  The selection is written
+// in descending order of logit.
+template <int K8M>
 __device__ __forceinline__ void route_cands(const LayerParams& p, const RouteLds& r) {
-  const int K = p.topk, K8 = min(K, 16), RT = p.E / 16, NC = RT * K8;
+  const int K = p.topk, K8 = min(K, 16), RT = p.E / 16;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const float* cv = p.route_cand + (long long)w * RT * 16;
-  const int* ci = reinterpret_cast<const int*>(p.route_cand) + ((long long)p.T + w) * RT * 16;
-  float lv[EPL];
-  int id[EPL];
+  const float* cv = p.route_cand + ((long long)w * RT + min(lane, RT - 1)) * 16;
+  const int* ci = reinterpret_cast<const int*>(p.route_cand) + ((long long)(p.T + w) * RT + min(lane, RT - 1)) * 16;
+  float lv[K8M];
+  int id[K8M];
+  uint32_t key[K8M];
 #pragma unroll
-  for (int i = 0; i < EPL; ++i) {
-    const int c = min(lane + 64 * i, NC - 1);
-    const int o = (c / K8) * 16 + c % K8;
-    lv[i] = ldg(cv + o);
-    id[i] = ldg(ci + o);
+  for (int i = 0; i < K8M; ++i) {
+    lv[i] = ldg(cv + min(i, K8 - 1));
+    id[i] = ldg(ci + min(i, K8 - 1));
   }
-  float mx = -INFINITY;
 #pragma unroll
-  for (int i = 0; i < EPL; ++i) mx = fmaxf(mx, lv[i]);   // clamped duplicates do not change the max
-  mx = wave_max(mx);
+  for (int i = 0; i < K8M; ++i) key[i] = lane < RT && i < K8 ? fkey(lv[i]) : 0u;   // 0: below every logit
   trace_x(p, 12);
-  uint32_t key[EPL];
+  float m0 = 0.f, ps = 0.f, myv = 0.f;
+  for (int k = 0; k < K; ++k) {
+    const uint32_t hk = key[0];
+    uint32_t mx = hk;
+    mx = max(mx, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mx, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+    mx = max(mx, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mx, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+    mx = max(mx, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mx, 0x124, 0xF, 0xF, false));  // row_ror:4
+    mx = max(mx, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mx, 0x128, 0xF, 0xF, false));  // row_ror:8
+    mx = max(mx, (uint32_t)__shfl_xor((int)mx, 16));
+    mx = max(mx, (uint32_t)__shfl_xor((int)mx, 32));
+    const int wl = __ffsll((long long)__ballot(hk == mx)) - 1;
+    const float v = __shfl(lv[0], wl);
+    const int e = __shfl(id[0], wl);
+    if (k == 0) m0 = v;
+    const float ex = __expf(v - m0);
+    ps += ex;
+    if (lane == k) myv = ex;
+    if (lane == 0) r.sel[w * kMaxTopK + k] = e;
+    // the winning lane's next candidate moves up
+    const bool win = lane == wl;
 #pragma unroll
-  for (int i = 0; i < EPL; ++i) key[i] = lane + 64 * i < NC ? fkey(lv[i]) : 0u;
-  uint32_t thr = 0u;                    // the K-th largest key
-  for (int b = 31; b >= 0; --b) {
-    const uint32_t cand = thr | (1u << b);
-    int cnt = 0;
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) cnt += __popcll(__ballot(key[i] >= cand));
-    if (cnt >= K) thr = cand;
-  }
-  int n_gt = 0;
-#pragma unroll
-  for (int i = 0; i < EPL; ++i) n_gt += __popcll(__ballot(key[i] > thr));
-  const int need_eq = K - n_gt;
-  const unsigned long long lt = lanemask_lt();
-  int base_eq = 0, base = 0;
-  float ps = 0.f;
-  bool sel[EPL];
-  float ex[EPL];
-#pragma unroll
-  for (int i = 0; i < EPL; ++i) {
-    const unsigned long long meq = __ballot(key[i] == thr);
-    const int rank_eq = base_eq + __popcll(meq & lt);
-    base_eq += __popcll(meq);
-    sel[i] = key[i] > thr || (key[i] == thr && rank_eq < need_eq);
-    ex[i] = __expf(lv[i] - mx);
-    ps += sel[i] ? ex[i] : 0.f;
-  }
-  const float psel = wave_sum(ps);
-#pragma unroll
-  for (int i = 0; i < EPL; ++i) {
-    const unsigned long long m = __ballot(sel[i]);
-    if (sel[i]) {
-      const int k = base + __popcll(m & lt);
-      r.sel[w * kMaxTopK + k] = id[i];
-      r.gate[w * kMaxTopK + k] = ex[i] / psel;
+    for (int i = 0; i < K8M - 1; ++i) {
+      key[i] = win ? key[i + 1] : key[i];
+      lv[i] = win ? lv[i + 1] : lv[i];
+      id[i] = win ? id[i + 1] : id[i];
     }
-    base += __popcll(m);
+    if (win) key[K8M - 1] = 0u;
   }
+  if (lane < K) r.gate[w * kMaxTopK + lane] = myv / ps;
 }
 
 // Router workgroup, after its units: for every unit (16 experts) and token,
 // the biased logits (also written to the logits tap) and the top min(k, 16)
-// of the 16 by (logit, lower index), compacted in ascending expert order.
+// of the 16 by (logit, lower index), stored in that order (rank r at r).
 // lgl[unit - u0][t][16] holds the unit's unbiased logits.
 __device__ __forceinline__ void router_candidates(const LayerParams& p, const float* lgl, int u0, int u1) {
   const int T = p.T, E = p.E, K8 = min(p.topk, 16), RT = E / 16;
@@ -1017,11 +1001,8 @@ __device__ __forceinline__ void router_candidates(const LayerParams& p, const fl
         const uint32_t kj = __shfl(k, j, 16);
         rank += (kj > k || (kj == k && j < lane)) ? 1 : 0;
       }
-      const bool s = rank < K8;
-      const unsigned long long m = __ballot(s) & 0xFFFFull;
-      if (s) {
-        const int pos = __popcll(m & lanemask_lt());
-        const long long o = ((long long)w * RT + u) * 16 + pos;
+      if (rank < K8) {
+        const long long o = ((long long)w * RT + u) * 16 + rank;
         p.route_cand[o] = v;
         reinterpret_cast<int*>(p.route_cand)[(long long)T * RT * 16 + o] = e;
       }
@@ -1038,15 +1019,22 @@ __device__ __forceinline__ void router_candidates(const LayerParams& p, const fl
 __device__ __forceinline__ void route_local(const LayerParams& p, const RouteLds& r) {
   const int T = p.T, E = p.E, K = p.topk, S0 = p.nshared;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  // the expert block table, loaded into LDS (the logit area is free) while the
-  // token waves load their candidates
+  // the expert block table, requested into registers together with the token
+  // waves' candidates (one round trip for both) and stored into LDS (the logit
+  // area is free) afterwards
+  constexpr int kEt = (kMaxExperts + 1 + kThreads - 1) / kThreads;
   const uint8_t** etab = reinterpret_cast<const uint8_t**>(r.lg);
-  for (int i = threadIdx.x; i < E + S0; i += kThreads) etab[i] = p.experts[i];
+  const uint8_t* ev[kEt];
+#pragma unroll
+  for (int j = 0; j < kEt; ++j) ev[j] = p.experts[min((int)threadIdx.x + j * kThreads, E + S0 - 1)];
   for (int i = threadIdx.x; i < E; i += kThreads) r.flags[i] = 0;
   if (w < T) {
-    if ((E / 16) * min(K, 16) <= 256) route_cands<4>(p, r);
-    else route_cands<kMaxExperts / 64>(p, r);
+    if (K <= 8) route_cands<8>(p, r);
+    else route_cands<16>(p, r);
   }
+#pragma unroll
+  for (int j = 0; j < kEt; ++j)
+    if ((int)threadIdx.x + j * kThreads < E + S0) etab[threadIdx.x + j * kThreads] = ev[j];
   __syncthreads();
   trace_x(p, 13);
   if (threadIdx.x < T * K) {
