@@ -30,6 +30,32 @@ __device__ __forceinline__ u32x4 ld_stream16(const uint8_t* p) {
   return __builtin_nontemporal_load((gptr<u32x4>)(p));
 }
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *(gptr<u32x4>)(p); }
+// A zero in a vector register that the compiler cannot see through.  An
+// address offset by it counts as divergent, so its load is issued on the
+// vector memory path (and counted with the weight loads around it) even when
+// the address is the same for the whole wave.
+__device__ __forceinline__ int vzero() {
+  int z;
+  asm("v_mov_b32 %0, 0" : "=v"(z));
+  return z;
+}
+// A register copy the compiler keeps: the copy gets a register of its own, so
+// that the source register is free for the next value loaded into it (left to
+// itself the compiler may merge the two, and a load into a register still in
+// use then lands elsewhere and has to be moved back, after a wait for it).
+__device__ __forceinline__ float keep_copy(float x) {
+  float y;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(y) : "v"(x));
+  return y;
+}
+// Waits until the memory operation that produced x has returned (an
+// instruction that reads x, so the compiler's counter wait covers exactly that
+// operation and everything issued before it; an empty asm statement does not
+// count as a read).
+__device__ __forceinline__ void wait_for(uint32_t x) {
+  uint32_t y;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(y) : "v"(x));
+}
 
 // LDS transpose read (gfx950 ds_read_b64_tr_b16).  Within each group of 16
 // lanes, let D[i][k] be the k-th 16-bit element of the 8 bytes at lane i's
@@ -130,6 +156,20 @@ template <>
 __device__ __forceinline__ f32x4 tile_mma<MK_FMT_FP8_B128>(const u32x4& a, const __bf16* b, f32x4 acc) {
   acc = mma_bf16_k32(fp8x8_to_bf16(a[0], a[1]), *reinterpret_cast<const bf16x8*>(b), acc);
   acc = mma_bf16_k32(fp8x8_to_bf16(a[2], a[3]), *reinterpret_cast<const bf16x8*>(b + 8), acc);
+  return acc;
+}
+
+// The B operand of one fp8 tile (its two k32 halves), read from LDS ahead of
+// the product, and the product itself from registers.
+struct BPair {
+  bf16x8 lo, hi;
+};
+__device__ __forceinline__ BPair b_pair(const __bf16* b) {
+  return BPair{*reinterpret_cast<const bf16x8*>(b), *reinterpret_cast<const bf16x8*>(b + 8)};
+}
+__device__ __forceinline__ f32x4 tile_mma_fp8(const u32x4& a, const BPair& b, f32x4 acc) {
+  acc = mma_bf16_k32(fp8x8_to_bf16(a[0], a[1]), b.lo, acc);
+  acc = mma_bf16_k32(fp8x8_to_bf16(a[2], a[3]), b.hi, acc);
   return acc;
 }
 
@@ -632,10 +672,12 @@ __device__ __forceinline__ void run_stream(int u0, int u1, int NT, int T, const 
 //
 // With a Done callback (not NoDone), the epilogue works on row pairs instead:
 // epi(u, row0, col, v0, v2_0, v1, v2_1) for rows row0 and row0 + 1 (threads
-// < 128), which then wait until their stores have completed; after a
-// workgroup barrier thread 0 calls done(u).  Each wave keeps one chunk in
-// flight and the next unit's multiplications wait for that chunk anyway, so
-// the wait costs little.
+// < 128) writes them with value-returning atomics and returns the reply.  A
+// unit is published one unit later: at the end of the next unit every thread
+// uses the replies it holds (so it waits for those writes alone, not for the
+// chunk requested since, which a wait for all its memory operations would
+// drain), and after a workgroup barrier thread 0 calls done(u).  The last
+// unit is published when the stream ends.
 struct NoDone {
   __device__ void operator()(int) const {}
 };
@@ -659,15 +701,20 @@ __device__ __forceinline__ void run_stream_dyn(int U, int NT, int T, const Src& 
   u32x4 buf[D], buf2[D];
   float sc[D], sc2[D];
   {
+    // issued exactly as the loop issues a chunk (same order, scales on the
+    // vector path too), so that the loop's waits count the same loads whether
+    // it is entered from here or from its own end
     const uint8_t* cbase = src.base(cur) + lane * 16 + (long long)toff * STRIDE;
+    const int vz = vzero();
 #pragma unroll
     for (int r = 0; r < D; ++r) {
       buf[r] = ld_stream16(cbase + r * STRIDE);
       if constexpr (DUAL) buf2[r] = ld_stream16(cbase + r * STRIDE + 1024);
       if constexpr (FMT == MK_FMT_FP8_B128) {
-        sc[r] = ldg(src.sbase(cur) + (((toff + r) * TK) >> 7));
-        if constexpr (DUAL) sc2[r] = ldg(src.sbase2(cur) + (((toff + r) * TK) >> 7));
+        sc[r] = ldg(src.sbase(cur) + (((toff + r) * TK) >> 7) + vz);
+        if constexpr (DUAL) sc2[r] = ldg(src.sbase2(cur) + (((toff + r) * TK) >> 7) + vz);
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
   uint32_t tk = 0;
@@ -676,6 +723,16 @@ __device__ __forceinline__ void run_stream_dyn(int U, int NT, int T, const Src& 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   f32x4 acc2 = {0.f, 0.f, 0.f, 0.f};
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  // fp8: each tile's B operand is read one tile ahead (bn) and its scaled
+  // product is added one tile later (tp * sp), so neither the LDS latency nor
+  // the MFMA latency lies between a tile's arrival and the request of its
+  // successor; the sums are formed in the same order as without the delay
+  BPair bn;
+  f32x4 tp = zero, tp2 = zero;
+  float sp = 0.f, sp2 = 0.f;
+  if constexpr (FMT == MK_FMT_FP8_B128) bn = b_pair(src.bbase(cur) + toff * TK);
+  uint32_t reply = 0;               // row-pair epilogue: the reply of this thread's last write
+  int prev = -1;                    // row-pair epilogue: the unit written but not yet published
   while (true) {
     if (cc == 0 && threadIdx.x == 0)
       tk = __hip_atomic_fetch_add(ctr + kCntStride * cq, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -699,11 +756,17 @@ __device__ __forceinline__ void run_stream_dyn(int U, int NT, int T, const Src& 
 #pragma unroll
     for (int r = 0; r < D; ++r) {
       if constexpr (FMT == MK_FMT_FP8_B128) {
-        const f32x4 tmp = tile_mma<FMT>(buf[r], bp + r * TK, zero);
-        acc += tmp * sc[r];
+        const BPair b = bn;
+        bn = b_pair(r + 1 < D ? bp + (r + 1) * TK : (has_next ? src.bbase(un) + tn * TK : bp));
+        const f32x4 tmp = tile_mma_fp8(buf[r], b, zero);
+        acc += tp * sp;
+        tp = tmp;
+        sp = keep_copy(sc[r]);
         if constexpr (DUAL) {
-          const f32x4 tmp2 = tile_mma<FMT>(buf2[r], bp + r * TK, zero);
-          acc2 += tmp2 * sc2[r];
+          const f32x4 tmp2 = tile_mma_fp8(buf2[r], b, zero);
+          acc2 += tp2 * sp2;
+          tp2 = tmp2;
+          sp2 = keep_copy(sc2[r]);
         }
       } else {
         acc = tile_mma<FMT>(buf[r], bp + r * TK, acc);
@@ -724,6 +787,16 @@ __device__ __forceinline__ void run_stream_dyn(int U, int NT, int T, const Src& 
     cc = ncc;
     if (ncc != 0) continue;
     // unit `cur` complete: reduce across the waves, publish the unit after nxt
+    if constexpr (FMT == MK_FMT_FP8_B128) {
+      acc += tp * sp;
+      tp = zero;
+      sp = 0.f;
+      if constexpr (DUAL) {
+        acc2 += tp2 * sp2;
+        tp2 = zero;
+        sp2 = 0.f;
+      }
+    }
     float* rb = red + (par ? UnitRed<FMT, DUAL>::kFloats : 0);
     *reinterpret_cast<f32x4*>(rb + (w * 64 + lane) * 4) = acc;
     if constexpr (DUAL) *reinterpret_cast<f32x4*>(rb + kWaves * 64 * 4 + (w * 64 + lane) * 4) = acc2;
@@ -752,6 +825,9 @@ __device__ __forceinline__ void run_stream_dyn(int U, int NT, int T, const Src& 
         }
       }
     } else {
+      // the previous unit's writes have completed once their replies are here
+      // (used before this unit's writes reuse the register)
+      wait_for(reply);
       if (threadIdx.x < 128) {
         const int col = threadIdx.x & 15, row = (threadIdx.x >> 4) * 2;
         const int l = (row >> 2) * 16 + col, e = row & 3;
@@ -766,12 +842,12 @@ __device__ __forceinline__ void run_stream_dyn(int U, int NT, int T, const Src& 
               w1 += rb[kWaves * 64 * 4 + (ww * 64 + l) * 4 + e + 1];
             }
           }
-          epi(cur, row, col, v0, w0, v1, w1);
+          reply = epi(cur, row, col, v0, w0, v1, w1);
         }
-        wait_vmem();
       }
       __syncthreads();
-      if (threadIdx.x == 0) done(cur);
+      if (threadIdx.x == 0 && prev >= 0) done(prev);
+      prev = cur;
     }
     acc = zero;
     acc2 = zero;
@@ -779,6 +855,11 @@ __device__ __forceinline__ void run_stream_dyn(int U, int NT, int T, const Src& 
     nxt = nxt >= 0 ? seq[par] : -1;
     par ^= 1;
     if (cur < 0) break;
+  }
+  if constexpr (kPairs) {
+    wait_for(reply);
+    __syncthreads();
+    if (threadIdx.x == 0 && prev >= 0) done(prev);
   }
   __syncthreads();
 }

@@ -1128,19 +1128,24 @@ __device__ __forceinline__ void gateup_units(const LayerParams& p, const uint8_t
     hb[((long long)sl * T + col) * f + rt * 16 + row] = to_act<A>(sg * v2);
   };
   if constexpr (MODE == 3) {
-    // row pairs written with agent-scope stores (they pass this XCD's L2, so a
-    // down projection on any XCD reads them once the slot's counter is full)
-    auto epi2 = [=](int u, int row, int col, float v0, float w0, float v1, float w1) {
+    // row pairs written with agent-scope exchanges (they pass this XCD's L2,
+    // so a down projection on any XCD reads them once the slot's counter is
+    // full); the reply tells the stream engine when the write has completed
+    auto epi2 = [=](int u, int row, int col, float v0, float w0, float v1, float w1) -> uint32_t {
       const int sl = s0 + u / RT, rt = u % RT;
       const float h0 = (v0 / (1.0f + expf(-v0))) * w0, h1 = (v1 / (1.0f + expf(-v1))) * w1;
       A* dst = hb + ((long long)sl * T + col) * f + rt * 16 + row;
       if constexpr (sizeof(A) == 2) {
         const bf16x2 pr = {(__bf16)h0, (__bf16)h1};
-        __hip_atomic_store(reinterpret_cast<uint32_t*>(dst), __builtin_bit_cast(uint32_t, pr), __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+        return __hip_atomic_exchange(reinterpret_cast<uint32_t*>(dst), __builtin_bit_cast(uint32_t, pr),
+                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       } else {
-        __hip_atomic_store(reinterpret_cast<float*>(dst), h0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(reinterpret_cast<float*>(dst) + 1, h1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t r0 = __hip_atomic_exchange(reinterpret_cast<uint32_t*>(dst), __builtin_bit_cast(uint32_t, h0),
+                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t r1 = __hip_atomic_exchange(reinterpret_cast<uint32_t*>(dst) + 1,
+                                                  __builtin_bit_cast(uint32_t, h1), __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT);
+        return r0 ^ r1;
       }
     };
     uint32_t* scnt = p.att_cnt + kSlotCnt;
@@ -1351,18 +1356,48 @@ __device__ __forceinline__ bool phase_down_dyn(const LayerParams& p, char* smem,
   const int n32 = T * f * (int)sizeof(A) / 4;             // dwords of one slot's rows
   const int rw = f * (int)sizeof(A) / 4;                  // dwords of one row
   const int hw = (kMaxT * f * (int)sizeof(A) / 4 + kThreads - 1) / kThreads;
+  // When a row is a whole number of kThreads-dword blocks (per of them),
+  // thread block c of a slot's rows lies in row c / per, so the row test and
+  // the block's offset are the same for the whole workgroup.  Otherwise the
+  // index is taken through an opaque move, so that the addresses are formed
+  // where they are used rather than hoisted out of the unit loop into
+  // registers that would stay occupied while the tiles stream.
+  const bool blk = rw % kThreads == 0;
+  const int per = blk ? rw / kThreads : 1;
   auto h_load = [&](int sl, uint32_t* hv) {
     const uint32_t* src = reinterpret_cast<const uint32_t*>(reinterpret_cast<const A*>(p.hbuf) + (long long)sl * T * f);
+    if (blk) {
+#pragma unroll
+      for (int c = 0; c < HW; ++c)
+        if (c < hw) {
+          const int t = c / per;
+          hv[c] = __hip_atomic_load(src + min(t, T - 1) * rw + (c - t * per) * kThreads + (int)threadIdx.x,
+                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      return;
+    }
+    int tid;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(tid) : "v"((int)threadIdx.x));
 #pragma unroll
     for (int c = 0; c < HW; ++c)
       if (c < hw)
-        hv[c] = __hip_atomic_load(src + min((int)threadIdx.x + kThreads * c, n32 - 1), __ATOMIC_RELAXED,
-                                  __HIP_MEMORY_SCOPE_AGENT);
+        hv[c] = __hip_atomic_load(src + min(tid + kThreads * c, n32 - 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   };
   auto h_store = [&](A* buf, const uint32_t* hv) {
+    if (blk) {
+#pragma unroll
+      for (int c = 0; c < HW; ++c) {
+        const int t = c / per;
+        if (c < hw && t < T)
+          reinterpret_cast<uint32_t*>(buf + (long long)t * HS)[(c - t * per) * kThreads + (int)threadIdx.x] = hv[c];
+      }
+      return;
+    }
+    int tid;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(tid) : "v"((int)threadIdx.x));
 #pragma unroll
     for (int c = 0; c < HW; ++c) {
-      const int i = (int)threadIdx.x + kThreads * c;
+      const int i = tid + kThreads * c;
       if (c < hw && i < n32) {
         const int t = i / rw;
         reinterpret_cast<uint32_t*>(buf + (long long)t * HS)[i - t * rw] = hv[c];
@@ -1403,12 +1438,15 @@ __device__ __forceinline__ bool phase_down_dyn(const LayerParams& p, char* smem,
   u32x4 buf[D];
   float sc[D];
   {
+    // issued as the loop issues a chunk (see run_stream_dyn)
     const uint8_t* cb = wbase(cur);
     const float* sp = EF == MK_FMT_FP8_B128 ? sbase(cur) : dsc;
+    const int vz = vzero();
 #pragma unroll
     for (int rr = 0; rr < D; ++rr) {
       buf[rr] = ld_stream16(cb + rr * 1024);
-      if constexpr (EF == MK_FMT_FP8_B128) sc[rr] = ldg(sp + (((kp * NTh + rr) * TK) >> 7));
+      if constexpr (EF == MK_FMT_FP8_B128) sc[rr] = ldg(sp + (((kp * NTh + rr) * TK) >> 7) + vz);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
   uint32_t tk = 0, cseen = 0;
@@ -1417,6 +1455,9 @@ __device__ __forceinline__ bool phase_down_dyn(const LayerParams& p, char* smem,
   bool hpend = false;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  BPair bn;
+  f32x4 tp = zero;
+  float sp = 0.f;
   const int j = lane & 15, g = lane >> 4, jj = j < T ? j : T - 1;
   float* yb = p.ybuf;
   while (true) {
@@ -1448,11 +1489,18 @@ __device__ __forceinline__ bool phase_down_dyn(const LayerParams& p, char* smem,
       if (has_next) nsp = sbase(un);
     }
     const A* bp = hls + hb * hsz + jj * HS + g * (TK / 4) + (kp * NTh + cc * D) * TK;
+    // fp8: B read one tile ahead, scaled products added one tile later (see
+    // run_stream_dyn); a chunk's first B is read here, after the rows' barrier
+    if constexpr (EF == MK_FMT_FP8_B128) bn = b_pair(bp);
 #pragma unroll
     for (int rr = 0; rr < D; ++rr) {
       if constexpr (EF == MK_FMT_FP8_B128) {
-        const f32x4 tmp = tile_mma<EF>(buf[rr], bp + rr * TK, zero);
-        acc += tmp * sc[rr];
+        const BPair b = bn;
+        if (rr + 1 < D) bn = b_pair(bp + (rr + 1) * TK);
+        const f32x4 tmp = tile_mma_fp8(buf[rr], b, zero);
+        acc += tp * sp;
+        tp = tmp;
+        sp = keep_copy(sc[rr]);
       } else {
         acc = tile_mma<EF>(buf[rr], bp + rr * TK, acc);
       }
@@ -1465,6 +1513,11 @@ __device__ __forceinline__ bool phase_down_dyn(const LayerParams& p, char* smem,
     if (ncc != 0) continue;
     // unit `cur` complete: the blocks of waves w and w + 4 added, the unit
     // after nxt published, the next slot's completion confirmed
+    if constexpr (EF == MK_FMT_FP8_B128) {
+      acc += tp * sp;
+      tp = zero;
+      sp = 0.f;
+    }
     float* rb = red + par * (kWaves * 64 * 4);
     *reinterpret_cast<f32x4*>(rb + (w * 64 + lane) * 4) = acc;
     if (threadIdx.x == 0) {
@@ -1495,7 +1548,13 @@ __device__ __forceinline__ bool phase_down_dyn(const LayerParams& p, char* smem,
     // the next unit's rows, when its slot differs (they are waited for when
     // it starts, together with every older load)
     hpend = nxt >= 0 && nxt / QP != cur / QP;
-    if (hpend) h_load(nxt / QP, hv);
+    if (hpend) {
+      h_load(nxt / QP, hv);
+    } else {
+      // defined on both paths, so that the registers are free while the tiles stream
+#pragma unroll
+      for (int c = 0; c < HW; ++c) hv[c] = 0u;
+    }
     acc = zero;
     cur = nxt;
     nxt = nxt >= 0 ? seq[par] : -1;
