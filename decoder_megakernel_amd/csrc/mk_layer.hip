@@ -960,11 +960,14 @@ __device__ __forceinline__ void route_cands(const LayerParams& p, const RouteLds
     mx = max(mx, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mx, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
     mx = max(mx, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mx, 0x124, 0xF, 0xF, false));  // row_ror:4
     mx = max(mx, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mx, 0x128, 0xF, 0xF, false));  // row_ror:8
-    mx = max(mx, (uint32_t)__shfl_xor((int)mx, 16));
-    mx = max(mx, (uint32_t)__shfl_xor((int)mx, 32));
+    // every lane of a 16-lane row now holds the row's maximum: the four rows
+    // are combined through lane reads (scalar, no LDS round trip), and the
+    // winner's logit and expert are read from its lane the same way
+    mx = max(max((uint32_t)__builtin_amdgcn_readlane((int)mx, 0), (uint32_t)__builtin_amdgcn_readlane((int)mx, 16)),
+             max((uint32_t)__builtin_amdgcn_readlane((int)mx, 32), (uint32_t)__builtin_amdgcn_readlane((int)mx, 48)));
     const int wl = __ffsll((long long)__ballot(hk == mx)) - 1;
-    const float v = __shfl(lv[0], wl);
-    const int e = __shfl(id[0], wl);
+    const float v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lv[0]), wl));
+    const int e = __builtin_amdgcn_readlane(id[0], wl);
     if (k == 0) m0 = v;
     const float ex = __expf(v - m0);
     ps += ex;
