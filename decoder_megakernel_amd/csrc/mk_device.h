@@ -217,17 +217,22 @@ __device__ __forceinline__ bool grid_barrier(const LayerParams& p, int idx, int*
       if (last) {
         __hip_atomic_fetch_add(&b->gen, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       } else {
-        while (__hip_atomic_load(&b->gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == g) {
-          __builtin_amdgcn_s_sleep(1);
+        // the generation and the fault word are requested together, so one
+        // poll costs one memory round trip
+        while (true) {
+          const uint32_t gc = __hip_atomic_load(&b->gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          const uint32_t fc = __hip_atomic_load(&b->fault, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (gc != g) break;
+          if (fc != 0) {
+            ok = 0;
+            break;
+          }
           if ((long long)(clock100() - t0) > p.timeout_ticks) {
             __hip_atomic_store(&b->fault, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             ok = 0;
             break;
           }
-          if (__hip_atomic_load(&b->fault, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) {
-            ok = 0;
-            break;
-          }
+          __builtin_amdgcn_s_sleep(1);
         }
       }
       acquire_agent();
