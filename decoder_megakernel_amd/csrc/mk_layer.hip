@@ -1430,14 +1430,6 @@ __device__ __forceinline__ bool phase_down_dyn(const LayerParams& p, char* smem,
     const int sl = u / QP, rt = 4 * (u - sl * QP) + sub;
     return reinterpret_cast<const float*>(r.blk[sl] + sc2_off) + (rt >> 3) * nbk;
   };
-  // the first unit's rows, staged synchronously
-  if (threadIdx.x == 0) *flag = slot_ready(cur / QP, 0);
-  __syncthreads();
-  if (!*flag) return false;
-  uint32_t hv[HW];
-  h_load(cur / QP, hv);
-  h_store(hls, hv);
-  __syncthreads();
   u32x4 buf[D];
   float sc[D];
   {
@@ -1452,6 +1444,15 @@ __device__ __forceinline__ bool phase_down_dyn(const LayerParams& p, char* smem,
       __builtin_amdgcn_sched_barrier(0);
     }
   }
+  // the first unit's rows, staged synchronously (its first weight chunk, which
+  // does not depend on the slot's gate/up units, is already on its way)
+  if (threadIdx.x == 0) *flag = slot_ready(cur / QP, 0);
+  __syncthreads();
+  if (!*flag) return false;
+  uint32_t hv[HW];
+  h_load(cur / QP, hv);
+  h_store(hls, hv);
+  __syncthreads();
   uint32_t tk = 0, cseen = 0;
   int cq = (int)blockIdx.x & 7;
   int cc = 0, par = 0, hb = 0;
