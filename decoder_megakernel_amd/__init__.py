@@ -37,7 +37,8 @@ EXPORTS = (
     "mk_layer_init", "mk_decode_step", "mk_debug_tap", "mk_get_stats", "mk_set_trace", "mk_read_trace",
     "mk_set_barrier_timeout_us", "mk_sync_status", "mk_layer_reset", "mk_layer_destroy",
     "mk_head_packed_bytes", "mk_pack_head", "mk_model_state_bytes", "mk_model_init", "mk_model_set_length",
-    "mk_model_length_ptr", "mk_model_step", "mk_model_destroy",
+    "mk_model_length_ptr", "mk_model_step", "mk_model_sync_status", "mk_model_reset",
+    "mk_model_set_hidden_record", "mk_model_destroy",
 )
 
 
@@ -115,6 +116,9 @@ def _load():
         "mk_model_set_length": (_int, [_vp, _i32]),
         "mk_model_length_ptr": (_vp, [_vp]),
         "mk_model_step": (_int, [_vp, _vp, _int, _vp, _vp, _vp, _vp, _vp]),
+        "mk_model_sync_status": (_int, [_vp]),
+        "mk_model_reset": (_int, [_vp]),
+        "mk_model_set_hidden_record": (_int, [_vp, _vp]),
         "mk_model_destroy": (None, [_vp]),
     }
     for name, (res, args) in sig.items():
@@ -275,6 +279,15 @@ class Model:
     def step(self, tokens: int, T: int, next_drafts, argmax: int, committed: int, logits=None,
              stream: int = 0) -> None:
         _chk(lib.mk_model_step(self.handle, tokens, T, next_drafts, argmax, committed, logits, stream))
+
+    def sync_status(self) -> int:
+        return lib.mk_model_sync_status(self.handle)
+
+    def reset(self) -> None:
+        _chk(lib.mk_model_reset(self.handle))
+
+    def set_hidden_record(self, record_dev) -> None:
+        _chk(lib.mk_model_set_hidden_record(self.handle, record_dev))
 
     def destroy(self) -> None:
         if self.handle:

@@ -276,6 +276,8 @@ struct mk_model {
   char* state;
   float* hidden;       // [2][kMaxT][d]
   int32_t* kv_len;
+  uint32_t* fault;     // the stack's fault word
+  float* hidden_rec;   // when set: [n_layers + 1][kMaxT][d], layer l reads slot l and writes slot l + 1
   float* best_val;
   int32_t* best_idx;
   uint32_t* counter;
@@ -493,8 +495,9 @@ int mk_layer_init(const mk_layer_config* cfg, const mk_layer_weights* w, void* s
 }
 
 static int launch_layer(mk_layer* L, const float* hin, int T, void* kv_rows, int capacity, int length,
-                        const int32_t* len_dev, float* hout, hipStream_t s) {
+                        const int32_t* len_dev, float* hout, uint32_t* model_fault, hipStream_t s) {
   LayerParams p = L->base;
+  p.model_fault = model_fault;
   p.T = T;
   p.L = length;
   p.L_dev = len_dev;
@@ -519,7 +522,8 @@ int mk_decode_step(mk_layer* L, const float* hidden_in, int T, const mk_kv_cache
   if (kv->length < 0 || kv->capacity < 0 || (long long)kv->length + T > kv->capacity)
     return fail(MK_ERR_INVALID_ARG, "KV length %d + T %d exceeds capacity %d", kv->length, T, kv->capacity);
   if (hidden_in == hidden_out) return fail(MK_ERR_INVALID_ARG, "hidden_out may not alias hidden_in");
-  return launch_layer(L, hidden_in, T, kv->rows, kv->capacity, kv->length, nullptr, hidden_out, (hipStream_t)stream);
+  return launch_layer(L, hidden_in, T, kv->rows, kv->capacity, kv->length, nullptr, hidden_out, nullptr,
+                      (hipStream_t)stream);
 }
 
 int mk_debug_tap(mk_layer* L, int tap, void* host_dst, size_t bytes, void* stream) {
@@ -613,14 +617,19 @@ int mk_set_barrier_timeout_us(mk_layer* L, int64_t us) {
   return MK_OK;
 }
 
+static int status_of_fault(uint32_t fault) {
+  if (fault == kFaultTimeout) return fail(MK_ERR_TIMEOUT, "a bounded device wait exceeded its limit");
+  if (fault == kFaultKvRange) return fail(MK_ERR_INVALID_ARG, "device KV length + T exceeded the cache capacity");
+  if (fault == kFaultToken) return fail(MK_ERR_INVALID_ARG, "a token id was outside [0, vocab)");
+  if (fault != 0) return fail(MK_ERR_DEVICE_FAULT, "device fault word %u", fault);
+  return MK_OK;
+}
+
 int mk_sync_status(mk_layer* L) {
   if (!L) return fail(MK_ERR_INVALID_ARG, "null layer");
   uint32_t fault = 0;
   HIP_OK(hipMemcpy(&fault, L->state + L->sl.bar + offsetof(BarrierState, fault), 4, hipMemcpyDeviceToHost));
-  if (fault == 1) return fail(MK_ERR_TIMEOUT, "a grid barrier wait exceeded its bound");
-  if (fault == 2) return fail(MK_ERR_INVALID_ARG, "device KV length + T exceeded the cache capacity");
-  if (fault != 0) return fail(MK_ERR_DEVICE_FAULT, "device fault word %u", fault);
-  return MK_OK;
+  return status_of_fault(fault);
 }
 
 int mk_layer_reset(mk_layer* L) {
@@ -657,7 +666,7 @@ int mk_pack_head(int32_t vocab, int32_t d_model, const uint16_t* src_bf16, void*
 }
 
 struct ModelStLayout {
-  size_t len, counter, best_val, best_idx, dummy, total;
+  size_t len, counter, fault, best_val, best_idx, dummy, total;
 };
 static ModelStLayout model_layout(int nwg) {
   ModelStLayout l;
@@ -665,6 +674,7 @@ static ModelStLayout model_layout(int nwg) {
   auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
   l.len = take(4);
   l.counter = take(4);
+  l.fault = take(4);
   l.best_val = take((size_t)nwg * 8 * 4);
   l.best_idx = take((size_t)nwg * 8 * 4);
   l.dummy = take(32768);
@@ -733,6 +743,8 @@ int mk_model_init(mk_layer* const* layers, int32_t n_layers, const uint16_t* emb
   const ModelStLayout ml = model_layout(nwg);
   m->kv_len = (int32_t*)(m->state + ml.len);
   m->counter = (uint32_t*)(m->state + ml.counter);
+  m->fault = (uint32_t*)(m->state + ml.fault);
+  m->hidden_rec = nullptr;
   m->best_val = (float*)(m->state + ml.best_val);
   m->best_idx = (int32_t*)(m->state + ml.best_idx);
   m->dummy = (const uint8_t*)(m->state + ml.dummy);
@@ -763,20 +775,52 @@ int mk_model_step(mk_model* m, int32_t* tokens_dev, int T, const int32_t* next_d
   if (T < 1 || T > kMaxT) return fail(MK_ERR_INVALID_ARG, "T=%d outside [1, %d]", T, kMaxT);
   hipStream_t s = (hipStream_t)stream;
   const int d = m->layers[0]->D.d;
-  float* h0 = m->hidden;
-  float* h1 = m->hidden + (size_t)kMaxT * d;
-  int rc = launch_embed(m->emb, m->V, d, tokens_dev, T, h0, s);
+  // hidden rows of layer l's input: two buffers in turn, or slot l of the record
+  const size_t rows = (size_t)kMaxT * d;
+  auto hid = [&](int l) -> float* {
+    return m->hidden_rec ? m->hidden_rec + (size_t)l * rows : m->hidden + (size_t)(l & 1) * rows;
+  };
+  int rc = launch_embed(m->emb, m->V, d, tokens_dev, T, hid(0), m->fault, s);
   if (rc) return fail(MK_ERR_HIP, "embedding launch failed");
   for (int l = 0; l < m->n_layers; ++l) {
-    // the KV length lives in device memory; capacity is checked by the caller's loop bound
-    rc = launch_layer(m->layers[l], (l & 1) ? h1 : h0, T, m->kv[l], m->capacity, 0, m->kv_len, (l & 1) ? h0 : h1, s);
+    // the KV length lives in device memory; a step that would pass the capacity faults on the device
+    rc = launch_layer(m->layers[l], hid(l), T, m->kv[l], m->capacity, 0, m->kv_len, hid(l + 1), m->fault, s);
     if (rc) return rc;
   }
-  float* hf = (m->n_layers & 1) ? h1 : h0;
-  rc = launch_head(m->head, m->V, d, m->gamma_f, m->layers[0]->cfg.rms_eps, hf, T, logits_dev, m->best_val,
-                   m->best_idx, m->counter, tokens_dev, next_drafts_dev, argmax_dev, committed_dev, m->kv_len,
-                   m->dummy, m->nwg_head, s);
+  rc = launch_head(m->head, m->V, d, m->gamma_f, m->layers[0]->cfg.rms_eps, hid(m->n_layers), T, logits_dev,
+                   m->best_val, m->best_idx, m->counter, tokens_dev, next_drafts_dev, argmax_dev, committed_dev,
+                   m->kv_len, m->dummy, m->fault, m->nwg_head, s);
   if (rc) return fail(MK_ERR_HIP, "head launch failed");
+  return MK_OK;
+}
+
+int mk_model_set_hidden_record(mk_model* m, float* record_dev) {
+  if (!m) return fail(MK_ERR_INVALID_ARG, "null model");
+  m->hidden_rec = record_dev;
+  return MK_OK;
+}
+
+int mk_model_sync_status(mk_model* m) {
+  if (!m) return fail(MK_ERR_INVALID_ARG, "null model");
+  uint32_t fault = 0;
+  HIP_OK(hipMemcpy(&fault, m->fault, 4, hipMemcpyDeviceToHost));
+  return status_of_fault(fault);
+}
+
+int mk_model_reset(mk_model* m) {
+  if (!m) return fail(MK_ERR_INVALID_ARG, "null model");
+  for (int l = 0; l < m->n_layers; ++l) {
+    const int rc = mk_layer_reset(m->layers[l]);
+    if (rc) return rc;
+  }
+  int cur = 0;
+  hipGetDevice(&cur);
+  hipSetDevice(m->layers[0]->dev);
+  hipError_t e1 = hipMemset(m->fault, 0, 4);
+  hipError_t e2 = hipMemset(m->counter, 0, 4);
+  hipError_t e3 = hipDeviceSynchronize();
+  hipSetDevice(cur);
+  if (e1 != hipSuccess || e2 != hipSuccess || e3 != hipSuccess) return fail(MK_ERR_HIP, "model reset failed");
   return MK_OK;
 }
 

@@ -46,6 +46,10 @@ __host__ __device__ constexpr int elem_bytes(int fmt) { return fmt == MK_FMT_F32
 // groups to `top` (group 0's leader adds the missing ones).  The last arriver
 // is the one whose addition makes the count a multiple of that power, so
 // nothing is reset between barriers or launches.
+// Fault words (the layer's own, in BarrierState, and a stack's): 0 = none.
+constexpr uint32_t kFaultTimeout = 1;      // a bounded wait gave up
+constexpr uint32_t kFaultKvRange = 2;      // KV length + T beyond the cache capacity
+constexpr uint32_t kFaultToken = 3;        // a token id outside [0, vocab)
 constexpr int kBarGroup = 16;
 static_assert((kBarGroup & (kBarGroup - 1)) == 0, "the group size must be a power of two");
 constexpr int kMaxBarGroups = 64;        // grids of up to 1024 workgroups
@@ -57,7 +61,7 @@ struct alignas(256) BarrierLine {
 struct alignas(256) BarrierState {
   uint32_t gen;
   uint32_t pad1[63];
-  uint32_t fault;          // 0 ok, 1 barrier timeout, 2 KV length out of range
+  uint32_t fault;          // kFault* below
   uint32_t pad2[63];
   unsigned long long slots_sum;   // sum over launches of experts streamed (routed distinct + shared)
   unsigned long long launches;    // launches that reached the expert phase
@@ -121,6 +125,8 @@ struct LayerParams {
   const uint8_t* dummy;    // 32 KiB scratch read by the streams' last (discarded) prefetch
   // state
   BarrierState* bar;
+  uint32_t* model_fault;   // stack-wide fault word (null for a layer run on its own): a launch
+                           // that finds it set does nothing, and one that fails sets it
   uint32_t* att_cnt;       // ticket counters (gate/up at kGateCnt, down at kDownCnt)
   long long* trace;        // [nwg][2 + 2*kBarriers] or null
   long long timeout_ticks; // 100 MHz ticks

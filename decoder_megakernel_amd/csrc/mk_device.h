@@ -228,7 +228,7 @@ __device__ __forceinline__ bool grid_barrier(const LayerParams& p, int idx, int*
             break;
           }
           if ((long long)(clock100() - t0) > p.timeout_ticks) {
-            __hip_atomic_store(&b->fault, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&b->fault, kFaultTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             ok = 0;
             break;
           }

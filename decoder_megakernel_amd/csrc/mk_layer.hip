@@ -1415,7 +1415,7 @@ __device__ __forceinline__ bool phase_down_dyn(const LayerParams& p, char* smem,
     while (__hip_atomic_load(scnt + kSlotStride * sl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < need) {
       __builtin_amdgcn_s_sleep(1);
       if ((long long)(clock100() - t0) > p.timeout_ticks) {
-        __hip_atomic_store(&p.bar->fault, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&p.bar->fault, kFaultTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         return 0;
       }
       if (__hip_atomic_load(&p.bar->fault, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) return 0;
@@ -1707,16 +1707,32 @@ __device__ __forceinline__ void specialise(LayerParams& p) {
   }
 }
 
+// A workgroup leaving the launch because a barrier failed passes the layer's
+// fault on to the stack's fault word (so that later layers skip their work and
+// the stack's head commits nothing).
+__device__ __forceinline__ void raise_model_fault(const LayerParams& p) {
+  if (p.model_fault && threadIdx.x == 0) {
+    const uint32_t f = __hip_atomic_load(&p.bar->fault, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(p.model_fault, f ? f : kFaultTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
 template <int AF, int EF, int KF, int KBMAX, int DBMAX, bool EXACT, int SPEC>
 __global__ __launch_bounds__(kThreads, 1) void layer_kernel(LayerParams p) {
   specialise<SPEC>(p);
   extern __shared__ __attribute__((aligned(16))) char smem[];
   int* flag = reinterpret_cast<int*>(smem + kFlagOff);
+  // a stack step that already failed (an earlier layer, a bad token id) does
+  // no further work; every workgroup reads the same word (written by earlier
+  // launches on the stream) and leaves before the first barrier
+  if (p.model_fault && __hip_atomic_load(p.model_fault, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) return;
   const int L = p.L_dev ? ldg(p.L_dev) : p.L;
   if (L < 0 || (long long)L + p.T > p.kv_capacity) {
     // every workgroup reads the same L and leaves before the first barrier
-    if (blockIdx.x == 0 && threadIdx.x == 0)
-      __hip_atomic_store(&p.bar->fault, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+      __hip_atomic_store(&p.bar->fault, kFaultKvRange, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (p.model_fault) __hip_atomic_store(p.model_fault, kFaultKvRange, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     return;
   }
   if (p.trace && threadIdx.x == 0) {
@@ -1732,7 +1748,7 @@ __global__ __launch_bounds__(kThreads, 1) void layer_kernel(LayerParams p) {
     __hip_atomic_store(&p.att_cnt[kSlotCnt + kSlotStride * threadIdx.x], 0u, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);   // slot completion counters
   phase_qkv<AF>(p, smem);
-  if (!grid_barrier(p, 0, flag)) return;
+  if (!grid_barrier(p, 0, flag)) return raise_model_fault(p);
   {
     // absorbed-query units on waves [0, wa) of every workgroup; when they fit
     // in half the waves, RoPE / KV insert runs on the other half meanwhile
@@ -1747,23 +1763,23 @@ __global__ __launch_bounds__(kThreads, 1) void layer_kernel(LayerParams p) {
       phase_absorb<AF>(p);
     }
   }
-  if (!grid_barrier(p, 1, flag)) return;
+  if (!grid_barrier(p, 1, flag)) return raise_model_fault(p);
   phase_attention<KF, KBMAX, DBMAX, EXACT>(p, L, smem);
-  if (!grid_barrier(p, 2, flag)) return;
+  if (!grid_barrier(p, 2, flag)) return raise_model_fault(p);
   phase_merge_uv<AF>(p, L, smem);
-  if (!grid_barrier(p, 3, flag)) return;
+  if (!grid_barrier(p, 3, flag)) return raise_model_fault(p);
   phase_wo<AF>(p, smem);
-  if (!grid_barrier(p, 4, flag)) return;
+  if (!grid_barrier(p, 4, flag)) return raise_model_fault(p);
   phase_router<AF, EF>(p, smem);
-  if (!grid_barrier(p, 5, flag)) return;
+  if (!grid_barrier(p, 5, flag)) return raise_model_fault(p);
   if (experts_fused<EF>(p, LdsPlan(p, EF == MK_FMT_F32 ? 4 : 2).xb)) {
     phase_experts_fused<AF, EF>(p, smem);
   } else {
     phase_route_gateup<AF, EF>(p, smem);
-    if (!grid_barrier(p, 6, flag)) return;
+    if (!grid_barrier(p, 6, flag)) return raise_model_fault(p);
     phase_down<EF>(p, smem);
   }
-  if (!grid_barrier(p, 7, flag)) return;
+  if (!grid_barrier(p, 7, flag)) return raise_model_fault(p);
   LdsPlan lp(p, EF == MK_FMT_F32 ? 4 : 2);
   phase_combine(p, smem, lp.xb);
   if (p.trace && threadIdx.x == 0) {

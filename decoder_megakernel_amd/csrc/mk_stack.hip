@@ -10,18 +10,26 @@
 
 namespace mk {
 
+// A token id outside [0, V) is not clamped: its row is left as zeros and the
+// stack's fault word is set, so the layers skip their work and the head
+// commits nothing.
 __global__ __launch_bounds__(256) void embed_kernel(const uint16_t* emb, int V, int d, const int32_t* tokens, int T,
-                                                    float* h) {
+                                                    float* h, uint32_t* fault) {
   for (int i = blockIdx.x * 256 + threadIdx.x; i < T * d; i += gridDim.x * 256) {
     const int t = i / d, k = i - t * d;
-    int tok = tokens[t];
-    tok = tok < 0 ? 0 : (tok >= V ? V - 1 : tok);
+    const int tok = tokens[t];
+    if (tok < 0 || tok >= V) {
+      h[i] = 0.f;
+      if (k == 0) __hip_atomic_store(fault, kFaultToken, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      continue;
+    }
     h[i] = __uint_as_float((uint32_t)emb[(long long)tok * d + k] << 16);
   }
 }
 
-int launch_embed(const uint16_t* emb, int V, int d, const int32_t* tokens, int T, float* h, hipStream_t s) {
-  hipLaunchKernelGGL(embed_kernel, dim3(64), dim3(256), 0, s, emb, V, d, tokens, T, h);
+int launch_embed(const uint16_t* emb, int V, int d, const int32_t* tokens, int T, float* h, uint32_t* fault,
+                 hipStream_t s) {
+  hipLaunchKernelGGL(embed_kernel, dim3(64), dim3(256), 0, s, emb, V, d, tokens, T, h, fault);
   return (int)hipGetLastError();
 }
 
@@ -29,6 +37,7 @@ struct HeadArgs {
   const uint8_t* head; int V, d; const float* gamma; float eps; const float* h; int T;
   float* logits; float* best_val; int32_t* best_idx; uint32_t* counter; int32_t* tokens;
   const int32_t* next_drafts; int32_t* argmax; int32_t* committed; int32_t* kv_len; const uint8_t* dummy;
+  const uint32_t* fault;   // the stack's fault word
 };
 
 constexpr int kHeadLds = 8 * (8192 + kXPad) * 2 + 2 * kWaves * 64 * 4 * 4 + 1024;
@@ -36,6 +45,16 @@ constexpr int kHeadLds = 8 * (8192 + kXPad) * 2 + 2 * kWaves * 64 * 4 * 4 + 1024
 __global__ __launch_bounds__(kThreads, 1) void head_kernel(HeadArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int T = a.T, d = a.d, XS = d + kXPad;
+  // a step in which a layer or the embedding failed commits nothing: no
+  // token, no KV length change, the token buffer left as it was (every
+  // workgroup reads the same word, written by earlier launches on the stream)
+  if (__hip_atomic_load(a.fault, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) {
+    if (blockIdx.x == 0 && (int)threadIdx.x < T) {
+      a.argmax[threadIdx.x] = -1;
+      if (threadIdx.x == 0) a.committed[0] = 0;
+    }
+    return;
+  }
   __bf16* xs = reinterpret_cast<__bf16*>(smem);
   float* red = reinterpret_cast<float*>(smem + 8 * XS * 2);
   float* misc = reinterpret_cast<float*>(smem + kHeadLds - 1024);
@@ -147,9 +166,9 @@ int head_kernel_occupancy(int* wgs_per_cu) {
 int launch_head(const void* head_packed, int V, int d, const float* gamma, float eps, const float* h, int T,
                 float* logits, float* best_val, int32_t* best_idx, uint32_t* counter, int32_t* tokens,
                 const int32_t* next_drafts, int32_t* argmax, int32_t* committed, int32_t* kv_len,
-                const uint8_t* dummy, int nwg, hipStream_t s) {
+                const uint8_t* dummy, const uint32_t* fault, int nwg, hipStream_t s) {
   HeadArgs a{(const uint8_t*)head_packed, V, d, gamma, eps, h, T, logits, best_val, best_idx, counter, tokens,
-             next_drafts, argmax, committed, kv_len, dummy};
+             next_drafts, argmax, committed, kv_len, dummy, fault};
   hipLaunchKernelGGL(head_kernel, dim3(nwg), dim3(kThreads), kHeadLds, s, a);
   return (int)hipGetLastError();
 }

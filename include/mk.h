@@ -158,9 +158,27 @@ typedef struct mk_layer mk_layer;
 typedef struct mk_model mk_model;
 
 /* ---- version, device, sizes ------------------------------------------------ */
+/* The library's MK_ABI_VERSION.  A caller compares it with the header it was
+ * built against before any other call: a caller of an older interface must
+ * fail, not run on quietly ("DeepSeek-V4.1-Flash breaks 1,000 tokens per
+ * second for one user", section "Before you try it: two traps and a tip",
+ * Trap 1: a caller of the old plugin interface started without error and
+ * served at the old speed).  Every mk_layer_config also carries the version
+ * and is refused with MK_ERR_ABI_MISMATCH when it differs.  No errors. */
 int mk_abi_version(void);
+/* Message of the calling thread's last failed call (thread-local; the pointer
+ * stays valid until that thread's next failing call).  Never NULL. */
 const char* mk_last_error(void);
-/* Fills `out` for `hip_device`; MK_ERR_UNSUPPORTED_DEVICE if it is not gfx950. */
+/* Fills `out` (caller's host memory) for `hip_device`: architecture, compute
+ * units and the persistent grid the layer kernel would use (one resident
+ * workgroup per compute unit, matched to the device rather than assumed).
+ * MK_ERR_UNSUPPORTED_DEVICE if the device is not gfx950 (refused at start-up,
+ * no fallback: "DeepSeek-V4.1-Flash breaks 1,000 tokens per second for one
+ * user", section "What NVIDIA shipped, and why B300 was refused", where the
+ * plugin refuses a GPU with fewer SMs than it keeps resident work blocks for,
+ * and section "A small patch", item 1: the resident block count set to the
+ * GPU's SM count); MK_ERR_NOT_CORESIDENT if the grid cannot be resident;
+ * MK_ERR_INVALID_ARG for a null `out` or a device index out of range. */
 int mk_query_device(int hip_device, mk_device_info* out);
 /* Validates a config (ABI version, formats, supported shape). */
 int mk_check_config(const mk_layer_config* cfg);
@@ -180,8 +198,17 @@ int mk_pack_expert(const mk_layer_config* cfg, const void* w1, const void* w3, c
                    const float* s1, const float* s3, const float* s2, void* dst, void* stream);
 
 /* ---- layer ------------------------------------------------------------------- */
-/* Checks the device (gfx950, co-residency of the persistent grid), copies the
- * expert table into `state`, clears its counters (synchronously). */
+/* Checks the device (gfx950, co-residency of the persistent grid: one
+ * workgroup per compute unit, all resident at once, as the pages' plugin keeps
+ * one resident work block per SM -- "DeepSeek-V4.1-Flash breaks 1,000 tokens
+ * per second for one user", sections "What NVIDIA shipped, and why B300 was
+ * refused" and "A small patch"), copies the expert table into `state`, clears
+ * its counters (synchronously).  `w` and its arrays are read during the call
+ * only; the device buffers it points to (and `state_dev`, `workspace_dev`) are
+ * borrowed until mk_layer_destroy.  On failure *out is NULL and nothing is
+ * kept.  Errors: MK_ERR_INVALID_ARG (null pointers, a router bias given iff
+ * the config says so), the config's errors, the device errors of
+ * mk_query_device, MK_ERR_HIP. */
 int mk_layer_init(const mk_layer_config* cfg, const mk_layer_weights* w, void* state_dev,
                   void* workspace_dev, int hip_device, mk_layer** out);
 /* One verify step: hidden_in [T][d_model] fp32 (device) -> hidden_out [T][d_model]
@@ -198,7 +225,13 @@ int mk_decode_step(mk_layer* layer, const float* hidden_in, int T, const mk_kv_c
  * 7 = gates [T][top_k].
  * Valid only after a step on this layer and before another layer reuses the workspace. */
 int mk_debug_tap(mk_layer* layer, int tap, void* host_dst, size_t bytes, void* stream);
-/* Synchronous: reads the device counters of this layer's state. */
+/* Synchronous: the launch count kept by the host and the counters the kernel
+ * kept on the device (launches that reached the expert phases, expert blocks
+ * streamed), so a caller can check that the fused path actually ran and how
+ * much it streamed ("DeepSeek-V4.1-Flash breaks 1,000 tokens per second for
+ * one user", section "Before you try it: two traps and a tip", Trap 2: a
+ * setting that made the engine run stock code on every step unnoticed, hence
+ * "check that the speed moved").  MK_ERR_INVALID_ARG for null arguments. */
 int mk_get_stats(const mk_layer* layer, mk_stats* out);
 /* Enables per-workgroup phase timestamps (written into the layer state);
  * enabling clears the trace buffer (synchronous). */
@@ -212,10 +245,18 @@ int mk_set_trace(mk_layer* layer, int enabled);
 int mk_read_trace(mk_layer* layer, int64_t* host_dst, size_t bytes, void* stream);
 /* Barrier wait bound in microseconds (default 2,000,000). */
 int mk_set_barrier_timeout_us(mk_layer* layer, int64_t us);
-/* Synchronises nothing; reads the device fault word (call after the stream is
- * synchronised).  MK_OK, or MK_ERR_TIMEOUT if a barrier wait gave up. */
+/* Synchronises nothing; reads the layer's device fault word (call after the
+ * stream is synchronised).  Every wait inside a launch is bounded: past the
+ * bound the fault word is set and all workgroups leave the launch, so a stuck
+ * step becomes a visible error instead of a hang ("DeepSeek-V4.1-Flash breaks
+ * 1,000 tokens per second for one user", section "The safety layer": the
+ * watchdog that turns a possible hang into a fast, visible stop).  MK_OK,
+ * MK_ERR_TIMEOUT if a bounded wait gave up, MK_ERR_INVALID_ARG if the device
+ * KV length + T passed the capacity.  The word stays set (and every later
+ * launch of the layer leaves at its first barrier) until mk_layer_reset. */
 int mk_sync_status(mk_layer* layer);
-/* Clears barrier counters and the fault word (synchronous). */
+/* Clears the barrier counters and the fault word (synchronous; no launch of
+ * this layer may be in flight). */
 int mk_layer_reset(mk_layer* layer);
 void mk_layer_destroy(mk_layer* layer);
 
@@ -238,15 +279,43 @@ int mk_model_init(mk_layer* const* layers, int32_t n_layers, const uint16_t* emb
 int mk_model_set_length(mk_model* m, int32_t length);
 /* Device pointer to the committed KV length (int32). */
 const int32_t* mk_model_length_ptr(const mk_model* m);
-/* One verify step.  tokens_dev [T]: t0 then T-1 drafts.  Greedy verification:
- * a_i = argmax of row i; n = the largest n <= T-1 with draft_j == a_{j-1} for
- * all j <= n; n+1 tokens are committed (drafts 1..n and a_n).  Writes
- * argmax_dev [T], committed_dev [1 + T] (count, then the tokens), advances the
- * device KV length by n+1 and sets tokens_dev[0] = a_n; if next_drafts_dev
- * ([T-1]) is non-NULL it is copied into tokens_dev[1..T-1] for the next step.
- * logits_dev ([T][vocab] fp32) may be NULL. */
+/* One verify step of the stack: T = k+1 rows, the last committed token and k
+ * drafts, verified in one pass; tokens per step = accepted drafts + 1 ("Why
+ * one GB300 doesn't beat 4x RTX PRO 6000 at single-stream decode", section
+ * "The decomposition"), with greedy acceptance (the byte-for-byte greedy gate
+ * of "DeepSeek-V4.1-Flash breaks 1,000 tokens per second for one user",
+ * section "The safety layer").  Launches: embedding, one per layer, one for
+ * the head, all asynchronous on `stream`; the host reads nothing back.
+ * tokens_dev [T] (device int32): t0 then T-1 drafts.  a_i = argmax of row i's
+ * logits (ties to the lower id); n = the largest n <= T-1 with draft_j ==
+ * a_{j-1} for all j <= n; n+1 tokens are committed (drafts 1..n and a_n).
+ * Writes argmax_dev [T], committed_dev [1 + T] (count, then the tokens),
+ * advances the device KV length by n+1 and sets tokens_dev[0] = a_n; if
+ * next_drafts_dev ([T-1]) is non-NULL it is copied into tokens_dev[1..T-1] for
+ * the next step.  logits_dev ([T][vocab] fp32) may be NULL.
+ * Device-side failures (a token id outside [0, vocab), KV length + T past the
+ * capacity, a layer's bounded wait giving up) set the stack's fault word: the
+ * remaining layers of the step do nothing and the head commits nothing
+ * (committed_dev[0] = 0, argmax_dev = -1, KV length and tokens_dev unchanged);
+ * mk_model_sync_status reports it.  Host-side errors: MK_ERR_INVALID_ARG (null
+ * pointers, T outside [1, MK_MAX_T]), MK_ERR_HIP (a launch failed). */
 int mk_model_step(mk_model* m, int32_t* tokens_dev, int T, const int32_t* next_drafts_dev,
                   int32_t* argmax_dev, int32_t* committed_dev, float* logits_dev, void* stream);
+/* Reads the stack's device fault word (call after the stream is synchronised):
+ * MK_OK, MK_ERR_INVALID_ARG (a token id outside [0, vocab), or KV length + T
+ * past the capacity), MK_ERR_TIMEOUT (a layer's bounded wait gave up), as in
+ * mk_sync_status ("The safety layer": a visible stop, not a silent one).  The
+ * word stays set, and every later step commits nothing, until mk_model_reset. */
+int mk_model_sync_status(mk_model* m);
+/* Clears the stack's fault word and resets every layer (mk_layer_reset);
+ * synchronous, no step may be in flight. */
+int mk_model_reset(mk_model* m);
+/* Diagnostics: with record_dev (device fp32 [n_layers + 1][MK_MAX_T][d_model],
+ * the caller's) set, a step keeps every layer's input rows: the embedding
+ * writes slot 0, layer l reads slot l and writes slot l + 1, the head reads
+ * slot n_layers.  NULL returns to the two internal buffers.  Takes effect at
+ * the next mk_model_step. */
+int mk_model_set_hidden_record(mk_model* m, float* record_dev);
 void mk_model_destroy(mk_model* m);
 
 #ifdef __cplusplus

@@ -185,9 +185,12 @@ def layer_step(s: LayerShape, w: dict, H: np.ndarray, kv: np.ndarray, L: int, fo
 
 
 def layer_step_lazy(s: LayerShape, seed: int, layer: int, H: np.ndarray, kv: np.ndarray, L: int,
-                    base_weights: dict | None = None, force_sel=None, expert_cache: dict | None = None):
+                    base_weights: dict | None = None, force_sel=None, expert_cache: dict | None = None,
+                    expert_fn=None):
     """Layer step that materialises only the experts the router picks (for the
-    384-expert shapes).  Returns (out, taps, weights_used)."""
+    384-expert shapes).  `expert_fn(layer, slot)`, when given, supplies an
+    expert's canonical tensors (the seeded generator's draws) instead of
+    synth.recipe.expert_host.  Returns (out, taps, weights_used)."""
     w = base_weights if base_weights is not None else recipe.layer_weights_host(s, seed, layer, experts=[])
     Hp, at = attn_block(s, w, H, kv, L)
     if force_sel is None:
@@ -201,7 +204,7 @@ def layer_step_lazy(s: LayerShape, seed: int, layer: int, H: np.ndarray, kv: np.
         if expert_cache is not None and key in expert_cache:
             experts[e] = expert_cache[key]
         else:
-            experts[e] = recipe.expert_host(s, seed, layer, e)
+            experts[e] = expert_fn(layer, e) if expert_fn is not None else recipe.expert_host(s, seed, layer, e)
             if expert_cache is not None:
                 expert_cache[key] = experts[e]
     wx = dict(w, experts=experts)

@@ -83,6 +83,10 @@ def test_null_arguments_are_refused_without_a_device():
     assert lib.mk_model_step(None, None, 6, None, None, None, None, None) == mk.MK_ERR_INVALID_ARG
     assert lib.mk_get_stats(None, None) == mk.MK_ERR_INVALID_ARG
     assert lib.mk_sync_status(None) == mk.MK_ERR_INVALID_ARG
+    assert lib.mk_model_sync_status(None) == mk.MK_ERR_INVALID_ARG
+    assert lib.mk_model_reset(None) == mk.MK_ERR_INVALID_ARG
+    assert lib.mk_model_set_hidden_record(None, None) == mk.MK_ERR_INVALID_ARG
+    assert lib.mk_layer_reset(None) == mk.MK_ERR_INVALID_ARG
     assert lib.mk_head_packed_bytes(129280, 4096, None) == mk.MK_ERR_INVALID_ARG
     n = ctypes.c_size_t()
     assert lib.mk_head_packed_bytes(129280, 4096, ctypes.byref(n)) == 0

@@ -1,0 +1,64 @@
+"""GPU parity of the 32-layer stack at its real shape: 32 layers of the fp8
+384-expert layer (16 routed-expert pools), d_model 4096, vocab 129,280,
+T = 6, cache from 4096 positions (capacity 8192) -- the same stack and launch
+configuration bench.py times.
+
+  - steps 0-3 against the oracle composed layer by layer on its own rows and
+    caches (free-running): logits normwise <= 5e-2, argmax and expert selection
+    by the measured-drift band, committed tokens exact wherever no argmax is a
+    near-tie (rules in tests/stack_parity.py);
+  - step 0 also layer by layer, each layer's oracle step teacher-forced on the
+    GPU's input rows and cache rows at the single-layer bands, and the head
+    (129,280 rows: every workgroup streams about 31 row tiles and the argmax is
+    merged across the grid) on the GPU's final rows;
+  - step 3 runs with every cache row at and past the committed length set to
+    NaN: nothing past the step's own rows is read.
+
+The oracle's expert weights are the seeded generator's draws made on the
+device and copied to the host (identical bits to the host build, checked in
+tests/test_gpu_generator.py), which keeps the oracle's share of the test to
+about two minutes."""
+import numpy as np
+import pytest
+
+import stack_parity as sp
+from synth import recipe
+from synth.configs import C5
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+
+def test_full_stack_32_layers_vocab_129280():
+    from decoder_megakernel_amd import harness
+    s = C5
+    print("[stack C5] building %s on the GPU" % s.name, flush=True)
+    st = harness.DeviceStack(s, 0, private_workspaces=True)
+    rec = sp.attach_record(st, s)
+    print("[stack C5] host tables", flush=True)
+    ws = [recipe.layer_weights_host(s, 0, l, experts=[]) for l in range(s.n_layers)]
+    kvs = [recipe.kv_prefill_host(s, 0, l) for l in range(s.n_layers)]
+    tables = recipe.stack_tables_host(s, 0)
+    draws = sp.DeviceExpertDraws(s, 0, cap=1600)
+    L = s.L
+    tokens = recipe.tokens_host(s, 0, 0)
+    for step in range(4):
+        nxt = recipe.tokens_host(s, 0, step + 1)[1:]
+        if step == 3:
+            for l in range(s.n_layers):
+                st.kv[l][L:] = torch.tensor(0x7FC0, dtype=torch.int16)      # bf16 quiet NaN
+            torch.cuda.synchronize()
+        g = sp.gpu_step(st, s, rec, tokens, nxt)
+        assert g["L"] == L
+        tag = " C5 step %d" % step
+        assert np.isfinite(g["logits"]).all() and np.isfinite(g["hidden"]).all()
+        o_lg, o_am, _ = sp.oracle_stack_step(s, ws, tables, kvs, tokens, L, g=g, expert_fn=draws, tag=tag)
+        com = sp.compare_free_running(s, g, o_lg, o_am, tokens, tag=tag)
+        if step == 0:
+            sp.check_layers_teacher_forced(st, s, ws, g, expert_fn=draws, tag=tag)
+            sp.check_head_teacher_forced(s, tables, g, tag=tag)
+        n = len(com)
+        assert g["len"] == L + n
+        assert g["tok"][0] == com[-1] and list(g["tok"][1:]) == list(nxt)
+        L += n
+        tokens = np.concatenate([[com[-1]], nxt]).astype(np.int32)

@@ -369,3 +369,87 @@ def test_head_argmax_ties_go_to_lower_id_and_embed_gathers_rows():
     head2[6] = emb[3] * 0 + synth.normal_bf16(d, 1, 1, 0.5)
     lg, am2 = oracle.head(head2, gf, h)
     assert am2[0] == int(np.argmax(lg[0]))
+
+
+# ---------------------------------------------------------------- pins of the softmax scale, head norm/gain, biased gates
+def test_two_key_softmax_scale_closed_form():
+    """One verify row over two cache rows (the prefilled row 0 and its own row 1):
+    z = p0 c0 + p1 c1 with p1 / p0 = exp((s1 - s0) / sqrt(d_h + d_r)), where
+    s_j = q~ . c_j + q^R . k^R_j is computed here from the taps and the stored
+    rows.  The ratio read back from z fixes the scale: 1/sqrt(d_h) (no RoPE
+    dims in the scale) or no scale at all would be off by far more than the
+    fp32 bound checked here."""
+    s = C0.with_(T=1, L=1, kv_capacity=2)
+    w, H, kv = fresh(s)
+    _, taps = oracle.layer_step(s, w, H, kv, s.L)
+    rows = kv.astype(np.float64)
+    c0, c1 = rows[0, : s.d_c], rows[1, : s.d_c]
+    k0, k1 = rows[0, s.d_c:], rows[1, s.d_c:]
+    dc = c1 - c0
+    for h in range(s.n_h):
+        qa = taps["qabs"][0, h].astype(np.float64)
+        qr = taps["q"][0, h, s.d_h:].astype(np.float64)
+        ds = qa @ (c1 - c0) + qr @ (k1 - k0)
+        z = taps["z"][0, h].astype(np.float64)
+        p1 = (z - c0) @ dc / (dc @ dc)                      # z lies on the segment c0 -> c1
+        assert np.allclose(z, c0 + p1 * dc, atol=1e-6)
+        ratio = p1 / (1.0 - p1)
+        want = math.exp(ds / math.sqrt(s.d_h + s.d_r))
+        assert abs(ratio / want - 1.0) < 1e-4, (h, ratio, want)
+        # the scale is not 1/sqrt(d_h) alone, and not 1
+        for wrong in (math.exp(ds / math.sqrt(s.d_h)), math.exp(ds)):
+            assert abs(wrong / want - 1.0) > 1e-3
+
+
+def _rms_rows(h, gamma, eps):
+    h = np.asarray(h, np.float64)
+    return h / np.sqrt((h * h).mean(axis=1, keepdims=True) + eps) * np.asarray(gamma, np.float64)
+
+
+def test_head_final_norm_and_gain():
+    """LM head logits = W_head (RMSNorm(h) * gamma_f) with a non-unit gain, in three ways
+    that each fail for a dropped norm or gain: (1) against fp64 arithmetic of the
+    definition, (2) invariance under a positive scale of h, (3) linearity in the gain."""
+    V, d, T = 96, 256, 3
+    head = synth.normal_bf16((V, d), 0, synth.stream_id("head"), 0.02)
+    gf = synth.normal_f32(d, 0, synth.stream_id("gamma_f"), 0.1, mean=1.0)
+    h = synth.normal_f32((T, d), 0, synth.stream_id("H"), 3.0)
+    eps = 1e-6
+    lg, am = oracle.head(head, gf, h, eps)
+    ref = _rms_rows(h, gf, eps) @ oracle.bf16_to_f32(head).astype(np.float64).T
+    assert normwise(lg, ref) < 1e-5
+    assert list(am) == list(np.argmax(ref, axis=1))
+    lg2, _ = oracle.head(head, gf, h * np.float32(0.25), eps)      # exact scaling of h
+    assert np.allclose(lg2, lg, rtol=1e-5, atol=1e-6)
+    lg3, _ = oracle.head(head, (gf * np.float32(2.0)).astype(np.float32), h, eps)
+    assert np.allclose(lg3, 2.0 * lg, rtol=1e-6, atol=1e-7)
+    # a unit gain gives a different answer (the gain is applied at all)
+    lg1, _ = oracle.head(head, np.ones(d, np.float32), h, eps)
+    assert normwise(lg1, ref) > 1e-2
+
+
+def test_gates_under_router_bias_use_the_biased_logits():
+    """With a router bias (the skewed-routing workload) the logits tap is the
+    unbiased logits plus the bias, and the gates are the softmax of the biased
+    logits renormalised over the selection; a softmax of the unbiased logits
+    would fail here."""
+    s = C0Q.with_(E=16, top_k=4, T=3)
+    w, H, kv = fresh(s)
+    _, t0 = oracle.layer_step(s, w, H, kv.copy(), s.L)
+    b = synth.normal_f32(s.E, 0, synth.stream_id("hot_perm"), 1.0)
+    wb = dict(w, router_bias=b)
+    _, tb = oracle.layer_step(s, wb, H, kv.copy(), s.L)
+    assert np.array_equal(tb["Hp"], t0["Hp"])
+    lb = tb["logits"].astype(np.float64)
+    assert np.allclose(lb - t0["logits"].astype(np.float64), b.astype(np.float64), atol=1e-6)
+    changed = 0
+    for i in range(s.T):
+        order = np.argsort(-lb[i], kind="stable")
+        assert list(tb["sel"][i]) == list(order[: s.top_k])
+        sel = tb["sel"][i]
+        e = np.exp(lb[i][sel] - lb[i][sel].max())
+        assert np.allclose(tb["gate"][i], e / e.sum(), rtol=1e-5)
+        lu = t0["logits"][i].astype(np.float64)[sel]
+        eu = np.exp(lu - lu.max())
+        changed += not np.allclose(tb["gate"][i], eu / eu.sum(), rtol=1e-3)
+    assert changed == s.T
