@@ -15,6 +15,7 @@ LIB_PATH = os.path.join(_HERE, "libmk.so")
 
 MK_ABI_VERSION = 1
 MK_MAX_T = 8   # verify rows per step
+MK_STATIC_SCRATCH_BYTES = 32 << 20
 
 MK_OK = 0
 MK_ERR_INVALID_ARG = -1
@@ -34,7 +35,7 @@ MK_T_WQ, MK_T_WDKV, MK_T_WUK, MK_T_WUV, MK_T_WO, MK_T_WR, MK_T_EXPERT = range(7)
 EXPORTS = (
     "mk_abi_version", "mk_last_error", "mk_query_device", "mk_check_config", "mk_packed_bytes",
     "mk_kv_bytes", "mk_layer_state_bytes", "mk_layer_workspace_bytes", "mk_pack_tensor", "mk_pack_expert",
-    "mk_layer_init", "mk_decode_step", "mk_debug_tap", "mk_get_stats", "mk_set_trace", "mk_read_trace",
+    "mk_layer_init", "mk_decode_step", "mk_decode_step_static", "mk_debug_tap", "mk_get_stats", "mk_set_trace", "mk_read_trace",
     "mk_set_barrier_timeout_us", "mk_sync_status", "mk_layer_reset", "mk_layer_destroy",
     "mk_head_packed_bytes", "mk_pack_head", "mk_model_state_bytes", "mk_model_init", "mk_model_set_length",
     "mk_model_length_ptr", "mk_model_step", "mk_model_sync_status", "mk_model_reset",
@@ -101,6 +102,7 @@ def _load():
         "mk_pack_expert": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
         "mk_layer_init": (_int, [_vp, _vp, _vp, _vp, _int, _vp]),
         "mk_decode_step": (_int, [_vp, _vp, _int, _vp, _vp, _vp]),
+        "mk_decode_step_static": (_int, [_vp, _vp, _int, _vp, _vp, _vp]),
         "mk_debug_tap": (_int, [_vp, _int, _vp, _sz, _vp]),
         "mk_get_stats": (_int, [_vp, _vp]),
         "mk_set_trace": (_int, [_vp, _int]),
@@ -211,6 +213,11 @@ class Layer:
                     stream: int = 0) -> None:
         kv = KvCache(kv_rows, capacity, length)
         _chk(lib.mk_decode_step(self.handle, hidden_in, T, ctypes.byref(kv), hidden_out, stream))
+
+    def decode_step_static(self, hidden_in: int, T: int, kv_rows: int, capacity: int, length: int,
+                           hidden_out: int, stream: int = 0) -> None:
+        kv = KvCache(kv_rows, capacity, length)
+        _chk(lib.mk_decode_step_static(self.handle, hidden_in, T, ctypes.byref(kv), hidden_out, stream))
 
     def debug_tap(self, tap: int, host_buf, stream: int = 0) -> None:
         _chk(lib.mk_debug_tap(self.handle, tap, host_buf.ctypes.data, host_buf.nbytes, stream))

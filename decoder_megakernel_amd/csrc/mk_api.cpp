@@ -8,6 +8,7 @@
 #include <cstdio>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 
@@ -234,6 +235,49 @@ StLayout st_layout(const Dims& D, const Schedule& s) {
   return l;
 }
 
+// Points the workspace fields of `p` into the workspace at `ws` (layout `wl`).
+void bind_workspace(LayerParams& p, const WsLayout& wl, char* ws) {
+  p.qkv_part = (float*)(ws + wl.qkv_part);
+  p.qrope = (float*)(ws + wl.qrope);
+  p.qabs = (float*)(ws + wl.qabs);
+  p.att_part = (float*)(ws + wl.att_part);
+  p.att_ml = (float*)(ws + wl.att_ml);
+  p.z = (float*)(ws + wl.z);
+  p.o = (float*)(ws + wl.o);
+  p.hp = (float*)(ws + wl.hp);
+  p.route_sel = (int32_t*)(ws + wl.route_sel);
+  p.route_gate = (float*)(ws + wl.route_gate);
+  p.route_cand = (float*)(ws + wl.route_cand);
+  p.logits = (float*)(ws + wl.logits);
+  p.hbuf = (float*)(ws + wl.hbuf);
+  p.ybuf = (float*)(ws + wl.ybuf);
+  p.dummy = (const uint8_t*)(ws + wl.dummy);
+}
+
+// ------------------------------------------------------------------ static scratch
+// The scratch of mk_decode_step_static: a file-scope device array that every
+// GPU the library runs on holds until the process ends.  In host code
+// `scratch` names a host-side stand-in, not device memory: its device address
+// is looked up once per device (hipGetSymbolAddress, with that device current,
+// in mk_layer_init) and only that address is ever passed to a kernel.
+constexpr size_t kStaticScratchBytes = MK_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[kMaxDevices];        // device address of `scratch` per device (null: not looked up)
+hipError_t g_scratch_err[kMaxDevices];   // the lookup's result per device
+
+// With `dev` current: looks up the device address of `scratch` once per device.
+void scratch_setup(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[dev]) return;
+  void* ptr = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  g_scratch_err[dev] = e;
+  if (e == hipSuccess && ptr) g_scratch_ptr[dev] = (char*)ptr;
+}
+
 Schedule make_schedule(const Dims& D, int nwg) {
   Schedule s;
   s.nwg = nwg;
@@ -257,6 +301,7 @@ struct mk_layer {
   char* ws;
   LayerKernelFn fn;
   LayerParams base;
+  LayerParams last;    // the workspace pointers of the last launch (the debug taps read these)
   int trace_on;
   long long timeout_us;
   long long steps, launches;
@@ -450,6 +495,7 @@ int mk_layer_init(const mk_layer_config* cfg, const mk_layer_weights* w, void* s
   hipError_t e1 = hipMemset(L->state, 0, L->sl.total);
   hipError_t e2 = hipMemcpy(L->state + L->sl.experts, w->experts, (size_t)(D.E + D.nshared) * 8, hipMemcpyHostToDevice);
   hipError_t e3 = hipDeviceSynchronize();
+  scratch_setup(hip_device);
   hipSetDevice(cur);
   if (e1 != hipSuccess || e2 != hipSuccess || e3 != hipSuccess) {
     delete L;
@@ -470,33 +516,22 @@ int mk_layer_init(const mk_layer_config* cfg, const mk_layer_weights* w, void* s
   p.experts = (const uint8_t* const*)(L->state + L->sl.experts);
   p.exp_w13_bytes = exp_w13(D);
   p.exp_w2_bytes = exp_w2(D);
-  char* ws = L->ws;
-  p.qkv_part = (float*)(ws + L->wl.qkv_part);
-  p.qrope = (float*)(ws + L->wl.qrope);
-  p.qabs = (float*)(ws + L->wl.qabs);
-  p.att_part = (float*)(ws + L->wl.att_part);
-  p.att_ml = (float*)(ws + L->wl.att_ml);
-  p.z = (float*)(ws + L->wl.z);
-  p.o = (float*)(ws + L->wl.o);
-  p.hp = (float*)(ws + L->wl.hp);
-  p.route_sel = (int32_t*)(ws + L->wl.route_sel);
-  p.route_gate = (float*)(ws + L->wl.route_gate);
-  p.route_cand = (float*)(ws + L->wl.route_cand);
-  p.logits = (float*)(ws + L->wl.logits);
-  p.hbuf = (float*)(ws + L->wl.hbuf);
-  p.ybuf = (float*)(ws + L->wl.ybuf);
-  p.dummy = (const uint8_t*)(ws + L->wl.dummy);
+  bind_workspace(p, L->wl, L->ws);
   p.bar = (BarrierState*)(L->state + L->sl.bar);
   p.att_cnt = (uint32_t*)(L->state + L->sl.att_cnt);
   p.trace = nullptr;
   p.sch = L->sch;
+  L->last = p;
   *out = L;
   return MK_OK;
 }
 
+// ws: the workspace to use (null: the layer's own).
 static int launch_layer(mk_layer* L, const float* hin, int T, void* kv_rows, int capacity, int length,
-                        const int32_t* len_dev, float* hout, uint32_t* model_fault, hipStream_t s) {
+                        const int32_t* len_dev, float* hout, uint32_t* model_fault, hipStream_t s,
+                        char* ws = nullptr) {
   LayerParams p = L->base;
+  if (ws) bind_workspace(p, L->wl, ws);
   p.model_fault = model_fault;
   p.T = T;
   p.L = length;
@@ -513,6 +548,7 @@ static int launch_layer(mk_layer* L, const float* hin, int T, void* kv_rows, int
   L->steps++;
   L->launches++;
   L->last_T = T;
+  L->last = p;
   return MK_OK;
 }
 
@@ -526,6 +562,24 @@ int mk_decode_step(mk_layer* L, const float* hidden_in, int T, const mk_kv_cache
                       (hipStream_t)stream);
 }
 
+int mk_decode_step_static(mk_layer* L, const float* hidden_in, int T, const mk_kv_cache* kv, float* hidden_out,
+                          void* stream) {
+  if (!L || !hidden_in || !kv || !kv->rows || !hidden_out) return fail(MK_ERR_INVALID_ARG, "null argument");
+  if (T < 1 || T > kMaxT) return fail(MK_ERR_INVALID_ARG, "T=%d outside [1, %d]", T, kMaxT);
+  if (kv->length < 0 || kv->capacity < 0 || (long long)kv->length + T > kv->capacity)
+    return fail(MK_ERR_INVALID_ARG, "KV length %d + T %d exceeds capacity %d", kv->length, T, kv->capacity);
+  if (hidden_in == hidden_out) return fail(MK_ERR_INVALID_ARG, "hidden_out may not alias hidden_in");
+  if (L->wl.total > kStaticScratchBytes)
+    return fail(MK_ERR_UNSUPPORTED_SHAPE, "the layer's scratch (%zu bytes) exceeds the static scratch of %zu bytes",
+                L->wl.total, kStaticScratchBytes);
+  char* ptr = (L->dev >= 0 && L->dev < kMaxDevices) ? g_scratch_ptr[L->dev] : nullptr;
+  if (!ptr)
+    return fail(MK_ERR_HIP, "static scratch of device %d unavailable: %s", L->dev,
+                hipGetErrorString(L->dev >= 0 && L->dev < kMaxDevices ? g_scratch_err[L->dev] : hipErrorInvalidDevice));
+  return launch_layer(L, hidden_in, T, kv->rows, kv->capacity, kv->length, nullptr, hidden_out, nullptr,
+                      (hipStream_t)stream, ptr);
+}
+
 int mk_debug_tap(mk_layer* L, int tap, void* host_dst, size_t bytes, void* stream) {
   if (!L || !host_dst) return fail(MK_ERR_INVALID_ARG, "null argument");
   const Dims& D = L->D;
@@ -533,7 +587,7 @@ int mk_debug_tap(mk_layer* L, int tap, void* host_dst, size_t bytes, void* strea
   if (T <= 0) return fail(MK_ERR_INVALID_ARG, "no step has run on this layer");
   const char* src = nullptr;
   size_t need = 0;
-  const LayerParams& p = L->base;
+  const LayerParams& p = L->last;
   switch (tap) {
     case 1: src = (const char*)p.qabs; need = (size_t)T * D.nh * D.dc * 4; break;
     case 2: src = (const char*)p.z; need = (size_t)T * D.nh * D.dc * 4; break;

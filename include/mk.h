@@ -46,6 +46,7 @@ extern "C" {
 
 #define MK_ABI_VERSION 1
 #define MK_MAX_T 8           /* verify rows per step: k drafts + 1, at most 8 */
+#define MK_STATIC_SCRATCH_BYTES (32u << 20)   /* scratch of mk_decode_step_static, per GPU */
 
 typedef enum mk_status {
   MK_OK = 0,
@@ -216,6 +217,24 @@ int mk_layer_init(const mk_layer_config* cfg, const mk_layer_weights* w, void* s
  * MK_ERR_INVALID_ARG if T is not in [1, MK_MAX_T] or length + T > capacity. */
 int mk_decode_step(mk_layer* layer, const float* hidden_in, int T, const mk_kv_cache* kv,
                    float* hidden_out, void* stream);
+/* For callers that cannot allocate device memory at step time (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same step as mk_decode_step, with the same kernels and results, but its
+ * scratch (activations, attention partials, expert rows: everything the layer's
+ * workspace holds) is a device array inside the library, of
+ * MK_STATIC_SCRATCH_BYTES per GPU, held by every GPU the library runs on until
+ * the process ends; the workspace given to mk_layer_init is not touched.  The
+ * caller still passes inputs, outputs and the KV rows, and the layer keeps its
+ * own state.  The call allocates nothing (no hipMalloc, hipFree or allocating
+ * library routine).  Every call on one GPU shares that GPU's array: calls that
+ * overlap in time on one GPU (different streams, or layers of different
+ * threads) race and give wrong results; issue them on one stream.  Nothing in
+ * the array needs clearing between calls.  Errors: those of mk_decode_step,
+ * and MK_ERR_UNSUPPORTED_SHAPE when the layer's workspace
+ * (mk_layer_workspace_bytes) exceeds MK_STATIC_SCRATCH_BYTES, MK_ERR_HIP when
+ * the array's device address could not be found at mk_layer_init. */
+int mk_decode_step_static(mk_layer* layer, const float* hidden_in, int T, const mk_kv_cache* kv,
+                          float* hidden_out, void* stream);
 /* Copies the step's intermediate results from the workspace to host memory
  * (synchronises `stream`).  tap: 0 = Q [T][n_h][d_h+d_r] (q^R rotated),
  * 1 = absorbed query q~ [T][n_h][d_latent], 2 = attention latent z [T][n_h][d_latent],
@@ -223,7 +242,8 @@ int mk_decode_step(mk_layer* layer, const float* hidden_in, int T, const mk_kv_c
  * in the matrix-core operand format), 4 = post-attention hidden [T][d_model],
  * 5 = router logits [T][n_experts], 6 = selected experts int32 [T][top_k],
  * 7 = gates [T][top_k].
- * Valid only after a step on this layer and before another layer reuses the workspace. */
+ * Valid only after a step on this layer and before another layer reuses the workspace
+ * (the workspace that step used: the layer's own, or the static scratch). */
 int mk_debug_tap(mk_layer* layer, int tap, void* host_dst, size_t bytes, void* stream);
 /* Synchronous: the launch count kept by the host and the counters the kernel
  * kept on the device (launches that reached the expert phases, expert blocks
