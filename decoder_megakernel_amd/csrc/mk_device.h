@@ -82,15 +82,16 @@ __device__ __forceinline__ void wg_release_begin() {
 }
 
 // Agent-scope release (L2 write-back of this compute unit's XCD, so other XCDs
-// can read what this workgroup wrote) and acquire (drop stale cached copies).
-// The write-back is complete when the wave's memory counter drains; the fence
-// alone may leave that wait out when no load or store of the wave is pending
-// (the write-back itself is not counted as pending), so it is spelled out.
+// can read what this workgroup wrote).  The write-back is complete when the
+// wave's memory counter drains; the fence alone may leave that wait out when
+// no load or store of the wave is pending (the write-back itself is not
+// counted as pending), so it is spelled out.
 __device__ __forceinline__ void release_agent() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
   wait_vmem();
 }
-__device__ __forceinline__ void acquire_agent() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
+// Orders the compiler only: no load after it is moved above it.
+__device__ __forceinline__ void compiler_fence() { __atomic_signal_fence(__ATOMIC_SEQ_CST); }
 
 __device__ __forceinline__ uint64_t clock100() { return __builtin_amdgcn_s_memrealtime(); }
 
@@ -186,10 +187,16 @@ __device__ __forceinline__ long long* trace_lds() {
 
 // ------------------------------------------------------------------ grid barrier
 // Two-level barrier over the whole persistent grid (see BarrierState).  Each
-// workgroup drains its stores and releases them at agent scope before it
-// arrives, and acquires after the release of the barrier.  The wait is bounded: past `timeout_ticks` (100 MHz clock) the fault word is set
-// and every later barrier returns false at once, so all workgroups leave the
-// kernel.
+// workgroup drains its stores and releases them at agent scope (L2 write-back)
+// before it arrives.  There is no acquire (L1/L2 invalidate) after the release:
+// every buffer one workgroup writes and another reads after a barrier is
+// written once per launch and read by no compute unit before it is written,
+// and the caches are invalidated when a launch starts, so no cache can hold a
+// stale copy of it; a per-workgroup invalidate would only make the first loads
+// of the next phase miss (measured on MI355X: about 2 us for the first load
+// after an agent-scope acquire, 0.3 us without).  The wait is bounded: past
+// `timeout_ticks` (100 MHz clock) the fault word is set and every later barrier
+// returns false at once, so all workgroups leave the kernel.
 __device__ __forceinline__ bool grid_barrier(const LayerParams& p, int idx, int* lds_flag) {
   wg_release_begin();
   if (threadIdx.x == 0) {
@@ -235,7 +242,7 @@ __device__ __forceinline__ bool grid_barrier(const LayerParams& p, int idx, int*
           __builtin_amdgcn_s_sleep(1);
         }
       }
-      acquire_agent();
+      compiler_fence();
     }
     if (p.trace) trace_lds()[2 + 2 * idx] = (long long)clock100();
     *lds_flag = ok;
