@@ -520,6 +520,8 @@ int mk_layer_init(const mk_layer_config* cfg, const mk_layer_weights* w, void* s
   p.bar = (BarrierState*)(L->state + L->sl.bar);
   p.att_cnt = (uint32_t*)(L->state + L->sl.att_cnt);
   p.trace = nullptr;
+  // MI355X runs workgroup b of a launch on XCD b % 8 (checked by the kernel at every barrier)
+  p.xcd_release = L->sch.nwg % 8 == 0 ? 1 : 0;
   p.sch = L->sch;
   L->last = p;
   *out = L;
@@ -675,6 +677,8 @@ static int status_of_fault(uint32_t fault) {
   if (fault == kFaultTimeout) return fail(MK_ERR_TIMEOUT, "a bounded device wait exceeded its limit");
   if (fault == kFaultKvRange) return fail(MK_ERR_INVALID_ARG, "device KV length + T exceeded the cache capacity");
   if (fault == kFaultToken) return fail(MK_ERR_INVALID_ARG, "a token id was outside [0, vocab)");
+  if (fault == kFaultXcd)
+    return fail(MK_ERR_DEVICE_FAULT, "a workgroup ran on another XCD than its barrier group assumes");
   if (fault != 0) return fail(MK_ERR_DEVICE_FAULT, "device fault word %u", fault);
   return MK_OK;
 }

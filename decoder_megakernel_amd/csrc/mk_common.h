@@ -38,18 +38,21 @@ __host__ __device__ constexpr int elem_bytes(int fmt) { return fmt == MK_FMT_F32
 
 // Per-layer device state (persistent across steps; zeroed at init).
 // The grid barrier is two-level: workgroups arrive on the counter of their
-// group of kBarGroup consecutive workgroups; the last of a group arrives on
+// group (the workgroups of one XCD, b % 8, when the grid is a multiple of 8;
+// else kBarGroup consecutive workgroups); the last of a group arrives on
 // `top`; the last group leader advances `gen`, which releases everyone.  The
 // 32-bit counters only grow (wrapping), and every barrier adds a power of two
-// to each: kBarGroup to a group counter (the first workgroup of a smaller last
-// group adds the missing arrivals), and the next power of two >= the number of
-// groups to `top` (group 0's leader adds the missing ones).  The last arriver
-// is the one whose addition makes the count a multiple of that power, so
-// nothing is reset between barriers or launches.
+// to each: the next power of two >= the group size to a group counter (the
+// first workgroup of a smaller group adds the missing arrivals), and the next
+// power of two >= the number of groups to `top` (group 0's leader adds the
+// missing ones).  The last arriver is the one whose addition makes the count a
+// multiple of that power, so nothing is reset between barriers or launches
+// (a layer keeps one grouping for its lifetime).
 // Fault words (the layer's own, in BarrierState, and a stack's): 0 = none.
 constexpr uint32_t kFaultTimeout = 1;      // a bounded wait gave up
 constexpr uint32_t kFaultKvRange = 2;      // KV length + T beyond the cache capacity
 constexpr uint32_t kFaultToken = 3;        // a token id outside [0, vocab)
+constexpr uint32_t kFaultXcd = 4;          // a workgroup found itself on another XCD than its barrier group's
 constexpr int kBarGroup = 16;
 static_assert((kBarGroup & (kBarGroup - 1)) == 0, "the group size must be a power of two");
 constexpr int kMaxBarGroups = 64;        // grids of up to 1024 workgroups
@@ -130,6 +133,7 @@ struct LayerParams {
   uint32_t* att_cnt;       // ticket counters (gate/up at kGateCnt, down at kDownCnt)
   long long* trace;        // [nwg][2 + 2*kBarriers] or null
   long long timeout_ticks; // 100 MHz ticks
+  int xcd_release;         // grid barrier groups = XCDs, one L2 write-back per XCD (grid a multiple of 8)
   Schedule sch;
 };
 

@@ -187,8 +187,17 @@ __device__ __forceinline__ long long* trace_lds() {
 
 // ------------------------------------------------------------------ grid barrier
 // Two-level barrier over the whole persistent grid (see BarrierState).  Each
-// workgroup drains its stores and releases them at agent scope (L2 write-back)
-// before it arrives.  There is no acquire (L1/L2 invalidate) after the release:
+// workgroup drains its stores into its XCD's L2 before it arrives.  With
+// xcd_release (a grid that is a multiple of 8), the groups are the XCDs --
+// MI355X runs workgroup b of a launch on XCD b % 8 -- and the last arrival of a
+// group writes that XCD's L2 back once (agent-scope release) for all of its
+// workgroups: a write-back per workgroup put the slowest workgroups' write-
+// backs on every phase's critical path (measured: 15 us per layer launch).
+// Every workgroup checks its XCD (hardware register XCC_ID) at each arrival; one
+// on another XCD than its group's writes its own stores back and sets the
+// fault word, so such a launch is reported, never silently wrong.  Otherwise
+// the groups are kBarGroup consecutive workgroups and each workgroup writes its
+// own stores back.  There is no acquire (L1/L2 invalidate) after the release:
 // every buffer one workgroup writes and another reads after a barrier is
 // written once per launch and read by no compute unit before it is written,
 // and the caches are invalidated when a launch starts, so no cache can hold a
@@ -209,18 +218,38 @@ __device__ __forceinline__ bool grid_barrier(const LayerParams& p, int idx, int*
     } else {
       // the generation is read (and waited for) before this workgroup arrives
       const uint32_t g = __hip_atomic_load(&b->gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      release_agent();
-      const uint32_t nwg = gridDim.x, grp = blockIdx.x / kBarGroup;
-      const uint32_t ngrp = (nwg + kBarGroup - 1) / kBarGroup;
-      const uint32_t gsz = min((uint32_t)kBarGroup, nwg - grp * kBarGroup);
-      const uint32_t add = blockIdx.x % kBarGroup == 0 ? kBarGroup - gsz + 1 : 1u;
-      const uint32_t tpow = ngrp > 1 ? 1u << (32 - __builtin_clz(ngrp - 1)) : 1u;
-      const uint32_t tadd = grp == 0 ? tpow - ngrp + 1 : 1u;
+      const uint32_t nwg = gridDim.x;
       bool last = false;
-      if (((__hip_atomic_fetch_add(&b->grp[grp].n, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + add) &
-           (kBarGroup - 1)) == 0)
-        last = ((__hip_atomic_fetch_add(&b->top.n, tadd, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + tadd) &
-                (tpow - 1)) == 0;
+      if (p.xcd_release) {
+        // groups = XCDs (workgroup b on XCD b % 8): every workgroup's stores are
+        // in its XCD's L2 when it arrives, so the group's last arrival writes
+        // that L2 back once for all of them.  A workgroup on another XCD than
+        // its group's writes its own stores back and flags the launch.
+        const uint32_t grp = blockIdx.x & 7, gsz = nwg / 8;
+        const uint32_t gpow = gsz > 1 ? 1u << (32 - __builtin_clz(gsz - 1)) : 1u;
+        const uint32_t add = blockIdx.x < 8 ? gpow - gsz + 1 : 1u;
+        if ((__builtin_amdgcn_s_getreg((20) | (0 << 6) | (3 << 11)) & 7u) != grp) {
+          __hip_atomic_store(&b->fault, kFaultXcd, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          release_agent();
+        }
+        if (((__hip_atomic_fetch_add(&b->grp[grp].n, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + add) &
+             (gpow - 1)) == 0) {
+          release_agent();
+          last = ((__hip_atomic_fetch_add(&b->top.n, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u) & 7u) == 0;
+        }
+      } else {
+        release_agent();
+        const uint32_t grp = blockIdx.x / kBarGroup;
+        const uint32_t ngrp = (nwg + kBarGroup - 1) / kBarGroup;
+        const uint32_t gsz = min((uint32_t)kBarGroup, nwg - grp * kBarGroup);
+        const uint32_t add = blockIdx.x % kBarGroup == 0 ? kBarGroup - gsz + 1 : 1u;
+        const uint32_t tpow = ngrp > 1 ? 1u << (32 - __builtin_clz(ngrp - 1)) : 1u;
+        const uint32_t tadd = grp == 0 ? tpow - ngrp + 1 : 1u;
+        if (((__hip_atomic_fetch_add(&b->grp[grp].n, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + add) &
+             (kBarGroup - 1)) == 0)
+          last = ((__hip_atomic_fetch_add(&b->top.n, tadd, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + tadd) &
+                  (tpow - 1)) == 0;
+      }
       if (last) {
         __hip_atomic_fetch_add(&b->gen, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       } else {
@@ -229,11 +258,11 @@ __device__ __forceinline__ bool grid_barrier(const LayerParams& p, int idx, int*
         while (true) {
           const uint32_t gc = __hip_atomic_load(&b->gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           const uint32_t fc = __hip_atomic_load(&b->fault, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          if (gc != g) break;
           if (fc != 0) {
             ok = 0;
             break;
           }
+          if (gc != g) break;
           if ((long long)(clock100() - t0) > p.timeout_ticks) {
             __hip_atomic_store(&b->fault, kFaultTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             ok = 0;

@@ -122,23 +122,31 @@ template <> __device__ __forceinline__ f32x4 round4<__bf16>(const f32x4& v) {
 // Stages T <= kMaxT fp32 rows of length K (K % 4 == 0, K <= kMaxModel) into
 // LDS as the MFMA operand type, row stride XS.  Wave w holds the float4
 // columns w*64 + lane + 512 c of every row, so a lane keeps at most
-// kMaxT x kRowCh float4s and the gain slice they share.  With NORM each row is
-// RMS-normalised on the way, x = (h * rsqrt(mean(h^2) + eps)) * gamma (the
-// VALU's reciprocal square root instruction, about 1 ulp): the
-// waves' partial sums of squares meet in LDS and are added in wave order.
-// `lo` (optional) receives the remainder x - round(x) for the router's split
-// operand.
+// kMaxT x kRowCh float4s and the gain slice they share.  With NORM the rows
+// are RMS-normalised, but not on the way: what is stored is h * gamma, and
+// 1/rms = rsqrt(mean(h^2) + eps) of each row (the VALU's reciprocal square
+// root instruction, about 1 ulp; the waves' partial sums of squares meet in
+// LDS and are added in wave order) goes to LDS (rsc_lds) for the consumers'
+// epilogues to scale their products by -- W (h gamma / rms) = (W (h gamma)) /
+// rms -- so no cross-wave reduction lies between the row loads and the stores
+// the first matrix product waits for.  `lo` (optional) receives the remainder
+// x - round(x) for the router's split operand.
 //
-// issue() only requests the row (and gain) loads; finish() normalises and
-// stores them.  A phase that also streams weights calls issue(), then requests
-// its first weight chunk, then finish(): each wave's loads complete in order,
-// so the activation rows arrive ahead of the weights instead of behind them.
-// Every lane issues the same number of loads (indices past a row are clamped
-// to its last float4, rows past T-1 to row T-1; neither is stored), so the
-// compiler can wait for exactly the older loads.
+// issue() only requests the row (and gain) loads; finish() stores them.  A
+// phase that also streams weights calls issue(), then requests its first
+// weight chunk, then finish(): each wave's loads complete in order, so the
+// activation rows arrive ahead of the weights instead of behind them.  Every
+// lane issues the same number of loads (indices past a row are clamped to its
+// last float4, rows past T-1 to row T-1; neither is stored), so the compiler
+// can wait for exactly the older loads.
 constexpr int kRowCh = kMaxModel / (kWaves * 64 * 4);     // float4s per lane per row
 constexpr int kNormLdsOff = kLdsBytes - 640;              // [kWaves][kMaxT] partial sums
+constexpr int kRscLdsOff = kLdsBytes - 384;               // [kMaxT] 1/rms of the staged rows
 static_assert(kTraceStride * 8 <= 384, "the normalisation partials follow the trace stamps");
+__device__ __forceinline__ const float* rsc_lds() {
+  extern __shared__ __attribute__((aligned(16))) char dyn_lds[];
+  return reinterpret_cast<const float*>(dyn_lds + kRscLdsOff);
+}
 template <class A, bool NORM>
 struct RowStager {
   f32x4 v[kMaxT][kRowCh];
@@ -160,9 +168,7 @@ struct RowStager {
     float* part = reinterpret_cast<float*>(dyn_lds + kNormLdsOff);
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int n4 = K / 4;
-    float r[kMaxT];
     if constexpr (NORM) {
-      const float invK = 1.0f / (float)K;
       float ss[kMaxT];
 #pragma unroll
       for (int t = 0; t < kMaxT; ++t) {
@@ -179,15 +185,6 @@ struct RowStager {
 #pragma unroll
         for (int t = 0; t < kMaxT; ++t) part[w * kMaxT + t] = ss[t];
       }
-      __syncthreads();
-      if (tr && threadIdx.x == 0) trace_lds()[2 + 2 * kBarriers + 14] = (long long)clock100();
-#pragma unroll
-      for (int t = 0; t < kMaxT; ++t) {
-        float ss = 0.f;
-#pragma unroll
-        for (int ww = 0; ww < kWaves; ++ww) ss += part[ww * kMaxT + t];
-        r[t] = __builtin_amdgcn_rsqf(ss * invK + eps);
-      }
     }
 #pragma unroll
     for (int c = 0; c < kRowCh; ++c) {
@@ -197,7 +194,7 @@ struct RowStager {
         for (int t = 0; t < kMaxT; ++t) {
           if (t < T) {
             f32x4 x = v[t][c];
-            if constexpr (NORM) x = (x * r[t]) * gm[c];
+            if constexpr (NORM) x = x * gm[c];
             store4<A>(xs + (long long)t * XS + 4 * i, x);
             if (lo) store4<A>(lo + (long long)t * XS + 4 * i, x - round4<A>(x));
           }
@@ -205,6 +202,15 @@ struct RowStager {
       }
     }
     __syncthreads();
+    if constexpr (NORM) {
+      // read by the epilogues after a later workgroup barrier
+      if ((int)threadIdx.x < kMaxT) {
+        float ss = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < kWaves; ++ww) ss += part[ww * kMaxT + threadIdx.x];
+        reinterpret_cast<float*>(dyn_lds + kRscLdsOff)[threadIdx.x] = __builtin_amdgcn_rsqf(ss * (1.0f / (float)K) + eps);
+      }
+    }
   }
 };
 
@@ -283,7 +289,9 @@ __device__ __forceinline__ void phase_qkv(const LayerParams& p, char* smem) {
   } src{p.wq, p.wdkv, RTq, KT, S, NT, bl};
   float* part = p.qkv_part;
   const int nq = p.nq, kvw = p.kvw;
+  const float* rsc = rsc_lds();       // the staged rows are h * gamma: scale by 1/rms
   auto epi = [=](int u, int row, int col, float v, float) {
+    v *= rsc[col];
     int rt = u / S, s = u - rt * S;
     int idx;
     if (rt < RTq) idx = rt * 16 + row;
@@ -1125,7 +1133,10 @@ __device__ __forceinline__ void gateup_units(const LayerParams& p, const uint8_t
   Src src{blk, RT, KT, nbk, bl, sc_off, sc_off + nsc13 * 4};
   A* hb = reinterpret_cast<A*>(p.hbuf);
   const int f = p.f;
+  const float* rsc = rsc_lds();       // the staged rows are h * gamma: scale by 1/rms
   auto epi = [=](int u, int row, int col, float v, float v2) {
+    v *= rsc[col];
+    v2 *= rsc[col];
     const int sl = s0 + u / RT, rt = u % RT;
     const float sg = v / (1.0f + expf(-v));
     hb[((long long)sl * T + col) * f + rt * 16 + row] = to_act<A>(sg * v2);
@@ -1135,6 +1146,11 @@ __device__ __forceinline__ void gateup_units(const LayerParams& p, const uint8_t
     // so a down projection on any XCD reads them once the slot's counter is
     // full); the reply tells the stream engine when the write has completed
     auto epi2 = [=](int u, int row, int col, float v0, float w0, float v1, float w1) -> uint32_t {
+      const float rc = rsc[col];
+      v0 *= rc;
+      w0 *= rc;
+      v1 *= rc;
+      w1 *= rc;
       const int sl = s0 + u / RT, rt = u % RT;
       const float h0 = (v0 / (1.0f + expf(-v0))) * w0, h1 = (v1 / (1.0f + expf(-v1))) * w1;
       A* dst = hb + ((long long)sl * T + col) * f + rt * 16 + row;
@@ -1236,7 +1252,8 @@ __device__ __forceinline__ void phase_router(const LayerParams& p, char* smem) {
     __device__ const float* sbase2(int) const { return nullptr; }
   } src{p.wr, KT, bl, (long long)(lp.xb / (int)sizeof(A))};
   float* lgl = reinterpret_cast<float*>(smem + 2 * lp.xb + 2 * kWaves * 64 * 4 * 4);   // [4][kMaxT][16]
-  auto epi = [=](int u, int row, int col, float v, float) { lgl[((u - u0) * kMaxT + col) * 16 + row] = v; };
+  const float* rsc = rsc_lds();       // the staged rows are h * gamma: scale by 1/rms
+  auto epi = [=](int u, int row, int col, float v, float) { lgl[((u - u0) * kMaxT + col) * 16 + row] = v * rsc[col]; };
   RowStager<A, true> rs;
   rs.issue(p.hp, T, p.d, p.g2);
   Chunk<AF, false, 16> ck;
