@@ -7,18 +7,22 @@ positions, vocab 129280), run as a device-resident verify loop: every step is
 the embedding gather, 32 layer launches and one LM-head/argmax/accept launch,
 with the KV length kept on the device.  Weights and inputs are synthetic and
 seeded (the trained model is not used); with random weights almost no draft is
-accepted, so a step commits ~1 token.
+accepted, so a step commits ~1 token, and tokens/s is also given for the
+acceptance lengths the pages report.
 
-Printed: one JSON line with the step time, tokens/s per stream, per-layer
-microseconds, algorithmic HBM bytes and bandwidth, the roofline of the layer
-kernel (live HIP-event timing of its launches), and the CPU oracle timed on a
-bounded sample as a baseline.  --workload C2|C3|C4 times a single layer
-instead (three rotating weight copies so the 256 MB last-level cache cannot
-serve repeats).
+Printed: one JSON line with the step time (and its per-step median, p10, p90),
+tokens/s per stream, per-layer microseconds, algorithmic HBM bytes and
+bandwidth, the roofline of the layer kernel (live HIP-event timing of its
+launches), the share of the layer kernel's time spent in grid barriers (from
+its in-kernel trace, on an untimed step), launches per step, the spread over
+several process starts, and the CPU oracle timed on a bounded sample as a
+baseline.  --workload C2|C3|C4 times a single layer instead (three rotating
+weight copies so the 256 MB last-level cache cannot serve repeats).
 """
 import argparse
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -29,6 +33,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decode step µs/layer & tok/s/stream at T=6; achieved HBM GB/s vs peak"
 PEAK_GBPS = 8000.0      # MI355X HBM3E peak
+TAUS = (3.3, 4.0, 5.17)  # tokens per verify step the pages report (bench, live traffic, single-GB300 lane)
 
 
 def log(*a):
@@ -98,46 +103,136 @@ def cores_used():
     return min(n, int(omp)) if omp and omp.isdigit() else n
 
 
-def cpu_baseline_stack(s, tokens_per_step):
-    """The oracle (untuned) on a bounded sample: one layer step (layer 0, T rows
-    at the initial cache length, experts drawn on demand) and one LM-head step;
-    a stack step is extrapolated as n_layers layer steps + one head step."""
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def pct(xs):
+    xs = np.asarray(xs, np.float64)
+    return {"median": round(float(np.median(xs)), 4), "p10": round(float(np.percentile(xs, 10)), 4),
+            "p90": round(float(np.percentile(xs, 90)), 4)}
+
+
+# ---------------------------------------------------------------- in-kernel trace: barrier share
+def trace_summary(layers, run_once):
+    """Runs one untimed step with the layers' in-kernel trace on and returns the
+    mean over the traced launches of: time in grid barriers (from the last
+    arrival to the release), the critical path of each phase, and the launch's
+    in-kernel total.  Timestamps: 100 MHz, per workgroup."""
+    for dl in layers:
+        dl.layer.set_trace(True)
+    run_once()
+    totals, bars, phases = [], [], []
+    for dl in layers:
+        st = dl.layer.stats()
+        nb = st.barriers_per_step
+        stride = 2 + 2 * nb + 16
+        tr = np.zeros((st.grid_wgs, stride), np.int64)
+        dl.layer.read_trace(tr)
+        start, end = tr[:, 0], tr[:, 1 + 2 * nb]
+        prev = start
+        bsum, ph = 0.0, []
+        for k in range(nb):
+            arr, rel = tr[:, 1 + 2 * k], tr[:, 2 + 2 * k]
+            if (arr == 0).all():
+                continue
+            ph.append((arr.max() - prev.min()) / 100.0)
+            bsum += (np.median(rel) - arr.max()) / 100.0
+            prev = rel
+        ph.append((end.max() - prev.min()) / 100.0)
+        totals.append((end.max() - start.min()) / 100.0)
+        bars.append(bsum)
+        phases.append(ph)
+    for dl in layers:
+        dl.layer.set_trace(False)
+    n = min(len(p) for p in phases)
+    return {"barrier_share": round(float(np.mean(bars) / np.mean(totals)), 4),
+            "barrier_us_per_launch": round(float(np.mean(bars)), 2),
+            "in_kernel_us_per_launch": round(float(np.mean(totals)), 2),
+            "phase_critical_path_us": [round(float(np.mean([p[i] for p in phases])), 2) for i in range(n)],
+            "phases": "P0 Q/KV proj, P1 RoPE+absorb, P2 attention, P3 merge+W_UV, P4 W_O, P5 norm+router, "
+                      "P6/7 experts, P8 combine",
+            "launches_traced": len(layers)}
+
+
+# ---------------------------------------------------------------- CPU baseline
+def _omp_threads(n):
+    import ctypes
+    try:
+        ctypes.CDLL("libgomp.so.1").omp_set_num_threads(int(n))
+    except OSError:
+        pass
+
+
+def _time_layer(s, wx, H, kv, reps):
+    import oracle
+    ts = []
+    for _ in range(reps):
+        k = kv.copy()
+        t0 = time.perf_counter()
+        oracle.layer_step(s, wx, H, k, s.L)
+        ts.append(time.perf_counter() - t0)
+    return ts
+
+
+def cpu_layer_sample(s):
+    """The oracle (untuned) on one layer step of the workload: all cores, three
+    repeats, and once on one thread; the routed experts the step needs are drawn
+    beforehand (outside the timing)."""
     import oracle
     from synth import recipe
     w = recipe.layer_weights_host(s, 0, 0, experts=[])
     H = recipe.hidden_host(s, 0, 0)
     kv = recipe.kv_prefill_host(s, 0, 0)
-    # draw the routed experts this step needs outside the timed region
     _, _, wx = oracle.layer_step_lazy(s, 0, 0, H, kv.copy(), s.L, base_weights=w)
-    t0 = time.perf_counter()
-    oracle.layer_step(s, wx, H, kv, s.L)
-    t_layer = time.perf_counter() - t0
+    n = cores_used()
+    _omp_threads(n)
+    multi = _time_layer(s, wx, H, kv, 3)
+    _omp_threads(1)
+    single = _time_layer(s, wx, H, kv, 1)[0]
+    _omp_threads(n)
+    return multi, single
+
+
+def cpu_baseline_stack(s, tokens_per_step):
+    """A stack step is extrapolated as n_layers layer steps + one LM-head step."""
+    import oracle
+    from synth import recipe
+    multi, single = cpu_layer_sample(s)
     emb, head, gf = recipe.stack_tables_host(s, 0)
     h = oracle.embed(emb, recipe.tokens_host(s, 0, 0))
     t0 = time.perf_counter()
     oracle.head(head, gf, h, s.eps, want_logits=False)
     t_head = time.perf_counter() - t0
+    t_layer = float(np.median(multi))
     t_step = s.n_layers * t_layer + t_head
     return {"value": tokens_per_step / t_step, "unit": "tok/s/stream", "cores": cores_used(), "kind": "oracle",
-            "sample": "one layer step (layer 0, T=%d, L=%d, experts drawn beforehand) took %.2f s and one LM-head "
-                      "step %.2f s; stack step = %d x layer + head = %.1f s; tokens/step as realized on the GPU"
-                      % (s.T, s.L, t_layer, t_head, s.n_layers, t_step)}
+            "cpu_model": cpu_model(),
+            "layer_step_s_all_cores": [round(x, 3) for x in multi],
+            "layer_step_s_one_thread": round(single, 3),
+            "head_step_s_all_cores": round(t_head, 3),
+            "sample": "one layer step (layer 0, T=%d, L=%d, experts drawn beforehand) timed 3 times on %d threads "
+                      "(median %.3f s) and once on 1 thread (%.2f s), one LM-head step %.2f s; stack step = %d x "
+                      "layer + head = %.1f s; tokens/step as realized on the GPU"
+                      % (s.T, s.L, cores_used(), t_layer, single, t_head, s.n_layers, t_step)}
 
 
 def cpu_baseline_layer(s):
-    import oracle
-    from synth import recipe
-    w = recipe.layer_weights_host(s, 0, 0, experts=[])
-    H = recipe.hidden_host(s, 0, 0)
-    kv = recipe.kv_prefill_host(s, 0, 0)
-    _, _, wx = oracle.layer_step_lazy(s, 0, 0, H, kv.copy(), s.L, base_weights=w)
-    t0 = time.perf_counter()
-    oracle.layer_step(s, wx, H, kv, s.L)
-    t = time.perf_counter() - t0
-    return {"value": t * 1e6, "unit": "us/layer", "cores": cores_used(), "kind": "oracle",
-            "sample": "one layer step (T=%d, L=%d), experts drawn beforehand" % (s.T, s.L)}
+    multi, single = cpu_layer_sample(s)
+    t = float(np.median(multi))
+    return {"value": t * 1e6, "unit": "us/layer", "cores": cores_used(), "kind": "oracle", "cpu_model": cpu_model(),
+            "layer_step_s_all_cores": [round(x, 3) for x in multi], "layer_step_s_one_thread": round(single, 3),
+            "sample": "one layer step (T=%d, L=%d), experts drawn beforehand, 3 times on %d threads, once on 1"
+                      % (s.T, s.L, cores_used())}
 
 
+# ---------------------------------------------------------------- stack
 def run_stack(s, args):
     import torch
     from decoder_megakernel_amd import harness
@@ -149,34 +244,39 @@ def run_stack(s, args):
     st = harness.DeviceStack(s, seed=0)
     log("[bench] stack of %d layers built in %.1f s" % (n_layers, time.perf_counter() - t0))
     K, W = args.steps, args.warmup
-    drafts = np.stack([recipe.tokens_host(s, 0, i + 1)[1:] for i in range(W + K)]).astype(np.int32)
+    drafts = np.stack([recipe.tokens_host(s, 0, i + 1)[1:] for i in range(W + K + 2)]).astype(np.int32)
     drafts_d = torch.from_numpy(drafts).to(dev)
     tokens = torch.from_numpy(recipe.tokens_host(s, 0, 0)).to(dev)
     am = torch.empty(s.T, dtype=torch.int32, device=dev)
     com = torch.zeros(s.T + 1, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream(dev)
     sh = stream.cuda_stream
-    for i in range(W):
+
+    def step(i):
         st.model.step(tokens.data_ptr(), s.T, drafts_d[i].data_ptr(), am.data_ptr(), com.data_ptr(), None, sh)
+
+    for i in range(W):
+        step(i)
     torch.cuda.synchronize(dev)
     len0 = read_i32(st.model.length_ptr())
     stats0 = [dl.layer.stats() for dl in st.layers]
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
     torch.cuda.synchronize(dev)
-    ev0.record(stream)
+    evs[0].record(stream)
     for i in range(K):
-        st.model.step(tokens.data_ptr(), s.T, drafts_d[W + i].data_ptr(), am.data_ptr(), com.data_ptr(), None, sh)
-    ev1.record(stream)
+        step(W + i)
+        evs[i + 1].record(stream)
     torch.cuda.synchronize(dev)
-    for dl in st.layers:
-        if dl.layer.sync_status() != 0:
-            raise RuntimeError("device fault during the timed steps")
-    ms = ev0.elapsed_time(ev1)
+    if st.model.sync_status() != 0:
+        raise RuntimeError("device fault during the timed steps")
+    ms = evs[0].elapsed_time(evs[K])
+    per_step = [evs[i].elapsed_time(evs[i + 1]) for i in range(K)]
     len1 = read_i32(st.model.length_ptr())
     stats1 = [dl.layer.stats() for dl in st.layers]
     committed = len1 - len0
     slots = [(b.expert_blocks_sum - a.expert_blocks_sum) / max(1, b.device_launches - a.device_launches)
              for a, b in zip(stats0, stats1)]
+    layer_launches = sum(b.launches - a.launches for a, b in zip(stats0, stats1))
     Lavg = 0.5 * (len0 + len1)
     step_bytes = sum(layer_bytes(s, Lavg, sl) for sl in slots) + s.V * s.d * 2 + s.T * s.d * 2 + s.d * 4
     ms_step = ms / K
@@ -204,6 +304,12 @@ def run_stack(s, args):
                for a, b in zip(stats2, stats3)]
     lb = sum(layer_bytes(s, Lnow, sl) for sl in slots_l) / n_layers
     achieved = lb / (us_layer * 1e-6) / 1e9
+
+    def traced_step():
+        step(W + K)
+        torch.cuda.synchronize(dev)
+
+    tsum = trace_summary(st.layers, traced_step) if args.layer_trace else None
     res = {
         "metric": METRIC, "value": round(tok_s, 3), "unit": "tok/s/stream", "n_gpus": 1, "steps": K, "warmup": W,
         "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
@@ -214,11 +320,16 @@ def run_stack(s, args):
                    "bf16 attention/router/embedding/head", "kv": s.kv_fmt,
                    "compute": "bf16 MFMA operands, fp32 accumulation"},
         "tokens_per_step": round(committed / K, 4),
+        "ms_per_step_dist": pct(per_step),
+        "tok_s_at_tokens_per_step": {str(t): round(t / (ms_step * 1e-3), 1) for t in TAUS},
+        "launches_per_step": round(layer_launches / K + 2, 2),
         "us_per_layer_step": round(ms_step * 1e3 / n_layers, 2),
         "us_per_layer_kernel": round(us_layer, 2),
         "step_bytes": int(step_bytes),
         "hbm_gbps_step": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
         "experts_streamed_per_layer": round(float(np.mean(slots)), 2),
+        "barrier_share": tsum["barrier_share"] if tsum else None,
+        "layer_trace": tsum,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_GBPS, 4),
                      "traffic": measured_traffic("layer_kernel_stack32_fp8_T6_hbm_counters.json"),
@@ -231,6 +342,7 @@ def run_stack(s, args):
     return res
 
 
+# ---------------------------------------------------------------- single layer
 def run_layer(s, args):
     import torch
     from decoder_megakernel_amd import harness
@@ -247,32 +359,46 @@ def run_layer(s, args):
     out = torch.empty((s.T, s.d), dtype=torch.float32, device=dev)
     seq = [(c, j) for j in range(4) for c in range(3)]
 
-    def run(n, off):
-        for i in range(n):
-            c, j = seq[(off + i) % len(seq)]
-            dl, kv, hs = copies[c]
-            dl.layer.decode_step(hs[j].data_ptr(), s.T, kv.data_ptr(), kv.shape[0], s.L, out.data_ptr(), sh)
+    def launch(i):
+        c, j = seq[i % len(seq)]
+        dl, kv, hs = copies[c]
+        dl.layer.decode_step(hs[j].data_ptr(), s.T, kv.data_ptr(), kv.shape[0], s.L, out.data_ptr(), sh)
 
-    run(args.warmup, 0)
+    for i in range(args.warmup):
+        launch(i)
     torch.cuda.synchronize(dev)
     st0 = [c[0].layer.stats() for c in copies]
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    run(args.steps, args.warmup)
-    e1.record(stream)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    evs[0].record(stream)
+    for i in range(args.steps):
+        launch(args.warmup + i)
+        evs[i + 1].record(stream)
     torch.cuda.synchronize(dev)
-    us = e0.elapsed_time(e1) * 1e3 / args.steps
+    for c in copies:
+        if c[0].layer.sync_status() != 0:
+            raise RuntimeError("device fault during the timed steps")
+    us = evs[0].elapsed_time(evs[-1]) * 1e3 / args.steps
+    per = [evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(args.steps)]
     st1 = [c[0].layer.stats() for c in copies]
     slots = sum(b.expert_blocks_sum - a.expert_blocks_sum for a, b in zip(st0, st1)) / args.steps
     lb = layer_bytes(s, s.L, slots)
     achieved = lb / (us * 1e-6) / 1e9
+
+    def traced():
+        launch(0)
+        torch.cuda.synchronize(dev)
+
+    tsum = trace_summary([copies[0][0]], traced) if args.layer_trace else None
     res = {
         "metric": METRIC, "value": round(us, 2), "unit": "us/layer", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(us / 1e3, 4), "higher_is_better": False, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": s.name, "T": s.T, "L": s.L, "experts": s.E, "top_k": s.top_k, "d_model": s.d,
-                   "d_ff": s.f, "expert_format": s.exp_fmt, "weight_copies": 3},
+                   "d_ff": s.f, "expert_format": s.exp_fmt, "routing": s.routing, "weight_copies": 3},
+        "us_per_launch_dist": pct(per),
         "experts_streamed_per_step": round(slots, 2), "step_bytes": int(lb),
+        "barrier_share": tsum["barrier_share"] if tsum else None,
+        "layer_trace": tsum,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_GBPS, 4), "traffic": None, "bytes_per_launch": int(lb),
                      "avg_launch_us": round(us, 2)},
@@ -280,6 +406,22 @@ def run_layer(s, args):
     if args.cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_layer(s)
     return res
+
+
+def process_starts(args, n):
+    """Runs the same measurement in n separate processes (one after another,
+    before this process touches the GPU) and returns their values."""
+    vals = []
+    cmd = [sys.executable, os.path.abspath(__file__), "--workload", args.workload, "--steps", str(args.steps),
+           "--warmup", str(args.warmup), "--no-cpu-baseline", "--starts", "1"]
+    for i in range(n):
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError("bench child process failed (%d): %s" % (r.returncode, r.stderr[-2000:]))
+        v = json.loads(r.stdout.strip().splitlines()[-1])["value"]
+        log("[bench] process start %d: %s" % (i + 1, v))
+        vals.append(v)
+    return vals
 
 
 def main():
@@ -290,7 +432,11 @@ def main():
     ap.add_argument("--workload", default="C5", choices=["C2", "C3", "C4", "C5"])
     ap.add_argument("--layers", type=int, default=None, help="stack depth override (diagnostics only)")
     ap.add_argument("--layer-reps", type=int, default=4)
+    ap.add_argument("--starts", type=int, default=5,
+                    help="process starts measured (this one and starts-1 child processes run before it)")
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
+    ap.add_argument("--no-layer-trace", dest="layer_trace", action="store_false",
+                    help="skip the traced (untimed) step that measures the barrier share")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after timing, run one elementwise kernel reading and writing this many MiB (a "
                          "known-size kernel for scaling hardware byte counters in a profile)")
@@ -304,11 +450,16 @@ def main():
     if s.n_layers > 1:
         args.steps = args.steps or 256
         args.warmup = args.warmup if args.warmup is not None else 8
-        res = run_stack(s, args)
     else:
         args.steps = args.steps or 60
         args.warmup = args.warmup if args.warmup is not None else 12
-        res = run_layer(s, args)
+    others = process_starts(args, args.starts - 1) if args.starts > 1 and args.layers is None else []
+    res = run_stack(s, args) if s.n_layers > 1 else run_layer(s, args)
+    if others:
+        allv = others + [res["value"]]
+        res["process_starts"] = {"values": allv, "median": round(float(np.median(allv)), 3),
+                                 "min": min(allv), "max": max(allv),
+                                 "spread": round((max(allv) - min(allv)) / float(np.median(allv)), 4)}
     if args.calib_copy_mib:
         import torch
         n = args.calib_copy_mib << 20
