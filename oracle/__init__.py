@@ -20,8 +20,8 @@ from synth.configs import LayerShape
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB = os.path.join(_HERE, "liborc.so")
 
-ORC_F32, ORC_BF16, ORC_FP8B128 = 0, 1, 2
-_FMT = {"f32": ORC_F32, "bf16": ORC_BF16, "fp8": ORC_FP8B128}
+ORC_F32, ORC_BF16, ORC_FP8B128, ORC_MXFP4 = 0, 1, 2, 3
+_FMT = {"f32": ORC_F32, "bf16": ORC_BF16, "fp8": ORC_FP8B128, "mxfp4": ORC_MXFP4}
 
 _vp = ctypes.c_void_p
 _i = ctypes.c_int
@@ -82,6 +82,10 @@ def lib():
         L.orc_f32_to_bf16.argtypes = [ctypes.c_float]
         L.orc_e4m3_to_f32.restype = ctypes.c_float
         L.orc_e4m3_to_f32.argtypes = [ctypes.c_uint8]
+        L.orc_e2m1_to_f32.restype = ctypes.c_float
+        L.orc_e2m1_to_f32.argtypes = [ctypes.c_uint8]
+        L.orc_e8m0_to_f32.restype = ctypes.c_float
+        L.orc_e8m0_to_f32.argtypes = [ctypes.c_uint8]
         _lib = L
     return _lib
 

@@ -37,11 +37,26 @@ float orc_e4m3_to_f32(uint8_t q) {
   return s ? -v : v;
 }
 
+/* OCP MX E2M1: sign, 2 exponent bits (bias 1), 1 mantissa bit; exponent field
+ * 0 is subnormal (m * 0.5).  Magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6. */
+float orc_e2m1_to_f32(uint8_t code) {
+  int s = (code >> 3) & 1, e = (code >> 1) & 3, m = code & 1;
+  float v = (e == 0) ? 0.5f * (float)m : ldexpf(1.0f + 0.5f * (float)m, e - 1);
+  return s ? -v : v;
+}
+
+/* OCP MX E8M0 scale: 2^(e - 127); the code 255 is NaN. */
+float orc_e8m0_to_f32(uint8_t e) { return e == 255 ? NAN : ldexpf(1.0f, (int)e - 127); }
+
 static float e4m3_lut[256];
+static float e2m1_lut[16];
+static float e8m0_lut[256];
 static int e4m3_lut_ready = 0;
 static void lut_init(void) {
   if (!e4m3_lut_ready) {
     for (int i = 0; i < 256; ++i) e4m3_lut[i] = orc_e4m3_to_f32((uint8_t)i);
+    for (int i = 0; i < 16; ++i) e2m1_lut[i] = orc_e2m1_to_f32((uint8_t)i);
+    for (int i = 0; i < 256; ++i) e8m0_lut[i] = orc_e8m0_to_f32((uint8_t)i);
     e4m3_lut_ready = 1;
   }
 }
@@ -50,29 +65,36 @@ static void lut_init(void) {
 typedef struct {
   const void* p;
   int fmt;
-  const float* s; /* fp8 block scales */
+  const void* s; /* fp8: fp32 block scales; MXFP4: E8M0 codes */
   long rows, cols;
 } wmat;
 
-static wmat mk_wmat(const void* p, int fmt, const float* s, long rows, long cols) {
+static wmat mk_wmat(const void* p, int fmt, const void* s, long rows, long cols) {
   wmat m = {p, fmt, s, rows, cols};
   return m;
 }
 
-/* element (r, k) widened to fp32 exactly (fp8: fp32 product of code and scale) */
+/* element (r, k) widened to fp32 exactly (fp8: fp32 product of code and scale;
+ * MXFP4: E2M1 value times a power of two) */
 static inline float wat(const wmat* m, long r, long k) {
   long i = r * m->cols + k;
   if (m->fmt == ORC_F32) return ((const float*)m->p)[i];
   if (m->fmt == ORC_BF16) return orc_bf16_to_f32(((const uint16_t*)m->p)[i]);
+  if (m->fmt == ORC_MXFP4) {
+    uint8_t b = ((const uint8_t*)m->p)[r * (m->cols / 2) + k / 2];
+    uint8_t code = (k & 1) ? (uint8_t)(b >> 4) : (uint8_t)(b & 15);
+    return e2m1_lut[code] * e8m0_lut[((const uint8_t*)m->s)[r * (m->cols / 32) + k / 32]];
+  }
   long nbk = (m->cols + 127) / 128;
-  return e4m3_lut[((const uint8_t*)m->p)[i]] * m->s[(r / 128) * nbk + k / 128];
+  return e4m3_lut[((const uint8_t*)m->p)[i]] * ((const float*)m->s)[(r / 128) * nbk + k / 128];
 }
 static inline double wat64(const wmat* m, long r, long k) {
+  if (m->fmt == ORC_MXFP4) return (double)wat(m, r, k);     /* exact in fp32 */
   long i = r * m->cols + k;
   if (m->fmt == ORC_F32) return (double)((const float*)m->p)[i];
   if (m->fmt == ORC_BF16) return (double)orc_bf16_to_f32(((const uint16_t*)m->p)[i]);
   long nbk = (m->cols + 127) / 128;
-  return (double)e4m3_lut[((const uint8_t*)m->p)[i]] * (double)m->s[(r / 128) * nbk + k / 128];
+  return (double)e4m3_lut[((const uint8_t*)m->p)[i]] * (double)((const float*)m->s)[(r / 128) * nbk + k / 128];
 }
 
 /* y = W x, fp32, sequential over k */
@@ -163,6 +185,7 @@ static int check_cfg(const orc_cfg* c, int T) {
   if (!c || T < 0 || c->d <= 0 || c->n_h <= 0 || c->d_h <= 0 || c->d_c <= 0 || c->d_r <= 0 ||
       (c->d_r & 1) || c->E <= 0 || c->top_k <= 0 || c->top_k > c->E || c->f <= 0 || c->n_shared < 0)
     return -1;
+  if (c->exp_fmt == ORC_MXFP4 && (c->d % 32 || c->f % 32)) return -1;
   return 0;
 }
 
@@ -319,11 +342,11 @@ int orc_router(const orc_cfg* c, const orc_weights* w, const float* Hp, int T,
 static int expert_fwd(const orc_cfg* c, const orc_weights* w, int e, const float* x, float* y,
                       float* a, float* b) {
   if (!w->w1 || !w->w3 || !w->w2 || !w->w1[e] || !w->w3[e] || !w->w2[e]) return -3;
-  int fp8 = c->exp_fmt == ORC_FP8B128;
-  if (fp8 && (!w->s1 || !w->s3 || !w->s2 || !w->s1[e] || !w->s3[e] || !w->s2[e])) return -3;
-  wmat W1 = mk_wmat(w->w1[e], c->exp_fmt, fp8 ? w->s1[e] : NULL, c->f, c->d);
-  wmat W3 = mk_wmat(w->w3[e], c->exp_fmt, fp8 ? w->s3[e] : NULL, c->f, c->d);
-  wmat W2 = mk_wmat(w->w2[e], c->exp_fmt, fp8 ? w->s2[e] : NULL, c->d, c->f);
+  int sc = c->exp_fmt == ORC_FP8B128 || c->exp_fmt == ORC_MXFP4;
+  if (sc && (!w->s1 || !w->s3 || !w->s2 || !w->s1[e] || !w->s3[e] || !w->s2[e])) return -3;
+  wmat W1 = mk_wmat(w->w1[e], c->exp_fmt, sc ? w->s1[e] : NULL, c->f, c->d);
+  wmat W3 = mk_wmat(w->w3[e], c->exp_fmt, sc ? w->s3[e] : NULL, c->f, c->d);
+  wmat W2 = mk_wmat(w->w2[e], c->exp_fmt, sc ? w->s2[e] : NULL, c->d, c->f);
   matvec(&W1, x, a);
   matvec(&W3, x, b);
   for (int j = 0; j < c->f; ++j) a[j] = silu(a[j]) * b[j];
@@ -510,10 +533,10 @@ int orc_layer_step_f64(const orc_cfg* c, const orc_weights* w, const float* H, i
       if (t < k) { e = sel[t]; g = (exp(lg[e] - mx) / z) / zs; }
       else { e = E + (t - k); g = 1.0; }
       if (!w->w1 || !w->w1[e] || !w->w3[e] || !w->w2[e]) { rc = -3; break; }
-      int fp8 = c->exp_fmt == ORC_FP8B128;
-      wmat W1 = mk_wmat(w->w1[e], c->exp_fmt, fp8 ? w->s1[e] : NULL, c->f, d);
-      wmat W3 = mk_wmat(w->w3[e], c->exp_fmt, fp8 ? w->s3[e] : NULL, c->f, d);
-      wmat W2 = mk_wmat(w->w2[e], c->exp_fmt, fp8 ? w->s2[e] : NULL, d, c->f);
+      int sc = c->exp_fmt == ORC_FP8B128 || c->exp_fmt == ORC_MXFP4;
+      wmat W1 = mk_wmat(w->w1[e], c->exp_fmt, sc ? w->s1[e] : NULL, c->f, d);
+      wmat W3 = mk_wmat(w->w3[e], c->exp_fmt, sc ? w->s3[e] : NULL, c->f, d);
+      wmat W2 = mk_wmat(w->w2[e], c->exp_fmt, sc ? w->s2[e] : NULL, d, c->f);
       matvec64(&W1, xp, a);
       matvec64(&W3, xp, b);
       for (int j = 0; j < c->f; ++j) a[j] = silu64(a[j]) * b[j];

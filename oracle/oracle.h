@@ -27,6 +27,10 @@
  *    adjacent-pair form), SwiGLU (Shazeer 2020), softmax top-k gating with
  *    renormalised gates over the selected experts.
  *  - OCP 8-bit floating point specification (E4M3) for fp8 weights.
+ *  - OCP Microscaling Formats (MX) specification v1.0 for MXFP4 expert weights
+ *    (E2M1 elements, E8M0 block scales over 32 elements): "DeepSeek-V4.1-Flash
+ *    breaks 1,000 tokens per second for one user", section "Appendix: method",
+ *    names MXFP4 expert weights as the serving format.
  *
  * Readings where the pages are silent (each listed in the design notes):
  * eps = 1e-6; softmax scale 1/sqrt(d_h + d_r); RoPE base 10000 with the angle
@@ -35,7 +39,8 @@
  * renormalised to sum to 1; the shared expert is added with weight 1; new KV
  * rows are rounded to the cache's storage format and read back by attention.
  *
- * Arithmetic: weights are widened/dequantised exactly (fp8: (float)q * s);
+ * Arithmetic: weights are widened/dequantised exactly (fp8: (float)q * s;
+ * MXFP4: E2M1(q) * 2^(e-127));
  * activations are fp32; every dot product accumulates in fp32 in increasing
  * index order.  The *_f64 entry points redo the layer in double precision in
  * the un-absorbed form (per-head keys and values expanded from the latent).
@@ -47,7 +52,7 @@
 extern "C" {
 #endif
 
-enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_FP8B128 = 2 };
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_FP8B128 = 2, ORC_MXFP4 = 3 };
 
 typedef struct orc_cfg {
   int d;          /* hidden size */
@@ -57,7 +62,7 @@ typedef struct orc_cfg {
   int n_shared;   /* shared experts (always applied, weight 1) */
   int f;          /* expert FFN width */
   int attn_fmt;   /* ORC_F32 | ORC_BF16: W_Q, W_DKV, W_UK, W_UV, W_O, W_R */
-  int exp_fmt;    /* ORC_F32 | ORC_BF16 | ORC_FP8B128: W1, W3, W2 */
+  int exp_fmt;    /* ORC_F32 | ORC_BF16 | ORC_FP8B128 | ORC_MXFP4: W1, W3, W2 */
   int kv_fmt;     /* ORC_F32 | ORC_BF16 */
   float eps;      /* RMSNorm epsilon */
   double rope_base;
@@ -72,7 +77,12 @@ typedef struct orc_cfg {
  *   W_UV  [n_h][d_h][d_c]      v_h   = W_UV[h] c
  *   W_O   [d][n_h*d_h]
  *   W_R   [E][d], router_bias [E] or NULL
- *   W1,W3 [f][d], W2 [d][f]; fp8 scales [ceil(rows/128)][ceil(cols/128)]   */
+ *   W1,W3 [f][d], W2 [d][f]; fp8 scales [ceil(rows/128)][ceil(cols/128)] fp32
+ *   MXFP4 (OCP Microscaling Formats spec v1.0: E2M1 elements, one E8M0 scale
+ *   per block of 32 consecutive elements): W1, W3, W2 as bytes [rows][cols/2],
+ *   element 2j in the low nibble of byte j and 2j+1 in the high nibble; the
+ *   scales s1, s3, s2 as bytes [rows][cols/32]; element value = E2M1(code) *
+ *   2^(scale - 127), exact in fp32.  cols must be a multiple of 32. */
 typedef struct orc_weights {
   const float* gamma1;
   const float* gamma2;
@@ -86,9 +96,9 @@ typedef struct orc_weights {
   const void* const* w1;
   const void* const* w3;
   const void* const* w2;
-  const float* const* s1;
-  const float* const* s3;
-  const float* const* s2;
+  const void* const* s1;    /* fp8: const float* scales; MXFP4: const uint8_t* E8M0 codes */
+  const void* const* s3;
+  const void* const* s2;
 } orc_weights;
 
 /* Optional intermediate outputs (any pointer may be NULL). */
@@ -153,6 +163,8 @@ int orc_greedy_accept(const int32_t* tokens, const int32_t* a, int T, int32_t* c
 float orc_bf16_to_f32(uint16_t b);
 uint16_t orc_f32_to_bf16(float x);
 float orc_e4m3_to_f32(uint8_t q);
+float orc_e2m1_to_f32(uint8_t code);   /* low 4 bits: S.EE.M, bias 1 */
+float orc_e8m0_to_f32(uint8_t e);      /* 2^(e-127); 255 is NaN */
 
 #ifdef __cplusplus
 }

@@ -1,7 +1,8 @@
 """Seeded synthetic inputs shared by the CPU oracle side and the GPU side.
 
 This package only draws numbers and encodes them into storage formats (fp32,
-bf16, OCP fp8 E4M3 with 128x128 block scales); it holds none of the decoder
+bf16, OCP fp8 E4M3 with 128x128 block scales, OCP MXFP4 with E8M0 scales per
+32 elements); it holds none of the decoder
 layer's arithmetic.  The generator definition is written out in ``synth.h``.
 Two builds implement it: ``libmksynth_host.so`` (C, OpenMP) and
 ``libmksynth_dev.so`` (HIP); a GPU test checks that they agree bit for bit.
@@ -59,6 +60,9 @@ def _host_lib():
         lib.mks_host_fp8_blocks.argtypes = [_vp, _vp, _i64, _i64, _u64, _u64, _f32]
         lib.mks_host_e4m3_encode.restype = ctypes.c_uint8
         lib.mks_host_e4m3_encode.argtypes = [_f32]
+        lib.mks_host_e2m1_encode.restype = ctypes.c_uint8
+        lib.mks_host_e2m1_encode.argtypes = [_f32]
+        lib.mks_host_mxfp4_blocks.argtypes = [_vp, _vp, _i64, _i64, _u64, _u64, _f32]
         lib.mks_host_bf16_encode.restype = ctypes.c_uint16
         lib.mks_host_bf16_encode.argtypes = [_f32]
         _host = lib
@@ -75,8 +79,9 @@ def _dev_lib():
         lib.mks_dev_normal_f32.argtypes = [_vp, _u64, _u64, _u64, _u64, _f32, _f32, _vp]
         lib.mks_dev_normal_bf16.argtypes = [_vp, _u64, _u64, _u64, _u64, _f32, _f32, _vp]
         lib.mks_dev_fp8_blocks.argtypes = [_vp, _vp, _i64, _i64, _u64, _u64, _f32, _vp]
+        lib.mks_dev_mxfp4_blocks.argtypes = [_vp, _vp, _i64, _i64, _u64, _u64, _f32, _vp]
         for f in (lib.mks_dev_raw_fill, lib.mks_dev_normal_f32, lib.mks_dev_normal_bf16,
-                  lib.mks_dev_fp8_blocks):
+                  lib.mks_dev_fp8_blocks, lib.mks_dev_mxfp4_blocks):
             f.restype = ctypes.c_int
         _dev = lib
     return _dev
@@ -136,6 +141,20 @@ def fp8_blocks(R: int, K: int, seed: int, stream: int, sigma: float):
     return codes, scales
 
 
+def mxfp4_blocks(R: int, K: int, seed: int, stream: int, sigma: float):
+    """(codes uint8 [R][K/2], two E2M1 codes per byte; E8M0 scale codes uint8 [R][K/32])."""
+    if K % 32:
+        raise ValueError("MXFP4 rows must be a multiple of 32 long")
+    codes = np.empty((R, K // 2), dtype=np.uint8)
+    scales = np.empty((R, K // 32), dtype=np.uint8)
+    _host_lib().mks_host_mxfp4_blocks(_ptr(codes), _ptr(scales), R, K, seed, stream, sigma_c(sigma))
+    return codes, scales
+
+
+def e2m1_encode(x: float) -> int:
+    return int(_host_lib().mks_host_e2m1_encode(float(x)))
+
+
 def e4m3_encode(x: float) -> int:
     return int(_host_lib().mks_host_e4m3_encode(float(x)))
 
@@ -178,6 +197,12 @@ def dev_normal_bf16(dst_ptr: int, n: int, seed: int, stream: int, sigma: float, 
                     offset: int = 0, hip_stream: int = 0):
     _chk(_dev_lib().mks_dev_normal_bf16(dst_ptr, n, seed, stream, offset, sigma_c(sigma),
                                         float(np.float32(mean)), hip_stream), "mks_dev_normal_bf16")
+
+
+def dev_mxfp4_blocks(codes_ptr: int, scales_ptr: int, R: int, K: int, seed: int, stream: int,
+                     sigma: float, hip_stream: int = 0):
+    _chk(_dev_lib().mks_dev_mxfp4_blocks(codes_ptr, scales_ptr, R, K, seed, stream, sigma_c(sigma),
+                                         hip_stream), "mks_dev_mxfp4_blocks")
 
 
 def dev_fp8_blocks(codes_ptr: int, scales_ptr: int, R: int, K: int, seed: int, stream: int,

@@ -16,7 +16,7 @@ import os
 
 import numpy as np
 
-from . import fp8_blocks, normal_bf16, normal_f32, permutation, stream_id, uniform_ints
+from . import fp8_blocks, mxfp4_blocks, normal_bf16, normal_f32, permutation, stream_id, uniform_ints
 from .configs import HOT_FRACTION, LayerShape
 
 W_SIGMA = 0.02
@@ -50,7 +50,8 @@ def expert_pool_layer(s: LayerShape, layer: int) -> int:
 
 
 def expert_host(s: LayerShape, seed: int, layer: int, slot: int):
-    """(w1, w3, w2, s1, s3, s2) of expert slot `slot`; scales are None unless fp8."""
+    """(w1, w3, w2, s1, s3, s2) of expert slot `slot`; scales are None unless fp8
+    (fp32 per 128x128 block) or mxfp4 (E8M0 codes per 32 elements of a row)."""
     lay = expert_pool_layer(s, layer) if slot < s.E else layer
     out = []
     scales = []
@@ -58,6 +59,10 @@ def expert_host(s: LayerShape, seed: int, layer: int, slot: int):
         st = stream_id(tag, lay, slot)
         if s.exp_fmt == "fp8":
             q, sc = fp8_blocks(R, K, seed, st, W_SIGMA)
+            out.append(q)
+            scales.append(sc)
+        elif s.exp_fmt == "mxfp4":
+            q, sc = mxfp4_blocks(R, K, seed, st, W_SIGMA)
             out.append(q)
             scales.append(sc)
         elif s.exp_fmt == "bf16":

@@ -29,6 +29,19 @@
  *                edges); per block s = amax/448 (s = 1 when amax == 0),
  *                codes q = e4m3(w / s) with IEEE division.  Scales are
  *                stored row-major [ceil(R/128)][ceil(K/128)].
+ *   e2m1(x)      OCP Microscaling (MX) E2M1: magnitudes 0, 0.5, 1, 1.5, 2,
+ *                3, 4, 6 with codes 0..7 and the sign in bit 3; round to
+ *                nearest, a tie going to the even code; saturating at +-6.
+ *   mxfp4 blocks a [R][K] tensor of normal() values (element (r,k) drawn at
+ *                counter r*K+k, as for fp8 blocks), K a multiple of 32, cut
+ *                into groups of 32 consecutive elements of a row; per group
+ *                with amax = max |w|: e = floor(log2 amax) - 2 (exact, from
+ *                amax's exponent bits; 2 is E2M1's largest exponent), scale
+ *                code = e + 127 clamped to [0, 254] (code 0 when amax == 0),
+ *                X = 2^(code - 127), elements q = e2m1(w / X) (an exact
+ *                division by a power of two).  Codes are packed two per byte,
+ *                element 2j in the low nibble of byte j: [R][K/2]; scale codes
+ *                (E8M0) [R][K/32].
  */
 #ifndef MK_SYNTH_H
 #define MK_SYNTH_H
@@ -46,7 +59,10 @@ void mks_host_normal_bf16(uint16_t* dst, uint64_t n, uint64_t seed, uint64_t str
                           uint64_t offset, float c, float mean);
 void mks_host_fp8_blocks(uint8_t* codes, float* scales, int64_t R, int64_t K,
                          uint64_t seed, uint64_t stream, float c);
+void mks_host_mxfp4_blocks(uint8_t* codes, uint8_t* scales, int64_t R, int64_t K,
+                           uint64_t seed, uint64_t stream, float c);
 uint8_t mks_host_e4m3_encode(float x);
+uint8_t mks_host_e2m1_encode(float x);
 uint16_t mks_host_bf16_encode(float x);
 
 /* device (synth_dev.hip); every call is asynchronous on `stream_handle`
@@ -59,6 +75,8 @@ int mks_dev_fp8_blocks(uint8_t* codes, float* scales, int64_t R, int64_t K,
                        uint64_t seed, uint64_t stream, float c, void* stream_handle);
 int mks_dev_raw_fill(uint64_t* dst, uint64_t n, uint64_t seed, uint64_t stream,
                      uint64_t offset, void* stream_handle);
+int mks_dev_mxfp4_blocks(uint8_t* codes, uint8_t* scales, int64_t R, int64_t K,
+                         uint64_t seed, uint64_t stream, float c, void* stream_handle);
 
 #ifdef __cplusplus
 }

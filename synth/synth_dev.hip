@@ -51,6 +51,25 @@ __device__ inline uint8_t e4m3_encode(float x) {
   return sign | (uint8_t)code;
 }
 
+__device__ inline uint8_t e2m1_encode(float x) {
+  const float mid[7] = {0.25f, 0.75f, 1.25f, 1.75f, 2.5f, 3.5f, 5.0f};
+  const uint8_t sign = (uint8_t)((__float_as_uint(x) >> 28) & 8u);
+  const float a = fabsf(x);
+  int i = 0;
+  while (i < 7 && a > mid[i]) ++i;
+  if (i < 7 && a == mid[i] && (i & 1)) ++i;
+  return sign | (uint8_t)i;
+}
+__device__ inline int floor_log2(float a) {
+  const uint32_t u = __float_as_uint(a);
+  const int e = (int)((u >> 23) & 0xFF);
+  if (e) return e - 127;
+  uint32_t m = u & 0x7FFFFFu;
+  int k = -127;
+  while (!(m & 0x400000u)) { m <<= 1; --k; }
+  return k;
+}
+
 __global__ void k_raw(uint64_t* dst, uint64_t n, uint64_t key, uint64_t offset) {
   for (uint64_t i = blockIdx.x * (uint64_t)blockDim.x + threadIdx.x; i < n;
        i += (uint64_t)gridDim.x * blockDim.x)
@@ -94,6 +113,32 @@ __global__ __launch_bounds__(256) void k_fp8_blocks(uint8_t* codes, float* scale
   }
 }
 
+// One thread per group of 32 consecutive elements of a row.
+__global__ __launch_bounds__(256) void k_mxfp4_blocks(uint8_t* codes, uint8_t* scales, int64_t R, int64_t K,
+                                                      uint64_t key, float c) {
+  const int64_t ng = K / 32;
+  for (int64_t gi = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; gi < R * ng; gi += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = gi / ng, g = gi % ng;
+    float w[32];
+    float amax = 0.0f;
+    for (int j = 0; j < 32; ++j) {
+      w[j] = normal_at(key, (uint64_t)(r * K + g * 32 + j), c, 0.0f);
+      amax = fmaxf(amax, fabsf(w[j]));
+    }
+    int code = 0;
+    if (amax > 0.0f) {
+      code = floor_log2(amax) - 2 + 127;
+      code = code < 0 ? 0 : (code > 254 ? 254 : code);
+    }
+    scales[gi] = (uint8_t)code;
+    for (int j = 0; j < 32; j += 2) {
+      const uint8_t lo = e2m1_encode(ldexpf(w[j], 127 - code));
+      const uint8_t hi = e2m1_encode(ldexpf(w[j + 1], 127 - code));
+      codes[r * (K / 2) + g * 16 + j / 2] = (uint8_t)(lo | (hi << 4));
+    }
+  }
+}
+
 inline unsigned grid_for(uint64_t n) {
   uint64_t g = (n + 255) / 256;
   return (unsigned)(g > 65536 ? 65536 : (g == 0 ? 1 : g));
@@ -128,5 +173,12 @@ extern "C" int mks_dev_fp8_blocks(uint8_t* codes, float* scales, int64_t R, int6
   int64_t nbr = (R + 127) / 128, nbk = (K + 127) / 128;
   hipLaunchKernelGGL(k_fp8_blocks, dim3((unsigned)(nbr * nbk)), dim3(256), 0, (hipStream_t)sh,
                      codes, scales, R, K, nbk, key_of(seed, stream), c);
+  return (int)hipGetLastError();
+}
+extern "C" int mks_dev_mxfp4_blocks(uint8_t* codes, uint8_t* scales, int64_t R, int64_t K,
+                                    uint64_t seed, uint64_t stream, float c, void* sh) {
+  if (R <= 0 || K <= 0 || K % 32) return R <= 0 || K <= 0 ? 0 : (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_mxfp4_blocks, dim3(grid_for((uint64_t)(R * (K / 32)))), dim3(256), 0, (hipStream_t)sh,
+                     codes, scales, R, K, key_of(seed, stream), c);
   return (int)hipGetLastError();
 }

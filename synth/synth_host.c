@@ -99,3 +99,54 @@ void mks_host_fp8_blocks(uint8_t* codes, float* scales, int64_t R, int64_t K,
       }
   }
 }
+
+uint8_t mks_host_e2m1_encode(float x) {
+  static const float mid[7] = {0.25f, 0.75f, 1.25f, 1.75f, 2.5f, 3.5f, 5.0f};
+  uint32_t u; memcpy(&u, &x, 4);
+  uint8_t sign = (uint8_t)((u >> 28) & 8u);
+  float a = fabsf(x);
+  int i = 0;
+  while (i < 7 && a > mid[i]) ++i;
+  if (i < 7 && a == mid[i] && (i & 1)) ++i;        /* a tie between codes i, i+1: the even one */
+  return sign | (uint8_t)i;
+}
+
+/* floor(log2 a) for a finite a > 0, from the exponent bits (exact) */
+static int floor_log2(float a) {
+  uint32_t u; memcpy(&u, &a, 4);
+  int e = (int)((u >> 23) & 0xFF);
+  if (e) return e - 127;
+  uint32_t m = u & 0x7FFFFFu;
+  int k = -127;
+  while (!(m & 0x400000u)) { m <<= 1; --k; }
+  return k;
+}
+
+void mks_host_mxfp4_blocks(uint8_t* codes, uint8_t* scales, int64_t R, int64_t K,
+                           uint64_t seed, uint64_t stream, float c) {
+  uint64_t k = key_of(seed, stream);
+  int64_t ng = K / 32;
+#pragma omp parallel for schedule(static)
+  for (int64_t gi = 0; gi < R * ng; ++gi) {
+    int64_t r = gi / ng, g = gi % ng;
+    float w[32];
+    float amax = 0.0f;
+    for (int j = 0; j < 32; ++j) {
+      w[j] = normal_at(k, (uint64_t)(r * K + g * 32 + j), c, 0.0f);
+      float a = fabsf(w[j]);
+      if (a > amax) amax = a;
+    }
+    int code = 0;
+    if (amax > 0.0f) {
+      code = floor_log2(amax) - 2 + 127;
+      if (code < 0) code = 0;
+      if (code > 254) code = 254;
+    }
+    scales[gi] = (uint8_t)code;
+    for (int j = 0; j < 32; j += 2) {
+      uint8_t lo = mks_host_e2m1_encode(ldexpf(w[j], 127 - code));
+      uint8_t hi = mks_host_e2m1_encode(ldexpf(w[j + 1], 127 - code));
+      codes[r * (K / 2) + g * 16 + j / 2] = (uint8_t)(lo | (hi << 4));
+    }
+  }
+}

@@ -453,3 +453,93 @@ def test_gates_under_router_bias_use_the_biased_logits():
         eu = np.exp(lu - lu.max())
         changed += not np.allclose(tb["gate"][i], eu / eu.sum(), rtol=1e-3)
     assert changed == s.T
+
+
+# ---------------------------------------------------------------- MXFP4 experts (OCP MX: E2M1 + E8M0 per 32)
+C0X = LayerShape("micro_mxfp4", d=256, n_h=2, d_h=32, d_c=64, d_r=16, E=6, top_k=2, n_shared=1,
+                 f=160, T=3, L=7, attn_fmt="bf16", exp_fmt="mxfp4", kv_fmt="bf16")
+
+
+def test_e2m1_and_e8m0_decode_match_the_mx_definitions():
+    g = json.load(open(os.path.join(GOLD, "ocp_mx_e2m1_values.json")))
+    L = oracle.lib()
+    for code, val in g["e2m1"].items():
+        got = L.orc_e2m1_to_f32(int(code))
+        assert got == val and math.copysign(1, got) == math.copysign(1, val), (code, got, val)
+    for code, val in g["e8m0"].items():
+        assert L.orc_e8m0_to_f32(int(code)) == np.float32(val), code
+    for code in g["e8m0_nan"]:
+        assert math.isnan(L.orc_e8m0_to_f32(code))
+
+
+def test_e2m1_encoder_rounds_to_nearest_even_code_and_saturates():
+    L = oracle.lib()
+    vals = [L.orc_e2m1_to_f32(c) for c in range(8)]
+    for c in range(16):
+        v = L.orc_e2m1_to_f32(c)
+        assert synth.e2m1_encode(v) == c, (c, v)                  # every code round-trips (-0 keeps its sign)
+    for i in range(7):
+        lo, hi = vals[i], vals[i + 1]
+        mid = (lo + hi) / 2
+        want = i if i % 2 == 0 else i + 1                          # the even code wins a tie
+        assert synth.e2m1_encode(mid) == want and synth.e2m1_encode(-mid) == 8 | want
+        assert synth.e2m1_encode(np.nextafter(np.float32(mid), np.float32(0))) == i
+        assert synth.e2m1_encode(np.nextafter(np.float32(mid), np.float32(9))) == i + 1
+    assert synth.e2m1_encode(7.9) == 7 and synth.e2m1_encode(-100.0) == 15
+
+
+def _mx_decode(codes, scales):
+    """Dense fp64 matrix of MXFP4 codes [R][K/2] and E8M0 scales [R][K/32], written from the MX definitions."""
+    mag = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6], np.float64)
+    lo, hi = codes & 15, codes >> 4
+    el = np.empty((codes.shape[0], codes.shape[1] * 2), np.int64)
+    el[:, 0::2], el[:, 1::2] = lo, hi
+    v = mag[el & 7] * np.where(el & 8, -1.0, 1.0)
+    return v * np.repeat(2.0 ** (scales.astype(np.float64) - 127.0), 32, axis=1)
+
+
+def test_mxfp4_blocks_quantise_by_the_mx_recipe():
+    R, K = 40, 256
+    q, sc = synth.mxfp4_blocks(R, K, 0, synth.stream_id("w2"), 0.02)
+    w = synth.normal_f32((R, K), 0, synth.stream_id("w2"), 0.02).astype(np.float64)
+    amax = np.abs(w).reshape(R, K // 32, 32).max(axis=2)
+    mant, ex = np.frexp(amax)                                  # amax = mant * 2^ex, mant in [0.5, 1)
+    assert np.array_equal(sc.astype(np.int64), (ex - 1) - 2 + 127)
+    deq = _mx_decode(q, sc)
+    X = np.repeat(2.0 ** (sc.astype(np.float64) - 127.0), 32, axis=1)
+    # each element is the nearest E2M1 value of w / X (saturating at 6): error <= half the local spacing
+    x = np.abs(w) / X
+    spacing = np.where(x < 2, 0.5, np.where(x < 4, 1.0, 2.0))
+    err = np.abs(deq - w) / X
+    assert np.all((err <= spacing / 2 + 1e-12) | (x > 6))
+    assert np.all(np.abs(deq)[x > 6] == 6 * X[x > 6])
+    assert np.array_equal(np.sign(deq)[deq != 0], np.sign(w)[deq != 0])
+
+
+def test_mxfp4_nibble_order_and_scale_indexing_against_an_explicit_dense_matrix():
+    """Distinct low and high nibbles and a distinct power-of-two scale per (row, 32-group):
+    the oracle's expert output equals a dense fp64 SwiGLU over the explicitly decoded matrices."""
+    s = C0X.with_(E=1, top_k=1, n_shared=0, T=2, L=0)
+    w, H, kv = fresh(s)
+    tup, mats = [], []
+    for i, (R, K) in enumerate(((s.f, s.d), (s.f, s.d), (s.d, s.f))):
+        r = np.arange(R)[:, None]
+        j = np.arange(K // 2)[None, :]
+        codes = (((r + j + i) % 16) | ((((r * 3 + j + 5) % 16)) << 4)).astype(np.uint8)
+        scales = (118 + (np.arange(R)[:, None] + 2 * np.arange(K // 32)[None, :] + i) % 7).astype(np.uint8)
+        tup.append((codes, scales))
+        mats.append(_mx_decode(codes, scales))
+    w["experts"] = {0: (tup[0][0], tup[1][0], tup[2][0], tup[0][1], tup[1][1], tup[2][1])}
+    out, taps = oracle.layer_step(s, w, H, kv, 0)
+    xp = taps["xp"].astype(np.float64)
+    a = xp @ mats[0].T
+    ffn = ((a / (1 + np.exp(-a))) * (xp @ mats[1].T)) @ mats[2].T
+    assert np.allclose(out - taps["Hp"], ffn, rtol=2e-5, atol=1e-7)
+
+
+def test_mxfp4_layer_matches_fp64_unabsorbed_bruteforce():
+    s = C0X
+    w, H, kv = fresh(s)
+    out, taps = oracle.layer_step(s, w, H, kv.copy(), s.L)
+    ref = oracle.layer_step_f64(s, w, H, kv, s.L, force_sel=taps["sel"])
+    assert normwise(out, ref["out"]) < 1e-5
