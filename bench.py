@@ -16,8 +16,9 @@ bandwidth, the roofline of the layer kernel (live HIP-event timing of its
 launches), the share of the layer kernel's time spent in grid barriers (from
 its in-kernel trace, on an untimed step), launches per step, the spread over
 several process starts, and the CPU oracle timed on a bounded sample as a
-baseline.  --workload C2|C3|C4 times a single layer instead (three rotating
-weight copies so the 256 MB last-level cache cannot serve repeats).
+baseline.  --workload C2|C3|C4|C3X times a single layer instead (three rotating
+weight copies so the 256 MB last-level cache cannot serve repeats); C5X is the
+stack with MXFP4 experts (each of the 32 layers with routed experts of its own).
 """
 import argparse
 import json
@@ -33,7 +34,10 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decode step µs/layer & tok/s/stream at T=6; achieved HBM GB/s vs peak"
 PEAK_GBPS = 8000.0      # MI355X HBM3E peak
-TAUS = (3.3, 4.0, 5.17)  # tokens per verify step the pages report (bench, live traffic, single-GB300 lane)
+TAUS = (3.3, 4.0, 5.17)
+EXPERT_DESC = {"fp8": "fp8 e4m3 experts (128x128 fp32 scales)",
+               "mxfp4": "mxfp4 experts (e2m1, an e8m0 scale per 32 elements)",
+               "bf16": "bf16 experts", "f32": "fp32 experts"}  # tokens per verify step the pages report (bench, live traffic, single-GB300 lane)
 
 
 def log(*a):
@@ -50,6 +54,8 @@ def router_bytes(s):
 
 
 def expert_bytes(s):
+    if s.exp_fmt == "mxfp4":
+        return 3 * s.f * s.d // 2 + 3 * s.f * s.d // 32      # half a byte per weight + a byte per 32
     if s.exp_fmt == "fp8":
         nsc = ((s.f + 127) // 128) * ((s.d + 127) // 128)
         return 3 * s.f * s.d + 3 * nsc * 4
@@ -316,8 +322,8 @@ def run_stack(s, args):
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": s.name, "layers": n_layers, "T": s.T, "kv_len_start": len0, "kv_len_end": len1,
                    "experts": s.E, "top_k": s.top_k, "shared": s.n_shared, "d_model": s.d, "d_ff": s.f,
-                   "vocab": s.V, "expert_pools": s.n_pools, "weights": "fp8 e4m3 experts (128x128 fp32 scales), "
-                   "bf16 attention/router/embedding/head", "kv": s.kv_fmt,
+                   "vocab": s.V, "expert_pools": s.n_pools or n_layers, "weights": EXPERT_DESC[s.exp_fmt] +
+                   ", bf16 attention/router/embedding/head", "kv": s.kv_fmt,
                    "compute": "bf16 MFMA operands, fp32 accumulation"},
         "tokens_per_step": round(committed / K, 4),
         "ms_per_step_dist": pct(per_step),
@@ -332,8 +338,8 @@ def run_stack(s, args):
         "layer_trace": tsum,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_GBPS, 4),
-                     "traffic": measured_traffic("layer_kernel_stack32_fp8_T6_hbm_counters.json"),
-                     "kernel": "layer_kernel<bf16, fp8, bf16>", "bytes_per_launch": int(lb),
+                     "traffic": measured_traffic("layer_kernel_stack32_%s_T6_hbm_counters.json" % s.exp_fmt),
+                     "kernel": "layer_kernel<bf16, %s, bf16>" % s.exp_fmt, "bytes_per_launch": int(lb),
                      "avg_launch_us": round(us_layer, 2), "launches_timed": launches},
     }
     if args.cpu_baseline:
@@ -429,7 +435,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--workload", default="C5", choices=["C2", "C3", "C4", "C5"])
+    ap.add_argument("--workload", default="C5", choices=["C2", "C3", "C4", "C5", "C3X", "C5X"])
     ap.add_argument("--layers", type=int, default=None, help="stack depth override (diagnostics only)")
     ap.add_argument("--layer-reps", type=int, default=4)
     ap.add_argument("--starts", type=int, default=5,

@@ -64,14 +64,16 @@ int check_cfg(const mk_layer_config* c) {
   const Dims D = dims_of(c);
   if (D.d <= 0 || D.nh <= 0 || D.dh <= 0 || D.dc <= 0 || D.dr <= 0 || D.E <= 0 || D.topk <= 0 || D.f <= 0)
     return fail(MK_ERR_INVALID_ARG, "non-positive dimension");
-  if (D.af < 0 || D.af > 1 || D.ef < 0 || D.ef > 2 || D.kf < 0 || D.kf > 1)
+  if (D.af < 0 || D.af > 1 || D.ef < 0 || D.ef > 3 || D.kf < 0 || D.kf > 1)
     return fail(MK_ERR_INVALID_ARG, "unknown format");
   if (c->has_router_bias != 0 && c->has_router_bias != 1) return fail(MK_ERR_INVALID_ARG, "has_router_bias must be 0 or 1");
   if (!(c->rms_eps >= 0.f) || !(c->rope_base > 0.f)) return fail(MK_ERR_INVALID_ARG, "bad eps or rope base");
   const bool f32 = D.af == MK_FMT_F32 && D.ef == MK_FMT_F32 && D.kf == MK_FMT_F32;
-  const bool bf = D.af == MK_FMT_BF16 && D.kf == MK_FMT_BF16 && (D.ef == MK_FMT_BF16 || D.ef == MK_FMT_FP8_B128);
+  const bool bf = D.af == MK_FMT_BF16 && D.kf == MK_FMT_BF16 &&
+                  (D.ef == MK_FMT_BF16 || D.ef == MK_FMT_FP8_B128 || D.ef == MK_FMT_MXFP4);
   if (!f32 && !bf)
-    return fail(MK_ERR_UNSUPPORTED_SHAPE, "formats must be all F32, or BF16 attention/KV with BF16 or FP8_B128 experts");
+    return fail(MK_ERR_UNSUPPORTED_SHAPE,
+                "formats must be all F32, or BF16 attention/KV with BF16, FP8_B128 or MXFP4 experts");
   if (D.d % 128 || D.f % 128) return fail(MK_ERR_UNSUPPORTED_SHAPE, "d_model and d_ff must be multiples of 128");
   if (D.dh % 32 || D.dc % 32 || D.dr % 32) return fail(MK_ERR_UNSUPPORTED_SHAPE, "d_head, d_latent, d_rope must be multiples of 32");
   if (D.E % 16) return fail(MK_ERR_UNSUPPORTED_SHAPE, "n_experts must be a multiple of 16");
@@ -115,6 +117,7 @@ long long tiles_bytes(int R, int K, int fmt) { return (long long)((R + 15) / 16)
 long long exp_w13(const Dims& D) { return 2 * tiles_bytes(D.f, D.d, D.ef); }
 long long exp_w2(const Dims& D) { return tiles_bytes(D.d, D.f, D.ef); }
 long long exp_scales(const Dims& D) {
+  if (D.ef == MK_FMT_MXFP4) return align256((size_t)(3LL * D.f * D.d / 32));   // one byte per 32 elements
   if (D.ef != MK_FMT_FP8_B128) return 0;
   const long long a = (long long)((D.f + 127) / 128) * ((D.d + 127) / 128);
   return align256((size_t)(3 * a * 4));
@@ -434,13 +437,21 @@ int mk_pack_expert(const mk_layer_config* cfg, const void* w1, const void* w3, c
   if (rc) return rc;
   const Dims D = dims_of(cfg);
   if (!w1 || !w3 || !w2 || !dst) return fail(MK_ERR_INVALID_ARG, "null tensor");
-  const bool fp8 = D.ef == MK_FMT_FP8_B128;
-  if (fp8 && (!s1 || !s3 || !s2)) return fail(MK_ERR_INVALID_ARG, "fp8 experts need three scale arrays");
+  const bool fp8 = D.ef == MK_FMT_FP8_B128, mx = D.ef == MK_FMT_MXFP4;
+  if ((fp8 || mx) && (!s1 || !s3 || !s2)) return fail(MK_ERR_INVALID_ARG, "fp8 and MXFP4 experts need three scale arrays");
   hipStream_t s = (hipStream_t)stream;
   const long long w13 = exp_w13(D), w2b = exp_w2(D);
-  rc = launch_pack(w1, D.ef, 1, D.f, D.d, 0, D.d, 1, dst, 2048, 0, s);
-  if (!rc) rc = launch_pack(w3, D.ef, 1, D.f, D.d, 0, D.d, 1, dst, 2048, 1024, s);
-  if (!rc) rc = launch_pack(w2, D.ef, 1, D.d, D.f, 0, D.f, 1, dst, 1024, w13, s);
+  // row strides in bytes for MXFP4 (two codes per byte), in elements otherwise
+  const int rd = mx ? D.d / 2 : D.d, rf = mx ? D.f / 2 : D.f;
+  rc = launch_pack(w1, D.ef, 1, D.f, D.d, 0, rd, 1, dst, 2048, 0, s);
+  if (!rc) rc = launch_pack(w3, D.ef, 1, D.f, D.d, 0, rd, 1, dst, 2048, 1024, s);
+  if (!rc) rc = launch_pack(w2, D.ef, 1, D.d, D.f, 0, rf, 1, dst, 1024, w13, s);
+  if (!rc && mx) {
+    const long long sc13 = w13 + w2b, sc2 = sc13 + (long long)(D.f / 16) * (D.d / 128) * 128;
+    rc = launch_pack_mx_scales(s1, D.f, D.d, dst, 128, sc13, s);
+    if (!rc) rc = launch_pack_mx_scales(s3, D.f, D.d, dst, 128, sc13 + 64, s);
+    if (!rc) rc = launch_pack_mx_scales(s2, D.d, D.f, dst, 64, sc2, s);
+  }
   if (rc) return fail(MK_ERR_HIP, "pack launch failed: %s", hipGetErrorString((hipError_t)rc));
   if (fp8) {
     const size_t a = (size_t)((D.f + 127) / 128) * ((D.d + 127) / 128) * 4;

@@ -33,8 +33,15 @@ constexpr int kMaxModel = kNormCh * 64 * 4;     // longest hidden row (d_model)
 // Packed tile geometry: one tile = 16 rows x kTileK[fmt] columns = 1 KiB,
 // lane l holds row (l % 16) and 16 consecutive bytes of columns
 // (l / 16) * (kTileK / 4) ... ; tiles of a matrix are row-tile major.
-__host__ __device__ constexpr int tile_k(int fmt) { return fmt == MK_FMT_F32 ? 16 : (fmt == MK_FMT_BF16 ? 32 : 64); }
+// MXFP4 tiles hold 16 rows x 128 columns of 4-bit codes: lane l's 16 bytes are
+// the 32 elements (one MX scale group) of row l % 16 at columns (l / 16) * 32.
+__host__ __device__ constexpr int tile_k(int fmt) {
+  return fmt == MK_FMT_F32 ? 16 : (fmt == MK_FMT_BF16 ? 32 : (fmt == MK_FMT_FP8_B128 ? 64 : 128));
+}
+// Bytes per element in the tiles (MXFP4: two elements per byte, see launch_pack).
 __host__ __device__ constexpr int elem_bytes(int fmt) { return fmt == MK_FMT_F32 ? 4 : (fmt == MK_FMT_BF16 ? 2 : 1); }
+// Formats whose tiles carry scales: fp8 (fp32 per 128x128 block) and MXFP4 (E8M0 per 32 elements of a row).
+__host__ __device__ constexpr bool scaled_fmt(int fmt) { return fmt == MK_FMT_FP8_B128 || fmt == MK_FMT_MXFP4; }
 
 // Per-layer device state (persistent across steps; zeroed at init).
 // The grid barrier is two-level: workgroups arrive on the counter of their

@@ -174,6 +174,47 @@ __device__ __forceinline__ f32x4 tile_mma_fp8(const u32x4& a, const BPair& b, f3
   return acc;
 }
 
+// Eight E2M1 codes (one dword, element 2j in the low nibble of byte j) times
+// the scale s -> eight bf16, one byte per instruction.  Exact: an E2M1 value
+// times a power of two is a bf16 value while it stays in bf16's range.  The
+// packed results are assembled as dwords (no element extraction).
+__device__ __forceinline__ bf16x8 fp4x8_to_bf16(uint32_t w, float s) {
+  const u32x4 r = {__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 0)),
+                   __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 1)),
+                   __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 2)),
+                   __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 3))};
+  return __builtin_bit_cast(bf16x8, r);
+}
+// One MXFP4 tile (16 rows x 128 columns; the lane's 32 codes form one MX scale
+// group of its row) times the lane's 32 activations at b: four k32 products,
+// the group's scale s applied while the codes are widened.
+__device__ __forceinline__ f32x4 tile_mma_mx(const u32x4& a, const __bf16* b, float s, f32x4 acc) {
+#pragma unroll
+  for (int d = 0; d < 4; ++d) acc = mma_bf16_k32(fp4x8_to_bf16(a[d], s), *reinterpret_cast<const bf16x8*>(b + 8 * d), acc);
+  return acc;
+}
+// E8M0 scale byte -> the fp32 whose exponent field it is: 2^(e - 127) for
+// 1 <= e <= 254; e = 0 (2^-127) as the subnormal with that value; e = 255 NaN.
+__device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
+  return __builtin_bit_cast(float, (e << 23) | ((e == 0u || e == 255u) ? 0x00400000u : 0u));
+}
+
+// The scale of tile t of a unit whose scales start at sp.
+//  fp8: one fp32 per 128x128 block; the unit's 16 rows lie in one block row,
+//       so tile t (columns t * 64 ...) takes entry (t * 64) / 128.
+//  MXFP4: 64 scale bytes per tile, byte l for lane l (its row's scale group);
+//       the W1 and W3 scales of a dual stream alternate per tile (stride 128).
+// vz (a vector zero, see vzero) keeps an fp8 scale load on the vector path.
+template <int FMT, bool DUAL>
+__device__ __forceinline__ float tile_scale(const float* sp, int t, int lane, int vz = 0) {
+  if constexpr (FMT == MK_FMT_MXFP4) {
+    const uint8_t* b = reinterpret_cast<const uint8_t*>(sp);
+    return e8m0_to_f32(ldg(b + t * (DUAL ? 128 : 64) + lane + vz));
+  } else {
+    return ldg(sp + ((t * tile_k(FMT)) >> 7) + vz);
+  }
+}
+
 // ------------------------------------------------------------------ tracing
 // Timestamps of a traced launch are kept in LDS (the last KiB of the dynamic
 // allocation, which no phase uses) and written out once at the end, so that no
@@ -314,12 +355,12 @@ __device__ __forceinline__ void run_units(int u0, int u1, int NT, int T, const S
   u32x4 buf[D];
   u32x4 buf2[D];
   float sc[D], sc2[D];
-  // issue cursor (fp8 block scales travel with their tiles)
+  // issue cursor (block scales travel with their tiles)
   int iu = 0, ij = 0;
   const uint8_t* ib = src.base(u0) + lane * 16;
   const float* isp = nullptr;
   const float* isp2 = nullptr;
-  if constexpr (FMT == MK_FMT_FP8_B128) {
+  if constexpr (scaled_fmt(FMT)) {
     isp = src.sbase(u0);
     if constexpr (DUAL) isp2 = src.sbase2(u0);
   }
@@ -329,16 +370,16 @@ __device__ __forceinline__ void run_units(int u0, int u1, int NT, int T, const S
       const uint8_t* tp = ib + (long long)t * STRIDE;
       buf[r] = ld_stream16(tp);
       if constexpr (DUAL) buf2[r] = ld_stream16(tp + 1024);
-      if constexpr (FMT == MK_FMT_FP8_B128) {
-        sc[r] = ldg(isp + ((t * TK) >> 7));
-        if constexpr (DUAL) sc2[r] = ldg(isp2 + ((t * TK) >> 7));
+      if constexpr (scaled_fmt(FMT)) {
+        sc[r] = tile_scale<FMT, DUAL>(isp, t, lane);
+        if constexpr (DUAL) sc2[r] = tile_scale<FMT, DUAL>(isp2, t, lane);
       }
     }
     if (++ij == c) {
       ij = 0;
       if (++iu < nu) {
         ib = src.base(u0 + iu) + lane * 16;
-        if constexpr (FMT == MK_FMT_FP8_B128) {
+        if constexpr (scaled_fmt(FMT)) {
           isp = src.sbase(u0 + iu);
           if constexpr (DUAL) isp2 = src.sbase2(u0 + iu);
         }
@@ -369,6 +410,9 @@ __device__ __forceinline__ void run_units(int u0, int u1, int NT, int T, const S
               const f32x4 tmp2 = tile_mma<FMT>(buf2[r], bp, zero);
               acc2 += tmp2 * sc2[r];
             }
+          } else if constexpr (FMT == MK_FMT_MXFP4) {
+            acc = tile_mma_mx(buf[r], bp, sc[r], acc);
+            if constexpr (DUAL) acc2 = tile_mma_mx(buf2[r], bp, sc2[r], acc2);
           } else {
             acc = tile_mma<FMT>(buf[r], bp, acc);
             if constexpr (HILO) acc = tile_mma<FMT>(buf[r], bp + src.lo_off, acc);
@@ -429,7 +473,7 @@ __device__ __forceinline__ void run_wave_units(int u0, int u1, int NT, int T, co
   const uint8_t* ib = src.base(u0 + w) + lane * 16;
   const float* isp = nullptr;
   const float* isp2 = nullptr;
-  if constexpr (FMT == MK_FMT_FP8_B128) {
+  if constexpr (scaled_fmt(FMT)) {
     isp = src.sbase(u0 + w);
     if constexpr (DUAL) isp2 = src.sbase2(u0 + w);
   }
@@ -437,16 +481,16 @@ __device__ __forceinline__ void run_wave_units(int u0, int u1, int NT, int T, co
     const uint8_t* tp = ib + (long long)it * STRIDE;
     buf[r] = ld_stream16(tp);
     if constexpr (DUAL) buf2[r] = ld_stream16(tp + 1024);
-    if constexpr (FMT == MK_FMT_FP8_B128) {
-      sc[r] = ldg(isp + ((it * TK) >> 7));
-      if constexpr (DUAL) sc2[r] = ldg(isp2 + ((it * TK) >> 7));
+    if constexpr (scaled_fmt(FMT)) {
+      sc[r] = tile_scale<FMT, DUAL>(isp, it, lane);
+      if constexpr (DUAL) sc2[r] = tile_scale<FMT, DUAL>(isp2, it, lane);
     }
     if (++it == NT) {
       it = 0;
       if (++iu < nu) {
         const int u = u0 + w + kWaves * iu;
         ib = src.base(u) + lane * 16;
-        if constexpr (FMT == MK_FMT_FP8_B128) {
+        if constexpr (scaled_fmt(FMT)) {
           isp = src.sbase(u);
           if constexpr (DUAL) isp2 = src.sbase2(u);
         }
@@ -474,6 +518,9 @@ __device__ __forceinline__ void run_wave_units(int u0, int u1, int NT, int T, co
             const f32x4 tmp2 = tile_mma<FMT>(buf2[r], bp, zero);
             acc2 += tmp2 * sc2[r];
           }
+        } else if constexpr (FMT == MK_FMT_MXFP4) {
+          acc = tile_mma_mx(buf[r], bp, sc[r], acc);
+          if constexpr (DUAL) acc2 = tile_mma_mx(buf2[r], bp, sc2[r], acc2);
         } else {
           acc = tile_mma<FMT>(buf[r], bp, acc);
           if constexpr (DUAL) acc2 = tile_mma<FMT>(buf2[r], bp, acc2);
@@ -528,7 +575,6 @@ struct Chunk {
 template <int FMT, bool DUAL, bool WG, int D, int PD = D, class Src>
 __device__ __forceinline__ void stream_prime(Chunk<FMT, DUAL, D>& c, int u0, int u1, int NT, const Src& src,
                                              const uint8_t* dummy, bool enable = true) {
-  constexpr int TK = tile_k(FMT);
   constexpr long long STRIDE = DUAL ? 2048 : 1024;
   const int w = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
@@ -543,7 +589,7 @@ __device__ __forceinline__ void stream_prime(Chunk<FMT, DUAL, D>& c, int u0, int
   if (any) {
     const int u = WG ? u0 : u0 + w;
     cbase = src.base(u) + lane * 16 + (long long)toff * STRIDE;
-    if constexpr (FMT == MK_FMT_FP8_B128) {
+    if constexpr (scaled_fmt(FMT)) {
       sp = src.sbase(u);
       if constexpr (DUAL) sp2 = src.sbase2(u);
     }
@@ -553,10 +599,10 @@ __device__ __forceinline__ void stream_prime(Chunk<FMT, DUAL, D>& c, int u0, int
   for (int r = 0; r < PD; ++r) {
     c.buf[r] = ld_stream16(cbase + r * STRIDE);
     if constexpr (DUAL) c.buf2[r] = ld_stream16(cbase + r * STRIDE + 1024);
-    if constexpr (FMT == MK_FMT_FP8_B128) {
-      const int si = any ? (((soff + r) * TK) >> 7) : 0;
-      c.sc[r] = ldg(sp + si);
-      if constexpr (DUAL) c.sc2[r] = ldg(sp2 + si);
+    if constexpr (scaled_fmt(FMT)) {
+      const int st = any ? soff + r : 0;
+      c.sc[r] = tile_scale<FMT, DUAL>(sp, st, lane);
+      if constexpr (DUAL) c.sc2[r] = tile_scale<FMT, DUAL>(sp2, st, lane);
     }
   }
 }
@@ -588,9 +634,9 @@ __device__ __forceinline__ void run_stream(int u0, int u1, int NT, int T, const 
     for (int r = 0; r < D; ++r) {
       buf[r] = ld_stream16(cbase + r * STRIDE);
       if constexpr (DUAL) buf2[r] = ld_stream16(cbase + r * STRIDE + 1024);
-      if constexpr (FMT == MK_FMT_FP8_B128) {
-        sc[r] = ldg(sp + (((tfirst + r) * TK) >> 7));
-        if constexpr (DUAL) sc2[r] = ldg(sp2 + (((tfirst + r) * TK) >> 7));
+      if constexpr (scaled_fmt(FMT)) {
+        sc[r] = tile_scale<FMT, DUAL>(sp, tfirst + r, lane);
+        if constexpr (DUAL) sc2[r] = tile_scale<FMT, DUAL>(sp2, tfirst + r, lane);
       }
     }
   };
@@ -598,7 +644,7 @@ __device__ __forceinline__ void run_stream(int u0, int u1, int NT, int T, const 
     const int u = ufirst;
     const float* sp = nullptr;
     const float* sp2 = nullptr;
-    if constexpr (FMT == MK_FMT_FP8_B128) {
+    if constexpr (scaled_fmt(FMT)) {
       sp = src.sbase(u);
       if constexpr (DUAL) sp2 = src.sbase2(u);
     }
@@ -611,9 +657,9 @@ __device__ __forceinline__ void run_stream(int u0, int u1, int NT, int T, const 
     for (int r = PD; r < D; ++r) {
       buf[r] = ld_stream16(cbase + r * STRIDE);
       if constexpr (DUAL) buf2[r] = ld_stream16(cbase + r * STRIDE + 1024);
-      if constexpr (FMT == MK_FMT_FP8_B128) {
-        sc[r] = ldg(src.sbase(u) + (((toff + r) * TK) >> 7));
-        if constexpr (DUAL) sc2[r] = ldg(src.sbase2(u) + (((toff + r) * TK) >> 7));
+      if constexpr (scaled_fmt(FMT)) {
+        sc[r] = tile_scale<FMT, DUAL>(src.sbase(u), toff + r, lane);
+        if constexpr (DUAL) sc2[r] = tile_scale<FMT, DUAL>(src.sbase2(u), toff + r, lane);
       }
     }
   }
@@ -633,7 +679,7 @@ __device__ __forceinline__ void run_stream(int u0, int u1, int NT, int T, const 
     const uint8_t* nb = has_next ? src.base(un) + lane * 16 + (long long)tn * STRIDE : dummy + lane * 16;
     const float* nsp = dsc;
     const float* nsp2 = dsc;
-    if constexpr (FMT == MK_FMT_FP8_B128) {
+    if constexpr (scaled_fmt(FMT)) {
       if (has_next) {
         nsp = src.sbase(un);
         if constexpr (DUAL) nsp2 = src.sbase2(un);
@@ -650,6 +696,9 @@ __device__ __forceinline__ void run_stream(int u0, int u1, int NT, int T, const 
           const f32x4 tmp2 = tile_mma<FMT>(buf2[r], bp + r * TK, zero);
           acc2 += tmp2 * sc2[r];
         }
+      } else if constexpr (FMT == MK_FMT_MXFP4) {
+        acc = tile_mma_mx(buf[r], bp + r * TK, sc[r], acc);
+        if constexpr (DUAL) acc2 = tile_mma_mx(buf2[r], bp + r * TK, sc2[r], acc2);
       } else {
         acc = tile_mma<FMT>(buf[r], bp + r * TK, acc);
         if constexpr (HILO) acc = tile_mma<FMT>(buf[r], bp + r * TK + src.lo_off, acc);
@@ -657,9 +706,10 @@ __device__ __forceinline__ void run_stream(int u0, int u1, int NT, int T, const 
       }
       buf[r] = ld_stream16(nb + r * STRIDE);
       if constexpr (DUAL) buf2[r] = ld_stream16(nb + r * STRIDE + 1024);
-      if constexpr (FMT == MK_FMT_FP8_B128) {
-        sc[r] = ldg(nsp + (has_next ? (((tn + r) * TK) >> 7) : 0));
-        if constexpr (DUAL) sc2[r] = ldg(nsp2 + (has_next ? (((tn + r) * TK) >> 7) : 0));
+      if constexpr (scaled_fmt(FMT)) {
+        const int st = has_next ? tn + r : 0;
+        sc[r] = tile_scale<FMT, DUAL>(nsp, st, lane);
+        if constexpr (DUAL) sc2[r] = tile_scale<FMT, DUAL>(nsp2, st, lane);
       }
     }
     if (ncc == 0) {
@@ -751,9 +801,9 @@ __device__ __forceinline__ void run_stream_dyn(int U, int NT, int T, const Src& 
     for (int r = 0; r < D; ++r) {
       buf[r] = ld_stream16(cbase + r * STRIDE);
       if constexpr (DUAL) buf2[r] = ld_stream16(cbase + r * STRIDE + 1024);
-      if constexpr (FMT == MK_FMT_FP8_B128) {
-        sc[r] = ldg(src.sbase(cur) + (((toff + r) * TK) >> 7) + vz);
-        if constexpr (DUAL) sc2[r] = ldg(src.sbase2(cur) + (((toff + r) * TK) >> 7) + vz);
+      if constexpr (scaled_fmt(FMT)) {
+        sc[r] = tile_scale<FMT, DUAL>(src.sbase(cur), toff + r, lane, vz);
+        if constexpr (DUAL) sc2[r] = tile_scale<FMT, DUAL>(src.sbase2(cur), toff + r, lane, vz);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -787,7 +837,7 @@ __device__ __forceinline__ void run_stream_dyn(int U, int NT, int T, const Src& 
     const uint8_t* nb = has_next ? src.base(un) + lane * 16 + (long long)tn * STRIDE : dummy + lane * 16;
     const float* nsp = dsc;
     const float* nsp2 = dsc;
-    if constexpr (FMT == MK_FMT_FP8_B128) {
+    if constexpr (scaled_fmt(FMT)) {
       if (has_next) {
         nsp = src.sbase(un);
         if constexpr (DUAL) nsp2 = src.sbase2(un);
@@ -809,15 +859,19 @@ __device__ __forceinline__ void run_stream_dyn(int U, int NT, int T, const Src& 
           tp2 = tmp2;
           sp2 = keep_copy(sc2[r]);
         }
+      } else if constexpr (FMT == MK_FMT_MXFP4) {
+        acc = tile_mma_mx(buf[r], bp + r * TK, sc[r], acc);
+        if constexpr (DUAL) acc2 = tile_mma_mx(buf2[r], bp + r * TK, sc2[r], acc2);
       } else {
         acc = tile_mma<FMT>(buf[r], bp + r * TK, acc);
         if constexpr (DUAL) acc2 = tile_mma<FMT>(buf2[r], bp + r * TK, acc2);
       }
       buf[r] = ld_stream16(nb + r * STRIDE);
       if constexpr (DUAL) buf2[r] = ld_stream16(nb + r * STRIDE + 1024);
-      if constexpr (FMT == MK_FMT_FP8_B128) {
-        sc[r] = ldg(nsp + (has_next ? (((tn + r) * TK) >> 7) : 0));
-        if constexpr (DUAL) sc2[r] = ldg(nsp2 + (has_next ? (((tn + r) * TK) >> 7) : 0));
+      if constexpr (scaled_fmt(FMT)) {
+        const int st = has_next ? tn + r : 0;
+        sc[r] = tile_scale<FMT, DUAL>(nsp, st, lane);
+        if constexpr (DUAL) sc2[r] = tile_scale<FMT, DUAL>(nsp2, st, lane);
       }
       // tile r's next load leaves before tile r + 1 is used: the loads stay in
       // the order they are consumed, so each wait is for one tile and D tiles

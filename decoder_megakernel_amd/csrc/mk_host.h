@@ -15,6 +15,9 @@ LayerKernelFn layer_kernel_for(int af, int ef, int kf, int d, int nh, int dh, in
 int launch_pack(const void* src, int fmt, int nb, int R, int K, long long sb, long long sr, long long sk,
                 void* dst, long long dst_stride, long long dst_off, hipStream_t stream);
 
+int launch_pack_mx_scales(const void* src, int R, int K, void* dst, long long tile_stride, long long dst_off,
+                          hipStream_t stream);
+
 struct HeadParams;
 int launch_embed(const uint16_t* emb, int V, int d, const int32_t* tokens, int T, float* h, uint32_t* fault,
                  hipStream_t s);

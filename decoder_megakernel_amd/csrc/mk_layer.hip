@@ -1098,6 +1098,48 @@ struct NoStage {
   __device__ void issue() {}
   __device__ void finish() {}
 };
+// Scales of a packed expert block (formats with scales), after the W1/W3 and W2 tiles.
+//  fp8: fp32 [ceil(rows/128)][ceil(cols/128)] per matrix, W1 then W3 then W2;
+//       a unit of 16 rows starting at row tile rt reads block row rt / 8.
+//  MXFP4: E8M0 bytes in tile order, 64 per tile (byte l for lane l: the scale
+//       of row l % 16 over columns (l / 16) * 32 ... of the tile), the W1 and
+//       W3 tiles' 64 bytes alternating (128 per W1/W3 tile pair), then W2's.
+template <int EF>
+struct ExpScales {
+  long long sc13, sc3, sc2;   // byte offsets: W1 (and, for fp8, W3) and W2 scales
+  int n13, n2;                // fp8: blocks per block row (W1/W3, W2); MXFP4: tiles per row tile
+  __device__ explicit ExpScales(const LayerParams& p) {
+    sc13 = p.exp_w13_bytes + p.exp_w2_bytes;
+    if constexpr (EF == MK_FMT_MXFP4) {
+      n13 = p.d / 128;
+      n2 = p.f / 128;
+      sc3 = sc13 + 64;
+      sc2 = sc13 + (long long)(p.f / 16) * n13 * 128;
+    } else {
+      n13 = (p.d + 127) / 128;
+      n2 = (p.f + 127) / 128;
+      const long long nb = (long long)((p.f + 127) / 128) * n13;
+      sc3 = sc13 + nb * 4;
+      sc2 = sc13 + 2 * nb * 4;
+    }
+  }
+  // the scales of row tile rt of W1 (W3 with w3), of W2
+  __device__ const float* w13(const uint8_t* blk, int rt, bool w3 = false) const {
+    const uint8_t* b = blk + (w3 ? sc3 : sc13);
+    if constexpr (EF == MK_FMT_MXFP4) return reinterpret_cast<const float*>(b + (long long)rt * n13 * 128);
+    else return reinterpret_cast<const float*>(b) + (rt >> 3) * n13;
+  }
+  __device__ const float* w2(const uint8_t* blk, int rt) const {
+    if constexpr (EF == MK_FMT_MXFP4) return reinterpret_cast<const float*>(blk + sc2 + (long long)rt * n2 * 64);
+    else return reinterpret_cast<const float*>(blk + sc2) + (rt >> 3) * n2;
+  }
+};
+// Tiles per chunk of the ticket-fed streams: gate/up (two matrices per tile
+// slot) and down projections.  An MXFP4 tile holds twice the columns of an fp8
+// tile, so a row of d_model or d_ff has half as many of them.
+__host__ __device__ constexpr int gateup_depth(int fmt) { return fmt == MK_FMT_MXFP4 ? 4 : 8; }
+__host__ __device__ constexpr int down_depth(int tk) { return tk >= 128 ? 8 : 16; }
+
 // MODE 0: workgroup units [u0, u1); 1: wave units [u0, u1); 2: workgroup units
 // 0 .. u1-1 handed out at run time by the ticket counters; 3: as 2, and every
 // completed unit counted on its slot's completion counter.  `stage` requests
@@ -1111,9 +1153,8 @@ __device__ __forceinline__ void gateup_units(const LayerParams& p, const uint8_t
   const int T = p.T, XS = p.d + kXPad;
   const int RT = p.f / 16, KT = p.d / TK;
   const A* bl = b_lane<A>(xs, XS, T, TK);
-  const int nbk = (p.d + 127) / 128;
   struct Src {
-    const uint8_t* const* blk; int RT, KT, nbk; const A* bl; long long sc_off, sc3_off;
+    const uint8_t* const* blk; int RT, KT; const A* bl; ExpScales<EF> es;
     __device__ const uint8_t* base(int u) const {
       const int sl = u / RT, rt = u - sl * RT;
       return blk[sl] + (long long)rt * KT * 2048;
@@ -1121,16 +1162,14 @@ __device__ __forceinline__ void gateup_units(const LayerParams& p, const uint8_t
     __device__ const A* bbase(int) const { return bl; }
     __device__ const float* sbase(int u) const {
       const int sl = u / RT, rt = u - sl * RT;
-      return reinterpret_cast<const float*>(blk[sl] + sc_off) + (rt >> 3) * nbk;
+      return es.w13(blk[sl], rt);
     }
     __device__ const float* sbase2(int u) const {
       const int sl = u / RT, rt = u - sl * RT;
-      return reinterpret_cast<const float*>(blk[sl] + sc3_off) + (rt >> 3) * nbk;
+      return es.w13(blk[sl], rt, true);
     }
   };
-  const long long nsc13 = (long long)((p.f + 127) / 128) * nbk;
-  const long long sc_off = p.exp_w13_bytes + p.exp_w2_bytes;
-  Src src{blk, RT, KT, nbk, bl, sc_off, sc_off + nsc13 * 4};
+  Src src{blk, RT, KT, bl, ExpScales<EF>(p)};
   A* hb = reinterpret_cast<A*>(p.hbuf);
   const int f = p.f;
   const float* rsc = rsc_lds();       // the staged rows are h * gamma: scale by 1/rms
@@ -1173,11 +1212,12 @@ __device__ __forceinline__ void gateup_units(const LayerParams& p, const uint8_t
     };
     stage.issue();
     stage.finish();
-    run_stream_dyn<EF, true, 8>(u1, KT, T, src, epi2, red, p.dummy, p.att_cnt + kGateCnt, seq_lds(), done);
+    run_stream_dyn<EF, true, gateup_depth(EF)>(u1, KT, T, src, epi2, red, p.dummy, p.att_cnt + kGateCnt, seq_lds(),
+                                               done);
   } else if constexpr (MODE == 2) {
     stage.issue();
     stage.finish();
-    run_stream_dyn<EF, true, 8>(u1, KT, T, src, epi, red, p.dummy, p.att_cnt + kGateCnt, seq_lds());
+    run_stream_dyn<EF, true, gateup_depth(EF)>(u1, KT, T, src, epi, red, p.dummy, p.att_cnt + kGateCnt, seq_lds());
   } else if constexpr (MODE == 1) {
     stage.issue();
     stage.finish();
@@ -1282,7 +1322,7 @@ __device__ __forceinline__ void phase_route_gateup(const LayerParams& p, char* s
   const int ns = *r.nslots;
   const int U = (ns - s0) * (p.f / 16);
   const int KT = p.d / tile_k(EF);
-  if (KT % kWaves == 0 && (KT / kWaves) % 8 == 0) {
+  if (KT % kWaves == 0 && (KT / kWaves) % gateup_depth(EF) == 0) {
     // units handed out at run time (ticket counter), 8 waves per unit
     gateup_units<EF, 2>(p, r.blk + s0, s0, 0, U, xs, red);
     return;
@@ -1315,7 +1355,7 @@ __device__ __forceinline__ void phase_route_gateup(const LayerParams& p, char* s
 // starts and checks it, waiting if needed, when the unit ends), and they are read
 // with agent-scope loads, which do not return stale lines of this XCD's L2.
 __host__ __device__ constexpr bool down_dyn_fits(int d, int f, int tk, int es, int xb) {
-  return d % 64 == 0 && (f / tk) % 32 == 0 && 2 * kMaxT * (f + kXPad) * es <= xb &&
+  return d % 64 == 0 && (f / tk) % (2 * down_depth(tk)) == 0 && 2 * kMaxT * (f + kXPad) * es <= xb &&
          kMaxT * f * es <= 16 * kThreads * 4;
 }
 
@@ -1326,7 +1366,7 @@ template <int EF>
 __device__ __forceinline__ bool experts_fused(const LayerParams& p, int xb) {
   constexpr int TK = tile_k(EF);
   const int KT = p.d / TK;
-  return KT % kWaves == 0 && (KT / kWaves) % 8 == 0 &&
+  return KT % kWaves == 0 && (KT / kWaves) % gateup_depth(EF) == 0 &&
          down_dyn_fits(p.d, p.f, TK, (int)sizeof(typename Act<EF>::T), xb);
 }
 
@@ -1335,7 +1375,7 @@ __device__ __forceinline__ bool phase_down_dyn(const LayerParams& p, char* smem,
                                                int s_wait) {
   typedef typename Act<EF>::T A;
   constexpr int TK = tile_k(EF);
-  constexpr int D = 16;
+  constexpr int D = down_depth(TK);
   constexpr int HW = 16;                                   // dwords of expert rows per thread, at most
   const int T = p.T, f = p.f, d = p.d, HS = f + kXPad;
   const int ns = *r.nslots;
@@ -1344,10 +1384,8 @@ __device__ __forceinline__ bool phase_down_dyn(const LayerParams& p, char* smem,
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int sub = w & 3, kp = w >> 2;
   const int nwg = (int)gridDim.x;
-  const int nbk = (f + 127) / 128;
   const long long w2_off = p.exp_w13_bytes;
-  const long long sc2_off = p.exp_w13_bytes + p.exp_w2_bytes +
-                            2LL * ((p.f + 127) / 128) * ((p.d + 127) / 128) * 4;
+  const ExpScales<EF> es(p);
   // the two row buffers: hls + 0 and hls + hsz (offsets rather than an array of
   // pointers, so that every access stays an LDS access and never becomes FLAT)
   A* const hls = reinterpret_cast<A*>(smem);
@@ -1445,19 +1483,19 @@ __device__ __forceinline__ bool phase_down_dyn(const LayerParams& p, char* smem,
   };
   auto sbase = [&](int u) {
     const int sl = u / QP, rt = 4 * (u - sl * QP) + sub;
-    return reinterpret_cast<const float*>(r.blk[sl] + sc2_off) + (rt >> 3) * nbk;
+    return es.w2(r.blk[sl], rt);
   };
   u32x4 buf[D];
   float sc[D];
   {
     // issued as the loop issues a chunk (see run_stream_dyn)
     const uint8_t* cb = wbase(cur);
-    const float* sp = EF == MK_FMT_FP8_B128 ? sbase(cur) : dsc;
+    const float* sp = scaled_fmt(EF) ? sbase(cur) : dsc;
     const int vz = vzero();
 #pragma unroll
     for (int rr = 0; rr < D; ++rr) {
       buf[rr] = ld_stream16(cb + rr * 1024);
-      if constexpr (EF == MK_FMT_FP8_B128) sc[rr] = ldg(sp + (((kp * NTh + rr) * TK) >> 7) + vz);
+      if constexpr (scaled_fmt(EF)) sc[rr] = tile_scale<EF, false>(sp, kp * NTh + rr, lane, vz);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -1506,7 +1544,7 @@ __device__ __forceinline__ bool phase_down_dyn(const LayerParams& p, char* smem,
     const bool has_next = un >= 0;
     const uint8_t* nb = has_next ? wbase(un) + (long long)ncc * D * 1024 : p.dummy + lane * 16;
     const float* nsp = dsc;
-    if constexpr (EF == MK_FMT_FP8_B128) {
+    if constexpr (scaled_fmt(EF)) {
       if (has_next) nsp = sbase(un);
     }
     const A* bp = hls + hb * hsz + jj * HS + g * (TK / 4) + (kp * NTh + cc * D) * TK;
@@ -1522,12 +1560,14 @@ __device__ __forceinline__ bool phase_down_dyn(const LayerParams& p, char* smem,
         acc += tp * sp;
         tp = tmp;
         sp = keep_copy(sc[rr]);
+      } else if constexpr (EF == MK_FMT_MXFP4) {
+        acc = tile_mma_mx(buf[rr], bp + rr * TK, sc[rr], acc);
       } else {
         acc = tile_mma<EF>(buf[rr], bp + rr * TK, acc);
       }
       buf[rr] = ld_stream16(nb + rr * 1024);
-      if constexpr (EF == MK_FMT_FP8_B128)
-        sc[rr] = ldg(nsp + (has_next ? (((kp * NTh + ncc * D + rr) * TK) >> 7) : 0));
+      if constexpr (scaled_fmt(EF))
+        sc[rr] = tile_scale<EF, false>(nsp, has_next ? kp * NTh + ncc * D + rr : 0, lane);
       __builtin_amdgcn_sched_barrier(0);   // loads in consumption order (see run_stream_dyn)
     }
     cc = ncc;
@@ -1602,28 +1642,22 @@ __device__ __forceinline__ void phase_down(const LayerParams& p, char* smem) {
   int u0, u1;
   split_range(U, gridDim.x, blockIdx.x, u0, u1);
   const A* bl = b_lane<A>(xs, XS, T, TK);
-  const int nbk = (p.f + 127) / 128;
-  const long long nsc13 = (long long)((p.f + 127) / 128) * ((p.d + 127) / 128);
-  const long long sc2_off = p.exp_w13_bytes + p.exp_w2_bytes + 2 * nsc13 * 4;
+  const ExpScales<EF> es(p);
   struct Src {
-    const uint8_t* blk; int RT, KT, nbk; const A* bl; long long w2_off, sc2_off;
+    const uint8_t* blk; int RT, KT; const A* bl; long long w2_off; ExpScales<EF> es;
     __device__ const uint8_t* base(int u) const { return blk + w2_off + (long long)(u % RT) * KT * 1024; }
     __device__ const A* bbase(int) const { return bl; }
-    __device__ const float* sbase(int u) const {
-      return reinterpret_cast<const float*>(blk + sc2_off) + ((u % RT) >> 3) * nbk;
-    }
+    __device__ const float* sbase(int u) const { return es.w2(blk, u % RT); }
     __device__ const float* sbase2(int) const { return nullptr; }
   };
   // several slots per source: each unit finds its slot's block and staged operand
   struct SrcMulti {
-    const uint8_t* const* blk; int RT, KT, nbk, sa; const A* bl; long long slot_elems, w2_off, sc2_off;
+    const uint8_t* const* blk; int RT, KT, sa; const A* bl; long long slot_elems, w2_off; ExpScales<EF> es;
     __device__ const uint8_t* base(int u) const {
       return blk[u / RT] + w2_off + (long long)(u % RT) * KT * 1024;
     }
     __device__ const A* bbase(int u) const { return bl + (u / RT - sa) * slot_elems; }
-    __device__ const float* sbase(int u) const {
-      return reinterpret_cast<const float*>(blk[u / RT] + sc2_off) + ((u % RT) >> 3) * nbk;
-    }
+    __device__ const float* sbase(int u) const { return es.w2(blk[u / RT], u % RT); }
     __device__ const float* sbase2(int) const { return nullptr; }
   };
   float* yb = p.ybuf;
@@ -1648,7 +1682,7 @@ __device__ __forceinline__ void phase_down(const LayerParams& p, char* smem) {
         rows_copy_lds<A>(reinterpret_cast<const A*>(p.hbuf) + (long long)sl * T * f, T, f, xs + (sl - sa) * slot_elems,
                          XS);
       if (u == u0) trace_x(p, 9);
-      SrcMulti src{r.blk, RT, KT, nbk, sa, bl, slot_elems, p.exp_w13_bytes, sc2_off};
+      SrcMulti src{r.blk, RT, KT, sa, bl, slot_elems, p.exp_w13_bytes, es};
       stream_units_wave<EF, false>(u, ue, KT, T, src, epi, p.dummy);
       __syncthreads();
       u = ue;
@@ -1659,7 +1693,7 @@ __device__ __forceinline__ void phase_down(const LayerParams& p, char* smem) {
       const int sl = u / RT;
       const int ue = min(u1, (sl + 1) * RT);
       rows_copy_lds<A>(reinterpret_cast<const A*>(p.hbuf) + (long long)sl * T * f, T, f, xs, XS);
-      Src src{r.blk[sl], RT, KT, nbk, bl, p.exp_w13_bytes, sc2_off};
+      Src src{r.blk[sl], RT, KT, bl, p.exp_w13_bytes, es};
       stream_units_wg<EF, false, false>(u, ue, KT, T, src, epi, red, p.dummy);
       u = ue;
     }
@@ -1807,7 +1841,7 @@ __global__ __launch_bounds__(kThreads, 1) void layer_kernel(LayerParams p) {
 }
 
 // Instantiations: all-fp32 (d_latent + d_rope <= 160, d_latent <= 128),
-// bf16 attention with bf16 or fp8 experts (d_latent + d_rope <= 576, d_latent <= 512),
+// bf16 attention with bf16, fp8 or MXFP4 experts (d_latent + d_rope <= 576, d_latent <= 512),
 // and the two fixed shapes of kSpecShapes (512 + 64 latent dims, so the
 // attention loop bounds are constants too).
 typedef void (*LayerKernelFn)(LayerParams);
@@ -1828,6 +1862,9 @@ LayerKernelFn layer_kernel_for(int af, int ef, int kf, int d, int nh, int dh, in
     if (ef == MK_FMT_FP8_B128)
       return is(2) ? layer_kernel<MK_FMT_BF16, MK_FMT_FP8_B128, MK_FMT_BF16, 18, 32, true, 2>
                    : layer_kernel<MK_FMT_BF16, MK_FMT_FP8_B128, MK_FMT_BF16, 18, 32, false, 0>;
+    if (ef == MK_FMT_MXFP4)
+      return is(2) ? layer_kernel<MK_FMT_BF16, MK_FMT_MXFP4, MK_FMT_BF16, 18, 32, true, 2>
+                   : layer_kernel<MK_FMT_BF16, MK_FMT_MXFP4, MK_FMT_BF16, 18, 32, false, 0>;
   }
   return nullptr;
 }

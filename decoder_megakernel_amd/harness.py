@@ -51,8 +51,13 @@ class ExpertStager:
     def __init__(self, s: LayerShape, device):
         self.s = s
         self.device = device
-        es = {"f32": 4, "bf16": 2, "fp8": 1}[s.exp_fmt]
         n = s.f * s.d
+        if s.exp_fmt == "mxfp4":
+            # codes [R][K/2] (two per byte) and E8M0 scale bytes [R][K/32]
+            self.w = [_bytes(n // 2, device) for _ in range(3)]
+            self.sc = [_bytes(n // 32, device) for _ in range(3)]
+            return
+        es = {"f32": 4, "bf16": 2, "fp8": 1}[s.exp_fmt]
         self.w = [_bytes(n * es, device) for _ in range(3)]
         nsc = ((s.f + 127) // 128) * ((s.d + 127) // 128)
         self.sc = [torch.empty(nsc, dtype=torch.float32, device=_dev(device)) for _ in range(3)]
@@ -63,13 +68,15 @@ class ExpertStager:
         dims = ((s.f, s.d), (s.f, s.d), (s.d, s.f))
         for i, (tag, (R, K)) in enumerate(zip(("w1", "w3", "w2"), dims)):
             st = synth.stream_id(tag, lay, slot)
-            if s.exp_fmt == "fp8":
+            if s.exp_fmt == "mxfp4":
+                synth.dev_mxfp4_blocks(self.w[i].data_ptr(), self.sc[i].data_ptr(), R, K, seed, st, recipe.W_SIGMA)
+            elif s.exp_fmt == "fp8":
                 synth.dev_fp8_blocks(self.w[i].data_ptr(), self.sc[i].data_ptr(), R, K, seed, st, recipe.W_SIGMA)
             elif s.exp_fmt == "bf16":
                 synth.dev_normal_bf16(self.w[i].data_ptr(), R * K, seed, st, recipe.W_SIGMA)
             else:
                 synth.dev_normal_f32(self.w[i].data_ptr(), R * K, seed, st, recipe.W_SIGMA)
-        scp = [t.data_ptr() for t in self.sc] if s.exp_fmt == "fp8" else [None, None, None]
+        scp = [t.data_ptr() for t in self.sc] if s.exp_fmt in ("fp8", "mxfp4") else [None, None, None]
         pack_expert(cfg, self.w[0].data_ptr(), self.w[1].data_ptr(), self.w[2].data_ptr(), scp[0], scp[1], scp[2],
                     dst_ptr)
 

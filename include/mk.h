@@ -61,8 +61,13 @@ typedef enum mk_status {
 } mk_status;
 
 /* Storage formats.  FP8_B128: OCP E4M3 ("FN": bias 7, max 448) codes with one
- * fp32 scale per 128x128 block of the [rows][cols] matrix (value = code * scale). */
-typedef enum mk_format { MK_FMT_F32 = 0, MK_FMT_BF16 = 1, MK_FMT_FP8_B128 = 2 } mk_format;
+ * fp32 scale per 128x128 block of the [rows][cols] matrix (value = code * scale).
+ * MXFP4: OCP Microscaling (MX v1.0) FP4 -- E2M1 codes, two per byte (element 2j
+ * in the low nibble of byte j), one E8M0 scale byte per 32 consecutive elements
+ * of a row (value = E2M1(code) * 2^(scale - 127)); the expert format the pages'
+ * serving stack uses ("DeepSeek-V4.1-Flash breaks 1,000 tokens per second for
+ * one user", section "Appendix: method"). */
+typedef enum mk_format { MK_FMT_F32 = 0, MK_FMT_BF16 = 1, MK_FMT_FP8_B128 = 2, MK_FMT_MXFP4 = 3 } mk_format;
 
 /* Layer shape.  Canonical weight layouts (row-major) that mk_pack_* consume:
  *   W_Q   [n_heads*(d_head+d_rope)][d_model]  head h owns rows h*(d_head+d_rope)..:
@@ -74,11 +79,11 @@ typedef enum mk_format { MK_FMT_F32 = 0, MK_FMT_BF16 = 1, MK_FMT_FP8_B128 = 2 } 
  *   W_R   [n_experts][d_model]                router; optional bias [n_experts] fp32
  *   W1,W3 [d_ff][d_model], W2 [d_model][d_ff] per expert (SwiGLU: W2 (silu(W1 x) * W3 x))
  * attn_format applies to W_Q, W_DKV, W_UK, W_UV, W_O, W_R (F32 or BF16);
- * expert_format to W1, W3, W2 (F32, BF16 or FP8_B128); kv_format to the cache.
+ * expert_format to W1, W3, W2 (F32, BF16, FP8_B128 or MXFP4); kv_format to the cache.
  * Supported shapes: d_model, d_ff multiples of 128; d_head, d_latent multiples
  * of 32, d_head <= 128, n_heads <= 128; d_rope a multiple of 32; n_experts a multiple of 16 and <= 1024;
  * top_k <= 16; d_model <= 4096; n_heads*d_head and d_ff <= 4608.
- * Formats must be all F32, or attention/KV BF16 with experts BF16 or FP8_B128. */
+ * Formats must be all F32, or attention/KV BF16 with experts BF16, FP8_B128 or MXFP4. */
 typedef struct mk_layer_config {
   int32_t abi_version;       /* must be MK_ABI_VERSION */
   int32_t d_model;
@@ -193,8 +198,10 @@ int mk_layer_workspace_bytes(const mk_layer_config* cfg, int hip_device, size_t*
 /* ---- packing (asynchronous on `stream`) ------------------------------------ */
 /* src: canonical device tensor in the tensor's format (layouts above). */
 int mk_pack_tensor(const mk_layer_config* cfg, int tensor, const void* src, void* dst, void* stream);
-/* One expert: canonical W1, W3 [d_ff][d_model], W2 [d_model][d_ff] in expert_format;
- * for FP8_B128 the three fp32 scale arrays [ceil(rows/128)][ceil(cols/128)], else NULL. */
+/* One expert: canonical W1, W3 [d_ff][d_model], W2 [d_model][d_ff] in expert_format
+ * (MXFP4: bytes [rows][cols/2]); for FP8_B128 the three fp32 scale arrays
+ * [ceil(rows/128)][ceil(cols/128)], for MXFP4 the three E8M0 scale byte arrays
+ * [rows][cols/32] (passed through the same pointers), else NULL. */
 int mk_pack_expert(const mk_layer_config* cfg, const void* w1, const void* w3, const void* w2,
                    const float* s1, const float* s3, const float* s2, void* dst, void* stream);
 

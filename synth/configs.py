@@ -25,7 +25,8 @@ class LayerShape:
     T: int            # verify rows (k drafts + 1)
     L: int            # cached positions before the step
     attn_fmt: str     # "f32" | "bf16"  (W_Q, W_DKV, W_UK, W_UV, W_O, W_R)
-    exp_fmt: str      # "f32" | "bf16" | "fp8"  (W1, W3, W2; fp8 = E4M3 + fp32 128x128 scales)
+    exp_fmt: str      # "f32" | "bf16" | "fp8" | "mxfp4"  (W1, W3, W2; fp8 = E4M3 + fp32 128x128 scales,
+                      #   mxfp4 = E2M1 + an E8M0 scale per 32 elements of a row)
     kv_fmt: str       # "f32" | "bf16"
     routing: str = "uniform"   # "uniform" | "skew" (hot experts get a router bias)
     n_layers: int = 1
@@ -70,8 +71,14 @@ C4 = C3.with_(name="fp8_E384_T6_L65536_skew", T=6, L=65536, routing="skew")
 C5 = C3.with_(name="stack32_fp8_E384_T6_L4096", T=6, L=4096, n_layers=32, V=129280, steps=512,
               kv_capacity=8192, n_pools=16)
 
-PRESETS = {s.name: s for s in (C0, C1, C2, C3, C4, C5)}
-BY_KEY = {"C0": C0, "C1": C1, "C2": C2, "C3": C3, "C4": C4, "C5": C5}
+# The C3 layer with MXFP4 experts (the expert format of the pages' serving stack).
+C3X = C3.with_(name="mxfp4_E384_T8_L8192", exp_fmt="mxfp4")
+# The C5 stack with MXFP4 experts: at half a byte per weight all 32 layers keep
+# routed experts of their own (about 165 GB).
+C5X = C5.with_(name="stack32_mxfp4_E384_T6_L4096", exp_fmt="mxfp4", n_pools=0)
+
+PRESETS = {s.name: s for s in (C0, C1, C2, C3, C4, C5, C3X, C5X)}
+BY_KEY = {"C0": C0, "C1": C1, "C2": C2, "C3": C3, "C4": C4, "C5": C5, "C3X": C3X, "C5X": C5X}
 
 # Skewed routing: the hot set is the first ceil(0.2 E) experts of a seeded permutation.
 HOT_FRACTION = 0.2

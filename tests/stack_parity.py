@@ -46,21 +46,27 @@ class DeviceExpertDraws:
     def __init__(self, s, seed=0, cap=512):
         self.s, self.seed, self.cap = s, seed, cap
         self.cache = OrderedDict()
-        es = {"f32": 4, "bf16": 2, "fp8": 1}[s.exp_fmt]
+        es = {"f32": 4, "bf16": 2, "fp8": 1, "mxfp4": 1}[s.exp_fmt]
         self.buf = torch.empty(s.f * s.d * es, dtype=torch.uint8, device="cuda")
-        nsc = ((s.f + 127) // 128) * ((s.d + 127) // 128)
-        self.sbuf = torch.empty(nsc, dtype=torch.float32, device="cuda")
+        nsc = max(((s.f + 127) // 128) * ((s.d + 127) // 128) * 4, s.f * s.d // 32)
+        self.sbuf = torch.empty(nsc, dtype=torch.uint8, device="cuda")
 
     def _draw(self, tag, R, K, lay, slot):
         s = self.s
         st = synth.stream_id(tag, lay, slot)
         n = R * K
+        if s.exp_fmt == "mxfp4":
+            synth.dev_mxfp4_blocks(self.buf.data_ptr(), self.sbuf.data_ptr(), R, K, self.seed, st, recipe.W_SIGMA)
+            torch.cuda.synchronize()
+            q = self.buf[:n // 2].cpu().numpy().reshape(R, K // 2)
+            sc = self.sbuf[:n // 32].cpu().numpy().reshape(R, K // 32)
+            return q, sc
         if s.exp_fmt == "fp8":
             synth.dev_fp8_blocks(self.buf.data_ptr(), self.sbuf.data_ptr(), R, K, self.seed, st, recipe.W_SIGMA)
             torch.cuda.synchronize()
             nsc = ((R + 127) // 128) * ((K + 127) // 128)
             q = self.buf[:n].cpu().numpy().reshape(R, K)
-            sc = self.sbuf[:nsc].cpu().numpy().reshape((R + 127) // 128, (K + 127) // 128)
+            sc = self.sbuf[:4 * nsc].cpu().numpy().view(np.float32).reshape((R + 127) // 128, (K + 127) // 128)
             return q, sc
         if s.exp_fmt == "bf16":
             synth.dev_normal_bf16(self.buf.data_ptr(), n, self.seed, st, recipe.W_SIGMA)

@@ -2,8 +2,9 @@
 (libmksynth_dev.so), which draws every weight the GPU path is fed, and the
 host build (libmksynth_host.so), which draws the same tensors for the CPU
 oracle.  Covered: raw 64-bit outputs, fp32 normals (with and without a mean),
-bf16 normals, and fp8 E4M3 blocks with their fp32 scales, on ragged shapes
-(edges of partial 128x128 blocks) and at the full size of one expert matrix."""
+bf16 normals, fp8 E4M3 blocks with their fp32 scales, and MXFP4 rows (E2M1
+codes with an E8M0 scale per 32 elements), on ragged shapes (edges of partial
+128x128 blocks) and at the full size of one expert matrix."""
 import numpy as np
 import pytest
 
@@ -59,6 +60,20 @@ def test_fp8_blocks_identical(R, K):
     torch.cuda.synchronize()
     hq, hs = synth.fp8_blocks(R, K, 0, st, 0.02)
     assert np.array_equal(sc.cpu().numpy().view(np.uint32), hs.ravel().view(np.uint32))
+    dq = q.cpu().numpy()
+    bad = np.flatnonzero(dq != hq.ravel())
+    assert bad.size == 0, (bad[:8], dq[bad[:8]], hq.ravel()[bad[:8]])
+
+
+@pytest.mark.parametrize("R,K", [(2048, 4096), (4096, 2048), (300, 224), (1, 32), (17, 96)])
+def test_mxfp4_blocks_identical(R, K):
+    st = synth.stream_id("w2", 9, 3)
+    q = _dev(R * K // 2, torch.uint8)
+    sc = _dev(R * K // 32, torch.uint8)
+    synth.dev_mxfp4_blocks(q.data_ptr(), sc.data_ptr(), R, K, 0, st, 0.02)
+    torch.cuda.synchronize()
+    hq, hs = synth.mxfp4_blocks(R, K, 0, st, 0.02)
+    assert np.array_equal(sc.cpu().numpy(), hs.ravel())
     dq = q.cpu().numpy()
     bad = np.flatnonzero(dq != hq.ravel())
     assert bad.size == 0, (bad[:8], dq[bad[:8]], hq.ravel()[bad[:8]])

@@ -4,7 +4,7 @@ import numpy as np
 import pytest
 
 from synth import recipe
-from synth.configs import C1, C2, C3, C4, LayerShape
+from synth.configs import C1, C2, C3, C3X, C4, LayerShape
 
 pytestmark = pytest.mark.gpu
 
@@ -16,6 +16,12 @@ MID_BF16 = LayerShape("mid_bf16", d=512, n_h=4, d_h=64, d_c=128, d_r=32, E=32, t
                       T=5, L=77, attn_fmt="bf16", exp_fmt="bf16", kv_fmt="bf16")
 MID_FP8 = LayerShape("mid_fp8", d=640, n_h=6, d_h=64, d_c=256, d_r=64, E=48, top_k=6, n_shared=1, f=384,
                      T=7, L=300, attn_fmt="bf16", exp_fmt="fp8", kv_fmt="bf16")
+# MXFP4 experts: 5 and 3 tiles of 128 columns per row (ragged slices), and
+# 16 and 8 (the streaming engines' chunked paths).
+MID_MX = LayerShape("mid_mxfp4", d=640, n_h=6, d_h=64, d_c=256, d_r=64, E=48, top_k=6, n_shared=1, f=384,
+                    T=7, L=300, attn_fmt="bf16", exp_fmt="mxfp4", kv_fmt="bf16")
+MID_MX_WIDE = LayerShape("mid_mxfp4_wide", d=2048, n_h=4, d_h=64, d_c=128, d_r=32, E=32, top_k=4, n_shared=1,
+                         f=1024, T=6, L=100, attn_fmt="bf16", exp_fmt="mxfp4", kv_fmt="bf16")
 MID_F32 = LayerShape("mid_f32", d=384, n_h=4, d_h=32, d_c=96, d_r=32, E=16, top_k=3, n_shared=1, f=256,
                      T=3, L=45, attn_fmt="f32", exp_fmt="f32", kv_fmt="f32")
 # Expert widths of 32 tiles, d_model of 64 tiles and d_model >= 2 d_ff: the
@@ -46,7 +52,7 @@ def _run(s, seed=0, layer=0, L=None, T=None, full_weights=True):
     return dl, kv, Hd, g_out, g_kv, errs
 
 
-@pytest.mark.parametrize("shape", [C1, MID_F32, MID_BF16, MID_FP8, MID_F32_DOWN, MID_BF16_DOWN],
+@pytest.mark.parametrize("shape", [C1, MID_F32, MID_BF16, MID_FP8, MID_F32_DOWN, MID_BF16_DOWN, MID_MX, MID_MX_WIDE],
                          ids=lambda s: s.name)
 def test_small_shapes_match_oracle(shape):
     _run(shape)
@@ -66,6 +72,10 @@ def test_full_size_bf16_E128_T6_L2048():
 
 def test_full_size_fp8_E384_T8_L8192():
     _run(C3, full_weights=False)
+
+
+def test_full_size_mxfp4_E384_T8_L8192():
+    _run(C3X, full_weights=False)
 
 
 def test_full_size_fp8_E384_T6_L65536_skew():

@@ -1,7 +1,8 @@
 """GPU parity of the 32-layer stack at its real shape: 32 layers of the fp8
 384-expert layer (16 routed-expert pools), d_model 4096, vocab 129,280,
 T = 6, cache from 4096 positions (capacity 8192) -- the same stack and launch
-configuration bench.py times.
+configuration bench.py times -- and the same stack with MXFP4 experts, every
+layer with routed experts of its own.
 
   - steps 0-3 against the oracle composed layer by layer on its own rows and
     caches (free-running): logits normwise <= 5e-2, argmax and expert selection
@@ -23,19 +24,19 @@ import pytest
 
 import stack_parity as sp
 from synth import recipe
-from synth.configs import C5
+from synth.configs import C5, C5X
 
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
 
 
-def test_full_stack_32_layers_vocab_129280():
+@pytest.mark.parametrize("s", [C5, C5X], ids=lambda s: s.name)
+def test_full_stack_32_layers_vocab_129280(s):
     from decoder_megakernel_amd import harness
-    s = C5
-    print("[stack C5] building %s on the GPU" % s.name, flush=True)
+    print("[stack] building %s on the GPU" % s.name, flush=True)
     st = harness.DeviceStack(s, 0, private_workspaces=True)
     rec = sp.attach_record(st, s)
-    print("[stack C5] host tables", flush=True)
+    print("[stack] host tables", flush=True)
     ws = [recipe.layer_weights_host(s, 0, l, experts=[]) for l in range(s.n_layers)]
     kvs = [recipe.kv_prefill_host(s, 0, l) for l in range(s.n_layers)]
     tables = recipe.stack_tables_host(s, 0)
@@ -50,7 +51,7 @@ def test_full_stack_32_layers_vocab_129280():
             torch.cuda.synchronize()
         g = sp.gpu_step(st, s, rec, tokens, nxt)
         assert g["L"] == L
-        tag = " C5 step %d" % step
+        tag = " %s step %d" % (s.name, step)
         assert np.isfinite(g["logits"]).all() and np.isfinite(g["hidden"]).all()
         o_lg, o_am, _ = sp.oracle_stack_step(s, ws, tables, kvs, tokens, L, g=g, expert_fn=draws, tag=tag)
         com = sp.compare_free_running(s, g, o_lg, o_am, tokens, tag=tag)
