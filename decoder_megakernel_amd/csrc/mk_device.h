@@ -761,6 +761,12 @@ __device__ __forceinline__ void run_stream(int u0, int u1, int NT, int T, const 
 // `ctr[kCntStride * c]` must be zero before the first workgroup gets here.  Requires slice = NT/8
 // to be a multiple of D.
 //
+// SPLIT = 2: the workgroup works on two units at a time (a group of units
+// 2g, 2g + 1 is what a ticket hands out), waves 0-3 on the first and 4-7 on the
+// second, each unit's NT tiles cut into 4 slices -- twice the bytes per wave
+// of a unit, for formats whose rows hold few tiles.  A group's second unit
+// beyond U (odd U) is streamed again as unit U - 1 and discarded.
+//
 // With a Done callback (not NoDone), the epilogue works on row pairs instead:
 // epi(u, row0, col, v0, v2_0, v1, v2_1) for rows row0 and row0 + 1 (threads
 // < 128) writes them with value-returning atomics and returns the reply.  A
@@ -772,21 +778,25 @@ __device__ __forceinline__ void run_stream(int u0, int u1, int NT, int T, const 
 struct NoDone {
   __device__ void operator()(int) const {}
 };
-template <int FMT, bool DUAL, int D, class Src, class Epi, class Done = NoDone>
+template <int FMT, bool DUAL, int D, int SPLIT = 1, class Src, class Epi, class Done = NoDone>
 __device__ __forceinline__ void run_stream_dyn(int U, int NT, int T, const Src& src, const Epi& epi, float* red,
                                                const uint8_t* dummy, uint32_t* ctr, int* seq,
                                                const Done& done = Done()) {
   constexpr bool kPairs = !std::is_same<Done, NoDone>::value;
   constexpr int TK = tile_k(FMT);
   constexpr long long STRIDE = DUAL ? 2048 : 1024;
+  constexpr int WPU = kWaves / SPLIT;              // waves per unit
   const int w = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int nwg = (int)gridDim.x;
-  const int slice = NT / kWaves;
+  const int half = w / WPU;                        // which unit of the group this wave streams
+  const int slice = NT / WPU;
   const int cps = slice / D;
-  const int toff = w * slice;
-  int cur = (int)blockIdx.x < U ? (int)blockIdx.x : -1;
-  int nxt = (int)blockIdx.x + nwg < U ? (int)blockIdx.x + nwg : -1;
+  const int toff = (w % WPU) * slice;
+  const int UG = (U + SPLIT - 1) / SPLIT;          // unit groups
+  auto sub = [&](int g) { return min(g * SPLIT + half, U - 1); };
+  int cur = (int)blockIdx.x < UG ? (int)blockIdx.x : -1;
+  int nxt = (int)blockIdx.x + nwg < UG ? (int)blockIdx.x + nwg : -1;
   if (cur < 0 || cps <= 0) return;
   const float* dsc = reinterpret_cast<const float*>(dummy);
   u32x4 buf[D], buf2[D];
@@ -795,15 +805,16 @@ __device__ __forceinline__ void run_stream_dyn(int U, int NT, int T, const Src& 
     // issued exactly as the loop issues a chunk (same order, scales on the
     // vector path too), so that the loop's waits count the same loads whether
     // it is entered from here or from its own end
-    const uint8_t* cbase = src.base(cur) + lane * 16 + (long long)toff * STRIDE;
+    const int u = sub(cur);
+    const uint8_t* cbase = src.base(u) + lane * 16 + (long long)toff * STRIDE;
     const int vz = vzero();
 #pragma unroll
     for (int r = 0; r < D; ++r) {
       buf[r] = ld_stream16(cbase + r * STRIDE);
       if constexpr (DUAL) buf2[r] = ld_stream16(cbase + r * STRIDE + 1024);
       if constexpr (scaled_fmt(FMT)) {
-        sc[r] = tile_scale<FMT, DUAL>(src.sbase(cur), toff + r, lane, vz);
-        if constexpr (DUAL) sc2[r] = tile_scale<FMT, DUAL>(src.sbase2(cur), toff + r, lane, vz);
+        sc[r] = tile_scale<FMT, DUAL>(src.sbase(u), toff + r, lane, vz);
+        if constexpr (DUAL) sc2[r] = tile_scale<FMT, DUAL>(src.sbase2(u), toff + r, lane, vz);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -821,7 +832,7 @@ __device__ __forceinline__ void run_stream_dyn(int U, int NT, int T, const Src& 
   BPair bn;
   f32x4 tp = zero, tp2 = zero;
   float sp = 0.f, sp2 = 0.f;
-  if constexpr (FMT == MK_FMT_FP8_B128) bn = b_pair(src.bbase(cur) + toff * TK);
+  if constexpr (FMT == MK_FMT_FP8_B128) bn = b_pair(src.bbase(sub(cur)) + toff * TK);
   uint32_t reply = 0;               // row-pair epilogue: the reply of this thread's last write
   int prev = -1;                    // row-pair epilogue: the unit written but not yet published
   while (true) {
@@ -834,21 +845,22 @@ __device__ __forceinline__ void run_stream_dyn(int U, int NT, int T, const Src& 
     }
     const bool has_next = un >= 0;
     const int tn = toff + ncc * D;
-    const uint8_t* nb = has_next ? src.base(un) + lane * 16 + (long long)tn * STRIDE : dummy + lane * 16;
+    const int unu = has_next ? sub(un) : 0;
+    const uint8_t* nb = has_next ? src.base(unu) + lane * 16 + (long long)tn * STRIDE : dummy + lane * 16;
     const float* nsp = dsc;
     const float* nsp2 = dsc;
     if constexpr (scaled_fmt(FMT)) {
       if (has_next) {
-        nsp = src.sbase(un);
-        if constexpr (DUAL) nsp2 = src.sbase2(un);
+        nsp = src.sbase(unu);
+        if constexpr (DUAL) nsp2 = src.sbase2(unu);
       }
     }
-    const auto* bp = src.bbase(cur) + (toff + cc * D) * TK;
+    const auto* bp = src.bbase(sub(cur)) + (toff + cc * D) * TK;
 #pragma unroll
     for (int r = 0; r < D; ++r) {
       if constexpr (FMT == MK_FMT_FP8_B128) {
         const BPair b = bn;
-        bn = b_pair(r + 1 < D ? bp + (r + 1) * TK : (has_next ? src.bbase(un) + tn * TK : bp));
+        bn = b_pair(r + 1 < D ? bp + (r + 1) * TK : (has_next ? src.bbase(unu) + tn * TK : bp));
         const f32x4 tmp = tile_mma_fp8(buf[r], b, zero);
         acc += tp * sp;
         tp = tmp;
@@ -897,39 +909,43 @@ __device__ __forceinline__ void run_stream_dyn(int U, int NT, int T, const Src& 
     if constexpr (DUAL) *reinterpret_cast<f32x4*>(rb + kWaves * 64 * 4 + (w * 64 + lane) * 4) = acc2;
     if (threadIdx.x == 0) {
       long long un2 = 2LL * nwg + 8LL * tk + cq;
-      for (int tries = 1; un2 >= U && tries < 8; ++tries) {
+      for (int tries = 1; un2 >= UG && tries < 8; ++tries) {
         cq = (cq + 1) & 7;
         tk = __hip_atomic_fetch_add(ctr + kCntStride * cq, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         un2 = 2LL * nwg + 8LL * tk + cq;
       }
-      seq[par] = un2 < U ? (int)un2 : -1;
+      seq[par] = un2 < UG ? (int)un2 : -1;
     }
     __syncthreads();
     if constexpr (!kPairs) {
-      if (threadIdx.x < 256) {
-        const int col = threadIdx.x & 15, row = threadIdx.x >> 4;
+      if (threadIdx.x < 256 * SPLIT) {
+        const int h = threadIdx.x >> 8, t = threadIdx.x & 255;
+        const int col = t & 15, row = t >> 4;
         const int l = (row >> 2) * 16 + col, e = row & 3;
-        if (col < T) {
+        const int u = cur * SPLIT + h;
+        if (col < T && u < U) {
           float v = 0.f, v2 = 0.f;
 #pragma unroll
-          for (int ww = 0; ww < kWaves; ++ww) {
+          for (int ww = h * WPU; ww < (h + 1) * WPU; ++ww) {
             v += rb[(ww * 64 + l) * 4 + e];
             if constexpr (DUAL) v2 += rb[kWaves * 64 * 4 + (ww * 64 + l) * 4 + e];
           }
-          epi(cur, row, col, v, v2);
+          epi(u, row, col, v, v2);
         }
       }
     } else {
       // the previous unit's writes have completed once their replies are here
       // (used before this unit's writes reuse the register)
       wait_for(reply);
-      if (threadIdx.x < 128) {
-        const int col = threadIdx.x & 15, row = (threadIdx.x >> 4) * 2;
+      if (threadIdx.x < 128 * SPLIT) {
+        const int h = threadIdx.x >> 7, t = threadIdx.x & 127;
+        const int col = t & 15, row = (t >> 4) * 2;
         const int l = (row >> 2) * 16 + col, e = row & 3;
-        if (col < T) {
+        const int u = cur * SPLIT + h;
+        if (col < T && u < U) {
           float v0 = 0.f, v1 = 0.f, w0 = 0.f, w1 = 0.f;
 #pragma unroll
-          for (int ww = 0; ww < kWaves; ++ww) {
+          for (int ww = h * WPU; ww < (h + 1) * WPU; ++ww) {
             v0 += rb[(ww * 64 + l) * 4 + e];
             v1 += rb[(ww * 64 + l) * 4 + e + 1];
             if constexpr (DUAL) {
@@ -937,11 +953,13 @@ __device__ __forceinline__ void run_stream_dyn(int U, int NT, int T, const Src& 
               w1 += rb[kWaves * 64 * 4 + (ww * 64 + l) * 4 + e + 1];
             }
           }
-          reply = epi(cur, row, col, v0, w0, v1, w1);
+          reply = epi(u, row, col, v0, w0, v1, w1);
         }
       }
       __syncthreads();
-      if (threadIdx.x == 0 && prev >= 0) done(prev);
+      if (threadIdx.x == 0 && prev >= 0)
+        for (int h = 0; h < SPLIT; ++h)
+          if (prev * SPLIT + h < U) done(prev * SPLIT + h);
       prev = cur;
     }
     acc = zero;
@@ -954,7 +972,9 @@ __device__ __forceinline__ void run_stream_dyn(int U, int NT, int T, const Src& 
   if constexpr (kPairs) {
     wait_for(reply);
     __syncthreads();
-    if (threadIdx.x == 0 && prev >= 0) done(prev);
+    if (threadIdx.x == 0 && prev >= 0)
+      for (int h = 0; h < SPLIT; ++h)
+        if (prev * SPLIT + h < U) done(prev * SPLIT + h);
   }
   __syncthreads();
 }

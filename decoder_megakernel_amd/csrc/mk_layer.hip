@@ -1134,11 +1134,19 @@ struct ExpScales {
     else return reinterpret_cast<const float*>(blk + sc2) + (rt >> 3) * n2;
   }
 };
-// Tiles per chunk of the ticket-fed streams: gate/up (two matrices per tile
-// slot) and down projections.  An MXFP4 tile holds twice the columns of an fp8
-// tile, so a row of d_model or d_ff has half as many of them.
-__host__ __device__ constexpr int gateup_depth(int fmt) { return fmt == MK_FMT_MXFP4 ? 4 : 8; }
-__host__ __device__ constexpr int down_depth(int tk) { return tk >= 128 ? 8 : 16; }
+// Shapes of the ticket-fed expert streams.  An MXFP4 tile holds twice the
+// columns of an fp8 tile, so a row of d_model or d_ff has half as many tiles;
+// to keep as many bytes per wave in flight, MXFP4 gate/up units go two to a
+// workgroup (four waves each), and MXFP4 down-projection units are eight row
+// tiles with each wave streaming one of them over all of d_ff.
+constexpr int kGateDepth = 8;                      // gate/up tiles per chunk (two matrices each)
+__host__ __device__ constexpr int gateup_split(int fmt) { return fmt == MK_FMT_MXFP4 ? 2 : 1; }
+__host__ __device__ constexpr bool gateup_dyn_fits(int KT, int fmt) {
+  return KT % (kWaves / gateup_split(fmt)) == 0 && (KT / (kWaves / gateup_split(fmt))) % kGateDepth == 0;
+}
+__host__ __device__ constexpr int down_rtu(int tk) { return tk >= 128 ? 8 : 4; }   // row tiles per unit
+__host__ __device__ constexpr int down_kp(int tk) { return kWaves / down_rtu(tk); }  // k parts per row tile
+constexpr int kDownDepth = 16;                     // down-projection tiles per chunk
 
 // MODE 0: workgroup units [u0, u1); 1: wave units [u0, u1); 2: workgroup units
 // 0 .. u1-1 handed out at run time by the ticket counters; 3: as 2, and every
@@ -1212,12 +1220,13 @@ __device__ __forceinline__ void gateup_units(const LayerParams& p, const uint8_t
     };
     stage.issue();
     stage.finish();
-    run_stream_dyn<EF, true, gateup_depth(EF)>(u1, KT, T, src, epi2, red, p.dummy, p.att_cnt + kGateCnt, seq_lds(),
-                                               done);
+    run_stream_dyn<EF, true, kGateDepth, gateup_split(EF)>(u1, KT, T, src, epi2, red, p.dummy, p.att_cnt + kGateCnt,
+                                                           seq_lds(), done);
   } else if constexpr (MODE == 2) {
     stage.issue();
     stage.finish();
-    run_stream_dyn<EF, true, gateup_depth(EF)>(u1, KT, T, src, epi, red, p.dummy, p.att_cnt + kGateCnt, seq_lds());
+    run_stream_dyn<EF, true, kGateDepth, gateup_split(EF)>(u1, KT, T, src, epi, red, p.dummy, p.att_cnt + kGateCnt,
+                                                           seq_lds());
   } else if constexpr (MODE == 1) {
     stage.issue();
     stage.finish();
@@ -1322,7 +1331,7 @@ __device__ __forceinline__ void phase_route_gateup(const LayerParams& p, char* s
   const int ns = *r.nslots;
   const int U = (ns - s0) * (p.f / 16);
   const int KT = p.d / tile_k(EF);
-  if (KT % kWaves == 0 && (KT / kWaves) % gateup_depth(EF) == 0) {
+  if (gateup_dyn_fits(KT, EF)) {
     // units handed out at run time (ticket counter), 8 waves per unit
     gateup_units<EF, 2>(p, r.blk + s0, s0, 0, U, xs, red);
     return;
@@ -1336,11 +1345,14 @@ __device__ __forceinline__ void phase_route_gateup(const LayerParams& p, char* s
 }
 
 // ------------------------------------------------------------------ P7 down projections (ticket-fed)
-// Unit u = (slot u / QP, row tiles 4 (u % QP) .. 4 (u % QP) + 3 of d_model),
-// QP = d_model / 64: four row tiles times all KT tiles of W2.  Wave w streams
-// row tile 4 (u % QP) + (w & 3) over K half w >> 2 (KT / 2 tiles in chunks of
-// D, the next chunk requested while the current one is multiplied, across unit
-// boundaries), and waves w and w + 4 add their blocks in LDS.  Workgroup b
+// Unit u = (slot u / QP, row tiles RTU (u % QP) ... RTU (u % QP) + RTU - 1 of
+// d_model), QP = d_model / (16 RTU): RTU row tiles times all KT tiles of W2.
+// Wave w streams row tile RTU (u % QP) + w % RTU over k part w / RTU (KT / KP
+// tiles, KP = 8 / RTU, in chunks of D, the next chunk requested while the
+// current one is multiplied, across unit boundaries); with two k parts the
+// waves w and w + 4 add their blocks in LDS.  RTU = 4 (two k parts), or 8 (one
+// k part, each wave's sums final) for MXFP4, whose rows hold half as many
+// tiles.  Workgroup b
 // first takes a run of R = min(8, units / nwg) consecutive units starting at
 // b R (one slot, so its rows are loaded once), then draws tickets for the rest
 // as run_stream_dyn does, so workgroups on faster XCDs take more units and the
@@ -1355,7 +1367,8 @@ __device__ __forceinline__ void phase_route_gateup(const LayerParams& p, char* s
 // starts and checks it, waiting if needed, when the unit ends), and they are read
 // with agent-scope loads, which do not return stale lines of this XCD's L2.
 __host__ __device__ constexpr bool down_dyn_fits(int d, int f, int tk, int es, int xb) {
-  return d % 64 == 0 && (f / tk) % (2 * down_depth(tk)) == 0 && 2 * kMaxT * (f + kXPad) * es <= xb &&
+  return d % (16 * down_rtu(tk)) == 0 && (f / tk) % (down_kp(tk) * kDownDepth) == 0 &&
+         2 * kMaxT * (f + kXPad) * es <= xb &&
          kMaxT * f * es <= 16 * kThreads * 4;
 }
 
@@ -1366,7 +1379,7 @@ template <int EF>
 __device__ __forceinline__ bool experts_fused(const LayerParams& p, int xb) {
   constexpr int TK = tile_k(EF);
   const int KT = p.d / TK;
-  return KT % kWaves == 0 && (KT / kWaves) % gateup_depth(EF) == 0 &&
+  return gateup_dyn_fits(KT, EF) &&
          down_dyn_fits(p.d, p.f, TK, (int)sizeof(typename Act<EF>::T), xb);
 }
 
@@ -1375,14 +1388,15 @@ __device__ __forceinline__ bool phase_down_dyn(const LayerParams& p, char* smem,
                                                int s_wait) {
   typedef typename Act<EF>::T A;
   constexpr int TK = tile_k(EF);
-  constexpr int D = down_depth(TK);
+  constexpr int D = kDownDepth;
+  constexpr int RTU = down_rtu(TK), KP = down_kp(TK);
   constexpr int HW = 16;                                   // dwords of expert rows per thread, at most
   const int T = p.T, f = p.f, d = p.d, HS = f + kXPad;
   const int ns = *r.nslots;
-  const int QP = d / 64, KT = f / TK, NTh = KT / 2, cps = NTh / D;
+  const int QP = d / (16 * RTU), KT = f / TK, NTh = KT / KP, cps = NTh / D;
   const int U = ns * QP;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int sub = w & 3, kp = w >> 2;
+  const int sub = w % RTU, kp = w / RTU;
   const int nwg = (int)gridDim.x;
   const long long w2_off = p.exp_w13_bytes;
   const ExpScales<EF> es(p);
@@ -1398,7 +1412,7 @@ __device__ __forceinline__ bool phase_down_dyn(const LayerParams& p, char* smem,
   int* flag = reinterpret_cast<int*>(smem + kFlagOff);
   const float* dsc = reinterpret_cast<const float*>(p.dummy);
   // This workgroup's first RS units are fixed: a run of R consecutive units
-  // (four row tiles each, all in one slot when R divides d_model / 64) when
+  // (all in one slot when R divides QP) when
   // there are at least two per workgroup, else units b and b + nwg; the rest
   // come from the tickets.  Consecutive units of one slot share its rows.
   const int R = min(8, U / nwg);
@@ -1478,11 +1492,11 @@ __device__ __forceinline__ bool phase_down_dyn(const LayerParams& p, char* smem,
     return 1;
   };
   auto wbase = [&](int u) {
-    const int sl = u / QP, rt = 4 * (u - sl * QP) + sub;
+    const int sl = u / QP, rt = RTU * (u - sl * QP) + sub;
     return r.blk[sl] + w2_off + (long long)rt * KT * 1024 + lane * 16 + (long long)kp * NTh * 1024;
   };
   auto sbase = [&](int u) {
-    const int sl = u / QP, rt = 4 * (u - sl * QP) + sub;
+    const int sl = u / QP, rt = RTU * (u - sl * QP) + sub;
     return es.w2(r.blk[sl], rt);
   };
   u32x4 buf[D];
@@ -1508,6 +1522,7 @@ __device__ __forceinline__ bool phase_down_dyn(const LayerParams& p, char* smem,
   h_load(cur / QP, hv);
   h_store(hls, hv);
   __syncthreads();
+  trace_x(p, 15);
   uint32_t tk = 0, cseen = 0;
   int cq = (int)blockIdx.x & 7;
   int cc = 0, par = 0, hb = 0;
@@ -1572,15 +1587,24 @@ __device__ __forceinline__ bool phase_down_dyn(const LayerParams& p, char* smem,
     }
     cc = ncc;
     if (ncc != 0) continue;
-    // unit `cur` complete: the blocks of waves w and w + 4 added, the unit
-    // after nxt published, the next slot's completion confirmed
+    // unit `cur` complete: the blocks of waves w and w + 4 added (two k
+    // parts), the unit after nxt published, the next slot's completion confirmed
     if constexpr (EF == MK_FMT_FP8_B128) {
       acc += tp * sp;
       tp = zero;
       sp = 0.f;
     }
     float* rb = red + par * (kWaves * 64 * 4);
-    *reinterpret_cast<f32x4*>(rb + (w * 64 + lane) * 4) = acc;
+    if constexpr (KP == 2) {
+      *reinterpret_cast<f32x4*>(rb + (w * 64 + lane) * 4) = acc;
+    } else {
+      // one k part: this wave's sums are final (lane: rows 4 g + e, column j)
+      if (j < T) {
+        const int sl = cur / QP, rt = RTU * (cur - sl * QP) + sub;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) yb[((long long)sl * T + j) * d + rt * 16 + 4 * g + e] = acc[e];
+      }
+    }
     if (threadIdx.x == 0) {
       if (kk + 2 < RS) {
         seq[par] = static_unit(kk + 2);
@@ -1597,12 +1621,13 @@ __device__ __forceinline__ bool phase_down_dyn(const LayerParams& p, char* smem,
     }
     __syncthreads();
     if (!*flag) return false;
-    {
+    if (kk == 0) trace_x(p, 4);
+    if constexpr (KP == 2) {
       const int s4 = threadIdx.x >> 7, rem = threadIdx.x & 127, row = rem >> 3, col = rem & 7;
       if (col < T) {
         const int l = (row >> 2) * 16 + col, e = row & 3;
         const float v = rb[(s4 * 64 + l) * 4 + e] + rb[((s4 + 4) * 64 + l) * 4 + e];
-        const int sl = cur / QP, rt = 4 * (cur - sl * QP) + s4;
+        const int sl = cur / QP, rt = RTU * (cur - sl * QP) + s4;
         yb[((long long)sl * T + col) * d + rt * 16 + row] = v;
       }
     }

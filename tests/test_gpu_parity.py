@@ -22,6 +22,11 @@ MID_MX = LayerShape("mid_mxfp4", d=640, n_h=6, d_h=64, d_c=256, d_r=64, E=48, to
                     T=7, L=300, attn_fmt="bf16", exp_fmt="mxfp4", kv_fmt="bf16")
 MID_MX_WIDE = LayerShape("mid_mxfp4_wide", d=2048, n_h=4, d_h=64, d_c=128, d_r=32, E=32, top_k=4, n_shared=1,
                          f=1024, T=6, L=100, attn_fmt="bf16", exp_fmt="mxfp4", kv_fmt="bf16")
+# d_model 4096 (32 MXFP4 tiles): ticket-fed gate/up with two units per workgroup;
+# with d_ff 2048 also the ticket-fed down projections of eight row tiles (fused).
+MID_MX_TICKET = LayerShape("mid_mxfp4_ticket", d=4096, n_h=4, d_h=64, d_c=128, d_r=32, E=16, top_k=3, n_shared=1,
+                           f=1024, T=5, L=60, attn_fmt="bf16", exp_fmt="mxfp4", kv_fmt="bf16")
+MID_MX_FUSED = MID_MX_TICKET.with_(name="mid_mxfp4_fused", f=2048, top_k=2, T=6, L=33)
 MID_F32 = LayerShape("mid_f32", d=384, n_h=4, d_h=32, d_c=96, d_r=32, E=16, top_k=3, n_shared=1, f=256,
                      T=3, L=45, attn_fmt="f32", exp_fmt="f32", kv_fmt="f32")
 # Expert widths of 32 tiles, d_model of 64 tiles and d_model >= 2 d_ff: the
@@ -52,8 +57,8 @@ def _run(s, seed=0, layer=0, L=None, T=None, full_weights=True):
     return dl, kv, Hd, g_out, g_kv, errs
 
 
-@pytest.mark.parametrize("shape", [C1, MID_F32, MID_BF16, MID_FP8, MID_F32_DOWN, MID_BF16_DOWN, MID_MX, MID_MX_WIDE],
-                         ids=lambda s: s.name)
+@pytest.mark.parametrize("shape", [C1, MID_F32, MID_BF16, MID_FP8, MID_F32_DOWN, MID_BF16_DOWN, MID_MX, MID_MX_WIDE,
+                                   MID_MX_TICKET, MID_MX_FUSED], ids=lambda s: s.name)
 def test_small_shapes_match_oracle(shape):
     _run(shape)
 
