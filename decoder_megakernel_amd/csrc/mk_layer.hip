@@ -493,6 +493,8 @@ template <> struct AttnTypes<MK_FMT_F32> {
   static constexpr int KBW = 16;
 };
 
+constexpr float kAttSlack = 8.f;                 // softmax reference moves when exceeded by this much
+
 // KV splits per query tile and keys per split (the same in P2 and P3).
 __device__ __forceinline__ void attn_splits(int NQT, int Lt, int& s_kv, int& SK) {
   s_kv = (int)gridDim.x / NQT;
@@ -630,23 +632,29 @@ __device__ __forceinline__ void phase_attention(const LayerParams& p, int L, cha
       }
       cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
       cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
-      const float m_new = fmaxf(m_run, cmax);
-      float alpha, pe[4];
-      if (m_new == -INFINITY) {
-        alpha = 1.f;
+      // The reference maximum m_run moves only when a chunk's maximum exceeds
+      // it by more than kAttSlack: any reference gives the same softmax, and
+      // exponentials up to e^kAttSlack are safe in fp32 sums, so the running
+      // sum and the accumulator are rescaled on few chunks (the decision is the
+      // same in every lane of the wave: both waves of a pair hold the same scores).
+      const int DBh = EXACT ? DBH : nl * PB;
+      const bool move = cmax > m_run + kAttSlack;
+      if (__builtin_amdgcn_ballot_w64(move) != 0) {
+        const float m_new = move ? cmax : m_run;
+        const float alpha = m_run == -INFINITY ? 0.f : __expf(m_run - m_new);
+        l_run *= alpha;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) pe[e] = 0.f;
-      } else {
-        alpha = __expf(m_run - m_new);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) pe[e] = __expf(sc[e] - m_new);
+        for (int db = 0; db < DBH; ++db)
+          if (db < DBh) acc[db] *= alpha;
+        m_run = m_new;
       }
+      float pe[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pe[e] = m_run == -INFINITY ? 0.f : __expf(sc[e] - m_run);
       float ps = pe[0] + pe[1] + pe[2] + pe[3];
       ps += __shfl_xor(ps, 16);
       ps += __shfl_xor(ps, 32);
-      l_run = l_run * alpha + ps;
-      m_run = m_new;
-      const int DBh = EXACT ? DBH : nl * PB;
+      l_run += ps;
       if (KF == MK_FMT_BF16) {
         bf16x4 pb;
 #pragma unroll
@@ -662,13 +670,13 @@ __device__ __forceinline__ void phase_attention(const LayerParams& p, int L, cha
             if (d0 + i < DBh) av[i] = lds_read_tr16(tb + (d0 + i) * 16);
 #pragma unroll
           for (int i = 0; i < 8; ++i)
-            if (d0 + i < DBh) acc[d0 + i] = mma_bf16_k16(av[i], pb, acc[d0 + i] * alpha);
+            if (d0 + i < DBh) acc[d0 + i] = mma_bf16_k16(av[i], pb, acc[d0 + i]);
         }
       } else {
 #pragma unroll
         for (int db = 0; db < DBH; ++db) {
           if (db < DBh) {
-            f32x4 a = acc[db] * alpha;
+            f32x4 a = acc[db];
 #pragma unroll
             for (int e = 0; e < 4; ++e) a = mma_f32_k4((float)vs[(4 * g + e) * CSH + db * 16 + j], pe[e], a);
             acc[db] = a;
