@@ -329,6 +329,7 @@ struct mk_model {
   float* best_val;
   int32_t* best_idx;
   uint32_t* counter;
+  uint32_t* tickets;   // the head's ticket counters
   const uint8_t* dummy;
   int nwg_head;
 };
@@ -735,7 +736,7 @@ int mk_pack_head(int32_t vocab, int32_t d_model, const uint16_t* src_bf16, void*
 }
 
 struct ModelStLayout {
-  size_t len, counter, fault, best_val, best_idx, dummy, total;
+  size_t len, counter, fault, best_val, best_idx, tickets, dummy, total;
 };
 static ModelStLayout model_layout(int nwg) {
   ModelStLayout l;
@@ -746,6 +747,7 @@ static ModelStLayout model_layout(int nwg) {
   l.fault = take(4);
   l.best_val = take((size_t)nwg * 8 * 4);
   l.best_idx = take((size_t)nwg * 8 * 4);
+  l.tickets = take((size_t)8 * kCntStride * 4);
   l.dummy = take(32768);
   l.total = off;
   return l;
@@ -816,6 +818,7 @@ int mk_model_init(mk_layer* const* layers, int32_t n_layers, const uint16_t* emb
   m->hidden_rec = nullptr;
   m->best_val = (float*)(m->state + ml.best_val);
   m->best_idx = (int32_t*)(m->state + ml.best_idx);
+  m->tickets = (uint32_t*)(m->state + ml.tickets);
   m->dummy = (const uint8_t*)(m->state + ml.dummy);
   m->nwg_head = nwg;
   hipError_t e = hipMemset(m->state, 0, ml.total);
@@ -857,7 +860,8 @@ int mk_model_step(mk_model* m, int32_t* tokens_dev, int T, const int32_t* next_d
     if (rc) return rc;
   }
   rc = launch_head(m->head, m->V, d, m->gamma_f, m->layers[0]->cfg.rms_eps, hid(m->n_layers), T, logits_dev,
-                   m->best_val, m->best_idx, m->counter, tokens_dev, next_drafts_dev, argmax_dev, committed_dev,
+                   m->best_val, m->best_idx, m->counter, m->tickets, tokens_dev, next_drafts_dev, argmax_dev,
+                   committed_dev,
                    m->kv_len, m->dummy, m->fault, m->nwg_head, s);
   if (rc) return fail(MK_ERR_HIP, "head launch failed");
   return MK_OK;
@@ -887,6 +891,7 @@ int mk_model_reset(mk_model* m) {
   hipSetDevice(m->layers[0]->dev);
   hipError_t e1 = hipMemset(m->fault, 0, 4);
   hipError_t e2 = hipMemset(m->counter, 0, 4);
+  if (e2 == hipSuccess) e2 = hipMemset(m->tickets, 0, (size_t)8 * kCntStride * 4);
   hipError_t e3 = hipDeviceSynchronize();
   hipSetDevice(cur);
   if (e1 != hipSuccess || e2 != hipSuccess || e3 != hipSuccess) return fail(MK_ERR_HIP, "model reset failed");

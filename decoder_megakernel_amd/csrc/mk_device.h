@@ -775,13 +775,19 @@ __device__ __forceinline__ void run_stream(int u0, int u1, int NT, int T, const 
 // chunk requested since, which a wait for all its memory operations would
 // drain), and after a workgroup barrier thread 0 calls done(u).  The last
 // unit is published when the stream ends.
+//
+// `pre` runs after the first chunk has been requested and before it is used
+// (the activation operand can be staged there while that chunk is on its way).
 struct NoDone {
   __device__ void operator()(int) const {}
 };
-template <int FMT, bool DUAL, int D, int SPLIT = 1, class Src, class Epi, class Done = NoDone>
+struct NoPre {
+  __device__ void operator()() const {}
+};
+template <int FMT, bool DUAL, int D, int SPLIT = 1, class Src, class Epi, class Done = NoDone, class Pre = NoPre>
 __device__ __forceinline__ void run_stream_dyn(int U, int NT, int T, const Src& src, const Epi& epi, float* red,
                                                const uint8_t* dummy, uint32_t* ctr, int* seq,
-                                               const Done& done = Done()) {
+                                               const Done& done = Done(), const Pre& pre = Pre()) {
   constexpr bool kPairs = !std::is_same<Done, NoDone>::value;
   constexpr int TK = tile_k(FMT);
   constexpr long long STRIDE = DUAL ? 2048 : 1024;
@@ -797,7 +803,10 @@ __device__ __forceinline__ void run_stream_dyn(int U, int NT, int T, const Src& 
   auto sub = [&](int g) { return min(g * SPLIT + half, U - 1); };
   int cur = (int)blockIdx.x < UG ? (int)blockIdx.x : -1;
   int nxt = (int)blockIdx.x + nwg < UG ? (int)blockIdx.x + nwg : -1;
-  if (cur < 0 || cps <= 0) return;
+  if (cur < 0 || cps <= 0) {
+    pre();
+    return;
+  }
   const float* dsc = reinterpret_cast<const float*>(dummy);
   u32x4 buf[D], buf2[D];
   float sc[D], sc2[D];
@@ -819,6 +828,7 @@ __device__ __forceinline__ void run_stream_dyn(int U, int NT, int T, const Src& 
       __builtin_amdgcn_sched_barrier(0);
     }
   }
+  pre();
   uint32_t tk = 0;
   int cq = (int)blockIdx.x & 7;     // counter drawn from (thread 0)
   int cc = 0, par = 0;

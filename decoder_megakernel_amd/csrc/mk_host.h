@@ -22,8 +22,8 @@ struct HeadParams;
 int launch_embed(const uint16_t* emb, int V, int d, const int32_t* tokens, int T, float* h, uint32_t* fault,
                  hipStream_t s);
 int launch_head(const void* head_packed, int V, int d, const float* gamma, float eps, const float* h, int T,
-                float* logits, float* best_val, int32_t* best_idx, uint32_t* counter, int32_t* tokens,
-                const int32_t* next_drafts, int32_t* argmax, int32_t* committed, int32_t* kv_len,
+                float* logits, float* best_val, int32_t* best_idx, uint32_t* counter, uint32_t* tickets,
+                int32_t* tokens, const int32_t* next_drafts, int32_t* argmax, int32_t* committed, int32_t* kv_len,
                 const uint8_t* dummy, const uint32_t* fault, int nwg, hipStream_t s);
 int head_kernel_occupancy(int* wgs_per_cu);
 
