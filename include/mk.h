@@ -119,7 +119,7 @@ typedef struct mk_device_info {
 /* Packed tensors (pre-tiled for coalesced streaming; opaque layout). */
 typedef enum mk_tensor {
   MK_T_WQ = 0, MK_T_WDKV = 1, MK_T_WUK = 2, MK_T_WUV = 3, MK_T_WO = 4, MK_T_WR = 5,
-  MK_T_EXPERT = 6            /* W1, W3, W2 (and fp8 scales) of one expert in one block */
+  MK_T_EXPERT = 6            /* W1, W3, W2 (and fp8 or MXFP4 scales) of one expert in one block */
 } mk_tensor;
 
 /* Packed layer weights (device pointers). */
