@@ -145,10 +145,18 @@ class DeviceLayer:
 
 
 def kv_cache(s: LayerShape, seed: int = 0, layer: int = 0, device: int = 0, capacity: int | None = None):
-    """KV rows [capacity][kvw]; rows [0, L) drawn as synth.recipe.kv_prefill_host draws them."""
+    """KV rows [capacity][kvw] (fp8 rows: uint8 [capacity][row bytes]); rows [0, L)
+    drawn as synth.recipe.kv_prefill_host draws them."""
     cap = capacity or s.capacity
     n = s.L * s.kvw
     st = synth.stream_id("kv_prefill", layer)
+    if s.kv_fmt == "fp8row":
+        rb = recipe.kv_row_bytes(s)
+        kv = torch.zeros((cap, rb), dtype=torch.uint8, device=_dev(device))
+        if s.L:
+            synth.dev_fp8row_kv(kv.data_ptr(), s.L, s.kvw, rb, seed, st, synth.stream_id("kv_scale", layer),
+                                recipe.ACT_SIGMA)
+        return kv
     if s.kv_fmt == "f32":
         kv = torch.zeros((cap, s.kvw), dtype=torch.float32, device=_dev(device))
         if n:

@@ -21,7 +21,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB = os.path.join(_HERE, "liborc.so")
 
 ORC_F32, ORC_BF16, ORC_FP8B128, ORC_MXFP4 = 0, 1, 2, 3
-_FMT = {"f32": ORC_F32, "bf16": ORC_BF16, "fp8": ORC_FP8B128, "mxfp4": ORC_MXFP4}
+ORC_FP8ROW = 4
+_FMT = {"f32": ORC_F32, "bf16": ORC_BF16, "fp8": ORC_FP8B128, "mxfp4": ORC_MXFP4, "fp8row": ORC_FP8ROW}
 
 _vp = ctypes.c_void_p
 _i = ctypes.c_int
@@ -86,6 +87,14 @@ def lib():
         L.orc_e2m1_to_f32.argtypes = [ctypes.c_uint8]
         L.orc_e8m0_to_f32.restype = ctypes.c_float
         L.orc_e8m0_to_f32.argtypes = [ctypes.c_uint8]
+        L.orc_f32_to_e4m3.restype = ctypes.c_uint8
+        L.orc_f32_to_e4m3.argtypes = [ctypes.c_float]
+        L.orc_fp8_row_scale.restype = ctypes.c_float
+        L.orc_fp8_row_scale.argtypes = [_vp, _i]
+        L.orc_kv_row_bytes.restype = _i
+        L.orc_kv_row_bytes.argtypes = [_i, _i]
+        L.orc_kv_decode_rows.restype = _i
+        L.orc_kv_decode_rows.argtypes = [_vp, _i, _i, _i, _vp]
         _lib = L
     return _lib
 
@@ -267,3 +276,24 @@ def greedy_accept(tokens, argmax):
 
 def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
     return (np.asarray(bits, dtype=np.uint32) << 16).view(np.float32)
+
+
+def kv_row_bytes(fmt: str, kvw: int) -> int:
+    return int(lib().orc_kv_row_bytes(_FMT[fmt], kvw))
+
+
+def kv_decode(kv: np.ndarray, fmt: str, kvw: int, nrows: int) -> np.ndarray:
+    """Rows [0, nrows) of a cache buffer (any dtype, the format's row layout) as fp32 [nrows][kvw]."""
+    buf = np.ascontiguousarray(kv)
+    out = np.empty((nrows, kvw), np.float32)
+    _chk(lib().orc_kv_decode_rows(_p(buf), _FMT[fmt], kvw, nrows, _p(out)), "orc_kv_decode_rows")
+    return out
+
+
+def f32_to_e4m3(x: float) -> int:
+    return int(lib().orc_f32_to_e4m3(float(x)))
+
+
+def fp8_row_scale(row: np.ndarray) -> float:
+    r = np.ascontiguousarray(row, dtype=np.float32)
+    return float(lib().orc_fp8_row_scale(_p(r), len(r)))

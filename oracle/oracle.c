@@ -37,6 +37,51 @@ float orc_e4m3_to_f32(uint8_t q) {
   return s ? -v : v;
 }
 
+/* OCP E4M3 ("FN") encoding, round to nearest with ties to even, saturating at
+ * +-448 (the largest finite value; S.1111.111 is NaN); NaN -> 0x7F.  Written
+ * from the definition: a normal value is (1 + m/8) 2^(e-7), e = 1..15, a
+ * subnormal m 2^-9. */
+uint8_t orc_f32_to_e4m3(float x) {
+  if (isnan(x)) return 0x7F;
+  const uint8_t sign = signbit(x) ? 0x80 : 0x00;
+  double a = fabs((double)x);
+  if (a >= 448.0) return sign | 0x7E;
+  if (a < ldexp(1.0, -6)) {                       /* subnormal range: steps of 2^-9 */
+    const int m = (int)rint(a * 512.0);           /* m = 8 is the smallest normal, code 0x08 */
+    return sign | (uint8_t)m;
+  }
+  int k;
+  frexp(a, &k);                                   /* a = f 2^k, f in [0.5, 1) */
+  int E = k - 1;                                  /* a in [2^E, 2^(E+1)) */
+  int m = (int)rint((a / ldexp(1.0, E) - 1.0) * 8.0);
+  if (m == 8) {
+    m = 0;
+    ++E;
+  }
+  if (E + 7 > 15 || (E + 7 == 15 && m == 7)) return sign | 0x7E;
+  return sign | (uint8_t)(((E + 7) << 3) | m);
+}
+
+/* Scale of one fp8 KV row: the smallest power of two 2^e with amax <= 448 2^e
+ * (1 when the row is all zeros), so that row / scale fits E4M3 without
+ * saturating and code * scale is exact in fp32 (and in bf16). */
+float orc_fp8_row_scale(const float* row, int n) {
+  double amax = 0.0;
+  for (int i = 0; i < n; ++i) amax = fmax(amax, fabs((double)row[i]));
+  if (amax == 0.0) return 1.0f;
+  int e = ilogb(amax) - 8;
+  while (amax > ldexp(448.0, e)) ++e;
+  while (amax <= ldexp(448.0, e - 1)) --e;
+  return ldexpf(1.0f, e);
+}
+
+int orc_kv_row_bytes(int kv_fmt, int kvw) {
+  if (kv_fmt == ORC_F32) return 4 * kvw;
+  if (kv_fmt == ORC_BF16) return 2 * kvw;
+  if (kv_fmt == ORC_FP8ROW) return (kvw + 4 + 15) / 16 * 16;
+  return -1;
+}
+
 /* OCP MX E2M1: sign, 2 exponent bits (bias 1), 1 mantissa bit; exponent field
  * 0 is subnormal (m * 0.5).  Magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6. */
 float orc_e2m1_to_f32(uint8_t code) {
@@ -167,15 +212,47 @@ static void rope64(double* v, int d_r, long pos, double base) {
   }
 }
 
-static inline float kv_get(const void* kv, int fmt, long idx) {
-  return fmt == ORC_F32 ? ((const float*)kv)[idx] : orc_bf16_to_f32(((const uint16_t*)kv)[idx]);
+/* element m of cache row `row` (kvw elements per row) */
+static inline float kv_get(const void* kv, int fmt, int kvw, long row, int m) {
+  if (fmt == ORC_F32) return ((const float*)kv)[row * kvw + m];
+  if (fmt == ORC_BF16) return orc_bf16_to_f32(((const uint16_t*)kv)[row * kvw + m]);
+  const uint8_t* r = (const uint8_t*)kv + row * orc_kv_row_bytes(fmt, kvw);
+  float sc;
+  memcpy(&sc, r + kvw, 4);
+  return orc_e4m3_to_f32(r[m]) * sc;
 }
-static inline void kv_put(void* kv, int fmt, long idx, float v) {
-  if (fmt == ORC_F32) ((float*)kv)[idx] = v;
-  else ((uint16_t*)kv)[idx] = orc_f32_to_bf16(v);
+/* stores one row (rounded to the cache's format: per element for fp32 / bf16,
+ * with the row's scale for fp8) */
+static void kv_put_row(void* kv, int fmt, int kvw, long row, const float* v) {
+  if (fmt == ORC_F32) {
+    memcpy((float*)kv + row * kvw, v, sizeof(float) * kvw);
+  } else if (fmt == ORC_BF16) {
+    for (int m = 0; m < kvw; ++m) ((uint16_t*)kv)[row * kvw + m] = orc_f32_to_bf16(v[m]);
+  } else {
+    uint8_t* r = (uint8_t*)kv + row * orc_kv_row_bytes(fmt, kvw);
+    const float sc = orc_fp8_row_scale(v, kvw);
+    for (int m = 0; m < kvw; ++m) r[m] = orc_f32_to_e4m3(v[m] / sc);
+    memcpy(r + kvw, &sc, 4);
+    memset(r + kvw + 4, 0, (size_t)(orc_kv_row_bytes(fmt, kvw) - kvw - 4));
+  }
 }
-static inline float storage_round(int fmt, float v) {
-  return fmt == ORC_F32 ? v : orc_bf16_to_f32(orc_f32_to_bf16(v));
+/* a row as the cache would give it back after storing it */
+static void kv_round_row(int fmt, int kvw, const float* v, float* out) {
+  if (fmt == ORC_F32) {
+    memcpy(out, v, sizeof(float) * kvw);
+  } else if (fmt == ORC_BF16) {
+    for (int m = 0; m < kvw; ++m) out[m] = orc_bf16_to_f32(orc_f32_to_bf16(v[m]));
+  } else {
+    const float sc = orc_fp8_row_scale(v, kvw);
+    for (int m = 0; m < kvw; ++m) out[m] = orc_e4m3_to_f32(orc_f32_to_e4m3(v[m] / sc)) * sc;
+  }
+}
+
+int orc_kv_decode_rows(const void* kv, int kv_fmt, int kvw, int nrows, float* out) {
+  if (!kv || !out || kvw <= 0 || nrows < 0 || orc_kv_row_bytes(kv_fmt, kvw) < 0) return -1;
+  for (long j = 0; j < nrows; ++j)
+    for (int m = 0; m < kvw; ++m) out[j * kvw + m] = kv_get(kv, kv_fmt, kvw, j, m);
+  return 0;
 }
 
 static float silu(float u) { return u / (1.0f + expf(-u)); }
@@ -186,6 +263,7 @@ static int check_cfg(const orc_cfg* c, int T) {
       (c->d_r & 1) || c->E <= 0 || c->top_k <= 0 || c->top_k > c->E || c->f <= 0 || c->n_shared < 0)
     return -1;
   if (c->exp_fmt == ORC_MXFP4 && (c->d % 32 || c->f % 32)) return -1;
+  if (c->kv_fmt != ORC_F32 && c->kv_fmt != ORC_BF16 && c->kv_fmt != ORC_FP8ROW) return -1;
   return 0;
 }
 
@@ -215,7 +293,7 @@ int orc_attn_block(const orc_cfg* c, const orc_weights* w, const float* H, int T
     matvec(&WD, x, ckv);
     for (int h = 0; h < nh; ++h) rope(q + (long)h * qw + dh, dr, pos, c->rope_base);
     rope(ckv + dc, dr, pos, c->rope_base);
-    for (int m = 0; m < kvw; ++m) kv_put(kv, c->kv_fmt, pos * kvw + m, ckv[m]);
+    kv_put_row(kv, c->kv_fmt, kvw, pos, ckv);
 
     /* absorbed query: qa_h[m] = sum_e W_UK[h][e][m] q^C_h[e] */
     for (int h = 0; h < nh; ++h) {
@@ -240,8 +318,8 @@ int orc_attn_block(const orc_cfg* c, const orc_weights* w, const float* H, int T
       float mx = -INFINITY;
       for (long j = 0; j <= pos; ++j) {
         float acc = 0.0f;
-        for (int m = 0; m < dc; ++m) acc += qah[m] * kv_get(kv, c->kv_fmt, j * kvw + m);
-        for (int r = 0; r < dr; ++r) acc += qr[r] * kv_get(kv, c->kv_fmt, j * kvw + dc + r);
+        for (int m = 0; m < dc; ++m) acc += qah[m] * kv_get(kv, c->kv_fmt, kvw, j, m);
+        for (int r = 0; r < dr; ++r) acc += qr[r] * kv_get(kv, c->kv_fmt, kvw, j, dc + r);
         sh[j] = acc * scale;
         if (sh[j] > mx) mx = sh[j];
       }
@@ -251,7 +329,7 @@ int orc_attn_block(const orc_cfg* c, const orc_weights* w, const float* H, int T
       for (int m = 0; m < dc; ++m) zh[m] = 0.0f;
       for (long j = 0; j <= pos; ++j) {
         float p = sh[j] / sum;
-        for (int m = 0; m < dc; ++m) zh[m] += p * kv_get(kv, c->kv_fmt, j * kvw + m);
+        for (int m = 0; m < dc; ++m) zh[m] += p * kv_get(kv, c->kv_fmt, kvw, j, m);
       }
       /* value up-projection: o_h[e] = sum_m W_UV[h][e][m] z_h[m] */
       for (int e = 0; e < dh; ++e) {
@@ -432,10 +510,13 @@ int orc_layer_step_f64(const orc_cfg* c, const orc_weights* w, const float* H, i
 
   /* all rows of the cache as double: prefill rows as stored, new rows rounded to storage */
   double* rows = malloc(sizeof(double) * npos * kvw);
-  for (long j = 0; j < (long)L * kvw; ++j) rows[j] = (double)kv_get(kv, c->kv_fmt, j);
+  for (long j = 0; j < L; ++j)
+    for (int m = 0; m < kvw; ++m) rows[j * kvw + m] = (double)kv_get(kv, c->kv_fmt, kvw, j, m);
   double* x = malloc(sizeof(double) * d);
   double* q = malloc(sizeof(double) * (long)T * nh * qw);
   double* ckv = malloc(sizeof(double) * kvw);
+  float* rowf = malloc(sizeof(float) * kvw);
+  float* rowr = malloc(sizeof(float) * kvw);
   for (int i = 0; i < T; ++i) {
     const long pos = (long)L + i;
     rmsnorm64(H + (long)i * d, w->gamma1, d, (double)c->eps, x);
@@ -443,10 +524,11 @@ int orc_layer_step_f64(const orc_cfg* c, const orc_weights* w, const float* H, i
     matvec64(&WD, x, ckv);
     for (int h = 0; h < nh; ++h) rope64(q + (long)i * nh * qw + (long)h * qw + dh, dr, pos, c->rope_base);
     rope64(ckv + dc, dr, pos, c->rope_base);
+    for (int m = 0; m < kvw; ++m) rowf[m] = (float)ckv[m];
+    kv_round_row(c->kv_fmt, kvw, rowf, rowr);
     for (int m = 0; m < kvw; ++m) {
-      double st = (double)storage_round(c->kv_fmt, (float)ckv[m]);
-      rows[pos * kvw + m] = st;
-      if (kv_new_f64) kv_new_f64[(long)i * kvw + m] = st;
+      rows[pos * kvw + m] = (double)rowr[m];
+      if (kv_new_f64) kv_new_f64[(long)i * kvw + m] = (double)rowr[m];
     }
   }
   /* un-absorbed keys/values per head: kc[h][j][e] = W_UK[h] c_j, v[h][j][e] = W_UV[h] c_j */
@@ -544,7 +626,7 @@ int orc_layer_step_f64(const orc_cfg* c, const orc_weights* w, const float* H, i
       for (int r = 0; r < d; ++r) oi[r] += g * y[r];
     }
   }
-  free(rows); free(x); free(q); free(ckv); free(kc); free(vv); free(o); free(att); free(hp);
+  free(rows); free(x); free(q); free(ckv); free(rowf); free(rowr); free(kc); free(vv); free(o); free(att); free(hp);
   free(xp); free(lg); free(a); free(b); free(y); free(sel);
   return rc;
 }

@@ -30,7 +30,9 @@
  *  - OCP Microscaling Formats (MX) specification v1.0 for MXFP4 expert weights
  *    (E2M1 elements, E8M0 block scales over 32 elements): "DeepSeek-V4.1-Flash
  *    breaks 1,000 tokens per second for one user", section "Appendix: method",
- *    names MXFP4 expert weights as the serving format.
+ *    names MXFP4 expert weights as the serving format, with an fp8 (E4M3) KV
+ *    cache; the page gives no scale layout for the cache, and the reading taken
+ *    is one power-of-two fp32 scale per cache row (orc_fp8_row_scale).
  *
  * Readings where the pages are silent (each listed in the design notes):
  * eps = 1e-6; softmax scale 1/sqrt(d_h + d_r); RoPE base 10000 with the angle
@@ -52,7 +54,7 @@
 extern "C" {
 #endif
 
-enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_FP8B128 = 2, ORC_MXFP4 = 3 };
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_FP8B128 = 2, ORC_MXFP4 = 3, ORC_FP8ROW = 4 };
 
 typedef struct orc_cfg {
   int d;          /* hidden size */
@@ -63,7 +65,7 @@ typedef struct orc_cfg {
   int f;          /* expert FFN width */
   int attn_fmt;   /* ORC_F32 | ORC_BF16: W_Q, W_DKV, W_UK, W_UV, W_O, W_R */
   int exp_fmt;    /* ORC_F32 | ORC_BF16 | ORC_FP8B128 | ORC_MXFP4: W1, W3, W2 */
-  int kv_fmt;     /* ORC_F32 | ORC_BF16 */
+  int kv_fmt;     /* ORC_F32 | ORC_BF16 | ORC_FP8ROW (see orc_kv_row_bytes) */
   float eps;      /* RMSNorm epsilon */
   double rope_base;
 } orc_cfg;
@@ -120,8 +122,17 @@ typedef struct orc_moe_taps {
   float* y_shared; /* [T][d]        sum of shared-expert outputs     */
 } orc_moe_taps;
 
+/* KV cache rows.  ORC_F32 / ORC_BF16: d_c+d_r elements.  ORC_FP8ROW: the row's
+ * d_c+d_r E4M3 codes (orc_f32_to_e4m3 of value / scale), then its scale as an
+ * fp32 (orc_fp8_row_scale, a power of two), zero bytes up to a multiple of 16;
+ * element value = E4M3(code) * scale, exact in fp32.  Bytes per row (-1 for an
+ * unknown format): */
+int orc_kv_row_bytes(int kv_fmt, int kvw);
+/* Rows [0, nrows) of a cache as fp32 values [nrows][kvw]. */
+int orc_kv_decode_rows(const void* kv, int kv_fmt, int kvw, int nrows, float* out);
+
 /* Attention block: Hp = H + W_O(attention).  Writes KV rows [L, L+T) of `kv`
- * ([capacity][d_c+d_r] in kv_fmt) and reads rows [0, L+i] for verify row i.
+ * ([capacity] rows in kv_fmt) and reads rows [0, L+i] for verify row i.
  * Returns 0, or a negative code on bad arguments. */
 int orc_attn_block(const orc_cfg* c, const orc_weights* w, const float* H, int T,
                    void* kv, int L, float* Hp, const orc_attn_taps* taps);
@@ -163,6 +174,8 @@ int orc_greedy_accept(const int32_t* tokens, const int32_t* a, int T, int32_t* c
 float orc_bf16_to_f32(uint16_t b);
 uint16_t orc_f32_to_bf16(float x);
 float orc_e4m3_to_f32(uint8_t q);
+uint8_t orc_f32_to_e4m3(float x);      /* RNE, saturating at +-448, NaN -> 0x7F */
+float orc_fp8_row_scale(const float* row, int n);   /* smallest 2^e >= amax / 448; 1 for a zero row */
 float orc_e2m1_to_f32(uint8_t code);   /* low 4 bits: S.EE.M, bias 1 */
 float orc_e8m0_to_f32(uint8_t e);      /* 2^(e-127); 255 is NaN */
 

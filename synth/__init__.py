@@ -63,6 +63,7 @@ def _host_lib():
         lib.mks_host_e2m1_encode.restype = ctypes.c_uint8
         lib.mks_host_e2m1_encode.argtypes = [_f32]
         lib.mks_host_mxfp4_blocks.argtypes = [_vp, _vp, _i64, _i64, _u64, _u64, _f32]
+        lib.mks_host_fp8row_kv.argtypes = [_vp, _i64, _i64, _i64, _u64, _u64, _u64, _f32]
         lib.mks_host_bf16_encode.restype = ctypes.c_uint16
         lib.mks_host_bf16_encode.argtypes = [_f32]
         _host = lib
@@ -80,8 +81,9 @@ def _dev_lib():
         lib.mks_dev_normal_bf16.argtypes = [_vp, _u64, _u64, _u64, _u64, _f32, _f32, _vp]
         lib.mks_dev_fp8_blocks.argtypes = [_vp, _vp, _i64, _i64, _u64, _u64, _f32, _vp]
         lib.mks_dev_mxfp4_blocks.argtypes = [_vp, _vp, _i64, _i64, _u64, _u64, _f32, _vp]
+        lib.mks_dev_fp8row_kv.argtypes = [_vp, _i64, _i64, _i64, _u64, _u64, _u64, _f32, _vp]
         for f in (lib.mks_dev_raw_fill, lib.mks_dev_normal_f32, lib.mks_dev_normal_bf16,
-                  lib.mks_dev_fp8_blocks, lib.mks_dev_mxfp4_blocks):
+                  lib.mks_dev_fp8_blocks, lib.mks_dev_mxfp4_blocks, lib.mks_dev_fp8row_kv):
             f.restype = ctypes.c_int
         _dev = lib
     return _dev
@@ -97,7 +99,7 @@ def sigma_c(sigma: float) -> float:
 TAGS = {
     "H": 1, "kv_prefill": 2, "gamma1": 3, "gamma2": 4, "wq": 5, "wdkv": 6, "wuk": 7,
     "wuv": 8, "wo": 9, "wr": 10, "w1": 11, "w3": 12, "w2": 13, "emb": 14, "head": 15,
-    "gamma_f": 16, "tokens": 17, "hot_perm": 18,
+    "gamma_f": 16, "tokens": 17, "hot_perm": 18, "kv_scale": 19,
 }
 
 
@@ -149,6 +151,16 @@ def mxfp4_blocks(R: int, K: int, seed: int, stream: int, sigma: float):
     scales = np.empty((R, K // 32), dtype=np.uint8)
     _host_lib().mks_host_mxfp4_blocks(_ptr(codes), _ptr(scales), R, K, seed, stream, sigma_c(sigma))
     return codes, scales
+
+
+def fp8row_kv(rows: int, kvw: int, row_bytes: int, seed: int, stream: int, scale_stream: int,
+              sigma: float) -> np.ndarray:
+    """uint8 [rows][row_bytes]: per row kvw E4M3 codes, the fp32 scale, zero padding."""
+    out = np.empty((rows, row_bytes), dtype=np.uint8)
+    if rows:
+        _host_lib().mks_host_fp8row_kv(_ptr(out), rows, kvw, row_bytes, seed, stream, scale_stream,
+                                       sigma_c(sigma))
+    return out
 
 
 def e2m1_encode(x: float) -> int:
@@ -203,6 +215,12 @@ def dev_mxfp4_blocks(codes_ptr: int, scales_ptr: int, R: int, K: int, seed: int,
                      sigma: float, hip_stream: int = 0):
     _chk(_dev_lib().mks_dev_mxfp4_blocks(codes_ptr, scales_ptr, R, K, seed, stream, sigma_c(sigma),
                                          hip_stream), "mks_dev_mxfp4_blocks")
+
+
+def dev_fp8row_kv(dst_ptr: int, rows: int, kvw: int, row_bytes: int, seed: int, stream: int,
+                  scale_stream: int, sigma: float, hip_stream: int = 0):
+    _chk(_dev_lib().mks_dev_fp8row_kv(dst_ptr, rows, kvw, row_bytes, seed, stream, scale_stream,
+                                      sigma_c(sigma), hip_stream), "mks_dev_fp8row_kv")
 
 
 def dev_fp8_blocks(codes_ptr: int, scales_ptr: int, R: int, K: int, seed: int, stream: int,

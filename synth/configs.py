@@ -27,7 +27,7 @@ class LayerShape:
     attn_fmt: str     # "f32" | "bf16"  (W_Q, W_DKV, W_UK, W_UV, W_O, W_R)
     exp_fmt: str      # "f32" | "bf16" | "fp8" | "mxfp4"  (W1, W3, W2; fp8 = E4M3 + fp32 128x128 scales,
                       #   mxfp4 = E2M1 + an E8M0 scale per 32 elements of a row)
-    kv_fmt: str       # "f32" | "bf16"
+    kv_fmt: str       # "f32" | "bf16" | "fp8row" (E4M3 codes + an fp32 power-of-two scale per row)
     routing: str = "uniform"   # "uniform" | "skew" (hot experts get a router bias)
     n_layers: int = 1
     V: int = 0                 # vocabulary (stacks only)

@@ -16,7 +16,7 @@ import os
 
 import numpy as np
 
-from . import fp8_blocks, mxfp4_blocks, normal_bf16, normal_f32, permutation, stream_id, uniform_ints
+from . import fp8_blocks, fp8row_kv, mxfp4_blocks, normal_bf16, normal_f32, permutation, stream_id, uniform_ints
 from .configs import HOT_FRACTION, LayerShape
 
 W_SIGMA = 0.02
@@ -114,10 +114,25 @@ def hidden_host(s: LayerShape, seed: int = 0, layer: int = 0, step: int = 0) -> 
     return normal_f32((s.T, s.d), seed, stream_id("H", layer, step), ACT_SIGMA)
 
 
+def kv_row_bytes(s: LayerShape) -> int:
+    """Bytes of one cache row: kvw elements (fp32 / bf16), or for fp8 rows kvw
+    E4M3 codes and an fp32 scale, padded to a multiple of 16 bytes."""
+    if s.kv_fmt == "f32":
+        return 4 * s.kvw
+    if s.kv_fmt == "bf16":
+        return 2 * s.kvw
+    return (s.kvw + 4 + 15) // 16 * 16
+
+
 def kv_prefill_host(s: LayerShape, seed: int = 0, layer: int = 0) -> np.ndarray:
     """Cache of `capacity` rows; rows [0, L) hold N(0,1) values in the cache format,
-    rows [L, capacity) are zero."""
+    rows [L, capacity) are zero.  fp8 rows are uint8 [capacity][kv_row_bytes]."""
     cap = s.capacity
+    if s.kv_fmt == "fp8row":
+        kv = np.zeros((cap, kv_row_bytes(s)), dtype=np.uint8)
+        kv[: s.L] = fp8row_kv(s.L, s.kvw, kv_row_bytes(s), seed, stream_id("kv_prefill", layer),
+                              stream_id("kv_scale", layer), ACT_SIGMA)
+        return kv
     if s.kv_fmt == "f32":
         kv = np.zeros((cap, s.kvw), dtype=np.float32)
         kv[: s.L] = normal_f32((s.L, s.kvw), seed, stream_id("kv_prefill", layer), ACT_SIGMA)

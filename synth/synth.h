@@ -42,6 +42,13 @@
  *                division by a power of two).  Codes are packed two per byte,
  *                element 2j in the low nibble of byte j: [R][K/2]; scale codes
  *                (E8M0) [R][K/32].
+ *   fp8 KV rows  `rows` rows of `row_bytes` bytes (row_bytes >= kvw + 4);
+ *                row r holds kvw E4M3 codes, then its fp32 scale, then zero
+ *                bytes.  The scale is 2^e_r with e_r = -6 + (raw(s, u, r) mod 3)
+ *                (u the scale stream), and code m is e4m3(normal(r*kvw+m) *
+ *                2^-e_r) (an exact scaling by a power of two), so the decoded
+ *                row approximates the same N(0, sigma) draws as the f32 / bf16
+ *                caches.  With sigma = 1 no code saturates (|normal| < 3.47).
  */
 #ifndef MK_SYNTH_H
 #define MK_SYNTH_H
@@ -59,6 +66,8 @@ void mks_host_normal_bf16(uint16_t* dst, uint64_t n, uint64_t seed, uint64_t str
                           uint64_t offset, float c, float mean);
 void mks_host_fp8_blocks(uint8_t* codes, float* scales, int64_t R, int64_t K,
                          uint64_t seed, uint64_t stream, float c);
+void mks_host_fp8row_kv(uint8_t* dst, int64_t rows, int64_t kvw, int64_t row_bytes,
+                        uint64_t seed, uint64_t stream, uint64_t scale_stream, float c);
 void mks_host_mxfp4_blocks(uint8_t* codes, uint8_t* scales, int64_t R, int64_t K,
                            uint64_t seed, uint64_t stream, float c);
 uint8_t mks_host_e4m3_encode(float x);
@@ -75,6 +84,8 @@ int mks_dev_fp8_blocks(uint8_t* codes, float* scales, int64_t R, int64_t K,
                        uint64_t seed, uint64_t stream, float c, void* stream_handle);
 int mks_dev_raw_fill(uint64_t* dst, uint64_t n, uint64_t seed, uint64_t stream,
                      uint64_t offset, void* stream_handle);
+int mks_dev_fp8row_kv(uint8_t* dst, int64_t rows, int64_t kvw, int64_t row_bytes,
+                      uint64_t seed, uint64_t stream, uint64_t scale_stream, float c, void* hip_stream);
 int mks_dev_mxfp4_blocks(uint8_t* codes, uint8_t* scales, int64_t R, int64_t K,
                          uint64_t seed, uint64_t stream, float c, void* stream_handle);
 

@@ -113,6 +113,25 @@ __global__ __launch_bounds__(256) void k_fp8_blocks(uint8_t* codes, float* scale
   }
 }
 
+// One workgroup per KV row (grid-stride over rows).
+__global__ __launch_bounds__(256) void k_fp8row_kv(uint8_t* dst, int64_t rows, int64_t kvw, int64_t row_bytes,
+                                                   uint64_t key, uint64_t skey, float c) {
+  for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+    uint8_t* row = dst + r * row_bytes;
+    const int e = -6 + (int)(mix64(skey + ((uint64_t)r + 1) * GAMMA) % 3u);
+    for (int64_t m = threadIdx.x; m < row_bytes; m += blockDim.x) {
+      uint8_t b = 0;
+      if (m < kvw) {
+        b = e4m3_encode(ldexpf(normal_at(key, (uint64_t)(r * kvw + m), c, 0.0f), -e));
+      } else if (m < kvw + 4) {
+        const uint32_t sb = __float_as_uint(ldexpf(1.0f, e));
+        b = (uint8_t)(sb >> (8 * (m - kvw)));
+      }
+      row[m] = b;
+    }
+  }
+}
+
 // One thread per group of 32 consecutive elements of a row.
 __global__ __launch_bounds__(256) void k_mxfp4_blocks(uint8_t* codes, uint8_t* scales, int64_t R, int64_t K,
                                                       uint64_t key, float c) {
@@ -173,6 +192,14 @@ extern "C" int mks_dev_fp8_blocks(uint8_t* codes, float* scales, int64_t R, int6
   int64_t nbr = (R + 127) / 128, nbk = (K + 127) / 128;
   hipLaunchKernelGGL(k_fp8_blocks, dim3((unsigned)(nbr * nbk)), dim3(256), 0, (hipStream_t)sh,
                      codes, scales, R, K, nbk, key_of(seed, stream), c);
+  return (int)hipGetLastError();
+}
+extern "C" int mks_dev_fp8row_kv(uint8_t* dst, int64_t rows, int64_t kvw, int64_t row_bytes,
+                                 uint64_t seed, uint64_t stream, uint64_t scale_stream, float c, void* sh) {
+  if (rows <= 0) return 0;
+  if (kvw <= 0 || row_bytes < kvw + 4) return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_fp8row_kv, dim3((unsigned)(rows < 65536 ? rows : 65536)), dim3(256), 0, (hipStream_t)sh,
+                     dst, rows, kvw, row_bytes, key_of(seed, stream), key_of(seed, scale_stream), c);
   return (int)hipGetLastError();
 }
 extern "C" int mks_dev_mxfp4_blocks(uint8_t* codes, uint8_t* scales, int64_t R, int64_t K,

@@ -100,6 +100,21 @@ void mks_host_fp8_blocks(uint8_t* codes, float* scales, int64_t R, int64_t K,
   }
 }
 
+void mks_host_fp8row_kv(uint8_t* dst, int64_t rows, int64_t kvw, int64_t row_bytes,
+                        uint64_t seed, uint64_t stream, uint64_t scale_stream, float c) {
+  uint64_t k = key_of(seed, stream), ks = key_of(seed, scale_stream);
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r) {
+    uint8_t* row = dst + r * row_bytes;
+    const int e = -6 + (int)(mix64(ks + ((uint64_t)r + 1) * GAMMA) % 3u);
+    for (int64_t m = 0; m < kvw; ++m)
+      row[m] = mks_host_e4m3_encode(ldexpf(normal_at(k, (uint64_t)(r * kvw + m), c, 0.0f), -e));
+    const float sc = ldexpf(1.0f, e);
+    memcpy(row + kvw, &sc, 4);
+    memset(row + kvw + 4, 0, (size_t)(row_bytes - kvw - 4));
+  }
+}
+
 uint8_t mks_host_e2m1_encode(float x) {
   static const float mid[7] = {0.25f, 0.75f, 1.25f, 1.75f, 2.5f, 3.5f, 5.0f};
   uint32_t u; memcpy(&u, &x, 4);

@@ -25,7 +25,7 @@ import oracle
 from synth import recipe
 
 TAU_SEL = 1e-3
-TOL = {"f32": 1e-4, "bf16": 2e-2, "fp8": 5e-2, "mxfp4": 5e-2}
+TOL = {"f32": 1e-4, "bf16": 2e-2, "fp8": 5e-2, "mxfp4": 5e-2, "fp8row": 5e-2}
 
 
 def _loosest(*fmts):
@@ -47,8 +47,35 @@ def normwise(a, ref):
     return float((np.abs(a - ref).max(axis=1) / den).max())
 
 
-def kv_to_f32(kv_np, fmt):
+def kv_to_f32(kv_np, fmt, kvw=None):
+    if fmt == "fp8row":
+        return oracle.kv_decode(kv_np, fmt, kvw, kv_np.shape[0])
     return oracle.bf16_to_f32(kv_np.view(np.uint16)) if fmt == "bf16" else kv_np.astype(np.float32)
+
+
+def fp8row_kv_check(g_codes, o_codes, kvw):
+    """New fp8 cache rows of the GPU against the oracle's.  The two sides quantize
+    rows whose values differ by bf16 rounding of the activations, so a code may
+    land one E4M3 step away and a row's power-of-two scale may differ by a factor
+    of two where its maximum sits at a boundary.  Asserts exactly that: every
+    decoded element within one code step of the oracle's at the larger of the
+    two scales, plus the activation tolerance.  Returns the largest distance in
+    code steps."""
+    g = oracle.kv_decode(g_codes, "fp8row", kvw, g_codes.shape[0]).astype(np.float64)
+    o = oracle.kv_decode(o_codes, "fp8row", kvw, o_codes.shape[0]).astype(np.float64)
+    gs = g_codes[:, kvw:kvw + 4].copy().view(np.float32).astype(np.float64)[:, 0]
+    os_ = o_codes[:, kvw:kvw + 4].copy().view(np.float32).astype(np.float64)[:, 0]
+    ratio = gs / os_
+    assert np.all((ratio == 1.0) | (ratio == 2.0) | (ratio == 0.5)), ratio
+    assert np.all(g_codes[:, kvw + 4:] == 0) and np.all(o_codes[:, kvw + 4:] == 0)
+    sc = np.maximum(gs, os_)[:, None]
+    # E4M3 step at magnitude a (in units of the row scale): 2^(floor(log2 a) - 3), 2^-9 below 2^-6
+    a = np.maximum(np.abs(o), np.abs(g)) / sc
+    step = np.where(a < 2.0 ** -6, 2.0 ** -9, 2.0 ** (np.floor(np.log2(np.maximum(a, 2.0 ** -6))) - 3))
+    dist = np.abs(g - o) / (step * sc)
+    act = TOL["bf16"] * np.abs(o).max(axis=1, keepdims=True)
+    assert np.all(np.abs(g - o) <= step * sc + act), float(dist.max())
+    return float(dist.max())
 
 
 def gpu_step(dl, s, H_dev, kv_dev, L, T=None):
@@ -69,7 +96,8 @@ def gpu_step(dl, s, H_dev, kv_dev, L, T=None):
         dl.layer.debug_tap(tap, buf)
         taps[name] = oracle.bf16_to_f32(buf) if dt == np.uint16 else buf
     kvn = kv_dev[L:L + T].cpu().numpy()
-    return out.cpu().numpy(), kv_to_f32(kvn, s.kv_fmt), taps
+    taps["kv_raw"] = kvn
+    return out.cpu().numpy(), kv_to_f32(kvn, s.kv_fmt, s.kvw), taps
 
 
 def oracle_step(s, seed, layer, H, L, kv_host=None, force_sel=None, full_weights=None, base_weights=None,
@@ -83,7 +111,8 @@ def oracle_step(s, seed, layer, H, L, kv_host=None, force_sel=None, full_weights
     else:
         out, taps, w = oracle.layer_step_lazy(s, seed, layer, H, kv, L, base_weights=base_weights,
                                               force_sel=force_sel, expert_fn=expert_fn)
-    return out, kv_to_f32(kv[L:L + H.shape[0]], s.kv_fmt), taps, w
+    taps["kv_raw"] = kv[L:L + H.shape[0]].copy()
+    return out, kv_to_f32(kv[L:L + H.shape[0]], s.kv_fmt, s.kvw), taps, w
 
 
 def compare_selection(s, gpu_sel, ora_logits, ora_sel):
@@ -127,6 +156,13 @@ def check_layer(s, seed, layer, g_out, g_kv, g_taps, H, L, kv_host=None, full_we
     }
     if report is not None:
         report.update(errs)
-    for k in ("attn_branch", "moe_branch", "out", "kv_new"):
+    if s.kv_fmt == "fp8row":
+        # rows are compared code by code (fp8row_kv_check) where the GPU's raw rows are at hand
+        if "kv_raw" in g_taps:
+            errs["kv_new_steps"] = fp8row_kv_check(g_taps["kv_raw"], o_taps["kv_raw"], s.kvw)
+        checked = ("attn_branch", "moe_branch", "out")
+    else:
+        checked = ("attn_branch", "moe_branch", "out", "kv_new")
+    for k in checked:
         assert errs[k] <= tols[k], (k, errs, tols)
     return errs

@@ -128,7 +128,7 @@ def gpu_step(st, s, rec, tokens, next_drafts=None):
     g = {"L": L, "am": am.cpu().numpy(), "com": com.cpu().numpy(), "logits": lg.cpu().numpy(),
          "len": read_i32(st.model.length_ptr()), "tok": tok.cpu().numpy(),
          "hidden": rec[:, : s.T].cpu().numpy().astype(np.float32),
-         "sel": [], "rlogits": [], "Hp": [], "kv_new": []}
+         "sel": [], "rlogits": [], "Hp": [], "kv_new": [], "kv_raw": []}
     for l, dl in enumerate(st.layers):
         assert dl.layer.sync_status() == MK_OK
         sel = np.empty((s.T, s.top_k), np.int32)
@@ -140,14 +140,19 @@ def gpu_step(st, s, rec, tokens, next_drafts=None):
         g["sel"].append(sel)
         g["rlogits"].append(rl)
         g["Hp"].append(hp)
-        g["kv_new"].append(parity.kv_to_f32(st.kv[l][L:L + s.T].cpu().numpy(), s.kv_fmt))
+        raw = st.kv[l][L:L + s.T].cpu().numpy()
+        g["kv_raw"].append(raw)
+        g["kv_new"].append(parity.kv_to_f32(raw, s.kv_fmt, s.kvw))
     return g
 
 
 def gpu_cache_host(st, s, l, L):
     """Host copy of the GPU's cache rows [0, L) of layer l (rows past L zero)."""
-    kv = np.zeros((s.capacity if s.capacity > L + s.T else L + s.T, s.kvw),
-                  np.uint16 if s.kv_fmt == "bf16" else np.float32)
+    rows = s.capacity if s.capacity > L + s.T else L + s.T
+    if s.kv_fmt == "fp8row":
+        kv = np.zeros((rows, recipe.kv_row_bytes(s)), np.uint8)
+    else:
+        kv = np.zeros((rows, s.kvw), np.uint16 if s.kv_fmt == "bf16" else np.float32)
     src = st.kv[l][:L].cpu().numpy()
     kv[:L] = src.view(np.uint16) if s.kv_fmt == "bf16" else src
     return kv
@@ -160,7 +165,7 @@ def check_layers_teacher_forced(st, s, ws, g, expert_fn=None, seed=0, layers=Non
     for l in (range(len(st.layers)) if layers is None else layers):
         H = g["hidden"][l]
         kvh = gpu_cache_host(st, s, l, L)
-        taps = {"Hp": g["Hp"][l], "sel": g["sel"][l]}
+        taps = {"Hp": g["Hp"][l], "sel": g["sel"][l], "kv_raw": g["kv_raw"][l]}
         kw = dict(full_weights=ws[l]) if "experts" in ws[l] and ws[l]["experts"] else \
             dict(base_weights=ws[l], expert_fn=expert_fn)
         errs = parity.check_layer(s, seed, l, g["hidden"][l + 1], g["kv_new"][l], taps, H, L, kv_host=kvh, **kw)

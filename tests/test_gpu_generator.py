@@ -77,3 +77,15 @@ def test_mxfp4_blocks_identical(R, K):
     dq = q.cpu().numpy()
     bad = np.flatnonzero(dq != hq.ravel())
     assert bad.size == 0, (bad[:8], dq[bad[:8]], hq.ravel()[bad[:8]])
+
+
+@pytest.mark.parametrize("rows,kvw,rb", [(1, 21, 32), (77, 576, 592), (300, 80, 96)])
+def test_fp8row_kv_identical(rows, kvw, rb):
+    st, ss = synth.stream_id("kv_prefill", 4), synth.stream_id("kv_scale", 4)
+    d = _dev(rows * rb, torch.uint8)
+    synth.dev_fp8row_kv(d.data_ptr(), rows, kvw, rb, 1, st, ss, 1.0)
+    torch.cuda.synchronize()
+    h = synth.fp8row_kv(rows, kvw, rb, 1, st, ss, 1.0)
+    dd = d.cpu().numpy()
+    bad = np.flatnonzero(dd != h.ravel())
+    assert bad.size == 0, (bad[:8], dd[bad[:8]], h.ravel()[bad[:8]])

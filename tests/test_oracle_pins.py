@@ -543,3 +543,151 @@ def test_mxfp4_layer_matches_fp64_unabsorbed_bruteforce():
     out, taps = oracle.layer_step(s, w, H, kv.copy(), s.L)
     ref = oracle.layer_step_f64(s, w, H, kv, s.L, force_sel=taps["sel"])
     assert normwise(out, ref["out"]) < 1e-5
+
+
+# ---------------------------------------------------------------- fp8 (E4M3) KV cache rows
+# "DeepSeek-V4.1-Flash breaks 1,000 tokens per second for one user", section
+# "Appendix: method": the cache may be held in fp8 E4M3.  Reading taken: one
+# power-of-two fp32 scale per row (the smallest that fits the row's maximum in
+# E4M3's +-448), codes by round-to-nearest-even of value / scale.
+C0K = C0Q.with_(name="micro_fp8kv", kv_fmt="fp8row", L=9)
+
+
+def _ocp_e4m3_table():
+    """All finite codes from the E4M3 bit layout (bias 7; exponent field 0 is
+    subnormal, m/8 * 2^-6), checked against the values the OCP document prints."""
+    t = {}
+    for c in range(256):
+        if c & 0x7F == 0x7F:
+            continue
+        e, m = (c >> 3) & 15, c & 7
+        v = m / 8 * 2.0 ** -6 if e == 0 else (1 + m / 8) * 2.0 ** (e - 7)
+        t[c] = -v if c & 0x80 else v
+    g = json.load(open(os.path.join(GOLD, "ocp_e4m3_values.json")))
+    for c, v in g["values"].items():
+        assert t[int(c, 16)] == v, c
+    return t
+
+
+def _nearest_e4m3_bruteforce(x, table):
+    """Nearest code of the published table, ties to the even code, saturating at +-448."""
+    x = float(x)
+    if abs(x) >= 448.0:
+        return 0xFE if x < 0 else 0x7E
+    best = None
+    for c, v in table.items():
+        if (c & 0x80) != (0x80 if math.copysign(1.0, x) < 0 else 0):
+            continue
+        dd = abs(v - x)
+        if best is None or dd < best[0] or (dd == best[0] and (c & 1) == 0 and (best[1] & 1) == 1):
+            best = (dd, c)
+    return best[1]
+
+
+def test_fp8_row_encoder_is_the_nearest_table_code_ties_to_even():
+    table = _ocp_e4m3_table()
+    vals = sorted(v for c, v in table.items() if c < 0x7F)
+    probes = [0.0, 447.9, 448.0, 500.0, 2.0 ** -10, 2.0 ** -9 * 0.5, 2.0 ** -9 * 1.5]
+    probes += [(a + b) / 2 for a, b in zip(vals, vals[1:])]            # every tie
+    probes += list(np.random.default_rng(3).standard_normal(400) * 50)
+    for x in probes:
+        for sx in (x, -x):
+            got = oracle.f32_to_e4m3(np.float32(sx))
+            want = _nearest_e4m3_bruteforce(np.float32(sx), table)
+            if want in (0x00, 0x80) and got in (0x00, 0x80):
+                continue                                                   # +-0
+            assert got == want, (sx, hex(got), hex(want))
+    assert oracle.f32_to_e4m3(float("nan")) == 0x7F
+
+
+def test_fp8_row_scale_is_the_smallest_fitting_power_of_two():
+    rng = np.random.default_rng(5)
+    for k in range(300):
+        row = (rng.standard_normal(40) * 10.0 ** rng.uniform(-6, 6)).astype(np.float32)
+        if k % 50 == 0:
+            row[:] = 0
+            row[k % 40] = np.float32(448.0 * 2.0 ** rng.integers(-20, 20))   # a boundary: exactly 448 s
+        s = oracle.fp8_row_scale(row)
+        m, e = math.frexp(s)
+        assert m == 0.5, s                                                 # a power of two
+        amax = float(np.abs(row).max())
+        assert amax <= 448.0 * s and amax > 448.0 * s / 2, (amax, s)
+    assert oracle.fp8_row_scale(np.zeros(7, np.float32)) == 1.0
+
+
+def test_fp8_row_layout_and_decode_against_the_table():
+    kvw = 21
+    rb = oracle.kv_row_bytes("fp8row", kvw)
+    assert rb == 32 and oracle.kv_row_bytes("fp8row", 576) == 592
+    assert oracle.kv_row_bytes("bf16", 576) == 1152 and oracle.kv_row_bytes("f32", 576) == 2304
+    table = _ocp_e4m3_table()
+    rng = np.random.default_rng(7)
+    buf = np.zeros((5, rb), np.uint8)
+    want = np.zeros((5, kvw), np.float64)
+    for r in range(5):
+        codes = rng.integers(0, 256, kvw)
+        codes[codes == 0x7F] = 0x7E
+        codes[codes == 0xFF] = 0xFE
+        sc = np.float32(2.0 ** int(rng.integers(-12, 4)))
+        buf[r, :kvw] = codes
+        buf[r, kvw:kvw + 4] = np.frombuffer(sc.tobytes(), np.uint8)
+        want[r] = [table[int(c)] * float(sc) for c in codes]
+    assert np.array_equal(oracle.kv_decode(buf, "fp8row", kvw, 5).astype(np.float64), want)
+
+
+def test_fp8_prefill_rows_decode_to_the_drawn_values():
+    """The generator's fp8 rows against the same N(0,1) draws the bf16 cache holds:
+    each element within half an E4M3 step (at the row's scale) of its draw."""
+    s = C0K.with_(L=40)
+    kv = recipe.kv_prefill_host(s, seed=2)
+    draws = synth.normal_f32((s.L, s.kvw), 2, synth.stream_id("kv_prefill", 0), recipe.ACT_SIGMA).astype(np.float64)
+    dec = oracle.kv_decode(kv, "fp8row", s.kvw, s.L).astype(np.float64)
+    sc = kv[: s.L, s.kvw:s.kvw + 4].copy().view(np.float32).astype(np.float64)
+    a = np.abs(draws) / sc
+    step = np.where(a < 2.0 ** -6, 2.0 ** -9, 2.0 ** (np.floor(np.log2(np.maximum(a, 2.0 ** -6))) - 3))
+    assert np.all(np.abs(dec - draws) <= step * sc / 2 + 1e-12)
+    assert set(np.log2(sc[:, 0]).astype(int)) <= {-6, -5, -4}
+    assert np.all(kv[s.L:] == 0) and np.all(kv[: s.L, s.kvw + 4:] == 0)
+
+
+def test_fp8_cache_new_rows_are_the_f32_rows_quantised_per_row():
+    """Same layer with an f32 cache holding the decoded fp8 prefill: the new rows
+    (which depend on H only) must come back as the f32 rows quantised by the
+    row rule (scale and codes checked against the table by brute force), and
+    the attention branch may differ only by that quantisation."""
+    s8 = C0K
+    w, H, kv8 = fresh(s8)
+    s32 = s8.with_(kv_fmt="f32")
+    kv32 = np.zeros((s32.capacity, s32.kvw), np.float32)
+    kv32[: s8.L] = oracle.kv_decode(kv8, "fp8row", s8.kvw, s8.L)
+    out8, t8 = oracle.layer_step(s8, w, H, kv8, s8.L)
+    out32, t32 = oracle.layer_step(s32, w, H, kv32, s8.L)
+    table = _ocp_e4m3_table()
+    x = kv32[s8.L:s8.L + s8.T].astype(np.float64)
+    for i in range(s8.T):
+        row = kv8[s8.L + i]
+        sc = float(row[s8.kvw:s8.kvw + 4].copy().view(np.float32)[0])
+        amax = np.abs(x[i]).max()
+        assert math.frexp(sc)[0] == 0.5 and 448 * sc / 2 < amax <= 448 * sc
+        for m in range(s8.kvw):
+            assert row[m] == _nearest_e4m3_bruteforce(np.float32(x[i, m] / sc), table), (i, m)
+        assert np.all(row[s8.kvw + 4:] == 0)
+    # attention over mostly shared rows: the branch moves by the quantisation of the new rows only
+    e = normwise(t8["Hp"].astype(np.float64) - H, t32["Hp"].astype(np.float64) - H)
+    assert 0 < e < 5e-2, e
+
+
+def test_fp8_cache_layer_matches_fp64_unabsorbed_bruteforce():
+    s = C0K
+    w, H, kv = fresh(s)
+    kv64 = kv.copy()
+    out, taps = oracle.layer_step(s, w, H, kv, s.L)
+    ref = oracle.layer_step_f64(s, w, H, kv64, s.L, force_sel=taps["sel"])
+    assert normwise(out, ref["out"]) < 1e-5
+    assert normwise(taps["Hp"].astype(np.float64) - H, ref["Hp"] - H) < 1e-4
+    # new rows: the fp32 and fp64 rows may round to neighbouring codes; the rows are
+    # otherwise equal after decoding
+    kvn = oracle.kv_decode(kv[s.L:s.L + s.T], "fp8row", s.kvw, s.T).astype(np.float64)
+    sc = kv[s.L:s.L + s.T, s.kvw:s.kvw + 4].copy().view(np.float32).astype(np.float64)
+    assert np.all(np.abs(kvn - ref["kv_new"]) <= 32 * sc)
+    assert np.mean(kvn == ref["kv_new"]) > 0.99

@@ -42,7 +42,7 @@ def test_static_scratch_step_matches_workspace_step_twice_second_smaller():
             buf = np.empty(shape, dt)
             dl.layer.debug_tap(tap, buf)
             taps[name] = buf
-        g_kv = parity.kv_to_f32(kv_b[L:L + T].cpu().numpy(), s.kv_fmt)
+        g_kv = parity.kv_to_f32(kv_b[L:L + T].cpu().numpy(), s.kv_fmt, s.kvw)
         errs = parity.check_layer(s2, 0, 0, out_b.cpu().numpy(), g_kv, taps, H, L, full_weights=w)
         print("[no-alloc] T=%d L=%d errors %s" % (T, L, errs), flush=True)
 
