@@ -64,8 +64,9 @@ def expert_bytes(s):
 
 def layer_bytes(s, L, slots):
     """Algorithmic bytes of one layer step: touched weights, KV read/write, activations in/out."""
-    kv_e = 2 if s.kv_fmt == "bf16" else 4
-    kv = (L + s.T) * s.kvw * kv_e + s.T * s.kvw * kv_e
+    from synth import recipe
+    rb = recipe.kv_row_bytes(s)          # one cache row (fp8 rows: codes, scale, padding)
+    kv = (L + s.T) * rb + s.T * rb
     act = 2 * s.T * s.d * 4 + 2 * s.d * 4
     return attn_bytes(s) + router_bytes(s) + slots * expert_bytes(s) + kv + act
 
@@ -435,7 +436,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--workload", default="C5", choices=["C2", "C3", "C4", "C5", "C3X", "C5X"])
+    ap.add_argument("--workload", default="C5", choices=["C2", "C3", "C4", "C5", "C3X", "C5X", "C3XK", "C5XK"])
     ap.add_argument("--layers", type=int, default=None, help="stack depth override (diagnostics only)")
     ap.add_argument("--layer-reps", type=int, default=4)
     ap.add_argument("--starts", type=int, default=5,

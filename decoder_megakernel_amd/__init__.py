@@ -27,8 +27,9 @@ MK_ERR_TIMEOUT = -6
 MK_ERR_DEVICE_FAULT = -7
 MK_ERR_UNSUPPORTED_SHAPE = -8
 
-MK_FMT_F32, MK_FMT_BF16, MK_FMT_FP8_B128, MK_FMT_MXFP4 = 0, 1, 2, 3
-FORMATS = {"f32": MK_FMT_F32, "bf16": MK_FMT_BF16, "fp8": MK_FMT_FP8_B128, "mxfp4": MK_FMT_MXFP4}
+MK_FMT_F32, MK_FMT_BF16, MK_FMT_FP8_B128, MK_FMT_MXFP4, MK_FMT_FP8_ROW = 0, 1, 2, 3, 4
+FORMATS = {"f32": MK_FMT_F32, "bf16": MK_FMT_BF16, "fp8": MK_FMT_FP8_B128, "mxfp4": MK_FMT_MXFP4,
+           "fp8row": MK_FMT_FP8_ROW}
 MK_T_WQ, MK_T_WDKV, MK_T_WUK, MK_T_WUV, MK_T_WO, MK_T_WR, MK_T_EXPERT = range(7)
 
 # Every entry point the header declares (checked by the CPU tests).

@@ -64,16 +64,16 @@ int check_cfg(const mk_layer_config* c) {
   const Dims D = dims_of(c);
   if (D.d <= 0 || D.nh <= 0 || D.dh <= 0 || D.dc <= 0 || D.dr <= 0 || D.E <= 0 || D.topk <= 0 || D.f <= 0)
     return fail(MK_ERR_INVALID_ARG, "non-positive dimension");
-  if (D.af < 0 || D.af > 1 || D.ef < 0 || D.ef > 3 || D.kf < 0 || D.kf > 1)
+  if (D.af < 0 || D.af > 1 || D.ef < 0 || D.ef > 3 || !(D.kf == MK_FMT_F32 || D.kf == MK_FMT_BF16 || D.kf == MK_FMT_FP8_ROW))
     return fail(MK_ERR_INVALID_ARG, "unknown format");
   if (c->has_router_bias != 0 && c->has_router_bias != 1) return fail(MK_ERR_INVALID_ARG, "has_router_bias must be 0 or 1");
   if (!(c->rms_eps >= 0.f) || !(c->rope_base > 0.f)) return fail(MK_ERR_INVALID_ARG, "bad eps or rope base");
   const bool f32 = D.af == MK_FMT_F32 && D.ef == MK_FMT_F32 && D.kf == MK_FMT_F32;
-  const bool bf = D.af == MK_FMT_BF16 && D.kf == MK_FMT_BF16 &&
+  const bool bf = D.af == MK_FMT_BF16 && (D.kf == MK_FMT_BF16 || D.kf == MK_FMT_FP8_ROW) &&
                   (D.ef == MK_FMT_BF16 || D.ef == MK_FMT_FP8_B128 || D.ef == MK_FMT_MXFP4);
   if (!f32 && !bf)
     return fail(MK_ERR_UNSUPPORTED_SHAPE,
-                "formats must be all F32, or BF16 attention/KV with BF16, FP8_B128 or MXFP4 experts");
+                "formats must be all F32, or BF16 attention with a BF16 or FP8_ROW cache and BF16, FP8_B128 or MXFP4 experts");
   if (D.d % 128 || D.f % 128) return fail(MK_ERR_UNSUPPORTED_SHAPE, "d_model and d_ff must be multiples of 128");
   if (D.dh % 32 || D.dc % 32 || D.dr % 32) return fail(MK_ERR_UNSUPPORTED_SHAPE, "d_head, d_latent, d_rope must be multiples of 32");
   if (D.E % 16) return fail(MK_ERR_UNSUPPORTED_SHAPE, "n_experts must be a multiple of 16");
@@ -376,7 +376,7 @@ int mk_kv_bytes(const mk_layer_config* cfg, int32_t capacity, size_t* bytes) {
   int rc = check_cfg(cfg);
   if (rc) return rc;
   if (!bytes || capacity < 0) return fail(MK_ERR_INVALID_ARG, "bad arguments");
-  *bytes = (size_t)capacity * (cfg->d_latent + cfg->d_rope) * (cfg->kv_format == MK_FMT_F32 ? 4 : 2);
+  *bytes = (size_t)capacity * kv_row_bytes(cfg->kv_format, cfg->d_latent + cfg->d_rope);
   return MK_OK;
 }
 

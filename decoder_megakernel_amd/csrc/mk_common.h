@@ -41,6 +41,10 @@ __host__ __device__ constexpr int tile_k(int fmt) {
 // Bytes per element in the tiles (MXFP4: two elements per byte, see launch_pack).
 __host__ __device__ constexpr int elem_bytes(int fmt) { return fmt == MK_FMT_F32 ? 4 : (fmt == MK_FMT_BF16 ? 2 : 1); }
 // Formats whose tiles carry scales: fp8 (fp32 per 128x128 block) and MXFP4 (E8M0 per 32 elements of a row).
+// Bytes of one KV cache row of kvw values (fp8 rows: codes, fp32 scale, padding to 16).
+__host__ __device__ constexpr int kv_row_bytes(int fmt, int kvw) {
+  return fmt == MK_FMT_FP8_ROW ? (kvw + 4 + 15) / 16 * 16 : kvw * (fmt == MK_FMT_F32 ? 4 : 2);
+}
 __host__ __device__ constexpr bool scaled_fmt(int fmt) { return fmt == MK_FMT_FP8_B128 || fmt == MK_FMT_MXFP4; }
 
 // Per-layer device state (persistent across steps; zeroed at init).

@@ -14,6 +14,7 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 
 // ------------------------------------------------------------------ memory helpers
 // Loads from device (global) memory through global-address-space pointers.
@@ -116,6 +117,34 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
   const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
   const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
   return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// eight E4M3 codes (two dwords) times a scale -> eight bf16, two codes per
+// instruction, assembled as dwords.  Exact while code * scale is a bf16 value
+// (always, for a power-of-two scale inside bf16's range).
+__device__ __forceinline__ u32x4 fp8x8_scaled_bf16(uint32_t w0, uint32_t w1, float s) {
+  return u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, s, false)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, s, true)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, s, false)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, s, true))};
+}
+// fp32 -> OCP E4M3 code (bias 7, largest finite 448), round to nearest even,
+// for |x| <= 448.  Below 2^-6 the codes are subnormal with a step of 2^-9
+// (x * 512 is exact, rintf rounds half to even, and 8 is the smallest normal
+// code); above, the fp32 mantissa is cut to 3 bits with the round-half-even
+// increment and the exponent rebiased from 127 to 7.
+__device__ __forceinline__ uint32_t e4m3_rne(float x) {
+  const uint32_t sign = (__builtin_bit_cast(uint32_t, x) >> 24) & 0x80u;
+  const float a = fabsf(x);
+  uint32_t code;
+  if (a < 0.015625f) {
+    code = (uint32_t)rintf(a * 512.f);
+  } else {
+    const uint32_t b = __builtin_bit_cast(uint32_t, a);
+    code = ((b + 0x7FFFFu + ((b >> 20) & 1u)) >> 20) - (120u << 3);
+    code = code < 0x7Eu ? code : 0x7Eu;
+  }
+  return sign | code;
 }
 
 // ------------------------------------------------------------------ MFMA

@@ -66,8 +66,16 @@ typedef enum mk_status {
  * in the low nibble of byte j), one E8M0 scale byte per 32 consecutive elements
  * of a row (value = E2M1(code) * 2^(scale - 127)); the expert format the pages'
  * serving stack uses ("DeepSeek-V4.1-Flash breaks 1,000 tokens per second for
- * one user", section "Appendix: method"). */
-typedef enum mk_format { MK_FMT_F32 = 0, MK_FMT_BF16 = 1, MK_FMT_FP8_B128 = 2, MK_FMT_MXFP4 = 3 } mk_format;
+ * one user", section "Appendix: method").
+ * FP8_ROW (KV cache only): per cache row, its d_latent + d_rope E4M3 codes, then
+ * the row's scale as an fp32, then zero bytes up to a multiple of 16
+ * (value = E4M3(code) * scale).  The same page names an fp8 E4M3 KV cache for
+ * that stack without a scale layout; the scale written by a step is the
+ * smallest power of two 2^e with max|row| <= 448 * 2^e (1 for a zero row),
+ * codes round to nearest even, so the stored value is exact in bf16. */
+typedef enum mk_format {
+  MK_FMT_F32 = 0, MK_FMT_BF16 = 1, MK_FMT_FP8_B128 = 2, MK_FMT_MXFP4 = 3, MK_FMT_FP8_ROW = 4
+} mk_format;
 
 /* Layer shape.  Canonical weight layouts (row-major) that mk_pack_* consume:
  *   W_Q   [n_heads*(d_head+d_rope)][d_model]  head h owns rows h*(d_head+d_rope)..:
@@ -79,11 +87,13 @@ typedef enum mk_format { MK_FMT_F32 = 0, MK_FMT_BF16 = 1, MK_FMT_FP8_B128 = 2, M
  *   W_R   [n_experts][d_model]                router; optional bias [n_experts] fp32
  *   W1,W3 [d_ff][d_model], W2 [d_model][d_ff] per expert (SwiGLU: W2 (silu(W1 x) * W3 x))
  * attn_format applies to W_Q, W_DKV, W_UK, W_UV, W_O, W_R (F32 or BF16);
- * expert_format to W1, W3, W2 (F32, BF16, FP8_B128 or MXFP4); kv_format to the cache.
+ * expert_format to W1, W3, W2 (F32, BF16, FP8_B128 or MXFP4); kv_format to the
+ * cache (F32, BF16 or FP8_ROW).
  * Supported shapes: d_model, d_ff multiples of 128; d_head, d_latent multiples
  * of 32, d_head <= 128, n_heads <= 128; d_rope a multiple of 32; n_experts a multiple of 16 and <= 1024;
  * top_k <= 16; d_model <= 4096; n_heads*d_head and d_ff <= 4608.
- * Formats must be all F32, or attention/KV BF16 with experts BF16, FP8_B128 or MXFP4. */
+ * Formats must be all F32, or attention BF16 with a BF16 or FP8_ROW cache and
+ * experts BF16, FP8_B128 or MXFP4. */
 typedef struct mk_layer_config {
   int32_t abi_version;       /* must be MK_ABI_VERSION */
   int32_t d_model;
@@ -138,7 +148,8 @@ typedef struct mk_layer_weights {
                                 may be shared between layers. */
 } mk_layer_weights;
 
-/* KV cache of one layer: rows [capacity][d_latent + d_rope] in kv_format, row
+/* KV cache of one layer: `capacity` rows in kv_format (mk_kv_bytes gives the
+ * size; an FP8_ROW row takes d_latent + d_rope + 4 bytes rounded up to 16), row
  * j = latent c_j followed by its RoPE-rotated key.  A step reads rows
  * [0, length) plus its own new rows and writes rows [length, length+T); it does
  * not change `length` (the caller commits accepted rows). */

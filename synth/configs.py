@@ -77,8 +77,13 @@ C3X = C3.with_(name="mxfp4_E384_T8_L8192", exp_fmt="mxfp4")
 # routed experts of their own (about 165 GB).
 C5X = C5.with_(name="stack32_mxfp4_E384_T6_L4096", exp_fmt="mxfp4", n_pools=0)
 
-PRESETS = {s.name: s for s in (C0, C1, C2, C3, C4, C5, C3X, C5X)}
-BY_KEY = {"C0": C0, "C1": C1, "C2": C2, "C3": C3, "C4": C4, "C5": C5, "C3X": C3X, "C5X": C5X}
+# The serving formats of the MXFP4 stack: MXFP4 experts with an fp8 (E4M3) KV
+# cache, one power-of-two scale per row.
+C3XK = C3X.with_(name="mxfp4_fp8kv_E384_T8_L8192", kv_fmt="fp8row")
+C5XK = C5X.with_(name="stack32_mxfp4_fp8kv_E384_T6_L4096", kv_fmt="fp8row")
+PRESETS = {s.name: s for s in (C0, C1, C2, C3, C4, C5, C3X, C5X, C3XK, C5XK)}
+BY_KEY = {"C0": C0, "C1": C1, "C2": C2, "C3": C3, "C4": C4, "C5": C5, "C3X": C3X, "C5X": C5X,
+          "C3XK": C3XK, "C5XK": C5XK}
 
 # Skewed routing: the hot set is the first ceil(0.2 E) experts of a seeded permutation.
 HOT_FRACTION = 0.2

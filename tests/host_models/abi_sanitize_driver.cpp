@@ -38,6 +38,8 @@ int main() {
       cfg(4096, 32, 128, 512, 64, 384, 8, 1, 2048, MK_FMT_BF16, MK_FMT_FP8_B128, MK_FMT_BF16),
       cfg(4096, 32, 128, 512, 64, 384, 8, 1, 2048, MK_FMT_BF16, MK_FMT_MXFP4, MK_FMT_BF16),
       cfg(640, 6, 64, 256, 64, 48, 6, 1, 384, MK_FMT_BF16, MK_FMT_MXFP4, MK_FMT_BF16),
+      cfg(4096, 32, 128, 512, 64, 384, 8, 1, 2048, MK_FMT_BF16, MK_FMT_MXFP4, MK_FMT_FP8_ROW),
+      cfg(640, 6, 64, 256, 64, 48, 6, 1, 384, MK_FMT_BF16, MK_FMT_BF16, MK_FMT_FP8_ROW),
   };
   for (const auto& c : good) {
     CHECK(mk_check_config(&c) == MK_OK);
@@ -49,8 +51,9 @@ int main() {
     size_t b = 0;
     CHECK(mk_packed_bytes(&c, 99, &b) == MK_ERR_INVALID_ARG);
     CHECK(mk_packed_bytes(&c, MK_T_WQ, nullptr) == MK_ERR_INVALID_ARG);
-    CHECK(mk_kv_bytes(&c, 8192, &b) == MK_OK && b == (size_t)8192 * (c.d_latent + c.d_rope) *
-                                                     (c.kv_format == MK_FMT_F32 ? 4 : 2));
+    const size_t row = c.kv_format == MK_FMT_FP8_ROW ? (size_t)(c.d_latent + c.d_rope + 4 + 15) / 16 * 16
+                                                     : (size_t)(c.d_latent + c.d_rope) * (c.kv_format == MK_FMT_F32 ? 4 : 2);
+    CHECK(mk_kv_bytes(&c, 8192, &b) == MK_OK && b == 8192 * row);
     CHECK(mk_kv_bytes(&c, -1, &b) == MK_ERR_INVALID_ARG);
     // without a GPU the device-dependent sizes are an error, not a crash
     CHECK(mk_layer_state_bytes(&c, 0, &b) != MK_OK);
@@ -65,6 +68,8 @@ int main() {
   c = good[2]; c.n_heads = -3; bad.push_back({c, MK_ERR_INVALID_ARG});
   c = good[2]; c.expert_format = 7; bad.push_back({c, MK_ERR_INVALID_ARG});
   c = good[2]; c.kv_format = -1; bad.push_back({c, MK_ERR_INVALID_ARG});
+  c = good[2]; c.kv_format = MK_FMT_FP8_B128; bad.push_back({c, MK_ERR_INVALID_ARG});
+  c = good[0]; c.kv_format = MK_FMT_FP8_ROW; bad.push_back({c, MK_ERR_UNSUPPORTED_SHAPE});
   c = good[2]; c.has_router_bias = 2; bad.push_back({c, MK_ERR_INVALID_ARG});
   c = good[2]; c.rms_eps = -1.f; bad.push_back({c, MK_ERR_INVALID_ARG});
   c = good[2]; c.d_model = 4000; bad.push_back({c, MK_ERR_UNSUPPORTED_SHAPE});

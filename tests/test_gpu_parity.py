@@ -4,7 +4,7 @@ import numpy as np
 import pytest
 
 from synth import recipe
-from synth.configs import C1, C2, C3, C3X, C4, LayerShape
+from synth.configs import C1, C2, C3, C3X, C3XK, C4, LayerShape
 
 pytestmark = pytest.mark.gpu
 
@@ -27,6 +27,10 @@ MID_MX_WIDE = LayerShape("mid_mxfp4_wide", d=2048, n_h=4, d_h=64, d_c=128, d_r=3
 MID_MX_TICKET = LayerShape("mid_mxfp4_ticket", d=4096, n_h=4, d_h=64, d_c=128, d_r=32, E=16, top_k=3, n_shared=1,
                            f=1024, T=5, L=60, attn_fmt="bf16", exp_fmt="mxfp4", kv_fmt="bf16")
 MID_MX_FUSED = MID_MX_TICKET.with_(name="mid_mxfp4_fused", f=2048, top_k=2, T=6, L=33)
+# fp8 (E4M3, one scale per row) cache: generic shapes with each expert format.
+MID_KV8 = MID_FP8.with_(name="mid_fp8_kv8", kv_fmt="fp8row")
+MID_BF16_KV8 = MID_BF16.with_(name="mid_bf16_kv8", kv_fmt="fp8row")
+MID_MX_KV8 = MID_MX_TICKET.with_(name="mid_mxfp4_kv8", kv_fmt="fp8row")
 MID_F32 = LayerShape("mid_f32", d=384, n_h=4, d_h=32, d_c=96, d_r=32, E=16, top_k=3, n_shared=1, f=256,
                      T=3, L=45, attn_fmt="f32", exp_fmt="f32", kv_fmt="f32")
 # Expert widths of 32 tiles, d_model of 64 tiles and d_model >= 2 d_ff: the
@@ -58,7 +62,8 @@ def _run(s, seed=0, layer=0, L=None, T=None, full_weights=True):
 
 
 @pytest.mark.parametrize("shape", [C1, MID_F32, MID_BF16, MID_FP8, MID_F32_DOWN, MID_BF16_DOWN, MID_MX, MID_MX_WIDE,
-                                   MID_MX_TICKET, MID_MX_FUSED], ids=lambda s: s.name)
+                                   MID_MX_TICKET, MID_MX_FUSED, MID_KV8, MID_BF16_KV8, MID_MX_KV8],
+                         ids=lambda s: s.name)
 def test_small_shapes_match_oracle(shape):
     _run(shape)
 
@@ -67,8 +72,16 @@ def test_single_row_empty_cache():
     _run(MID_BF16, L=0, T=1)
 
 
+def test_single_row_empty_fp8_cache():
+    _run(MID_KV8, L=0, T=1)
+
+
 def test_max_rows():
     _run(MID_FP8, T=8, L=13)
+
+
+def test_max_rows_fp8_cache():
+    _run(MID_KV8, T=8, L=13)
 
 
 def test_full_size_bf16_E128_T6_L2048():
@@ -83,13 +96,17 @@ def test_full_size_mxfp4_E384_T8_L8192():
     _run(C3X, full_weights=False)
 
 
+def test_full_size_mxfp4_fp8kv_E384_T8_L8192():
+    _run(C3XK, full_weights=False)
+
+
 def test_full_size_fp8_E384_T6_L65536_skew():
     _run(C4, full_weights=False)
 
 
-def test_run_twice_bitwise_identical():
+@pytest.mark.parametrize("s", [MID_FP8, MID_KV8], ids=lambda s: s.name)
+def test_run_twice_bitwise_identical(s):
     from decoder_megakernel_amd import harness
-    s = MID_FP8
     dl = harness.DeviceLayer(s, 0, 0)
     H = harness.hidden(s)
     outs = []
@@ -98,7 +115,7 @@ def test_run_twice_bitwise_identical():
         out = torch.empty_like(H)
         dl.step(H, s.T, kv, s.L, out)
         torch.cuda.synchronize()
-        outs.append((out.cpu().numpy().view(np.uint32), kv.cpu().numpy().view(np.uint16)))
+        outs.append((out.cpu().numpy().view(np.uint32), kv.cpu().numpy().view(np.uint8)))
     assert np.array_equal(outs[0][0], outs[1][0])
     assert np.array_equal(outs[0][1], outs[1][1])
 

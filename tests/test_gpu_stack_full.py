@@ -2,7 +2,8 @@
 384-expert layer (16 routed-expert pools), d_model 4096, vocab 129,280,
 T = 6, cache from 4096 positions (capacity 8192) -- the same stack and launch
 configuration bench.py times -- and the same stack with MXFP4 experts, every
-layer with routed experts of its own.
+layer with routed experts of its own, with a bf16 and with an fp8 (E4M3, one
+scale per row) cache.
 
   - steps 0-3 against the oracle composed layer by layer on its own rows and
     caches (free-running): logits normwise <= 5e-2, argmax and expert selection
@@ -24,13 +25,13 @@ import pytest
 
 import stack_parity as sp
 from synth import recipe
-from synth.configs import C5, C5X
+from synth.configs import C5, C5X, C5XK
 
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
 
 
-@pytest.mark.parametrize("s", [C5, C5X], ids=lambda s: s.name)
+@pytest.mark.parametrize("s", [C5, C5X, C5XK], ids=lambda s: s.name)
 def test_full_stack_32_layers_vocab_129280(s):
     from decoder_megakernel_amd import harness
     print("[stack] building %s on the GPU" % s.name, flush=True)
@@ -47,7 +48,10 @@ def test_full_stack_32_layers_vocab_129280(s):
         nxt = recipe.tokens_host(s, 0, step + 1)[1:]
         if step == 3:
             for l in range(s.n_layers):
-                st.kv[l][L:] = torch.tensor(0x7FC0, dtype=torch.int16)      # bf16 quiet NaN
+                if s.kv_fmt == "fp8row":
+                    st.kv[l][L:] = torch.tensor(0x7F, dtype=torch.uint8)    # E4M3 NaN codes
+                else:
+                    st.kv[l][L:] = torch.tensor(0x7FC0, dtype=torch.int16)  # bf16 quiet NaN
             torch.cuda.synchronize()
         g = sp.gpu_step(st, s, rec, tokens, nxt)
         assert g["L"] == L
