@@ -77,6 +77,16 @@ def lib():
         L.orc_embed.argtypes = [_vp, _i, _i, _vp, _i, _vp]
         L.orc_head.argtypes = [_vp, _i, _i, _vp, ctypes.c_float, _vp, _i, _vp, _vp]
         L.orc_greedy_accept.argtypes = [_vp, _vp, _i, _vp]
+        L.orc_head_fmt.restype = _i
+        L.orc_head_fmt.argtypes = [_vp, _i, _vp, _i, _i, _vp, ctypes.c_float, _vp, _i, _vp, _vp]
+        L.orc_verify_sampled.restype = _i
+        L.orc_verify_sampled.argtypes = [_vp, _i, _i, _vp, ctypes.c_float, ctypes.c_uint64, _vp, _vp]
+        L.orc_splitmix64_mix.restype = ctypes.c_uint64
+        L.orc_splitmix64_mix.argtypes = [ctypes.c_uint64]
+        L.orc_sample_key.restype = ctypes.c_uint64
+        L.orc_sample_key.argtypes = [ctypes.c_uint64, ctypes.c_uint32]
+        L.orc_sample_uniform.restype = ctypes.c_float
+        L.orc_sample_uniform.argtypes = [ctypes.c_uint64, ctypes.c_uint64]
         L.orc_bf16_to_f32.restype = ctypes.c_float
         L.orc_bf16_to_f32.argtypes = [ctypes.c_uint16]
         L.orc_f32_to_bf16.restype = ctypes.c_uint16
@@ -262,6 +272,44 @@ def head(headw: np.ndarray, gamma_f: np.ndarray, h: np.ndarray, eps: float = 1e-
     _chk(lib().orc_head(_p(np.ascontiguousarray(headw)), V, d, _p(gamma_f), eps, _p(h), T, _p(lg),
                         _p(am)), "orc_head")
     return lg, am
+
+
+def head_fp8(codes: np.ndarray, scales: np.ndarray, gamma_f: np.ndarray, h: np.ndarray, eps: float = 1e-6):
+    """LM head with E4M3 codes [V][d] and fp32 128x128 block scales."""
+    V, d = codes.shape
+    T = h.shape[0]
+    h = np.ascontiguousarray(h, dtype=np.float32)
+    lg = np.empty((T, V), np.float32)
+    am = np.empty(T, np.int32)
+    sc = np.ascontiguousarray(scales, dtype=np.float32)
+    _chk(lib().orc_head_fmt(_p(np.ascontiguousarray(codes)), ORC_FP8B128, _p(sc), V, d, _p(gamma_f), eps, _p(h), T,
+                            _p(lg), _p(am)), "orc_head_fmt")
+    return lg, am
+
+
+def sample_key(seed: int, step: int) -> int:
+    return int(lib().orc_sample_key(seed, step))
+
+
+def splitmix64_mix(z: int) -> int:
+    return int(lib().orc_splitmix64_mix(z))
+
+
+def sample_uniform(key: int, i: int) -> float:
+    return float(lib().orc_sample_uniform(key, i))
+
+
+def verify_sampled(logits: np.ndarray, tokens, tau: float, key: int):
+    """Returns (sample [T], committed tokens)."""
+    lg = np.ascontiguousarray(logits, dtype=np.float32)
+    T, V = lg.shape
+    t = np.ascontiguousarray(tokens, dtype=np.int32)
+    smp = np.empty(T, np.int32)
+    com = np.empty(T + 1, np.int32)
+    n = lib().orc_verify_sampled(_p(lg), V, T, _p(t), tau, key, _p(smp), _p(com))
+    if n <= 0:
+        raise RuntimeError("orc_verify_sampled failed")
+    return smp, com[1:n + 1].copy()
 
 
 def greedy_accept(tokens, argmax):

@@ -643,10 +643,17 @@ int orc_embed(const uint16_t* emb, int V, int d, const int32_t* tokens, int T, f
 
 int orc_head(const uint16_t* head, int V, int d, const float* gamma_f, float eps,
              const float* h, int T, float* logits, int32_t* argmax) {
+  return orc_head_fmt(head, ORC_BF16, NULL, V, d, gamma_f, eps, h, T, logits, argmax);
+}
+
+int orc_head_fmt(const void* head, int fmt, const float* scales, int V, int d, const float* gamma_f, float eps,
+                 const float* h, int T, float* logits, int32_t* argmax) {
   if (!head || !gamma_f || !h || V <= 0 || d <= 0) return -1;
+  if (fmt != ORC_BF16 && !(fmt == ORC_FP8B128 && scales)) return -1;
+  lut_init();
   float* x = malloc(sizeof(float) * d);
   float* lg = logits ? NULL : malloc(sizeof(float) * V);
-  wmat W = mk_wmat(head, ORC_BF16, NULL, V, d);
+  wmat W = mk_wmat(head, fmt, scales, V, d);
   for (int i = 0; i < T; ++i) {
     float* li = logits ? logits + (long)i * V : lg;
     rmsnorm(h + (long)i * d, gamma_f, d, eps, x);
@@ -657,6 +664,85 @@ int orc_head(const uint16_t* head, int V, int d, const float* gamma_f, float eps
   }
   free(x); free(lg);
   return 0;
+}
+
+/* ------------------------------------------------------------------ sampled verification */
+/* SplitMix64's output function (Steele, Lea and Flood, OOPSLA 2014; the
+ * constants of the reference implementation splitmix64.c). */
+uint64_t orc_splitmix64_mix(uint64_t z) {
+  z ^= z >> 30;
+  z *= 0xBF58476D1CE4E5B9ull;
+  z ^= z >> 27;
+  z *= 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+#define ORC_GOLDEN_GAMMA 0x9E3779B97F4A7C15ull
+
+uint64_t orc_sample_key(uint64_t seed, uint32_t step) {
+  return orc_splitmix64_mix(seed + ((uint64_t)step + 1) * ORC_GOLDEN_GAMMA);
+}
+
+/* Draw i of a step: the top 23 bits of SplitMix64's i-th output from the
+ * step's key, as the midpoint (k + 1/2) 2^-23 -- in (0, 1), exact in fp32. */
+float orc_sample_uniform(uint64_t key, uint64_t i) {
+  const uint64_t r = orc_splitmix64_mix(key + (i + 1) * ORC_GOLDEN_GAMMA);
+  return (float)(((double)(r >> 41) + 0.5) * 0x1p-23);
+}
+
+/* Speculative sampling with the drafts taken as point proposals (a draft
+ * distribution that puts all its mass on the drafted token): row i's target
+ * distribution is p_i = softmax(logits_i / tau).  Draft i+1 is accepted when
+ * the row's acceptance draw is below p_i(draft); at the first rejection the
+ * step commits a token drawn from p_i with the draft removed (renormalised),
+ * and after T-1 acceptances a token drawn from p_{T-1}.  Token draws are
+ * Gumbel-max: argmax_v logits_iv / tau - ln(-ln u_iv), ties to the lower id.
+ * Draws: u_iv = uniform(key, i (V+1) + v) for v < V, the acceptance draw
+ * uniform(key, i (V+1) + V).  All arithmetic in fp64 on the fp32 logits. */
+int orc_verify_sampled(const float* logits, int V, int T, const int32_t* tokens, float tau, uint64_t key,
+                       int32_t* sample, int32_t* committed) {
+  if (!logits || !tokens || V <= 0 || T <= 0 || !(tau > 0.f)) return -1;
+  const double it = 1.0 / (double)tau;
+  int32_t* smp = malloc(sizeof(int32_t) * T);
+  int32_t* res = malloc(sizeof(int32_t) * T);        /* row i's draw without draft i+1 */
+  double* pd = malloc(sizeof(double) * T);           /* p_i(draft i+1) */
+  for (int i = 0; i < T; ++i) {
+    const float* l = logits + (long)i * V;
+    const int dn = i + 1 < T ? tokens[i + 1] : -1;
+    double M = -INFINITY;
+    for (int v = 0; v < V; ++v) M = fmax(M, (double)l[v] * it);
+    double S = 0.0;
+    for (int v = 0; v < V; ++v) S += exp((double)l[v] * it - M);
+    pd[i] = (dn >= 0 && dn < V) ? exp((double)l[dn] * it - M) / S : 0.0;
+    double b = -INFINITY, bx = -INFINITY;
+    int bi = -1, bxi = -1;
+    for (int v = 0; v < V; ++v) {
+      const double u = (double)orc_sample_uniform(key, (uint64_t)i * (uint64_t)(V + 1) + (uint64_t)v);
+      const double y = (double)l[v] * it - log(-log(u));
+      if (y > b) { b = y; bi = v; }
+      if (v != dn && y > bx) { bx = y; bxi = v; }
+    }
+    smp[i] = bi;
+    res[i] = bxi;
+  }
+  int n = 0, last = -1;
+  for (int i = 0; i + 1 < T; ++i) {
+    const double ua = (double)orc_sample_uniform(key, (uint64_t)i * (uint64_t)(V + 1) + (uint64_t)V);
+    if (ua < pd[i]) {
+      ++n;
+      continue;
+    }
+    last = res[i];
+    break;
+  }
+  if (n == T - 1) last = smp[T - 1];
+  if (sample) memcpy(sample, smp, sizeof(int32_t) * T);
+  if (committed) {
+    committed[0] = n + 1;
+    for (int j = 1; j <= n; ++j) committed[j] = tokens[j];
+    committed[n + 1] = last;
+  }
+  free(smp); free(res); free(pd);
+  return n + 1;
 }
 
 int orc_greedy_accept(const int32_t* tokens, const int32_t* a, int T, int32_t* committed) {

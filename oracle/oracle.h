@@ -33,6 +33,15 @@
  *    names MXFP4 expert weights as the serving format, with an fp8 (E4M3) KV
  *    cache; the page gives no scale layout for the cache, and the reading taken
  *    is one power-of-two fp32 scale per cache row (orc_fp8_row_scale).
+ *  - Verification: greedy (the byte-for-byte greedy gate of "DeepSeek-V4.1-Flash
+ *    breaks 1,000 tokens per second for one user", section "The safety layer"),
+ *    or sampled at a temperature with matched random draws (same section) and
+ *    one rejection step per speculative step ("Why one GB300 ...", section
+ *    "Where the 11.2 ms goes"): speculative sampling (Leviathan et al. 2023;
+ *    Chen et al. 2023) with the drafts read as point proposals, token draws by
+ *    the Gumbel-max trick, draws from SplitMix64 (Steele, Lea and Flood 2014).
+ *    The LM head may be fp8 with 128x128 block scales (the fp8 head named as a
+ *    small item in "Why one GB300 ...", section "Three readings").
  *
  * Readings where the pages are silent (each listed in the design notes):
  * eps = 1e-6; softmax scale 1/sqrt(d_h + d_r); RoPE base 10000 with the angle
@@ -165,6 +174,19 @@ int orc_embed(const uint16_t* emb, int V, int d, const int32_t* tokens, int T, f
 /* logits[i] = W_head (RMSNorm(h_i) * gamma_f), fp32; argmax with ties to the lower id. */
 int orc_head(const uint16_t* head, int V, int d, const float* gamma_f, float eps,
              const float* h, int T, float* logits, int32_t* argmax);
+/* The same in a weight format: ORC_BF16 (scales NULL) or ORC_FP8B128 (E4M3
+ * codes [V][d], fp32 scales [ceil(V/128)][ceil(d/128)]). */
+int orc_head_fmt(const void* head, int fmt, const float* scales, int V, int d, const float* gamma_f, float eps,
+                 const float* h, int T, float* logits, int32_t* argmax);
+/* Sampled verification (temperature tau > 0) with the step's draws made from
+ * a 64-bit key: see oracle.c.  tokens = t0, d_1 .. d_{T-1}.  Writes sample[T]
+ * (row i's Gumbel-max draw from softmax(logits_i / tau)) and committed[1 + T]
+ * (count n+1, then d_1..d_n and the final draw); returns n+1, or -1. */
+int orc_verify_sampled(const float* logits, int V, int T, const int32_t* tokens, float tau, uint64_t key,
+                       int32_t* sample, int32_t* committed);
+uint64_t orc_splitmix64_mix(uint64_t z);
+uint64_t orc_sample_key(uint64_t seed, uint32_t step);      /* mix(seed + (step + 1) gamma) */
+float orc_sample_uniform(uint64_t key, uint64_t i);         /* ((mix(key + (i+1) gamma) >> 41) + 1/2) 2^-23 */
 /* Greedy verification.  tokens = t0, d_1 .. d_{T-1}; a = argmax per row.
  * n = largest n <= T-1 with d_j == a_{j-1} for every j <= n.  Commits n+1 tokens
  * (d_1..d_n, a_n) into committed[0..n]; returns n+1. */

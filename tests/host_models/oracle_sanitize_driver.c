@@ -151,6 +151,16 @@ static void run_stack_pieces(void) {
   for (int t = 0; t < T; ++t) CHECK(am[t] >= 0 && am[t] < V);
   const int n = orc_greedy_accept(tokens, am, T, committed);
   CHECK(n >= 1 && n <= T);
+  int32_t smp[4], com[5];
+  const int ns = orc_verify_sampled(logits, V, T, tokens, 0.7f, orc_sample_key(5, 2), smp, com);
+  CHECK(ns >= 1 && ns <= T && com[0] == ns);
+  CHECK(orc_verify_sampled(logits, V, T, tokens, 0.f, 1, smp, com) < 0);
+  uint8_t* codes = (uint8_t*)malloc((size_t)V * d);
+  float scales[1] = {0.01f};
+  for (int i = 0; i < V * d; ++i) codes[i] = (uint8_t)(i * 37 % 126);
+  CHECK(orc_head_fmt(codes, ORC_FP8B128, scales, V, d, gf, 1e-6f, h, T, logits, am) == 0);
+  CHECK(orc_head_fmt(codes, ORC_FP8B128, NULL, V, d, gf, 1e-6f, h, T, logits, am) < 0);
+  free(codes);
   int32_t bad[1] = {V};
   CHECK(orc_embed(emb, V, d, bad, 1, h) < 0);
   free(emb); free(head); free(gf); free(h); free(logits);

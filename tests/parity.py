@@ -57,14 +57,19 @@ def fp8row_kv_check(g_codes, o_codes, kvw):
     """New fp8 cache rows of the GPU against the oracle's.  The two sides quantize
     rows whose values differ by bf16 rounding of the activations, so a code may
     land one E4M3 step away and a row's power-of-two scale may differ by a factor
-    of two where its maximum sits at a boundary.  Asserts exactly that: every
-    decoded element within one code step of the oracle's at the larger of the
-    two scales, plus the activation tolerance.  Returns the largest distance in
-    code steps."""
+    of two where its maximum sits at a boundary.  Asserts: every scale a power of
+    two and the smallest that fits the row (its largest code value is at least
+    224 = 448 / 2), scales equal to the oracle's up to that factor, zero padding,
+    and every decoded element within one code step of the oracle's at the larger
+    of the two scales plus the activation tolerance.  Returns the fraction of
+    codes identical to the oracle's (rows with equal scales)."""
     g = oracle.kv_decode(g_codes, "fp8row", kvw, g_codes.shape[0]).astype(np.float64)
     o = oracle.kv_decode(o_codes, "fp8row", kvw, o_codes.shape[0]).astype(np.float64)
     gs = g_codes[:, kvw:kvw + 4].copy().view(np.float32).astype(np.float64)[:, 0]
     os_ = o_codes[:, kvw:kvw + 4].copy().view(np.float32).astype(np.float64)[:, 0]
+    assert np.all(np.frexp(gs)[0] == 0.5), gs
+    top = np.abs(g).max(axis=1) / gs
+    assert np.all((top >= 224.0) & (top <= 448.0)), top
     ratio = gs / os_
     assert np.all((ratio == 1.0) | (ratio == 2.0) | (ratio == 0.5)), ratio
     assert np.all(g_codes[:, kvw + 4:] == 0) and np.all(o_codes[:, kvw + 4:] == 0)
@@ -72,10 +77,10 @@ def fp8row_kv_check(g_codes, o_codes, kvw):
     # E4M3 step at magnitude a (in units of the row scale): 2^(floor(log2 a) - 3), 2^-9 below 2^-6
     a = np.maximum(np.abs(o), np.abs(g)) / sc
     step = np.where(a < 2.0 ** -6, 2.0 ** -9, 2.0 ** (np.floor(np.log2(np.maximum(a, 2.0 ** -6))) - 3))
-    dist = np.abs(g - o) / (step * sc)
     act = TOL["bf16"] * np.abs(o).max(axis=1, keepdims=True)
-    assert np.all(np.abs(g - o) <= step * sc + act), float(dist.max())
-    return float(dist.max())
+    assert np.all(np.abs(g - o) <= step * sc + act), float((np.abs(g - o) - step * sc - act).max())
+    same = ratio == 1.0
+    return float((g_codes[same, :kvw] == o_codes[same, :kvw]).mean()) if same.any() else 0.0
 
 
 def gpu_step(dl, s, H_dev, kv_dev, L, T=None):
@@ -159,7 +164,7 @@ def check_layer(s, seed, layer, g_out, g_kv, g_taps, H, L, kv_host=None, full_we
     if s.kv_fmt == "fp8row":
         # rows are compared code by code (fp8row_kv_check) where the GPU's raw rows are at hand
         if "kv_raw" in g_taps:
-            errs["kv_new_steps"] = fp8row_kv_check(g_taps["kv_raw"], o_taps["kv_raw"], s.kvw)
+            errs["kv_new_same_codes"] = fp8row_kv_check(g_taps["kv_raw"], o_taps["kv_raw"], s.kvw)
         checked = ("attn_branch", "moe_branch", "out")
     else:
         checked = ("attn_branch", "moe_branch", "out", "kv_new")

@@ -691,3 +691,126 @@ def test_fp8_cache_layer_matches_fp64_unabsorbed_bruteforce():
     sc = kv[s.L:s.L + s.T, s.kvw:s.kvw + 4].copy().view(np.float32).astype(np.float64)
     assert np.all(np.abs(kvn - ref["kv_new"]) <= 32 * sc)
     assert np.mean(kvn == ref["kv_new"]) > 0.99
+
+
+def test_fp8_row_parity_rule_accepts_rounding_differences_and_rejects_a_loose_scale():
+    """The GPU-side rule for new fp8 rows (tests/parity.py), exercised on the CPU:
+    the oracle's rows against the rows of the same layer fed bf16-rounded hidden
+    rows pass; the same rows with a scale twice too large (codes halved, values
+    kept) fail the minimality check; codes moved by two steps fail."""
+    import parity
+    s = C0K
+    w, H, kv = fresh(s)
+    kv2 = kv.copy()
+    oracle.layer_step(s, w, H, kv, s.L)
+    Hb = oracle.bf16_to_f32(np.array([[oracle.lib().orc_f32_to_bf16(float(x)) for x in r] for r in H], np.uint16))
+    oracle.layer_step(s, w, Hb.astype(np.float32), kv2, s.L)
+    a, b = kv[s.L:s.L + s.T], kv2[s.L:s.L + s.T]
+    assert parity.fp8row_kv_check(b, a, s.kvw) > 0.5
+    loose = b.copy()
+    table = _ocp_e4m3_table()
+    for r in range(s.T):
+        sc = loose[r, s.kvw:s.kvw + 4].copy().view(np.float32)[0]
+        vals = [table[int(c)] for c in loose[r, :s.kvw]]
+        loose[r, :s.kvw] = [_nearest_e4m3_bruteforce(np.float32(v / 2), table) for v in vals]
+        loose[r, s.kvw:s.kvw + 4] = np.frombuffer(np.float32(sc * 2).tobytes(), np.uint8)
+    with pytest.raises(AssertionError):
+        parity.fp8row_kv_check(loose, a, s.kvw)
+    off = b.copy()
+    i = int(np.argmax(np.abs(oracle.kv_decode(b, "fp8row", s.kvw, s.T)[0])))
+    off[0, i] = off[0, i] - 2 if off[0, i] & 0x7 >= 2 else off[0, i] + 2
+    with pytest.raises(AssertionError):
+        parity.fp8row_kv_check(off, a, s.kvw)
+
+
+# ---------------------------------------------------------------- sampled verification and the fp8 head
+# "DeepSeek-V4.1-Flash breaks 1,000 tokens per second for one user", section
+# "The safety layer": sampling uses matched random draws; "Why one GB300 doesn't
+# beat 4x RTX PRO 6000 at single-stream decode", section "Where the 11.2 ms goes":
+# one rejection kernel per speculative step, and an fp8 head as a small item.
+def test_splitmix64_matches_the_published_first_outputs():
+    g = json.load(open(os.path.join(GOLD, "splitmix64_state0.json")))
+    gamma = 0x9E3779B97F4A7C15
+    for k, want in enumerate(g["outputs"]):
+        assert oracle.splitmix64_mix(((k + 1) * gamma) % (1 << 64)) == int(want, 16)
+
+
+def test_sample_uniform_is_an_odd_multiple_of_2_to_minus_24():
+    key = oracle.sample_key(11, 3)
+    u = np.array([oracle.sample_uniform(key, i) for i in range(50000)], np.float64)
+    m = u * 2.0 ** 24
+    assert np.all(m == np.round(m)) and np.all(np.round(m) % 2 == 1)
+    assert 0 < u.min() and u.max() < 1
+    assert abs(u.mean() - 0.5) < 5 * math.sqrt(1 / 12 / len(u))
+    assert abs(u.var() - 1 / 12) < 2e-3
+    assert oracle.sample_key(11, 3) != oracle.sample_key(11, 4) != oracle.sample_key(12, 3)
+
+
+def _softmax(x):
+    e = np.exp(x - x.max())
+    return e / e.sum()
+
+
+def test_sampled_verification_commits_tokens_distributed_as_the_target():
+    """Speculative sampling's guarantee: the first committed token is a draw
+    from the target p_0 = softmax(l_0 / tau) whatever the draft, the draft is
+    accepted with probability p_0(draft), and after an acceptance the next
+    token is a draw from p_1 (counts within 5 standard deviations)."""
+    l = np.array([[1.0, 0.2, -0.5, 0.7, 0.0], [0.3, -1.0, 0.9, 0.1, 0.5]], np.float32)
+    tau, draft = 0.8, 3
+    p0, p1 = _softmax(l[0].astype(np.float64) / tau), _softmax(l[1].astype(np.float64) / tau)
+    N = 20000
+    first = np.zeros(5)
+    second = np.zeros(5)
+    acc = 0
+    for k in range(N):
+        _, com = oracle.verify_sampled(l, [4, draft], tau, oracle.sample_key(7, k))
+        first[com[0]] += 1
+        if len(com) == 2:
+            acc += 1
+            assert com[0] == draft
+            second[com[1]] += 1
+        else:
+            assert com[0] != draft
+    for v in range(5):
+        assert abs(first[v] / N - p0[v]) < 5 * math.sqrt(p0[v] * (1 - p0[v]) / N), (v, first / N, p0)
+        assert abs(second[v] / acc - p1[v]) < 5 * math.sqrt(p1[v] * (1 - p1[v]) / acc), (v, second / acc, p1)
+    assert abs(acc / N - p0[draft]) < 5 * math.sqrt(p0[draft] * (1 - p0[draft]) / N)
+
+
+def test_sampled_verification_at_low_temperature_is_greedy():
+    rng = np.random.default_rng(4)
+    V, T = 50, 6
+    for trial in range(20):
+        l = np.stack([rng.permutation(V) * 0.05 for _ in range(T)]).astype(np.float32)
+        am = l.argmax(axis=1)
+        toks = [int(rng.integers(V))] + [int(am[i]) if rng.random() < 0.7 else int(rng.integers(V))
+                                         for i in range(T - 1)]
+        smp, com = oracle.verify_sampled(l, toks, 1e-3, oracle.sample_key(1, trial))
+        assert np.array_equal(smp, am)
+        assert np.array_equal(com, oracle.greedy_accept(toks, am))
+
+
+def test_sampled_verification_certain_and_impossible_drafts():
+    l = np.zeros((3, 8), np.float32)
+    l[0, 5] = 1e4           # draft 1 = 5 is certain
+    l[1, 2] = -1e4          # draft 2 = 2 is impossible
+    for k in range(200):
+        smp, com = oracle.verify_sampled(l, [0, 5, 2], 1.0, oracle.sample_key(3, k))
+        assert len(com) == 2 and com[0] == 5 and com[1] != 2
+        assert smp[0] == 5
+
+
+def test_fp8_head_against_an_explicit_dense_matrix():
+    V, d, T = 300, 256, 3
+    codes, scales = synth.fp8_blocks(V, d, 0, synth.stream_id("head", 0), 0.02)
+    lut = np.array([oracle.lib().orc_e4m3_to_f32(i) for i in range(256)], np.float64)
+    dense = lut[codes] * np.repeat(np.repeat(scales.astype(np.float64), 128, 0), 128, 1)[:V, :d]
+    h = recipe.normal_f32((T, d), 0, synth.stream_id("H", 0), 1.0)
+    gf = recipe.normal_f32(d, 0, synth.stream_id("gamma_f", 0), 0.1, mean=1.0)
+    lg, am = oracle.head_fp8(codes, scales, gf, h, 1e-6)
+    x = h.astype(np.float64)
+    x = x / np.sqrt((x * x).mean(axis=1, keepdims=True) + 1e-6) * gf
+    ref = x @ dense.T
+    assert np.abs(lg - ref).max() <= 1e-5 * np.abs(ref).max()
+    assert np.array_equal(am, ref.argmax(axis=1))
