@@ -339,8 +339,9 @@ def run_stack(s, args):
         "layer_trace": tsum,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_GBPS, 4),
-                     "traffic": measured_traffic("layer_kernel_stack32_%s_T6_hbm_counters.json" % s.exp_fmt),
-                     "kernel": "layer_kernel<bf16, %s, bf16>" % s.exp_fmt, "bytes_per_launch": int(lb),
+                     "traffic": measured_traffic("layer_kernel_stack32_%s_T6_hbm_counters.json"
+                                                 % (s.exp_fmt + ("" if s.kv_fmt == "bf16" else "_kv" + s.kv_fmt))),
+                     "kernel": "layer_kernel<bf16, %s, %s>" % (s.exp_fmt, s.kv_fmt), "bytes_per_launch": int(lb),
                      "avg_launch_us": round(us_layer, 2), "launches_timed": launches},
     }
     if args.cpu_baseline:

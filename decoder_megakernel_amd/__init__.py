@@ -38,7 +38,8 @@ EXPORTS = (
     "mk_kv_bytes", "mk_layer_state_bytes", "mk_layer_workspace_bytes", "mk_pack_tensor", "mk_pack_expert",
     "mk_layer_init", "mk_decode_step", "mk_decode_step_static", "mk_debug_tap", "mk_get_stats", "mk_set_trace", "mk_read_trace",
     "mk_set_barrier_timeout_us", "mk_sync_status", "mk_layer_reset", "mk_layer_destroy",
-    "mk_head_packed_bytes", "mk_pack_head", "mk_model_state_bytes", "mk_model_init", "mk_model_set_length",
+    "mk_head_packed_bytes", "mk_pack_head", "mk_head_packed_bytes_fmt", "mk_pack_head_fp8",
+    "mk_model_state_bytes", "mk_model_init", "mk_model_init_ex", "mk_model_set_sampling", "mk_model_set_length",
     "mk_model_length_ptr", "mk_model_step", "mk_model_sync_status", "mk_model_reset",
     "mk_model_set_hidden_record", "mk_model_destroy",
 )
@@ -115,7 +116,11 @@ def _load():
         "mk_head_packed_bytes": (_int, [_i32, _i32, _vp]),
         "mk_pack_head": (_int, [_i32, _i32, _vp, _vp, _vp]),
         "mk_model_state_bytes": (_int, [_i32, _i32, _int, _vp]),
+        "mk_head_packed_bytes_fmt": (_int, [_i32, _i32, _i32, _vp]),
+        "mk_pack_head_fp8": (_int, [_i32, _i32, _vp, _vp, _vp, _vp]),
         "mk_model_init": (_int, [_vp, _i32, _vp, _vp, _vp, _i32, _vp, _i32, _vp, _vp, _vp]),
+        "mk_model_init_ex": (_int, [_vp, _i32, _vp, _vp, _i32, _vp, _i32, _vp, _i32, _vp, _vp, _vp]),
+        "mk_model_set_sampling": (_int, [_vp, ctypes.c_float, ctypes.c_uint64]),
         "mk_model_set_length": (_int, [_vp, _i32]),
         "mk_model_length_ptr": (_vp, [_vp]),
         "mk_model_step": (_int, [_vp, _vp, _int, _vp, _vp, _vp, _vp, _vp]),
@@ -255,8 +260,12 @@ class Layer:
             pass
 
 
-def head_packed_bytes(vocab: int, d_model: int) -> int:
-    return _size_out(lib.mk_head_packed_bytes, vocab, d_model)
+def head_packed_bytes(vocab: int, d_model: int, fmt=MK_FMT_BF16) -> int:
+    return _size_out(lib.mk_head_packed_bytes_fmt, vocab, d_model, FORMATS[fmt] if isinstance(fmt, str) else fmt)
+
+
+def pack_head_fp8(vocab: int, d_model: int, codes: int, scales: int, dst: int, stream: int = 0) -> None:
+    _chk(lib.mk_pack_head_fp8(vocab, d_model, codes, scales, dst, stream))
 
 
 def pack_head(vocab: int, d_model: int, src: int, dst: int, stream: int = 0) -> None:
@@ -269,14 +278,18 @@ def model_state_bytes(n_layers: int, vocab: int, hip_device: int = 0) -> int:
 
 class Model:
     def __init__(self, layers, embedding: int, head_packed: int, gamma_final: int, vocab: int, kv_rows,
-                 capacity: int, state: int, hidden: int):
+                 capacity: int, state: int, hidden: int, head_fmt=MK_FMT_BF16):
         self.layers = list(layers)
         self._lh = (ctypes.c_void_p * len(layers))(*[l.handle.value for l in layers])
         self._kv = (ctypes.c_void_p * len(kv_rows))(*kv_rows)
         h = _vp()
-        _chk(lib.mk_model_init(self._lh, len(layers), embedding, head_packed, gamma_final, vocab, self._kv,
-                               capacity, state, hidden, ctypes.byref(h)))
+        hf = FORMATS[head_fmt] if isinstance(head_fmt, str) else head_fmt
+        _chk(lib.mk_model_init_ex(self._lh, len(layers), embedding, head_packed, hf, gamma_final, vocab, self._kv,
+                                  capacity, state, hidden, ctypes.byref(h)))
         self.handle = h
+
+    def set_sampling(self, temperature: float, seed: int) -> None:
+        _chk(lib.mk_model_set_sampling(self.handle, temperature, seed))
 
     def set_length(self, length: int) -> None:
         _chk(lib.mk_model_set_length(self.handle, length))

@@ -332,6 +332,12 @@ struct mk_model {
   uint32_t* tickets;   // the head's ticket counters
   const uint8_t* dummy;
   int nwg_head;
+  int head_fmt;              // MK_FMT_BF16 or MK_FMT_FP8_B128
+  const float* head_scales;  // fp8 head: its block scales (inside the packed head)
+  float temperature;         // 0: greedy verification
+  uint64_t seed;             // sampled verification: draws keyed by (seed, step)
+  uint32_t* step;            // sampled verification: device step counter
+  float* part;               // sampled verification: per-workgroup row states
 };
 
 extern "C" {
@@ -718,10 +724,42 @@ int mk_layer_reset(mk_layer* L) {
 void mk_layer_destroy(mk_layer* L) { delete L; }
 
 // ------------------------------------------------------------------ stack
-int mk_head_packed_bytes(int32_t vocab, int32_t d_model, size_t* bytes) {
+// fp8 head: the E4M3 tiles, then (at a 256-byte boundary) the fp32 block scales
+static long long head_scales_offset(int32_t vocab, int32_t d_model) {
+  return (long long)align256((size_t)tiles_bytes(vocab, d_model, MK_FMT_FP8_B128));
+}
+
+int mk_head_packed_bytes_fmt(int32_t vocab, int32_t d_model, int32_t format, size_t* bytes) {
   if (!bytes || vocab <= 0 || d_model <= 0 || vocab % 16 || d_model % 128)
     return fail(MK_ERR_INVALID_ARG, "vocab must be a positive multiple of 16 and d_model of 128");
-  *bytes = (size_t)tiles_bytes(vocab, d_model, MK_FMT_BF16);
+  if (format == MK_FMT_BF16) {
+    *bytes = (size_t)tiles_bytes(vocab, d_model, MK_FMT_BF16);
+  } else if (format == MK_FMT_FP8_B128) {
+    *bytes = (size_t)head_scales_offset(vocab, d_model) +
+             (size_t)((vocab + 127) / 128) * (size_t)((d_model + 127) / 128) * 4;
+  } else {
+    return fail(MK_ERR_INVALID_ARG, "head format must be BF16 or FP8_B128");
+  }
+  return MK_OK;
+}
+
+int mk_head_packed_bytes(int32_t vocab, int32_t d_model, size_t* bytes) {
+  return mk_head_packed_bytes_fmt(vocab, d_model, MK_FMT_BF16, bytes);
+}
+
+int mk_pack_head_fp8(int32_t vocab, int32_t d_model, const uint8_t* codes, const float* scales, void* dst,
+                     void* stream) {
+  size_t b;
+  int rc = mk_head_packed_bytes_fmt(vocab, d_model, MK_FMT_FP8_B128, &b);
+  if (rc) return rc;
+  if (!codes || !scales || !dst) return fail(MK_ERR_INVALID_ARG, "null tensor");
+  hipStream_t s = (hipStream_t)stream;
+  rc = launch_pack(codes, MK_FMT_FP8_B128, 1, vocab, d_model, 0, d_model, 1, dst, 1024, 0, s);
+  if (rc) return fail(MK_ERR_HIP, "pack launch failed");
+  const size_t nsc = (size_t)((vocab + 127) / 128) * (size_t)((d_model + 127) / 128) * 4;
+  if (hipMemcpyAsync((char*)dst + head_scales_offset(vocab, d_model), scales, nsc, hipMemcpyDeviceToDevice, s) !=
+      hipSuccess)
+    return fail(MK_ERR_HIP, "copy of the head scales failed");
   return MK_OK;
 }
 
@@ -736,7 +774,7 @@ int mk_pack_head(int32_t vocab, int32_t d_model, const uint16_t* src_bf16, void*
 }
 
 struct ModelStLayout {
-  size_t len, counter, fault, best_val, best_idx, tickets, dummy, total;
+  size_t len, counter, fault, best_val, best_idx, tickets, dummy, step, part, total;
 };
 static ModelStLayout model_layout(int nwg) {
   ModelStLayout l;
@@ -749,6 +787,8 @@ static ModelStLayout model_layout(int nwg) {
   l.best_idx = take((size_t)nwg * 8 * 4);
   l.tickets = take((size_t)8 * kCntStride * 4);
   l.dummy = take(32768);
+  l.step = take(4);
+  l.part = take((size_t)nwg * 8 * 8 * 4);
   l.total = off;
   return l;
 }
@@ -780,6 +820,13 @@ int mk_model_state_bytes(int32_t n_layers, int32_t vocab, int hip_device, size_t
 int mk_model_init(mk_layer* const* layers, int32_t n_layers, const uint16_t* embedding, const void* head_packed,
                   const float* gamma_final, int32_t vocab, void* const* kv_rows, int32_t capacity, void* state_dev,
                   void* hidden_dev, mk_model** out) {
+  return mk_model_init_ex(layers, n_layers, embedding, head_packed, MK_FMT_BF16, gamma_final, vocab, kv_rows,
+                          capacity, state_dev, hidden_dev, out);
+}
+
+int mk_model_init_ex(mk_layer* const* layers, int32_t n_layers, const uint16_t* embedding, const void* head_packed,
+                     int32_t head_format, const float* gamma_final, int32_t vocab, void* const* kv_rows,
+                     int32_t capacity, void* state_dev, void* hidden_dev, mk_model** out) {
   if (!out) return fail(MK_ERR_INVALID_ARG, "null output");
   *out = nullptr;
   if (!layers || n_layers <= 0 || !embedding || !head_packed || !gamma_final || !kv_rows || !state_dev || !hidden_dev)
@@ -790,7 +837,7 @@ int mk_model_init(mk_layer* const* layers, int32_t n_layers, const uint16_t* emb
       return fail(MK_ERR_INVALID_ARG, "layer %d has a different config", l);
   }
   size_t hb;
-  int rc = mk_head_packed_bytes(vocab, layers[0]->D.d, &hb);
+  int rc = mk_head_packed_bytes_fmt(vocab, layers[0]->D.d, head_format, &hb);
   if (rc) return rc;
   int nwg = 0;
   rc = head_grid(layers[0]->dev, &nwg);
@@ -821,6 +868,14 @@ int mk_model_init(mk_layer* const* layers, int32_t n_layers, const uint16_t* emb
   m->tickets = (uint32_t*)(m->state + ml.tickets);
   m->dummy = (const uint8_t*)(m->state + ml.dummy);
   m->nwg_head = nwg;
+  m->head_fmt = head_format;
+  m->head_scales = head_format == MK_FMT_FP8_B128
+                       ? (const float*)((const char*)head_packed + head_scales_offset(vocab, layers[0]->D.d))
+                       : nullptr;
+  m->temperature = 0.f;
+  m->seed = 0;
+  m->step = (uint32_t*)(m->state + ml.step);
+  m->part = (float*)(m->state + ml.part);
   hipError_t e = hipMemset(m->state, 0, ml.total);
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) {
@@ -859,11 +914,30 @@ int mk_model_step(mk_model* m, int32_t* tokens_dev, int T, const int32_t* next_d
     rc = launch_layer(m->layers[l], hid(l), T, m->kv[l], m->capacity, 0, m->kv_len, hid(l + 1), m->fault, s);
     if (rc) return rc;
   }
-  rc = launch_head(m->head, m->V, d, m->gamma_f, m->layers[0]->cfg.rms_eps, hid(m->n_layers), T, logits_dev,
-                   m->best_val, m->best_idx, m->counter, m->tickets, tokens_dev, next_drafts_dev, argmax_dev,
-                   committed_dev,
-                   m->kv_len, m->dummy, m->fault, m->nwg_head, s);
+  HeadLaunch h;
+  h.head_packed = m->head; h.head_fmt = m->head_fmt; h.scales = m->head_scales;
+  h.V = m->V; h.d = d; h.gamma = m->gamma_f; h.eps = m->layers[0]->cfg.rms_eps; h.hidden = hid(m->n_layers);
+  h.best_val = m->best_val; h.best_idx = m->best_idx; h.counter = m->counter; h.tickets = m->tickets;
+  h.kv_len = m->kv_len; h.dummy = m->dummy; h.fault = m->fault; h.nwg = m->nwg_head;
+  h.temperature = m->temperature; h.seed = m->seed; h.step = m->step; h.part = m->part;
+  rc = launch_head(h, T, logits_dev, tokens_dev, next_drafts_dev, argmax_dev, committed_dev, s);
   if (rc) return fail(MK_ERR_HIP, "head launch failed");
+  return MK_OK;
+}
+
+int mk_model_set_sampling(mk_model* m, float temperature, uint64_t seed) {
+  if (!m) return fail(MK_ERR_INVALID_ARG, "null model");
+  if (!(temperature >= 0.f) || !std::isfinite(temperature))
+    return fail(MK_ERR_INVALID_ARG, "temperature must be finite and >= 0");
+  int cur = 0;
+  hipGetDevice(&cur);
+  hipSetDevice(m->layers[0]->dev);
+  hipError_t e = hipMemset(m->step, 0, 4);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  hipSetDevice(cur);
+  if (e != hipSuccess) return fail(MK_ERR_HIP, "sampling reset failed");
+  m->temperature = temperature;
+  m->seed = seed;
   return MK_OK;
 }
 

@@ -18,13 +18,18 @@ int launch_pack(const void* src, int fmt, int nb, int R, int K, long long sb, lo
 int launch_pack_mx_scales(const void* src, int R, int K, void* dst, long long tile_stride, long long dst_off,
                           hipStream_t stream);
 
-struct HeadParams;
 int launch_embed(const uint16_t* emb, int V, int d, const int32_t* tokens, int T, float* h, uint32_t* fault,
                  hipStream_t s);
-int launch_head(const void* head_packed, int V, int d, const float* gamma, float eps, const float* h, int T,
-                float* logits, float* best_val, int32_t* best_idx, uint32_t* counter, uint32_t* tickets,
-                int32_t* tokens, const int32_t* next_drafts, int32_t* argmax, int32_t* committed, int32_t* kv_len,
-                const uint8_t* dummy, const uint32_t* fault, int nwg, hipStream_t s);
+// Everything the head launch takes that does not change from step to step.
+struct HeadLaunch {
+  const void* head_packed; int head_fmt; const float* scales;   // scales: fp8 head only
+  int V, d; const float* gamma; float eps; const float* hidden;
+  float* best_val; int32_t* best_idx; uint32_t* counter; uint32_t* tickets; int32_t* kv_len;
+  const uint8_t* dummy; const uint32_t* fault; int nwg;
+  float temperature; uint64_t seed; uint32_t* step; float* part;   // temperature 0: greedy
+};
+int launch_head(const HeadLaunch& h, int T, float* logits, int32_t* tokens, const int32_t* next_drafts,
+                int32_t* argmax, int32_t* committed, hipStream_t s);
 int head_kernel_occupancy(int* wgs_per_cu);
 
 }  // namespace mk

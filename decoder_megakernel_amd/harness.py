@@ -16,7 +16,7 @@ from synth.configs import LayerShape
 
 from . import (FORMATS, MK_T_EXPERT, MK_T_WDKV, MK_T_WO, MK_T_WQ, MK_T_WR, MK_T_WUK, MK_T_WUV, Layer,
                LayerWeights, Model, head_packed_bytes, kv_bytes, layer_state_bytes, layer_workspace_bytes,
-               make_config, model_state_bytes, pack_expert, pack_head, pack_tensor, packed_bytes)
+               make_config, model_state_bytes, pack_expert, pack_head, pack_head_fp8, pack_tensor, packed_bytes)
 
 
 def config_of(s: LayerShape):
@@ -202,11 +202,21 @@ class DeviceStack:
         V, d = s.V, s.d
         self.emb = torch.empty((V, d), dtype=torch.int16, device=dev)
         synth.dev_normal_bf16(self.emb.data_ptr(), V * d, seed, synth.stream_id("emb"), recipe.W_SIGMA)
-        head_src = torch.empty((V, d), dtype=torch.int16, device=dev)
-        synth.dev_normal_bf16(head_src.data_ptr(), V * d, seed, synth.stream_id("head"), recipe.W_SIGMA)
-        self.head = _bytes(head_packed_bytes(V, d), device)
-        pack_head(V, d, head_src.data_ptr(), self.head.data_ptr())
-        del head_src
+        self.head = _bytes(head_packed_bytes(V, d, s.head_fmt), device)
+        if s.head_fmt == "fp8":
+            # E4M3 codes with 128x128 block scales, drawn as the fp8 experts are
+            codes = torch.empty((V, d), dtype=torch.uint8, device=dev)
+            scales = torch.empty(((V + 127) // 128) * ((d + 127) // 128), dtype=torch.float32, device=dev)
+            synth.dev_fp8_blocks(codes.data_ptr(), scales.data_ptr(), V, d, seed, synth.stream_id("head"),
+                                 recipe.W_SIGMA)
+            pack_head_fp8(V, d, codes.data_ptr(), scales.data_ptr(), self.head.data_ptr())
+            torch.cuda.synchronize(dev)
+            del codes, scales
+        else:
+            head_src = torch.empty((V, d), dtype=torch.int16, device=dev)
+            synth.dev_normal_bf16(head_src.data_ptr(), V * d, seed, synth.stream_id("head"), recipe.W_SIGMA)
+            pack_head(V, d, head_src.data_ptr(), self.head.data_ptr())
+            del head_src
         self.gf = torch.empty(d, dtype=torch.float32, device=dev)
         synth.dev_normal_f32(self.gf.data_ptr(), d, seed, synth.stream_id("gamma_f"), recipe.GAIN_SIGMA, 1.0)
         self.capacity = capacity or s.capacity
@@ -216,5 +226,5 @@ class DeviceStack:
         torch.cuda.synchronize(dev)
         self.model = Model([dl.layer for dl in self.layers], self.emb.data_ptr(), self.head.data_ptr(),
                            self.gf.data_ptr(), V, [k.data_ptr() for k in self.kv], self.capacity,
-                           self.state.data_ptr(), self.hidden.data_ptr())
+                           self.state.data_ptr(), self.hidden.data_ptr(), head_fmt=s.head_fmt)
         self.model.set_length(s.L)

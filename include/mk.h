@@ -300,12 +300,24 @@ void mk_layer_destroy(mk_layer* layer);
 
 /* ---- stack ------------------------------------------------------------------- */
 /* A stack of layers plus bf16 embedding and LM-head tables [vocab][d_model]
- * (the head packed with mk_pack_head) and a final RMSNorm gain.  One step:
- * embedding gather, every layer (one launch each), final norm + LM head +
- * argmax (ties to the lower id) + greedy acceptance, all on the device with the
- * KV length kept in device memory (no host synchronisation). */
+ * (the head packed with mk_pack_head, or fp8 with mk_pack_head_fp8) and a
+ * final RMSNorm gain.  One step: embedding gather, every layer (one launch
+ * each), final norm + LM head + argmax (ties to the lower id) + greedy
+ * acceptance (or sampled verification, mk_model_set_sampling), all on the
+ * device with the KV length kept in device memory (no host synchronisation). */
 int mk_head_packed_bytes(int32_t vocab, int32_t d_model, size_t* bytes);
 int mk_pack_head(int32_t vocab, int32_t d_model, const uint16_t* src_bf16, void* dst, void* stream);
+/* An fp8 head (the fp8 head that "Why one GB300 doesn't beat 4x RTX PRO 6000 at
+ * single-stream decode", section "Three readings", counts as a small item):
+ * E4M3 codes [vocab][d_model] (device) with fp32 scales per 128x128 block
+ * [ceil(vocab/128)][ceil(d_model/128)] (device), value = E4M3(code) * scale.
+ * mk_head_packed_bytes_fmt gives the packed size for format MK_FMT_BF16 or
+ * MK_FMT_FP8_B128 (MK_ERR_INVALID_ARG otherwise); mk_pack_head_fp8 repacks
+ * into dst (the caller's device buffer of that size), asynchronously on
+ * `stream`; the sources may be freed once the stream has passed the call. */
+int mk_head_packed_bytes_fmt(int32_t vocab, int32_t d_model, int32_t format, size_t* bytes);
+int mk_pack_head_fp8(int32_t vocab, int32_t d_model, const uint8_t* codes, const float* scales, void* dst,
+                     void* stream);
 int mk_model_state_bytes(int32_t n_layers, int32_t vocab, int hip_device, size_t* bytes);
 /* layers: n_layers initialised layers sharing one config; kv_rows: HOST array of
  * n_layers device pointers, each [capacity][d_latent + d_rope]. */
@@ -313,6 +325,29 @@ int mk_model_init(mk_layer* const* layers, int32_t n_layers, const uint16_t* emb
                   const void* head_packed, const float* gamma_final, int32_t vocab,
                   void* const* kv_rows, int32_t capacity, void* state_dev, void* hidden_dev,
                   mk_model** out);
+/* The same with the head's format: MK_FMT_BF16 (mk_pack_head) or
+ * MK_FMT_FP8_B128 (mk_pack_head_fp8). */
+int mk_model_init_ex(mk_layer* const* layers, int32_t n_layers, const uint16_t* embedding,
+                     const void* head_packed, int32_t head_format, const float* gamma_final, int32_t vocab,
+                     void* const* kv_rows, int32_t capacity, void* state_dev, void* hidden_dev, mk_model** out);
+/* Verification mode of the following steps.  temperature 0 (the default):
+ * greedy, as described at mk_model_step.  temperature > 0: sampled
+ * verification with matched random draws ("DeepSeek-V4.1-Flash breaks 1,000
+ * tokens per second for one user", section "The safety layer"): speculative
+ * sampling with the drafts taken as point proposals.  Row i's target is
+ * p_i = softmax(logits_i / temperature); draft i+1 is accepted when the row's
+ * acceptance draw is below p_i(draft); the first rejection commits a draw from
+ * p_i without the rejected draft, T-1 acceptances a draw from p_{T-1}.  Token
+ * draws are Gumbel-max: argmax_v logits_iv / temperature - ln(-ln u_iv), ties
+ * to the lower id.  The draws of the s-th step after this call (s = 0, 1, ...,
+ * counted on the device by every step that commits) are SplitMix64 outputs:
+ * key = mix(seed + (s+1) G), u(i) = ((mix(key + (i+1) G) >> 41) + 1/2) 2^-23
+ * (G = 0x9E3779B97F4A7C15, mix = SplitMix64's output function), with
+ * u_iv = u(i (vocab+1) + v) and the acceptance draw u(i (vocab+1) + vocab).
+ * argmax_dev then receives each row's token draw.  Synchronous (resets the
+ * device step counter); no step may be in flight.  MK_ERR_INVALID_ARG for a
+ * negative or non-finite temperature. */
+int mk_model_set_sampling(mk_model* m, float temperature, uint64_t seed);
 /* Sets the committed KV length (synchronous copy). */
 int mk_model_set_length(mk_model* m, int32_t length);
 /* Device pointer to the committed KV length (int32). */

@@ -34,6 +34,7 @@ class LayerShape:
     steps: int = 1             # verify steps (stacks only)
     kv_capacity: int = 0       # 0 -> L + T
     n_pools: int = 0           # distinct routed-expert weight pools in a stack (0 = one per layer)
+    head_fmt: str = "bf16"     # LM head: "bf16" | "fp8" (E4M3 + fp32 128x128 scales)
     eps: float = 1e-6
     rope_base: float = 10000.0
 

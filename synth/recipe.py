@@ -143,9 +143,14 @@ def kv_prefill_host(s: LayerShape, seed: int = 0, layer: int = 0) -> np.ndarray:
 
 
 def stack_tables_host(s: LayerShape, seed: int = 0):
-    """(embedding [V][d] bf16 bits, LM head [V][d] bf16 bits, final gain [d] fp32)."""
+    """(embedding [V][d] bf16 bits, LM head, final gain [d] fp32).  The head is
+    [V][d] bf16 bits, or for an fp8 head (E4M3 codes [V][d], fp32 128x128 block
+    scales) drawn as the fp8 experts are."""
     emb = normal_bf16((s.V, s.d), seed, stream_id("emb"), W_SIGMA)
-    head = normal_bf16((s.V, s.d), seed, stream_id("head"), W_SIGMA)
+    if s.head_fmt == "fp8":
+        head = fp8_blocks(s.V, s.d, seed, stream_id("head"), W_SIGMA)
+    else:
+        head = normal_bf16((s.V, s.d), seed, stream_id("head"), W_SIGMA)
     gf = normal_f32(s.d, seed, stream_id("gamma_f"), GAIN_SIGMA, mean=1.0)
     return emb, head, gf
 

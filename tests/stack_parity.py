@@ -175,19 +175,27 @@ def check_layers_teacher_forced(st, s, ws, g, expert_fn=None, seed=0, layers=Non
     return out
 
 
-def check_head_teacher_forced(s, tables, g, tag=""):
-    """The oracle's head on the GPU's final rows: logits and the argmax rule."""
-    emb, head, gf = tables
-    o_lg, o_am = oracle.head(head, gf, g["hidden"][-1], s.eps)
+def oracle_head(s, tables, h):
+    """The oracle's head (bf16 or fp8 table) on hidden rows h: (logits, argmax)."""
+    _, head, gf = tables
+    if s.head_fmt == "fp8":
+        return oracle.head_fp8(head[0], head[1], gf, h, s.eps)
+    return oracle.head(head, gf, h, s.eps)
+
+
+def check_head_teacher_forced(s, tables, g, tag="", argmax=True):
+    """The oracle's head on the GPU's final rows: logits, and the argmax rule
+    (argmax=False for a sampled step, whose argmax output holds the draws)."""
+    o_lg, o_am = oracle_head(s, tables, g["hidden"][-1])
     err = parity.normwise(g["logits"], o_lg)
     near = 0
-    for i in range(s.T):
+    for i in range(s.T if argmax else 0):
         if g["am"][i] != o_am[i]:
             lg = o_lg[i].astype(np.float64)
             assert lg[g["am"][i]] >= lg[o_am[i]] - TAU_SEL, (i, g["am"][i], o_am[i])
             near += 1
     print("[stack%s] head teacher-forced: logits normwise %.3e, argmax near-ties %d" % (tag, err, near), flush=True)
-    assert err <= parity.TOL["bf16"], err
+    assert err <= parity.TOL["fp8" if s.head_fmt == "fp8" else "bf16"], err
     return err, near
 
 
@@ -226,7 +234,7 @@ def oracle_stack_step(s, ws, tables, kvs, tokens, L, g=None, expert_fn=None, see
                 else:
                     out, taps = oracle.layer_step(s, w, h, kvs[l], L, force_sel=gs)
         h = out
-    logits, am = oracle.head(head, gf, h, s.eps)
+    logits, am = oracle_head(s, tables, h)
     if g is not None:
         print("[stack%s] free-running: router-logit drift max %.3e (last layer %.3e), tokens with a differing "
               "selection %d, layers forced %d" % (tag, max(drift), drift[-1], near, forced), flush=True)
@@ -254,3 +262,40 @@ def compare_free_running(s, g, o_lg, o_am, tokens, tag=""):
     if near == 0:
         assert g_com == o_com
     return g_com
+
+
+def check_sampled_verification(s, g, tokens, tau, key, tag=""):
+    """The GPU's sampled verification against the oracle's, both on the GPU's
+    own logits (so that only the verification is compared; the logits are
+    checked by check_head_teacher_forced).  A row's token draw may differ only
+    where the oracle's two perturbed values are within 1e-4 of each other, and
+    an acceptance decision only where the draw is within 1e-5 of p_i(draft);
+    without such a near-tie the committed tokens, the count, the KV length and
+    the next t0 must be identical.  Returns the number of committed tokens."""
+    lg = g["logits"].astype(np.float32)
+    o_smp, o_com = oracle.verify_sampled(lg, tokens, tau, key)
+    T, V = lg.shape
+    near = 0
+    for i in range(T):
+        if g["am"][i] != o_smp[i]:
+            u = np.array([oracle.sample_uniform(key, i * (V + 1) + v) for v in (g["am"][i], o_smp[i])], np.float64)
+            y = lg[i, [g["am"][i], o_smp[i]]].astype(np.float64) / tau - np.log(-np.log(u))
+            assert abs(y[0] - y[1]) <= 1e-4 * max(1.0, abs(y[1])), (i, g["am"][i], o_smp[i], y)
+            near += 1
+    for i in range(T - 1):
+        x = lg[i].astype(np.float64) / tau
+        p = np.exp(x[tokens[i + 1]] - x.max()) / np.exp(x - x.max()).sum()
+        ua = oracle.sample_uniform(key, i * (V + 1) + V)
+        if abs(ua - p) < 1e-5:
+            near += 1
+    n = int(g["com"][0])
+    gcom = list(g["com"][1:1 + n])
+    print("[stack%s] sampled verification (tau %g): gpu %s oracle %s, near-ties %d"
+          % (tag, tau, gcom, list(o_com), near), flush=True)
+    if near == 0:
+        assert gcom == list(o_com)
+        assert list(g["am"]) == list(o_smp)
+    assert g["len"] == g["L"] + n and g["tok"][0] == gcom[-1]
+    for j in range(1, n):
+        assert gcom[j - 1] == tokens[j]
+    return n

@@ -92,6 +92,14 @@ def test_null_arguments_are_refused_without_a_device():
     assert lib.mk_head_packed_bytes(129280, 4096, ctypes.byref(n)) == 0
     assert n.value == 129280 * 4096 * 2
     assert lib.mk_head_packed_bytes(129281, 4096, ctypes.byref(n)) == mk.MK_ERR_INVALID_ARG
+    # fp8 head: E4M3 tiles, then the 128x128 block scales at a 256-byte boundary
+    assert lib.mk_head_packed_bytes_fmt(129280, 4096, mk.MK_FMT_FP8_B128, ctypes.byref(n)) == 0
+    assert n.value == 129280 * 4096 + 1010 * 32 * 4
+    assert lib.mk_head_packed_bytes_fmt(129280, 4096, mk.MK_FMT_MXFP4, ctypes.byref(n)) == mk.MK_ERR_INVALID_ARG
+    assert lib.mk_pack_head_fp8(129280, 4096, None, None, None, None) == mk.MK_ERR_INVALID_ARG
+    assert lib.mk_model_set_sampling(None, 1.0, 0) == mk.MK_ERR_INVALID_ARG
+    assert lib.mk_model_init_ex(None, 1, None, None, mk.MK_FMT_BF16, None, 16, None, 8, None, None, None) \
+        == mk.MK_ERR_INVALID_ARG
 
 
 def test_no_device_is_an_error_not_a_crash():

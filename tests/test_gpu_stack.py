@@ -1,6 +1,7 @@
 """GPU parity of the stack step (embedding, layers, final norm + LM head +
-argmax + greedy acceptance, device-resident KV length) against the CPU oracle,
-at a small shape: 3 layers sharing 2 routed-expert pools, vocab 2048.  Rules in
+argmax + greedy acceptance or sampled verification, bf16 or fp8 head,
+device-resident KV length) against the CPU oracle, at a small shape: 3 layers
+sharing 2 routed-expert pools, vocab 2048.  Rules in
 tests/stack_parity.py (per-layer checks teacher-forced on the GPU's state at
 the single-layer selection band; free-running composition with the measured
 drift band; the oracle follows the GPU at a near-tie instead of giving up)."""
@@ -96,3 +97,61 @@ def test_poisoned_rows_past_the_committed_length_are_never_read():
     sp.check_layers_teacher_forced(st, s, ws, g, tag=" poisoned")
     o_lg, o_am, _ = sp.oracle_stack_step(s, ws, tables, kvs, tokens, L, g=g, tag=" poisoned")
     sp.compare_free_running(s, g, o_lg, o_am, tokens, tag=" poisoned")
+
+
+def test_fp8_head_stack_steps_match_oracle():
+    s = STACK_SMALL.with_(name="stack3_fp8_fp8head", head_fmt="fp8", steps=2)
+    st, rec, ws, kvs, tables = _setup(s)
+    L = s.L
+    tokens = recipe.tokens_host(s, 0, 0)
+    for step in range(s.steps):
+        nxt = recipe.tokens_host(s, 0, step + 1)[1:]
+        g = sp.gpu_step(st, s, rec, tokens, nxt)
+        tag = " fp8 head step %d" % step
+        sp.check_head_teacher_forced(s, tables, g, tag=tag)
+        o_lg, o_am, _ = sp.oracle_stack_step(s, ws, tables, kvs, tokens, L, g=g, tag=tag)
+        com = sp.compare_free_running(s, g, o_lg, o_am, tokens, tag=tag)
+        assert g["len"] == L + len(com)
+        L += len(com)
+        tokens = np.concatenate([[com[-1]], nxt]).astype(np.int32)
+
+
+@pytest.mark.parametrize("head_fmt", ["bf16", "fp8"])
+def test_sampled_verification_matches_oracle(head_fmt):
+    """Temperature 1 with seeded drafts (rejected: each step commits one draw
+    from the target without the draft), three steps in a row: the device step
+    counter keys each step's draws."""
+    s = STACK_SMALL.with_(name="stack3_sampled_" + head_fmt, head_fmt=head_fmt)
+    st, rec, ws, kvs, tables = _setup(s)
+    seed, tau = 123, 1.0
+    st.model.set_sampling(tau, seed)
+    tokens = recipe.tokens_host(s, 0, 0)
+    for step in range(3):
+        nxt = recipe.tokens_host(s, 0, step + 1)[1:]
+        g = sp.gpu_step(st, s, rec, tokens, nxt)
+        tag = " sampled %s step %d" % (head_fmt, step)
+        sp.check_head_teacher_forced(s, tables, g, tag=tag, argmax=False)
+        n = sp.check_sampled_verification(s, g, tokens, tau, oracle.sample_key(seed, step), tag=tag)
+        tokens = np.concatenate([[g["tok"][0]], nxt]).astype(np.int32)
+        assert n >= 1
+
+
+def test_sampled_verification_accepts_a_greedy_chain_at_low_temperature():
+    """Drafts that follow greedy decoding, verified at temperature 0.01: the
+    target puts almost all its mass on the greedy token, so the drafts are
+    accepted (as the oracle decides on the same logits)."""
+    s = STACK_SMALL
+    st, rec, ws, kvs, tables = _setup(s)
+    kv_chain = [k.copy() for k in kvs]
+    one = s.with_(T=1)
+    chain = [int(recipe.tokens_host(s, 0, 0)[0])]
+    for i in range(s.T - 1):
+        _, am, _ = sp.oracle_stack_step(one, ws, tables, kv_chain, np.array([chain[-1]], np.int32), s.L + i)
+        chain.append(int(am[0]))
+    tokens = np.array(chain, np.int32)
+    seed, tau = 5, 0.01
+    st.model.set_sampling(tau, seed)
+    g = sp.gpu_step(st, s, rec, tokens)
+    n = sp.check_sampled_verification(s, g, tokens, tau, oracle.sample_key(seed, 0), tag=" low-temperature chain")
+    assert n >= 2
+    st.model.set_sampling(0.0, 0)

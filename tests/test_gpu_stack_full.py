@@ -67,3 +67,39 @@ def test_full_stack_32_layers_vocab_129280(s):
         assert g["tok"][0] == com[-1] and list(g["tok"][1:]) == list(nxt)
         L += n
         tokens = np.concatenate([[com[-1]], nxt]).astype(np.int32)
+
+
+def test_fp8_head_and_sampled_verification_at_vocab_129280():
+    """One layer of the stack's shape with an fp8 LM head of 129,280 rows
+    (about 31 row tiles per workgroup, the cross-grid merges): a greedy step
+    against the oracle (head teacher-forced, then the free-running step), then
+    two sampled steps at temperature 1 whose verification matches the oracle's
+    on the GPU's logits."""
+    import oracle
+    from decoder_megakernel_amd import harness
+    s = C5.with_(name="stack1_fp8head_V129280", n_layers=1, head_fmt="fp8")
+    print("[stack] building %s on the GPU" % s.name, flush=True)
+    st = harness.DeviceStack(s, 0, private_workspaces=True)
+    rec = sp.attach_record(st, s)
+    ws = [recipe.layer_weights_host(s, 0, 0, experts=[])]
+    kvs = [recipe.kv_prefill_host(s, 0, 0)]
+    tables = recipe.stack_tables_host(s, 0)
+    draws = sp.DeviceExpertDraws(s, 0, cap=400)
+    L = s.L
+    tokens = recipe.tokens_host(s, 0, 0)
+    nxt = recipe.tokens_host(s, 0, 1)[1:]
+    g = sp.gpu_step(st, s, rec, tokens, nxt)
+    sp.check_head_teacher_forced(s, tables, g, tag=" fp8 head")
+    o_lg, o_am, _ = sp.oracle_stack_step(s, ws, tables, kvs, tokens, L, g=g, expert_fn=draws, tag=" fp8 head")
+    com = sp.compare_free_running(s, g, o_lg, o_am, tokens, tag=" fp8 head")
+    assert g["len"] == L + len(com)
+    tokens = np.concatenate([[com[-1]], nxt]).astype(np.int32)
+    seed, tau = 77, 1.0
+    st.model.set_sampling(tau, seed)
+    for step in range(2):
+        nxt = recipe.tokens_host(s, 0, step + 2)[1:]
+        g = sp.gpu_step(st, s, rec, tokens, nxt)
+        tag = " fp8 head sampled step %d" % step
+        sp.check_head_teacher_forced(s, tables, g, tag=tag, argmax=False)
+        sp.check_sampled_verification(s, g, tokens, tau, oracle.sample_key(seed, step), tag=tag)
+        tokens = np.concatenate([[g["tok"][0]], nxt]).astype(np.int32)
