@@ -62,6 +62,13 @@ def expert_bytes(s):
     return 3 * s.f * s.d * (2 if s.exp_fmt == "bf16" else 4)
 
 
+def head_bytes(s):
+    """LM-head table bytes read per step (bf16, or E4M3 codes + fp32 128x128 block scales)."""
+    if s.head_fmt == "fp8":
+        return s.V * s.d + ((s.V + 127) // 128) * ((s.d + 127) // 128) * 4
+    return s.V * s.d * 2
+
+
 def layer_bytes(s, L, slots):
     """Algorithmic bytes of one layer step: touched weights, KV read/write, activations in/out."""
     from synth import recipe
@@ -215,7 +222,10 @@ def cpu_baseline_stack(s, tokens_per_step):
     emb, head, gf = recipe.stack_tables_host(s, 0)
     h = oracle.embed(emb, recipe.tokens_host(s, 0, 0))
     t0 = time.perf_counter()
-    oracle.head(head, gf, h, s.eps, want_logits=False)
+    if s.head_fmt == "fp8":
+        oracle.head_fp8(head[0], head[1], gf, h, s.eps)
+    else:
+        oracle.head(head, gf, h, s.eps, want_logits=False)
     t_head = time.perf_counter() - t0
     t_layer = float(np.median(multi))
     t_step = s.n_layers * t_layer + t_head
@@ -250,6 +260,8 @@ def run_stack(s, args):
     t0 = time.perf_counter()
     st = harness.DeviceStack(s, seed=0)
     log("[bench] stack of %d layers built in %.1f s" % (n_layers, time.perf_counter() - t0))
+    if args.temperature > 0:
+        st.model.set_sampling(args.temperature, 0)
     K, W = args.steps, args.warmup
     drafts = np.stack([recipe.tokens_host(s, 0, i + 1)[1:] for i in range(W + K + 2)]).astype(np.int32)
     drafts_d = torch.from_numpy(drafts).to(dev)
@@ -285,7 +297,7 @@ def run_stack(s, args):
              for a, b in zip(stats0, stats1)]
     layer_launches = sum(b.launches - a.launches for a, b in zip(stats0, stats1))
     Lavg = 0.5 * (len0 + len1)
-    step_bytes = sum(layer_bytes(s, Lavg, sl) for sl in slots) + s.V * s.d * 2 + s.T * s.d * 2 + s.d * 4
+    step_bytes = sum(layer_bytes(s, Lavg, sl) for sl in slots) + head_bytes(s) + s.T * s.d * 2 + s.d * 4
     ms_step = ms / K
     tok_s = committed / (ms / 1e3)
 
@@ -324,7 +336,9 @@ def run_stack(s, args):
         "config": {"workload": s.name, "layers": n_layers, "T": s.T, "kv_len_start": len0, "kv_len_end": len1,
                    "experts": s.E, "top_k": s.top_k, "shared": s.n_shared, "d_model": s.d, "d_ff": s.f,
                    "vocab": s.V, "expert_pools": s.n_pools or n_layers, "weights": EXPERT_DESC[s.exp_fmt] +
-                   ", bf16 attention/router/embedding/head", "kv": s.kv_fmt,
+                   ", bf16 attention/router/embedding, %s head" % s.head_fmt, "kv": s.kv_fmt,
+                   "verification": ("sampled, temperature %g" % args.temperature) if args.temperature > 0
+                   else "greedy",
                    "compute": "bf16 MFMA operands, fp32 accumulation"},
         "tokens_per_step": round(committed / K, 4),
         "ms_per_step_dist": pct(per_step),
@@ -421,7 +435,8 @@ def process_starts(args, n):
     before this process touches the GPU) and returns their values."""
     vals = []
     cmd = [sys.executable, os.path.abspath(__file__), "--workload", args.workload, "--steps", str(args.steps),
-           "--warmup", str(args.warmup), "--no-cpu-baseline", "--starts", "1"]
+           "--warmup", str(args.warmup), "--no-cpu-baseline", "--starts", "1", "--head-fmt", args.head_fmt,
+           "--temperature", repr(args.temperature)]
     for i in range(n):
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
@@ -439,6 +454,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="C5", choices=["C2", "C3", "C4", "C5", "C3X", "C5X", "C3XK", "C5XK"])
     ap.add_argument("--layers", type=int, default=None, help="stack depth override (diagnostics only)")
+    ap.add_argument("--head-fmt", default="bf16", choices=["bf16", "fp8"],
+                    help="LM-head table format (the stack workload names bf16)")
+    ap.add_argument("--temperature", type=float, default=0.0,
+                    help="0: greedy verification; > 0: sampled verification at this temperature")
     ap.add_argument("--layer-reps", type=int, default=4)
     ap.add_argument("--starts", type=int, default=5,
                     help="process starts measured (this one and starts-1 child processes run before it)")
@@ -454,7 +473,7 @@ def main():
               "described in DESIGN.md); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     from synth.configs import BY_KEY
-    s = BY_KEY[args.workload]
+    s = BY_KEY[args.workload].with_(head_fmt=args.head_fmt)
     if s.n_layers > 1:
         args.steps = args.steps or 256
         args.warmup = args.warmup if args.warmup is not None else 8

@@ -93,6 +93,10 @@ __device__ __forceinline__ void row_state_merge(RowState& a, const RowState& b) 
 constexpr int kHeadLds = 8 * (8192 + kXPad) * 2 + 2 * kWaves * 64 * 4 * 4 + 1024;
 constexpr int kHeadMergeB = 4;           // per-workgroup states loaded together per thread in the grid merge
 
+__device__ __forceinline__ RowState rs_shfl_xor(const RowState& r, int m) {
+  return RowState{__shfl_xor(r.m, m), __shfl_xor(r.s, m), __shfl_xor(r.yb, m), __shfl_xor(r.yx, m),
+                  __shfl_xor(r.xd, m), __shfl_xor(r.ib, m), __shfl_xor(r.ix, m)};
+}
 // LDS slots of RowState for kThreads threads (7 arrays of kThreads words)
 __device__ __forceinline__ void rs_put(char* base, int i, const RowState& r) {
   float* f = reinterpret_cast<float*>(base);
@@ -112,16 +116,21 @@ __device__ __forceinline__ RowState rs_get(const char* base, int i) {
 // the bookkeeping.  cvb: LDS free for 7 * kThreads words; misc: 1 KiB of LDS.
 __device__ __forceinline__ void head_sample_tail(const HeadArgs& a, const RowState& mine, uint64_t key, char* cvb, float* misc) {
   const int T = a.T, V = a.V;
-  rs_put(cvb, threadIdx.x, mine);
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // the four lanes of a wave that hold one column, then the 8 waves (LDS)
+  RowState r0 = mine;
+  row_state_merge(r0, rs_shfl_xor(r0, 16));
+  row_state_merge(r0, rs_shfl_xor(r0, 32));
+  if (lane < 16) rs_put(cvb, w * 16 + lane, r0);
   __syncthreads();
   if ((int)threadIdx.x < T) {
     RowState r = rs_get(cvb, threadIdx.x);
-    for (int q = 1; q < kThreads / 16; ++q) row_state_merge(r, rs_get(cvb, q * 16 + threadIdx.x));
+    for (int q = 1; q < kWaves; ++q) row_state_merge(r, rs_get(cvb, q * 16 + threadIdx.x));
     // agent-scope stores pass this XCD's L2 (read by the merging workgroup on any XCD)
     float* dst = a.part + ((long long)blockIdx.x * 8 + threadIdx.x) * 8;
-    const float w[7] = {r.m, r.s, r.yb, r.yx, r.xd, __int_as_float(r.ib), __int_as_float(r.ix)};
+    const float wd[7] = {r.m, r.s, r.yb, r.yx, r.xd, __int_as_float(r.ib), __int_as_float(r.ix)};
 #pragma unroll
-    for (int k = 0; k < 7; ++k) __hip_atomic_store(dst + k, w[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int k = 0; k < 7; ++k) __hip_atomic_store(dst + k, wd[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   wg_release_begin();
   int* flag = reinterpret_cast<int*>(misc + 250);
@@ -146,22 +155,26 @@ __device__ __forceinline__ void head_sample_tail(const HeadArgs& a, const RowSta
     RowState r = row_state_empty();
     if (t < T) {
       for (int bb = b0; bb < (int)gridDim.x; bb += 64 * kHeadMergeB) {
-        float w[kHeadMergeB][7];
+        float wd[kHeadMergeB][7];
 #pragma unroll
         for (int i = 0; i < kHeadMergeB; ++i) {
           const int b = bb + 64 * i;
           const float* src = a.part + ((long long)min(b, (int)gridDim.x - 1) * 8 + t) * 8;
 #pragma unroll
-          for (int k = 0; k < 7; ++k) w[i][k] = __hip_atomic_load(src + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          for (int k = 0; k < 7; ++k) wd[i][k] = __hip_atomic_load(src + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
 #pragma unroll
         for (int i = 0; i < kHeadMergeB; ++i)
           if (bb + 64 * i < (int)gridDim.x)
-            row_state_merge(r, RowState{w[i][0], w[i][1], w[i][2], w[i][3], w[i][4], __float_as_int(w[i][5]),
-                                        __float_as_int(w[i][6])});
+            row_state_merge(r, RowState{wd[i][0], wd[i][1], wd[i][2], wd[i][3], wd[i][4], __float_as_int(wd[i][5]),
+                                        __float_as_int(wd[i][6])});
       }
     }
-    rs_put(cvb, threadIdx.x, r);
+    // the eight lanes of a wave that hold one row, then the 8 waves (LDS)
+    row_state_merge(r, rs_shfl_xor(r, 8));
+    row_state_merge(r, rs_shfl_xor(r, 16));
+    row_state_merge(r, rs_shfl_xor(r, 32));
+    if (lane < 8) rs_put(cvb, w * 8 + lane, r);
   }
   int* am = reinterpret_cast<int*>(misc + 200);
   int* tk = reinterpret_cast<int*>(misc + 208);
@@ -171,7 +184,7 @@ __device__ __forceinline__ void head_sample_tail(const HeadArgs& a, const RowSta
   __syncthreads();
   if ((int)threadIdx.x < T) {
     RowState r = rs_get(cvb, threadIdx.x);
-    for (int q = 1; q < kThreads / 8; ++q) row_state_merge(r, rs_get(cvb, q * 8 + threadIdx.x));
+    for (int q = 1; q < kWaves; ++q) row_state_merge(r, rs_get(cvb, q * 8 + threadIdx.x));
     am[threadIdx.x] = r.ib;
     rx[threadIdx.x] = r.ix;
     pa[threadIdx.x] = r.xd == -INFINITY ? 0.f : expf(r.xd - r.m) / r.s;   // p_i(next draft)
@@ -263,7 +276,11 @@ __global__ __launch_bounds__(kThreads, 1) void head_kernel(HeadArgs a) {
     __syncthreads();
   };
   constexpr int TK = tile_k(HF);
-  constexpr int D = HF == MK_FMT_FP8_B128 ? 8 : 16;       // tiles per wave per chunk
+  constexpr int D = 16;                                  // tiles per wave per chunk
+  // fp8 rows are half as long: two row tiles per workgroup at a time, four
+  // waves on each, so a wave still streams 16 KiB per chunk
+  constexpr int SPLIT = HF == MK_FMT_FP8_B128 ? 2 : 1;
+  constexpr int WPU = kWaves / SPLIT;
   const int RT = a.V / 16, KT = d / TK;
   const long long U = RT;
   const int u0 = (int)(U * blockIdx.x / gridDim.x), u1 = (int)(U * (blockIdx.x + 1) / gridDim.x);
@@ -310,13 +327,13 @@ __global__ __launch_bounds__(kThreads, 1) void head_kernel(HeadArgs a) {
       if (v > bv || (v == bv && id < bi)) { bv = v; bi = id; }
     }
   };
-  if (KT % kWaves == 0 && (KT / kWaves) % D == 0) {
+  if (KT % WPU == 0 && (KT / WPU) % D == 0) {
     // row tiles handed out at run time (workgroups b and b + nwg first, then
     // tickets), the 8 waves of a workgroup on one tile's k slices: workgroups
     // on faster XCDs take more tiles and the last tiles spread over the grid;
     // the rows are normalised while the first tile is on its way
     int* seq = reinterpret_cast<int*>(misc + 230);
-    run_stream_dyn<HF, false, D>(RT, KT, T, src, epi, red, a.dummy, a.tickets, seq, NoDone(), stage);
+    run_stream_dyn<HF, false, D, SPLIT>(RT, KT, T, src, epi, red, a.dummy, a.tickets, seq, NoDone(), stage);
   } else {
     stage();
     stream_units_wave<HF, false>(u0, u1, KT, T, src, epi, a.dummy);
@@ -326,19 +343,23 @@ __global__ __launch_bounds__(kThreads, 1) void head_kernel(HeadArgs a) {
     return;
   }
   // workgroup best per row: every thread holds a candidate for column lane % 16
+  // (the four lanes of a wave that hold a column, then the 8 waves through LDS)
   float* cv = reinterpret_cast<float*>(smem + 8 * XS * 2);
   int* ci = reinterpret_cast<int*>(cv + kThreads);
-  cv[threadIdx.x] = bv;
-  ci[threadIdx.x] = bi;
+  auto best_of = [](float& v, int& id, float ov, int oi) {
+    if (ov > v || (ov == v && oi < id)) { v = ov; id = oi; }
+  };
+  best_of(bv, bi, __shfl_xor(bv, 16), __shfl_xor(bi, 16));
+  best_of(bv, bi, __shfl_xor(bv, 32), __shfl_xor(bi, 32));
+  if (lane < 16) {
+    cv[w * 16 + lane] = bv;
+    ci[w * 16 + lane] = bi;
+  }
   __syncthreads();
   if (threadIdx.x < T) {
     float v = -INFINITY;
     int id = 0x7fffffff;
-    for (int r = 0; r < kThreads / 16; ++r) {
-      const float ov = cv[r * 16 + threadIdx.x];
-      const int oi = ci[r * 16 + threadIdx.x];
-      if (ov > v || (ov == v && oi < id)) { v = ov; id = oi; }
-    }
+    for (int r = 0; r < kWaves; ++r) best_of(v, id, cv[r * 16 + threadIdx.x], ci[r * 16 + threadIdx.x]);
     // agent-scope stores pass this XCD's L2, so the merging workgroup (on any
     // XCD) reads them from memory once the store has completed (waited for
     // below) -- no write-back of the whole L2
@@ -364,8 +385,8 @@ __global__ __launch_bounds__(kThreads, 1) void head_kernel(HeadArgs a) {
   if (!*flag) return;
   // grid-wide best per row: thread x takes column x % 8 of workgroups
   // x / 8, x / 8 + 64, ... (its loads issued together), then the 64 partial
-  // bests of a column are merged in LDS.  The result does not depend on the
-  // order (largest logit, lowest row id among equal ones).
+  // bests of a column are merged (shuffles, then LDS).  The result does not
+  // depend on the order (largest logit, lowest row id among equal ones).
   int* am = reinterpret_cast<int*>(misc + 200);
   int* tk = reinterpret_cast<int*>(misc + 208);
   {
@@ -383,23 +404,24 @@ __global__ __launch_bounds__(kThreads, 1) void head_kernel(HeadArgs a) {
           oi[i] = __hip_atomic_load(a.best_idx + b * 8 + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
 #pragma unroll
-        for (int i = 0; i < kHeadMergeB; ++i)
-          if (ov[i] > v || (ov[i] == v && oi[i] < id)) { v = ov[i]; id = oi[i]; }
+        for (int i = 0; i < kHeadMergeB; ++i) best_of(v, id, ov[i], oi[i]);
       }
     }
-    cv[threadIdx.x] = v;
-    ci[threadIdx.x] = id;
+    // the eight lanes of a wave that hold a row, then the 8 waves (LDS)
+    best_of(v, id, __shfl_xor(v, 8), __shfl_xor(id, 8));
+    best_of(v, id, __shfl_xor(v, 16), __shfl_xor(id, 16));
+    best_of(v, id, __shfl_xor(v, 32), __shfl_xor(id, 32));
+    if (lane < 8) {
+      cv[w * 8 + lane] = v;
+      ci[w * 8 + lane] = id;
+    }
     if ((int)threadIdx.x < T) tk[threadIdx.x] = a.tokens[threadIdx.x];
   }
   __syncthreads();
   if (threadIdx.x < T) {
     float v = -INFINITY;
     int id = 0x7fffffff;
-    for (int r = 0; r < kThreads / 8; ++r) {
-      const float ov = cv[r * 8 + threadIdx.x];
-      const int oi = ci[r * 8 + threadIdx.x];
-      if (ov > v || (ov == v && oi < id)) { v = ov; id = oi; }
-    }
+    for (int r = 0; r < kWaves; ++r) best_of(v, id, cv[r * 8 + threadIdx.x], ci[r * 8 + threadIdx.x]);
     am[threadIdx.x] = id;
     a.argmax[threadIdx.x] = id;
   }
