@@ -78,15 +78,18 @@ def layer_bytes(s, L, slots):
     return attn_bytes(s) + router_bytes(s) + slots * expert_bytes(s) + kv + act
 
 
+# The sources that make up the layer kernel and its launch configuration
+# (the head, pack and embedding units do not change it).
+LAYER_SOURCES = ("mk_common.h", "mk_device.h", "mk_layer_kernel.h", "mk_layer.hip", "mk_layer_kv8.hip", "mk_api.cpp")
+
+
 def kernel_source_hash():
-    import glob
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "decoder_megakernel_amd", "csrc")
-    for f in sorted(glob.glob(os.path.join(csrc, "*.h")) + glob.glob(os.path.join(csrc, "*.hip")) +
-                    glob.glob(os.path.join(csrc, "*.cpp"))):
-        h.update(os.path.basename(f).encode())
-        h.update(open(f, "rb").read())
+    for name in LAYER_SOURCES:
+        h.update(name.encode())
+        h.update(open(os.path.join(csrc, name), "rb").read())
     return h.hexdigest()
 
 
