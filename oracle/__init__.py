@@ -39,13 +39,15 @@ def build() -> None:
 class Cfg(ctypes.Structure):
     _fields_ = [("d", _i), ("n_h", _i), ("d_h", _i), ("d_c", _i), ("d_r", _i), ("E", _i),
                 ("top_k", _i), ("n_shared", _i), ("f", _i), ("attn_fmt", _i), ("exp_fmt", _i),
-                ("kv_fmt", _i), ("eps", ctypes.c_float), ("rope_base", ctypes.c_double)]
+                ("kv_fmt", _i), ("eps", ctypes.c_float), ("rope_base", ctypes.c_double),
+                ("q_lora", _i), ("kv_norm", _i)]
 
 
 class Weights(ctypes.Structure):
     _fields_ = [("gamma1", _vp), ("gamma2", _vp), ("wq", _vp), ("wdkv", _vp), ("wuk", _vp),
                 ("wuv", _vp), ("wo", _vp), ("wr", _vp), ("router_bias", _vp),
-                ("w1", _vp), ("w3", _vp), ("w2", _vp), ("s1", _vp), ("s3", _vp), ("s2", _vp)]
+                ("w1", _vp), ("w3", _vp), ("w2", _vp), ("s1", _vp), ("s3", _vp), ("s2", _vp),
+                ("wdq", _vp), ("wuq", _vp), ("gamma_q", _vp), ("gamma_kv", _vp)]
 
 
 class AttnTaps(ctypes.Structure):
@@ -115,7 +117,7 @@ def _p(a):
 
 def cfg_of(s: LayerShape) -> Cfg:
     return Cfg(s.d, s.n_h, s.d_h, s.d_c, s.d_r, s.E, s.top_k, s.n_shared, s.f, _FMT[s.attn_fmt],
-               _FMT[s.exp_fmt], _FMT[s.kv_fmt], s.eps, s.rope_base)
+               _FMT[s.exp_fmt], _FMT[s.kv_fmt], s.eps, s.rope_base, s.q_lora, 1 if s.kv_norm else 0)
 
 
 class _WeightsHolder:
@@ -138,12 +140,14 @@ class _WeightsHolder:
             for k, a in zip(("w1", "w3", "w2", "s1", "s3", "s2"), tup):
                 ptrs[k][slot] = keep(a)
         self.ptr_arrays.extend(ptrs.values())
-        self.struct = Weights(keep(w["gamma1"]), keep(w["gamma2"]), keep(w["wq"]), keep(w["wdkv"]),
+        self.struct = Weights(keep(w["gamma1"]), keep(w["gamma2"]), keep(w.get("wq")), keep(w["wdkv"]),
                               keep(w["wuk"]), keep(w["wuv"]), keep(w["wo"]), keep(w["wr"]),
                               keep(w.get("router_bias")),
                               ctypes.cast(ptrs["w1"], _vp), ctypes.cast(ptrs["w3"], _vp),
                               ctypes.cast(ptrs["w2"], _vp), ctypes.cast(ptrs["s1"], _vp),
-                              ctypes.cast(ptrs["s3"], _vp), ctypes.cast(ptrs["s2"], _vp))
+                              ctypes.cast(ptrs["s3"], _vp), ctypes.cast(ptrs["s2"], _vp),
+                              keep(w.get("wdq")), keep(w.get("wuq")), keep(w.get("gamma_q")),
+                              keep(w.get("gamma_kv")))
 
 
 def _chk(rc, what):

@@ -264,20 +264,32 @@ static int check_cfg(const orc_cfg* c, int T) {
     return -1;
   if (c->exp_fmt == ORC_MXFP4 && (c->d % 32 || c->f % 32)) return -1;
   if (c->kv_fmt != ORC_F32 && c->kv_fmt != ORC_BF16 && c->kv_fmt != ORC_FP8ROW) return -1;
+  if (c->q_lora < 0 || (c->kv_norm != 0 && c->kv_norm != 1)) return -1;
+  return 0;
+}
+static int check_lowrank(const orc_cfg* c, const orc_weights* w) {
+  if (c->q_lora > 0 && (!w->wdq || !w->wuq || !w->gamma_q)) return -1;
+  if (c->kv_norm && !w->gamma_kv) return -1;
+  if (c->q_lora == 0 && !w->wq) return -1;
   return 0;
 }
 
 /* ------------------------------------------------------------------ attention */
 int orc_attn_block(const orc_cfg* c, const orc_weights* w, const float* H, int T,
                    void* kv, int L, float* Hp, const orc_attn_taps* taps) {
-  if (check_cfg(c, T) || !w || !H || !kv || !Hp || L < 0) return -1;
-  const int d = c->d, nh = c->n_h, dh = c->d_h, dc = c->d_c, dr = c->d_r;
+  if (check_cfg(c, T) || !w || !H || !kv || !Hp || L < 0 || check_lowrank(c, w)) return -1;
+  const int d = c->d, nh = c->n_h, dh = c->d_h, dc = c->d_c, dr = c->d_r, ql = c->q_lora;
   const int qw = dh + dr, kvw = dc + dr;
   wmat WQ = mk_wmat(w->wq, c->attn_fmt, NULL, (long)nh * qw, d);
+  wmat WDQ = mk_wmat(w->wdq, c->attn_fmt, NULL, ql, d);
+  wmat WUQ = mk_wmat(w->wuq, c->attn_fmt, NULL, (long)nh * qw, ql);
   wmat WD = mk_wmat(w->wdkv, c->attn_fmt, NULL, kvw, d);
   wmat WO = mk_wmat(w->wo, c->attn_fmt, NULL, d, (long)nh * dh);
   const float scale = (float)(1.0 / sqrt((double)(dh + dr)));
 
+  float* cq = malloc(sizeof(float) * (ql > 0 ? ql : 1));
+  float* cqn = malloc(sizeof(float) * (ql > 0 ? ql : 1));
+  float* cn = malloc(sizeof(float) * dc);
   float* x = malloc(sizeof(float) * d);
   float* q = malloc(sizeof(float) * nh * qw);
   float* ckv = malloc(sizeof(float) * kvw);
@@ -289,8 +301,20 @@ int orc_attn_block(const orc_cfg* c, const orc_weights* w, const float* H, int T
   for (int i = 0; i < T; ++i) {
     const long pos = (long)L + i;
     rmsnorm(H + (long)i * d, w->gamma1, d, c->eps, x);
-    matvec(&WQ, x, q);
+    if (ql > 0) {
+      /* low-rank query: c^Q = W_DQ x, q-norm, q = W_UQ norm(c^Q) */
+      matvec(&WDQ, x, cq);
+      rmsnorm(cq, w->gamma_q, ql, c->eps, cqn);
+      matvec(&WUQ, cqn, q);
+    } else {
+      matvec(&WQ, x, q);
+    }
     matvec(&WD, x, ckv);
+    if (c->kv_norm) {
+      /* the latent is normalised before it is cached (the RoPE key is not) */
+      rmsnorm(ckv, w->gamma_kv, dc, c->eps, cn);
+      memcpy(ckv, cn, sizeof(float) * dc);
+    }
     for (int h = 0; h < nh; ++h) rope(q + (long)h * qw + dh, dr, pos, c->rope_base);
     rope(ckv + dc, dr, pos, c->rope_base);
     kv_put_row(kv, c->kv_fmt, kvw, pos, ckv);
@@ -356,7 +380,7 @@ int orc_attn_block(const orc_cfg* c, const orc_weights* w, const float* H, int T
       if (taps->o) memcpy(taps->o + (long)i * nh * dh, o, sizeof(float) * nh * dh);
     }
   }
-  free(x); free(q); free(ckv); free(qa); free(z); free(o); free(att);
+  free(x); free(q); free(ckv); free(qa); free(z); free(o); free(att); free(cq); free(cqn); free(cn);
   return 0;
 }
 
@@ -496,12 +520,14 @@ int orc_layer_step_f64(const orc_cfg* c, const orc_weights* w, const float* H, i
                        const void* kv, int L, const int32_t* force_sel,
                        double* out, double* hp_out, double* kv_new_f64, double* logits_out,
                        int32_t* sel_out) {
-  if (check_cfg(c, T) || !w || !H || !kv || !out || L < 0) return -1;
+  if (check_cfg(c, T) || !w || !H || !kv || !out || L < 0 || check_lowrank(c, w)) return -1;
   lut_init();
   const int d = c->d, nh = c->n_h, dh = c->d_h, dc = c->d_c, dr = c->d_r, E = c->E, k = c->top_k;
-  const int qw = dh + dr, kvw = dc + dr;
+  const int qw = dh + dr, kvw = dc + dr, ql = c->q_lora;
   const long npos = (long)L + T;
   wmat WQ = mk_wmat(w->wq, c->attn_fmt, NULL, (long)nh * qw, d);
+  wmat WDQ = mk_wmat(w->wdq, c->attn_fmt, NULL, ql, d);
+  wmat WUQ = mk_wmat(w->wuq, c->attn_fmt, NULL, (long)nh * qw, ql);
   wmat WD = mk_wmat(w->wdkv, c->attn_fmt, NULL, kvw, d);
   wmat WO = mk_wmat(w->wo, c->attn_fmt, NULL, d, (long)nh * dh);
   wmat WUK = mk_wmat(w->wuk, c->attn_fmt, NULL, (long)nh * dh, dc);
@@ -517,11 +543,24 @@ int orc_layer_step_f64(const orc_cfg* c, const orc_weights* w, const float* H, i
   double* ckv = malloc(sizeof(double) * kvw);
   float* rowf = malloc(sizeof(float) * kvw);
   float* rowr = malloc(sizeof(float) * kvw);
+  double* cq = malloc(sizeof(double) * (ql > 0 ? ql : 1));
+  double* cqn = malloc(sizeof(double) * (ql > 0 ? ql : 1));
+  double* cn = malloc(sizeof(double) * dc);
   for (int i = 0; i < T; ++i) {
     const long pos = (long)L + i;
     rmsnorm64(H + (long)i * d, w->gamma1, d, (double)c->eps, x);
-    matvec64(&WQ, x, q + (long)i * nh * qw);
+    if (ql > 0) {
+      matvec64(&WDQ, x, cq);
+      rmsnorm64d(cq, w->gamma_q, ql, (double)c->eps, cqn);
+      matvec64(&WUQ, cqn, q + (long)i * nh * qw);
+    } else {
+      matvec64(&WQ, x, q + (long)i * nh * qw);
+    }
     matvec64(&WD, x, ckv);
+    if (c->kv_norm) {
+      rmsnorm64d(ckv, w->gamma_kv, dc, (double)c->eps, cn);
+      memcpy(ckv, cn, sizeof(double) * dc);
+    }
     for (int h = 0; h < nh; ++h) rope64(q + (long)i * nh * qw + (long)h * qw + dh, dr, pos, c->rope_base);
     rope64(ckv + dc, dr, pos, c->rope_base);
     for (int m = 0; m < kvw; ++m) rowf[m] = (float)ckv[m];
@@ -627,6 +666,7 @@ int orc_layer_step_f64(const orc_cfg* c, const orc_weights* w, const float* H, i
     }
   }
   free(rows); free(x); free(q); free(ckv); free(rowf); free(rowr); free(kc); free(vv); free(o); free(att); free(hp);
+  free(cq); free(cqn); free(cn);
   free(xp); free(lg); free(a); free(b); free(y); free(sel);
   return rc;
 }

@@ -43,6 +43,13 @@
  *    The LM head may be fp8 with 128x128 block scales (the fp8 head named as a
  *    small item in "Why one GB300 ...", section "Three readings").
  *
+ *  - Layer variant: the low-rank query of the DeepSeek-V2 paper (section 2.1,
+ *    c^Q = W_DQ x, q = W_UQ c^Q) with the q-norm named by the pages'
+ *    "q-norm-rope-insert" kernel ("Why one GB300 ...", section "Where the
+ *    11.2 ms goes") as an RMSNorm of c^Q with its own gain, and an RMSNorm of
+ *    the latent before it is cached (the normalised compressed latents of the
+ *    DeepSeek-V2 architecture); the RoPE key is not normalised.
+ *
  * Readings where the pages are silent (each listed in the design notes):
  * eps = 1e-6; softmax scale 1/sqrt(d_h + d_r); RoPE base 10000 with the angle
  * p * theta_j formed in double; selection by logit with ties to the lower
@@ -77,6 +84,9 @@ typedef struct orc_cfg {
   int kv_fmt;     /* ORC_F32 | ORC_BF16 | ORC_FP8ROW (see orc_kv_row_bytes) */
   float eps;      /* RMSNorm epsilon */
   double rope_base;
+  int q_lora;     /* 0: one W_Q; > 0: low-rank query of this rank, c^Q = W_DQ x,
+                     q-norm (RMSNorm with gain gamma_q), q = W_UQ norm(c^Q) */
+  int kv_norm;    /* 1: RMSNorm with gain gamma_kv on the latent c before it is cached */
 } orc_cfg;
 
 /* Canonical (row-major) weights.  Expert slot e in [0, E) is routed expert e,
@@ -89,6 +99,9 @@ typedef struct orc_cfg {
  *   W_O   [d][n_h*d_h]
  *   W_R   [E][d], router_bias [E] or NULL
  *   W1,W3 [f][d], W2 [d][f]; fp8 scales [ceil(rows/128)][ceil(cols/128)] fp32
+ *   q_lora > 0 (the low-rank query of the DeepSeek-V2 paper, section 2.1, with
+ *   the q-norm of the pages' q-norm-rope-insert kernel): W_DQ [q_lora][d],
+ *   W_UQ [n_h*(d_h+d_r)][q_lora] in place of W_Q; kv_norm: gain [d_c].
  *   MXFP4 (OCP Microscaling Formats spec v1.0: E2M1 elements, one E8M0 scale
  *   per block of 32 consecutive elements): W1, W3, W2 as bytes [rows][cols/2],
  *   element 2j in the low nibble of byte j and 2j+1 in the high nibble; the
@@ -110,6 +123,10 @@ typedef struct orc_weights {
   const void* const* s1;    /* fp8: const float* scales; MXFP4: const uint8_t* E8M0 codes */
   const void* const* s3;
   const void* const* s2;
+  const void* wdq;          /* q_lora > 0: W_DQ [q_lora][d], W_UQ [n_h*(d_h+d_r)][q_lora] (attn_fmt), */
+  const void* wuq;          /*   gamma_q [q_lora] (W_Q is then unused)                                */
+  const float* gamma_q;
+  const float* gamma_kv;    /* kv_norm: [d_c] */
 } orc_weights;
 
 /* Optional intermediate outputs (any pointer may be NULL). */

@@ -35,6 +35,8 @@ class LayerShape:
     kv_capacity: int = 0       # 0 -> L + T
     n_pools: int = 0           # distinct routed-expert weight pools in a stack (0 = one per layer)
     head_fmt: str = "bf16"     # LM head: "bf16" | "fp8" (E4M3 + fp32 128x128 scales)
+    q_lora: int = 0            # 0: one W_Q; > 0: low-rank query W_DQ -> q-norm -> W_UQ of this rank
+    kv_norm: bool = False      # RMSNorm (gain gamma_kv) on the latent before it is cached
     eps: float = 1e-6
     rope_base: float = 10000.0
 

@@ -35,8 +35,11 @@ def _attn_tensor(shape_rc, fmt, seed, stream):
 
 
 def attn_shapes(s: LayerShape):
+    """Attention-format tensors of a layer; with a low-rank query, W_DQ and W_UQ
+    take the place of W_Q."""
+    q = {"wdq": (s.q_lora, s.d), "wuq": (s.n_h * s.qw, s.q_lora)} if s.q_lora else {"wq": (s.n_h * s.qw, s.d)}
     return {
-        "wq": (s.n_h * s.qw, s.d),
+        **q,
         "wdkv": (s.kvw, s.d),
         "wuk": (s.n_h, s.d_h, s.d_c),
         "wuv": (s.n_h, s.d_h, s.d_c),
@@ -101,6 +104,10 @@ def layer_weights_host(s: LayerShape, seed: int = 0, layer: int = 0, experts=Non
         "gamma1": normal_f32(s.d, seed, stream_id("gamma1", layer), GAIN_SIGMA, mean=1.0),
         "gamma2": normal_f32(s.d, seed, stream_id("gamma2", layer), GAIN_SIGMA, mean=1.0),
     }
+    if s.q_lora:
+        w["gamma_q"] = normal_f32(s.q_lora, seed, stream_id("gamma_q", layer), GAIN_SIGMA, mean=1.0)
+    if s.kv_norm:
+        w["gamma_kv"] = normal_f32(s.d_c, seed, stream_id("gamma_kv", layer), GAIN_SIGMA, mean=1.0)
     for name, shp in attn_shapes(s).items():
         w[name] = _attn_tensor(shp, s.attn_fmt, seed, stream_id(name, layer))
     w["router_bias"] = router_bias(s, seed, layer)

@@ -814,3 +814,63 @@ def test_fp8_head_against_an_explicit_dense_matrix():
     ref = x @ dense.T
     assert np.abs(lg - ref).max() <= 1e-5 * np.abs(ref).max()
     assert np.array_equal(am, ref.argmax(axis=1))
+
+
+# ---------------------------------------------------------------- low-rank query, q-norm, latent norm
+# The low-rank query of the DeepSeek-V2 paper (section 2.1: c^Q = W_DQ x,
+# q = W_UQ c^Q) with the q-norm the pages' "q-norm-rope-insert" kernel names
+# ("Why one GB300 doesn't beat 4x RTX PRO 6000 at single-stream decode",
+# section "Where the 11.2 ms goes"), and an RMSNorm of the cached latent.
+C0L = C0.with_(name="micro_lowrank", q_lora=48, kv_norm=True)
+C0QL = C0Q.with_(name="micro_fp8_lowrank", q_lora=64, kv_norm=True)
+
+
+@pytest.mark.parametrize("shape", [C0L, C0QL], ids=lambda s: s.name)
+def test_lowrank_layer_matches_fp64_unabsorbed_bruteforce(shape):
+    w, H, kv = fresh(shape)
+    kv64 = kv.copy()
+    out, taps = oracle.layer_step(shape, w, H, kv, shape.L)
+    ref = oracle.layer_step_f64(shape, w, H, kv64, shape.L, force_sel=taps["sel"])
+    assert normwise(out, ref["out"]) < 1e-5
+    assert normwise(taps["Hp"].astype(np.float64) - H, ref["Hp"] - H) < 1e-4
+
+
+def test_lowrank_query_with_identity_down_projection_is_the_single_wq_layer():
+    """W_DQ = I (rank d) and gamma_1 = 1: the normalised input x has unit RMS,
+    so the q-norm returns x * gamma_q and q = (W_UQ diag(gamma_q)) x -- the
+    one-W_Q layer with that matrix (up to eps / mean square ~ 1e-6)."""
+    s = C0.with_(name="micro_lowrank_identity", q_lora=C0.d)
+    w, H, kv = fresh(s)
+    w["gamma1"] = np.ones_like(w["gamma1"])
+    w["wdq"] = np.eye(s.d, dtype=np.float32)
+    s1 = C0
+    w1 = {k: v for k, v in w.items() if k not in ("wdq", "wuq", "gamma_q")}
+    w1["wq"] = (w["wuq"].astype(np.float64) * w["gamma_q"].astype(np.float64)[None, :]).astype(np.float32)
+    kv1 = kv.copy()
+    out, taps = oracle.layer_step(s, w, H, kv, s.L)
+    out1, taps1 = oracle.layer_step(s1, w1, H, kv1, s.L)
+    assert normwise(taps["q"], taps1["q"]) < 1e-5
+    assert normwise(taps["Hp"].astype(np.float64) - H, taps1["Hp"].astype(np.float64) - H) < 1e-4
+    assert normwise(out, out1) < 1e-5
+    # dropping the q-norm's gain is far outside that
+    w2 = dict(w, gamma_q=np.ones_like(w["gamma_q"]))
+    _, taps2 = oracle.layer_step(s, w2, H, kv.copy(), s.L)
+    assert normwise(taps2["q"], taps1["q"]) > 3e-2
+
+
+def test_latent_norm_gives_unit_rms_rows_before_the_gain_and_leaves_the_key():
+    s = C0.with_(name="micro_kvnorm", kv_norm=True)
+    w, H, kv = fresh(s)
+    s0 = C0
+    kv0 = kv.copy()
+    oracle.layer_step(s, w, H, kv, s.L)
+    oracle.layer_step(s0, {k: v for k, v in w.items() if k != "gamma_kv"}, H, kv0, s.L)
+    c = kv[s.L:s.L + s.T, : s.d_c].astype(np.float64) / w["gamma_kv"].astype(np.float64)
+    c0 = kv0[s.L:s.L + s.T, : s.d_c].astype(np.float64)
+    ms0 = (c0 * c0).mean(axis=1)
+    # closed form: RMS of c / gamma = sqrt(ms / (ms + eps)) for the un-normalised mean square ms
+    assert np.allclose(np.sqrt((c * c).mean(axis=1)), np.sqrt(ms0 / (ms0 + s.eps)), rtol=1e-6)
+    # the RoPE key is not normalised; the latent is the un-normalised one rescaled
+    assert np.array_equal(kv[s.L:s.L + s.T, s.d_c:], kv0[s.L:s.L + s.T, s.d_c:])
+    ratio = c / c0
+    assert np.allclose(ratio, ratio[:, :1], rtol=1e-5)
