@@ -46,7 +46,9 @@ def log(*a):
 
 def attn_bytes(s):
     e = 2 if s.attn_fmt == "bf16" else 4
-    return e * (s.n_h * s.qw * s.d + s.kvw * s.d + 2 * s.n_h * s.d_h * s.d_c + s.d * s.n_h * s.d_h)
+    # the query projection: W_Q, or W_DQ and W_UQ (+ the q-norm gain) with a low-rank query
+    q = s.q_lora * s.d + s.n_h * s.qw * s.q_lora + 2 * s.q_lora if s.q_lora else s.n_h * s.qw * s.d
+    return e * (q + s.kvw * s.d + 2 * s.n_h * s.d_h * s.d_c + s.d * s.n_h * s.d_h) + (4 * s.d_c if s.kv_norm else 0)
 
 
 def router_bytes(s):
@@ -80,7 +82,8 @@ def layer_bytes(s, L, slots):
 
 # The sources that make up the layer kernel and its launch configuration
 # (the head, pack and embedding units do not change it).
-LAYER_SOURCES = ("mk_common.h", "mk_device.h", "mk_layer_kernel.h", "mk_layer.hip", "mk_layer_kv8.hip", "mk_api.cpp")
+LAYER_SOURCES = ("mk_common.h", "mk_device.h", "mk_layer_kernel.h", "mk_layer.hip", "mk_layer_kv8.hip",
+                 "mk_layer_lr.hip", "mk_api.cpp")
 
 
 def kernel_source_hash():
@@ -455,7 +458,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--workload", default="C5", choices=["C2", "C3", "C4", "C5", "C3X", "C5X", "C3XK", "C5XK"])
+    ap.add_argument("--workload", default="C5", choices=["C2", "C3", "C4", "C5", "C3X", "C5X", "C3XK", "C5XK", "C3Q"])
     ap.add_argument("--layers", type=int, default=None, help="stack depth override (diagnostics only)")
     ap.add_argument("--head-fmt", default="bf16", choices=["bf16", "fp8"],
                     help="LM-head table format (the stack workload names bf16)")

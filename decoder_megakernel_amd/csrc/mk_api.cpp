@@ -42,10 +42,13 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 struct Dims {
   int d, nh, dh, dc, dr, qw, kvw, nq, E, topk, nshared, f;
   int af, ef, kf;
+  int ql, kvn;       // low-rank query rank (0: one W_Q), latent norm
+  int nqp() const { return ql > 0 ? ql : nq; }   // rows of the first projection's query part
 };
 
 // s_q: the projection's split-K factor of the schedule (0 when not known yet).
 LayerKernelFn kernel_of(const Dims& D, int s_q = 0, int nwg = 0) {
+  if (D.ql > 0) return layer_kernel_lowrank_for(D.af, D.ef, D.kf, D.dc, D.dr);
   return layer_kernel_for(D.af, D.ef, D.kf, D.d, D.nh, D.dh, D.dc, D.dr, D.E, D.topk, D.nshared, D.f, s_q, nwg);
 }
 
@@ -54,6 +57,7 @@ Dims dims_of(const mk_layer_config* c) {
   D.d = c->d_model; D.nh = c->n_heads; D.dh = c->d_head; D.dc = c->d_latent; D.dr = c->d_rope;
   D.qw = D.dh + D.dr; D.kvw = D.dc + D.dr; D.nq = D.nh * D.qw; D.E = c->n_experts; D.topk = c->top_k;
   D.nshared = c->n_shared; D.f = c->d_ff; D.af = c->attn_format; D.ef = c->expert_format; D.kf = c->kv_format;
+  D.ql = c->q_lora_rank; D.kvn = c->kv_norm;
   return D;
 }
 
@@ -67,6 +71,10 @@ int check_cfg(const mk_layer_config* c) {
   if (D.af < 0 || D.af > 1 || D.ef < 0 || D.ef > 3 || !(D.kf == MK_FMT_F32 || D.kf == MK_FMT_BF16 || D.kf == MK_FMT_FP8_ROW))
     return fail(MK_ERR_INVALID_ARG, "unknown format");
   if (c->has_router_bias != 0 && c->has_router_bias != 1) return fail(MK_ERR_INVALID_ARG, "has_router_bias must be 0 or 1");
+  if (D.ql < 0 || (D.kvn != 0 && D.kvn != 1)) return fail(MK_ERR_INVALID_ARG, "q_lora_rank must be >= 0 and kv_norm 0 or 1");
+  if (D.ql > 0 && (D.af != MK_FMT_BF16 || D.ql % 32 || D.ql > D.d))
+    return fail(MK_ERR_UNSUPPORTED_SHAPE, "a low-rank query needs bf16 attention and a rank that is a multiple of 32, <= d_model");
+  if (D.kvn && D.ql == 0) return fail(MK_ERR_UNSUPPORTED_SHAPE, "the latent norm is built with the low-rank query only");
   if (!(c->rms_eps >= 0.f) || !(c->rope_base > 0.f)) return fail(MK_ERR_INVALID_ARG, "bad eps or rope base");
   const bool f32 = D.af == MK_FMT_F32 && D.ef == MK_FMT_F32 && D.kf == MK_FMT_F32;
   const bool bf = D.af == MK_FMT_BF16 && (D.kf == MK_FMT_BF16 || D.kf == MK_FMT_FP8_ROW) &&
@@ -134,6 +142,11 @@ int packed_bytes(const mk_layer_config* c, int tensor, size_t* out) {
     case MK_T_WO: b = tiles_bytes(D.d, D.nh * D.dh, D.af); break;
     case MK_T_WR: b = tiles_bytes(D.E, D.d, D.af); break;
     case MK_T_EXPERT: b = exp_w13(D) + exp_w2(D) + exp_scales(D); break;
+    case MK_T_WDQ:
+    case MK_T_WUQ:
+      if (D.ql == 0) return fail(MK_ERR_INVALID_ARG, "W_DQ / W_UQ need q_lora_rank > 0");
+      b = tensor == MK_T_WDQ ? tiles_bytes(D.ql, D.d, D.af) : tiles_bytes(D.nq, D.ql, D.af);
+      break;
     default: return fail(MK_ERR_INVALID_ARG, "unknown tensor id %d", tensor);
   }
   *out = (size_t)b;
@@ -192,7 +205,7 @@ int device_info(int dev, DevInfo* di, LayerKernelFn fn) {
 
 struct WsLayout {
   size_t qkv_part, qrope, qabs, att_part, att_ml, z, o, hp, route_sel, route_gate, route_cand, logits, hbuf,
-      ybuf, dummy,
+      ybuf, dummy, qbuf,
       total;
 };
 struct StLayout {
@@ -207,7 +220,7 @@ WsLayout ws_layout(const Dims& D, const Schedule& s) {
   const int nqt = (T * D.nh + 15) / 16;
   const int units = std::max(s.nwg, nqt);
   const int slots = std::min(D.E, T * D.topk) + D.nshared;
-  w.qkv_part = take((size_t)s.s_q * T * (D.nq + D.kvw) * 4);
+  w.qkv_part = take((size_t)s.s_q * T * (D.nqp() + D.kvw) * 4);
   w.qrope = take((size_t)T * D.nh * D.dr * 4);
   w.qabs = take((size_t)T * D.nh * D.dc * 4);
   w.att_part = take((size_t)units * 16 * D.dc * 4);
@@ -222,6 +235,7 @@ WsLayout ws_layout(const Dims& D, const Schedule& s) {
   w.hbuf = take((size_t)slots * T * D.f * 4);
   w.ybuf = take((size_t)slots * T * D.d * 4);
   w.dummy = take(32768);
+  w.qbuf = D.ql > 0 ? take((size_t)T * D.nq * 4) : 0;
   w.total = off;
   return w;
 }
@@ -255,6 +269,7 @@ void bind_workspace(LayerParams& p, const WsLayout& wl, char* ws) {
   p.hbuf = (float*)(ws + wl.hbuf);
   p.ybuf = (float*)(ws + wl.ybuf);
   p.dummy = (const uint8_t*)(ws + wl.dummy);
+  p.qbuf = wl.qbuf ? (float*)(ws + wl.qbuf) : nullptr;
 }
 
 // ------------------------------------------------------------------ static scratch
@@ -286,7 +301,7 @@ Schedule make_schedule(const Dims& D, int nwg) {
   s.nwg = nwg;
   s.grid_min = 0;
   const int KTa = D.d / tile_k(D.af);
-  s.s_q = choose_split(D.nq / 16 + (D.kvw + 15) / 16, KTa, nwg);
+  s.s_q = choose_split(D.nqp() / 16 + (D.kvw + 15) / 16, KTa, nwg);
   return s;
 }
 
@@ -432,6 +447,14 @@ int mk_pack_tensor(const mk_layer_config* cfg, int tensor, const void* src, void
     case MK_T_WUV: rc = launch_pack(src, f, D.nh, D.dh, D.dc, (long long)D.dh * D.dc, D.dc, 1, dst, 1024, 0, s); break;
     case MK_T_WO: rc = launch_pack(src, f, 1, D.d, D.nh * D.dh, 0, D.nh * D.dh, 1, dst, 1024, 0, s); break;
     case MK_T_WR: rc = launch_pack(src, f, 1, D.E, D.d, 0, D.d, 1, dst, 1024, 0, s); break;
+    case MK_T_WDQ:
+      if (D.ql == 0) return fail(MK_ERR_INVALID_ARG, "W_DQ needs q_lora_rank > 0");
+      rc = launch_pack(src, f, 1, D.ql, D.d, 0, D.d, 1, dst, 1024, 0, s);
+      break;
+    case MK_T_WUQ:
+      if (D.ql == 0) return fail(MK_ERR_INVALID_ARG, "W_UQ needs q_lora_rank > 0");
+      rc = launch_pack(src, f, 1, D.nq, D.ql, 0, D.ql, 1, dst, 1024, 0, s);
+      break;
     default: return fail(MK_ERR_INVALID_ARG, "tensor %d is not packed with mk_pack_tensor", tensor);
   }
   if (rc) return fail(MK_ERR_HIP, "pack launch failed: %s", hipGetErrorString((hipError_t)rc));
@@ -477,8 +500,11 @@ int mk_layer_init(const mk_layer_config* cfg, const mk_layer_weights* w, void* s
   int rc = check_cfg(cfg);
   if (rc) return rc;
   if (!w || !state_dev || !workspace_dev) return fail(MK_ERR_INVALID_ARG, "null weights, state or workspace");
-  if (!w->gamma1 || !w->gamma2 || !w->wq || !w->wdkv || !w->wuk || !w->wuv || !w->wo || !w->wr || !w->experts)
+  if (!w->gamma1 || !w->gamma2 || !w->wdkv || !w->wuk || !w->wuv || !w->wo || !w->wr || !w->experts)
     return fail(MK_ERR_INVALID_ARG, "null weight tensor");
+  if (cfg->q_lora_rank > 0 ? (!w->wdq || !w->wuq || !w->gamma_q) : !w->wq)
+    return fail(MK_ERR_INVALID_ARG, "null query projection (W_Q, or W_DQ, W_UQ and gamma_q with a low-rank query)");
+  if (cfg->kv_norm && !w->gamma_kv) return fail(MK_ERR_INVALID_ARG, "kv_norm needs gamma_kv");
   if ((cfg->has_router_bias != 0) != (w->router_bias != nullptr))
     return fail(MK_ERR_INVALID_ARG, "router_bias must be given iff has_router_bias");
   const Dims D = dims_of(cfg);
@@ -531,6 +557,8 @@ int mk_layer_init(const mk_layer_config* cfg, const mk_layer_weights* w, void* s
   p.wq = (const uint8_t*)w->wq; p.wdkv = (const uint8_t*)w->wdkv; p.wuk = (const uint8_t*)w->wuk;
   p.wuv = (const uint8_t*)w->wuv; p.wo = (const uint8_t*)w->wo; p.wr = (const uint8_t*)w->wr;
   p.rbias = w->router_bias;
+  p.ql = D.ql; p.kv_norm = D.kvn;
+  p.wdq = (const uint8_t*)w->wdq; p.wuq = (const uint8_t*)w->wuq; p.gq = w->gamma_q; p.gkv = w->gamma_kv;
   p.experts = (const uint8_t* const*)(L->state + L->sl.experts);
   p.exp_w13_bytes = exp_w13(D);
   p.exp_w2_bytes = exp_w2(D);
@@ -619,11 +647,13 @@ int mk_debug_tap(mk_layer* L, int tap, void* host_dst, size_t bytes, void* strea
     case 0: {
       // Q with rotated q^R: rebuild [T][nh][qw] from the split-K partials and the rotated part
       if (bytes < (size_t)T * D.nh * D.qw * 4) return fail(MK_ERR_INVALID_ARG, "tap buffer too small");
-      const int S = L->sch.s_q, nrow = D.nq + D.kvw;
+      // (a low-rank query is kept whole in qbuf: one "partial" of row length nq)
+      const bool lr = D.ql > 0;
+      const int S = lr ? 1 : L->sch.s_q, nrow = lr ? D.nq : D.nq + D.kvw;
       std::string tmp((size_t)S * T * nrow * 4, '\0');
       std::string rq((size_t)T * D.nh * D.dr * 4, '\0');
       HIP_OK(hipStreamSynchronize((hipStream_t)stream));
-      HIP_OK(hipMemcpy(&tmp[0], p.qkv_part, tmp.size(), hipMemcpyDeviceToHost));
+      HIP_OK(hipMemcpy(&tmp[0], lr ? p.qbuf : p.qkv_part, tmp.size(), hipMemcpyDeviceToHost));
       HIP_OK(hipMemcpy(&rq[0], p.qrope, rq.size(), hipMemcpyDeviceToHost));
       const float* pt = (const float*)tmp.data();
       const float* pr = (const float*)rq.data();

@@ -117,12 +117,19 @@ struct LayerParams {
   const uint8_t* wo;
   const uint8_t* wr;
   const float* rbias;
+  // low-rank query (ql > 0): W_DQ [ql][d], q-norm gain, W_UQ [nq][ql]; latent norm gain (kv_norm)
+  int ql, kv_norm;
+  const uint8_t* wdq;
+  const uint8_t* wuq;
+  const float* gq;
+  const float* gkv;
   const uint8_t* const* experts;   // [E + nshared] packed expert blocks
   // packed expert block geometry (bytes)
   long long exp_w13_bytes;         // interleaved W1/W3 tiles
   long long exp_w2_bytes;          // W2 tiles
   // workspace
-  float* qkv_part;         // [s_q][T][nq + kvw]
+  float* qkv_part;         // [s_q][T][nq + kvw] (low-rank query: [s_q][T][ql + kvw])
+  float* qbuf;             // low-rank query: q [T][nq]
   float* qrope;            // [T][nh][dr]
   float* qabs;             // [T][nh][dc]
   float* att_part;         // [units][16][dc]

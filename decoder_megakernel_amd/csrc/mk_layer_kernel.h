@@ -164,6 +164,25 @@ struct RowStager {
         v[t][c] = ldg(reinterpret_cast<const f32x4*>(src + (long long)min(t, T - 1) * K + 4 * i));
     }
   }
+  // The rows as sums of S split-K partials: row t element k = sum_s
+  // part[(s T + t) stride + k] (the S loads of an element are issued together).
+  __device__ __forceinline__ void issue_sum(const float* part, int S, int T, long long stride, int K,
+                                            const float* gamma) {
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int n4 = K / 4;
+#pragma unroll
+    for (int c = 0; c < kRowCh; ++c) {
+      const int i = min(w * 64 + lane + c * kWaves * 64, n4 - 1);
+      if constexpr (NORM) gm[c] = ldg(reinterpret_cast<const f32x4*>(gamma + 4 * i));
+#pragma unroll
+      for (int t = 0; t < kMaxT; ++t) {
+        f32x4 a = {0.f, 0.f, 0.f, 0.f};
+        for (int s = 0; s < S; ++s)
+          a += ldg(reinterpret_cast<const f32x4*>(part + ((long long)s * T + min(t, T - 1)) * stride + 4 * i));
+        v[t][c] = a;
+      }
+    }
+  }
   __device__ __forceinline__ void finish(int T, int K, A* xs, A* lo, int XS, float eps, bool tr = false) {
     extern __shared__ __attribute__((aligned(16))) char dyn_lds[];
     float* part = reinterpret_cast<float*>(dyn_lds + kNormLdsOff);
@@ -263,7 +282,8 @@ __device__ __forceinline__ const A* b_lane(const A* xs, int XS, int T, int TK) {
 }
 
 // ------------------------------------------------------------------ P0
-template <int AF>
+// LR (low-rank query): the query rows are W_DQ's ql rows (c^Q) instead of W_Q's.
+template <int AF, bool LR = false>
 __device__ __forceinline__ void phase_qkv(const LayerParams& p, char* smem) {
   typedef typename Act<AF>::T A;
   constexpr int TK = tile_k(AF);
@@ -271,12 +291,13 @@ __device__ __forceinline__ void phase_qkv(const LayerParams& p, char* smem) {
   LdsPlan lp(p, sizeof(A));
   A* xs = reinterpret_cast<A*>(smem);
   float* red = reinterpret_cast<float*>(smem + lp.xb);
-  const int RTq = p.nq / 16, RTkv = (p.kvw + 15) / 16, KT = p.d / TK, S = p.sch.s_q, NT = KT / S;
+  const int nqp = LR ? p.ql : p.nq;
+  const int RTq = nqp / 16, RTkv = (p.kvw + 15) / 16, KT = p.d / TK, S = p.sch.s_q, NT = KT / S;
   const int U = (RTq + RTkv) * S;
   int u0, u1;
   split_range(U, gridDim.x, blockIdx.x, u0, u1);
   const A* bl = b_lane<A>(xs, XS, T, TK);
-  const int nrow = p.nq + p.kvw;
+  const int nrow = nqp + p.kvw;
   struct Src {
     const uint8_t* wq; const uint8_t* wd; int RTq, KT, S, NT; const A* bl;
     __device__ const uint8_t* base(int u) const {
@@ -287,9 +308,9 @@ __device__ __forceinline__ void phase_qkv(const LayerParams& p, char* smem) {
     __device__ const A* bbase(int u) const { return bl + (u % S) * NT * TK; }
     __device__ const float* sbase(int) const { return nullptr; }
     __device__ const float* sbase2(int) const { return nullptr; }
-  } src{p.wq, p.wdkv, RTq, KT, S, NT, bl};
+  } src{LR ? p.wdq : p.wq, p.wdkv, RTq, KT, S, NT, bl};
   float* part = p.qkv_part;
-  const int nq = p.nq, kvw = p.kvw;
+  const int nq = nqp, kvw = p.kvw;
   const float* rsc = rsc_lds();       // the staged rows are h * gamma: scale by 1/rms
   auto epi = [=](int u, int row, int col, float v, float) {
     v *= rsc[col];
@@ -315,6 +336,40 @@ __device__ __forceinline__ void phase_qkv(const LayerParams& p, char* smem) {
   rs.finish(T, p.d, xs, (A*)nullptr, XS, p.eps, p.trace != nullptr);
   trace_x(p, 5);
   stream_units_wg_primed<AF, false, false, kPrimeTiles>(u0, u1, NT, T, src, epi, red, p.dummy, ck, pr);
+}
+
+// ------------------------------------------------------------------ P0b (low-rank query)
+// q = W_UQ (q-norm(c^Q)): every workgroup sums the split-K partials of c^Q for
+// the T rows, stages c^Q * gamma_q into LDS with 1/rms per row (as RMSNorm-1
+// is staged), then the row tiles of W_UQ are streamed over the grid and each
+// product is scaled by its row's 1/rms into qbuf [T][nq].
+template <int AF>
+__device__ __forceinline__ void phase_uq(const LayerParams& p, char* smem) {
+  typedef typename Act<AF>::T A;
+  constexpr int TK = tile_k(AF);
+  const int T = p.T, K = p.ql, XS = K + kXPad;
+  LdsPlan lp(p, sizeof(A));
+  A* xs = reinterpret_cast<A*>(smem);
+  float* red = reinterpret_cast<float*>(smem + lp.xb);
+  const int RT = p.nq / 16, KT = K / TK;
+  int u0, u1;
+  split_range(RT, gridDim.x, blockIdx.x, u0, u1);
+  const A* bl = b_lane<A>(xs, XS, T, TK);
+  struct Src {
+    const uint8_t* w; int KT; const A* bl;
+    __device__ const uint8_t* base(int u) const { return w + (long long)u * KT * 1024; }
+    __device__ const A* bbase(int) const { return bl; }
+    __device__ const float* sbase(int) const { return nullptr; }
+    __device__ const float* sbase2(int) const { return nullptr; }
+  } src{p.wuq, KT, bl};
+  float* q = p.qbuf;
+  const int nq = p.nq;
+  const float* rsc = rsc_lds();
+  auto epi = [=](int u, int row, int col, float v, float) { q[(long long)col * nq + u * 16 + row] = v * rsc[col]; };
+  RowStager<A, true> rs;
+  rs.issue_sum(p.qkv_part, p.sch.s_q, T, p.ql + p.kvw, K, p.gq);
+  rs.finish(T, K, xs, (A*)nullptr, XS, p.eps);
+  stream_units_wg<AF, false, false>(u0, u1, KT, T, src, epi, red, p.dummy);
 }
 
 // ------------------------------------------------------------------ P1
@@ -358,11 +413,14 @@ __device__ __forceinline__ void rope_cs(long long pos, int pidx, double step, fl
   s = (float)sn;
 }
 
-template <int KF>
 // Work items are spread over the threads [tid0, tid0 + nthreads) of the grid
-// given by the caller (`tid` is this thread's index in that range).
+// given by the caller (`tid` is this thread's index in that range).  LR: the
+// layer has a low-rank query, which P0b left whole in qbuf; the first
+// projection's partials then hold [c^Q | c | k_R] rows of ql + kvw values.
+template <int KF, bool LR = false>
 __device__ __forceinline__ void phase_rope_kv(const LayerParams& p, int L, int tid, int nthreads) {
-  const int T = p.T, S = p.sch.s_q, nrow = p.nq + p.kvw, dr2 = p.dr / 2;
+  const int T = p.T, S = p.sch.s_q, dr2 = p.dr / 2;
+  const int kvoff = LR ? p.ql : p.nq, nrow = kvoff + p.kvw;    // where c starts in a partial row
   const int per_t = p.dc + dr2 + p.nh * dr2;
   const float* part = p.qkv_part;
   auto psum = [&](int t, int idx) {
@@ -370,11 +428,16 @@ __device__ __forceinline__ void phase_rope_kv(const LayerParams& p, int L, int t
     for (int s = 0; s < S; ++s) v += ldg(part + ((long long)s * T + t) * nrow + idx);
     return v;
   };
-  if constexpr (KF == MK_FMT_FP8_ROW) {
+  // element idx of row t's query [n_h][d_h + d_r]
+  auto qval = [&](int t, int idx) { return LR ? ldg(p.qbuf + (long long)t * p.nq + idx) : psum(t, idx); };
+  if constexpr (KF == MK_FMT_FP8_ROW || LR) {
     // One wave per new cache row (the thread range is whole waves): each lane
-    // forms runs of 8 consecutive values (latent, or 4 rotated key pairs), the
-    // wave takes the row maximum, the row's scale is the smallest power of two
-    // 2^e with max <= 448 * 2^e, and each value is stored as E4M3(v / 2^e).
+    // forms runs of 8 consecutive values (latent, or 4 rotated key pairs).
+    // With the latent norm the wave first takes the latent's mean square and
+    // scales it by 1/rms and the gain.  fp8 rows: the wave takes the row
+    // maximum, the row's scale is the smallest power of two 2^e with
+    // max <= 448 * 2^e, and each value is stored as E4M3(v / 2^e); fp32 / bf16
+    // rows store the values.
     const int lane = tid & 63, wv = tid >> 6, nwv = nthreads >> 6;
     const int rb = kv_row_bytes(KF, p.kvw), nrun = p.kvw / 8;
     for (int t = wv; t < T; t += nwv) {
@@ -389,7 +452,7 @@ __device__ __forceinline__ void phase_rope_kv(const LayerParams& p, int L, int t
         if (c < nrun) {
           f32x4 a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
           for (int s = 0; s < S; ++s) {
-            const float* src = part + ((long long)s * T + t) * nrow + p.nq + m0;
+            const float* src = part + ((long long)s * T + t) * nrow + kvoff + m0;
             a += ldg(reinterpret_cast<const f32x4*>(src));
             b += ldg(reinterpret_cast<const f32x4*>(src + 4));
           }
@@ -408,10 +471,56 @@ __device__ __forceinline__ void phase_rope_kv(const LayerParams& p, int L, int t
               v[i][2 * k + 1] = x0 * sn + x1 * cs;
             }
           }
-#pragma unroll
-          for (int k = 0; k < 8; ++k) amax = fmaxf(amax, fabsf(v[i][k]));
         }
       }
+      if (LR && p.kv_norm) {
+        // RMSNorm of the latent (runs below d_c), as 1 / sqrt(mean square + eps) times the gain
+        float ss = 0.f;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          if (8 * (lane + 64 * i) < p.dc)
+#pragma unroll
+            for (int k = 0; k < 8; ++k) ss += v[i][k] * v[i][k];
+        ss = wave_sum(ss);
+        const float r = 1.0f / sqrtf(ss / (float)p.dc + p.eps);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int m0 = 8 * (lane + 64 * i);
+          if (m0 < p.dc) {
+            const f32x4 g0 = ldg(reinterpret_cast<const f32x4*>(p.gkv + m0));
+            const f32x4 g1 = ldg(reinterpret_cast<const f32x4*>(p.gkv + m0 + 4));
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              v[i][k] = (v[i][k] * r) * g0[k];
+              v[i][k + 4] = (v[i][k + 4] * r) * g1[k];
+            }
+          }
+        }
+      }
+      if constexpr (KF != MK_FMT_FP8_ROW) {
+        // fp32 / bf16 rows: the values themselves
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int c = lane + 64 * i;
+          if (c < nrun) {
+            if constexpr (KF == MK_FMT_F32) {
+              float* dst = reinterpret_cast<float*>(p.kv) + pos * p.kvw + 8 * c;
+              *reinterpret_cast<f32x4*>(dst) = f32x4{v[i][0], v[i][1], v[i][2], v[i][3]};
+              *reinterpret_cast<f32x4*>(dst + 4) = f32x4{v[i][4], v[i][5], v[i][6], v[i][7]};
+            } else {
+              bf16x8 o;
+#pragma unroll
+              for (int k = 0; k < 8; ++k) o[k] = (__bf16)v[i][k];
+              *reinterpret_cast<bf16x8*>(reinterpret_cast<__bf16*>(p.kv) + pos * p.kvw + 8 * c) = o;
+            }
+          }
+        }
+        continue;
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int k = 0; k < 8; ++k) amax = fmaxf(amax, fabsf(v[i][k]));
 #pragma unroll
       for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
       int e = 0;
@@ -445,7 +554,7 @@ __device__ __forceinline__ void phase_rope_kv(const LayerParams& p, int L, int t
       const int t = it / per_q, q = it - t * per_q, h = q / dr2, pi = q - h * dr2;
       const long long pos = (long long)L + t;
       const int src = h * p.qw + p.dh + 2 * pi;
-      const float x0 = psum(t, src), x1 = psum(t, src + 1);
+      const float x0 = qval(t, src), x1 = qval(t, src + 1);
       float c, sn;
       rope_cs(pos, pi, p.rope_step, c, sn);
       p.qrope[((long long)t * p.nh + h) * p.dr + 2 * pi] = x0 * c - x1 * sn;
@@ -522,12 +631,14 @@ __device__ __forceinline__ f32x4 make_b<MK_FMT_F32>(const f32x4& a, const f32x4&
 template <>
 __device__ __forceinline__ bf16x8 make_b<MK_FMT_BF16>(const f32x4& a, const f32x4& b) { return to_bf16x8(a, b); }
 
-// q~[t][h][m] = sum_e W_UK[h][e][m] q^C[t][h][e]  (wave-level units: one head, 16 m-rows, all of K)
-template <int AF>
+// q~[t][h][m] = sum_e W_UK[h][e][m] q^C[t][h][e]  (wave-level units: one head, 16 m-rows, all of K).
+// LR: q^C comes whole from qbuf (low-rank query) instead of the split-K partials.
+template <int AF, bool LR = false>
 __device__ __forceinline__ void phase_absorb(const LayerParams& p) {
   constexpr int TK = tile_k(AF);
   constexpr int EPL = TK / 4;          // elements per lane per tile
-  const int T = p.T, S = p.sch.s_q, nrow = p.nq + p.kvw;
+  const int T = p.T, S = LR ? 1 : p.sch.s_q, nrow = LR ? p.nq : p.nq + p.kvw;
+  const float* qsrc = LR ? p.qbuf : p.qkv_part;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, j = lane & 15, g = lane >> 4;
   const int jj = j < T ? j : T - 1;
   const int RT = p.dc / 16, KT = p.dh / TK, U = p.nh * RT;
@@ -546,7 +657,7 @@ __device__ __forceinline__ void phase_absorb(const LayerParams& p) {
       const int e0 = kt * TK + g * EPL;
       f32x4 q0 = {0.f, 0.f, 0.f, 0.f}, q1 = {0.f, 0.f, 0.f, 0.f};
       for (int s = 0; s < S; ++s) {
-        const float* src = p.qkv_part + ((long long)s * T + jj) * nrow + h * p.qw + e0;
+        const float* src = qsrc + ((long long)s * T + jj) * nrow + h * p.qw + e0;
         q0 += ldg(reinterpret_cast<const f32x4*>(src));
         if (EPL == 8) q1 += ldg(reinterpret_cast<const f32x4*>(src + 4));
       }
@@ -1908,7 +2019,9 @@ __device__ __forceinline__ void raise_model_fault(const LayerParams& p) {
   }
 }
 
-template <int AF, int EF, int KF, int KBMAX, int DBMAX, bool EXACT, int SPEC>
+// LR: the layer has a low-rank query (W_DQ, q-norm, W_UQ; phase P0b between
+// P0 and P1, one grid barrier more) and may normalise its cached latent.
+template <int AF, int EF, int KF, int KBMAX, int DBMAX, bool EXACT, int SPEC, bool LR = false>
 __global__ __launch_bounds__(kThreads, 1) void layer_kernel(LayerParams p) {
   specialise<SPEC>(p);
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -1938,20 +2051,24 @@ __global__ __launch_bounds__(kThreads, 1) void layer_kernel(LayerParams p) {
   if (blockIdx.x == 0 && threadIdx.x < kMaxSlots)
     __hip_atomic_store(&p.att_cnt[kSlotCnt + kSlotStride * threadIdx.x], 0u, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);   // slot completion counters
-  phase_qkv<AF>(p, smem);
+  phase_qkv<AF, LR>(p, smem);
   if (!grid_barrier(p, 0, flag)) return raise_model_fault(p);
+  if constexpr (LR) {
+    phase_uq<AF>(p, smem);
+    if (!grid_barrier(p, 0, flag)) return raise_model_fault(p);
+  }
   {
     // absorbed-query units on waves [0, wa) of every workgroup; when they fit
     // in half the waves, RoPE / KV insert runs on the other half meanwhile
     const int gs = p.sch.grid_min > 0 ? p.sch.grid_min : (int)gridDim.x;   // never above the grid
     const int wa = (p.nh * (p.dc / 16) + gs - 1) / gs;
     if (wa <= kWaves / 2) {
-      if ((int)threadIdx.x < kThreads / 2) phase_absorb<AF>(p);
-      else phase_rope_kv<KF>(p, L, blockIdx.x * (kThreads / 2) + threadIdx.x - kThreads / 2,
-                             gridDim.x * (kThreads / 2));
+      if ((int)threadIdx.x < kThreads / 2) phase_absorb<AF, LR>(p);
+      else phase_rope_kv<KF, LR>(p, L, blockIdx.x * (kThreads / 2) + threadIdx.x - kThreads / 2,
+                                 gridDim.x * (kThreads / 2));
     } else {
-      phase_rope_kv<KF>(p, L, blockIdx.x * kThreads + threadIdx.x, gridDim.x * kThreads);
-      phase_absorb<AF>(p);
+      phase_rope_kv<KF, LR>(p, L, blockIdx.x * kThreads + threadIdx.x, gridDim.x * kThreads);
+      phase_absorb<AF, LR>(p);
     }
   }
   if (!grid_barrier(p, 1, flag)) return raise_model_fault(p);

@@ -14,7 +14,8 @@ import synth
 from synth import recipe
 from synth.configs import LayerShape
 
-from . import (FORMATS, MK_T_EXPERT, MK_T_WDKV, MK_T_WO, MK_T_WQ, MK_T_WR, MK_T_WUK, MK_T_WUV, Layer,
+from . import (FORMATS, MK_T_EXPERT, MK_T_WDKV, MK_T_WDQ, MK_T_WO, MK_T_WQ, MK_T_WR, MK_T_WUK, MK_T_WUQ, MK_T_WUV,
+               Layer,
                LayerWeights, Model, head_packed_bytes, kv_bytes, layer_state_bytes, layer_workspace_bytes,
                make_config, model_state_bytes, pack_expert, pack_head, pack_head_fp8, pack_tensor, packed_bytes)
 
@@ -22,7 +23,7 @@ from . import (FORMATS, MK_T_EXPERT, MK_T_WDKV, MK_T_WO, MK_T_WQ, MK_T_WR, MK_T_
 def config_of(s: LayerShape):
     return make_config(s.d, s.n_h, s.d_h, s.d_c, s.d_r, s.E, s.top_k, s.n_shared, s.f, s.attn_fmt, s.exp_fmt,
                        s.kv_fmt, has_router_bias=1 if s.routing == "skew" else 0, rms_eps=s.eps,
-                       rope_base=s.rope_base)
+                       rope_base=s.rope_base, q_lora_rank=s.q_lora, kv_norm=1 if s.kv_norm else 0)
 
 
 def _dev(device):
@@ -104,9 +105,12 @@ class DeviceLayer:
         self.device = device
         cfg = self.cfg
         self.packed = {}
-        for name, tid in (("wq", MK_T_WQ), ("wdkv", MK_T_WDKV), ("wuk", MK_T_WUK), ("wuv", MK_T_WUV),
-                          ("wo", MK_T_WO), ("wr", MK_T_WR)):
-            src = _gen_attn_tensor(s, name, recipe.attn_shapes(s)[name], seed, layer, device)
+        shapes = recipe.attn_shapes(s)
+        for name, tid in (("wq", MK_T_WQ), ("wdq", MK_T_WDQ), ("wuq", MK_T_WUQ), ("wdkv", MK_T_WDKV),
+                          ("wuk", MK_T_WUK), ("wuv", MK_T_WUV), ("wo", MK_T_WO), ("wr", MK_T_WR)):
+            if name not in shapes:
+                continue
+            src = _gen_attn_tensor(s, name, shapes[name], seed, layer, device)
             dst = _bytes(packed_bytes(cfg, tid), device)
             pack_tensor(cfg, tid, src.data_ptr(), dst.data_ptr())
             self.packed[name] = dst
@@ -114,6 +118,15 @@ class DeviceLayer:
         self.g2 = torch.empty(s.d, dtype=torch.float32, device=_dev(device))
         synth.dev_normal_f32(self.g1.data_ptr(), s.d, seed, synth.stream_id("gamma1", layer), recipe.GAIN_SIGMA, 1.0)
         synth.dev_normal_f32(self.g2.data_ptr(), s.d, seed, synth.stream_id("gamma2", layer), recipe.GAIN_SIGMA, 1.0)
+        self.gq = self.gkv = None
+        if s.q_lora:
+            self.gq = torch.empty(s.q_lora, dtype=torch.float32, device=_dev(device))
+            synth.dev_normal_f32(self.gq.data_ptr(), s.q_lora, seed, synth.stream_id("gamma_q", layer),
+                                 recipe.GAIN_SIGMA, 1.0)
+        if s.kv_norm:
+            self.gkv = torch.empty(s.d_c, dtype=torch.float32, device=_dev(device))
+            synth.dev_normal_f32(self.gkv.data_ptr(), s.d_c, seed, synth.stream_id("gamma_kv", layer),
+                                 recipe.GAIN_SIGMA, 1.0)
         rb = recipe.router_bias(s, seed, layer)
         self.rbias = None if rb is None else torch.from_numpy(rb).to(_dev(device))
         block = packed_bytes(cfg, MK_T_EXPERT)
@@ -133,10 +146,13 @@ class DeviceLayer:
         self.state = _bytes(layer_state_bytes(cfg, device), device)
         self.workspace = workspace if workspace is not None else _bytes(layer_workspace_bytes(cfg, device), device)
         torch.cuda.synchronize(_dev(device))
-        w = LayerWeights(self.g1.data_ptr(), self.g2.data_ptr(), self.packed["wq"].data_ptr(),
+        ptr = lambda k: self.packed[k].data_ptr() if k in self.packed else None
+        w = LayerWeights(self.g1.data_ptr(), self.g2.data_ptr(), ptr("wq"),
                          self.packed["wdkv"].data_ptr(), self.packed["wuk"].data_ptr(),
                          self.packed["wuv"].data_ptr(), self.packed["wo"].data_ptr(), self.packed["wr"].data_ptr(),
-                         None if self.rbias is None else self.rbias.data_ptr(), None)
+                         None if self.rbias is None else self.rbias.data_ptr(), None,
+                         ptr("wdq"), ptr("wuq"), None if self.gq is None else self.gq.data_ptr(),
+                         None if self.gkv is None else self.gkv.data_ptr())
         self.layer = Layer(cfg, w, ptrs, self.state.data_ptr(), self.workspace.data_ptr(), device)
 
     def step(self, hin: torch.Tensor, T: int, kv: torch.Tensor, length: int, hout: torch.Tensor, stream: int = 0):

@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define MK_ABI_VERSION 1
+#define MK_ABI_VERSION 2
 #define MK_MAX_T 8           /* verify rows per step: k drafts + 1, at most 8 */
 #define MK_STATIC_SCRATCH_BYTES (32u << 20)   /* scratch of mk_decode_step_static, per GPU */
 
@@ -111,6 +111,14 @@ typedef struct mk_layer_config {
   int32_t has_router_bias;
   float rms_eps;             /* RMSNorm epsilon */
   float rope_base;           /* RoPE base (angles formed in double on the device) */
+  int32_t q_lora_rank;       /* 0: one W_Q.  > 0: low-rank query of this rank (a multiple of 32,
+                                <= d_model; bf16 attention): c^Q = W_DQ x, q-norm (RMSNorm of c^Q
+                                with gain gamma_q), q = W_UQ norm(c^Q) -- the low-rank query of
+                                the DeepSeek-V2 paper, section 2.1, with the q-norm of the pages'
+                                q-norm-rope-insert kernel ("Why one GB300 doesn't beat 4x RTX PRO
+                                6000 at single-stream decode", section "Where the 11.2 ms goes") */
+  int32_t kv_norm;           /* 1: RMSNorm (gain gamma_kv) of the latent c before it is cached
+                                (the RoPE key is not normalised); with q_lora_rank > 0 only */
 } mk_layer_config;
 
 typedef struct mk_device_info {
@@ -129,7 +137,9 @@ typedef struct mk_device_info {
 /* Packed tensors (pre-tiled for coalesced streaming; opaque layout). */
 typedef enum mk_tensor {
   MK_T_WQ = 0, MK_T_WDKV = 1, MK_T_WUK = 2, MK_T_WUV = 3, MK_T_WO = 4, MK_T_WR = 5,
-  MK_T_EXPERT = 6            /* W1, W3, W2 (and fp8 or MXFP4 scales) of one expert in one block */
+  MK_T_EXPERT = 6,           /* W1, W3, W2 (and fp8 or MXFP4 scales) of one expert in one block */
+  MK_T_WDQ = 7,              /* W_DQ [q_lora_rank][d_model] (q_lora_rank > 0) */
+  MK_T_WUQ = 8               /* W_UQ [n_heads*(d_head+d_rope)][q_lora_rank], rows as W_Q's */
 } mk_tensor;
 
 /* Packed layer weights (device pointers). */
@@ -146,6 +156,10 @@ typedef struct mk_layer_weights {
   const void* const* experts;/* HOST array of n_experts + n_shared device pointers to packed
                                 expert blocks; slot n_experts + s is shared expert s.  Blocks
                                 may be shared between layers. */
+  const void* wdq;           /* q_lora_rank > 0: packed W_DQ and W_UQ (wq is then unused and may be */
+  const void* wuq;           /*   NULL), gamma_q [q_lora_rank] fp32; NULL otherwise                  */
+  const float* gamma_q;
+  const float* gamma_kv;     /* kv_norm: [d_latent] fp32; NULL otherwise */
 } mk_layer_weights;
 
 /* KV cache of one layer: `capacity` rows in kv_format (mk_kv_bytes gives the

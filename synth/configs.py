@@ -84,9 +84,11 @@ C5X = C5.with_(name="stack32_mxfp4_E384_T6_L4096", exp_fmt="mxfp4", n_pools=0)
 # cache, one power-of-two scale per row.
 C3XK = C3X.with_(name="mxfp4_fp8kv_E384_T8_L8192", kv_fmt="fp8row")
 C5XK = C5X.with_(name="stack32_mxfp4_fp8kv_E384_T6_L4096", kv_fmt="fp8row")
-PRESETS = {s.name: s for s in (C0, C1, C2, C3, C4, C5, C3X, C5X, C3XK, C5XK)}
+# The layer variant with a low-rank query (rank 1536, q-norm) and the latent norm.
+C3Q = C3.with_(name="fp8_lowrankq_E384_T8_L8192", q_lora=1536, kv_norm=True)
+PRESETS = {s.name: s for s in (C0, C1, C2, C3, C4, C5, C3X, C5X, C3XK, C5XK, C3Q)}
 BY_KEY = {"C0": C0, "C1": C1, "C2": C2, "C3": C3, "C4": C4, "C5": C5, "C3X": C3X, "C5X": C5X,
-          "C3XK": C3XK, "C5XK": C5XK}
+          "C3XK": C3XK, "C5XK": C5XK, "C3Q": C3Q}
 
 # Skewed routing: the hot set is the first ceil(0.2 E) experts of a seeded permutation.
 HOT_FRACTION = 0.2

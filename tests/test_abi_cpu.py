@@ -27,7 +27,7 @@ def test_library_exports_every_header_function():
 
 def test_abi_version():
     import decoder_megakernel_amd as mk
-    assert mk.abi_version() == mk.MK_ABI_VERSION == 1
+    assert mk.abi_version() == mk.MK_ABI_VERSION == 2
 
 
 def _cfg(**kw):
@@ -66,6 +66,11 @@ def test_valid_configs_pass_and_sizes():
     (dict(attn_format="f32"), -8),
     (dict(d_latent=1024), -8),
     (dict(d_head=0), -1),
+    (dict(q_lora_rank=-32), -1),
+    (dict(q_lora_rank=100), -8),
+    (dict(q_lora_rank=8192), -8),
+    (dict(kv_norm=1), -8),
+    (dict(kv_norm=2, q_lora_rank=256), -1),
 ])
 def test_invalid_configs_are_refused(kw, code):
     import decoder_megakernel_amd as mk
@@ -109,3 +114,14 @@ def test_no_device_is_an_error_not_a_crash():
         pytest.skip("a GPU is present")
     with pytest.raises(mk.MkError):
         mk.query_device(0)
+
+
+def test_lowrank_query_config_and_packed_sizes():
+    import decoder_megakernel_amd as mk
+    cfg = _cfg(q_lora_rank=1536, kv_norm=1)
+    mk.check_config(cfg)
+    assert mk.packed_bytes(cfg, mk.MK_T_WDQ) == 1536 * 4096 * 2
+    assert mk.packed_bytes(cfg, mk.MK_T_WUQ) == 32 * 192 * 1536 * 2
+    with pytest.raises(mk.MkError) as ei:
+        mk.packed_bytes(_cfg(), mk.MK_T_WDQ)
+    assert ei.value.code == mk.MK_ERR_INVALID_ARG

@@ -168,3 +168,25 @@ def test_verify_rows_match_sequential_single_row_steps():
     kvs = parity.kv_to_f32(kv2[s.L:s.L + s.T].cpu().numpy(), "bf16")
     kvb = parity.kv_to_f32(kv[s.L:s.L + s.T].cpu().numpy(), "bf16")
     assert parity.normwise(kvb, kvs) < 2e-2
+
+
+# The low-rank query variant (W_DQ, q-norm, W_UQ) with the latent norm, on each
+# expert format and cache format; one without the latent norm.
+MID_LR_BF16 = MID_BF16.with_(name="mid_bf16_lowrank", q_lora=256, kv_norm=True)
+MID_LR_FP8 = MID_FP8.with_(name="mid_fp8_lowrank", q_lora=384, kv_norm=True)
+MID_LR_FP8_NOKVN = MID_FP8.with_(name="mid_fp8_lowrank_no_kvnorm", q_lora=224)
+MID_LR_MX_KV8 = MID_MX_TICKET.with_(name="mid_mxfp4_kv8_lowrank", kv_fmt="fp8row", q_lora=512, kv_norm=True)
+
+
+@pytest.mark.parametrize("shape", [MID_LR_BF16, MID_LR_FP8, MID_LR_FP8_NOKVN, MID_LR_MX_KV8], ids=lambda s: s.name)
+def test_lowrank_query_shapes_match_oracle(shape):
+    _run(shape)
+
+
+def test_lowrank_query_single_row_empty_cache():
+    _run(MID_LR_FP8, L=0, T=1)
+
+
+def test_full_size_lowrank_query_fp8_E384_T8_L8192():
+    from synth.configs import C3Q
+    _run(C3Q, full_weights=False)
