@@ -83,7 +83,7 @@ def layer_bytes(s, L, slots):
 # The sources that make up the layer kernel and its launch configuration
 # (the head, pack and embedding units do not change it).
 LAYER_SOURCES = ("mk_common.h", "mk_device.h", "mk_layer_kernel.h", "mk_layer.hip", "mk_layer_kv8.hip",
-                 "mk_layer_lr.hip", "mk_api.cpp")
+                 "mk_layer_lr.hip", "mk_layer_lr_spec.hip", "mk_api.cpp")
 
 
 def kernel_source_hash():

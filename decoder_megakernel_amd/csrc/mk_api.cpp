@@ -48,7 +48,9 @@ struct Dims {
 
 // s_q: the projection's split-K factor of the schedule (0 when not known yet).
 LayerKernelFn kernel_of(const Dims& D, int s_q = 0, int nwg = 0) {
-  if (D.ql > 0) return layer_kernel_lowrank_for(D.af, D.ef, D.kf, D.dc, D.dr);
+  if (D.ql > 0)
+    return layer_kernel_lowrank_for(D.af, D.ef, D.kf, D.d, D.nh, D.dh, D.dc, D.dr, D.E, D.topk, D.nshared, D.f, s_q,
+                                    nwg);
   return layer_kernel_for(D.af, D.ef, D.kf, D.d, D.nh, D.dh, D.dc, D.dr, D.E, D.topk, D.nshared, D.f, s_q, nwg);
 }
 
@@ -75,6 +77,9 @@ int check_cfg(const mk_layer_config* c) {
   if (D.ql > 0 && (D.af != MK_FMT_BF16 || D.ql % 32 || D.ql > D.d))
     return fail(MK_ERR_UNSUPPORTED_SHAPE, "a low-rank query needs bf16 attention and a rank that is a multiple of 32, <= d_model");
   if (D.kvn && D.ql == 0) return fail(MK_ERR_UNSUPPORTED_SHAPE, "the latent norm is built with the low-rank query only");
+  // the one-wave-per-row cache writer (fp8 cache, low-rank variant) forms one key RoPE pair per lane
+  if ((D.kf == MK_FMT_FP8_ROW || D.ql > 0) && D.dr > 128)
+    return fail(MK_ERR_UNSUPPORTED_SHAPE, "d_rope must be <= 128 with an fp8 cache or a low-rank query");
   if (!(c->rms_eps >= 0.f) || !(c->rope_base > 0.f)) return fail(MK_ERR_INVALID_ARG, "bad eps or rope base");
   const bool f32 = D.af == MK_FMT_F32 && D.ef == MK_FMT_F32 && D.kf == MK_FMT_F32;
   const bool bf = D.af == MK_FMT_BF16 && (D.kf == MK_FMT_BF16 || D.kf == MK_FMT_FP8_ROW) &&

@@ -11,8 +11,9 @@ typedef void (*LayerKernelFn)(LayerParams);
 // factor and grid).
 LayerKernelFn layer_kernel_for(int af, int ef, int kf, int d, int nh, int dh, int dc, int dr, int E, int topk,
                                int nshared, int f, int s_q, int nwg);
-// The instance for a layer with a low-rank query (null if none).
-LayerKernelFn layer_kernel_lowrank_for(int af, int ef, int kf, int dc, int dr);
+// The instance for a layer with a low-rank query (null if none); arguments as above.
+LayerKernelFn layer_kernel_lowrank_for(int af, int ef, int kf, int d, int nh, int dh, int dc, int dr, int E, int topk,
+                                       int nshared, int f, int s_q, int nwg);
 
 int launch_pack(const void* src, int fmt, int nb, int R, int K, long long sb, long long sr, long long sk,
                 void* dst, long long dst_stride, long long dst_off, hipStream_t stream);

@@ -442,6 +442,21 @@ __device__ __forceinline__ void phase_rope_kv(const LayerParams& p, int L, int t
     const int rb = kv_row_bytes(KF, p.kvw), nrun = p.kvw / 8;
     for (int t = wv; t < T; t += nwv) {
       const long long pos = (long long)L + t;
+      // the key's RoPE pairs: lane j < d_r / 2 forms pair j's cos and sin, and the
+      // lanes holding rotated runs fetch theirs (shuffles in uniform control flow)
+      float rc = 1.f, rsn = 0.f;
+      if (lane < dr2) rope_cs(pos, lane, p.rope_step, rc, rsn);
+      float pcs[2][4], psn[2][4];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int c = lane + 64 * i;
+        const int pb = (8 * c >= p.dc && c < nrun) ? (8 * c - p.dc) / 2 : 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          pcs[i][k] = __shfl(rc, pb + k);
+          psn[i][k] = __shfl(rsn, pb + k);
+        }
+      }
       float v[2][8];
       float amax = 0.f;
 #pragma unroll
@@ -464,8 +479,7 @@ __device__ __forceinline__ void phase_rope_kv(const LayerParams& p, int L, int t
           if (m0 >= p.dc) {
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-              float cs, sn;
-              rope_cs(pos, (m0 - p.dc) / 2 + k, p.rope_step, cs, sn);
+              const float cs = pcs[i][k], sn = psn[i][k];
               const float x0 = v[i][2 * k], x1 = v[i][2 * k + 1];
               v[i][2 * k] = x0 * cs - x1 * sn;
               v[i][2 * k + 1] = x0 * sn + x1 * cs;

@@ -190,3 +190,8 @@ def test_lowrank_query_single_row_empty_cache():
 def test_full_size_lowrank_query_fp8_E384_T8_L8192():
     from synth.configs import C3Q
     _run(C3Q, full_weights=False)
+
+
+def test_full_size_lowrank_query_mxfp4_fp8kv_E384_T8_L8192():
+    from synth.configs import C3XK
+    _run(C3XK.with_(name="mxfp4_fp8kv_lowrankq_E384_T8_L8192", q_lora=1536, kv_norm=True), full_weights=False)
