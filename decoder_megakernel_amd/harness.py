@@ -164,7 +164,7 @@ def kv_cache(s: LayerShape, seed: int = 0, layer: int = 0, device: int = 0, capa
     """KV rows [capacity][kvw] (fp8 rows: uint8 [capacity][row bytes]); rows [0, L)
     drawn as synth.recipe.kv_prefill_host draws them."""
     cap = capacity or s.capacity
-    n = s.L * s.kvw
+    n = s.L * s.kv_row
     st = synth.stream_id("kv_prefill", layer)
     if s.kv_fmt == "fp8row":
         rb = recipe.kv_row_bytes(s)
@@ -174,11 +174,11 @@ def kv_cache(s: LayerShape, seed: int = 0, layer: int = 0, device: int = 0, capa
                                 recipe.ACT_SIGMA)
         return kv
     if s.kv_fmt == "f32":
-        kv = torch.zeros((cap, s.kvw), dtype=torch.float32, device=_dev(device))
+        kv = torch.zeros((cap, s.kv_row), dtype=torch.float32, device=_dev(device))
         if n:
             synth.dev_normal_f32(kv.data_ptr(), n, seed, st, recipe.ACT_SIGMA)
     else:
-        kv = torch.zeros((cap, s.kvw), dtype=torch.int16, device=_dev(device))
+        kv = torch.zeros((cap, s.kv_row), dtype=torch.int16, device=_dev(device))
         if n:
             synth.dev_normal_bf16(kv.data_ptr(), n, seed, st, recipe.ACT_SIGMA)
     return kv

@@ -40,18 +40,19 @@ class Cfg(ctypes.Structure):
     _fields_ = [("d", _i), ("n_h", _i), ("d_h", _i), ("d_c", _i), ("d_r", _i), ("E", _i),
                 ("top_k", _i), ("n_shared", _i), ("f", _i), ("attn_fmt", _i), ("exp_fmt", _i),
                 ("kv_fmt", _i), ("eps", ctypes.c_float), ("rope_base", ctypes.c_double),
-                ("q_lora", _i), ("kv_norm", _i)]
+                ("q_lora", _i), ("kv_norm", _i), ("idx_heads", _i), ("idx_dim", _i), ("idx_topk", _i)]
 
 
 class Weights(ctypes.Structure):
     _fields_ = [("gamma1", _vp), ("gamma2", _vp), ("wq", _vp), ("wdkv", _vp), ("wuk", _vp),
                 ("wuv", _vp), ("wo", _vp), ("wr", _vp), ("router_bias", _vp),
                 ("w1", _vp), ("w3", _vp), ("w2", _vp), ("s1", _vp), ("s3", _vp), ("s2", _vp),
-                ("wdq", _vp), ("wuq", _vp), ("gamma_q", _vp), ("gamma_kv", _vp)]
+                ("wdq", _vp), ("wuq", _vp), ("gamma_q", _vp), ("gamma_kv", _vp), ("widx", _vp)]
 
 
 class AttnTaps(ctypes.Structure):
-    _fields_ = [("x", _vp), ("q", _vp), ("ckv", _vp), ("qabs", _vp), ("z", _vp), ("o", _vp)]
+    _fields_ = [("x", _vp), ("q", _vp), ("ckv", _vp), ("qabs", _vp), ("z", _vp), ("o", _vp), ("sel", _vp),
+                ("iscore", _vp)]
 
 
 class MoeTaps(ctypes.Structure):
@@ -117,7 +118,8 @@ def _p(a):
 
 def cfg_of(s: LayerShape) -> Cfg:
     return Cfg(s.d, s.n_h, s.d_h, s.d_c, s.d_r, s.E, s.top_k, s.n_shared, s.f, _FMT[s.attn_fmt],
-               _FMT[s.exp_fmt], _FMT[s.kv_fmt], s.eps, s.rope_base, s.q_lora, 1 if s.kv_norm else 0)
+               _FMT[s.exp_fmt], _FMT[s.kv_fmt], s.eps, s.rope_base, s.q_lora, 1 if s.kv_norm else 0,
+               s.idx_heads, s.idx_dim, s.idx_topk)
 
 
 class _WeightsHolder:
@@ -147,7 +149,7 @@ class _WeightsHolder:
                               ctypes.cast(ptrs["w2"], _vp), ctypes.cast(ptrs["s1"], _vp),
                               ctypes.cast(ptrs["s3"], _vp), ctypes.cast(ptrs["s2"], _vp),
                               keep(w.get("wdq")), keep(w.get("wuq")), keep(w.get("gamma_q")),
-                              keep(w.get("gamma_kv")))
+                              keep(w.get("gamma_kv")), keep(w.get("widx")))
 
 
 def _chk(rc, what):
@@ -163,7 +165,11 @@ def attn_block(s: LayerShape, w: dict, H: np.ndarray, kv: np.ndarray, L: int):
     taps = {"x": np.empty((T, s.d), np.float32), "q": np.empty((T, s.n_h, s.qw), np.float32),
             "ckv": np.empty((T, s.kvw), np.float32), "qabs": np.empty((T, s.n_h, s.d_c), np.float32),
             "z": np.empty((T, s.n_h, s.d_c), np.float32), "o": np.empty((T, s.n_h * s.d_h), np.float32)}
-    at = AttnTaps(*[taps[k].ctypes.data for k in ("x", "q", "ckv", "qabs", "z", "o")])
+    if s.idx_topk:
+        taps["isel"] = np.full((T, s.idx_topk), -1, np.int32)      # kept cache rows (sparse attention)
+        taps["iscore"] = np.full((T, L + T), np.nan, np.float32)
+    at = AttnTaps(*[taps[k].ctypes.data if k in taps else None
+                    for k in ("x", "q", "ckv", "qabs", "z", "o", "isel", "iscore")])
     wh = _WeightsHolder(s, w)
     c = cfg_of(s)
     _chk(lib().orc_attn_block(ctypes.byref(c), ctypes.byref(wh.struct), _p(H), T, _p(kv), L,

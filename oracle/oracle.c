@@ -268,10 +268,47 @@ static int check_cfg(const orc_cfg* c, int T) {
   return 0;
 }
 static int check_lowrank(const orc_cfg* c, const orc_weights* w) {
+  if (c->idx_topk < 0 || (c->idx_topk > 0 && (c->idx_heads <= 0 || c->idx_dim <= 0 || !w->widx ||
+                                               c->kv_fmt == ORC_FP8ROW)))
+    return -1;
   if (c->q_lora > 0 && (!w->wdq || !w->wuq || !w->gamma_q)) return -1;
   if (c->kv_norm && !w->gamma_kv) return -1;
   if (c->q_lora == 0 && !w->wq) return -1;
   return 0;
+}
+
+/* ------------------------------------------------------------------ sparse attention */
+/* row `row` of a row-major [rows][cols] matrix in format fmt (fp32 or bf16) */
+static const void* mat_row(const void* p, int fmt, long row, long cols) {
+  return fmt == ORC_F32 ? (const void*)((const float*)p + row * cols) : (const void*)((const uint16_t*)p + row * cols);
+}
+typedef struct { double v; long i; } scored;
+static int by_score_desc(const void* a, const void* b) {
+  const scored* x = (const scored*)a;
+  const scored* y = (const scored*)b;
+  if (x->v != y->v) return x->v > y->v ? -1 : 1;
+  return x->i < y->i ? -1 : (x->i > y->i ? 1 : 0);
+}
+static int by_index(const void* a, const void* b) {
+  const long x = *(const long*)a, y = *(const long*)b;
+  return x < y ? -1 : (x > y ? 1 : 0);
+}
+/* The kept rows of a query row at position pos: all rows 0..pos when pos + 1 <= k,
+ * else the k highest scores (ties to the lower row), in ascending row order.
+ * Returns how many. */
+static long select_rows(const double* score, long pos, int k, long* out) {
+  const long n = pos + 1;
+  if (n <= k) {
+    for (long j = 0; j < n; ++j) out[j] = j;
+    return n;
+  }
+  scored* a = malloc(sizeof(scored) * n);
+  for (long j = 0; j < n; ++j) { a[j].v = score[j]; a[j].i = j; }
+  qsort(a, (size_t)n, sizeof(scored), by_score_desc);
+  for (int t = 0; t < k; ++t) out[t] = a[t].i;
+  free(a);
+  qsort(out, (size_t)k, sizeof(long), by_index);
+  return k;
 }
 
 /* ------------------------------------------------------------------ attention */
@@ -290,9 +327,19 @@ int orc_attn_block(const orc_cfg* c, const orc_weights* w, const float* H, int T
   float* cq = malloc(sizeof(float) * (ql > 0 ? ql : 1));
   float* cqn = malloc(sizeof(float) * (ql > 0 ? ql : 1));
   float* cn = malloc(sizeof(float) * dc);
+  /* sparse attention: the indexer's projections and the row width with the index key */
+  const int sparse = c->idx_topk > 0, HI = c->idx_heads, dI = c->idx_dim, KI = c->idx_topk;
+  const int rw = kvw + (sparse ? dI : 0);
+  wmat WIQ = mk_wmat(sparse ? w->widx : NULL, c->attn_fmt, NULL, (long)HI * dI, d);
+  wmat WIW = mk_wmat(sparse ? mat_row(w->widx, c->attn_fmt, (long)HI * dI, d) : NULL, c->attn_fmt, NULL, HI, d);
+  wmat WIK = mk_wmat(sparse ? mat_row(w->widx, c->attn_fmt, (long)HI * dI + HI, d) : NULL, c->attn_fmt, NULL, dI, d);
+  float* qi = malloc(sizeof(float) * (sparse ? (long)HI * dI : 1));
+  float* wi = malloc(sizeof(float) * (sparse ? HI : 1));
+  double* isc = malloc(sizeof(double) * ((long)L + T));
+  long* sel = malloc(sizeof(long) * ((long)L + T));
   float* x = malloc(sizeof(float) * d);
   float* q = malloc(sizeof(float) * nh * qw);
-  float* ckv = malloc(sizeof(float) * kvw);
+  float* ckv = malloc(sizeof(float) * rw);
   float* qa = malloc(sizeof(float) * nh * dc);
   float* z = malloc(sizeof(float) * nh * dc);
   float* o = malloc(sizeof(float) * nh * dh);
@@ -317,7 +364,29 @@ int orc_attn_block(const orc_cfg* c, const orc_weights* w, const float* H, int T
     }
     for (int h = 0; h < nh; ++h) rope(q + (long)h * qw + dh, dr, pos, c->rope_base);
     rope(ckv + dc, dr, pos, c->rope_base);
-    kv_put_row(kv, c->kv_fmt, kvw, pos, ckv);
+    if (sparse) matvec(&WIK, x, ckv + kvw);     /* the row's index key, cached with it */
+    kv_put_row(kv, c->kv_fmt, rw, pos, ckv);
+    /* the rows this query row attends to */
+    long nsel = pos + 1;
+    if (sparse) {
+      matvec(&WIQ, x, qi);
+      matvec(&WIW, x, wi);
+      for (long j = 0; j <= pos; ++j) {
+        float sc = 0.0f;
+        for (int hh = 0; hh < HI; ++hh) {
+          float dot = 0.0f;
+          for (int m = 0; m < dI; ++m) dot += qi[(long)hh * dI + m] * kv_get(kv, c->kv_fmt, rw, j, kvw + m);
+          if (dot > 0.0f) sc += wi[hh] * dot;
+        }
+        isc[j] = (double)sc;
+        if (taps && taps->iscore) taps->iscore[(long)i * (L + T) + j] = sc;
+      }
+      nsel = select_rows(isc, pos, KI, sel);
+      if (taps && taps->sel)
+        for (int t = 0; t < KI; ++t) taps->sel[(long)i * KI + t] = t < nsel ? (int32_t)sel[t] : -1;
+    } else {
+      for (long j = 0; j <= pos; ++j) sel[j] = j;
+    }
 
     /* absorbed query: qa_h[m] = sum_e W_UK[h][e][m] q^C_h[e] */
     for (int h = 0; h < nh; ++h) {
@@ -336,24 +405,25 @@ int orc_attn_block(const orc_cfg* c, const orc_weights* w, const float* H, int T
     /* attention over stored rows 0 .. pos, per head */
 #pragma omp parallel for schedule(static)
     for (int h = 0; h < nh; ++h) {
-      float* sh = malloc(sizeof(float) * (pos + 1));
+      float* sh = malloc(sizeof(float) * nsel);
       const float* qah = qa + (long)h * dc;
       const float* qr = q + (long)h * qw + dh;
       float mx = -INFINITY;
-      for (long j = 0; j <= pos; ++j) {
+      for (long u = 0; u < nsel; ++u) {
+        const long j = sel[u];
         float acc = 0.0f;
-        for (int m = 0; m < dc; ++m) acc += qah[m] * kv_get(kv, c->kv_fmt, kvw, j, m);
-        for (int r = 0; r < dr; ++r) acc += qr[r] * kv_get(kv, c->kv_fmt, kvw, j, dc + r);
-        sh[j] = acc * scale;
-        if (sh[j] > mx) mx = sh[j];
+        for (int m = 0; m < dc; ++m) acc += qah[m] * kv_get(kv, c->kv_fmt, rw, j, m);
+        for (int r = 0; r < dr; ++r) acc += qr[r] * kv_get(kv, c->kv_fmt, rw, j, dc + r);
+        sh[u] = acc * scale;
+        if (sh[u] > mx) mx = sh[u];
       }
       float sum = 0.0f;
-      for (long j = 0; j <= pos; ++j) { sh[j] = expf(sh[j] - mx); sum += sh[j]; }
+      for (long u = 0; u < nsel; ++u) { sh[u] = expf(sh[u] - mx); sum += sh[u]; }
       float* zh = z + (long)h * dc;
       for (int m = 0; m < dc; ++m) zh[m] = 0.0f;
-      for (long j = 0; j <= pos; ++j) {
-        float p = sh[j] / sum;
-        for (int m = 0; m < dc; ++m) zh[m] += p * kv_get(kv, c->kv_fmt, kvw, j, m);
+      for (long u = 0; u < nsel; ++u) {
+        float p = sh[u] / sum;
+        for (int m = 0; m < dc; ++m) zh[m] += p * kv_get(kv, c->kv_fmt, rw, sel[u], m);
       }
       /* value up-projection: o_h[e] = sum_m W_UV[h][e][m] z_h[m] */
       for (int e = 0; e < dh; ++e) {
@@ -374,13 +444,14 @@ int orc_attn_block(const orc_cfg* c, const orc_weights* w, const float* H, int T
     if (taps) {
       if (taps->x) memcpy(taps->x + (long)i * d, x, sizeof(float) * d);
       if (taps->q) memcpy(taps->q + (long)i * nh * qw, q, sizeof(float) * nh * qw);
-      if (taps->ckv) memcpy(taps->ckv + (long)i * kvw, ckv, sizeof(float) * kvw);
+      if (taps->ckv) memcpy(taps->ckv + (long)i * kvw, ckv, sizeof(float) * kvw);   /* without the index key */
       if (taps->qabs) memcpy(taps->qabs + (long)i * nh * dc, qa, sizeof(float) * nh * dc);
       if (taps->z) memcpy(taps->z + (long)i * nh * dc, z, sizeof(float) * nh * dc);
       if (taps->o) memcpy(taps->o + (long)i * nh * dh, o, sizeof(float) * nh * dh);
     }
   }
   free(x); free(q); free(ckv); free(qa); free(z); free(o); free(att); free(cq); free(cqn); free(cn);
+  free(qi); free(wi); free(isc); free(sel);
   return 0;
 }
 
@@ -534,15 +605,25 @@ int orc_layer_step_f64(const orc_cfg* c, const orc_weights* w, const float* H, i
   wmat WUV = mk_wmat(w->wuv, c->attn_fmt, NULL, (long)nh * dh, dc);
   wmat WR = mk_wmat(w->wr, c->attn_fmt, NULL, E, d);
 
+  /* sparse attention: the indexer, and cache rows that carry their index key */
+  const int sparse = c->idx_topk > 0, HI = c->idx_heads, dI = c->idx_dim, KI = c->idx_topk;
+  const int rw = kvw + (sparse ? dI : 0);
+  wmat WIQ = mk_wmat(sparse ? w->widx : NULL, c->attn_fmt, NULL, (long)HI * dI, d);
+  wmat WIW = mk_wmat(sparse ? mat_row(w->widx, c->attn_fmt, (long)HI * dI, d) : NULL, c->attn_fmt, NULL, HI, d);
+  wmat WIK = mk_wmat(sparse ? mat_row(w->widx, c->attn_fmt, (long)HI * dI + HI, d) : NULL, c->attn_fmt, NULL, dI, d);
+  double* qi = malloc(sizeof(double) * (sparse ? (long)T * HI * dI : 1));
+  double* wi = malloc(sizeof(double) * (sparse ? (long)T * HI : 1));
+  double* isc = malloc(sizeof(double) * npos);
+  long* selr = malloc(sizeof(long) * npos);
   /* all rows of the cache as double: prefill rows as stored, new rows rounded to storage */
-  double* rows = malloc(sizeof(double) * npos * kvw);
+  double* rows = malloc(sizeof(double) * npos * rw);
   for (long j = 0; j < L; ++j)
-    for (int m = 0; m < kvw; ++m) rows[j * kvw + m] = (double)kv_get(kv, c->kv_fmt, kvw, j, m);
+    for (int m = 0; m < rw; ++m) rows[j * rw + m] = (double)kv_get(kv, c->kv_fmt, rw, j, m);
   double* x = malloc(sizeof(double) * d);
   double* q = malloc(sizeof(double) * (long)T * nh * qw);
-  double* ckv = malloc(sizeof(double) * kvw);
-  float* rowf = malloc(sizeof(float) * kvw);
-  float* rowr = malloc(sizeof(float) * kvw);
+  double* ckv = malloc(sizeof(double) * rw);
+  float* rowf = malloc(sizeof(float) * rw);
+  float* rowr = malloc(sizeof(float) * rw);
   double* cq = malloc(sizeof(double) * (ql > 0 ? ql : 1));
   double* cqn = malloc(sizeof(double) * (ql > 0 ? ql : 1));
   double* cn = malloc(sizeof(double) * dc);
@@ -563,11 +644,16 @@ int orc_layer_step_f64(const orc_cfg* c, const orc_weights* w, const float* H, i
     }
     for (int h = 0; h < nh; ++h) rope64(q + (long)i * nh * qw + (long)h * qw + dh, dr, pos, c->rope_base);
     rope64(ckv + dc, dr, pos, c->rope_base);
-    for (int m = 0; m < kvw; ++m) rowf[m] = (float)ckv[m];
-    kv_round_row(c->kv_fmt, kvw, rowf, rowr);
-    for (int m = 0; m < kvw; ++m) {
-      rows[pos * kvw + m] = (double)rowr[m];
-      if (kv_new_f64) kv_new_f64[(long)i * kvw + m] = (double)rowr[m];
+    if (sparse) {
+      matvec64(&WIK, x, ckv + kvw);
+      matvec64(&WIQ, x, qi + (long)i * HI * dI);
+      matvec64(&WIW, x, wi + (long)i * HI);
+    }
+    for (int m = 0; m < rw; ++m) rowf[m] = (float)ckv[m];
+    kv_round_row(c->kv_fmt, rw, rowf, rowr);
+    for (int m = 0; m < rw; ++m) {
+      rows[pos * rw + m] = (double)rowr[m];
+      if (kv_new_f64 && m < kvw) kv_new_f64[(long)i * kvw + m] = (double)rowr[m];
     }
   }
   /* un-absorbed keys/values per head: kc[h][j][e] = W_UK[h] c_j, v[h][j][e] = W_UV[h] c_j */
@@ -579,8 +665,8 @@ int orc_layer_step_f64(const orc_cfg* c, const orc_weights* w, const float* H, i
     for (int e = 0; e < dh; ++e) {
       double ak = 0.0, av = 0.0;
       for (int m = 0; m < dc; ++m) {
-        ak += wat64(&WUK, h * dh + e, m) * rows[j * kvw + m];
-        av += wat64(&WUV, h * dh + e, m) * rows[j * kvw + m];
+        ak += wat64(&WUK, h * dh + e, m) * rows[j * rw + m];
+        av += wat64(&WUV, h * dh + e, m) * rows[j * rw + m];
       }
       kc[hj * dh + e] = ak;
       vv[hj * dh + e] = av;
@@ -592,22 +678,38 @@ int orc_layer_step_f64(const orc_cfg* c, const orc_weights* w, const float* H, i
   double* hp = malloc(sizeof(double) * (long)T * d);
   for (int i = 0; i < T; ++i) {
     const long pos = (long)L + i;
+    long nsel = pos + 1;
+    if (sparse) {
+      for (long j = 0; j <= pos; ++j) {
+        double sc = 0.0;
+        for (int hh = 0; hh < HI; ++hh) {
+          double dot = 0.0;
+          for (int m = 0; m < dI; ++m) dot += qi[((long)i * HI + hh) * dI + m] * rows[j * rw + kvw + m];
+          if (dot > 0.0) sc += wi[(long)i * HI + hh] * dot;
+        }
+        isc[j] = sc;
+      }
+      nsel = select_rows(isc, pos, KI, selr);
+    } else {
+      for (long j = 0; j <= pos; ++j) selr[j] = j;
+    }
     for (int h = 0; h < nh; ++h) {
       const double* qh = q + (long)i * nh * qw + (long)h * qw;
-      double* sc = malloc(sizeof(double) * (pos + 1));
+      double* sc = malloc(sizeof(double) * nsel);
       double mx = -INFINITY;
-      for (long j = 0; j <= pos; ++j) {
+      for (long u = 0; u < nsel; ++u) {
+        const long j = selr[u];
         double a = 0.0;
         for (int e = 0; e < dh; ++e) a += qh[e] * kc[((long)h * npos + j) * dh + e];
-        for (int r = 0; r < dr; ++r) a += qh[dh + r] * rows[j * kvw + dc + r];
-        sc[j] = a * scale;
-        if (sc[j] > mx) mx = sc[j];
+        for (int r = 0; r < dr; ++r) a += qh[dh + r] * rows[j * rw + dc + r];
+        sc[u] = a * scale;
+        if (sc[u] > mx) mx = sc[u];
       }
       double sum = 0.0;
-      for (long j = 0; j <= pos; ++j) { sc[j] = exp(sc[j] - mx); sum += sc[j]; }
+      for (long u = 0; u < nsel; ++u) { sc[u] = exp(sc[u] - mx); sum += sc[u]; }
       for (int e = 0; e < dh; ++e) {
         double a = 0.0;
-        for (long j = 0; j <= pos; ++j) a += (sc[j] / sum) * vv[((long)h * npos + j) * dh + e];
+        for (long u = 0; u < nsel; ++u) a += (sc[u] / sum) * vv[((long)h * npos + selr[u]) * dh + e];
         o[(long)h * dh + e] = a;
       }
       free(sc);
@@ -666,7 +768,7 @@ int orc_layer_step_f64(const orc_cfg* c, const orc_weights* w, const float* H, i
     }
   }
   free(rows); free(x); free(q); free(ckv); free(rowf); free(rowr); free(kc); free(vv); free(o); free(att); free(hp);
-  free(cq); free(cqn); free(cn);
+  free(cq); free(cqn); free(cn); free(qi); free(wi); free(isc); free(selr);
   free(xp); free(lg); free(a); free(b); free(y); free(sel);
   return rc;
 }

@@ -50,6 +50,13 @@
  *    the latent before it is cached (the normalised compressed latents of the
  *    DeepSeek-V2 architecture); the RoPE key is not normalised.
  *
+ *  - Sparse attention: the pages' sparse attention mode with an indexer
+ *    ("Why one GB300 ...", sections "Where the 11.2 ms goes" and "Corrections
+ *    to things we said") read as the lightning indexer and top-k selection of
+ *    the DeepSeek-V3.2 report (index scores sum_j w_j relu(q_j . k_s), each
+ *    query row attends to its top-k cache rows); no normalisation or RoPE of
+ *    the index keys, which the cache rows carry after the RoPE key.
+ *
  * Readings where the pages are silent (each listed in the design notes):
  * eps = 1e-6; softmax scale 1/sqrt(d_h + d_r); RoPE base 10000 with the angle
  * p * theta_j formed in double; selection by logit with ties to the lower
@@ -87,6 +94,9 @@ typedef struct orc_cfg {
   int q_lora;     /* 0: one W_Q; > 0: low-rank query of this rank, c^Q = W_DQ x,
                      q-norm (RMSNorm with gain gamma_q), q = W_UQ norm(c^Q) */
   int kv_norm;    /* 1: RMSNorm with gain gamma_kv on the latent c before it is cached */
+  int idx_heads;  /* sparse attention (idx_topk > 0): indexer heads H_I, index key dim d_I,   */
+  int idx_dim;    /*   keys kept per query row k; each cache row then holds its index key    */
+  int idx_topk;   /*   after the latent and the RoPE key (d_c + d_r + d_I values)            */
 } orc_cfg;
 
 /* Canonical (row-major) weights.  Expert slot e in [0, E) is routed expert e,
@@ -102,6 +112,12 @@ typedef struct orc_cfg {
  *   q_lora > 0 (the low-rank query of the DeepSeek-V2 paper, section 2.1, with
  *   the q-norm of the pages' q-norm-rope-insert kernel): W_DQ [q_lora][d],
  *   W_UQ [n_h*(d_h+d_r)][q_lora] in place of W_Q; kv_norm: gain [d_c].
+ *   Sparse attention (idx_topk > 0): the lightning indexer of the DeepSeek-V3.2
+ *   report (the pages' SparseAttnFwdMode and indexer) -- per query row t,
+ *   q^I = W_IQ x [H_I][d_I], w^I = W_IW x [H_I], its index key k^I = W_IK x
+ *   (cached with the row); score of cache row s <= pos: sum_j w^I_j *
+ *   max(0, q^I_j . k^I_s); the row attends to the idx_topk highest-scoring
+ *   rows (ties to the lower row; all rows when pos + 1 <= idx_topk).
  *   MXFP4 (OCP Microscaling Formats spec v1.0: E2M1 elements, one E8M0 scale
  *   per block of 32 consecutive elements): W1, W3, W2 as bytes [rows][cols/2],
  *   element 2j in the low nibble of byte j and 2j+1 in the high nibble; the
@@ -127,6 +143,7 @@ typedef struct orc_weights {
   const void* wuq;          /*   gamma_q [q_lora] (W_Q is then unused)                                */
   const float* gamma_q;
   const float* gamma_kv;    /* kv_norm: [d_c] */
+  const void* widx;         /* sparse: [W_IQ; W_IW; W_IK] rows [H_I*d_I + H_I + d_I][d] (attn_fmt) */
 } orc_weights;
 
 /* Optional intermediate outputs (any pointer may be NULL). */
@@ -137,6 +154,8 @@ typedef struct orc_attn_taps {
   float* qabs;  /* [T][n_h][d_c]          absorbed query q~                       */
   float* z;     /* [T][n_h][d_c]          attention-weighted latent               */
   float* o;     /* [T][n_h*d_h]           per-head value up-projection            */
+  int32_t* sel; /* [T][idx_topk]          sparse: kept cache rows, ascending, -1 padded */
+  float* iscore;/* [T][L+T]               sparse: index scores (row i: 0 .. L+i)   */
 } orc_attn_taps;
 
 typedef struct orc_moe_taps {

@@ -100,7 +100,7 @@ TAGS = {
     "H": 1, "kv_prefill": 2, "gamma1": 3, "gamma2": 4, "wq": 5, "wdkv": 6, "wuk": 7,
     "wuv": 8, "wo": 9, "wr": 10, "w1": 11, "w3": 12, "w2": 13, "emb": 14, "head": 15,
     "gamma_f": 16, "tokens": 17, "hot_perm": 18, "kv_scale": 19, "wdq": 20, "wuq": 21, "gamma_q": 22,
-    "gamma_kv": 23,
+    "gamma_kv": 23, "widx": 24,
 }
 
 

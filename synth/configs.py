@@ -37,12 +37,20 @@ class LayerShape:
     head_fmt: str = "bf16"     # LM head: "bf16" | "fp8" (E4M3 + fp32 128x128 scales)
     q_lora: int = 0            # 0: one W_Q; > 0: low-rank query W_DQ -> q-norm -> W_UQ of this rank
     kv_norm: bool = False      # RMSNorm (gain gamma_kv) on the latent before it is cached
+    idx_heads: int = 0         # sparse attention (idx_topk > 0): indexer heads, index key dim, rows kept
+    idx_dim: int = 0
+    idx_topk: int = 0
     eps: float = 1e-6
     rope_base: float = 10000.0
 
     @property
     def kvw(self) -> int:
         return self.d_c + self.d_r
+
+    @property
+    def kv_row(self) -> int:
+        """Values per cache row: latent, RoPE key, and the index key with sparse attention."""
+        return self.kvw + (self.idx_dim if self.idx_topk else 0)
 
     @property
     def qw(self) -> int:

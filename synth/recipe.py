@@ -38,8 +38,10 @@ def attn_shapes(s: LayerShape):
     """Attention-format tensors of a layer; with a low-rank query, W_DQ and W_UQ
     take the place of W_Q."""
     q = {"wdq": (s.q_lora, s.d), "wuq": (s.n_h * s.qw, s.q_lora)} if s.q_lora else {"wq": (s.n_h * s.qw, s.d)}
+    idx = {"widx": (s.idx_heads * s.idx_dim + s.idx_heads + s.idx_dim, s.d)} if s.idx_topk else {}
     return {
         **q,
+        **idx,
         "wdkv": (s.kvw, s.d),
         "wuk": (s.n_h, s.d_h, s.d_c),
         "wuv": (s.n_h, s.d_h, s.d_c),
@@ -125,10 +127,10 @@ def kv_row_bytes(s: LayerShape) -> int:
     """Bytes of one cache row: kvw elements (fp32 / bf16), or for fp8 rows kvw
     E4M3 codes and an fp32 scale, padded to a multiple of 16 bytes."""
     if s.kv_fmt == "f32":
-        return 4 * s.kvw
+        return 4 * s.kv_row
     if s.kv_fmt == "bf16":
-        return 2 * s.kvw
-    return (s.kvw + 4 + 15) // 16 * 16
+        return 2 * s.kv_row
+    return (s.kv_row + 4 + 15) // 16 * 16
 
 
 def kv_prefill_host(s: LayerShape, seed: int = 0, layer: int = 0) -> np.ndarray:
@@ -141,11 +143,11 @@ def kv_prefill_host(s: LayerShape, seed: int = 0, layer: int = 0) -> np.ndarray:
                               stream_id("kv_scale", layer), ACT_SIGMA)
         return kv
     if s.kv_fmt == "f32":
-        kv = np.zeros((cap, s.kvw), dtype=np.float32)
-        kv[: s.L] = normal_f32((s.L, s.kvw), seed, stream_id("kv_prefill", layer), ACT_SIGMA)
+        kv = np.zeros((cap, s.kv_row), dtype=np.float32)
+        kv[: s.L] = normal_f32((s.L, s.kv_row), seed, stream_id("kv_prefill", layer), ACT_SIGMA)
     else:
-        kv = np.zeros((cap, s.kvw), dtype=np.uint16)
-        kv[: s.L] = normal_bf16((s.L, s.kvw), seed, stream_id("kv_prefill", layer), ACT_SIGMA)
+        kv = np.zeros((cap, s.kv_row), dtype=np.uint16)
+        kv[: s.L] = normal_bf16((s.L, s.kv_row), seed, stream_id("kv_prefill", layer), ACT_SIGMA)
     return kv
 
 

@@ -152,7 +152,7 @@ def gpu_cache_host(st, s, l, L):
     if s.kv_fmt == "fp8row":
         kv = np.zeros((rows, recipe.kv_row_bytes(s)), np.uint8)
     else:
-        kv = np.zeros((rows, s.kvw), np.uint16 if s.kv_fmt == "bf16" else np.float32)
+        kv = np.zeros((rows, s.kv_row), np.uint16 if s.kv_fmt == "bf16" else np.float32)
     src = st.kv[l][:L].cpu().numpy()
     kv[:L] = src.view(np.uint16) if s.kv_fmt == "bf16" else src
     return kv

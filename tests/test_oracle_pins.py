@@ -874,3 +874,95 @@ def test_latent_norm_gives_unit_rms_rows_before_the_gain_and_leaves_the_key():
     assert np.array_equal(kv[s.L:s.L + s.T, s.d_c:], kv0[s.L:s.L + s.T, s.d_c:])
     ratio = c / c0
     assert np.allclose(ratio, ratio[:, :1], rtol=1e-5)
+
+
+# ---------------------------------------------------------------- sparse attention with an indexer
+# The pages' sparse attention mode and indexer ("Why one GB300 ...", sections
+# "Where the 11.2 ms goes" and "Corrections to things we said"), read as the
+# lightning indexer of the DeepSeek-V3.2 report: score(t, s) = sum_j w_tj *
+# relu(q_tj . k_s); each query row attends to its top-k cache rows.
+C0S = C0.with_(name="micro_sparse", idx_heads=4, idx_dim=16, idx_topk=4, L=9)
+C0QS = C0Q.with_(name="micro_bf16_sparse", idx_heads=4, idx_dim=32, idx_topk=5, L=12)
+
+
+def _dense_of(s, kv):
+    """The same layer without the indexer, on the same cache rows minus their index keys."""
+    sd = s.with_(idx_heads=0, idx_dim=0, idx_topk=0)
+    return sd, np.ascontiguousarray(kv[:, : s.kvw])
+
+
+def test_sparse_with_topk_covering_every_row_is_the_dense_layer_bitwise():
+    s = C0S.with_(idx_topk=64)
+    w, H, kv = fresh(s)
+    sd, kvd = _dense_of(s, kv)
+    wd = {k: v for k, v in w.items() if k != "widx"}
+    out, taps = oracle.layer_step(s, w, H, kv, s.L)
+    outd, tapsd = oracle.layer_step(sd, wd, H, kvd, s.L)
+    assert np.array_equal(taps["Hp"].view(np.uint32), tapsd["Hp"].view(np.uint32))
+    assert np.array_equal(out.view(np.uint32), outd.view(np.uint32))
+    for i in range(s.T):
+        assert list(taps["isel"][i][: s.L + i + 1]) == list(range(s.L + i + 1))
+
+
+def _decode(a, fmt):
+    return oracle.bf16_to_f32(a).astype(np.float64) if fmt == "bf16" else a.astype(np.float64)
+
+
+@pytest.mark.parametrize("shape", [C0S, C0QS], ids=lambda s: s.name)
+def test_sparse_selection_is_the_topk_of_independently_computed_index_scores(shape):
+    s = shape
+    w, H, kv = fresh(s)
+    out, taps = oracle.layer_step(s, w, H, kv, s.L)
+    HI, dI, k = s.idx_heads, s.idx_dim, s.idx_topk
+    W = _decode(w["widx"], s.attn_fmt)
+    x = taps["x"].astype(np.float64)
+    rows = _decode(kv, s.kv_fmt)[: s.L + s.T]
+    kI = rows[:, s.kvw:]
+    # the new rows carry W_IK x as their index key (stored at the cache's precision)
+    tol_k = 1e-5 if s.kv_fmt == "f32" else 2 ** -8
+    assert normwise(kI[s.L:], x @ W[HI * dI + HI:].T) < tol_k
+    for i in range(s.T):
+        pos = s.L + i
+        qI = (W[: HI * dI] @ x[i]).reshape(HI, dI)
+        wI = W[HI * dI: HI * dI + HI] @ x[i]
+        sc = (np.maximum(kI[: pos + 1] @ qI.T, 0.0) * wI[None, :]).sum(axis=1)
+        got = taps["iscore"][i, : pos + 1].astype(np.float64)
+        assert np.abs(got - sc).max() <= 1e-4 * np.abs(sc).max()
+        sel = [j for j in taps["isel"][i] if j >= 0]
+        assert sel == sorted(sel) and len(sel) == min(k, pos + 1)
+        out_rows = sorted(set(range(pos + 1)) - set(sel))
+        if out_rows:
+            # every kept row scores at least as high as every dropped one (up to fp32 rounding)
+            assert sc[sel].min() >= sc[out_rows].max() - 1e-5 * np.abs(sc).max()
+
+
+@pytest.mark.parametrize("shape", [C0S, C0QS], ids=lambda s: s.name)
+def test_sparse_layer_matches_fp64_unabsorbed_bruteforce(shape):
+    s = shape
+    w, H, kv = fresh(s)
+    kv64 = kv.copy()
+    out, taps = oracle.layer_step(s, w, H, kv, s.L)
+    ref = oracle.layer_step_f64(s, w, H, kv64, s.L, force_sel=taps["sel"])
+    assert normwise(out, ref["out"]) < 1e-5
+    assert normwise(taps["Hp"].astype(np.float64) - H, ref["Hp"] - H) < 1e-4
+
+
+def test_sparse_attention_weights_only_the_kept_rows():
+    """z of every (row, head) against numpy attention over the kept rows alone,
+    from the oracle's absorbed query, rotated query and the stored cache rows."""
+    s = C0S
+    w, H, kv = fresh(s)
+    out, taps = oracle.layer_step(s, w, H, kv, s.L)
+    rows = kv[: s.L + s.T].astype(np.float64)
+    scale = 1.0 / math.sqrt(s.d_h + s.d_r)
+    for i in range(s.T):
+        sel = [j for j in taps["isel"][i] if j >= 0]
+        assert len(sel) == s.idx_topk < s.L + i + 1
+        for h in range(s.n_h):
+            qa = taps["qabs"][i, h].astype(np.float64)
+            qr = taps["q"][i, h, s.d_h:].astype(np.float64)
+            sc = (rows[sel, : s.d_c] @ qa + rows[sel, s.d_c:s.kvw] @ qr) * scale
+            p = np.exp(sc - sc.max())
+            p /= p.sum()
+            z = p @ rows[sel, : s.d_c]
+            assert np.abs(taps["z"][i, h] - z).max() <= 1e-5 * np.abs(z).max()
