@@ -83,7 +83,7 @@ def layer_bytes(s, L, slots):
 # The sources that make up the layer kernel and its launch configuration
 # (the head, pack and embedding units do not change it).
 LAYER_SOURCES = ("mk_common.h", "mk_device.h", "mk_layer_kernel.h", "mk_layer.hip", "mk_layer_kv8.hip",
-                 "mk_layer_lr.hip", "mk_layer_lr_spec.hip", "mk_api.cpp")
+                 "mk_layer_lr.hip", "mk_layer_lr_spec.hip", "mk_layer_sparse.hip", "mk_api.cpp")
 
 
 def kernel_source_hash():
@@ -458,7 +458,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--workload", default="C5", choices=["C2", "C3", "C4", "C5", "C3X", "C5X", "C3XK", "C5XK", "C3Q"])
+    ap.add_argument("--workload", default="C5", choices=["C2", "C3", "C4", "C5", "C3X", "C5X", "C3XK", "C5XK", "C3Q", "C4S"])
     ap.add_argument("--layers", type=int, default=None, help="stack depth override (diagnostics only)")
     ap.add_argument("--head-fmt", default="bf16", choices=["bf16", "fp8"],
                     help="LM-head table format (the stack workload names bf16)")

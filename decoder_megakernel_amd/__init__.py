@@ -13,7 +13,7 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmk.so")
 
-MK_ABI_VERSION = 2
+MK_ABI_VERSION = 3
 MK_MAX_T = 8   # verify rows per step
 MK_STATIC_SCRATCH_BYTES = 32 << 20
 
@@ -30,7 +30,7 @@ MK_ERR_UNSUPPORTED_SHAPE = -8
 MK_FMT_F32, MK_FMT_BF16, MK_FMT_FP8_B128, MK_FMT_MXFP4, MK_FMT_FP8_ROW = 0, 1, 2, 3, 4
 FORMATS = {"f32": MK_FMT_F32, "bf16": MK_FMT_BF16, "fp8": MK_FMT_FP8_B128, "mxfp4": MK_FMT_MXFP4,
            "fp8row": MK_FMT_FP8_ROW}
-MK_T_WQ, MK_T_WDKV, MK_T_WUK, MK_T_WUV, MK_T_WO, MK_T_WR, MK_T_EXPERT, MK_T_WDQ, MK_T_WUQ = range(9)
+MK_T_WQ, MK_T_WDKV, MK_T_WUK, MK_T_WUV, MK_T_WO, MK_T_WR, MK_T_EXPERT, MK_T_WDQ, MK_T_WUQ, MK_T_WIDX = range(10)
 
 # Every entry point the header declares (checked by the CPU tests).
 EXPORTS = (
@@ -62,7 +62,8 @@ class LayerConfig(ctypes.Structure):
                 ("d_latent", _i32), ("d_rope", _i32), ("n_experts", _i32), ("top_k", _i32),
                 ("n_shared", _i32), ("d_ff", _i32), ("attn_format", _i32), ("expert_format", _i32),
                 ("kv_format", _i32), ("has_router_bias", _i32), ("rms_eps", ctypes.c_float),
-                ("rope_base", ctypes.c_float), ("q_lora_rank", _i32), ("kv_norm", _i32)]
+                ("rope_base", ctypes.c_float), ("q_lora_rank", _i32), ("kv_norm", _i32), ("idx_heads", _i32),
+                ("idx_dim", _i32), ("idx_topk", _i32), ("idx_max_rows", _i32)]
 
 
 class DeviceInfo(ctypes.Structure):
@@ -74,7 +75,7 @@ class DeviceInfo(ctypes.Structure):
 class LayerWeights(ctypes.Structure):
     _fields_ = [("gamma1", _vp), ("gamma2", _vp), ("wq", _vp), ("wdkv", _vp), ("wuk", _vp), ("wuv", _vp),
                 ("wo", _vp), ("wr", _vp), ("router_bias", _vp), ("experts", _vp),
-                ("wdq", _vp), ("wuq", _vp), ("gamma_q", _vp), ("gamma_kv", _vp)]
+                ("wdq", _vp), ("wuq", _vp), ("gamma_q", _vp), ("gamma_kv", _vp), ("widx", _vp)]
 
 
 class KvCache(ctypes.Structure):
@@ -162,11 +163,12 @@ def query_device(hip_device: int = 0) -> DeviceInfo:
 
 def make_config(d_model, n_heads, d_head, d_latent, d_rope, n_experts, top_k, n_shared, d_ff,
                 attn_format, expert_format, kv_format, has_router_bias=0, rms_eps=1e-6, rope_base=10000.0,
-                abi_version=MK_ABI_VERSION, q_lora_rank=0, kv_norm=0) -> LayerConfig:
+                abi_version=MK_ABI_VERSION, q_lora_rank=0, kv_norm=0, idx_heads=0, idx_dim=0, idx_topk=0,
+                idx_max_rows=0) -> LayerConfig:
     fm = lambda f: FORMATS[f] if isinstance(f, str) else int(f)
     return LayerConfig(abi_version, d_model, n_heads, d_head, d_latent, d_rope, n_experts, top_k, n_shared, d_ff,
                        fm(attn_format), fm(expert_format), fm(kv_format), int(has_router_bias), rms_eps, rope_base,
-                       int(q_lora_rank), int(kv_norm))
+                       int(q_lora_rank), int(kv_norm), int(idx_heads), int(idx_dim), int(idx_topk), int(idx_max_rows))
 
 
 def check_config(cfg: LayerConfig) -> None:

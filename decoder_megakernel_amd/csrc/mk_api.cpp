@@ -43,11 +43,20 @@ struct Dims {
   int d, nh, dh, dc, dr, qw, kvw, nq, E, topk, nshared, f;
   int af, ef, kf;
   int ql, kvn;       // low-rank query rank (0: one W_Q), latent norm
+  int ih, idm, ik, imax;   // sparse attention: indexer heads, key dim, rows kept, largest L + T
   int nqp() const { return ql > 0 ? ql : nq; }   // rows of the first projection's query part
+  int nidx() const { return ik > 0 ? ih * idm + ih + idm : 0; }   // indexer rows of the first projection
+  int kvrow() const { return kvw + (ik > 0 ? idm : 0); }           // values per cache row
 };
 
 // s_q: the projection's split-K factor of the schedule (0 when not known yet).
 LayerKernelFn kernel_of(const Dims& D, int s_q = 0, int nwg = 0) {
+  if (D.ik > 0) {
+    const bool spec = D.d == 4096 && D.nh == 32 && D.dh == 128 && D.dc == 512 && D.dr == 64 && D.E == 384 &&
+                      D.topk == 8 && D.nshared == 1 && D.f == 2048 && (s_q == 0 || s_q == 1) &&
+                      (nwg == 0 || nwg >= kSpecMinGrid);
+    return layer_kernel_sparse_for(D.af, D.ef, D.kf, D.ql > 0, spec);
+  }
   if (D.ql > 0)
     return layer_kernel_lowrank_for(D.af, D.ef, D.kf, D.d, D.nh, D.dh, D.dc, D.dr, D.E, D.topk, D.nshared, D.f, s_q,
                                     nwg);
@@ -60,6 +69,7 @@ Dims dims_of(const mk_layer_config* c) {
   D.qw = D.dh + D.dr; D.kvw = D.dc + D.dr; D.nq = D.nh * D.qw; D.E = c->n_experts; D.topk = c->top_k;
   D.nshared = c->n_shared; D.f = c->d_ff; D.af = c->attn_format; D.ef = c->expert_format; D.kf = c->kv_format;
   D.ql = c->q_lora_rank; D.kvn = c->kv_norm;
+  D.ih = c->idx_heads; D.idm = c->idx_dim; D.ik = c->idx_topk; D.imax = c->idx_max_rows;
   return D;
 }
 
@@ -77,6 +87,18 @@ int check_cfg(const mk_layer_config* c) {
   if (D.ql > 0 && (D.af != MK_FMT_BF16 || D.ql % 32 || D.ql > D.d))
     return fail(MK_ERR_UNSUPPORTED_SHAPE, "a low-rank query needs bf16 attention and a rank that is a multiple of 32, <= d_model");
   if (D.kvn && D.ql == 0) return fail(MK_ERR_UNSUPPORTED_SHAPE, "the latent norm is built with the low-rank query only");
+  if (D.ik < 0) return fail(MK_ERR_INVALID_ARG, "idx_topk must be >= 0");
+  if (D.ik > 0) {
+    if (D.af != MK_FMT_BF16 || D.kf != MK_FMT_BF16)
+      return fail(MK_ERR_UNSUPPORTED_SHAPE, "sparse attention needs bf16 attention and a bf16 cache");
+    if (D.nh % 16 || D.ih <= 0 || D.ih % 16 || D.idm <= 0 || D.idm % 32 || D.ih * D.idm > 8192 || D.ik > 8192)
+      return fail(MK_ERR_UNSUPPORTED_SHAPE, "sparse attention: n_heads and idx_heads multiples of 16, idx_dim a "
+                                            "multiple of 32, idx_heads * idx_dim <= 8192, idx_topk <= 8192");
+    if (D.imax < 1 || D.imax > (1 << 24)) return fail(MK_ERR_INVALID_ARG, "idx_max_rows must be in [1, 2^24]");
+    // the index scores phase stages every row's index queries (bf16, 8 pad per head) and weights in LDS
+    if ((long long)kMaxT * D.ih * (D.idm + 8) * 2 + 16 + (long long)kMaxT * D.ih * 4 > kLdsBytes - 1024)
+      return fail(MK_ERR_UNSUPPORTED_SHAPE, "idx_heads * (idx_dim + 8) too large for the LDS plan");
+  }
   // the one-wave-per-row cache writer (fp8 cache, low-rank variant) forms one key RoPE pair per lane
   if ((D.kf == MK_FMT_FP8_ROW || D.ql > 0) && D.dr > 128)
     return fail(MK_ERR_UNSUPPORTED_SHAPE, "d_rope must be <= 128 with an fp8 cache or a low-rank query");
@@ -152,6 +174,10 @@ int packed_bytes(const mk_layer_config* c, int tensor, size_t* out) {
       if (D.ql == 0) return fail(MK_ERR_INVALID_ARG, "W_DQ / W_UQ need q_lora_rank > 0");
       b = tensor == MK_T_WDQ ? tiles_bytes(D.ql, D.d, D.af) : tiles_bytes(D.nq, D.ql, D.af);
       break;
+    case MK_T_WIDX:
+      if (D.ik == 0) return fail(MK_ERR_INVALID_ARG, "the indexer's weights need idx_topk > 0");
+      b = tiles_bytes(D.nidx(), D.d, D.af);
+      break;
     default: return fail(MK_ERR_INVALID_ARG, "unknown tensor id %d", tensor);
   }
   *out = (size_t)b;
@@ -210,7 +236,7 @@ int device_info(int dev, DevInfo* di, LayerKernelFn fn) {
 
 struct WsLayout {
   size_t qkv_part, qrope, qabs, att_part, att_ml, z, o, hp, route_sel, route_gate, route_cand, logits, hbuf,
-      ybuf, dummy, qbuf,
+      ybuf, dummy, qbuf, iscore, isel,
       total;
 };
 struct StLayout {
@@ -225,7 +251,7 @@ WsLayout ws_layout(const Dims& D, const Schedule& s) {
   const int nqt = (T * D.nh + 15) / 16;
   const int units = std::max(s.nwg, nqt);
   const int slots = std::min(D.E, T * D.topk) + D.nshared;
-  w.qkv_part = take((size_t)s.s_q * T * (D.nqp() + D.kvw) * 4);
+  w.qkv_part = take((size_t)s.s_q * T * (D.nqp() + D.kvw + D.nidx()) * 4);
   w.qrope = take((size_t)T * D.nh * D.dr * 4);
   w.qabs = take((size_t)T * D.nh * D.dc * 4);
   w.att_part = take((size_t)units * 16 * D.dc * 4);
@@ -241,6 +267,8 @@ WsLayout ws_layout(const Dims& D, const Schedule& s) {
   w.ybuf = take((size_t)slots * T * D.d * 4);
   w.dummy = take(32768);
   w.qbuf = D.ql > 0 ? take((size_t)T * D.nq * 4) : 0;
+  w.iscore = D.ik > 0 ? take((size_t)T * D.imax * 4) : 0;
+  w.isel = D.ik > 0 ? take((size_t)T * D.ik * 4) : 0;
   w.total = off;
   return w;
 }
@@ -275,6 +303,8 @@ void bind_workspace(LayerParams& p, const WsLayout& wl, char* ws) {
   p.ybuf = (float*)(ws + wl.ybuf);
   p.dummy = (const uint8_t*)(ws + wl.dummy);
   p.qbuf = wl.qbuf ? (float*)(ws + wl.qbuf) : nullptr;
+  p.iscore = wl.iscore ? (float*)(ws + wl.iscore) : nullptr;
+  p.isel = wl.isel ? (int32_t*)(ws + wl.isel) : nullptr;
 }
 
 // ------------------------------------------------------------------ static scratch
@@ -306,7 +336,7 @@ Schedule make_schedule(const Dims& D, int nwg) {
   s.nwg = nwg;
   s.grid_min = 0;
   const int KTa = D.d / tile_k(D.af);
-  s.s_q = choose_split(D.nqp() / 16 + (D.kvw + 15) / 16, KTa, nwg);
+  s.s_q = choose_split(D.nqp() / 16 + (D.kvw + 15) / 16 + D.nidx() / 16, KTa, nwg);
   return s;
 }
 
@@ -402,7 +432,7 @@ int mk_kv_bytes(const mk_layer_config* cfg, int32_t capacity, size_t* bytes) {
   int rc = check_cfg(cfg);
   if (rc) return rc;
   if (!bytes || capacity < 0) return fail(MK_ERR_INVALID_ARG, "bad arguments");
-  *bytes = (size_t)capacity * kv_row_bytes(cfg->kv_format, cfg->d_latent + cfg->d_rope);
+  *bytes = (size_t)capacity * kv_row_bytes(cfg->kv_format, dims_of(cfg).kvrow());
   return MK_OK;
 }
 
@@ -460,6 +490,10 @@ int mk_pack_tensor(const mk_layer_config* cfg, int tensor, const void* src, void
       if (D.ql == 0) return fail(MK_ERR_INVALID_ARG, "W_UQ needs q_lora_rank > 0");
       rc = launch_pack(src, f, 1, D.nq, D.ql, 0, D.ql, 1, dst, 1024, 0, s);
       break;
+    case MK_T_WIDX:
+      if (D.ik == 0) return fail(MK_ERR_INVALID_ARG, "the indexer's weights need idx_topk > 0");
+      rc = launch_pack(src, f, 1, D.nidx(), D.d, 0, D.d, 1, dst, 1024, 0, s);
+      break;
     default: return fail(MK_ERR_INVALID_ARG, "tensor %d is not packed with mk_pack_tensor", tensor);
   }
   if (rc) return fail(MK_ERR_HIP, "pack launch failed: %s", hipGetErrorString((hipError_t)rc));
@@ -510,6 +544,7 @@ int mk_layer_init(const mk_layer_config* cfg, const mk_layer_weights* w, void* s
   if (cfg->q_lora_rank > 0 ? (!w->wdq || !w->wuq || !w->gamma_q) : !w->wq)
     return fail(MK_ERR_INVALID_ARG, "null query projection (W_Q, or W_DQ, W_UQ and gamma_q with a low-rank query)");
   if (cfg->kv_norm && !w->gamma_kv) return fail(MK_ERR_INVALID_ARG, "kv_norm needs gamma_kv");
+  if (cfg->idx_topk > 0 && !w->widx) return fail(MK_ERR_INVALID_ARG, "sparse attention needs the indexer's weights");
   if ((cfg->has_router_bias != 0) != (w->router_bias != nullptr))
     return fail(MK_ERR_INVALID_ARG, "router_bias must be given iff has_router_bias");
   const Dims D = dims_of(cfg);
@@ -564,6 +599,8 @@ int mk_layer_init(const mk_layer_config* cfg, const mk_layer_weights* w, void* s
   p.rbias = w->router_bias;
   p.ql = D.ql; p.kv_norm = D.kvn;
   p.wdq = (const uint8_t*)w->wdq; p.wuq = (const uint8_t*)w->wuq; p.gq = w->gamma_q; p.gkv = w->gamma_kv;
+  p.ihead = D.ih; p.idim = D.idm; p.itopk = D.ik; p.imax = D.imax; p.kv_row = D.kvrow();
+  p.widx = (const uint8_t*)w->widx;
   p.experts = (const uint8_t* const*)(L->state + L->sl.experts);
   p.exp_w13_bytes = exp_w13(D);
   p.exp_w2_bytes = exp_w2(D);
@@ -607,6 +644,8 @@ static int launch_layer(mk_layer* L, const float* hin, int T, void* kv_rows, int
 
 int mk_decode_step(mk_layer* L, const float* hidden_in, int T, const mk_kv_cache* kv, float* hidden_out, void* stream) {
   if (!L || !hidden_in || !kv || !kv->rows || !hidden_out) return fail(MK_ERR_INVALID_ARG, "null argument");
+  if (L->D.ik > 0 && (long long)kv->length + T > L->D.imax)
+    return fail(MK_ERR_INVALID_ARG, "KV length %d + T %d exceeds idx_max_rows %d", kv->length, T, L->D.imax);
   if (T < 1 || T > kMaxT) return fail(MK_ERR_INVALID_ARG, "T=%d outside [1, %d]", T, kMaxT);
   if (kv->length < 0 || kv->capacity < 0 || (long long)kv->length + T > kv->capacity)
     return fail(MK_ERR_INVALID_ARG, "KV length %d + T %d exceeds capacity %d", kv->length, T, kv->capacity);
@@ -649,6 +688,12 @@ int mk_debug_tap(mk_layer* L, int tap, void* host_dst, size_t bytes, void* strea
     case 5: src = (const char*)p.logits; need = (size_t)T * D.E * 4; break;
     case 6: src = (const char*)p.route_sel; need = (size_t)T * D.topk * 4; break;
     case 7: src = (const char*)p.route_gate; need = (size_t)T * D.topk * 4; break;
+    case 8:   // sparse attention: kept cache rows [T][idx_topk] (ascending; entries past a row's count unspecified)
+    case 9:   // sparse attention: index scores [T][idx_max_rows] (row t: columns 0 .. L + T - 1)
+      if (D.ik == 0) return fail(MK_ERR_INVALID_ARG, "tap %d needs sparse attention", tap);
+      src = tap == 8 ? (const char*)p.isel : (const char*)p.iscore;
+      need = (size_t)T * (tap == 8 ? D.ik : D.imax) * 4;
+      break;
     case 0: {
       // Q with rotated q^R: rebuild [T][nh][qw] from the split-K partials and the rotated part
       if (bytes < (size_t)T * D.nh * D.qw * 4) return fail(MK_ERR_INVALID_ARG, "tap buffer too small");

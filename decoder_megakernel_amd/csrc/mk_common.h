@@ -42,7 +42,7 @@ __host__ __device__ constexpr int tile_k(int fmt) {
 __host__ __device__ constexpr int elem_bytes(int fmt) { return fmt == MK_FMT_F32 ? 4 : (fmt == MK_FMT_BF16 ? 2 : 1); }
 // Formats whose tiles carry scales: fp8 (fp32 per 128x128 block) and MXFP4 (E8M0 per 32 elements of a row).
 // Bytes of one KV cache row of kvw values (fp8 rows: codes, fp32 scale, padding to 16).
-__host__ __device__ constexpr int kv_row_bytes(int fmt, int kvw) {
+__host__ __device__ constexpr int kv_row_bytes(int fmt, int kvw) {   // kvw: values per row
   return fmt == MK_FMT_FP8_ROW ? (kvw + 4 + 15) / 16 * 16 : kvw * (fmt == MK_FMT_F32 ? 4 : 2);
 }
 __host__ __device__ constexpr bool scaled_fmt(int fmt) { return fmt == MK_FMT_FP8_B128 || fmt == MK_FMT_MXFP4; }
@@ -123,6 +123,10 @@ struct LayerParams {
   const uint8_t* wuq;
   const float* gq;
   const float* gkv;
+  // sparse attention (itopk > 0): indexer heads and key dims, rows kept per query row
+  int ihead, idim, itopk;
+  int kv_row;                      // values per cache row (kvw, + idim with sparse attention)
+  const uint8_t* widx;             // [W_IQ; W_IW; W_IK] tiles
   const uint8_t* const* experts;   // [E + nshared] packed expert blocks
   // packed expert block geometry (bytes)
   long long exp_w13_bytes;         // interleaved W1/W3 tiles
@@ -130,6 +134,9 @@ struct LayerParams {
   // workspace
   float* qkv_part;         // [s_q][T][nq + kvw] (low-rank query: [s_q][T][ql + kvw])
   float* qbuf;             // low-rank query: q [T][nq]
+  float* iscore;           // sparse: index scores [T][idx_max_rows]
+  int32_t* isel;           // sparse: kept rows [T][itopk], ascending
+  int imax;                // sparse: idx_max_rows
   float* qrope;            // [T][nh][dr]
   float* qabs;             // [T][nh][dc]
   float* att_part;         // [units][16][dc]

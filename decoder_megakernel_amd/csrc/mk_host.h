@@ -11,6 +11,9 @@ typedef void (*LayerKernelFn)(LayerParams);
 // factor and grid).
 LayerKernelFn layer_kernel_for(int af, int ef, int kf, int d, int nh, int dh, int dc, int dr, int E, int topk,
                                int nshared, int f, int s_q, int nwg);
+// The instance for a layer with sparse attention (null if none).
+// spec: the 384-expert layer's dimensions (fixed-shape instances for fp8 experts).
+LayerKernelFn layer_kernel_sparse_for(int af, int ef, int kf, bool lowrank, bool spec);
 // The instance for a layer with a low-rank query (null if none); arguments as above.
 LayerKernelFn layer_kernel_lowrank_for(int af, int ef, int kf, int d, int nh, int dh, int dc, int dr, int E, int topk,
                                        int nshared, int f, int s_q, int nwg);

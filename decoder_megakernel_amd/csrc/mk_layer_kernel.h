@@ -283,7 +283,7 @@ __device__ __forceinline__ const A* b_lane(const A* xs, int XS, int T, int TK) {
 
 // ------------------------------------------------------------------ P0
 // LR (low-rank query): the query rows are W_DQ's ql rows (c^Q) instead of W_Q's.
-template <int AF, bool LR = false>
+template <int AF, bool LR = false, bool SP = false>
 __device__ __forceinline__ void phase_qkv(const LayerParams& p, char* smem) {
   typedef typename Act<AF>::T A;
   constexpr int TK = tile_k(AF);
@@ -292,23 +292,26 @@ __device__ __forceinline__ void phase_qkv(const LayerParams& p, char* smem) {
   A* xs = reinterpret_cast<A*>(smem);
   float* red = reinterpret_cast<float*>(smem + lp.xb);
   const int nqp = LR ? p.ql : p.nq;
-  const int RTq = nqp / 16, RTkv = (p.kvw + 15) / 16, KT = p.d / TK, S = p.sch.s_q, NT = KT / S;
-  const int U = (RTq + RTkv) * S;
+  const int nidx = SP ? p.ihead * p.idim + p.ihead + p.idim : 0;     // the indexer's rows (sparse attention)
+  const int RTq = nqp / 16, RTkv = (p.kvw + 15) / 16, RTi = nidx / 16, KT = p.d / TK, S = p.sch.s_q, NT = KT / S;
+  const int U = (RTq + RTkv + RTi) * S;
   int u0, u1;
   split_range(U, gridDim.x, blockIdx.x, u0, u1);
   const A* bl = b_lane<A>(xs, XS, T, TK);
-  const int nrow = nqp + p.kvw;
+  const int nrow = nqp + p.kvw + nidx;
   struct Src {
-    const uint8_t* wq; const uint8_t* wd; int RTq, KT, S, NT; const A* bl;
+    const uint8_t* wq; const uint8_t* wd; const uint8_t* wi; int RTq, RTkv, KT, S, NT; const A* bl;
     __device__ const uint8_t* base(int u) const {
       const int rt = u / S, s = u - rt * S;
-      const uint8_t* b = rt < RTq ? wq + (long long)rt * KT * 1024 : wd + (long long)(rt - RTq) * KT * 1024;
+      const uint8_t* b = rt < RTq ? wq + (long long)rt * KT * 1024
+                       : (!SP || rt < RTq + RTkv) ? wd + (long long)(rt - RTq) * KT * 1024
+                       : wi + (long long)(rt - RTq - RTkv) * KT * 1024;
       return b + (long long)s * NT * 1024;
     }
     __device__ const A* bbase(int u) const { return bl + (u % S) * NT * TK; }
     __device__ const float* sbase(int) const { return nullptr; }
     __device__ const float* sbase2(int) const { return nullptr; }
-  } src{LR ? p.wdq : p.wq, p.wdkv, RTq, KT, S, NT, bl};
+  } src{LR ? p.wdq : p.wq, p.wdkv, p.widx, RTq, RTkv, KT, S, NT, bl};
   float* part = p.qkv_part;
   const int nq = nqp, kvw = p.kvw;
   const float* rsc = rsc_lds();       // the staged rows are h * gamma: scale by 1/rms
@@ -317,10 +320,12 @@ __device__ __forceinline__ void phase_qkv(const LayerParams& p, char* smem) {
     int rt = u / S, s = u - rt * S;
     int idx;
     if (rt < RTq) idx = rt * 16 + row;
-    else {
+    else if (!SP || rt < RTq + RTkv) {
       int r = (rt - RTq) * 16 + row;
       if (r >= kvw) return;
       idx = nq + r;
+    } else {
+      idx = nq + kvw + (rt - RTq - RTkv) * 16 + row;
     }
     part[((long long)s * T + col) * nrow + idx] = v;
   };
@@ -343,7 +348,7 @@ __device__ __forceinline__ void phase_qkv(const LayerParams& p, char* smem) {
 // the T rows, stages c^Q * gamma_q into LDS with 1/rms per row (as RMSNorm-1
 // is staged), then the row tiles of W_UQ are streamed over the grid and each
 // product is scaled by its row's 1/rms into qbuf [T][nq].
-template <int AF>
+template <int AF, bool SP = false>
 __device__ __forceinline__ void phase_uq(const LayerParams& p, char* smem) {
   typedef typename Act<AF>::T A;
   constexpr int TK = tile_k(AF);
@@ -367,7 +372,7 @@ __device__ __forceinline__ void phase_uq(const LayerParams& p, char* smem) {
   const float* rsc = rsc_lds();
   auto epi = [=](int u, int row, int col, float v, float) { q[(long long)col * nq + u * 16 + row] = v * rsc[col]; };
   RowStager<A, true> rs;
-  rs.issue_sum(p.qkv_part, p.sch.s_q, T, p.ql + p.kvw, K, p.gq);
+  rs.issue_sum(p.qkv_part, p.sch.s_q, T, p.ql + p.kvw + (SP ? p.ihead * p.idim + p.ihead + p.idim : 0), K, p.gq);
   rs.finish(T, K, xs, (A*)nullptr, XS, p.eps);
   stream_units_wg<AF, false, false>(u0, u1, KT, T, src, epi, red, p.dummy);
 }
@@ -417,11 +422,15 @@ __device__ __forceinline__ void rope_cs(long long pos, int pidx, double step, fl
 // given by the caller (`tid` is this thread's index in that range).  LR: the
 // layer has a low-rank query, which P0b left whole in qbuf; the first
 // projection's partials then hold [c^Q | c | k_R] rows of ql + kvw values.
-template <int KF, bool LR = false>
+// SP (sparse attention): the partial rows end with the indexer's rows [q^I | w^I | k^I], and
+// each new cache row also receives its index key k^I after the RoPE key.
+template <int KF, bool LR = false, bool SP = false>
 __device__ __forceinline__ void phase_rope_kv(const LayerParams& p, int L, int tid, int nthreads) {
   const int T = p.T, S = p.sch.s_q, dr2 = p.dr / 2;
-  const int kvoff = LR ? p.ql : p.nq, nrow = kvoff + p.kvw;    // where c starts in a partial row
-  const int per_t = p.dc + dr2 + p.nh * dr2;
+  const int kvoff = LR ? p.ql : p.nq;                              // where c starts in a partial row
+  const int kioff = kvoff + p.kvw + (SP ? p.ihead * p.idim + p.ihead : 0);   // where k^I starts
+  const int nrow = kvoff + p.kvw + (SP ? p.ihead * p.idim + p.ihead + p.idim : 0);
+  const int per_t = p.dc + dr2 + p.nh * dr2 + (SP ? p.idim : 0);
   const float* part = p.qkv_part;
   auto psum = [&](int t, int idx) {
     float v = 0.f;
@@ -439,7 +448,7 @@ __device__ __forceinline__ void phase_rope_kv(const LayerParams& p, int L, int t
     // max <= 448 * 2^e, and each value is stored as E4M3(v / 2^e); fp32 / bf16
     // rows store the values.
     const int lane = tid & 63, wv = tid >> 6, nwv = nthreads >> 6;
-    const int rb = kv_row_bytes(KF, p.kvw), nrun = p.kvw / 8;
+    const int rb = kv_row_bytes(KF, p.kv_row), nrun = p.kvw / 8;
     for (int t = wv; t < T; t += nwv) {
       const long long pos = (long long)L + t;
       // the key's RoPE pairs: lane j < d_r / 2 forms pair j's cos and sin, and the
@@ -518,15 +527,22 @@ __device__ __forceinline__ void phase_rope_kv(const LayerParams& p, int L, int t
           const int c = lane + 64 * i;
           if (c < nrun) {
             if constexpr (KF == MK_FMT_F32) {
-              float* dst = reinterpret_cast<float*>(p.kv) + pos * p.kvw + 8 * c;
+              float* dst = reinterpret_cast<float*>(p.kv) + pos * p.kv_row + 8 * c;
               *reinterpret_cast<f32x4*>(dst) = f32x4{v[i][0], v[i][1], v[i][2], v[i][3]};
               *reinterpret_cast<f32x4*>(dst + 4) = f32x4{v[i][4], v[i][5], v[i][6], v[i][7]};
             } else {
               bf16x8 o;
 #pragma unroll
               for (int k = 0; k < 8; ++k) o[k] = (__bf16)v[i][k];
-              *reinterpret_cast<bf16x8*>(reinterpret_cast<__bf16*>(p.kv) + pos * p.kvw + 8 * c) = o;
+              *reinterpret_cast<bf16x8*>(reinterpret_cast<__bf16*>(p.kv) + pos * p.kv_row + 8 * c) = o;
             }
+          }
+        }
+        if constexpr (SP) {
+          for (int m = lane; m < p.idim; m += 64) {
+            const float v = psum(t, kioff + m);
+            if constexpr (KF == MK_FMT_F32) reinterpret_cast<float*>(p.kv)[pos * p.kv_row + p.kvw + m] = v;
+            else reinterpret_cast<__bf16*>(p.kv)[pos * p.kv_row + p.kvw + m] = (__bf16)v;
           }
         }
         continue;
@@ -579,10 +595,18 @@ __device__ __forceinline__ void phase_rope_kv(const LayerParams& p, int L, int t
   for (int it = tid; it < T * per_t; it += nthreads) {
     const int t = it / per_t, r = it - t * per_t;
     const long long pos = (long long)L + t;
+    if (SP && r >= p.dc + dr2 + p.nh * dr2) {
+      // the row's index key, after the RoPE key
+      const int m = r - (p.dc + dr2 + p.nh * dr2);
+      const float v = psum(t, kioff + m);
+      if (KF == MK_FMT_F32) reinterpret_cast<float*>(p.kv)[pos * p.kv_row + p.kvw + m] = v;
+      else reinterpret_cast<__bf16*>(p.kv)[pos * p.kv_row + p.kvw + m] = (__bf16)v;
+      continue;
+    }
     if (r < p.dc) {
       float v = psum(t, p.nq + r);
-      if (KF == MK_FMT_F32) reinterpret_cast<float*>(p.kv)[pos * p.kvw + r] = v;
-      else reinterpret_cast<__bf16*>(p.kv)[pos * p.kvw + r] = (__bf16)v;
+      if (KF == MK_FMT_F32) reinterpret_cast<float*>(p.kv)[pos * p.kv_row + r] = v;
+      else reinterpret_cast<__bf16*>(p.kv)[pos * p.kv_row + r] = (__bf16)v;
       continue;
     }
     // a RoPE pair: of the key (k^R, into the cache) or of head h's query
@@ -594,7 +618,7 @@ __device__ __forceinline__ void phase_rope_kv(const LayerParams& p, int L, int t
     rope_cs(pos, pi, p.rope_step, c, sn);
     const float v0 = x0 * c - x1 * sn, v1 = x0 * sn + x1 * c;
     if (key) {
-      const long long o = pos * p.kvw + p.dc + 2 * pi;
+      const long long o = pos * p.kv_row + p.dc + 2 * pi;
       if (KF == MK_FMT_F32) {
         reinterpret_cast<float*>(p.kv)[o] = v0;
         reinterpret_cast<float*>(p.kv)[o + 1] = v1;
@@ -647,11 +671,12 @@ __device__ __forceinline__ bf16x8 make_b<MK_FMT_BF16>(const f32x4& a, const f32x
 
 // q~[t][h][m] = sum_e W_UK[h][e][m] q^C[t][h][e]  (wave-level units: one head, 16 m-rows, all of K).
 // LR: q^C comes whole from qbuf (low-rank query) instead of the split-K partials.
-template <int AF, bool LR = false>
+template <int AF, bool LR = false, bool SP = false>
 __device__ __forceinline__ void phase_absorb(const LayerParams& p) {
   constexpr int TK = tile_k(AF);
   constexpr int EPL = TK / 4;          // elements per lane per tile
-  const int T = p.T, S = LR ? 1 : p.sch.s_q, nrow = LR ? p.nq : p.nq + p.kvw;
+  const int T = p.T, S = LR ? 1 : p.sch.s_q;
+  const int nrow = LR ? p.nq : p.nq + p.kvw + (SP ? p.ihead * p.idim + p.ihead + p.idim : 0);
   const float* qsrc = LR ? p.qbuf : p.qkv_part;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, j = lane & 15, g = lane >> 4;
   const int jj = j < T ? j : T - 1;
@@ -681,6 +706,163 @@ __device__ __forceinline__ void phase_absorb(const LayerParams& p) {
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         p.qabs[((long long)j * p.nh + h) * p.dc + rt * 16 + 4 * g + e] = acc[e];
+    }
+  }
+}
+
+// ------------------------------------------------------------------ P1b, P1c sparse attention
+// Index scores: every workgroup stages the T rows' index queries q^I (bf16,
+// LDS row stride idx_dim + 8 per head) and weights w^I (fp32) from the split-K
+// partials; the cache rows [0, L + T) are cut into chunks of 16 spread over the
+// grid, and wave t < T scores verify row t against each chunk: S[key][head] =
+// k^I_key . q^I_head on the matrix cores (16 keys x 16 heads per product,
+// idim / 32 k-steps), then the sum over heads of w^I_head * max(0, S), the 16
+// head lanes added by shuffles.  Scores go to iscore[t][key].
+template <bool LR>
+__device__ __forceinline__ void phase_iscore(const LayerParams& p, int L, char* smem) {
+  const int T = p.T, HI = p.ihead, dI = p.idim, S = p.sch.s_q;
+  const int qoff = (LR ? p.ql : p.nq) + p.kvw, woff = qoff + HI * dI, nrow = woff + HI + dI;
+  const int HS = dI + 8, QS = HI * HS;                 // LDS strides (bf16): head, verify row
+  __bf16* qs = reinterpret_cast<__bf16*>(smem);
+  float* wsm = reinterpret_cast<float*>(smem + ((long long)kMaxT * QS * 2 + 15) / 16 * 16);
+  const float* part = p.qkv_part;
+  const int n4 = HI * dI / 4;
+  for (int i = threadIdx.x; i < T * n4; i += kThreads) {
+    const int t = i / n4, e = (i - t * n4) * 4, h = e / dI, m = e - h * dI;
+    f32x4 a = {0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < S; ++s) a += ldg(reinterpret_cast<const f32x4*>(part + ((long long)s * T + t) * nrow + qoff + e));
+    store4<__bf16>(qs + t * QS + h * HS + m, a);
+  }
+  for (int i = threadIdx.x; i < T * HI; i += kThreads) {
+    const int t = i / HI, h = i - t * HI;
+    float a = 0.f;
+    for (int s = 0; s < S; ++s) a += ldg(part + ((long long)s * T + t) * nrow + woff + h);
+    wsm[t * HI + h] = a;
+  }
+  __syncthreads();
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, j = lane & 15, g = lane >> 4;
+  const int Lt = L + T, nch = (Lt + 15) / 16;
+  int c0, c1;
+  split_range(nch, gridDim.x, blockIdx.x, c0, c1);
+  if (w >= T) return;
+  const int nht = HI / 16, nkb = dI / 32;
+  const __bf16* kvb = reinterpret_cast<const __bf16*>(p.kv);
+  const __bf16* qrow = qs + w * QS + g * 8;
+  for (int c = c0; c < c1; ++c) {
+    const int key = min(c * 16 + j, Lt - 1);
+    const __bf16* krow = kvb + (long long)key * p.kv_row + p.kvw + g * 8;
+    float sc[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int ht = 0; ht < nht; ++ht) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int kb = 0; kb < nkb; ++kb)
+        acc = mma_bf16_k32(__builtin_bit_cast(bf16x8, ld16(krow + kb * 32)),
+                           *reinterpret_cast<const bf16x8*>(qrow + (ht * 16 + j) * HS + kb * 32), acc);
+      const float wh = wsm[w * HI + ht * 16 + j];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sc[e] += acc[e] > 0.f ? wh * acc[e] : 0.f;
+    }
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sc[e] += __shfl_xor(sc[e], o);
+    if (j == 0) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int k = c * 16 + 4 * g + e;
+        if (k < Lt) p.iscore[(long long)w * p.imax + k] = sc[e];
+      }
+    }
+  }
+}
+
+// Top-k per verify row: workgroup t < T keeps row t's idx_topk highest scores
+// among cache rows [0, L + t]: a radix select on the scores' order-preserving
+// 32-bit keys (four 8-bit digits from the top, a histogram per digit in LDS)
+// finds the threshold key and how many rows equal to it are kept; then each
+// thread takes a contiguous segment of rows, the counts above and at the
+// threshold are scanned across the threads, and the kept rows are written in
+// ascending order (rows at the threshold: the lower ones first).
+__device__ __forceinline__ uint32_t order_key(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+// inclusive scan of v over the workgroup's threads through LDS (buf: kThreads ints)
+__device__ __forceinline__ int wg_scan_incl(int v, int* buf) {
+  buf[threadIdx.x] = v;
+  __syncthreads();
+  for (int o = 1; o < kThreads; o <<= 1) {
+    const int a = (int)threadIdx.x >= o ? buf[threadIdx.x - o] : 0;
+    __syncthreads();
+    buf[threadIdx.x] += a;
+    __syncthreads();
+  }
+  return buf[threadIdx.x];
+}
+__device__ __forceinline__ void phase_topk(const LayerParams& p, int L, char* smem) {
+  const int t = blockIdx.x;
+  if (t >= p.T) return;
+  const int K = p.itopk, n = L + t + 1;
+  int32_t* out = p.isel + (long long)t * K;
+  if (n <= K) {
+    for (int i = threadIdx.x; i < n; i += kThreads) out[i] = i;
+    return;
+  }
+  const float* sc = p.iscore + (long long)t * p.imax;
+  int* hist = reinterpret_cast<int*>(smem);                        // [256]
+  uint32_t* st = reinterpret_cast<uint32_t*>(smem + 1024);         // prefix, mask, rows still to take
+  int* sbuf = reinterpret_cast<int*>(smem + 2048);                 // [kThreads]
+  if (threadIdx.x == 0) {
+    st[0] = 0u;
+    st[1] = 0u;
+    st[2] = (uint32_t)K;
+  }
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    if (threadIdx.x < 256) hist[threadIdx.x] = 0;
+    __syncthreads();
+    const uint32_t prefix = st[0], mask = st[1];
+    for (int i = threadIdx.x; i < n; i += kThreads) {
+      const uint32_t u = order_key(ldg(sc + i));
+      if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1);
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const int need = (int)st[2];
+      int cum = 0, dg = 0;
+      for (int b = 255; b >= 0; --b) {
+        if (cum + hist[b] >= need) {
+          dg = b;
+          break;
+        }
+        cum += hist[b];
+      }
+      st[0] = prefix | ((uint32_t)dg << shift);
+      st[1] = mask | (255u << shift);
+      st[2] = (uint32_t)(need - cum);
+    }
+    __syncthreads();
+  }
+  const uint32_t thr = st[0];
+  const int need = (int)st[2];                                     // rows equal to the threshold kept
+  const int seg = (n + kThreads - 1) / kThreads;
+  const int i0 = min(n, (int)threadIdx.x * seg), i1 = min(n, i0 + seg);
+  int ngt = 0, neq = 0;
+  for (int i = i0; i < i1; ++i) {
+    const uint32_t u = order_key(ldg(sc + i));
+    ngt += u > thr;
+    neq += u == thr;
+  }
+  const int gt_base = wg_scan_incl(ngt, sbuf) - ngt;
+  __syncthreads();
+  const int eq_base = wg_scan_incl(neq, sbuf) - neq;
+  int pos = gt_base + min(eq_base, need), eq = eq_base;
+  for (int i = i0; i < i1; ++i) {
+    const uint32_t u = order_key(ldg(sc + i));
+    if (u > thr) {
+      out[pos++] = i;
+    } else if (u == thr) {
+      if (eq < need) out[pos++] = i;
+      ++eq;
     }
   }
 }
@@ -733,7 +915,11 @@ __device__ __forceinline__ void attn_splits(int NQT, int Lt, int& s_kv, int& SK)
 // blocks, staged in its LDS slice and read transposed).  The next chunk's key
 // rows are requested before the current chunk is used.  At the end the four
 // pairs' (m, l, Z) are merged in LDS.
-template <int KF, int KBMAX, int DBMAX, bool EXACT>
+// SP (sparse attention): query tile qt holds 16 heads of one verify row t (n_heads
+// is a multiple of 16), and its keys are that row's kept cache rows (isel), of
+// which there are min(idx_topk, L + t + 1); the splits cut min(idx_topk, L + T)
+// positions of the kept list.
+template <int KF, int KBMAX, int DBMAX, bool EXACT, bool SP = false>
 __device__ __forceinline__ void phase_attention(const LayerParams& p, int L, char* smem) {
   typedef typename AttnTypes<KF>::E E;
   constexpr int KBW = AttnTypes<KF>::KBW;
@@ -746,7 +932,7 @@ __device__ __forceinline__ void phase_attention(const LayerParams& p, int L, cha
   constexpr int DBH = (NLMAX + 1) / 2 * PB;            // value blocks per half, at most
   const int T = p.T, nh = p.nh;
   const int dc = EXACT ? 16 * DBMAX : p.dc, kvw = EXACT ? KBMAX * KBW : p.kvw;
-  const int NQ = T * nh, NQT = (NQ + 15) / 16, Lt = L + T;
+  const int NQ = T * nh, NQT = (NQ + 15) / 16, Lt = SP ? min(p.itopk, L + T) : L + T;
   const int nlat = EXACT ? NLMAX : dc / KBW, KB = EXACT ? KBMAX : kvw / KBW, nrope = KB - nlat;
   const int la = (nlat + 1) / 2, ra = nrope / 2;
   int s_kv, SK;
@@ -765,13 +951,16 @@ __device__ __forceinline__ void phase_attention(const LayerParams& p, int L, cha
   f32x4* sx = reinterpret_cast<f32x4*>(smem + (((long long)kWaves * 16 * CSH + 16LL * QS) * sizeof(E) + 15) / 16 * 16);
   const E* qlane = qs + j * QS + g * (KBW / 4);
   const uint8_t* kvb = reinterpret_cast<const uint8_t*>(p.kv);
-  const long long rb = kv_row_bytes(KF, kvw);
+  const long long rb = kv_row_bytes(KF, p.kv_row);
   auto kblk = [&](int i) { return (EXACT ? i < NLMAX / 2 : i < nl) ? l0 + i : r0 + i - nl; };
   for (int u = blockIdx.x; u < units; u += gridDim.x) {
     const int qt = u / s_kv, s = u - qt * s_kv;
     const int qi = qt * 16 + j, qc = qi < NQ ? qi : NQ - 1;
     const int tq = qc / nh;
     const int limit = L + tq;                          // keys 0..limit are visible
+    const int tt = SP ? (qt * 16) / nh : 0;            // sparse: the tile's verify row
+    const int cnt = SP ? min(p.itopk, L + tt + 1) : 0; // sparse: its kept rows
+    const int32_t* kept = SP ? p.isel + (long long)tt * p.itopk : nullptr;
     const int k0 = s * SK, k1 = min(Lt, k0 + SK);
     const int nch = k1 > k0 ? (k1 - k0 + 15) / 16 : 0;
     const int nit = (nch + 3) / 4;                     // chunk rounds (the same for every wave)
@@ -780,7 +969,8 @@ __device__ __forceinline__ void phase_attention(const LayerParams& p, int L, cha
     KR ka[KHMAX], kn[KHMAX];
     float ksa = 1.f, ksn = 1.f;                        // fp8 rows: the key's row scale
     auto load_chunk = [&](int c, KR (&kr)[KHMAX], float& ks) {
-      const int key = min(k0 + c * 16 + j, Lt - 1);
+      const int pk = min(k0 + c * 16 + j, (SP ? cnt : Lt) - 1);
+      const int key = SP ? ldg(kept + pk) : pk;
       const uint8_t* row = kvb + key * rb;
       if constexpr (F8) {
 #pragma unroll
@@ -858,7 +1048,7 @@ __device__ __forceinline__ void phase_attention(const LayerParams& p, int L, cha
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int kk = kbase + 4 * g + e;
-        sc[e] = (kk <= limit && kk < k1) ? st[e] * p.scale : -INFINITY;
+        sc[e] = ((SP ? kk < cnt : kk <= limit) && kk < k1) ? st[e] * p.scale : -INFINITY;
         cmax = fmaxf(cmax, sc[e]);
       }
       cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
@@ -995,7 +1185,7 @@ __device__ __forceinline__ void phase_attention(const LayerParams& p, int L, cha
 constexpr int kMergeRows = 2;
 constexpr int kMergeSB = 12;                      // splits per thread per batch
 constexpr int kMergeXOff = 8192;                  // LDS: half-merge exchange after the z operand
-template <int AF>
+template <int AF, bool SP = false>
 __device__ __forceinline__ void phase_merge_uv(const LayerParams& p, int L, char* smem) {
   typedef typename Act<AF>::T A;
   constexpr int TK = tile_k(AF);
@@ -1003,7 +1193,7 @@ __device__ __forceinline__ void phase_merge_uv(const LayerParams& p, int L, char
   const int T = p.T, nh = p.nh, dc = p.dc, dh = p.dh;
   const int NQ = T * nh, NQT = (NQ + 15) / 16;
   int s_kv, SK;
-  attn_splits(NQT, L + T, s_kv, SK);
+  attn_splits(NQT, SP ? min(p.itopk, L + T) : L + T, s_kv, SK);
   const int TG = (T + kMergeRows - 1) / kMergeRows;
   const int U = nh * TG, XS = dc + kXPad, RT = dh / 16, KT = dc / TK, D4 = dc / 4;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, j = lane & 15, g = lane >> 4;
@@ -2020,6 +2210,7 @@ __device__ __forceinline__ void specialise(LayerParams& p) {
     p.E = s.E; p.topk = s.topk; p.nshared = s.nshared; p.f = s.f;
     p.sch.s_q = s.s_q;
     p.sch.grid_min = kSpecMinGrid;
+    if (p.itopk == 0) p.kv_row = s.dc + s.dr;
   }
 }
 
@@ -2035,7 +2226,10 @@ __device__ __forceinline__ void raise_model_fault(const LayerParams& p) {
 
 // LR: the layer has a low-rank query (W_DQ, q-norm, W_UQ; phase P0b between
 // P0 and P1, one grid barrier more) and may normalise its cached latent.
-template <int AF, int EF, int KF, int KBMAX, int DBMAX, bool EXACT, int SPEC, bool LR = false>
+// SP: sparse attention (indexer projections in P0, index keys cached in P1,
+// index scores P1b and top-k P1c, each followed by a grid barrier; attention
+// over the kept rows).
+template <int AF, int EF, int KF, int KBMAX, int DBMAX, bool EXACT, int SPEC, bool LR = false, bool SP = false>
 __global__ __launch_bounds__(kThreads, 1) void layer_kernel(LayerParams p) {
   specialise<SPEC>(p);
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -2045,7 +2239,7 @@ __global__ __launch_bounds__(kThreads, 1) void layer_kernel(LayerParams p) {
   // launches on the stream) and leaves before the first barrier
   if (p.model_fault && __hip_atomic_load(p.model_fault, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) return;
   const int L = p.L_dev ? ldg(p.L_dev) : p.L;
-  if (L < 0 || (long long)L + p.T > p.kv_capacity) {
+  if (L < 0 || (long long)L + p.T > p.kv_capacity || (SP && (long long)L + p.T > p.imax)) {
     // every workgroup reads the same L and leaves before the first barrier
     if (blockIdx.x == 0 && threadIdx.x == 0) {
       __hip_atomic_store(&p.bar->fault, kFaultKvRange, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -2065,10 +2259,10 @@ __global__ __launch_bounds__(kThreads, 1) void layer_kernel(LayerParams p) {
   if (blockIdx.x == 0 && threadIdx.x < kMaxSlots)
     __hip_atomic_store(&p.att_cnt[kSlotCnt + kSlotStride * threadIdx.x], 0u, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);   // slot completion counters
-  phase_qkv<AF, LR>(p, smem);
+  phase_qkv<AF, LR, SP>(p, smem);
   if (!grid_barrier(p, 0, flag)) return raise_model_fault(p);
   if constexpr (LR) {
-    phase_uq<AF>(p, smem);
+    phase_uq<AF, SP>(p, smem);
     if (!grid_barrier(p, 0, flag)) return raise_model_fault(p);
   }
   {
@@ -2077,18 +2271,24 @@ __global__ __launch_bounds__(kThreads, 1) void layer_kernel(LayerParams p) {
     const int gs = p.sch.grid_min > 0 ? p.sch.grid_min : (int)gridDim.x;   // never above the grid
     const int wa = (p.nh * (p.dc / 16) + gs - 1) / gs;
     if (wa <= kWaves / 2) {
-      if ((int)threadIdx.x < kThreads / 2) phase_absorb<AF, LR>(p);
-      else phase_rope_kv<KF, LR>(p, L, blockIdx.x * (kThreads / 2) + threadIdx.x - kThreads / 2,
-                                 gridDim.x * (kThreads / 2));
+      if ((int)threadIdx.x < kThreads / 2) phase_absorb<AF, LR, SP>(p);
+      else phase_rope_kv<KF, LR, SP>(p, L, blockIdx.x * (kThreads / 2) + threadIdx.x - kThreads / 2,
+                                     gridDim.x * (kThreads / 2));
     } else {
-      phase_rope_kv<KF, LR>(p, L, blockIdx.x * kThreads + threadIdx.x, gridDim.x * kThreads);
-      phase_absorb<AF, LR>(p);
+      phase_rope_kv<KF, LR, SP>(p, L, blockIdx.x * kThreads + threadIdx.x, gridDim.x * kThreads);
+      phase_absorb<AF, LR, SP>(p);
     }
   }
   if (!grid_barrier(p, 1, flag)) return raise_model_fault(p);
-  phase_attention<KF, KBMAX, DBMAX, EXACT>(p, L, smem);
+  if constexpr (SP) {
+    phase_iscore<LR>(p, L, smem);
+    if (!grid_barrier(p, 1, flag)) return raise_model_fault(p);
+    phase_topk(p, L, smem);
+    if (!grid_barrier(p, 1, flag)) return raise_model_fault(p);
+  }
+  phase_attention<KF, KBMAX, DBMAX, EXACT, SP>(p, L, smem);
   if (!grid_barrier(p, 2, flag)) return raise_model_fault(p);
-  phase_merge_uv<AF>(p, L, smem);
+  phase_merge_uv<AF, SP>(p, L, smem);
   if (!grid_barrier(p, 3, flag)) return raise_model_fault(p);
   phase_wo<AF>(p, smem);
   if (!grid_barrier(p, 4, flag)) return raise_model_fault(p);

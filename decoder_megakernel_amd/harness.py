@@ -14,8 +14,8 @@ import synth
 from synth import recipe
 from synth.configs import LayerShape
 
-from . import (FORMATS, MK_T_EXPERT, MK_T_WDKV, MK_T_WDQ, MK_T_WO, MK_T_WQ, MK_T_WR, MK_T_WUK, MK_T_WUQ, MK_T_WUV,
-               Layer,
+from . import (FORMATS, MK_T_EXPERT, MK_T_WDKV, MK_T_WDQ, MK_T_WIDX, MK_T_WO, MK_T_WQ, MK_T_WR, MK_T_WUK, MK_T_WUQ,
+               MK_T_WUV, Layer,
                LayerWeights, Model, head_packed_bytes, kv_bytes, layer_state_bytes, layer_workspace_bytes,
                make_config, model_state_bytes, pack_expert, pack_head, pack_head_fp8, pack_tensor, packed_bytes)
 
@@ -23,7 +23,9 @@ from . import (FORMATS, MK_T_EXPERT, MK_T_WDKV, MK_T_WDQ, MK_T_WO, MK_T_WQ, MK_T
 def config_of(s: LayerShape):
     return make_config(s.d, s.n_h, s.d_h, s.d_c, s.d_r, s.E, s.top_k, s.n_shared, s.f, s.attn_fmt, s.exp_fmt,
                        s.kv_fmt, has_router_bias=1 if s.routing == "skew" else 0, rms_eps=s.eps,
-                       rope_base=s.rope_base, q_lora_rank=s.q_lora, kv_norm=1 if s.kv_norm else 0)
+                       rope_base=s.rope_base, q_lora_rank=s.q_lora, kv_norm=1 if s.kv_norm else 0,
+                       idx_heads=s.idx_heads, idx_dim=s.idx_dim, idx_topk=s.idx_topk,
+                       idx_max_rows=s.capacity if s.idx_topk else 0)
 
 
 def _dev(device):
@@ -106,8 +108,8 @@ class DeviceLayer:
         cfg = self.cfg
         self.packed = {}
         shapes = recipe.attn_shapes(s)
-        for name, tid in (("wq", MK_T_WQ), ("wdq", MK_T_WDQ), ("wuq", MK_T_WUQ), ("wdkv", MK_T_WDKV),
-                          ("wuk", MK_T_WUK), ("wuv", MK_T_WUV), ("wo", MK_T_WO), ("wr", MK_T_WR)):
+        for name, tid in (("wq", MK_T_WQ), ("wdq", MK_T_WDQ), ("wuq", MK_T_WUQ), ("widx", MK_T_WIDX),
+                          ("wdkv", MK_T_WDKV), ("wuk", MK_T_WUK), ("wuv", MK_T_WUV), ("wo", MK_T_WO), ("wr", MK_T_WR)):
             if name not in shapes:
                 continue
             src = _gen_attn_tensor(s, name, shapes[name], seed, layer, device)
@@ -152,7 +154,7 @@ class DeviceLayer:
                          self.packed["wuv"].data_ptr(), self.packed["wo"].data_ptr(), self.packed["wr"].data_ptr(),
                          None if self.rbias is None else self.rbias.data_ptr(), None,
                          ptr("wdq"), ptr("wuq"), None if self.gq is None else self.gq.data_ptr(),
-                         None if self.gkv is None else self.gkv.data_ptr())
+                         None if self.gkv is None else self.gkv.data_ptr(), ptr("widx"))
         self.layer = Layer(cfg, w, ptrs, self.state.data_ptr(), self.workspace.data_ptr(), device)
 
     def step(self, hin: torch.Tensor, T: int, kv: torch.Tensor, length: int, hout: torch.Tensor, stream: int = 0):

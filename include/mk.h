@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define MK_ABI_VERSION 2
+#define MK_ABI_VERSION 3
 #define MK_MAX_T 8           /* verify rows per step: k drafts + 1, at most 8 */
 #define MK_STATIC_SCRATCH_BYTES (32u << 20)   /* scratch of mk_decode_step_static, per GPU */
 
@@ -119,6 +119,20 @@ typedef struct mk_layer_config {
                                 6000 at single-stream decode", section "Where the 11.2 ms goes") */
   int32_t kv_norm;           /* 1: RMSNorm (gain gamma_kv) of the latent c before it is cached
                                 (the RoPE key is not normalised); with q_lora_rank > 0 only */
+  /* Sparse attention (idx_topk > 0): the pages' sparse attention mode with an indexer ("Why one
+   * GB300 ...", sections "Where the 11.2 ms goes" and "Corrections to things we said"), as the
+   * lightning indexer of the DeepSeek-V3.2 report.  Per verify row t: q^I = W_IQ x [idx_heads]
+   * [idx_dim], w^I = W_IW x [idx_heads], the row's index key k^I = W_IK x (x: the RMSNorm-1
+   * output), cached after the RoPE key (a cache row holds d_latent + d_rope + idx_dim values);
+   * score of cache row s <= L + t: sum_j w^I_j max(0, q^I_j . k^I_s); the row attends to its
+   * idx_topk highest-scoring rows (ties to the lower row; every row when L + t + 1 <= idx_topk).
+   * Needs bf16 attention and cache, n_heads a multiple of 16, idx_heads a multiple of 16,
+   * idx_dim a multiple of 32, idx_heads * idx_dim <= 8192, idx_topk <= 8192. */
+  int32_t idx_heads;
+  int32_t idx_dim;
+  int32_t idx_topk;
+  int32_t idx_max_rows;      /* sparse: the largest L + T a step may use (sizes the workspace's
+                                index scores); a step past it is refused */
 } mk_layer_config;
 
 typedef struct mk_device_info {
@@ -139,7 +153,9 @@ typedef enum mk_tensor {
   MK_T_WQ = 0, MK_T_WDKV = 1, MK_T_WUK = 2, MK_T_WUV = 3, MK_T_WO = 4, MK_T_WR = 5,
   MK_T_EXPERT = 6,           /* W1, W3, W2 (and fp8 or MXFP4 scales) of one expert in one block */
   MK_T_WDQ = 7,              /* W_DQ [q_lora_rank][d_model] (q_lora_rank > 0) */
-  MK_T_WUQ = 8               /* W_UQ [n_heads*(d_head+d_rope)][q_lora_rank], rows as W_Q's */
+  MK_T_WUQ = 8,              /* W_UQ [n_heads*(d_head+d_rope)][q_lora_rank], rows as W_Q's */
+  MK_T_WIDX = 9              /* sparse attention: [W_IQ; W_IW; W_IK] rows [idx_heads*idx_dim +
+                                idx_heads + idx_dim][d_model] (W_IQ row j*idx_dim + m = head j, dim m) */
 } mk_tensor;
 
 /* Packed layer weights (device pointers). */
@@ -160,6 +176,7 @@ typedef struct mk_layer_weights {
   const void* wuq;           /*   NULL), gamma_q [q_lora_rank] fp32; NULL otherwise                  */
   const float* gamma_q;
   const float* gamma_kv;     /* kv_norm: [d_latent] fp32; NULL otherwise */
+  const void* widx;          /* sparse attention: packed MK_T_WIDX; NULL otherwise */
 } mk_layer_weights;
 
 /* KV cache of one layer: `capacity` rows in kv_format (mk_kv_bytes gives the
@@ -273,7 +290,9 @@ int mk_decode_step_static(mk_layer* layer, const float* hidden_in, int T, const 
  * 3 = o [T][n_h*d_head] (fp32 for F32 layers, else bf16 bit patterns: it is kept
  * in the matrix-core operand format), 4 = post-attention hidden [T][d_model],
  * 5 = router logits [T][n_experts], 6 = selected experts int32 [T][top_k],
- * 7 = gates [T][top_k].
+ * 7 = gates [T][top_k]; sparse attention: 8 = kept cache rows int32 [T][idx_topk]
+ * (ascending; row t keeps min(idx_topk, L + t + 1)), 9 = index scores fp32
+ * [T][idx_max_rows] (row t: columns 0 .. L + T - 1 written).
  * Valid only after a step on this layer and before another layer reuses the workspace
  * (the workspace that step used: the layer's own, or the static scratch). */
 int mk_debug_tap(mk_layer* layer, int tap, void* host_dst, size_t bytes, void* stream);

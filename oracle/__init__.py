@@ -47,7 +47,8 @@ class Weights(ctypes.Structure):
     _fields_ = [("gamma1", _vp), ("gamma2", _vp), ("wq", _vp), ("wdkv", _vp), ("wuk", _vp),
                 ("wuv", _vp), ("wo", _vp), ("wr", _vp), ("router_bias", _vp),
                 ("w1", _vp), ("w3", _vp), ("w2", _vp), ("s1", _vp), ("s3", _vp), ("s2", _vp),
-                ("wdq", _vp), ("wuq", _vp), ("gamma_q", _vp), ("gamma_kv", _vp), ("widx", _vp)]
+                ("wdq", _vp), ("wuq", _vp), ("gamma_q", _vp), ("gamma_kv", _vp), ("widx", _vp),
+                ("force_isel", _vp)]
 
 
 class AttnTaps(ctypes.Structure):
@@ -149,7 +150,9 @@ class _WeightsHolder:
                               ctypes.cast(ptrs["w2"], _vp), ctypes.cast(ptrs["s1"], _vp),
                               ctypes.cast(ptrs["s3"], _vp), ctypes.cast(ptrs["s2"], _vp),
                               keep(w.get("wdq")), keep(w.get("wuq")), keep(w.get("gamma_q")),
-                              keep(w.get("gamma_kv")), keep(w.get("widx")))
+                              keep(w.get("gamma_kv")), keep(w.get("widx")),
+                              keep(None if w.get("force_isel") is None
+                                   else np.ascontiguousarray(w["force_isel"], dtype=np.int32)))
 
 
 def _chk(rc, what):

@@ -371,6 +371,7 @@ int orc_attn_block(const orc_cfg* c, const orc_weights* w, const float* H, int T
     if (sparse) {
       matvec(&WIQ, x, qi);
       matvec(&WIW, x, wi);
+#pragma omp parallel for schedule(static)
       for (long j = 0; j <= pos; ++j) {
         float sc = 0.0f;
         for (int hh = 0; hh < HI; ++hh) {
@@ -382,6 +383,8 @@ int orc_attn_block(const orc_cfg* c, const orc_weights* w, const float* H, int T
         if (taps && taps->iscore) taps->iscore[(long)i * (L + T) + j] = sc;
       }
       nsel = select_rows(isc, pos, KI, sel);
+      if (w->force_isel)
+        for (long u = 0; u < nsel; ++u) sel[u] = w->force_isel[(long)i * KI + u];
       if (taps && taps->sel)
         for (int t = 0; t < KI; ++t) taps->sel[(long)i * KI + t] = t < nsel ? (int32_t)sel[t] : -1;
     } else {
@@ -680,6 +683,7 @@ int orc_layer_step_f64(const orc_cfg* c, const orc_weights* w, const float* H, i
     const long pos = (long)L + i;
     long nsel = pos + 1;
     if (sparse) {
+#pragma omp parallel for schedule(static)
       for (long j = 0; j <= pos; ++j) {
         double sc = 0.0;
         for (int hh = 0; hh < HI; ++hh) {
@@ -690,6 +694,8 @@ int orc_layer_step_f64(const orc_cfg* c, const orc_weights* w, const float* H, i
         isc[j] = sc;
       }
       nsel = select_rows(isc, pos, KI, selr);
+      if (w->force_isel)
+        for (long u = 0; u < nsel; ++u) selr[u] = w->force_isel[(long)i * KI + u];
     } else {
       for (long j = 0; j <= pos; ++j) selr[j] = j;
     }

@@ -144,6 +144,8 @@ typedef struct orc_weights {
   const float* gamma_q;
   const float* gamma_kv;    /* kv_norm: [d_c] */
   const void* widx;         /* sparse: [W_IQ; W_IW; W_IK] rows [H_I*d_I + H_I + d_I][d] (attn_fmt) */
+  const int32_t* force_isel;/* sparse, optional: kept rows [T][idx_topk] to use instead of the
+                               selection (the scores are still computed and tapped) */
 } orc_weights;
 
 /* Optional intermediate outputs (any pointer may be NULL). */

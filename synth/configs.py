@@ -94,9 +94,12 @@ C3XK = C3X.with_(name="mxfp4_fp8kv_E384_T8_L8192", kv_fmt="fp8row")
 C5XK = C5X.with_(name="stack32_mxfp4_fp8kv_E384_T6_L4096", kv_fmt="fp8row")
 # The layer variant with a low-rank query (rank 1536, q-norm) and the latent norm.
 C3Q = C3.with_(name="fp8_lowrankq_E384_T8_L8192", q_lora=1536, kv_norm=True)
-PRESETS = {s.name: s for s in (C0, C1, C2, C3, C4, C5, C3X, C5X, C3XK, C5XK, C3Q)}
+# The long-context layer with sparse attention: an indexer of 64 heads x 128
+# dims, each verify row attends to its top 2048 cache rows.
+C4S = C4.with_(name="fp8_sparse2048_E384_T6_L65536_skew", idx_heads=64, idx_dim=128, idx_topk=2048)
+PRESETS = {s.name: s for s in (C0, C1, C2, C3, C4, C5, C3X, C5X, C3XK, C5XK, C3Q, C4S)}
 BY_KEY = {"C0": C0, "C1": C1, "C2": C2, "C3": C3, "C4": C4, "C5": C5, "C3X": C3X, "C5X": C5X,
-          "C3XK": C3XK, "C5XK": C5XK, "C3Q": C3Q}
+          "C3XK": C3XK, "C5XK": C5XK, "C3Q": C3Q, "C4S": C4S}
 
 # Skewed routing: the hot set is the first ceil(0.2 E) experts of a seeded permutation.
 HOT_FRACTION = 0.2

@@ -100,16 +100,28 @@ def gpu_step(dl, s, H_dev, kv_dev, L, T=None):
         buf = np.empty(shape, dt)
         dl.layer.debug_tap(tap, buf)
         taps[name] = oracle.bf16_to_f32(buf) if dt == np.uint16 else buf
+    if s.idx_topk:
+        for name, tap, shape, dt in (("isel", 8, (T, s.idx_topk), np.int32), ("iscore", 9, (T, s.capacity), np.float32)):
+            buf = np.empty(shape, dt)
+            dl.layer.debug_tap(tap, buf)
+            taps[name] = buf
     kvn = kv_dev[L:L + T].cpu().numpy()
     taps["kv_raw"] = kvn
     return out.cpu().numpy(), kv_to_f32(kvn, s.kv_fmt, s.kvw), taps
 
 
 def oracle_step(s, seed, layer, H, L, kv_host=None, force_sel=None, full_weights=None, base_weights=None,
-                expert_fn=None):
+                expert_fn=None, force_isel=None):
     """Oracle layer step on the host copies of the same seeded inputs (kv_host
-    is written in place).  Returns (out, new KV rows float32, taps, weights used)."""
+    is written in place).  force_isel: sparse attention's kept rows to use.
+    Returns (out, new KV rows float32, taps, weights used)."""
     kv = recipe.kv_prefill_host(s, seed, layer) if kv_host is None else kv_host
+    if force_isel is not None:
+        if full_weights is not None:
+            full_weights = dict(full_weights, force_isel=force_isel)
+        else:
+            base = base_weights if base_weights is not None else recipe.layer_weights_host(s, seed, layer, experts=[])
+            base_weights = dict(base, force_isel=force_isel)
     if full_weights is not None:
         out, taps = oracle.layer_step(s, full_weights, H, kv, L, force_sel=force_sel)
         w = full_weights
@@ -141,14 +153,48 @@ def compare_selection(s, gpu_sel, ora_logits, ora_sel):
     return near, forced
 
 
+def compare_kept_rows(s, g_taps, o_taps, L):
+    """Sparse attention: the GPU's index scores against the oracle's (bf16 index
+    queries on the GPU: the bf16 bound), and its kept rows (ascending, the right
+    count per row).  Where the kept sets differ, every row the GPU keeps and the
+    oracle drops must score within that bound of the oracle's k-th score.
+    Returns (rows kept differently, whether the oracle must follow the GPU)."""
+    K = s.idx_topk
+    near, forced = 0, False
+    for t in range(g_taps["isel"].shape[0]):
+        n = L + t + 1
+        cnt = min(K, n)
+        g = g_taps["isel"][t][:cnt].tolist()
+        o = o_taps["isel"][t][:cnt].tolist()
+        assert g == sorted(g) and len(set(g)) == cnt and 0 <= g[0] and g[-1] < n, (t, g[:8], g[-8:])
+        osc = o_taps["iscore"][t][:n].astype(np.float64)
+        assert normwise(g_taps["iscore"][t:t + 1, :n], osc[None]) <= TOL["bf16"], t
+        if set(g) != set(o):
+            kth = np.sort(osc)[::-1][cnt - 1]
+            band = TOL["bf16"] * np.abs(osc).max()
+            for r in set(g) - set(o):
+                assert osc[r] >= kth - band, (t, r, osc[r], kth, band)
+            near += len(set(g) - set(o))
+            forced = True
+    return near, forced
+
+
 def check_layer(s, seed, layer, g_out, g_kv, g_taps, H, L, kv_host=None, full_weights=None, report=None,
                 base_weights=None, expert_fn=None):
     """Full parity check of one step against the oracle.  Returns a dict of errors."""
     kw = dict(full_weights=full_weights, base_weights=base_weights, expert_fn=expert_fn)
+    kv0 = None if kv_host is None else kv_host.copy()
     o_out, o_kv, o_taps, w = oracle_step(s, seed, layer, H, L, kv_host=kv_host, **kw)
+    rows_near, rows_forced = 0, False
+    if s.idx_topk:
+        rows_near, rows_forced = compare_kept_rows(s, g_taps, o_taps, L)
+        if rows_forced:
+            kvh = recipe.kv_prefill_host(s, seed, layer) if kv0 is None else kv0.copy()
+            kw["force_isel"] = g_taps["isel"]
+            o_out, o_kv, o_taps, w = oracle_step(s, seed, layer, H, L, kv_host=kvh, **kw)
     near, forced = compare_selection(s, g_taps["sel"], o_taps["logits"], o_taps["sel"])
     if forced:
-        kvh = recipe.kv_prefill_host(s, seed, layer) if kv_host is None else kv_host
+        kvh = recipe.kv_prefill_host(s, seed, layer) if kv0 is None else kv0.copy()
         o_out, o_kv, o_taps, w = oracle_step(s, seed, layer, H, L, kv_host=kvh, force_sel=g_taps["sel"], **kw)
     tols = tols_of(s)
     errs = {
@@ -159,6 +205,9 @@ def check_layer(s, seed, layer, g_out, g_kv, g_taps, H, L, kv_host=None, full_we
         "near_ties": near,
         "forced": bool(forced),
     }
+    if s.idx_topk:
+        errs["kept_rows_differing"] = rows_near
+        errs["kept_rows_forced"] = bool(rows_forced)
     if report is not None:
         report.update(errs)
     if s.kv_fmt == "fp8row":

@@ -27,7 +27,7 @@ def test_library_exports_every_header_function():
 
 def test_abi_version():
     import decoder_megakernel_amd as mk
-    assert mk.abi_version() == mk.MK_ABI_VERSION == 2
+    assert mk.abi_version() == mk.MK_ABI_VERSION == 3
 
 
 def _cfg(**kw):
@@ -71,6 +71,11 @@ def test_valid_configs_pass_and_sizes():
     (dict(q_lora_rank=8192), -8),
     (dict(kv_norm=1), -8),
     (dict(kv_norm=2, q_lora_rank=256), -1),
+    (dict(idx_topk=-1), -1),
+    (dict(idx_topk=2048, idx_heads=64, idx_dim=128, idx_max_rows=0), -1),
+    (dict(idx_topk=2048, idx_heads=60, idx_dim=128, idx_max_rows=70000), -8),
+    (dict(idx_topk=2048, idx_heads=64, idx_dim=128, idx_max_rows=70000, kv_format="fp8row"), -8),
+    (dict(idx_topk=2048, idx_heads=256, idx_dim=32, idx_max_rows=70000), -8),
 ])
 def test_invalid_configs_are_refused(kw, code):
     import decoder_megakernel_amd as mk
@@ -125,3 +130,11 @@ def test_lowrank_query_config_and_packed_sizes():
     with pytest.raises(mk.MkError) as ei:
         mk.packed_bytes(_cfg(), mk.MK_T_WDQ)
     assert ei.value.code == mk.MK_ERR_INVALID_ARG
+
+
+def test_sparse_attention_config_and_sizes():
+    import decoder_megakernel_amd as mk
+    cfg = _cfg(idx_heads=64, idx_dim=128, idx_topk=2048, idx_max_rows=70000)
+    mk.check_config(cfg)
+    assert mk.packed_bytes(cfg, mk.MK_T_WIDX) == (64 * 128 + 64 + 128) * 4096 * 2
+    assert mk.kv_bytes(cfg, 1000) == 1000 * (512 + 64 + 128) * 2

@@ -195,3 +195,31 @@ def test_full_size_lowrank_query_fp8_E384_T8_L8192():
 def test_full_size_lowrank_query_mxfp4_fp8kv_E384_T8_L8192():
     from synth.configs import C3XK
     _run(C3XK.with_(name="mxfp4_fp8kv_lowrankq_E384_T8_L8192", q_lora=1536, kv_norm=True), full_weights=False)
+
+
+# Sparse attention (indexer + top-k kept rows): 16 heads per query tile, 100
+# rows kept of ~300; with a low-rank query; with MXFP4 experts; and a top-k
+# that covers every row (the dense attention).
+MID_SP = LayerShape("mid_sparse", d=1024, n_h=16, d_h=64, d_c=128, d_r=32, E=32, top_k=4, n_shared=1, f=256,
+                    T=6, L=300, attn_fmt="bf16", exp_fmt="fp8", kv_fmt="bf16", idx_heads=16, idx_dim=64, idx_topk=100)
+MID_SP_LR = MID_SP.with_(name="mid_sparse_lowrank", q_lora=256, kv_norm=True)
+MID_SP_MX = MID_SP.with_(name="mid_sparse_mxfp4", exp_fmt="mxfp4")
+MID_SP_ALL = MID_SP.with_(name="mid_sparse_topk_covers_all", idx_topk=512)
+
+
+@pytest.mark.parametrize("shape", [MID_SP, MID_SP_LR, MID_SP_MX, MID_SP_ALL], ids=lambda s: s.name)
+def test_sparse_attention_shapes_match_oracle(shape):
+    _run(shape)
+
+
+def test_sparse_attention_single_row_empty_cache():
+    _run(MID_SP, L=0, T=1)
+
+
+def test_sparse_attention_rows_just_past_topk():
+    _run(MID_SP, L=97, T=6)
+
+
+def test_full_size_sparse_fp8_E384_T6_L65536_skew():
+    from synth.configs import C4S
+    _run(C4S, full_weights=False)

@@ -63,7 +63,8 @@ def test_oracle_and_generator_under_address_and_ub_sanitizers(tmp_path):
 
 @pytest.mark.skipif(not os.path.exists(HIPCC), reason="no hipcc")
 def test_abi_host_code_under_address_and_ub_sanitizers(tmp_path):
-    objs = [os.path.join(CSRC, n) for n in ("mk_layer.o", "mk_layer_kv8.o", "mk_layer_lr.o", "mk_layer_lr_spec.o", "mk_pack.o", "mk_stack.o")]
+    objs = [os.path.join(CSRC, n) for n in ("mk_layer.o", "mk_layer_kv8.o", "mk_layer_lr.o", "mk_layer_lr_spec.o", "mk_layer_sparse.o", "mk_pack.o",
+                                             "mk_stack.o")]
     if not all(os.path.exists(o) for o in objs):
         pytest.skip("the library's kernel objects are not built (run __graft_entry__.build())")
     # sanitizers for the host pass only (the kernels are not instrumented)
