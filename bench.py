@@ -140,6 +140,10 @@ def pct(xs):
 
 
 # ---------------------------------------------------------------- in-kernel trace: barrier share
+# the phase that ends at each barrier slot of a layer launch, then the last phase
+PHASE_NAMES = {0: "P0 Q/KV proj", 8: "P0b W_UQ", 1: "P1 RoPE+absorb", 9: "P1b index scores", 10: "P1c top-k",
+               2: "P2 attention", 3: "P3 merge+W_UV", 4: "P4 W_O", 5: "P5 norm+router", 6: "P6 gate/up",
+               7: "P6/7 experts", 11: "P8 combine"}
 def trace_summary(layers, run_once):
     """Runs one untimed step with the layers' in-kernel trace on and returns the
     mean over the traced launches of: time in grid barriers (from the last
@@ -156,28 +160,27 @@ def trace_summary(layers, run_once):
         tr = np.zeros((st.grid_wgs, stride), np.int64)
         dl.layer.read_trace(tr)
         start, end = tr[:, 0], tr[:, 1 + 2 * nb]
+        # the barrier slots a launch used, in the order it reached them
+        used = [k for k in range(nb) if (tr[:, 1 + 2 * k] != 0).any()]
+        used.sort(key=lambda k: np.median(tr[:, 2 + 2 * k]))
         prev = start
-        bsum, ph = 0.0, []
-        for k in range(nb):
+        bsum, ph = 0.0, {}
+        for k in used:
             arr, rel = tr[:, 1 + 2 * k], tr[:, 2 + 2 * k]
-            if (arr == 0).all():
-                continue
-            ph.append((arr.max() - prev.min()) / 100.0)
+            ph[PHASE_NAMES[k]] = (arr.max() - prev.min()) / 100.0
             bsum += (np.median(rel) - arr.max()) / 100.0
             prev = rel
-        ph.append((end.max() - prev.min()) / 100.0)
+        ph[PHASE_NAMES[nb]] = (end.max() - prev.min()) / 100.0
         totals.append((end.max() - start.min()) / 100.0)
         bars.append(bsum)
         phases.append(ph)
     for dl in layers:
         dl.layer.set_trace(False)
-    n = min(len(p) for p in phases)
+    names = [k for k in phases[0] if all(k in p for p in phases)]
     return {"barrier_share": round(float(np.mean(bars) / np.mean(totals)), 4),
             "barrier_us_per_launch": round(float(np.mean(bars)), 2),
             "in_kernel_us_per_launch": round(float(np.mean(totals)), 2),
-            "phase_critical_path_us": [round(float(np.mean([p[i] for p in phases])), 2) for i in range(n)],
-            "phases": "P0 Q/KV proj, P1 RoPE+absorb, P2 attention, P3 merge+W_UV, P4 W_O, P5 norm+router, "
-                      "P6/7 experts, P8 combine",
+            "phase_critical_path_us": {k: round(float(np.mean([p[k] for p in phases])), 2) for k in names},
             "launches_traced": len(layers)}
 
 

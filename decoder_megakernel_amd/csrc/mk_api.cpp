@@ -94,10 +94,11 @@ int check_cfg(const mk_layer_config* c) {
     if (D.nh % 16 || D.ih <= 0 || D.ih % 16 || D.idm <= 0 || D.idm % 32 || D.ih * D.idm > 8192 || D.ik > 8192)
       return fail(MK_ERR_UNSUPPORTED_SHAPE, "sparse attention: n_heads and idx_heads multiples of 16, idx_dim a "
                                             "multiple of 32, idx_heads * idx_dim <= 8192, idx_topk <= 8192");
-    if (D.imax < 1 || D.imax > (1 << 24)) return fail(MK_ERR_INVALID_ARG, "idx_max_rows must be in [1, 2^24]");
-    // the index scores phase stages every row's index queries (bf16, 8 pad per head) and weights in LDS
-    if ((long long)kMaxT * D.ih * (D.idm + 8) * 2 + 16 + (long long)kMaxT * D.ih * 4 > kLdsBytes - 1024)
-      return fail(MK_ERR_UNSUPPORTED_SHAPE, "idx_heads * (idx_dim + 8) too large for the LDS plan");
+    if (D.imax < 4 || D.imax > (1 << 24) || D.imax % 4)
+      return fail(MK_ERR_INVALID_ARG, "idx_max_rows must be a multiple of 4 in [4, 2^24]");
+    // the index-score phase holds a row's index queries in 16 fragments per lane and
+    // stages 512 index keys (bf16, 8 pad each) and the head weights in LDS
+    if (D.idm > 128) return fail(MK_ERR_UNSUPPORTED_SHAPE, "idx_dim must be <= 128");
   }
   // the one-wave-per-row cache writer (fp8 cache, low-rank variant) forms one key RoPE pair per lane
   if ((D.kf == MK_FMT_FP8_ROW || D.ql > 0) && D.dr > 128)
@@ -236,7 +237,7 @@ int device_info(int dev, DevInfo* di, LayerKernelFn fn) {
 
 struct WsLayout {
   size_t qkv_part, qrope, qabs, att_part, att_ml, z, o, hp, route_sel, route_gate, route_cand, logits, hbuf,
-      ybuf, dummy, qbuf, iscore, isel,
+      ybuf, dummy, qbuf, iq, iw, iscore, isel,
       total;
 };
 struct StLayout {
@@ -267,6 +268,8 @@ WsLayout ws_layout(const Dims& D, const Schedule& s) {
   w.ybuf = take((size_t)slots * T * D.d * 4);
   w.dummy = take(32768);
   w.qbuf = D.ql > 0 ? take((size_t)T * D.nq * 4) : 0;
+  w.iq = D.ik > 0 ? take((size_t)T * D.ih * D.idm * 2) : 0;
+  w.iw = D.ik > 0 ? take((size_t)T * D.ih * 4) : 0;
   w.iscore = D.ik > 0 ? take((size_t)T * D.imax * 4) : 0;
   w.isel = D.ik > 0 ? take((size_t)T * D.ik * 4) : 0;
   w.total = off;
@@ -303,6 +306,8 @@ void bind_workspace(LayerParams& p, const WsLayout& wl, char* ws) {
   p.ybuf = (float*)(ws + wl.ybuf);
   p.dummy = (const uint8_t*)(ws + wl.dummy);
   p.qbuf = wl.qbuf ? (float*)(ws + wl.qbuf) : nullptr;
+  p.iq = wl.iq ? (void*)(ws + wl.iq) : nullptr;
+  p.iw = wl.iw ? (float*)(ws + wl.iw) : nullptr;
   p.iscore = wl.iscore ? (float*)(ws + wl.iscore) : nullptr;
   p.isel = wl.isel ? (int32_t*)(ws + wl.isel) : nullptr;
 }

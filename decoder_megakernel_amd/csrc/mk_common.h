@@ -11,7 +11,7 @@ constexpr int kThreads = 512;            // threads per workgroup (8 wave64s)
 constexpr int kWaves = kThreads / 64;
 constexpr int kMaxT = MK_MAX_T;          // verify rows the LDS budget is sized for
 constexpr int kXPad = 8;                 // LDS row padding of activation operands (elements)
-constexpr int kBarriers = 8;             // grid barriers in one layer launch
+constexpr int kBarriers = 11;            // grid barrier slots of one layer launch (trace stamps)
 constexpr int kTraceX = 16;              // extra per-workgroup timestamps (sub-phase marks)
 constexpr int kTraceStride = 2 + 2 * kBarriers + kTraceX;
 constexpr int kLdsBytes = 160 * 1024 - 256;
@@ -134,6 +134,8 @@ struct LayerParams {
   // workspace
   float* qkv_part;         // [s_q][T][nq + kvw] (low-rank query: [s_q][T][ql + kvw])
   float* qbuf;             // low-rank query: q [T][nq]
+  void* iq;                // sparse: index queries, bf16 [T][ihead][idim]
+  float* iw;               // sparse: index head weights [T][ihead]
   float* iscore;           // sparse: index scores [T][idx_max_rows]
   int32_t* isel;           // sparse: kept rows [T][itopk], ascending
   int imax;                // sparse: idx_max_rows

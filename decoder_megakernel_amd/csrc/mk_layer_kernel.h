@@ -711,77 +711,132 @@ __device__ __forceinline__ void phase_absorb(const LayerParams& p) {
 }
 
 // ------------------------------------------------------------------ P1b, P1c sparse attention
-// Index scores: every workgroup stages the T rows' index queries q^I (bf16,
-// LDS row stride idx_dim + 8 per head) and weights w^I (fp32) from the split-K
-// partials; the cache rows [0, L + T) are cut into chunks of 16 spread over the
-// grid, and wave t < T scores verify row t against each chunk: S[key][head] =
-// k^I_key . q^I_head on the matrix cores (16 keys x 16 heads per product,
-// idim / 32 k-steps), then the sum over heads of w^I_head * max(0, S), the 16
-// head lanes added by shuffles.  Scores go to iscore[t][key].
+// Index queries: during P1 the grid sums the split-K partials of the indexer's
+// query rows q^I (T x idx_heads x idx_dim) into bf16 and of its head weights
+// w^I into fp32, once, so that every workgroup of the index-score phase reads
+// half the bytes of the fp32 partials.
 template <bool LR>
-__device__ __forceinline__ void phase_iscore(const LayerParams& p, int L, char* smem) {
+__device__ __forceinline__ void stage_index_queries(const LayerParams& p, int gi, int gn) {
   const int T = p.T, HI = p.ihead, dI = p.idim, S = p.sch.s_q;
   const int qoff = (LR ? p.ql : p.nq) + p.kvw, woff = qoff + HI * dI, nrow = woff + HI + dI;
-  const int HS = dI + 8, QS = HI * HS;                 // LDS strides (bf16): head, verify row
-  __bf16* qs = reinterpret_cast<__bf16*>(smem);
-  float* wsm = reinterpret_cast<float*>(smem + ((long long)kMaxT * QS * 2 + 15) / 16 * 16);
+  const int n4 = HI * dI / 4, nq4 = T * n4;
   const float* part = p.qkv_part;
-  const int n4 = HI * dI / 4;
-  for (int i = threadIdx.x; i < T * n4; i += kThreads) {
-    const int t = i / n4, e = (i - t * n4) * 4, h = e / dI, m = e - h * dI;
-    f32x4 a = {0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < S; ++s) a += ldg(reinterpret_cast<const f32x4*>(part + ((long long)s * T + t) * nrow + qoff + e));
-    store4<__bf16>(qs + t * QS + h * HS + m, a);
-  }
-  for (int i = threadIdx.x; i < T * HI; i += kThreads) {
-    const int t = i / HI, h = i - t * HI;
-    float a = 0.f;
-    for (int s = 0; s < S; ++s) a += ldg(part + ((long long)s * T + t) * nrow + woff + h);
-    wsm[t * HI + h] = a;
-  }
-  __syncthreads();
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, j = lane & 15, g = lane >> 4;
-  const int Lt = L + T, nch = (Lt + 15) / 16;
-  int c0, c1;
-  split_range(nch, gridDim.x, blockIdx.x, c0, c1);
-  if (w >= T) return;
-  const int nht = HI / 16, nkb = dI / 32;
-  const __bf16* kvb = reinterpret_cast<const __bf16*>(p.kv);
-  const __bf16* qrow = qs + w * QS + g * 8;
-  for (int c = c0; c < c1; ++c) {
-    const int key = min(c * 16 + j, Lt - 1);
-    const __bf16* krow = kvb + (long long)key * p.kv_row + p.kvw + g * 8;
-    float sc[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int ht = 0; ht < nht; ++ht) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      for (int kb = 0; kb < nkb; ++kb)
-        acc = mma_bf16_k32(__builtin_bit_cast(bf16x8, ld16(krow + kb * 32)),
-                           *reinterpret_cast<const bf16x8*>(qrow + (ht * 16 + j) * HS + kb * 32), acc);
-      const float wh = wsm[w * HI + ht * 16 + j];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) sc[e] += acc[e] > 0.f ? wh * acc[e] : 0.f;
-    }
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) sc[e] += __shfl_xor(sc[e], o);
-    if (j == 0) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int k = c * 16 + 4 * g + e;
-        if (k < Lt) p.iscore[(long long)w * p.imax + k] = sc[e];
-      }
+  for (int i = gi; i < nq4 + T * HI; i += gn) {
+    if (i < nq4) {
+      const int t = i / n4, e = (i - t * n4) * 4;
+      f32x4 a = {0.f, 0.f, 0.f, 0.f};
+      for (int s = 0; s < S; ++s) a += ldg(reinterpret_cast<const f32x4*>(part + ((long long)s * T + t) * nrow + qoff + e));
+      store4<__bf16>(reinterpret_cast<__bf16*>(p.iq) + (long long)t * HI * dI + e, a);
+    } else {
+      const int k = i - nq4, t = k / HI, h = k - t * HI;
+      float a = 0.f;
+      for (int s = 0; s < S; ++s) a += ldg(part + ((long long)s * T + t) * nrow + woff + h);
+      p.iw[k] = a;
     }
   }
 }
 
+// Index scores: the cache rows [0, L + T) are cut into chunks of 16 spread over
+// the grid; a workgroup stages up to kIdxBlk of its chunks' index keys in LDS
+// (bf16, row stride idx_dim + 8).  Wave w scores verify row t = w / (8 / T)
+// against every (8 / T)-th staged chunk, with that row's index queries held in
+// registers: S[head][key] = q^I_head . k^I_key on the matrix cores (16 heads x
+// 16 keys per product, idim / 32 k-steps), then the sum over heads of
+// w^I_head * max(0, S) -- four heads per lane, the four lane groups added by
+// shuffles.  Scores go to iscore[t][key] (row stride idx_max_rows, a multiple of 4).
+constexpr int kIdxBlk = 32;                       // chunks of 16 keys staged at a time
+static_assert(kIdxBlk * 16 * (128 + 8) * 2 + kMaxT * 256 * 4 <= kLdsBytes - 1024,
+              "index keys (idx_dim <= 128) and head weights (idx_heads <= 256) fit the LDS");
+template <int NKB>                                // idx_dim / 32
+__device__ __forceinline__ void iscore_rows(const LayerParams& p, int L, char* smem) {
+  constexpr int kMaxHt = 16 / NKB;                // idx_heads * idx_dim <= 8192: 16 query fragments per lane
+  const int T = p.T, HI = p.ihead, nht = HI / 16, dI = NKB * 32, KS = dI + 8;
+  __bf16* ks = reinterpret_cast<__bf16*>(smem);                              // [kIdxBlk * 16][KS]
+  float* wsm = reinterpret_cast<float*>(smem + kIdxBlk * 16 * KS * 2);       // [T][HI]
+  for (int i = threadIdx.x; i < T * HI; i += kThreads) wsm[i] = ldg(p.iw + i);
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, j = lane & 15, g = lane >> 4;
+  const int wpt = T < kWaves ? kWaves / T : 1;
+  const bool act = w < T * wpt;
+  const int t = act ? w / wpt : 0, sub = w - t * wpt;
+  bf16x8 qf[kMaxHt][NKB];
+  {
+    const __bf16* qrow = reinterpret_cast<const __bf16*>(p.iq) + (long long)t * HI * dI + g * 8;
+#pragma unroll
+    for (int ht = 0; ht < kMaxHt; ++ht)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+        qf[ht][kb] = ht < nht && act ? __builtin_bit_cast(bf16x8, ld16(qrow + (ht * 16 + j) * dI + kb * 32))
+                                     : bf16x8{};
+  }
+  const int Lt = L + T, nch = (Lt + 15) / 16, np = dI / 8;
+  int c0, c1;
+  split_range(nch, gridDim.x, blockIdx.x, c0, c1);
+  const __bf16* kvb = reinterpret_cast<const __bf16*>(p.kv) + p.kvw;
+  for (int cb = c0; cb < c1; cb += kIdxBlk) {
+    const int nb = min(kIdxBlk, c1 - cb), tot = nb * 16 * np;
+    constexpr int kB = 8;                         // 16-byte loads in flight per thread
+    __syncthreads();                              // the previous block's keys are no longer read
+    for (int i0 = threadIdx.x; i0 < tot; i0 += kB * kThreads) {
+      u32x4 v[kB];
+#pragma unroll
+      for (int q = 0; q < kB; ++q) {
+        const int i = min(i0 + q * kThreads, tot - 1), k = i / np;
+        v[q] = ld16(kvb + (long long)min(cb * 16 + k, Lt - 1) * p.kv_row + (i - k * np) * 8);
+      }
+#pragma unroll
+      for (int q = 0; q < kB; ++q) {
+        const int i = i0 + q * kThreads, k = i / np;
+        if (i < tot) *reinterpret_cast<u32x4*>(ks + k * KS + (i - k * np) * 8) = v[q];
+      }
+    }
+    __syncthreads();
+    if (!act) continue;
+    for (int cl = sub; cl < nb; cl += wpt) {
+      bf16x8 kf[NKB];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) kf[kb] = *reinterpret_cast<const bf16x8*>(ks + (cl * 16 + j) * KS + kb * 32 + g * 8);
+      float sc = 0.f;
+#pragma unroll
+      for (int ht = 0; ht < kMaxHt; ++ht) {
+        if (ht < nht) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb) acc = mma_bf16_k32(qf[ht][kb], kf[kb], acc);
+          const f32x4 wh = *reinterpret_cast<const f32x4*>(wsm + t * HI + ht * 16 + 4 * g);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sc += acc[e] > 0.f ? wh[e] * acc[e] : 0.f;
+        }
+      }
+      sc += __shfl_xor(sc, 16);
+      sc += __shfl_xor(sc, 32);
+      const int key = (cb + cl) * 16 + j;
+      if (g == 0 && key < Lt) p.iscore[(long long)t * p.imax + key] = sc;
+    }
+  }
+}
+__device__ __forceinline__ void phase_iscore(const LayerParams& p, int L, char* smem) {
+  switch (p.idim / 32) {
+    case 1: iscore_rows<1>(p, L, smem); break;
+    case 2: iscore_rows<2>(p, L, smem); break;
+    case 3: iscore_rows<3>(p, L, smem); break;
+    default: iscore_rows<4>(p, L, smem); break;
+  }
+}
+
 // Top-k per verify row: workgroup t < T keeps row t's idx_topk highest scores
-// among cache rows [0, L + t]: a radix select on the scores' order-preserving
-// 32-bit keys (four 8-bit digits from the top, a histogram per digit in LDS)
-// finds the threshold key and how many rows equal to it are kept; then each
-// thread takes a contiguous segment of rows, the counts above and at the
-// threshold are scanned across the threads, and the kept rows are written in
-// ascending order (rows at the threshold: the lower ones first).
+// among cache rows [0, L + t], by a radix select on the scores' order-
+// preserving 32-bit keys: digits of 11, 11 and 10 bits from the top, a
+// histogram per wave in LDS for each, the bin where the running count from the
+// top reaches the rows still to take found by a scan over the threads.  Wave w
+// owns a contiguous range of the row and reads it in tiles of 256 (a float4 per
+// lane).  After the first digit, the rows in its bin and above it -- the kept
+// rows and the candidates -- are usually few: they are copied, in ascending
+// row order, into a list in LDS (each lane's place found by ballots, each
+// wave's from the per-wave histograms), and the last two digits and the output
+// work on that list.  When the list would not fit (many equal or nearly equal
+// scores), the last two digits and the output read the row again.  Either way
+// the kept rows are written in ascending order, and of the rows equal to the
+// threshold key the lower ones are kept.
 __device__ __forceinline__ uint32_t order_key(float f) {
   const uint32_t u = __float_as_uint(f);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
@@ -798,6 +853,120 @@ __device__ __forceinline__ int wg_scan_incl(int v, int* buf) {
   }
   return buf[threadIdx.x];
 }
+__device__ __forceinline__ int wave_sum_int(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+constexpr int kTopkBatch = 8;                     // tiles (a float4 per lane) in flight
+constexpr int kTopkBins = 2048;
+constexpr int kTopkList = 11264;                  // LDS list capacity (rows)
+// calls f(tile base, keys of the lane's 4 rows) for the wave's tiles in [b0, b1);
+// rows at or past n read a clamped address (the row's own stride holds them)
+template <class F>
+__device__ __forceinline__ void for_tiles(const float* sc, int b0, int b1, int n, F&& f) {
+  const int lane = threadIdx.x & 63, cap = (n - 1) / 4 * 4;
+  for (int b = b0; b < b1; b += 256 * kTopkBatch) {
+    f32x4 v[kTopkBatch];
+#pragma unroll
+    for (int q = 0; q < kTopkBatch; ++q) v[q] = ldg(reinterpret_cast<const f32x4*>(sc + min(b + q * 256 + 4 * lane, cap)));
+#pragma unroll
+    for (int q = 0; q < kTopkBatch; ++q) {
+      if (b + q * 256 < b1) {
+        uint32_t u[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) u[e] = order_key(v[q][e]);
+        f(b + q * 256, u);
+      }
+    }
+  }
+}
+struct TopkLds {
+  int* hist;       // [kWaves][kTopkBins]
+  int* sbuf;       // [kThreads]
+  uint32_t* st;    // prefix, mask, rows at the prefix still to take, rows in the digit's bin and above
+  int* wc;         // [kWaves][2]
+  uint32_t* lkey;  // [kTopkList]
+  int* lrow;       // [kTopkList]
+  __device__ explicit TopkLds(char* smem) {
+    hist = reinterpret_cast<int*>(smem);
+    sbuf = hist + kWaves * kTopkBins;
+    st = reinterpret_cast<uint32_t*>(sbuf + kThreads);
+    wc = reinterpret_cast<int*>(st + 4);
+    lkey = reinterpret_cast<uint32_t*>(wc + 2 * kWaves);
+    lrow = reinterpret_cast<int*>(lkey + kTopkList);
+  }
+};
+static_assert((kWaves * kTopkBins + kThreads + 4 + 2 * kWaves + 2 * kTopkList) * 4 <= kLdsBytes - 1024,
+              "the top-k LDS plan fits");
+// The digit of one radix pass from the per-wave histograms: thread x sums bins
+// 2047 - 4x .. 2044 - 4x of all waves; the thread whose running count from the
+// top reaches `need` picks the digit among them and updates st.  Ends synced.
+__device__ __forceinline__ void topk_digit(const TopkLds& s, int shift, uint32_t dmask, uint32_t prefix,
+                                           uint32_t mask, int need) {
+  int h4[4], s4 = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int bin = kTopkBins - 1 - 4 * (int)threadIdx.x - q;
+    h4[q] = 0;
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v) h4[q] += s.hist[v * kTopkBins + bin];
+    s4 += h4[q];
+  }
+  const int incl = wg_scan_incl(s4, s.sbuf);
+  const int before = incl - s4;
+  if (before < need && need <= incl) {
+    int cum = before, dg = 0, hb = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (cum + h4[q] >= need) {
+        dg = kTopkBins - 1 - 4 * (int)threadIdx.x - q;
+        hb = h4[q];
+        break;
+      }
+      cum += h4[q];
+    }
+    s.st[0] = prefix | ((uint32_t)dg << shift);
+    s.st[1] = mask | (dmask << shift);
+    s.st[2] = (uint32_t)(need - cum);
+    s.st[3] = (uint32_t)(cum + hb);
+  }
+  __syncthreads();
+}
+// Writes the kept rows of one group of up to 64 x NE rows in ascending order:
+// lane l holds rows[l * NE + e] (ok: the row takes part) with keys u; G / E
+// count the rows above / at the threshold before the group (wave-uniform, updated).
+template <int NE>
+__device__ __forceinline__ void topk_write(int32_t* out, const int (&rows)[NE], const uint32_t (&u)[NE],
+                                           const bool (&ok)[NE], uint32_t thr, int need, int& G, int& E) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t lt = (1ull << lane) - 1ull;
+  bool gt[NE], eq[NE];
+  int gb = 0, eb = 0, gs = 0, es = 0;
+#pragma unroll
+  for (int e = 0; e < NE; ++e) {
+    gt[e] = ok[e] && u[e] > thr;
+    eq[e] = ok[e] && u[e] == thr;
+    const uint64_t bg = __ballot(gt[e]), be = __ballot(eq[e]);
+    gb += __popcll(bg & lt);
+    eb += __popcll(be & lt);
+    gs += __popcll(bg);
+    es += __popcll(be);
+  }
+  int gi = G + gb, ei = E + eb;
+#pragma unroll
+  for (int e = 0; e < NE; ++e) {
+    if (gt[e]) {
+      out[gi + min(ei, need)] = rows[e];
+      ++gi;
+    } else if (eq[e]) {
+      if (ei < need) out[gi + ei] = rows[e];
+      ++ei;
+    }
+  }
+  G += gs;
+  E += es;
+}
 __device__ __forceinline__ void phase_topk(const LayerParams& p, int L, char* smem) {
   const int t = blockIdx.x;
   if (t >= p.T) return;
@@ -808,63 +977,149 @@ __device__ __forceinline__ void phase_topk(const LayerParams& p, int L, char* sm
     return;
   }
   const float* sc = p.iscore + (long long)t * p.imax;
-  int* hist = reinterpret_cast<int*>(smem);                        // [256]
-  uint32_t* st = reinterpret_cast<uint32_t*>(smem + 1024);         // prefix, mask, rows still to take
-  int* sbuf = reinterpret_cast<int*>(smem + 2048);                 // [kThreads]
-  if (threadIdx.x == 0) {
-    st[0] = 0u;
-    st[1] = 0u;
-    st[2] = (uint32_t)K;
-  }
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    if (threadIdx.x < 256) hist[threadIdx.x] = 0;
-    __syncthreads();
-    const uint32_t prefix = st[0], mask = st[1];
-    for (int i = threadIdx.x; i < n; i += kThreads) {
-      const uint32_t u = order_key(ldg(sc + i));
-      if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1);
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      const int need = (int)st[2];
-      int cum = 0, dg = 0;
-      for (int b = 255; b >= 0; --b) {
-        if (cum + hist[b] >= need) {
-          dg = b;
-          break;
-        }
-        cum += hist[b];
-      }
-      st[0] = prefix | ((uint32_t)dg << shift);
-      st[1] = mask | (255u << shift);
-      st[2] = (uint32_t)(need - cum);
-    }
-    __syncthreads();
-  }
-  const uint32_t thr = st[0];
-  const int need = (int)st[2];                                     // rows equal to the threshold kept
-  const int seg = (n + kThreads - 1) / kThreads;
-  const int i0 = min(n, (int)threadIdx.x * seg), i1 = min(n, i0 + seg);
-  int ngt = 0, neq = 0;
-  for (int i = i0; i < i1; ++i) {
-    const uint32_t u = order_key(ldg(sc + i));
-    ngt += u > thr;
-    neq += u == thr;
-  }
-  const int gt_base = wg_scan_incl(ngt, sbuf) - ngt;
+  const TopkLds s(smem);
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int segw = (n + kWaves * 256 - 1) / (kWaves * 256) * 256;
+  const int wb = min(n, w * segw), we = min(n, wb + segw);
+  int* hw = s.hist + w * kTopkBins;
+  auto clear_hist = [&]() {                       // a wave clears its own histogram
+#pragma unroll
+    for (int c = 0; c < kTopkBins / 256; ++c) *reinterpret_cast<int4*>(hw + 4 * (lane + 64 * c)) = int4{0, 0, 0, 0};
+  };
+  auto hist_row = [&](int shift, uint32_t dmask, uint32_t prefix, uint32_t mask) {
+    for_tiles(sc, wb, we, n, [&](int b, const uint32_t (&u)[4]) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (b + 4 * lane + e < we && (u[e] & mask) == prefix) atomicAdd(&hw[(u[e] >> shift) & dmask], 1);
+    });
+  };
+  // this wave's rows in its histogram's bins above / at digit dg
+  auto wave_above = [&](int dg) {
+    int a = 0;
+#pragma unroll
+    for (int c = 0; c < kTopkBins / 64; ++c) a += lane + 64 * c > dg ? hw[lane + 64 * c] : 0;
+    return wave_sum_int(a);
+  };
+  // first digit over the whole row
+  clear_hist();
+  hist_row(21, 2047u, 0u, 0u);
   __syncthreads();
-  const int eq_base = wg_scan_incl(neq, sbuf) - neq;
-  int pos = gt_base + min(eq_base, need), eq = eq_base;
-  for (int i = i0; i < i1; ++i) {
-    const uint32_t u = order_key(ldg(sc + i));
-    if (u > thr) {
-      out[pos++] = i;
-    } else if (u == thr) {
-      if (eq < need) out[pos++] = i;
-      ++eq;
+  topk_digit(s, 21, 2047u, 0u, 0u, K);
+  uint32_t prefix = s.st[0], mask = s.st[1];
+  int need = (int)s.st[2];
+  const int nlist = (int)s.st[3];                 // rows in the digit's bin and above
+  const int dg0 = (int)(prefix >> 21);
+  int above = wave_above(dg0), at = hw[dg0];
+  if (nlist <= kTopkList) {
+    // ---- the rows in the first digit's bin and above, in order, into the LDS list
+    if (lane == 0) s.wc[w] = above + at;
+    __syncthreads();
+    int off = 0;
+    for (int v = 0; v < w; ++v) off += s.wc[v];
+    const uint32_t lo = prefix;                   // keys >= lo: first digit >= dg0
+    const uint64_t lt = (1ull << lane) - 1ull;
+    for_tiles(sc, wb, we, n, [&](int b, const uint32_t (&u)[4]) {
+      bool sel[4];
+      int pb = 0, ps = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sel[e] = b + 4 * lane + e < we && u[e] >= lo;
+        const uint64_t m = __ballot(sel[e]);
+        pb += __popcll(m & lt);
+        ps += __popcll(m);
+      }
+      int pos = off + pb;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (sel[e]) {
+          s.lkey[pos] = u[e];
+          s.lrow[pos] = b + 4 * lane + e;
+          ++pos;
+        }
+      off += ps;
+    });
+    __syncthreads();
+    // ---- the last two digits over the list's candidates (first digit == dg0)
+    for (int pass = 1; pass < 3; ++pass) {
+      const int shift = pass == 1 ? 10 : 0;
+      const uint32_t dmask = pass == 2 ? 1023u : 2047u;
+      clear_hist();
+      for (int m = threadIdx.x; m < nlist; m += kThreads) {
+        const uint32_t u = s.lkey[m];
+        if ((u & mask) == prefix) atomicAdd(&hw[(u >> shift) & dmask], 1);
+      }
+      __syncthreads();
+      topk_digit(s, shift, dmask, prefix, mask, need);
+      prefix = s.st[0];
+      mask = s.st[1];
+      need = (int)s.st[2];
     }
+    // ---- output: wave w writes list entries [w * segl, (w + 1) * segl)
+    const int segl = (nlist + kWaves * 64 - 1) / (kWaves * 64) * 64;
+    const int lb = min(nlist, w * segl), le = min(nlist, lb + segl);
+    int ga = 0, ea = 0;
+    for (int m = lb + lane; m < le; m += 64) {
+      const uint32_t u = s.lkey[m];
+      ga += u > prefix;
+      ea += u == prefix;
+    }
+    ga = wave_sum_int(ga);
+    ea = wave_sum_int(ea);
+    __syncthreads();                              // every wave has read wc above
+    if (lane == 0) {
+      s.wc[2 * w] = ga;
+      s.wc[2 * w + 1] = ea;
+    }
+    __syncthreads();
+    int G = 0, E = 0;
+    for (int v = 0; v < w; ++v) {
+      G += s.wc[2 * v];
+      E += s.wc[2 * v + 1];
+    }
+    for (int m0 = lb; m0 < le; m0 += 64) {
+      const int m = m0 + lane;
+      const bool ok[1] = {m < le};
+      const int rows[1] = {ok[0] ? s.lrow[m] : 0};
+      const uint32_t u[1] = {ok[0] ? s.lkey[m] : 0u};
+      topk_write<1>(out, rows, u, ok, prefix, need, G, E);
+    }
+    return;
   }
+  // ---- the list would not fit: the last two digits and the output read the row
+  for (int pass = 1; pass < 3; ++pass) {
+    const int shift = pass == 1 ? 10 : 0;
+    const uint32_t dmask = pass == 2 ? 1023u : 2047u;
+    clear_hist();
+    hist_row(shift, dmask, prefix, mask);
+    __syncthreads();
+    topk_digit(s, shift, dmask, prefix, mask, need);
+    prefix = s.st[0];
+    mask = s.st[1];
+    need = (int)s.st[2];
+    const int dg = (int)((prefix >> shift) & dmask);
+    above += wave_above(dg);
+    if (pass == 2) at = hw[dg];
+  }
+  if (lane == 0) {
+    s.wc[2 * w] = above;
+    s.wc[2 * w + 1] = at;
+  }
+  __syncthreads();
+  int G = 0, E = 0;                               // rows above / at the threshold before the wave's range
+  for (int v = 0; v < w; ++v) {
+    G += s.wc[2 * v];
+    E += s.wc[2 * v + 1];
+  }
+  for_tiles(sc, wb, we, n, [&](int b, const uint32_t (&u)[4]) {
+    int rows[4];
+    bool ok[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      rows[e] = b + 4 * lane + e;
+      ok[e] = rows[e] < we;
+    }
+    topk_write<4>(out, rows, u, ok, prefix, need, G, E);
+  });
 }
 
 // ------------------------------------------------------------------ P2 attention
@@ -2263,8 +2518,9 @@ __global__ __launch_bounds__(kThreads, 1) void layer_kernel(LayerParams p) {
   if (!grid_barrier(p, 0, flag)) return raise_model_fault(p);
   if constexpr (LR) {
     phase_uq<AF, SP>(p, smem);
-    if (!grid_barrier(p, 0, flag)) return raise_model_fault(p);
+    if (!grid_barrier(p, 8, flag)) return raise_model_fault(p);
   }
+  if constexpr (SP) stage_index_queries<LR>(p, blockIdx.x * kThreads + threadIdx.x, gridDim.x * kThreads);
   {
     // absorbed-query units on waves [0, wa) of every workgroup; when they fit
     // in half the waves, RoPE / KV insert runs on the other half meanwhile
@@ -2281,10 +2537,10 @@ __global__ __launch_bounds__(kThreads, 1) void layer_kernel(LayerParams p) {
   }
   if (!grid_barrier(p, 1, flag)) return raise_model_fault(p);
   if constexpr (SP) {
-    phase_iscore<LR>(p, L, smem);
-    if (!grid_barrier(p, 1, flag)) return raise_model_fault(p);
+    phase_iscore(p, L, smem);
+    if (!grid_barrier(p, 9, flag)) return raise_model_fault(p);
     phase_topk(p, L, smem);
-    if (!grid_barrier(p, 1, flag)) return raise_model_fault(p);
+    if (!grid_barrier(p, 10, flag)) return raise_model_fault(p);
   }
   phase_attention<KF, KBMAX, DBMAX, EXACT, SP>(p, L, smem);
   if (!grid_barrier(p, 2, flag)) return raise_model_fault(p);

@@ -127,12 +127,12 @@ typedef struct mk_layer_config {
    * score of cache row s <= L + t: sum_j w^I_j max(0, q^I_j . k^I_s); the row attends to its
    * idx_topk highest-scoring rows (ties to the lower row; every row when L + t + 1 <= idx_topk).
    * Needs bf16 attention and cache, n_heads a multiple of 16, idx_heads a multiple of 16,
-   * idx_dim a multiple of 32, idx_heads * idx_dim <= 8192, idx_topk <= 8192. */
+   * idx_dim a multiple of 32 and <= 128, idx_heads * idx_dim <= 8192, idx_topk <= 8192. */
   int32_t idx_heads;
   int32_t idx_dim;
   int32_t idx_topk;
-  int32_t idx_max_rows;      /* sparse: the largest L + T a step may use (sizes the workspace's
-                                index scores); a step past it is refused */
+  int32_t idx_max_rows;      /* sparse: the largest L + T a step may use, a multiple of 4 (sizes
+                                the workspace's index scores); a step past it is refused */
 } mk_layer_config;
 
 typedef struct mk_device_info {
@@ -308,11 +308,16 @@ int mk_get_stats(const mk_layer* layer, mk_stats* out);
  * enabling clears the trace buffer (synchronous). */
 int mk_set_trace(mk_layer* layer, int enabled);
 /* Copies the trace of the last step: int64 ticks of a 100 MHz clock,
- * [grid_wgs][2 + 2*barriers_per_step + 16]: start, (arrive, release) per barrier, end,
+ * [grid_wgs][2 + 2*barriers_per_step + 16]: start, (arrive, release) per barrier slot, end,
  * then 16 sub-phase stamps (0 where a workgroup did not reach the mark): 0-4 attention
  * (query tile staged, key chunks done, wave merge written, split counter, split merge
  * done), 5 projection input normalised, 6 output-projection input staged, 7 router
- * input normalised, 8 routing done, 9 first down-projection input staged. */
+ * input normalised, 8 routing done, 9 first down-projection input staged.  Barrier
+ * slots 0-7 follow the phases in launch order (0 after the first projection, 1 after
+ * RoPE / cache insert / absorbed query, 2 attention, 3 merge and W_UV, 4 W_O, 5 router,
+ * 6 gate/up when not fused, 7 experts); 8 follows the low-rank query's up-projection,
+ * 9 the index scores and 10 the top-k of sparse attention; a slot a variant does not
+ * use stays 0. */
 int mk_read_trace(mk_layer* layer, int64_t* host_dst, size_t bytes, void* stream);
 /* Barrier wait bound in microseconds (default 2,000,000). */
 int mk_set_barrier_timeout_us(mk_layer* layer, int64_t us);

@@ -101,7 +101,8 @@ def gpu_step(dl, s, H_dev, kv_dev, L, T=None):
         dl.layer.debug_tap(tap, buf)
         taps[name] = oracle.bf16_to_f32(buf) if dt == np.uint16 else buf
     if s.idx_topk:
-        for name, tap, shape, dt in (("isel", 8, (T, s.idx_topk), np.int32), ("iscore", 9, (T, s.capacity), np.float32)):
+        imax = (s.capacity + 3) // 4 * 4
+        for name, tap, shape, dt in (("isel", 8, (T, s.idx_topk), np.int32), ("iscore", 9, (T, imax), np.float32)):
             buf = np.empty(shape, dt)
             dl.layer.debug_tap(tap, buf)
             taps[name] = buf
@@ -167,6 +168,10 @@ def compare_kept_rows(s, g_taps, o_taps, L):
         g = g_taps["isel"][t][:cnt].tolist()
         o = o_taps["isel"][t][:cnt].tolist()
         assert g == sorted(g) and len(set(g)) == cnt and 0 <= g[0] and g[-1] < n, (t, g[:8], g[-8:])
+        # exact: the kept rows are the top-k of the GPU's own scores, ties to the lower row
+        gs = g_taps["iscore"][t][:n].astype(np.float64)
+        own = np.sort(np.lexsort((np.arange(n), -gs))[:cnt]).tolist()
+        assert g == own, (t, sorted(set(g) ^ set(own))[:8])
         osc = o_taps["iscore"][t][:n].astype(np.float64)
         assert normwise(g_taps["iscore"][t:t + 1, :n], osc[None]) <= TOL["bf16"], t
         if set(g) != set(o):

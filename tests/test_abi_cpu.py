@@ -74,8 +74,9 @@ def test_valid_configs_pass_and_sizes():
     (dict(idx_topk=-1), -1),
     (dict(idx_topk=2048, idx_heads=64, idx_dim=128, idx_max_rows=0), -1),
     (dict(idx_topk=2048, idx_heads=60, idx_dim=128, idx_max_rows=70000), -8),
+    (dict(idx_topk=2048, idx_heads=64, idx_dim=128, idx_max_rows=70001), -1),
     (dict(idx_topk=2048, idx_heads=64, idx_dim=128, idx_max_rows=70000, kv_format="fp8row"), -8),
-    (dict(idx_topk=2048, idx_heads=256, idx_dim=32, idx_max_rows=70000), -8),
+    (dict(idx_topk=2048, idx_heads=32, idx_dim=160, idx_max_rows=70000), -8),
 ])
 def test_invalid_configs_are_refused(kw, code):
     import decoder_megakernel_amd as mk

@@ -220,6 +220,32 @@ def test_sparse_attention_rows_just_past_topk():
     _run(MID_SP, L=97, T=6)
 
 
+@pytest.mark.parametrize("L", [9000, 16384])
+def test_sparse_attention_all_scores_equal(L):
+    """Indexer weights of zero: every index score is 0 and the kept rows are the
+    lowest idx_topk rows (ties go to the lower row).  At L = 9000 every row is a
+    candidate of the first digit's bin and still fits the workgroup's list; at
+    L = 16384 it does not, and the top-k reads the row again for each digit."""
+    from decoder_megakernel_amd import harness
+    import parity
+    s = MID_SP.with_(name="mid_sparse_ties", L=L, idx_topk=2048)
+    s = s.with_(kv_capacity=max(s.capacity, L + s.T))
+    print("[parity] %s L=%d" % (s.name, L), flush=True)
+    dl = harness.DeviceLayer(s, 0, 0)
+    dl.packed["widx"].zero_()
+    kv = harness.kv_cache(s, 0, 0)
+    H = recipe.hidden_host(s, 0, 0)
+    g_out, g_kv, g_taps = parity.gpu_step(dl, s, torch.from_numpy(H).cuda(), kv, L, s.T)
+    assert not g_taps["iscore"][:, :L + s.T].any()
+    for t in range(s.T):
+        assert g_taps["isel"][t].tolist() == list(range(2048)), t
+    w = recipe.layer_weights_host(s, 0, 0)
+    w["widx"] = np.zeros_like(w["widx"])
+    errs = parity.check_layer(s, 0, 0, g_out, g_kv, g_taps, H, L, full_weights=w)
+    print("[parity] %s errors %s" % (s.name, errs), flush=True)
+    assert errs["kept_rows_differing"] == 0 and not errs["kept_rows_forced"]
+
+
 def test_full_size_sparse_fp8_E384_T6_L65536_skew():
     from synth.configs import C4S
     _run(C4S, full_weights=False)
