@@ -48,7 +48,10 @@ def attn_bytes(s):
     e = 2 if s.attn_fmt == "bf16" else 4
     # the query projection: W_Q, or W_DQ and W_UQ (+ the q-norm gain) with a low-rank query
     q = s.q_lora * s.d + s.n_h * s.qw * s.q_lora + 2 * s.q_lora if s.q_lora else s.n_h * s.qw * s.d
-    return e * (q + s.kvw * s.d + 2 * s.n_h * s.d_h * s.d_c + s.d * s.n_h * s.d_h) + (4 * s.d_c if s.kv_norm else 0)
+    # sparse attention: the indexer's rows [W_IQ; W_IW; W_IK] of the first projection
+    idx = (s.idx_heads * s.idx_dim + s.idx_heads + s.idx_dim) * s.d if s.idx_topk else 0
+    return e * (q + idx + s.kvw * s.d + 2 * s.n_h * s.d_h * s.d_c + s.d * s.n_h * s.d_h) + \
+        (4 * s.d_c if s.kv_norm else 0)
 
 
 def router_bytes(s):
@@ -71,11 +74,18 @@ def head_bytes(s):
     return s.V * s.d * 2
 
 
-def layer_bytes(s, L, slots):
-    """Algorithmic bytes of one layer step: touched weights, KV read/write, activations in/out."""
+def layer_bytes(s, L, slots, kept_rows=None):
+    """Algorithmic bytes of one layer step: touched weights, KV read/write, activations in/out.
+    Sparse attention reads every row's index key and, of the latent and RoPE key,
+    only the rows some verify row keeps (kept_rows: the size of that union)."""
     from synth import recipe
     rb = recipe.kv_row_bytes(s)          # one cache row (fp8 rows: codes, scale, padding)
-    kv = (L + s.T) * rb + s.T * rb
+    if s.idx_topk and kept_rows is None:
+        raise ValueError("sparse attention: the kept-row count is needed")
+    if s.idx_topk:
+        kv = (L + s.T) * 2 * s.idx_dim + kept_rows * 2 * s.kvw + s.T * rb
+    else:
+        kv = (L + s.T) * rb + s.T * rb
     act = 2 * s.T * s.d * 4 + 2 * s.d * 4
     return attn_bytes(s) + router_bytes(s) + slots * expert_bytes(s) + kv + act
 
@@ -412,7 +422,19 @@ def run_layer(s, args):
     per = [evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(args.steps)]
     st1 = [c[0].layer.stats() for c in copies]
     slots = sum(b.expert_blocks_sum - a.expert_blocks_sum for a, b in zip(st0, st1)) / args.steps
-    lb = layer_bytes(s, s.L, slots)
+    kept = None
+    if s.idx_topk:
+        # rows of the cache some verify row keeps, per launch (the mean over the weight copies)
+        sizes = []
+        for i in range(len(copies)):
+            launch(i)
+            torch.cuda.synchronize(dev)
+            sel = np.empty((s.T, s.idx_topk), np.int32)
+            copies[i][0].layer.debug_tap(8, sel)
+            n_t = [min(s.idx_topk, s.L + t + 1) for t in range(s.T)]
+            sizes.append(len(set(np.concatenate([sel[t, :n_t[t]] for t in range(s.T)]).tolist())))
+        kept = float(np.mean(sizes))
+    lb = layer_bytes(s, s.L, slots, kept)
     achieved = lb / (us * 1e-6) / 1e9
 
     def traced():
@@ -428,6 +450,7 @@ def run_layer(s, args):
                    "d_ff": s.f, "expert_format": s.exp_fmt, "routing": s.routing, "weight_copies": 3},
         "us_per_launch_dist": pct(per),
         "experts_streamed_per_step": round(slots, 2), "step_bytes": int(lb),
+        "kept_rows_union": kept,
         "barrier_share": tsum["barrier_share"] if tsum else None,
         "layer_trace": tsum,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS, "unit": "GB/s",

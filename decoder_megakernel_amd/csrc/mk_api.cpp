@@ -94,8 +94,8 @@ int check_cfg(const mk_layer_config* c) {
     if (D.nh % 16 || D.ih <= 0 || D.ih % 16 || D.idm <= 0 || D.idm % 32 || D.ih * D.idm > 8192 || D.ik > 8192)
       return fail(MK_ERR_UNSUPPORTED_SHAPE, "sparse attention: n_heads and idx_heads multiples of 16, idx_dim a "
                                             "multiple of 32, idx_heads * idx_dim <= 8192, idx_topk <= 8192");
-    if (D.imax < 4 || D.imax > (1 << 24) || D.imax % 4)
-      return fail(MK_ERR_INVALID_ARG, "idx_max_rows must be a multiple of 4 in [4, 2^24]");
+    if (D.imax < 8 || D.imax > (1 << 24) || D.imax % 8)
+      return fail(MK_ERR_INVALID_ARG, "idx_max_rows must be a multiple of 8 in [8, 2^24]");
     // the index-score phase holds a row's index queries in 16 fragments per lane and
     // stages 512 index keys (bf16, 8 pad each) and the head weights in LDS
     if (D.idm > 128) return fail(MK_ERR_UNSUPPORTED_SHAPE, "idx_dim must be <= 128");
@@ -237,7 +237,7 @@ int device_info(int dev, DevInfo* di, LayerKernelFn fn) {
 
 struct WsLayout {
   size_t qkv_part, qrope, qabs, att_part, att_ml, z, o, hp, route_sel, route_gate, route_cand, logits, hbuf,
-      ybuf, dummy, qbuf, iq, iw, iscore, isel,
+      ybuf, dummy, qbuf, iq, iw, iscore, ik16, isel, ihist, ictr, icnt, icand,
       total;
 };
 struct StLayout {
@@ -271,6 +271,11 @@ WsLayout ws_layout(const Dims& D, const Schedule& s) {
   w.iq = D.ik > 0 ? take((size_t)T * D.ih * D.idm * 2) : 0;
   w.iw = D.ik > 0 ? take((size_t)T * D.ih * 4) : 0;
   w.iscore = D.ik > 0 ? take((size_t)T * D.imax * 4) : 0;
+  w.ik16 = D.ik > 0 ? take((size_t)T * D.imax * 2) : 0;
+  w.ihist = D.ik > 0 ? take((size_t)T * 2048 * 4) : 0;
+  w.ictr = D.ik > 0 ? take((size_t)T * kIdxCtrStride * 4) : 0;
+  w.icnt = D.ik > 0 ? take((size_t)T * kThreads * 4) : 0;
+  w.icand = D.ik > 0 ? take((size_t)T * D.imax * 8) : 0;
   w.isel = D.ik > 0 ? take((size_t)T * D.ik * 4) : 0;
   w.total = off;
   return w;
@@ -309,6 +314,11 @@ void bind_workspace(LayerParams& p, const WsLayout& wl, char* ws) {
   p.iq = wl.iq ? (void*)(ws + wl.iq) : nullptr;
   p.iw = wl.iw ? (float*)(ws + wl.iw) : nullptr;
   p.iscore = wl.iscore ? (float*)(ws + wl.iscore) : nullptr;
+  p.ik16 = wl.ik16 ? (uint16_t*)(ws + wl.ik16) : nullptr;
+  p.ihist = wl.ihist ? (uint32_t*)(ws + wl.ihist) : nullptr;
+  p.ictr = wl.ictr ? (uint32_t*)(ws + wl.ictr) : nullptr;
+  p.icnt = wl.icnt ? (uint32_t*)(ws + wl.icnt) : nullptr;
+  p.icand = wl.icand ? (uint32_t*)(ws + wl.icand) : nullptr;
   p.isel = wl.isel ? (int32_t*)(ws + wl.isel) : nullptr;
 }
 
@@ -562,6 +572,8 @@ int mk_layer_init(const mk_layer_config* cfg, const mk_layer_weights* w, void* s
   if ((D.E / 16 + di.nwg - 1) / di.nwg > 4)
     return fail(MK_ERR_UNSUPPORTED_SHAPE, "n_experts / 16 exceeds 4 router units per workgroup on %d workgroups",
                 di.nwg);
+  if (D.ik > 0 && di.nwg < kMaxT)
+    return fail(MK_ERR_UNSUPPORTED_SHAPE, "sparse attention needs at least %d workgroups (one per verify row)", kMaxT);
   mk_layer* L = new (std::nothrow) mk_layer();
   if (!L) return fail(MK_ERR_INVALID_ARG, "out of host memory");
   L->cfg = *cfg;

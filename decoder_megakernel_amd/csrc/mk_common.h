@@ -16,6 +16,7 @@ constexpr int kTraceX = 16;              // extra per-workgroup timestamps (sub-
 constexpr int kTraceStride = 2 + 2 * kBarriers + kTraceX;
 constexpr int kLdsBytes = 160 * 1024 - 256;
 constexpr int kMaxTopK = 16;
+constexpr int kIdxCtrStride = 64;        // words between two rows' top-k part counters (two each)
 constexpr int kGateCnt = 128;            // index of the first of 8 gate/up ticket counters in att_cnt,
 constexpr int kCntStride = 64;           // which sit 256 bytes apart (device-scope atomics on one
                                          // line are serialised where they are performed)
@@ -137,6 +138,11 @@ struct LayerParams {
   void* iq;                // sparse: index queries, bf16 [T][ihead][idim]
   float* iw;               // sparse: index head weights [T][ihead]
   float* iscore;           // sparse: index scores [T][idx_max_rows]
+  uint16_t* ik16;          // sparse: the scores' order keys, top 16 bits [T][idx_max_rows]
+  uint32_t* ihist;         // sparse: the top-k's first-digit histogram of each row [kMaxT][2048]
+  uint32_t* ictr;          // sparse: the top-k's part counters [kMaxT][kIdxCtrStride]
+  uint32_t* icnt;          // sparse: pairs per part [kMaxT][512]
+  uint32_t* icand;         // sparse: (row, top 16 bits) pairs of the parts [kMaxT][idx_max_rows][2]
   int32_t* isel;           // sparse: kept rows [T][itopk], ascending
   int imax;                // sparse: idx_max_rows
   float* qrope;            // [T][nh][dr]

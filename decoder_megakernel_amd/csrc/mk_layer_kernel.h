@@ -736,6 +736,11 @@ __device__ __forceinline__ void stage_index_queries(const LayerParams& p, int gi
   }
 }
 
+// Order-preserving 32-bit key of a score: a larger float has a larger key.
+__device__ __forceinline__ uint32_t order_key(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
 // Index scores: the cache rows [0, L + T) are cut into chunks of 16 spread over
 // the grid; a workgroup stages up to kIdxBlk of its chunks' index keys in LDS
 // (bf16, row stride idx_dim + 8).  Wave w scores verify row t = w / (8 / T)
@@ -810,7 +815,10 @@ __device__ __forceinline__ void iscore_rows(const LayerParams& p, int L, char* s
       sc += __shfl_xor(sc, 16);
       sc += __shfl_xor(sc, 32);
       const int key = (cb + cl) * 16 + j;
-      if (g == 0 && key < Lt) p.iscore[(long long)t * p.imax + key] = sc;
+      if (g == 0 && key < Lt) {
+        p.iscore[(long long)t * p.imax + key] = sc;
+        p.ik16[(long long)t * p.imax + key] = (uint16_t)(order_key(sc) >> 16);
+      }
     }
   }
 }
@@ -823,46 +831,58 @@ __device__ __forceinline__ void phase_iscore(const LayerParams& p, int L, char* 
   }
 }
 
-// Top-k per verify row: workgroup t < T keeps row t's idx_topk highest scores
-// among cache rows [0, L + t], by a radix select on the scores' order-
-// preserving 32-bit keys: digits of 11, 11 and 10 bits from the top, a
-// histogram per wave in LDS for each, the bin where the running count from the
-// top reaches the rows still to take found by a scan over the threads.  Wave w
-// owns a contiguous range of the row and reads it in tiles of 256 (a float4 per
-// lane).  After the first digit, the rows in its bin and above it -- the kept
-// rows and the candidates -- are usually few: they are copied, in ascending
-// row order, into a list in LDS (each lane's place found by ballots, each
-// wave's from the per-wave histograms), and the last two digits and the output
-// work on that list.  When the list would not fit (many equal or nearly equal
-// scores), the last two digits and the output read the row again.  Either way
-// the kept rows are written in ascending order, and of the rows equal to the
-// threshold key the lower ones are kept.
-__device__ __forceinline__ uint32_t order_key(float f) {
-  const uint32_t u = __float_as_uint(f);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-// inclusive scan of v over the workgroup's threads through LDS (buf: kThreads ints)
+// Top-k per verify row: row t keeps its idx_topk highest scores among cache
+// rows [0, L + t], by a radix select on the scores' order-preserving 32-bit
+// keys, digit by digit from the top; each digit is the bin where the running
+// count from the top of a histogram reaches the rows still to take (found by a
+// scan over the threads).  Row t is shared by P = grid / T workgroups, each
+// taking a part of at least 2048 consecutive rows; the index-score phase also
+// stored every key's top 16 bits, and the parts work on those:
+//  - each part counts the top 11 bits of its rows in LDS and adds the bins into
+//    the row's histogram in memory (device-scope atomics), then waits until
+//    every part of the row has (a bounded wait on a counter) and reads the sum:
+//    every part finds the same first digit;
+//  - each part writes its rows at or above that digit's bin -- the kept rows
+//    above it and the candidates in it -- as (row, top 16 bits) pairs, in
+//    ascending order from its first row's place, with their count, and counts
+//    itself done;
+//  - the row's first part waits for the others, gathers the pairs into a list
+//    in LDS (ascending rows), takes the next 5 bits from the list, reads the
+//    full keys of the rows that share the threshold's top 16 bits for the last
+//    16 bits (11 + 5), and writes the kept rows in ascending order (each lane's
+//    place found by ballots); of the rows equal to the threshold key the lower
+//    ones are kept.
+// Pairs, counts and histograms are written and read with device-scope
+// accesses, so no cache on the way holds a stale copy.  When the list would
+// not fit in LDS (many equal or nearly equal scores), the first part alone
+// takes every digit and the output from the row's full keys.
+// Inclusive scan of v over the workgroup's threads: wave scans by shuffles,
+// then the wave totals through LDS (buf: kWaves ints).  Ends synced.
 __device__ __forceinline__ int wg_scan_incl(int v, int* buf) {
-  buf[threadIdx.x] = v;
-  __syncthreads();
-  for (int o = 1; o < kThreads; o <<= 1) {
-    const int a = (int)threadIdx.x >= o ? buf[threadIdx.x - o] : 0;
-    __syncthreads();
-    buf[threadIdx.x] += a;
-    __syncthreads();
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(v, o);
+    if (lane >= o) v += y;
   }
-  return buf[threadIdx.x];
+  if (lane == 63) buf[w] = v;
+  __syncthreads();
+  int base = 0;
+  for (int u = 0; u < w; ++u) base += buf[u];
+  __syncthreads();
+  return v + base;
 }
 __device__ __forceinline__ int wave_sum_int(int v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
   return v;
 }
-constexpr int kTopkBatch = 8;                     // tiles (a float4 per lane) in flight
+constexpr int kTopkBatch = 8;                     // float4 tiles in flight per lane
 constexpr int kTopkBins = 2048;
 constexpr int kTopkList = 11264;                  // LDS list capacity (rows)
-// calls f(tile base, keys of the lane's 4 rows) for the wave's tiles in [b0, b1);
-// rows at or past n read a clamped address (the row's own stride holds them)
+constexpr int kTopkPart = 2048;                   // least rows of one part of a row
+// calls f(tile base, keys of the lane's 4 rows) for the wave's float tiles in
+// [b0, b1); rows at or past n read a clamped address (the row's own stride holds them)
 template <class F>
 __device__ __forceinline__ void for_tiles(const float* sc, int b0, int b1, int n, F&& f) {
   const int lane = threadIdx.x & 63, cap = (n - 1) / 4 * 4;
@@ -881,39 +901,23 @@ __device__ __forceinline__ void for_tiles(const float* sc, int b0, int b1, int n
     }
   }
 }
-struct TopkLds {
-  int* hist;       // [kWaves][kTopkBins]
-  int* sbuf;       // [kThreads]
-  uint32_t* st;    // prefix, mask, rows at the prefix still to take, rows in the digit's bin and above
-  int* wc;         // [kWaves][2]
-  uint32_t* lkey;  // [kTopkList]
-  int* lrow;       // [kTopkList]
-  __device__ explicit TopkLds(char* smem) {
-    hist = reinterpret_cast<int*>(smem);
-    sbuf = hist + kWaves * kTopkBins;
-    st = reinterpret_cast<uint32_t*>(sbuf + kThreads);
-    wc = reinterpret_cast<int*>(st + 4);
-    lkey = reinterpret_cast<uint32_t*>(wc + 2 * kWaves);
-    lrow = reinterpret_cast<int*>(lkey + kTopkList);
-  }
-};
-static_assert((kWaves * kTopkBins + kThreads + 4 + 2 * kWaves + 2 * kTopkList) * 4 <= kLdsBytes - 1024,
-              "the top-k LDS plan fits");
-// The digit of one radix pass from the per-wave histograms: thread x sums bins
-// 2047 - 4x .. 2044 - 4x of all waves; the thread whose running count from the
-// top reaches `need` picks the digit among them and updates st.  Ends synced.
-__device__ __forceinline__ void topk_digit(const TopkLds& s, int shift, uint32_t dmask, uint32_t prefix,
-                                           uint32_t mask, int need) {
-  int h4[4], s4 = 0;
+// the 8 16-bit keys of rows [b, b + 8) (b a multiple of 8; rows at or past n
+// read a clamped address inside the row's stride)
+__device__ __forceinline__ void keys16(const uint16_t* k16, int b, int n, uint32_t (&u)[8]) {
+  const u32x4 v = ld16(k16 + min(b, (n - 1) / 8 * 8));
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int bin = kTopkBins - 1 - 4 * (int)threadIdx.x - q;
-    h4[q] = 0;
-#pragma unroll
-    for (int v = 0; v < kWaves; ++v) h4[q] += s.hist[v * kTopkBins + bin];
-    s4 += h4[q];
+  for (int e = 0; e < 4; ++e) {
+    u[2 * e] = v[e] & 0xFFFFu;
+    u[2 * e + 1] = v[e] >> 16;
   }
-  const int incl = wg_scan_incl(s4, s.sbuf);
+}
+// the digit of a 2048-bin histogram: thread x holds bins 2047 - 4x .. 2044 - 4x
+// (h4[q] = bin 2047 - 4x - q); the thread whose running count from the top
+// reaches `need` writes the bin, the rows in higher bins and the rows in it to
+// res[0..2].  Ends synced.
+__device__ __forceinline__ void digit_of(const int (&h4)[4], int need, int* sbuf, int* res) {
+  const int s4 = h4[0] + h4[1] + h4[2] + h4[3];
+  const int incl = wg_scan_incl(s4, sbuf);
   const int before = incl - s4;
   if (before < need && need <= incl) {
     int cum = before, dg = 0, hb = 0;
@@ -926,13 +930,46 @@ __device__ __forceinline__ void topk_digit(const TopkLds& s, int shift, uint32_t
       }
       cum += h4[q];
     }
-    s.st[0] = prefix | ((uint32_t)dg << shift);
-    s.st[1] = mask | (dmask << shift);
-    s.st[2] = (uint32_t)(need - cum);
-    s.st[3] = (uint32_t)(cum + hb);
+    res[0] = dg;
+    res[1] = cum;
+    res[2] = hb;
   }
   __syncthreads();
 }
+// Thread 0 waits (bounded) until *ctr reaches `target`; false when the wait gave
+// up or the launch already failed (the fault word is then set).
+__device__ __forceinline__ bool wait_count(const LayerParams& p, const uint32_t* ctr, uint32_t target) {
+  const uint64_t t0 = clock100();
+  while (true) {
+    if (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= target) return true;
+    if (__hip_atomic_load(&p.bar->fault, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) return false;
+    if ((long long)(clock100() - t0) > p.timeout_ticks) {
+      __hip_atomic_store(&p.bar->fault, kFaultTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return false;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+struct TopkLds {
+  int* hist;       // [kWaves][kTopkBins]
+  int* sbuf;       // [kWaves]
+  int* res;        // digit: bin, rows in higher bins, rows in it; flag
+  int* wc;         // [kWaves][2]
+  int* poff;       // [kThreads] parts' places in the list
+  uint32_t* lkey;  // [kTopkList]
+  int* lrow;       // [kTopkList]
+  __device__ explicit TopkLds(char* smem) {
+    hist = reinterpret_cast<int*>(smem);
+    sbuf = hist + kWaves * kTopkBins;
+    res = sbuf + kWaves;
+    wc = res + 4;
+    poff = wc + 2 * kWaves;
+    lkey = reinterpret_cast<uint32_t*>(poff + kThreads);
+    lrow = reinterpret_cast<int*>(lkey + kTopkList);
+  }
+};
+static_assert((kWaves * kTopkBins + kWaves + 4 + 2 * kWaves + kThreads + 2 * kTopkList) * 4 <= kLdsBytes - 1024,
+              "the top-k LDS plan fits");
 // Writes the kept rows of one group of up to 64 x NE rows in ascending order:
 // lane l holds rows[l * NE + e] (ok: the row takes part) with keys u; G / E
 // count the rows above / at the threshold before the group (wave-uniform, updated).
@@ -967,137 +1004,60 @@ __device__ __forceinline__ void topk_write(int32_t* out, const int (&rows)[NE], 
   G += gs;
   E += es;
 }
-__device__ __forceinline__ void phase_topk(const LayerParams& p, int L, char* smem) {
-  const int t = blockIdx.x;
-  if (t >= p.T) return;
-  const int K = p.itopk, n = L + t + 1;
-  int32_t* out = p.isel + (long long)t * K;
-  if (n <= K) {
-    for (int i = threadIdx.x; i < n; i += kThreads) out[i] = i;
-    return;
+// the digit of the next pass from the per-wave histograms (thread x sums bins
+// 2047 - 4x .. 2044 - 4x of all waves); updates the threshold's bits and the
+// rows still to take at them, returns the digit
+__device__ __forceinline__ int topk_next_digit(const TopkLds& s, int shift, uint32_t dmask, uint32_t& prefix,
+                                               uint32_t& mask, int& need) {
+  int g4[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int bin = kTopkBins - 1 - 4 * (int)threadIdx.x - q;
+    g4[q] = 0;
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v) g4[q] += s.hist[v * kTopkBins + bin];
   }
-  const float* sc = p.iscore + (long long)t * p.imax;
-  const TopkLds s(smem);
+  digit_of(g4, need, s.sbuf, s.res);
+  const int dg = s.res[0];
+  prefix |= (uint32_t)dg << shift;
+  mask |= dmask << shift;
+  need -= s.res[1];
+  return dg;
+}
+__device__ __forceinline__ void topk_clear_hist(int* hw) {      // a wave clears its own histogram
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int c = 0; c < kTopkBins / 256; ++c) *reinterpret_cast<int4*>(hw + 4 * (lane + 64 * c)) = int4{0, 0, 0, 0};
+}
+// One workgroup takes every digit and the output from row t's full keys: wave
+// w reads a contiguous range of the row in tiles of 256 (a float4 per lane);
+// its histograms also give how many of its rows lie above and at the
+// threshold, so the waves' output places follow from eight counts.
+__device__ __forceinline__ void topk_full_row(const float* sc, int n, int K, int32_t* out, const TopkLds& s) {
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  int* hw = s.hist + w * kTopkBins;
+  uint32_t prefix = 0u, mask = 0u;
+  int need = K;
   const int segw = (n + kWaves * 256 - 1) / (kWaves * 256) * 256;
   const int wb = min(n, w * segw), we = min(n, wb + segw);
-  int* hw = s.hist + w * kTopkBins;
-  auto clear_hist = [&]() {                       // a wave clears its own histogram
-#pragma unroll
-    for (int c = 0; c < kTopkBins / 256; ++c) *reinterpret_cast<int4*>(hw + 4 * (lane + 64 * c)) = int4{0, 0, 0, 0};
-  };
-  auto hist_row = [&](int shift, uint32_t dmask, uint32_t prefix, uint32_t mask) {
+  int above = 0, at = 0;                          // this wave's rows above / at the threshold
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+    const uint32_t dmask = pass == 2 ? 1023u : 2047u;
+    __syncthreads();                              // every wave is done with the histograms
+    topk_clear_hist(hw);
+    const uint32_t pf = prefix, mk = mask;
     for_tiles(sc, wb, we, n, [&](int b, const uint32_t (&u)[4]) {
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        if (b + 4 * lane + e < we && (u[e] & mask) == prefix) atomicAdd(&hw[(u[e] >> shift) & dmask], 1);
+        if (b + 4 * lane + e < we && (u[e] & mk) == pf) atomicAdd(&hw[(u[e] >> shift) & dmask], 1);
     });
-  };
-  // this wave's rows in its histogram's bins above / at digit dg
-  auto wave_above = [&](int dg) {
-    int a = 0;
+    __syncthreads();
+    const int dg = topk_next_digit(s, shift, dmask, prefix, mask, need);
+    int a = 0;                                    // this wave's rows in its bins above the digit
 #pragma unroll
     for (int c = 0; c < kTopkBins / 64; ++c) a += lane + 64 * c > dg ? hw[lane + 64 * c] : 0;
-    return wave_sum_int(a);
-  };
-  // first digit over the whole row
-  clear_hist();
-  hist_row(21, 2047u, 0u, 0u);
-  __syncthreads();
-  topk_digit(s, 21, 2047u, 0u, 0u, K);
-  uint32_t prefix = s.st[0], mask = s.st[1];
-  int need = (int)s.st[2];
-  const int nlist = (int)s.st[3];                 // rows in the digit's bin and above
-  const int dg0 = (int)(prefix >> 21);
-  int above = wave_above(dg0), at = hw[dg0];
-  if (nlist <= kTopkList) {
-    // ---- the rows in the first digit's bin and above, in order, into the LDS list
-    if (lane == 0) s.wc[w] = above + at;
-    __syncthreads();
-    int off = 0;
-    for (int v = 0; v < w; ++v) off += s.wc[v];
-    const uint32_t lo = prefix;                   // keys >= lo: first digit >= dg0
-    const uint64_t lt = (1ull << lane) - 1ull;
-    for_tiles(sc, wb, we, n, [&](int b, const uint32_t (&u)[4]) {
-      bool sel[4];
-      int pb = 0, ps = 0;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        sel[e] = b + 4 * lane + e < we && u[e] >= lo;
-        const uint64_t m = __ballot(sel[e]);
-        pb += __popcll(m & lt);
-        ps += __popcll(m);
-      }
-      int pos = off + pb;
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (sel[e]) {
-          s.lkey[pos] = u[e];
-          s.lrow[pos] = b + 4 * lane + e;
-          ++pos;
-        }
-      off += ps;
-    });
-    __syncthreads();
-    // ---- the last two digits over the list's candidates (first digit == dg0)
-    for (int pass = 1; pass < 3; ++pass) {
-      const int shift = pass == 1 ? 10 : 0;
-      const uint32_t dmask = pass == 2 ? 1023u : 2047u;
-      clear_hist();
-      for (int m = threadIdx.x; m < nlist; m += kThreads) {
-        const uint32_t u = s.lkey[m];
-        if ((u & mask) == prefix) atomicAdd(&hw[(u >> shift) & dmask], 1);
-      }
-      __syncthreads();
-      topk_digit(s, shift, dmask, prefix, mask, need);
-      prefix = s.st[0];
-      mask = s.st[1];
-      need = (int)s.st[2];
-    }
-    // ---- output: wave w writes list entries [w * segl, (w + 1) * segl)
-    const int segl = (nlist + kWaves * 64 - 1) / (kWaves * 64) * 64;
-    const int lb = min(nlist, w * segl), le = min(nlist, lb + segl);
-    int ga = 0, ea = 0;
-    for (int m = lb + lane; m < le; m += 64) {
-      const uint32_t u = s.lkey[m];
-      ga += u > prefix;
-      ea += u == prefix;
-    }
-    ga = wave_sum_int(ga);
-    ea = wave_sum_int(ea);
-    __syncthreads();                              // every wave has read wc above
-    if (lane == 0) {
-      s.wc[2 * w] = ga;
-      s.wc[2 * w + 1] = ea;
-    }
-    __syncthreads();
-    int G = 0, E = 0;
-    for (int v = 0; v < w; ++v) {
-      G += s.wc[2 * v];
-      E += s.wc[2 * v + 1];
-    }
-    for (int m0 = lb; m0 < le; m0 += 64) {
-      const int m = m0 + lane;
-      const bool ok[1] = {m < le};
-      const int rows[1] = {ok[0] ? s.lrow[m] : 0};
-      const uint32_t u[1] = {ok[0] ? s.lkey[m] : 0u};
-      topk_write<1>(out, rows, u, ok, prefix, need, G, E);
-    }
-    return;
-  }
-  // ---- the list would not fit: the last two digits and the output read the row
-  for (int pass = 1; pass < 3; ++pass) {
-    const int shift = pass == 1 ? 10 : 0;
-    const uint32_t dmask = pass == 2 ? 1023u : 2047u;
-    clear_hist();
-    hist_row(shift, dmask, prefix, mask);
-    __syncthreads();
-    topk_digit(s, shift, dmask, prefix, mask, need);
-    prefix = s.st[0];
-    mask = s.st[1];
-    need = (int)s.st[2];
-    const int dg = (int)((prefix >> shift) & dmask);
-    above += wave_above(dg);
+    above += wave_sum_int(a);
     if (pass == 2) at = hw[dg];
   }
   if (lane == 0) {
@@ -1120,6 +1080,205 @@ __device__ __forceinline__ void phase_topk(const LayerParams& p, int L, char* sm
     }
     topk_write<4>(out, rows, u, ok, prefix, need, G, E);
   });
+}
+// The parts' work; returns true when this workgroup (a row's first part) must
+// take the row from its full keys instead.
+__device__ __forceinline__ bool topk_parts(const LayerParams& p, int L, const TopkLds& s) {
+  const int T = p.T, K = p.itopk, P = max(1, (int)gridDim.x / T);
+  const int t = blockIdx.x / P, part = blockIdx.x - t * P;
+  if (t >= T) return false;
+  const int n = L + t + 1;
+  int32_t* out = p.isel + (long long)t * K;
+  if (n <= K) {
+    if (part == 0)
+      for (int i = threadIdx.x; i < n; i += kThreads) out[i] = i;
+    return false;
+  }
+  const float* sc = p.iscore + (long long)t * p.imax;
+  const int S = max(kTopkPart, ((n + P - 1) / P + 511) / 512 * 512), parts = (n + S - 1) / S;
+  if (parts > kThreads || S / 512 > kThreads) return part == 0;   // (beyond the parts' LDS tables)
+  if (part >= parts) return false;
+  const uint16_t* k16 = p.ik16 + (long long)t * p.imax;
+  uint32_t* ghist = p.ihist + (long long)t * kTopkBins;
+  uint32_t* done1 = p.ictr + t * kIdxCtrStride;                // parts that added their bins
+  uint32_t* done2 = done1 + kIdxCtrStride / 2;                  // parts that wrote their pairs
+  uint64_t* pairs = reinterpret_cast<uint64_t*>(p.icand) + (long long)t * p.imax;
+  uint32_t* pcnt = p.icnt + t * kThreads;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const uint64_t lt = (1ull << lane) - 1ull;
+  const int kb = part * S, ke = min(n, kb + S), ntile = (ke - kb + 511) / 512;
+  // ---- this part's first-digit histogram, added into the row's
+  int* lh = s.hist;                               // one histogram for the workgroup
+  for (int i = threadIdx.x; i < kTopkBins / 4; i += kThreads) reinterpret_cast<int4*>(lh)[i] = int4{0, 0, 0, 0};
+  __syncthreads();
+  for (int tile = w; tile < ntile; tile += kWaves) {
+    const int b = kb + tile * 512 + 8 * lane;
+    uint32_t u[8];
+    keys16(k16, b, n, u);
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (b + e < ke) atomicAdd(&lh[u[e] >> 5], 1);
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < kTopkBins; i += kThreads) {
+    const int v = lh[i];
+    if (v) __hip_atomic_fetch_add(ghist + i, (uint32_t)v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  wg_release_begin();                             // the additions are performed
+  if (threadIdx.x == 0) {
+    __hip_atomic_fetch_add(done1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s.res[3] = wait_count(p, done1, (uint32_t)parts);
+  }
+  __syncthreads();
+  if (!s.res[3]) return false;
+  // ---- the first digit (top 11 bits) from the row's histogram
+  int h4[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    h4[q] = (int)__hip_atomic_load(ghist + kTopkBins - 1 - 4 * threadIdx.x - q, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+  digit_of(h4, K, s.sbuf, s.res);
+  const int d0 = s.res[0], cum0 = s.res[1], nlist = s.res[1] + s.res[2];
+  const uint32_t lo = (uint32_t)d0 << 5;
+  // ---- this part's rows at or above the digit's bin, as (top 16 bits, row)
+  // pairs in ascending row order from the part's first row's place
+  int* tc = s.poff;                               // [ntile]: a tile's pairs, then its first place
+  for (int tile = w; tile < ntile; tile += kWaves) {
+    const int b = kb + tile * 512 + 8 * lane;
+    uint32_t u[8];
+    keys16(k16, b, n, u);
+    int c = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) c += __popcll(__ballot(b + e < ke && u[e] >= lo));
+    if (lane == 0) tc[tile] = c;
+  }
+  __syncthreads();
+  const int tcv = (int)threadIdx.x < ntile ? tc[threadIdx.x] : 0;
+  const int tinc = wg_scan_incl(tcv, s.sbuf);
+  if ((int)threadIdx.x < ntile) tc[threadIdx.x] = tinc - tcv;
+  if (threadIdx.x == kThreads - 1) s.res[3] = tinc;             // the part's pairs
+  __syncthreads();
+  for (int tile = w; tile < ntile; tile += kWaves) {
+    const int b = kb + tile * 512 + 8 * lane;
+    uint32_t u[8];
+    keys16(k16, b, n, u);
+    bool sel[8];
+    int pb = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      sel[e] = b + e < ke && u[e] >= lo;
+      pb += __popcll(__ballot(sel[e]) & lt);
+    }
+    int pos = kb + tc[tile] + pb;
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (sel[e]) {
+        __hip_atomic_store(pairs + pos, ((uint64_t)u[e] << 32) | (uint32_t)(b + e), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+        ++pos;
+      }
+  }
+  if (threadIdx.x == 0) __hip_atomic_store(pcnt + part, (uint32_t)s.res[3], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  wg_release_begin();                             // the pairs are written
+  if (threadIdx.x == 0) __hip_atomic_fetch_add(done2, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (part != 0) return false;
+  // ---- the row's first part: every part's pairs, in order, into the LDS list
+  if (threadIdx.x == 0) s.res[3] = wait_count(p, done2, (uint32_t)parts);
+  __syncthreads();
+  if (!s.res[3]) return false;
+  bool fits = nlist <= kTopkList;
+  if (fits) {
+    const int pc = (int)threadIdx.x < parts
+                       ? (int)__hip_atomic_load(pcnt + threadIdx.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                       : 0;
+    const int pinc = wg_scan_incl(pc, s.sbuf);
+    s.poff[threadIdx.x] = pinc - pc;
+    if (threadIdx.x == kThreads - 1) s.res[3] = pinc;
+    __syncthreads();
+    fits = s.res[3] == nlist;                     // (always: the same keys and digit)
+  }
+  if (!fits) return true;
+  // list place m: part q with poff[q] <= m < poff[q + 1], its pair m - poff[q]
+  constexpr int kU = 8;
+  for (int m0 = threadIdx.x; m0 < nlist; m0 += kThreads * kU) {
+    uint64_t e[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int m = min(m0 + u * kThreads, nlist - 1);
+      int a = 0, z = parts - 1;                   // the last part whose first place <= m
+      while (a < z) {
+        const int mid = (a + z + 1) >> 1;
+        if (s.poff[mid] <= m) a = mid;
+        else z = mid - 1;
+      }
+      e[u] = __hip_atomic_load(pairs + a * S + (m - s.poff[a]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int m = m0 + u * kThreads;
+      if (m < nlist) {
+        s.lrow[m] = (int)(uint32_t)e[u];
+        s.lkey[m] = (uint32_t)(e[u] >> 32) << 16;
+      }
+    }
+  }
+  __syncthreads();
+  uint32_t prefix = (uint32_t)d0 << 21, mask = 2047u << 21;     // the threshold's bits found so far
+  int need = K - cum0;                                          // rows at the prefix still to take
+  int* hw = s.hist + w * kTopkBins;
+  auto list_digit = [&](int shift, uint32_t dmask) {
+    topk_clear_hist(hw);
+    for (int m = threadIdx.x; m < nlist; m += kThreads) {
+      const uint32_t u = s.lkey[m];
+      if ((u & mask) == prefix) atomicAdd(&hw[(u >> shift) & dmask], 1);
+    }
+    __syncthreads();
+    topk_next_digit(s, shift, dmask, prefix, mask, need);
+  };
+  list_digit(16, 31u);                            // bits 16..20
+  // the rows that share the threshold's top 16 bits read their full keys
+  for (int m = threadIdx.x; m < nlist; m += kThreads)
+    if (s.lkey[m] == prefix) s.lkey[m] = order_key(ldg(sc + s.lrow[m]));
+  __syncthreads();
+  list_digit(5, 2047u);                           // bits 5..15
+  list_digit(0, 31u);                             // bits 0..4
+  // ---- output: wave w writes list entries [w * segl, (w + 1) * segl)
+  const int segl = (nlist + kWaves * 64 - 1) / (kWaves * 64) * 64;
+  const int lb = min(nlist, w * segl), le = min(nlist, lb + segl);
+  int ga = 0, ea = 0;
+  for (int m = lb + lane; m < le; m += 64) {
+    const uint32_t u = s.lkey[m];
+    ga += u > prefix;
+    ea += u == prefix;
+  }
+  ga = wave_sum_int(ga);
+  ea = wave_sum_int(ea);
+  if (lane == 0) {
+    s.wc[2 * w] = ga;
+    s.wc[2 * w + 1] = ea;
+  }
+  __syncthreads();
+  int G = 0, E = 0;
+  for (int v = 0; v < w; ++v) {
+    G += s.wc[2 * v];
+    E += s.wc[2 * v + 1];
+  }
+  for (int m0 = lb; m0 < le; m0 += 64) {
+    const int m = m0 + lane;
+    const bool ok[1] = {m < le};
+    const int rows[1] = {ok[0] ? s.lrow[m] : 0};
+    const uint32_t u[1] = {ok[0] ? s.lkey[m] : 0u};
+    topk_write<1>(out, rows, u, ok, prefix, need, G, E);
+  }
+  return false;
+}
+
+__device__ __forceinline__ void phase_topk(const LayerParams& p, int L, char* smem) {
+  const TopkLds s(smem);
+  if (topk_parts(p, L, s)) {
+    const int t = blockIdx.x / max(1, (int)gridDim.x / p.T);
+    topk_full_row(p.iscore + (long long)t * p.imax, L + t + 1, p.itopk, p.isel + (long long)t * p.itopk, s);
+  }
 }
 
 // ------------------------------------------------------------------ P2 attention
@@ -2520,7 +2679,13 @@ __global__ __launch_bounds__(kThreads, 1) void layer_kernel(LayerParams p) {
     phase_uq<AF, SP>(p, smem);
     if (!grid_barrier(p, 8, flag)) return raise_model_fault(p);
   }
-  if constexpr (SP) stage_index_queries<LR>(p, blockIdx.x * kThreads + threadIdx.x, gridDim.x * kThreads);
+  if constexpr (SP) {
+    stage_index_queries<LR>(p, blockIdx.x * kThreads + threadIdx.x, gridDim.x * kThreads);
+    // the top-k's row histograms and part counters start at zero
+    for (int i = blockIdx.x * kThreads + threadIdx.x; i < kMaxT * (kTopkBins + kIdxCtrStride); i += gridDim.x * kThreads)
+      __hip_atomic_store(i < kMaxT * kTopkBins ? p.ihist + i : p.ictr + (i - kMaxT * kTopkBins), 0u,
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
   {
     // absorbed-query units on waves [0, wa) of every workgroup; when they fit
     // in half the waves, RoPE / KV insert runs on the other half meanwhile

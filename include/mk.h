@@ -131,7 +131,7 @@ typedef struct mk_layer_config {
   int32_t idx_heads;
   int32_t idx_dim;
   int32_t idx_topk;
-  int32_t idx_max_rows;      /* sparse: the largest L + T a step may use, a multiple of 4 (sizes
+  int32_t idx_max_rows;      /* sparse: the largest L + T a step may use, a multiple of 8 (sizes
                                 the workspace's index scores); a step past it is refused */
 } mk_layer_config;
 

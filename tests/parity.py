@@ -101,7 +101,7 @@ def gpu_step(dl, s, H_dev, kv_dev, L, T=None):
         dl.layer.debug_tap(tap, buf)
         taps[name] = oracle.bf16_to_f32(buf) if dt == np.uint16 else buf
     if s.idx_topk:
-        imax = (s.capacity + 3) // 4 * 4
+        imax = (s.capacity + 7) // 8 * 8
         for name, tap, shape, dt in (("isel", 8, (T, s.idx_topk), np.int32), ("iscore", 9, (T, imax), np.float32)):
             buf = np.empty(shape, dt)
             dl.layer.debug_tap(tap, buf)
