@@ -966,3 +966,19 @@ def test_sparse_attention_weights_only_the_kept_rows():
             p /= p.sum()
             z = p @ rows[sel, : s.d_c]
             assert np.abs(taps["z"][i, h] - z).max() <= 1e-5 * np.abs(z).max()
+
+
+def test_sparse_ties_keep_the_lower_rows():
+    """Indexer weights of zero make every index score 0: each row keeps the
+    lowest idx_topk rows it may see (ties go to the lower row), in both the
+    fp32 and the fp64 path."""
+    s = C0S
+    w, H, kv = fresh(s)
+    w["widx"] = np.zeros_like(w["widx"])
+    kv64 = kv.copy()
+    out, taps = oracle.layer_step(s, w, H, kv, s.L)
+    assert not taps["iscore"][:, : s.L + s.T].any()
+    for i in range(s.T):
+        assert list(taps["isel"][i][: s.idx_topk]) == list(range(s.idx_topk))
+    ref = oracle.layer_step_f64(s, w, H, kv64, s.L, force_sel=taps["sel"])
+    assert normwise(out, ref["out"]) < 1e-5
