@@ -977,8 +977,8 @@ def test_sparse_ties_keep_the_lower_rows():
     w["widx"] = np.zeros_like(w["widx"])
     kv64 = kv.copy()
     out, taps = oracle.layer_step(s, w, H, kv, s.L)
-    assert not taps["iscore"][:, : s.L + s.T].any()
     for i in range(s.T):
+        assert not taps["iscore"][i, : s.L + i + 1].any()      # the rows row i may see
         assert list(taps["isel"][i][: s.idx_topk]) == list(range(s.idx_topk))
     ref = oracle.layer_step_f64(s, w, H, kv64, s.L, force_sel=taps["sel"])
     assert normwise(out, ref["out"]) < 1e-5
