@@ -13,7 +13,7 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmk.so")
 
-MK_ABI_VERSION = 3
+MK_ABI_VERSION = 4
 MK_MAX_T = 8   # verify rows per step
 MK_STATIC_SCRATCH_BYTES = 32 << 20
 
@@ -63,7 +63,8 @@ class LayerConfig(ctypes.Structure):
                 ("n_shared", _i32), ("d_ff", _i32), ("attn_format", _i32), ("expert_format", _i32),
                 ("kv_format", _i32), ("has_router_bias", _i32), ("rms_eps", ctypes.c_float),
                 ("rope_base", ctypes.c_float), ("q_lora_rank", _i32), ("kv_norm", _i32), ("idx_heads", _i32),
-                ("idx_dim", _i32), ("idx_topk", _i32), ("idx_max_rows", _i32)]
+                ("idx_dim", _i32), ("idx_topk", _i32), ("idx_max_rows", _i32),
+                ("kv_max_rows", _i32)]
 
 
 class DeviceInfo(ctypes.Structure):
@@ -164,11 +165,12 @@ def query_device(hip_device: int = 0) -> DeviceInfo:
 def make_config(d_model, n_heads, d_head, d_latent, d_rope, n_experts, top_k, n_shared, d_ff,
                 attn_format, expert_format, kv_format, has_router_bias=0, rms_eps=1e-6, rope_base=10000.0,
                 abi_version=MK_ABI_VERSION, q_lora_rank=0, kv_norm=0, idx_heads=0, idx_dim=0, idx_topk=0,
-                idx_max_rows=0) -> LayerConfig:
+                idx_max_rows=0, kv_max_rows=0) -> LayerConfig:
     fm = lambda f: FORMATS[f] if isinstance(f, str) else int(f)
     return LayerConfig(abi_version, d_model, n_heads, d_head, d_latent, d_rope, n_experts, top_k, n_shared, d_ff,
                        fm(attn_format), fm(expert_format), fm(kv_format), int(has_router_bias), rms_eps, rope_base,
-                       int(q_lora_rank), int(kv_norm), int(idx_heads), int(idx_dim), int(idx_topk), int(idx_max_rows))
+                       int(q_lora_rank), int(kv_norm), int(idx_heads), int(idx_dim), int(idx_topk), int(idx_max_rows),
+                       int(kv_max_rows))
 
 
 def check_config(cfg: LayerConfig) -> None:

@@ -44,6 +44,9 @@ struct Dims {
   int af, ef, kf;
   int ql, kvn;       // low-rank query rank (0: one W_Q), latent norm
   int ih, idm, ik, imax;   // sparse attention: indexer heads, key dim, rows kept, largest L + T
+  int kvmax;               // the largest L + T the caller expects (0: not stated)
+  // long contexts may take the four-tile attention units (their partials are sized for it)
+  bool att_share() const { return kf == MK_FMT_BF16 && dc == 512 && dr == 64 && ik == 0 && kvmax >= 16384; }
   int nqp() const { return ql > 0 ? ql : nq; }   // rows of the first projection's query part
   int nidx() const { return ik > 0 ? ih * idm + ih + idm : 0; }   // indexer rows of the first projection
   int kvrow() const { return kvw + (ik > 0 ? idm : 0); }           // values per cache row
@@ -70,6 +73,7 @@ Dims dims_of(const mk_layer_config* c) {
   D.nshared = c->n_shared; D.f = c->d_ff; D.af = c->attn_format; D.ef = c->expert_format; D.kf = c->kv_format;
   D.ql = c->q_lora_rank; D.kvn = c->kv_norm;
   D.ih = c->idx_heads; D.idm = c->idx_dim; D.ik = c->idx_topk; D.imax = c->idx_max_rows;
+  D.kvmax = c->kv_max_rows;
   return D;
 }
 
@@ -87,6 +91,7 @@ int check_cfg(const mk_layer_config* c) {
   if (D.ql > 0 && (D.af != MK_FMT_BF16 || D.ql % 32 || D.ql > D.d))
     return fail(MK_ERR_UNSUPPORTED_SHAPE, "a low-rank query needs bf16 attention and a rank that is a multiple of 32, <= d_model");
   if (D.kvn && D.ql == 0) return fail(MK_ERR_UNSUPPORTED_SHAPE, "the latent norm is built with the low-rank query only");
+  if (D.kvmax < 0) return fail(MK_ERR_INVALID_ARG, "kv_max_rows must be >= 0");
   if (D.ik < 0) return fail(MK_ERR_INVALID_ARG, "idx_topk must be >= 0");
   if (D.ik > 0) {
     if (D.af != MK_FMT_BF16 || D.kf != MK_FMT_BF16)
@@ -250,7 +255,9 @@ WsLayout ws_layout(const Dims& D, const Schedule& s) {
   auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
   const int T = kMaxT;
   const int nqt = (T * D.nh + 15) / 16;
-  const int units = std::max(s.nwg, nqt);
+  // attention partials: one per (query tile, key split); four-tile units take
+  // grid / ceil(tiles / 4) splits, so up to four partials per workgroup
+  const int units = D.att_share() ? 4 * s.nwg + nqt : std::max(s.nwg, nqt);
   const int slots = std::min(D.E, T * D.topk) + D.nshared;
   w.qkv_part = take((size_t)s.s_q * T * (D.nqp() + D.kvw + D.nidx()) * 4);
   w.qrope = take((size_t)T * D.nh * D.dr * 4);
@@ -617,6 +624,7 @@ int mk_layer_init(const mk_layer_config* cfg, const mk_layer_weights* w, void* s
   p.ql = D.ql; p.kv_norm = D.kvn;
   p.wdq = (const uint8_t*)w->wdq; p.wuq = (const uint8_t*)w->wuq; p.gq = w->gamma_q; p.gkv = w->gamma_kv;
   p.ihead = D.ih; p.idim = D.idm; p.itopk = D.ik; p.imax = D.imax; p.kv_row = D.kvrow();
+  p.att_share = D.att_share() ? 1 : 0;
   p.widx = (const uint8_t*)w->widx;
   p.experts = (const uint8_t* const*)(L->state + L->sl.experts);
   p.exp_w13_bytes = exp_w13(D);

@@ -145,6 +145,7 @@ struct LayerParams {
   uint32_t* icand;         // sparse: (row, top 16 bits) pairs of the parts [kMaxT][idx_max_rows][2]
   int32_t* isel;           // sparse: kept rows [T][itopk], ascending
   int imax;                // sparse: idx_max_rows
+  int att_share;           // long contexts may take the four-tile attention units (partials sized for them)
   float* qrope;            // [T][nh][dr]
   float* qabs;             // [T][nh][dc]
   float* att_part;         // [units][16][dc]

@@ -1306,9 +1306,18 @@ template <> struct AttnTypes<MK_FMT_FP8_ROW> {
 
 constexpr float kAttSlack = 8.f;                 // softmax reference moves when exceeded by this much
 
+// Long contexts: a unit is four query tiles and one key split (see
+// phase_attention_shared).  Used when the layer allows it (the dense bf16
+// cache of the 512 + 64 latent shape, with room for the partials) and a split
+// of the one-tile plan would hold at least kAttShareRows keys.
+constexpr int kAttShareRows = 1024;
+__device__ __forceinline__ bool attn_shared(const LayerParams& p, int NQT, int Lt) {
+  const int s1 = max(1, (int)gridDim.x / NQT);
+  return p.att_share && (Lt + s1 - 1) / s1 >= kAttShareRows;
+}
 // KV splits per query tile and keys per split (the same in P2 and P3).
-__device__ __forceinline__ void attn_splits(int NQT, int Lt, int& s_kv, int& SK) {
-  s_kv = (int)gridDim.x / NQT;
+__device__ __forceinline__ void attn_splits(int NQT, int Lt, int& s_kv, int& SK, bool shared = false) {
+  s_kv = (int)gridDim.x / (shared ? (NQT + 3) / 4 : NQT);
   if (s_kv < 1) s_kv = 1;
   const int nchunk_all = (Lt + 15) / 16;
   if (s_kv > nchunk_all) s_kv = nchunk_all;
@@ -1586,6 +1595,187 @@ __device__ __forceinline__ void phase_attention(const LayerParams& p, int L, cha
   }
 }
 
+// P2 for long contexts (dense, bf16 cache, d_latent 512 + d_rope 64): one unit
+// = (a group of four query tiles, one key split).  Pair c of the 8 waves takes
+// tile 4 * group + c, and every pair works on the same key chunk, which the
+// workgroup stages in LDS once: each chunk's 16 rows are loaded by all threads
+// kStageAhead chunks ahead into registers and stored into a ring of three LDS
+// buffers one round before use, so a key row is read from memory once per four
+// query tiles instead of once per tile.  As in phase_attention, the two waves
+// of a pair take half of the key dims each (their query fragments held in
+// LDS for the whole unit), add their halves of S through LDS, run the
+// same online softmax and multiply P into their half of Z, reading the value
+// rows transposed from the staged chunk.  A pair's partial (Z, max, sum) is its
+// tile's partial for this split; no merge across pairs is needed.
+constexpr int kStageAhead = 2;
+__device__ __forceinline__ void phase_attention_shared(const LayerParams& p, int L, char* smem) {
+  constexpr int KBW = 32, NLAT = 16, DC = 512, KVW = 576, NKB = 9, DBH = 16;
+  constexpr int KS = KVW + 8;                          // LDS row stride (bf16) of queries and keys
+  constexpr int PIECES = 16 * KVW / 8;                 // 16-byte pieces of one chunk (1152)
+  constexpr int PT = (PIECES + kThreads - 1) / kThreads;   // per thread (3)
+  const int T = p.T, nh = p.nh;
+  const int NQ = T * nh, NQT = (NQ + 15) / 16, NG = (NQT + 3) / 4, Lt = L + T;
+  int s_kv, SK;
+  attn_splits(NQT, Lt, s_kv, SK, true);
+  const int units = NG * s_kv;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, j = lane & 15, g = lane >> 4;
+  const int hf = w & 1, cg = w >> 1;
+  __bf16* qs = reinterpret_cast<__bf16*>(smem);                        // [4 tiles][16][KS]
+  __bf16* ring = qs + 4 * 16 * KS;                                     // [3][16][KS]
+  f32x4* sx = reinterpret_cast<f32x4*>(ring + 3 * 16 * KS);            // [2][8 waves][64]
+  const __bf16* kvb = reinterpret_cast<const __bf16*>(p.kv);
+  // this wave's key blocks: latent blocks 8 hf .. 8 hf + 7, then RoPE block 16 + hf
+  auto kblk = [&](int i) { return i < 8 ? 8 * hf + i : NLAT + hf; };
+#pragma unroll 1
+  for (int v = blockIdx.x; v < units; v += gridDim.x) {
+    const int grp = v / s_kv, s = v - grp * s_kv;
+    const int qt = grp * 4 + cg;                       // this pair's tile (qt >= NQT: the pair only keeps step)
+    const bool live = qt < NQT;
+    const int qc = min(min(qt, NQT - 1) * 16 + j, NQ - 1);
+    const int limit = L + qc / nh;                     // keys 0..limit are visible
+    const int k0 = s * SK, k1 = min(Lt, k0 + SK);
+    const int nch = k1 > k0 ? (k1 - k0 + 15) / 16 : 0;
+    // the 16-byte pieces this thread loads of chunk c (rows past the split clamped)
+    auto load_chunk = [&](int c, u32x4 (&r)[PT]) {
+#pragma unroll
+      for (int q = 0; q < PT; ++q) {
+        const int pc = min((int)threadIdx.x + q * kThreads, PIECES - 1), row = pc / (KVW / 8);
+        const int key = min(k0 + c * 16 + row, Lt - 1);
+        r[q] = ld16(kvb + (long long)key * KVW + (pc - row * (KVW / 8)) * 8);
+      }
+    };
+    auto store_chunk = [&](int slot, const u32x4 (&r)[PT]) {
+#pragma unroll
+      for (int q = 0; q < PT; ++q) {
+        const int pc = (int)threadIdx.x + q * kThreads, row = pc / (KVW / 8);
+        if (pc < PIECES)
+          *reinterpret_cast<u32x4*>(ring + (slot * 16 + row) * KS + (pc - row * (KVW / 8)) * 8) = r[q];
+      }
+    };
+    __syncthreads();                                   // the previous unit is done with the LDS
+    // the four tiles' queries [q~ | rotated q^R] -> LDS (bf16), loads first,
+    // then chunk 0 and the next kStageAhead chunks
+    {
+      // two rounds of 9 float4s per thread (4 tiles x 16 queries x 144 float4s)
+      constexpr int N4 = KVW / 4, NV = 9, NQV = 4 * 16 * N4;
+      u32x4 c0[PT];
+      load_chunk(0, c0);
+#pragma unroll 1
+      for (int half = 0; half < 2; ++half) {
+        f32x4 qv[NV];
+#pragma unroll
+        for (int c = 0; c < NV; ++c) {
+          const int i = min((int)threadIdx.x + (half * NV + c) * kThreads, NQV - 1);
+          const int jq = i / N4, dd = (i - jq * N4) * 4;
+          const int qq = min(grp * 64 + jq, NQ - 1);
+          const float* src = dd < DC ? p.qabs + (long long)qq * DC + dd : p.qrope + (long long)qq * p.dr + (dd - DC);
+          qv[c] = ldg(reinterpret_cast<const f32x4*>(src));
+        }
+#pragma unroll
+        for (int c = 0; c < NV; ++c) {
+          const int i = threadIdx.x + (half * NV + c) * kThreads;
+          if (i < NQV) {
+            const int jq = i / N4, dd = (i - jq * N4) * 4;
+            store4<__bf16>(qs + jq * KS + dd, qv[c]);
+          }
+        }
+      }
+      store_chunk(0, c0);
+    }
+    u32x4 pre[kStageAhead][PT];                        // chunks c + 1 .. c + kStageAhead
+#pragma unroll
+    for (int a = 0; a < kStageAhead; ++a) load_chunk(1 + a, pre[a]);
+    __syncthreads();
+    // this wave's query fragments (B operand): query j, dims kblk(i) * 32 + 8 g .. + 7
+    const __bf16* qlane = qs + (cg * 16 + j) * KS + g * 8;
+    trace_x(p, 0);
+    float m_run = -INFINITY, l_run = 0.f;
+    f32x4 acc[DBH];
+#pragma unroll
+    for (int db = 0; db < DBH; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+    for (int c = 0; c < nch; ++c) {
+      const int kbase = k0 + c * 16;
+      const __bf16* kc = ring + (c % 3) * 16 * KS;
+      // this wave's half of S^T = K Q^T (keys from the staged chunk)
+      f32x4 st = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < NKB; ++i)
+        st = mma_bf16_k32(*reinterpret_cast<const bf16x8*>(kc + j * KS + kblk(i) * KBW + g * 8),
+                          *reinterpret_cast<const bf16x8*>(qlane + kblk(i) * KBW), st);
+      f32x4* sxb = sx + (c & 1) * (kWaves * 64);
+      sxb[w * 64 + lane] = st;
+      // the next chunk goes to its ring slot (its readers are two rounds back)
+      // and the chunk kStageAhead past it is requested
+      if (c + 1 < nch) store_chunk((c + 1) % 3, pre[0]);
+#pragma unroll
+      for (int a = 0; a + 1 < kStageAhead; ++a)
+#pragma unroll
+        for (int q = 0; q < PT; ++q) pre[a][q] = pre[a + 1][q];
+      load_chunk(c + 1 + kStageAhead, pre[kStageAhead - 1]);
+      __syncthreads();
+      {
+        const f32x4 o = sxb[(w ^ 1) * 64 + lane];
+        st = hf ? o + st : st + o;
+      }
+      float sc[4];
+      float cmax = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int kk = kbase + 4 * g + e;
+        sc[e] = (kk <= limit && kk < k1) ? st[e] * p.scale : -INFINITY;
+        cmax = fmaxf(cmax, sc[e]);
+      }
+      cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
+      cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
+      const bool move = cmax > m_run + kAttSlack;
+      if (__builtin_amdgcn_ballot_w64(move) != 0) {
+        const float m_new = move ? cmax : m_run;
+        const float alpha = m_run == -INFINITY ? 0.f : __expf(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < DBH; ++db) acc[db] *= alpha;
+        m_run = m_new;
+      }
+      float pe[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pe[e] = m_run == -INFINITY ? 0.f : __expf(sc[e] - m_run);
+      float ps = pe[0] + pe[1] + pe[2] + pe[3];
+      ps += __shfl_xor(ps, 16);
+      ps += __shfl_xor(ps, 32);
+      l_run += ps;
+      bf16x4 pb;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pb[e] = (__bf16)pe[e];
+      // A operand (dims x keys) read transposed from the staged rows: lane
+      // (g, 4e + q) points at key 4g + e, dims 256 hf + 16 db + 4q .. + 3
+      const __bf16* tb = kc + (4 * g + (j >> 2)) * KS + 256 * hf + 4 * (j & 3);
+#pragma unroll
+      for (int d0 = 0; d0 < DBH; d0 += 8) {
+        bf16x4 av[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) av[i] = lds_read_tr16(tb + (d0 + i) * 16);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[d0 + i] = mma_bf16_k16(av[i], pb, acc[d0 + i]);
+      }
+    }
+    trace_x(p, 1);
+    if (live) {
+      // the pair's partial: wave hf writes latent dims 256 hf .. 256 hf + 255 of
+      // its 16 queries (query-major), wave 0 of the pair the (max, sum)
+      const int u = qt * s_kv + s;
+      f32x4* zp = reinterpret_cast<f32x4*>(p.att_part + (long long)u * 16 * DC);
+#pragma unroll
+      for (int db = 0; db < DBH; ++db) zp[j * (DC / 4) + (16 * hf + db) * 4 + g] = acc[db];
+      if (hf == 0 && g == 0) {
+        p.att_ml[((long long)u * 16 + j) * 2] = m_run;
+        p.att_ml[((long long)u * 16 + j) * 2 + 1] = l_run;
+      }
+    }
+    trace_x(p, 2);
+  }
+}
+
 // ------------------------------------------------------------------ P3  split merge and o = W_UV z
 // One unit = (head h, a group of up to kMergeRows verify rows).  Wave w
 // requests row tile w of W_UV^(h) first; then two threads per latent item
@@ -1600,14 +1790,14 @@ constexpr int kMergeRows = 2;
 constexpr int kMergeSB = 12;                      // splits per thread per batch
 constexpr int kMergeXOff = 8192;                  // LDS: half-merge exchange after the z operand
 template <int AF, bool SP = false>
-__device__ __forceinline__ void phase_merge_uv(const LayerParams& p, int L, char* smem) {
+__device__ __forceinline__ void phase_merge_uv(const LayerParams& p, int L, char* smem, bool shared = false) {
   typedef typename Act<AF>::T A;
   constexpr int TK = tile_k(AF);
   constexpr int KTMAX = 16;                       // d_latent / tile_k <= 16 for every supported shape
   const int T = p.T, nh = p.nh, dc = p.dc, dh = p.dh;
   const int NQ = T * nh, NQT = (NQ + 15) / 16;
   int s_kv, SK;
-  attn_splits(NQT, SP ? min(p.itopk, L + T) : L + T, s_kv, SK);
+  attn_splits(NQT, SP ? min(p.itopk, L + T) : L + T, s_kv, SK, shared);
   const int TG = (T + kMergeRows - 1) / kMergeRows;
   const int U = nh * TG, XS = dc + kXPad, RT = dh / 16, KT = dc / TK, D4 = dc / 4;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, j = lane & 15, g = lane >> 4;
@@ -2707,9 +2897,15 @@ __global__ __launch_bounds__(kThreads, 1) void layer_kernel(LayerParams p) {
     phase_topk(p, L, smem);
     if (!grid_barrier(p, 10, flag)) return raise_model_fault(p);
   }
-  phase_attention<KF, KBMAX, DBMAX, EXACT, SP>(p, L, smem);
+  // long contexts: four query tiles per unit (the instance for the dense bf16
+  // cache of the 512 + 64 latent shape only); P3 merges the same plan
+  bool att_sh = false;
+  if constexpr (KF == MK_FMT_BF16 && EXACT && !SP && KBMAX == 18 && DBMAX == 32)
+    att_sh = attn_shared(p, (p.T * p.nh + 15) / 16, L + p.T);
+  if (att_sh) phase_attention_shared(p, L, smem);
+  else phase_attention<KF, KBMAX, DBMAX, EXACT, SP>(p, L, smem);
   if (!grid_barrier(p, 2, flag)) return raise_model_fault(p);
-  phase_merge_uv<AF, SP>(p, L, smem);
+  phase_merge_uv<AF, SP>(p, L, smem, att_sh);
   if (!grid_barrier(p, 3, flag)) return raise_model_fault(p);
   phase_wo<AF>(p, smem);
   if (!grid_barrier(p, 4, flag)) return raise_model_fault(p);

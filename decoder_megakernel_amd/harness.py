@@ -25,7 +25,7 @@ def config_of(s: LayerShape):
                        s.kv_fmt, has_router_bias=1 if s.routing == "skew" else 0, rms_eps=s.eps,
                        rope_base=s.rope_base, q_lora_rank=s.q_lora, kv_norm=1 if s.kv_norm else 0,
                        idx_heads=s.idx_heads, idx_dim=s.idx_dim, idx_topk=s.idx_topk,
-                       idx_max_rows=(s.capacity + 7) // 8 * 8 if s.idx_topk else 0)
+                       idx_max_rows=(s.capacity + 7) // 8 * 8 if s.idx_topk else 0, kv_max_rows=s.capacity)
 
 
 def _dev(device):

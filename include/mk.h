@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define MK_ABI_VERSION 3
+#define MK_ABI_VERSION 4
 #define MK_MAX_T 8           /* verify rows per step: k drafts + 1, at most 8 */
 #define MK_STATIC_SCRATCH_BYTES (32u << 20)   /* scratch of mk_decode_step_static, per GPU */
 
@@ -133,6 +133,12 @@ typedef struct mk_layer_config {
   int32_t idx_topk;
   int32_t idx_max_rows;      /* sparse: the largest L + T a step may use, a multiple of 8 (sizes
                                 the workspace's index scores); a step past it is refused */
+  int32_t kv_max_rows;       /* the largest L + T the caller expects (0: not stated).  With the bf16
+                                cache and the 512 + 64 latent shape (dense attention), 16,384 or more
+                                sizes the workspace for the four-tile attention units that long
+                                contexts use ("Why one GB300 doesn't beat 4x RTX PRO 6000 at
+                                single-stream decode", section "The decomposition": step time
+                                against context); steps of any length stay allowed */
 } mk_layer_config;
 
 typedef struct mk_device_info {

@@ -27,7 +27,7 @@ def test_library_exports_every_header_function():
 
 def test_abi_version():
     import decoder_megakernel_amd as mk
-    assert mk.abi_version() == mk.MK_ABI_VERSION == 3
+    assert mk.abi_version() == mk.MK_ABI_VERSION == 4
 
 
 def _cfg(**kw):
@@ -77,6 +77,7 @@ def test_valid_configs_pass_and_sizes():
     (dict(idx_topk=2048, idx_heads=64, idx_dim=128, idx_max_rows=70001), -1),
     (dict(idx_topk=2048, idx_heads=64, idx_dim=128, idx_max_rows=70000, kv_format="fp8row"), -8),
     (dict(idx_topk=2048, idx_heads=32, idx_dim=160, idx_max_rows=70000), -8),
+    (dict(kv_max_rows=-1), -1),
 ])
 def test_invalid_configs_are_refused(kw, code):
     import decoder_megakernel_amd as mk
