@@ -172,7 +172,7 @@ def kv_cache(s: LayerShape, seed: int = 0, layer: int = 0, device: int = 0, capa
         rb = recipe.kv_row_bytes(s)
         kv = torch.zeros((cap, rb), dtype=torch.uint8, device=_dev(device))
         if s.L:
-            synth.dev_fp8row_kv(kv.data_ptr(), s.L, s.kvw, rb, seed, st, synth.stream_id("kv_scale", layer),
+            synth.dev_fp8row_kv(kv.data_ptr(), s.L, s.kv_row, rb, seed, st, synth.stream_id("kv_scale", layer),
                                 recipe.ACT_SIGMA)
         return kv
     if s.kv_fmt == "f32":

@@ -268,8 +268,7 @@ static int check_cfg(const orc_cfg* c, int T) {
   return 0;
 }
 static int check_lowrank(const orc_cfg* c, const orc_weights* w) {
-  if (c->idx_topk < 0 || (c->idx_topk > 0 && (c->idx_heads <= 0 || c->idx_dim <= 0 || !w->widx ||
-                                               c->kv_fmt == ORC_FP8ROW)))
+  if (c->idx_topk < 0 || (c->idx_topk > 0 && (c->idx_heads <= 0 || c->idx_dim <= 0 || !w->widx)))
     return -1;
   if (c->q_lora > 0 && (!w->wdq || !w->wuq || !w->gamma_q)) return -1;
   if (c->kv_norm && !w->gamma_kv) return -1;

@@ -96,7 +96,8 @@ typedef struct orc_cfg {
   int kv_norm;    /* 1: RMSNorm with gain gamma_kv on the latent c before it is cached */
   int idx_heads;  /* sparse attention (idx_topk > 0): indexer heads H_I, index key dim d_I,   */
   int idx_dim;    /*   keys kept per query row k; each cache row then holds its index key    */
-  int idx_topk;   /*   after the latent and the RoPE key (d_c + d_r + d_I values)            */
+  int idx_topk;   /*   after the latent and the RoPE key (d_c + d_r + d_I values; an fp8     */
+                  /*   row holds them as d_c + d_r + d_I codes under the row's one scale)   */
 } orc_cfg;
 
 /* Canonical (row-major) weights.  Expert slot e in [0, E) is routed expert e,
@@ -169,8 +170,9 @@ typedef struct orc_moe_taps {
   float* y_shared; /* [T][d]        sum of shared-expert outputs     */
 } orc_moe_taps;
 
-/* KV cache rows.  ORC_F32 / ORC_BF16: d_c+d_r elements.  ORC_FP8ROW: the row's
- * d_c+d_r E4M3 codes (orc_f32_to_e4m3 of value / scale), then its scale as an
+/* KV cache rows of kvw values (d_c+d_r, plus d_I with sparse attention).
+ * ORC_F32 / ORC_BF16: kvw elements.  ORC_FP8ROW: the row's kvw E4M3 codes
+ * (orc_f32_to_e4m3 of value / scale), then its scale as an
  * fp32 (orc_fp8_row_scale, a power of two), zero bytes up to a multiple of 16;
  * element value = E4M3(code) * scale, exact in fp32.  Bytes per row (-1 for an
  * unknown format): */

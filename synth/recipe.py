@@ -124,8 +124,9 @@ def hidden_host(s: LayerShape, seed: int = 0, layer: int = 0, step: int = 0) -> 
 
 
 def kv_row_bytes(s: LayerShape) -> int:
-    """Bytes of one cache row: kvw elements (fp32 / bf16), or for fp8 rows kvw
-    E4M3 codes and an fp32 scale, padded to a multiple of 16 bytes."""
+    """Bytes of one cache row of kv_row values (kvw, plus idx_dim with sparse
+    attention): fp32 / bf16 elements, or for fp8 rows kv_row E4M3 codes and one
+    fp32 scale, padded to a multiple of 16 bytes."""
     if s.kv_fmt == "f32":
         return 4 * s.kv_row
     if s.kv_fmt == "bf16":
@@ -139,7 +140,7 @@ def kv_prefill_host(s: LayerShape, seed: int = 0, layer: int = 0) -> np.ndarray:
     cap = s.capacity
     if s.kv_fmt == "fp8row":
         kv = np.zeros((cap, kv_row_bytes(s)), dtype=np.uint8)
-        kv[: s.L] = fp8row_kv(s.L, s.kvw, kv_row_bytes(s), seed, stream_id("kv_prefill", layer),
+        kv[: s.L] = fp8row_kv(s.L, s.kv_row, kv_row_bytes(s), seed, stream_id("kv_prefill", layer),
                               stream_id("kv_scale", layer), ACT_SIGMA)
         return kv
     if s.kv_fmt == "f32":

@@ -108,7 +108,7 @@ def gpu_step(dl, s, H_dev, kv_dev, L, T=None):
             taps[name] = buf
     kvn = kv_dev[L:L + T].cpu().numpy()
     taps["kv_raw"] = kvn
-    return out.cpu().numpy(), kv_to_f32(kvn, s.kv_fmt, s.kvw), taps
+    return out.cpu().numpy(), kv_to_f32(kvn, s.kv_fmt, s.kv_row), taps
 
 
 def oracle_step(s, seed, layer, H, L, kv_host=None, force_sel=None, full_weights=None, base_weights=None,
@@ -130,7 +130,7 @@ def oracle_step(s, seed, layer, H, L, kv_host=None, force_sel=None, full_weights
         out, taps, w = oracle.layer_step_lazy(s, seed, layer, H, kv, L, base_weights=base_weights,
                                               force_sel=force_sel, expert_fn=expert_fn)
     taps["kv_raw"] = kv[L:L + H.shape[0]].copy()
-    return out, kv_to_f32(kv[L:L + H.shape[0]], s.kv_fmt, s.kvw), taps, w
+    return out, kv_to_f32(kv[L:L + H.shape[0]], s.kv_fmt, s.kv_row), taps, w
 
 
 def compare_selection(s, gpu_sel, ora_logits, ora_sel):
@@ -218,7 +218,7 @@ def check_layer(s, seed, layer, g_out, g_kv, g_taps, H, L, kv_host=None, full_we
     if s.kv_fmt == "fp8row":
         # rows are compared code by code (fp8row_kv_check) where the GPU's raw rows are at hand
         if "kv_raw" in g_taps:
-            errs["kv_new_same_codes"] = fp8row_kv_check(g_taps["kv_raw"], o_taps["kv_raw"], s.kvw)
+            errs["kv_new_same_codes"] = fp8row_kv_check(g_taps["kv_raw"], o_taps["kv_raw"], s.kv_row)
         checked = ("attn_branch", "moe_branch", "out")
     else:
         checked = ("attn_branch", "moe_branch", "out", "kv_new")

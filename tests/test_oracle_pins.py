@@ -635,60 +635,91 @@ def test_fp8_row_layout_and_decode_against_the_table():
     assert np.array_equal(oracle.kv_decode(buf, "fp8row", kvw, 5).astype(np.float64), want)
 
 
-def test_fp8_prefill_rows_decode_to_the_drawn_values():
+# With sparse attention an fp8 row holds the latent, the RoPE key and the index
+# key as one run of kvw + idx_dim codes under the row's one scale (reading: the
+# pages give one fp8 cache and no separate index-key format).
+C0KS = C0K.with_(name="micro_fp8kv_sparse", idx_heads=4, idx_dim=32, idx_topk=5, L=12)
+
+
+@pytest.mark.parametrize("shape", [C0K, C0KS], ids=lambda s: s.name)
+def test_fp8_prefill_rows_decode_to_the_drawn_values(shape):
     """The generator's fp8 rows against the same N(0,1) draws the bf16 cache holds:
     each element within half an E4M3 step (at the row's scale) of its draw."""
-    s = C0K.with_(L=40)
+    s = shape.with_(L=40)
+    rw = s.kv_row
     kv = recipe.kv_prefill_host(s, seed=2)
-    draws = synth.normal_f32((s.L, s.kvw), 2, synth.stream_id("kv_prefill", 0), recipe.ACT_SIGMA).astype(np.float64)
-    dec = oracle.kv_decode(kv, "fp8row", s.kvw, s.L).astype(np.float64)
-    sc = kv[: s.L, s.kvw:s.kvw + 4].copy().view(np.float32).astype(np.float64)
+    draws = synth.normal_f32((s.L, rw), 2, synth.stream_id("kv_prefill", 0), recipe.ACT_SIGMA).astype(np.float64)
+    dec = oracle.kv_decode(kv, "fp8row", rw, s.L).astype(np.float64)
+    sc = kv[: s.L, rw:rw + 4].copy().view(np.float32).astype(np.float64)
     a = np.abs(draws) / sc
     step = np.where(a < 2.0 ** -6, 2.0 ** -9, 2.0 ** (np.floor(np.log2(np.maximum(a, 2.0 ** -6))) - 3))
     assert np.all(np.abs(dec - draws) <= step * sc / 2 + 1e-12)
     assert set(np.log2(sc[:, 0]).astype(int)) <= {-6, -5, -4}
-    assert np.all(kv[s.L:] == 0) and np.all(kv[: s.L, s.kvw + 4:] == 0)
+    assert np.all(kv[s.L:] == 0) and np.all(kv[: s.L, rw + 4:] == 0)
 
 
-def test_fp8_cache_new_rows_are_the_f32_rows_quantised_per_row():
+@pytest.mark.parametrize("shape", [C0K, C0KS], ids=lambda s: s.name)
+def test_fp8_cache_new_rows_are_the_f32_rows_quantised_per_row(shape):
     """Same layer with an f32 cache holding the decoded fp8 prefill: the new rows
     (which depend on H only) must come back as the f32 rows quantised by the
     row rule (scale and codes checked against the table by brute force), and
-    the attention branch may differ only by that quantisation."""
-    s8 = C0K
+    the attention branch may differ only by that quantisation.  With sparse
+    attention the index key shares the row's scale and the kept rows are those
+    of the f32 layer wherever its scores are not within the quantisation of a tie."""
+    s8 = shape
+    rw = s8.kv_row
     w, H, kv8 = fresh(s8)
     s32 = s8.with_(kv_fmt="f32")
-    kv32 = np.zeros((s32.capacity, s32.kvw), np.float32)
-    kv32[: s8.L] = oracle.kv_decode(kv8, "fp8row", s8.kvw, s8.L)
+    kv32 = np.zeros((s32.capacity, rw), np.float32)
+    kv32[: s8.L] = oracle.kv_decode(kv8, "fp8row", rw, s8.L)
     out8, t8 = oracle.layer_step(s8, w, H, kv8, s8.L)
     out32, t32 = oracle.layer_step(s32, w, H, kv32, s8.L)
     table = _ocp_e4m3_table()
     x = kv32[s8.L:s8.L + s8.T].astype(np.float64)
     for i in range(s8.T):
         row = kv8[s8.L + i]
-        sc = float(row[s8.kvw:s8.kvw + 4].copy().view(np.float32)[0])
+        sc = float(row[rw:rw + 4].copy().view(np.float32)[0])
         amax = np.abs(x[i]).max()
         assert math.frexp(sc)[0] == 0.5 and 448 * sc / 2 < amax <= 448 * sc
-        for m in range(s8.kvw):
+        for m in range(rw):
             assert row[m] == _nearest_e4m3_bruteforce(np.float32(x[i, m] / sc), table), (i, m)
-        assert np.all(row[s8.kvw + 4:] == 0)
+        assert np.all(row[rw + 4:] == 0)
+    if s8.idx_topk:
+        for i in range(s8.T):
+            n = s8.L + i + 1
+            a, b = t8["iscore"][i, :n].astype(np.float64), t32["iscore"][i, :n].astype(np.float64)
+            # prefill rows score the same on both sides (same decoded values); the
+            # new rows move by their index keys' quantisation, at most d
+            assert np.array_equal(a[: s8.L], b[: s8.L])
+            d = np.abs(a - b).max()
+            sel8 = set(t8["isel"][i][t8["isel"][i] >= 0].tolist())
+            sel32 = set(t32["isel"][i][t32["isel"][i] >= 0].tolist())
+            # a row only the f32 layer keeps is within 2 d of the fp8 layer's cut
+            for r in sel32 - sel8:
+                assert a[r] >= min(a[list(sel8)]) - 2 * d, (i, r)
+        # the branch compared on the same kept rows
+        w32 = dict(w, force_isel=t8["isel"])
+        kv32[s8.L:] = 0
+        out32, t32 = oracle.layer_step(s32, w32, H, kv32, s8.L)
     # attention over mostly shared rows: the branch moves by the quantisation of the new rows only
     e = normwise(t8["Hp"].astype(np.float64) - H, t32["Hp"].astype(np.float64) - H)
     assert 0 < e < 5e-2, e
 
 
-def test_fp8_cache_layer_matches_fp64_unabsorbed_bruteforce():
-    s = C0K
+@pytest.mark.parametrize("shape", [C0K, C0KS], ids=lambda s: s.name)
+def test_fp8_cache_layer_matches_fp64_unabsorbed_bruteforce(shape):
+    s = shape
+    rw = s.kv_row
     w, H, kv = fresh(s)
     kv64 = kv.copy()
     out, taps = oracle.layer_step(s, w, H, kv, s.L)
     ref = oracle.layer_step_f64(s, w, H, kv64, s.L, force_sel=taps["sel"])
     assert normwise(out, ref["out"]) < 1e-5
     assert normwise(taps["Hp"].astype(np.float64) - H, ref["Hp"] - H) < 1e-4
-    # new rows: the fp32 and fp64 rows may round to neighbouring codes; the rows are
-    # otherwise equal after decoding
-    kvn = oracle.kv_decode(kv[s.L:s.L + s.T], "fp8row", s.kvw, s.T).astype(np.float64)
-    sc = kv[s.L:s.L + s.T, s.kvw:s.kvw + 4].copy().view(np.float32).astype(np.float64)
+    # new rows (the latent and RoPE key the fp64 path returns): the fp32 and fp64
+    # rows may round to neighbouring codes; the rows are otherwise equal after decoding
+    kvn = oracle.kv_decode(kv[s.L:s.L + s.T], "fp8row", rw, s.T).astype(np.float64)[:, : s.kvw]
+    sc = kv[s.L:s.L + s.T, rw:rw + 4].copy().view(np.float32).astype(np.float64)
     assert np.all(np.abs(kvn - ref["kv_new"]) <= 32 * sc)
     assert np.mean(kvn == ref["kv_new"]) > 0.99
 
@@ -904,11 +935,13 @@ def test_sparse_with_topk_covering_every_row_is_the_dense_layer_bitwise():
         assert list(taps["isel"][i][: s.L + i + 1]) == list(range(s.L + i + 1))
 
 
-def _decode(a, fmt):
+def _decode(a, fmt, rw=None):
+    if fmt == "fp8row":
+        return oracle.kv_decode(a, fmt, rw, a.shape[0]).astype(np.float64)
     return oracle.bf16_to_f32(a).astype(np.float64) if fmt == "bf16" else a.astype(np.float64)
 
 
-@pytest.mark.parametrize("shape", [C0S, C0QS], ids=lambda s: s.name)
+@pytest.mark.parametrize("shape", [C0S, C0QS, C0KS], ids=lambda s: s.name)
 def test_sparse_selection_is_the_topk_of_independently_computed_index_scores(shape):
     s = shape
     w, H, kv = fresh(s)
@@ -916,10 +949,17 @@ def test_sparse_selection_is_the_topk_of_independently_computed_index_scores(sha
     HI, dI, k = s.idx_heads, s.idx_dim, s.idx_topk
     W = _decode(w["widx"], s.attn_fmt)
     x = taps["x"].astype(np.float64)
-    rows = _decode(kv, s.kv_fmt)[: s.L + s.T]
+    rows = _decode(kv, s.kv_fmt, s.kv_row)[: s.L + s.T]
     kI = rows[:, s.kvw:]
-    # the new rows carry W_IK x as their index key (stored at the cache's precision)
-    tol_k = 1e-5 if s.kv_fmt == "f32" else 2 ** -8
+    # the new rows carry W_IK x as their index key (stored at the cache's
+    # precision; an fp8 row's index key is rounded at the row's scale, which its
+    # latent may set, so the bound is an E4M3 half step at the row maximum)
+    tol_k = {"f32": 1e-5, "bf16": 2 ** -8}.get(s.kv_fmt)
+    if tol_k is None:
+        amax = np.abs(rows[s.L:]).max(axis=1, keepdims=True)
+        err = np.abs(kI[s.L:] - x @ W[HI * dI + HI:].T)
+        assert np.all(err <= amax * 2.0 ** -4), float((err / amax).max())
+        tol_k = np.inf
     assert normwise(kI[s.L:], x @ W[HI * dI + HI:].T) < tol_k
     for i in range(s.T):
         pos = s.L + i
@@ -936,7 +976,7 @@ def test_sparse_selection_is_the_topk_of_independently_computed_index_scores(sha
             assert sc[sel].min() >= sc[out_rows].max() - 1e-5 * np.abs(sc).max()
 
 
-@pytest.mark.parametrize("shape", [C0S, C0QS], ids=lambda s: s.name)
+@pytest.mark.parametrize("shape", [C0S, C0QS, C0KS], ids=lambda s: s.name)
 def test_sparse_layer_matches_fp64_unabsorbed_bruteforce(shape):
     s = shape
     w, H, kv = fresh(s)
