@@ -83,7 +83,10 @@ def layer_bytes(s, L, slots, kept_rows=None):
     if s.idx_topk and kept_rows is None:
         raise ValueError("sparse attention: the kept-row count is needed")
     if s.idx_topk:
-        kv = (L + s.T) * 2 * s.idx_dim + kept_rows * 2 * s.kvw + s.T * rb
+        # per row read: its index key, and for a kept row its latent and RoPE key
+        # (fp8 rows: the codes, and the row's scale with each)
+        ib, kb = (s.idx_dim + 4, s.kvw + 4) if s.kv_fmt == "fp8row" else (2 * s.idx_dim, 2 * s.kvw)
+        kv = (L + s.T) * ib + kept_rows * kb + s.T * rb
     else:
         kv = (L + s.T) * rb + s.T * rb
     act = 2 * s.T * s.d * 4 + 2 * s.d * 4
@@ -93,7 +96,8 @@ def layer_bytes(s, L, slots, kept_rows=None):
 # The sources that make up the layer kernel and its launch configuration
 # (the head, pack and embedding units do not change it).
 LAYER_SOURCES = ("mk_common.h", "mk_device.h", "mk_layer_kernel.h", "mk_layer.hip", "mk_layer_kv8.hip",
-                 "mk_layer_lr.hip", "mk_layer_lr_spec.hip", "mk_layer_sparse.hip", "mk_api.cpp")
+                 "mk_layer_lr.hip", "mk_layer_lr_spec.hip", "mk_layer_sparse.hip", "mk_layer_sparse_kv8.hip",
+                 "mk_api.cpp")
 
 
 def kernel_source_hash():
@@ -480,11 +484,12 @@ def process_starts(args, n):
 
 
 def main():
+    from synth.configs import BY_KEY
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--workload", default="C5", choices=["C2", "C3", "C4", "C5", "C3X", "C5X", "C3XK", "C5XK", "C3Q", "C4S"])
+    ap.add_argument("--workload", default="C5", choices=[k for k in BY_KEY if k not in ("C0", "C1")])
     ap.add_argument("--layers", type=int, default=None, help="stack depth override (diagnostics only)")
     ap.add_argument("--head-fmt", default="bf16", choices=["bf16", "fp8"],
                     help="LM-head table format (the stack workload names bf16)")
@@ -501,10 +506,9 @@ def main():
                          "known-size kernel for scaling hardware byte counters in a profile)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (the layer's sharding is "
-              "described in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path; run with --gpus 1",
+              file=sys.stderr)
         sys.exit(2)
-    from synth.configs import BY_KEY
     s = BY_KEY[args.workload].with_(head_fmt=args.head_fmt)
     if s.n_layers > 1:
         args.steps = args.steps or 256

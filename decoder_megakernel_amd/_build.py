@@ -7,7 +7,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmk.so")
 SOURCES = ["mk_api.cpp", "mk_layer.hip", "mk_layer_kv8.hip", "mk_layer_lr.hip", "mk_layer_lr_spec.hip", "mk_layer_sparse.hip",
-           "mk_pack.hip",
+           "mk_layer_sparse_kv8.hip", "mk_pack.hip",
            "mk_stack.hip"]
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -94,8 +94,8 @@ int check_cfg(const mk_layer_config* c) {
   if (D.kvmax < 0) return fail(MK_ERR_INVALID_ARG, "kv_max_rows must be >= 0");
   if (D.ik < 0) return fail(MK_ERR_INVALID_ARG, "idx_topk must be >= 0");
   if (D.ik > 0) {
-    if (D.af != MK_FMT_BF16 || D.kf != MK_FMT_BF16)
-      return fail(MK_ERR_UNSUPPORTED_SHAPE, "sparse attention needs bf16 attention and a bf16 cache");
+    if (D.af != MK_FMT_BF16 || (D.kf != MK_FMT_BF16 && D.kf != MK_FMT_FP8_ROW))
+      return fail(MK_ERR_UNSUPPORTED_SHAPE, "sparse attention needs bf16 attention and a bf16 or fp8 cache");
     if (D.nh % 16 || D.ih <= 0 || D.ih % 16 || D.idm <= 0 || D.idm % 32 || D.ih * D.idm > 8192 || D.ik > 8192)
       return fail(MK_ERR_UNSUPPORTED_SHAPE, "sparse attention: n_heads and idx_heads multiples of 16, idx_dim a "
                                             "multiple of 32, idx_heads * idx_dim <= 8192, idx_topk <= 8192");

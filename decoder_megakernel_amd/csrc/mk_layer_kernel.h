@@ -441,14 +441,15 @@ __device__ __forceinline__ void phase_rope_kv(const LayerParams& p, int L, int t
   auto qval = [&](int t, int idx) { return LR ? ldg(p.qbuf + (long long)t * p.nq + idx) : psum(t, idx); };
   if constexpr (KF == MK_FMT_FP8_ROW || LR) {
     // One wave per new cache row (the thread range is whole waves): each lane
-    // forms runs of 8 consecutive values (latent, or 4 rotated key pairs).
+    // forms runs of 8 consecutive values (latent, 4 rotated key pairs, or with
+    // sparse attention the index key, whose runs follow the RoPE key's).
     // With the latent norm the wave first takes the latent's mean square and
     // scales it by 1/rms and the gain.  fp8 rows: the wave takes the row
     // maximum, the row's scale is the smallest power of two 2^e with
     // max <= 448 * 2^e, and each value is stored as E4M3(v / 2^e); fp32 / bf16
     // rows store the values.
     const int lane = tid & 63, wv = tid >> 6, nwv = nthreads >> 6;
-    const int rb = kv_row_bytes(KF, p.kv_row), nrun = p.kvw / 8;
+    const int rb = kv_row_bytes(KF, p.kv_row), nrun = p.kvw / 8, nall = p.kv_row / 8;
     for (int t = wv; t < T; t += nwv) {
       const long long pos = (long long)L + t;
       // the key's RoPE pairs: lane j < d_r / 2 forms pair j's cos and sin, and the
@@ -473,10 +474,11 @@ __device__ __forceinline__ void phase_rope_kv(const LayerParams& p, int L, int t
         const int c = lane + 64 * i, m0 = 8 * c;
 #pragma unroll
         for (int k = 0; k < 8; ++k) v[i][k] = 0.f;
-        if (c < nrun) {
+        if (c < nall) {
           f32x4 a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
+          const int off = c < nrun ? kvoff + m0 : kioff + (m0 - p.kvw);
           for (int s = 0; s < S; ++s) {
-            const float* src = part + ((long long)s * T + t) * nrow + kvoff + m0;
+            const float* src = part + ((long long)s * T + t) * nrow + off;
             a += ldg(reinterpret_cast<const f32x4*>(src));
             b += ldg(reinterpret_cast<const f32x4*>(src + 4));
           }
@@ -485,7 +487,7 @@ __device__ __forceinline__ void phase_rope_kv(const LayerParams& p, int L, int t
             v[i][k] = a[k];
             v[i][k + 4] = b[k];
           }
-          if (m0 >= p.dc) {
+          if (m0 >= p.dc && c < nrun) {
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
               const float cs = pcs[i][k], sn = psn[i][k];
@@ -525,7 +527,7 @@ __device__ __forceinline__ void phase_rope_kv(const LayerParams& p, int L, int t
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
           const int c = lane + 64 * i;
-          if (c < nrun) {
+          if (c < nall) {
             if constexpr (KF == MK_FMT_F32) {
               float* dst = reinterpret_cast<float*>(p.kv) + pos * p.kv_row + 8 * c;
               *reinterpret_cast<f32x4*>(dst) = f32x4{v[i][0], v[i][1], v[i][2], v[i][3]};
@@ -536,13 +538,6 @@ __device__ __forceinline__ void phase_rope_kv(const LayerParams& p, int L, int t
               for (int k = 0; k < 8; ++k) o[k] = (__bf16)v[i][k];
               *reinterpret_cast<bf16x8*>(reinterpret_cast<__bf16*>(p.kv) + pos * p.kv_row + 8 * c) = o;
             }
-          }
-        }
-        if constexpr (SP) {
-          for (int m = lane; m < p.idim; m += 64) {
-            const float v = psum(t, kioff + m);
-            if constexpr (KF == MK_FMT_F32) reinterpret_cast<float*>(p.kv)[pos * p.kv_row + p.kvw + m] = v;
-            else reinterpret_cast<__bf16*>(p.kv)[pos * p.kv_row + p.kvw + m] = (__bf16)v;
           }
         }
         continue;
@@ -564,7 +559,7 @@ __device__ __forceinline__ void phase_rope_kv(const LayerParams& p, int L, int t
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int c = lane + 64 * i;
-        if (c < nrun) {
+        if (c < nall) {
           uint32_t w0 = 0, w1 = 0;
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
@@ -574,9 +569,9 @@ __device__ __forceinline__ void phase_rope_kv(const LayerParams& p, int L, int t
           *reinterpret_cast<u32x2*>(row + 8 * c) = u32x2{w0, w1};
         }
       }
-      // the scale and the zero padding: the 16 bytes after the codes (kvw is a multiple of 16)
+      // the scale and the zero padding: the 16 bytes after the codes (kv_row is a multiple of 16)
       if (lane == 0)
-        *reinterpret_cast<u32x4*>(row + p.kvw) = u32x4{(uint32_t)(127 + e) << 23, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4*>(row + p.kv_row) = u32x4{(uint32_t)(127 + e) << 23, 0u, 0u, 0u};
     }
     // the queries' RoPE pairs, one per thread
     const int per_q = p.nh * dr2;
@@ -743,7 +738,8 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 }
 // Index scores: the cache rows [0, L + T) are cut into chunks of 16 spread over
 // the grid; a workgroup stages up to kIdxBlk of its chunks' index keys in LDS
-// (bf16, row stride idx_dim + 8).  Wave w scores verify row t = w / (8 / T)
+// (bf16, row stride idx_dim + 8; F8: fp8 rows, whose index-key codes are widened
+// with the row's scale, exactly).  Wave w scores verify row t = w / (8 / T)
 // against every (8 / T)-th staged chunk, with that row's index queries held in
 // registers: S[head][key] = q^I_head . k^I_key on the matrix cores (16 heads x
 // 16 keys per product, idim / 32 k-steps), then the sum over heads of
@@ -752,7 +748,7 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 constexpr int kIdxBlk = 32;                       // chunks of 16 keys staged at a time
 static_assert(kIdxBlk * 16 * (128 + 8) * 2 + kMaxT * 256 * 4 <= kLdsBytes - 1024,
               "index keys (idx_dim <= 128) and head weights (idx_heads <= 256) fit the LDS");
-template <int NKB>                                // idx_dim / 32
+template <int NKB, bool F8>                       // idx_dim / 32, fp8 cache rows
 __device__ __forceinline__ void iscore_rows(const LayerParams& p, int L, char* smem) {
   constexpr int kMaxHt = 16 / NKB;                // idx_heads * idx_dim <= 8192: 16 query fragments per lane
   const int T = p.T, HI = p.ihead, nht = HI / 16, dI = NKB * 32, KS = dI + 8;
@@ -777,10 +773,36 @@ __device__ __forceinline__ void iscore_rows(const LayerParams& p, int L, char* s
   int c0, c1;
   split_range(nch, gridDim.x, blockIdx.x, c0, c1);
   const __bf16* kvb = reinterpret_cast<const __bf16*>(p.kv) + p.kvw;
+  const uint8_t* kv8 = reinterpret_cast<const uint8_t*>(p.kv);
+  const long long rb8 = kv_row_bytes(MK_FMT_FP8_ROW, p.kv_row);
   for (int cb = c0; cb < c1; cb += kIdxBlk) {
     const int nb = min(kIdxBlk, c1 - cb), tot = nb * 16 * np;
     constexpr int kB = 8;                         // 16-byte loads in flight per thread
     __syncthreads();                              // the previous block's keys are no longer read
+    if constexpr (F8) {
+      // 16 codes (16 bytes) and the row's scale per piece -> 16 bf16
+      const int np16 = np / 2, tot16 = tot / 2;
+      for (int i0 = threadIdx.x; i0 < tot16; i0 += kB * kThreads) {
+        u32x4 v[kB];
+        float sc[kB];
+#pragma unroll
+        for (int q = 0; q < kB; ++q) {
+          const int i = min(i0 + q * kThreads, tot16 - 1), k = i / np16;
+          const uint8_t* row = kv8 + (long long)min(cb * 16 + k, Lt - 1) * rb8;
+          v[q] = ldg(reinterpret_cast<const u32x4*>(row + p.kvw + (i - k * np16) * 16));
+          sc[q] = ldg(reinterpret_cast<const float*>(row + p.kv_row));
+        }
+#pragma unroll
+        for (int q = 0; q < kB; ++q) {
+          const int i = i0 + q * kThreads, k = i / np16;
+          if (i < tot16) {
+            __bf16* dst = ks + k * KS + (i - k * np16) * 16;
+            *reinterpret_cast<u32x4*>(dst) = fp8x8_scaled_bf16(v[q][0], v[q][1], sc[q]);
+            *reinterpret_cast<u32x4*>(dst + 8) = fp8x8_scaled_bf16(v[q][2], v[q][3], sc[q]);
+          }
+        }
+      }
+    } else
     for (int i0 = threadIdx.x; i0 < tot; i0 += kB * kThreads) {
       u32x4 v[kB];
 #pragma unroll
@@ -822,12 +844,13 @@ __device__ __forceinline__ void iscore_rows(const LayerParams& p, int L, char* s
     }
   }
 }
+template <bool F8>
 __device__ __forceinline__ void phase_iscore(const LayerParams& p, int L, char* smem) {
   switch (p.idim / 32) {
-    case 1: iscore_rows<1>(p, L, smem); break;
-    case 2: iscore_rows<2>(p, L, smem); break;
-    case 3: iscore_rows<3>(p, L, smem); break;
-    default: iscore_rows<4>(p, L, smem); break;
+    case 1: iscore_rows<1, F8>(p, L, smem); break;
+    case 2: iscore_rows<2, F8>(p, L, smem); break;
+    case 3: iscore_rows<3, F8>(p, L, smem); break;
+    default: iscore_rows<4, F8>(p, L, smem); break;
   }
 }
 
@@ -1399,7 +1422,7 @@ __device__ __forceinline__ void phase_attention(const LayerParams& p, int L, cha
 #pragma unroll
         for (int i = 0; i < KHMAX; ++i)
           if (EXACT || i < nk) kr[i] = ldg(reinterpret_cast<const u32x2*>(row + kblk(i) * KBW + g * 8));
-        ks = ldg(reinterpret_cast<const float*>(row + kvw));
+        ks = ldg(reinterpret_cast<const float*>(row + (SP ? p.kv_row : kvw)));   // after all codes
       } else {
         const E* er = reinterpret_cast<const E*>(row) + g * (KBW / 4);
 #pragma unroll
@@ -2892,7 +2915,7 @@ __global__ __launch_bounds__(kThreads, 1) void layer_kernel(LayerParams p) {
   }
   if (!grid_barrier(p, 1, flag)) return raise_model_fault(p);
   if constexpr (SP) {
-    phase_iscore(p, L, smem);
+    phase_iscore<KF == MK_FMT_FP8_ROW>(p, L, smem);
     if (!grid_barrier(p, 9, flag)) return raise_model_fault(p);
     phase_topk(p, L, smem);
     if (!grid_barrier(p, 10, flag)) return raise_model_fault(p);

@@ -7,8 +7,12 @@
 
 namespace mk {
 
+LayerKernelFn layer_kernel_sparse_kv8_for(int ef, bool lowrank, bool spec);
+
 LayerKernelFn layer_kernel_sparse_for(int af, int ef, int kf, bool lowrank, bool spec) {
-  if (af != MK_FMT_BF16 || kf != MK_FMT_BF16) return nullptr;
+  if (af != MK_FMT_BF16) return nullptr;
+  if (kf == MK_FMT_FP8_ROW) return layer_kernel_sparse_kv8_for(ef, lowrank, spec);   // mk_layer_sparse_kv8.hip
+  if (kf != MK_FMT_BF16) return nullptr;
   constexpr int A = MK_FMT_BF16, K = MK_FMT_BF16;
   if (spec && ef == MK_FMT_FP8_B128)
     return lowrank ? layer_kernel<A, MK_FMT_FP8_B128, K, 18, 32, true, 2, true, true>

@@ -67,7 +67,8 @@ typedef enum mk_status {
  * of a row (value = E2M1(code) * 2^(scale - 127)); the expert format the pages'
  * serving stack uses ("DeepSeek-V4.1-Flash breaks 1,000 tokens per second for
  * one user", section "Appendix: method").
- * FP8_ROW (KV cache only): per cache row, its d_latent + d_rope E4M3 codes, then
+ * FP8_ROW (KV cache only): per cache row, its d_latent + d_rope E4M3 codes (with
+ * sparse attention also its idx_dim index-key codes, under the same scale), then
  * the row's scale as an fp32, then zero bytes up to a multiple of 16
  * (value = E4M3(code) * scale).  The same page names an fp8 E4M3 KV cache for
  * that stack without a scale layout; the scale written by a step is the
@@ -126,7 +127,7 @@ typedef struct mk_layer_config {
    * output), cached after the RoPE key (a cache row holds d_latent + d_rope + idx_dim values);
    * score of cache row s <= L + t: sum_j w^I_j max(0, q^I_j . k^I_s); the row attends to its
    * idx_topk highest-scoring rows (ties to the lower row; every row when L + t + 1 <= idx_topk).
-   * Needs bf16 attention and cache, n_heads a multiple of 16, idx_heads a multiple of 16,
+   * Needs bf16 attention, a bf16 or FP8_ROW cache, n_heads a multiple of 16, idx_heads a multiple of 16,
    * idx_dim a multiple of 32 and <= 128, idx_heads * idx_dim <= 8192, idx_topk <= 8192. */
   int32_t idx_heads;
   int32_t idx_dim;
@@ -186,8 +187,9 @@ typedef struct mk_layer_weights {
 } mk_layer_weights;
 
 /* KV cache of one layer: `capacity` rows in kv_format (mk_kv_bytes gives the
- * size; an FP8_ROW row takes d_latent + d_rope + 4 bytes rounded up to 16), row
- * j = latent c_j followed by its RoPE-rotated key.  A step reads rows
+ * size; an FP8_ROW row takes its values' count + 4 bytes rounded up to 16), row
+ * j = latent c_j followed by its RoPE-rotated key (and with sparse attention its
+ * index key).  A step reads rows
  * [0, length) plus its own new rows and writes rows [length, length+T); it does
  * not change `length` (the caller commits accepted rows). */
 typedef struct mk_kv_cache {

@@ -97,9 +97,12 @@ C3Q = C3.with_(name="fp8_lowrankq_E384_T8_L8192", q_lora=1536, kv_norm=True)
 # The long-context layer with sparse attention: an indexer of 64 heads x 128
 # dims, each verify row attends to its top 2048 cache rows.
 C4S = C4.with_(name="fp8_sparse2048_E384_T6_L65536_skew", idx_heads=64, idx_dim=128, idx_topk=2048)
-PRESETS = {s.name: s for s in (C0, C1, C2, C3, C4, C5, C3X, C5X, C3XK, C5XK, C3Q, C4S)}
+# The same in the serving formats: MXFP4 experts and the fp8 cache, whose rows
+# then carry the index key under the row's scale.
+C4SXK = C4S.with_(name="mxfp4_fp8kv_sparse2048_E384_T6_L65536_skew", exp_fmt="mxfp4", kv_fmt="fp8row")
+PRESETS = {s.name: s for s in (C0, C1, C2, C3, C4, C5, C3X, C5X, C3XK, C5XK, C3Q, C4S, C4SXK)}
 BY_KEY = {"C0": C0, "C1": C1, "C2": C2, "C3": C3, "C4": C4, "C5": C5, "C3X": C3X, "C5X": C5X,
-          "C3XK": C3XK, "C5XK": C5XK, "C3Q": C3Q, "C4S": C4S}
+          "C3XK": C3XK, "C5XK": C5XK, "C3Q": C3Q, "C4S": C4S, "C4SXK": C4SXK}
 
 # Skewed routing: the hot set is the first ceil(0.2 E) experts of a seeded permutation.
 HOT_FRACTION = 0.2

@@ -75,7 +75,7 @@ def test_valid_configs_pass_and_sizes():
     (dict(idx_topk=2048, idx_heads=64, idx_dim=128, idx_max_rows=0), -1),
     (dict(idx_topk=2048, idx_heads=60, idx_dim=128, idx_max_rows=70000), -8),
     (dict(idx_topk=2048, idx_heads=64, idx_dim=128, idx_max_rows=70001), -1),
-    (dict(idx_topk=2048, idx_heads=64, idx_dim=128, idx_max_rows=70000, kv_format="fp8row"), -8),
+    (dict(idx_topk=2048, idx_heads=64, idx_dim=128, idx_max_rows=70000, kv_format="f32"), -8),
     (dict(idx_topk=2048, idx_heads=32, idx_dim=160, idx_max_rows=70000), -8),
     (dict(kv_max_rows=-1), -1),
 ])
@@ -140,3 +140,9 @@ def test_sparse_attention_config_and_sizes():
     mk.check_config(cfg)
     assert mk.packed_bytes(cfg, mk.MK_T_WIDX) == (64 * 128 + 64 + 128) * 4096 * 2
     assert mk.kv_bytes(cfg, 1000) == 1000 * (512 + 64 + 128) * 2
+    # an fp8 row holds the 704 codes, the scale and padding to 16 bytes
+    k8 = _cfg(idx_heads=64, idx_dim=128, idx_topk=2048, idx_max_rows=70000, kv_format="fp8row")
+    mk.check_config(k8)
+    assert mk.kv_bytes(k8, 1000) == 1000 * 720
+    mk.check_config(_cfg(idx_heads=64, idx_dim=128, idx_topk=2048, idx_max_rows=70000, kv_format="fp8row",
+                         expert_format="mxfp4", q_lora_rank=1536, kv_norm=1))

@@ -205,11 +205,19 @@ MID_SP = LayerShape("mid_sparse", d=1024, n_h=16, d_h=64, d_c=128, d_r=32, E=32,
 MID_SP_LR = MID_SP.with_(name="mid_sparse_lowrank", q_lora=256, kv_norm=True)
 MID_SP_MX = MID_SP.with_(name="mid_sparse_mxfp4", exp_fmt="mxfp4")
 MID_SP_ALL = MID_SP.with_(name="mid_sparse_topk_covers_all", idx_topk=512)
+# fp8 cache rows carrying the index key under the row's scale
+MID_SP_K = MID_SP.with_(name="mid_sparse_fp8kv", kv_fmt="fp8row")
+MID_SP_K_LR = MID_SP_LR.with_(name="mid_sparse_fp8kv_lowrank", kv_fmt="fp8row", exp_fmt="mxfp4")
 
 
-@pytest.mark.parametrize("shape", [MID_SP, MID_SP_LR, MID_SP_MX, MID_SP_ALL], ids=lambda s: s.name)
+@pytest.mark.parametrize("shape", [MID_SP, MID_SP_LR, MID_SP_MX, MID_SP_ALL, MID_SP_K, MID_SP_K_LR],
+                         ids=lambda s: s.name)
 def test_sparse_attention_shapes_match_oracle(shape):
     _run(shape)
+
+
+def test_sparse_attention_fp8kv_single_row_empty_cache():
+    _run(MID_SP_K, L=0, T=1)
 
 
 def test_sparse_attention_single_row_empty_cache():
@@ -249,3 +257,8 @@ def test_sparse_attention_all_scores_equal(L):
 def test_full_size_sparse_fp8_E384_T6_L65536_skew():
     from synth.configs import C4S
     _run(C4S, full_weights=False)
+
+
+def test_full_size_sparse_mxfp4_fp8kv_E384_T6_L65536_skew():
+    from synth.configs import C4SXK
+    _run(C4SXK, full_weights=False)

@@ -12,6 +12,7 @@
   built with AddressSanitizer and UndefinedBehaviorSanitizer for the host pass,
   driven through its checks and error paths without a GPU.
 """
+import importlib.util
 import os
 import shutil
 import subprocess
@@ -63,8 +64,11 @@ def test_oracle_and_generator_under_address_and_ub_sanitizers(tmp_path):
 
 @pytest.mark.skipif(not os.path.exists(HIPCC), reason="no hipcc")
 def test_abi_host_code_under_address_and_ub_sanitizers(tmp_path):
-    objs = [os.path.join(CSRC, n) for n in ("mk_layer.o", "mk_layer_kv8.o", "mk_layer_lr.o", "mk_layer_lr_spec.o", "mk_layer_sparse.o", "mk_pack.o",
-                                             "mk_stack.o")]
+    # the device units as the library build leaves them (every source but the host-side API)
+    spec = importlib.util.spec_from_file_location("_mk_build", os.path.join(ROOT, "decoder_megakernel_amd", "_build.py"))
+    bld = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bld)
+    objs = [os.path.join(CSRC, os.path.splitext(n)[0] + ".o") for n in bld.SOURCES if n != "mk_api.cpp"]
     if not all(os.path.exists(o) for o in objs):
         pytest.skip("the library's kernel objects are not built (run __graft_entry__.build())")
     # sanitizers for the host pass only (the kernels are not instrumented)
