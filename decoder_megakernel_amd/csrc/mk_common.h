@@ -142,7 +142,7 @@ struct LayerParams {
   uint32_t* ihist;         // sparse: the top-k's first-digit histogram of each row [kMaxT][2048]
   uint32_t* ictr;          // sparse: the top-k's part counters [kMaxT][kIdxCtrStride]
   uint32_t* icnt;          // sparse: pairs per part [kMaxT][512]
-  uint32_t* icand;         // sparse: (row, top 16 bits) pairs of the parts [kMaxT][idx_max_rows][2]
+  uint32_t* icand;         // sparse: (row, 32-bit key) pairs of the parts [kMaxT][idx_max_rows][2]
   int32_t* isel;           // sparse: kept rows [T][itopk], ascending
   int imax;                // sparse: idx_max_rows
   int att_share;           // long contexts may take the four-tile attention units (partials sized for them)

@@ -866,15 +866,13 @@ __device__ __forceinline__ void phase_iscore(const LayerParams& p, int L, char* 
 //    every part of the row has (a bounded wait on a counter) and reads the sum:
 //    every part finds the same first digit;
 //  - each part writes its rows at or above that digit's bin -- the kept rows
-//    above it and the candidates in it -- as (row, top 16 bits) pairs, in
-//    ascending order from its first row's place, with their count, and counts
-//    itself done;
+//    above it and the candidates in it -- as (row, full 32-bit key) pairs (the
+//    scores read for those rows only), in ascending order from its first row's
+//    place, with their count, and counts itself done;
 //  - the row's first part waits for the others, gathers the pairs into a list
-//    in LDS (ascending rows), takes the next 5 bits from the list, reads the
-//    full keys of the rows that share the threshold's top 16 bits for the last
-//    16 bits (11 + 5), and writes the kept rows in ascending order (each lane's
-//    place found by ballots); of the rows equal to the threshold key the lower
-//    ones are kept.
+//    in LDS (ascending rows), takes the last 21 bits from the list (11 + 10),
+//    and writes the kept rows in ascending order (each lane's place found by
+//    ballots); of the rows equal to the threshold key the lower ones are kept.
 // Pairs, counts and histograms are written and read with device-scope
 // accesses, so no cache on the way holds a stale copy.  When the list would
 // not fit in LDS (many equal or nearly equal scores), the first part alone
@@ -1134,10 +1132,14 @@ __device__ __forceinline__ bool topk_parts(const LayerParams& p, int L, const To
   int* lh = s.hist;                               // one histogram for the workgroup
   for (int i = threadIdx.x; i < kTopkBins / 4; i += kThreads) reinterpret_cast<int4*>(lh)[i] = int4{0, 0, 0, 0};
   __syncthreads();
+  uint32_t u0k[8];                                // the keys of the wave's first tile, kept for the later passes
   for (int tile = w; tile < ntile; tile += kWaves) {
     const int b = kb + tile * 512 + 8 * lane;
     uint32_t u[8];
     keys16(k16, b, n, u);
+    if (tile == w)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) u0k[e] = u[e];
 #pragma unroll
     for (int e = 0; e < 8; ++e)
       if (b + e < ke) atomicAdd(&lh[u[e] >> 5], 1);
@@ -1163,13 +1165,18 @@ __device__ __forceinline__ bool topk_parts(const LayerParams& p, int L, const To
   digit_of(h4, K, s.sbuf, s.res);
   const int d0 = s.res[0], cum0 = s.res[1], nlist = s.res[1] + s.res[2];
   const uint32_t lo = (uint32_t)d0 << 5;
-  // ---- this part's rows at or above the digit's bin, as (top 16 bits, row)
+  // ---- this part's rows at or above the digit's bin, as (full key, row)
   // pairs in ascending row order from the part's first row's place
   int* tc = s.poff;                               // [ntile]: a tile's pairs, then its first place
   for (int tile = w; tile < ntile; tile += kWaves) {
     const int b = kb + tile * 512 + 8 * lane;
     uint32_t u[8];
-    keys16(k16, b, n, u);
+    if (tile == w) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) u[e] = u0k[e];
+    } else {
+      keys16(k16, b, n, u);
+    }
     int c = 0;
 #pragma unroll
     for (int e = 0; e < 8; ++e) c += __popcll(__ballot(b + e < ke && u[e] >= lo));
@@ -1184,7 +1191,12 @@ __device__ __forceinline__ bool topk_parts(const LayerParams& p, int L, const To
   for (int tile = w; tile < ntile; tile += kWaves) {
     const int b = kb + tile * 512 + 8 * lane;
     uint32_t u[8];
-    keys16(k16, b, n, u);
+    if (tile == w) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) u[e] = u0k[e];
+    } else {
+      keys16(k16, b, n, u);
+    }
     bool sel[8];
     int pb = 0;
 #pragma unroll
@@ -1192,11 +1204,15 @@ __device__ __forceinline__ bool topk_parts(const LayerParams& p, int L, const To
       sel[e] = b + e < ke && u[e] >= lo;
       pb += __popcll(__ballot(sel[e]) & lt);
     }
+    // the selected rows' full 32-bit keys (their scores, read only for them)
+    float f[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = sel[e] ? ldg(sc + b + e) : 0.f;
     int pos = kb + tc[tile] + pb;
 #pragma unroll
     for (int e = 0; e < 8; ++e)
       if (sel[e]) {
-        __hip_atomic_store(pairs + pos, ((uint64_t)u[e] << 32) | (uint32_t)(b + e), __ATOMIC_RELAXED,
+        __hip_atomic_store(pairs + pos, ((uint64_t)order_key(f[e]) << 32) | (uint32_t)(b + e), __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
         ++pos;
       }
@@ -1241,7 +1257,7 @@ __device__ __forceinline__ bool topk_parts(const LayerParams& p, int L, const To
       const int m = m0 + u * kThreads;
       if (m < nlist) {
         s.lrow[m] = (int)(uint32_t)e[u];
-        s.lkey[m] = (uint32_t)(e[u] >> 32) << 16;
+        s.lkey[m] = (uint32_t)(e[u] >> 32);
       }
     }
   }
@@ -1258,13 +1274,8 @@ __device__ __forceinline__ bool topk_parts(const LayerParams& p, int L, const To
     __syncthreads();
     topk_next_digit(s, shift, dmask, prefix, mask, need);
   };
-  list_digit(16, 31u);                            // bits 16..20
-  // the rows that share the threshold's top 16 bits read their full keys
-  for (int m = threadIdx.x; m < nlist; m += kThreads)
-    if (s.lkey[m] == prefix) s.lkey[m] = order_key(ldg(sc + s.lrow[m]));
-  __syncthreads();
-  list_digit(5, 2047u);                           // bits 5..15
-  list_digit(0, 31u);                             // bits 0..4
+  list_digit(10, 2047u);                          // bits 10..20
+  list_digit(0, 1023u);                           // bits 0..9
   // ---- output: wave w writes list entries [w * segl, (w + 1) * segl)
   const int segl = (nlist + kWaves * 64 - 1) / (kWaves * 64) * 64;
   const int lb = min(nlist, w * segl), le = min(nlist, lb + segl);

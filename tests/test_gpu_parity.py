@@ -254,6 +254,27 @@ def test_sparse_attention_all_scores_equal(L):
     assert errs["kept_rows_differing"] == 0 and not errs["kept_rows_forced"]
 
 
+@pytest.mark.parametrize("s", [MID_SP.with_(name="mid_sparse_L20000", L=20000, idx_topk=2048),
+                               MID_SP_K.with_(name="mid_sparse_fp8kv_L20000", L=20000, idx_topk=2048)],
+                         ids=lambda s: s.name)
+def test_sparse_run_twice_bitwise_identical(s):
+    """Two runs of the same sparse step (the top-k over ten parts of the row, its
+    sums of part histograms made with atomics) give bitwise the same output, new
+    cache rows, index scores and kept rows."""
+    from decoder_megakernel_amd import harness
+    import parity
+    print("[parity] %s L=%d" % (s.name, s.L), flush=True)
+    dl = harness.DeviceLayer(s, 0, 0)
+    H = harness.hidden(s)
+    res = []
+    for _ in range(2):
+        kv = harness.kv_cache(s)
+        out, kvn, taps = parity.gpu_step(dl, s, H, kv, s.L, s.T)
+        res.append((out.view(np.uint32), taps["kv_raw"].view(np.uint8), taps["iscore"].view(np.uint32), taps["isel"]))
+    for a, b in zip(res[0], res[1]):
+        assert np.array_equal(a, b)
+
+
 def test_full_size_sparse_fp8_E384_T6_L65536_skew():
     from synth.configs import C4S
     _run(C4S, full_weights=False)
