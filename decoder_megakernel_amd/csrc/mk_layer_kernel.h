@@ -802,18 +802,20 @@ __device__ __forceinline__ void iscore_rows(const LayerParams& p, int L, char* s
           }
         }
       }
-    } else
-    for (int i0 = threadIdx.x; i0 < tot; i0 += kB * kThreads) {
-      u32x4 v[kB];
+    } else {
+      // bf16 rows: 8 values (16 bytes) per piece
+      for (int i0 = threadIdx.x; i0 < tot; i0 += kB * kThreads) {
+        u32x4 v[kB];
 #pragma unroll
-      for (int q = 0; q < kB; ++q) {
-        const int i = min(i0 + q * kThreads, tot - 1), k = i / np;
-        v[q] = ld16(kvb + (long long)min(cb * 16 + k, Lt - 1) * p.kv_row + (i - k * np) * 8);
-      }
+        for (int q = 0; q < kB; ++q) {
+          const int i = min(i0 + q * kThreads, tot - 1), k = i / np;
+          v[q] = ld16(kvb + (long long)min(cb * 16 + k, Lt - 1) * p.kv_row + (i - k * np) * 8);
+        }
 #pragma unroll
-      for (int q = 0; q < kB; ++q) {
-        const int i = i0 + q * kThreads, k = i / np;
-        if (i < tot) *reinterpret_cast<u32x4*>(ks + k * KS + (i - k * np) * 8) = v[q];
+        for (int q = 0; q < kB; ++q) {
+          const int i = i0 + q * kThreads, k = i / np;
+          if (i < tot) *reinterpret_cast<u32x4*>(ks + k * KS + (i - k * np) * 8) = v[q];
+        }
       }
     }
     __syncthreads();
