@@ -140,9 +140,17 @@ def gpu_step(st, s, rec, tokens, next_drafts=None):
         g["sel"].append(sel)
         g["rlogits"].append(rl)
         g["Hp"].append(hp)
+        if s.idx_topk:
+            # sparse attention: the layer's kept rows and index scores
+            isel = np.empty((s.T, s.idx_topk), np.int32)
+            dl.layer.debug_tap(8, isel)
+            isc = np.empty((s.T, (s.capacity + 7) // 8 * 8), np.float32)
+            dl.layer.debug_tap(9, isc)
+            g.setdefault("isel", []).append(isel)
+            g.setdefault("iscore", []).append(isc)
         raw = st.kv[l][L:L + s.T].cpu().numpy()
         g["kv_raw"].append(raw)
-        g["kv_new"].append(parity.kv_to_f32(raw, s.kv_fmt, s.kvw))
+        g["kv_new"].append(parity.kv_to_f32(raw, s.kv_fmt, s.kv_row))
     return g
 
 
@@ -166,6 +174,8 @@ def check_layers_teacher_forced(st, s, ws, g, expert_fn=None, seed=0, layers=Non
         H = g["hidden"][l]
         kvh = gpu_cache_host(st, s, l, L)
         taps = {"Hp": g["Hp"][l], "sel": g["sel"][l], "kv_raw": g["kv_raw"][l]}
+        if s.idx_topk:
+            taps.update(isel=g["isel"][l], iscore=g["iscore"][l])
         kw = dict(full_weights=ws[l]) if "experts" in ws[l] and ws[l]["experts"] else \
             dict(base_weights=ws[l], expert_fn=expert_fn)
         errs = parity.check_layer(s, seed, l, g["hidden"][l + 1], g["kv_new"][l], taps, H, L, kv_host=kvh, **kw)

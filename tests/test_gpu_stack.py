@@ -54,6 +54,38 @@ def test_stack_steps_match_oracle():
         tokens = np.concatenate([[com[-1]], nxt]).astype(np.int32)
 
 
+# Sparse attention over the fp8 cache in the stack: 16 heads (a query tile per
+# verify row), each verify row keeps 24 of its 41..58 visible rows.
+STACK_SPARSE = STACK_SMALL.with_(name="stack3_sparse_fp8kv", n_h=16, kv_fmt="fp8row", idx_heads=16, idx_dim=64,
+                                 idx_topk=24)
+
+
+def test_sparse_fp8kv_stack_steps_match_oracle_teacher_forced():
+    """The stack step with sparse-attention layers over the fp8 cache (the
+    device-resident length feeding the indexer and the top-k): every layer
+    against the oracle on the GPU's own input rows and cache (kept rows checked
+    as in the single-layer tests), the head on the GPU's final rows, and the
+    length advanced by the committed count."""
+    s = STACK_SPARSE
+    st, rec, ws, kvs, tables = _setup(s)
+    L = s.L
+    tokens = recipe.tokens_host(s, 0, 0)
+    for step in range(s.steps):
+        nxt = recipe.tokens_host(s, 0, step + 1)[1:]
+        g = sp.gpu_step(st, s, rec, tokens, nxt)
+        assert g["L"] == L
+        tag = " sparse step %d" % step
+        errs = sp.check_layers_teacher_forced(st, s, ws, g, tag=tag)
+        assert all("kept_rows_differing" in e for e in errs)
+        sp.check_head_teacher_forced(s, tables, g, tag=tag)
+        n = int(g["com"][0])
+        com = list(g["com"][1:1 + n])
+        assert com == list(oracle.greedy_accept(tokens, g["am"])) and g["len"] == L + n
+        assert g["tok"][0] == com[-1] and list(g["tok"][1:]) == list(nxt)
+        L += n
+        tokens = np.concatenate([[com[-1]], nxt]).astype(np.int32)
+
+
 def test_all_drafts_accepted_when_drafts_follow_greedy_decoding():
     """Drafts built by single-token greedy oracle steps: the oracle accepts every
     one of them (causal invariant), and so does the GPU unless an argmax is a
