@@ -15,12 +15,14 @@ torch = pytest.importorskip("torch")
 
 SHAPE = LayerShape("noalloc_fp8", d=640, n_h=6, d_h=64, d_c=256, d_r=64, E=48, top_k=6, n_shared=1, f=384,
                    T=7, L=300, attn_fmt="bf16", exp_fmt="fp8", kv_fmt="bf16", kv_capacity=320)
+# sparse attention over the fp8 cache (the top-k's histograms and counters live in the scratch too)
+SHAPE_SP = SHAPE.with_(name="noalloc_sparse_fp8kv", n_h=16, kv_fmt="fp8row", idx_heads=16, idx_dim=64, idx_topk=100)
 
 
-def test_static_scratch_step_matches_workspace_step_twice_second_smaller():
+@pytest.mark.parametrize("s", [SHAPE, SHAPE_SP], ids=lambda s: s.name)
+def test_static_scratch_step_matches_workspace_step_twice_second_smaller(s):
     from decoder_megakernel_amd import MK_OK, harness
     import parity
-    s = SHAPE
     dl = harness.DeviceLayer(s, 0, 0)
     w = recipe.layer_weights_host(s, 0, 0)
     for T, L in ((7, 300), (3, 120)):
@@ -35,14 +37,18 @@ def test_static_scratch_step_matches_workspace_step_twice_second_smaller():
         torch.cuda.synchronize()
         assert dl.layer.sync_status() == MK_OK
         assert np.array_equal(out_a.cpu().numpy().view(np.uint32), out_b.cpu().numpy().view(np.uint32))
-        assert np.array_equal(kv_a.cpu().numpy().view(np.uint16), kv_b.cpu().numpy().view(np.uint16))
+        assert np.array_equal(kv_a.cpu().numpy().view(np.uint8), kv_b.cpu().numpy().view(np.uint8))
         # the static step's taps and outputs against the oracle
         taps = {}
-        for name, tap, shape, dt in (("Hp", 4, (T, s.d), np.float32), ("sel", 6, (T, s.top_k), np.int32)):
+        pairs = [("Hp", 4, (T, s.d), np.float32), ("sel", 6, (T, s.top_k), np.int32)]
+        if s.idx_topk:
+            pairs += [("isel", 8, (T, s.idx_topk), np.int32), ("iscore", 9, (T, (s.capacity + 7) // 8 * 8), np.float32)]
+        for name, tap, shape, dt in pairs:
             buf = np.empty(shape, dt)
             dl.layer.debug_tap(tap, buf)
             taps[name] = buf
-        g_kv = parity.kv_to_f32(kv_b[L:L + T].cpu().numpy(), s.kv_fmt, s.kvw)
+        taps["kv_raw"] = kv_b[L:L + T].cpu().numpy()
+        g_kv = parity.kv_to_f32(kv_b[L:L + T].cpu().numpy(), s.kv_fmt, s.kv_row)
         errs = parity.check_layer(s2, 0, 0, out_b.cpu().numpy(), g_kv, taps, H, L, full_weights=w)
         print("[no-alloc] T=%d L=%d errors %s" % (T, L, errs), flush=True)
 
