@@ -473,6 +473,8 @@ def process_starts(args, n):
     cmd = [sys.executable, os.path.abspath(__file__), "--workload", args.workload, "--steps", str(args.steps),
            "--warmup", str(args.warmup), "--no-cpu-baseline", "--starts", "1", "--head-fmt", args.head_fmt,
            "--temperature", repr(args.temperature)]
+    if args.kv_len is not None:
+        cmd += ["--kv-len", str(args.kv_len)]
     for i in range(n):
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
@@ -491,6 +493,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="C5", choices=[k for k in BY_KEY if k not in ("C0", "C1")])
     ap.add_argument("--layers", type=int, default=None, help="stack depth override (diagnostics only)")
+    ap.add_argument("--kv-len", type=int, default=None,
+                    help="cached positions before the step, for a single-layer workload (context sweeps)")
     ap.add_argument("--head-fmt", default="bf16", choices=["bf16", "fp8"],
                     help="LM-head table format (the stack workload names bf16)")
     ap.add_argument("--temperature", type=float, default=0.0,
@@ -510,6 +514,11 @@ def main():
               file=sys.stderr)
         sys.exit(2)
     s = BY_KEY[args.workload].with_(head_fmt=args.head_fmt)
+    if args.kv_len is not None:
+        if s.n_layers > 1 or args.kv_len < 0:
+            print("--kv-len applies to single-layer workloads, with a length >= 0", file=sys.stderr)
+            sys.exit(2)
+        s = s.with_(name="%s@L%d" % (s.name, args.kv_len), L=args.kv_len, kv_capacity=0)
     if s.n_layers > 1:
         args.steps = args.steps or 256
         args.warmup = args.warmup if args.warmup is not None else 8
