@@ -209,9 +209,11 @@ MID_SP_ALL = MID_SP.with_(name="mid_sparse_topk_covers_all", idx_topk=512)
 MID_SP_K = MID_SP.with_(name="mid_sparse_fp8kv", kv_fmt="fp8row")
 MID_SP_K_LR = MID_SP_LR.with_(name="mid_sparse_fp8kv_lowrank", kv_fmt="fp8row", exp_fmt="mxfp4")
 MID_SP_K_ALL = MID_SP_K.with_(name="mid_sparse_fp8kv_topk_covers_all", idx_topk=512)
+MID_SP_K_BF = MID_SP_K.with_(name="mid_sparse_fp8kv_bf16_experts", exp_fmt="bf16")
 
 
-@pytest.mark.parametrize("shape", [MID_SP, MID_SP_LR, MID_SP_MX, MID_SP_ALL, MID_SP_K, MID_SP_K_LR, MID_SP_K_ALL],
+@pytest.mark.parametrize("shape", [MID_SP, MID_SP_LR, MID_SP_MX, MID_SP_ALL, MID_SP_K, MID_SP_K_LR, MID_SP_K_ALL,
+                                   MID_SP_K_BF],
                          ids=lambda s: s.name)
 def test_sparse_attention_shapes_match_oracle(shape):
     _run(shape)
