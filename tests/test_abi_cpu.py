@@ -146,3 +146,5 @@ def test_sparse_attention_config_and_sizes():
     assert mk.kv_bytes(k8, 1000) == 1000 * 720
     mk.check_config(_cfg(idx_heads=64, idx_dim=128, idx_topk=2048, idx_max_rows=70000, kv_format="fp8row",
                          expert_format="mxfp4", q_lora_rank=1536, kv_norm=1))
+    mk.check_config(_cfg(idx_heads=64, idx_dim=128, idx_topk=2048, idx_max_rows=70000, kv_format="fp8row",
+                         expert_format="bf16"))
